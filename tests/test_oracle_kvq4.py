@@ -1,0 +1,158 @@
+"""Pins of the int4 group oracle ([P4] Sec. 3.2, 3.3, 5.2) against exact
+rational brute force, round-trip bounds and reductions to the int8 path or to
+library attention."""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import kvq4, kvq8
+from tests.exact import f16, f32, fr, round_half_even
+import workloads as W
+
+SM = float(np.float32(1.0) / np.sqrt(np.float32(128.0)))
+
+
+def _brute_group(vals):
+    xs = [fr(v) for v in vals]
+    mx, mn = max(xs), min(xs)
+    s32 = Fraction(1) if mx == mn else f32(f32(mx - mn) / 15)
+    s32 = max(s32, f32(Fraction(1, 10 ** 7)))
+    s = f16(s32)
+    z = min(15, max(0, round_half_even(f32(-mn / s))))
+    codes = [min(15, max(0, round_half_even(f32(f32(x / s) + z)))) for x in xs]
+    return codes, s, z
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_group_quantization_bruteforce(seed):
+    r = W.rng(200, seed)
+    x = np.concatenate([W.normal_f32(r, (2, 128)), W.normal_f32(r, (1, 128), 4.0),
+                        W.normal_f32(r, (1, 128), 0.01), np.abs(W.normal_f32(r, (1, 128))),
+                        # groups lying wholly above or below zero: the zero-point clamp binds
+                        W.normal_f32(r, (1, 128), 0.1) + np.float32(3), W.normal_f32(r, (1, 128), 0.1) - np.float32(3)])
+    c, s, z = kvq4.quantize_groups_q4(x)
+    assert c.dtype == np.uint8 and s.dtype == np.float16 and z.dtype == np.float16
+    for i in range(len(x)):
+        for g in range(2):
+            bc, bs, bz = _brute_group(x[i, 64 * g:64 * g + 64])
+            assert fr(s[i, g]) == bs and fr(z[i, g]) == bz
+            assert c[i, 64 * g:64 * g + 64].tolist() == bc
+
+
+def test_codes_range_and_half_step_round_trip():
+    r = W.rng(201)
+    x = W.per_unit_sigma_normal(r, (400, 128), 1, 0.2, 5.0)
+    c, s, z = kvq4.quantize_groups_q4(x)
+    assert c.max() <= 15
+    assert np.all((z >= 0) & (z <= 15)) and np.all(z == np.round(z))
+    xr = kvq4.dequantize_groups_q4(c, s, z)
+    step = np.repeat(s.astype(np.float64), 64, axis=-1)
+    # [P4] Sec. 3.2: asymmetric rounding error stays within half a step (plus
+    # the float16 rounding of the scale, which moves the grid ends slightly)
+    lo = np.repeat(x.reshape(400, 2, 64).min(-1), 64, axis=-1)
+    inside = np.abs(x - lo) <= 14.5 * step
+    assert np.all(np.abs(x - xr)[inside] <= step[inside] * 0.5 * (1 + 1e-3) + 1e-7)
+    assert np.all(np.abs(x - xr) <= step * 1.5)
+
+
+def test_constant_groups_use_unit_scale():
+    # [P4] Sec. 3.2: a group with max == min gets scale 1.0, so integer
+    # constants in [-15, 15] come back exactly and others within half a unit
+    x = np.zeros((3, 128), np.float32)
+    x[0, :64], x[0, 64:] = -3.0, 0.0
+    x[1, :64], x[1, 64:] = 5.0, -15.0
+    x[2, :] = 0.25
+    c, s, z = kvq4.quantize_groups_q4(x)
+    assert np.all(s == np.float16(1.0))
+    xr = kvq4.dequantize_groups_q4(c, s, z)
+    np.testing.assert_array_equal(xr[:2], x[:2].astype(np.float64))
+    assert np.all(xr[2] == 0.0)
+
+
+def test_pack_high_nibble_first_and_round_trip():
+    assert kvq4.pack_nibbles(np.array([1, 2, 15, 0], np.uint8)).tolist() == [0x12, 0xF0]
+    r = W.rng(202)
+    c = r.integers(0, 16, size=(7, 128)).astype(np.uint8)
+    p = kvq4.pack_nibbles(c)
+    assert p.shape == (7, 64)
+    assert np.array_equal(kvq4.unpack_nibbles(p), c)
+
+
+def _pools(r, B, n4, n8, nkv, kv_bs, k4=None, v4=None, k8=None, v8=None):
+    bt4, nb4 = W.paged_block_tables(r, [n4] * B, kv_bs)
+    bt8, nb8 = W.paged_block_tables(r, [n8] * B, kv_bs)
+    P4 = [np.zeros((nb4, kv_bs, nkv, 64), np.uint8), np.zeros((nb4, kv_bs, nkv, 2), np.float16),
+          np.zeros((nb4, kv_bs, nkv, 2), np.float16), np.zeros((nb4, kv_bs, nkv, 64), np.uint8),
+          np.zeros((nb4, kv_bs, nkv, 2), np.float16), np.zeros((nb4, kv_bs, nkv, 2), np.float16)]
+    P8 = [np.zeros((nb8, kv_bs, nkv, 128), np.int8), np.zeros((nb8, kv_bs, nkv), np.float32),
+          np.zeros((nb8, kv_bs, nkv, 128), np.int8), np.zeros((nb8, kv_bs, nkv), np.float32)]
+    for b in range(B):
+        if n4:
+            sl = W.slots_for_positions(bt4, [b] * n4, np.arange(n4), kv_bs)
+            kvq4.quantize_append_q4(P4[0], P4[3], P4[1], P4[2], P4[4], P4[5], k4[b], v4[b], sl)
+        if n8:
+            sl = W.slots_for_positions(bt8, [b] * n8, np.arange(n8), kv_bs)
+            kvq8.quantize_append(P8[0], P8[2], P8[1], P8[3], k8[b], v8[b], sl)
+    return (P4[0], P4[1], P4[2], P4[3], P4[4], P4[5]), bt4, (P8[0], P8[1], P8[2], P8[3]), bt8
+
+
+def test_all_int8_equals_int8_path():
+    r = W.rng(210)
+    B, n8, nq, nkv, bs = 2, 40, 8, 2, 16
+    k8 = W.normal_f32(r, (B, n8, nkv, 128))
+    v8 = W.normal_f32(r, (B, n8, nkv, 128))
+    q = W.normal_f32(r, (B, nq, 128))
+    p4, bt4, p8, bt8 = _pools(r, B, 0, n8, nkv, bs, k8=k8, v8=v8)
+    out = kvq4.decode_attention_mixed(q, p4, bt4, [0] * B, p8, bt8, [n8] * B, bs, SM)
+    ref = kvq8.decode_attention_q8(q, p8[0], p8[1], p8[2], p8[3], bt8, [n8] * B, bs, SM)
+    np.testing.assert_allclose(out, ref, rtol=1e-14, atol=1e-15)
+
+
+def test_grid_exact_int4_matches_library_attention():
+    # values (c - z) * s with power-of-two s, integer z in [0, 15], and every
+    # group touching both code 0 and code 15: the quantizer returns them
+    # exactly, so the mixed decode must equal plain attention.
+    r = W.rng(211)
+    B, n4, n8, nq, nkv, bs = 2, 50, 20, 8, 2, 16
+
+    def grid(shape):
+        c = r.integers(0, 16, size=shape + (2, 64))
+        c[..., 0], c[..., 1] = 0, 15
+        z = r.integers(0, 16, size=shape + (2, 1))
+        s = 2.0 ** r.integers(-6, -2, size=shape + (2, 1))
+        return ((c - z) * s).reshape(shape + (128,)).astype(np.float32)
+    k4, v4 = grid((B, n4, nkv)), grid((B, n4, nkv))
+    k8c = r.integers(-126, 127, size=(B, n8, nkv, 128))
+    k8c[..., 5] = 127
+    k8 = (k8c * 2.0 ** -7).astype(np.float32)
+    v8 = (np.roll(k8c, 3, axis=-1) * 2.0 ** -6).astype(np.float32)
+    qc = r.integers(-126, 127, size=(B, nq, 4, 32))
+    qc[..., 0] = -127
+    q = (qc * 2.0 ** -5).reshape(B, nq, 128).astype(np.float32)
+    p4, bt4, p8, bt8 = _pools(r, B, n4, n8, nkv, bs, k4, v4, k8, v8)
+    out = kvq4.decode_attention_mixed(q, p4, bt4, [n4] * B, p8, bt8, [n8] * B, bs, SM)
+    K = np.concatenate([k4, k8], 1).astype(np.float64)
+    V = np.concatenate([v4, v8], 1).astype(np.float64)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q.astype(np.float64))[:, :, None], torch.from_numpy(K).permute(0, 2, 1, 3),
+        torch.from_numpy(V).permute(0, 2, 1, 3), scale=SM, enable_gqa=True)[:, :, 0].numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-6, atol=1e-7)
+
+
+def test_page_order_and_empty_context():
+    # attention does not depend on token order: permuting whole pages of a
+    # full sequence leaves the output unchanged; an empty context is zero
+    r = W.rng(212)
+    nkv, bs, n = 1, 16, 48
+    k4 = W.normal_f32(r, (1, n, nkv, 128))
+    v4 = W.normal_f32(r, (1, n, nkv, 128))
+    p4, bt4, p8, bt8 = _pools(r, 1, n, 0, nkv, bs, k4, v4)
+    q = W.normal_f32(r, (1, 2, 128))
+    a = kvq4.decode_attention_mixed(q, p4, bt4, [n], p8, bt8, [0], bs, SM)
+    bt4p = bt4[:, [2, 0, 1]]
+    b = kvq4.decode_attention_mixed(q, p4, bt4p, [n], p8, bt8, [0], bs, SM)
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-14)
+    z = kvq4.decode_attention_mixed(q, p4, bt4, [0], p8, bt8, [0], bs, SM)
+    assert np.all(z == 0)
