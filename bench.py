@@ -1,0 +1,198 @@
+#!/usr/bin/env python3
+"""Benchmark of the int8-KV decode hot path on one MI355X.
+
+One step = one decode step of a Qwen3-VL-2B-shaped model at 8K context
+(28 layers x 16 query / 8 kv heads, head dim 128, batch 1, paged int8 cache
+with 16-token blocks): for every layer, the write path quantizes the current
+token's K and V (float32) into its cache slot, then decode attention reads
+the layer's 8192 cached tokens.  Inputs are seeded synthetic tensors already
+resident in HBM; the 28 layer caches (484 MB) exceed the 256 MB Infinity
+Cache, so the layers are streamed from HBM.
+
+Output: one JSON line with the effective HBM bandwidth of the whole step
+(algorithmic bytes: int8 K+V codes and float32 steps read by decode, plus the
+write path's input read and code/step writes), microseconds per step, a
+roofline entry for the decode chunk kernel timed with HIP events on its
+stream, and the CPU oracle timed on a bounded sample on the host.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, vendor figure
+TOK_HEAD_BYTES = 2 * 128 + 2 * 4   # K+V codes + K/V float32 steps per (token, kv-head)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--layers", type=int, default=28)
+    p.add_argument("--ctx", type=int, default=8192)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    return p.parse_args()
+
+
+class Layer:
+    """One layer's paged int8 cache, block table and per-step inputs."""
+
+    def __init__(self, K, W, torch, layer, L, nq, nkv, bs):
+        self.bt_np, nb = W.paged_block_tables(W.rng(2, layer, 3), [L], bs)
+        shp = (nb, bs, nkv, 128)
+        self.k = torch.zeros(shp, dtype=torch.int8, device="cuda")
+        self.v = torch.zeros(shp, dtype=torch.int8, device="cuda")
+        self.ks = torch.zeros(shp[:3], dtype=torch.float32, device="cuda")
+        self.vs = torch.zeros(shp[:3], dtype=torch.float32, device="cuda")
+        kf = W.torch_normal((L, nkv, 128), "cuda", (2, layer, 0))
+        vf = W.torch_normal((L, nkv, 128), "cuda", (2, layer, 1))
+        slots = W.slots_for_positions(self.bt_np, [0] * L, np.arange(L), bs)
+        K.kvq8_quantize_append(self.k, self.v, self.ks, self.vs, kf, vf, torch.from_numpy(slots).cuda())
+        self.k_new = kf[L - 1:L].clone()            # the current token's K / V (re-written each step)
+        self.v_new = vf[L - 1:L].clone()
+        del kf, vf
+        self.slot = torch.from_numpy(slots[L - 1:L].copy()).cuda()
+        self.q = W.torch_normal((1, nq, 128), "cuda", (2, layer, 2))
+        self.bt = torch.from_numpy(self.bt_np).cuda()
+        self.lens = torch.tensor([L], dtype=torch.int32, device="cuda")
+        self.out = torch.empty((1, nq, 128), dtype=torch.float32, device="cuda")
+
+
+def cpu_baseline(args, nq, nkv, bs, L, bytes_per_layer):
+    """The oracle, untouched, on a bounded sample of the same workload: whole
+    layers (write the current token, then decode over L tokens) until about
+    args.cpu_seconds of host time.  BLAS is pinned to one thread."""
+    from threadpoolctl import threadpool_limits
+
+    import workloads as W
+    from oracle import kvq8 as O8
+
+    sm = float(np.float32(1) / np.sqrt(np.float32(128)))
+    r = W.rng(2, 1000)
+    bt, nb = W.paged_block_tables(r, [L], bs)
+    k = W.normal_f32(r, (L, nkv, 128))
+    v = W.normal_f32(r, (L, nkv, 128))
+    kp = np.zeros((nb, bs, nkv, 128), np.int8)
+    vp = np.zeros_like(kp)
+    ks = np.zeros((nb, bs, nkv), np.float32)
+    vs = np.zeros_like(ks)
+    slots = W.slots_for_positions(bt, [0] * L, np.arange(L), bs)
+    O8.quantize_append(kp, vp, ks, vs, k, v, slots)
+    q = W.normal_f32(r, (1, nq, 128))
+    layers = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while True:
+            O8.quantize_append(kp, vp, ks, vs, k[-1:], v[-1:], slots[-1:])
+            O8.decode_attention_q8(q, kp, ks, vp, vs, bt, [L], bs, sm)
+            layers += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds:
+                break
+    return {"value": round(bytes_per_layer * layers / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{layers} layers of the same workload (write 1 token + decode over {L} tokens, {nq}/{nkv} "
+                      f"heads), {el:.1f} s single-threaded numpy; ms/layer {1e3 * el / layers:.1f}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build has no multi-GPU path)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import decode_attention_int8_amd as K
+    import workloads as W
+
+    cfg = W.QWEN2B_8K
+    nq, nkv, bs, L, n_layers = cfg["nq"], cfg["nkv"], cfg["kv_bs"], args.ctx, args.layers
+    sm = 1.0 / math.sqrt(128)
+    layers = [Layer(K, W, torch, i, L, nq, nkv, bs) for i in range(n_layers)]
+    chunk = K.kvq8_decode_chunk_tokens(1, nkv, L)
+    ws = K.alloc_workspace(K.kvq8_decode_workspace_size(1, nq, nkv, L, 0), "cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
+        for i, ly in enumerate(layers):
+            K.kvq8_quantize_append(ly.k, ly.v, ly.ks, ly.vs, ly.k_new, ly.v_new, ly.slot, stream)
+            if events is not None:
+                events[i][0].record(stream)
+            K.kvq8_decode_attn(ly.out, ly.q, ly.k, ly.v, ly.ks, ly.vs, ly.bt, ly.lens, L, sm, 0, ws, stream)
+            if events is not None:
+                events[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K whole steps
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for _ in range(args.steps):
+        step()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+
+    # decode-call durations from HIP events on the launch stream, over a
+    # second pass of the same steps
+    ev_steps = max(1, min(args.steps, 50))
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in layers]
+           for _ in range(ev_steps)]
+    for s in range(ev_steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    durs = [a.elapsed_time(b) for st in evs for a, b in st]
+    decode_us = 1e3 * float(np.mean(durs))
+
+    decode_bytes_layer = L * nkv * TOK_HEAD_BYTES
+    write_bytes_layer = nkv * 2 * 128 * 4 + nkv * 2 * (128 + 4)
+    step_bytes = n_layers * (decode_bytes_layer + write_bytes_layer)
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = decode_bytes_layer / (decode_us * 1e-6) / 1e9
+
+    res = {
+        "metric": "q8-KV decode attention: effective HBM GB/s (% of peak) and us/step at 8K ctx",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8 KV codes, fp32 steps and accumulation",
+        "data": "synthetic (seeded N(0,1) K/V/q, paged blocks in shuffled order)",
+        "config": {"workload": f"qwen2b-shaped decode: {n_layers} layers x {nq}q/{nkv}kv heads, hd 128, batch 1, "
+                               f"ctx {L}, kv_bs {bs}, write 1 token + decode per layer",
+                   "global_batch": 1, "seq_len": L, "chunk_tokens": chunk, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "kvq_decode_chunk_kernel<2> + kvq_merge_kernel (one kvq8_decode_attn call)",
+                     "bytes_per_launch": decode_bytes_layer, "avg_call_us": round(decode_us, 3)},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(args, nq, nkv, bs, L, decode_bytes_layer + write_bytes_layer)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,24 @@
+"""int8 / int4 KV-cache decode attention for AMD Instinct MI355X (gfx950).
+
+The compute lives in the HIP library ``libkvq8.so`` (C ABI in
+``include/kvq8.h``); :mod:`decode_attention_int8_amd.kvq8` is its thin ctypes
+binding.  Importing this package does not load the library; the first call
+does, and raises if the library has not been built.
+"""
+from .kvq8 import (  # noqa: F401
+    KVQ8Error,
+    alloc_workspace,
+    kvq4_decode_attn,
+    kvq4_decode_chunk_tokens,
+    kvq4_decode_workspace_size,
+    kvq4_quantize_append,
+    kvq8_decode_attn,
+    kvq8_decode_chunk_tokens,
+    kvq8_decode_workspace_size,
+    kvq8_qk_partials,
+    kvq8_quantize_append,
+    kvq8_quantize_q,
+    kvq8_status_string,
+    kvq8_version,
+    lib,
+)

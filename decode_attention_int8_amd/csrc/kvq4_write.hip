@@ -1,0 +1,128 @@
+// Write path of the int4 group variant ([P4] Sec. 3.2 quantizer with the
+// Sec. 5.2 checklist).
+//
+// kvq4_quantize_append_kernel: one (token, kv-head, K-or-V) row per 16 lanes,
+// 8 values per lane; each 64-value group is one aligned 8-lane half row, so
+// its max / min need only quad and half-mirror DPP steps.
+#include "kvq8.h"
+#include "kvq_device.h"
+#include "kvq_host.h"
+
+namespace kvq {
+
+template <int DT>
+__device__ __forceinline__ void load8_any(const void* base, size_t elem_off, float (&x)[8]) {
+    if constexpr (DT == KVQ8_F32) {
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem_off);
+        const float4 u = p[0], v = p[1];
+        x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
+        x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
+    } else {
+        const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem_off);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (DT == KVQ8_BF16) {
+                x[2 * i] = __uint_as_float(w[i] << 16);
+                x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+            } else {
+                x[2 * i] = half_bits_f(w[i] & 0xFFFFu);
+                x[2 * i + 1] = half_bits_f(w[i] >> 16);
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ uint16_t f16_bits_rne(float x) {
+    return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+// Quantize the lane's 8 values of a 64-value group held by an aligned 8-lane
+// half row: returns 4 packed bytes (value 2k in the high nibble of byte k),
+// the binary16 scale and the zero point.
+__device__ __forceinline__ void quantize_group8x8(const float (&x)[8], uint32_t& packed, uint16_t& s16,
+                                                  uint16_t& z16) {
+#pragma clang fp contract(off)
+    float mx = x[0], mn = x[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) {
+        mx = fmaxf(mx, x[e]);
+        mn = fminf(mn, x[e]);
+    }
+    mx = fmaxf(mx, dpp_f<kDppXor1>(mx));
+    mn = fminf(mn, dpp_f<kDppXor1>(mn));
+    mx = fmaxf(mx, dpp_f<kDppXor2>(mx));
+    mn = fminf(mn, dpp_f<kDppXor2>(mn));
+    mx = fmaxf(mx, dpp_f<kDppHalfMirror>(mx));
+    mn = fminf(mn, dpp_f<kDppHalfMirror>(mn));
+    float s32 = (mx == mn) ? 1.0f : (mx - mn) / 15.0f;
+    s32 = fmaxf(s32, 1e-7f);
+    s16 = f16_bits_rne(s32);
+    const float s = half_bits_f(s16);
+    const float z = fminf(fmaxf(rintf(-mn / s), 0.0f), 15.0f);
+    z16 = f16_bits_rne(z);
+    uint32_t w = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float ce = fminf(fmaxf(rintf(x[2 * k] / s + z), 0.0f), 15.0f);
+        const float co = fminf(fmaxf(rintf(x[2 * k + 1] / s + z), 0.0f), 15.0f);
+        w |= (((uint32_t)ce << 4) | (uint32_t)co) << (8 * k);
+    }
+    packed = w;
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void kvq4_quantize_append_kernel(
+    uint8_t* __restrict__ kc, uint8_t* __restrict__ vc, uint16_t* __restrict__ ks, uint16_t* __restrict__ kz,
+    uint16_t* __restrict__ vs, uint16_t* __restrict__ vz, long n_slots, int nkv, const void* __restrict__ k_new,
+    const void* __restrict__ v_new, long n_rows, const int32_t* __restrict__ slots) {
+    const int l16 = threadIdx.x & 15;
+    const long row = (long)blockIdx.x * 16 + (threadIdx.x >> 4);
+    if (row >= n_rows) return;                     // whole 16-lane rows leave together
+    const int kind = (int)(row & 1);
+    const long tr = row >> 1;
+    const long tok = tr / nkv;
+    const int kh = (int)(tr - tok * nkv);
+    float x[8];
+    load8_any<DT>(kind ? v_new : k_new, (size_t)tr * kHD + 8 * l16, x);
+    uint32_t packed;
+    uint16_t s16, z16;
+    quantize_group8x8(x, packed, s16, z16);
+    const long slot = slots[tok];
+    if (slot < 0 || slot >= n_slots) return;
+    const size_t dst = (size_t)slot * nkv + kh;
+    *reinterpret_cast<uint32_t*>((kind ? vc : kc) + dst * (kHD / 2) + 4 * l16) = packed;
+    if ((l16 & 7) == 0) {
+        (kind ? vs : ks)[dst * 2 + (l16 >> 3)] = s16;
+        (kind ? vz : kz)[dst * 2 + (l16 >> 3)] = z16;
+    }
+}
+
+}  // namespace kvq
+
+using namespace kvq;
+
+extern "C" int kvq4_quantize_append(uint8_t* k_cache, uint8_t* v_cache, uint16_t* k_scale, uint16_t* k_zero,
+                                    uint16_t* v_scale, uint16_t* v_zero, int n_blocks, int kv_bs, int nkv, int hd,
+                                    const void* k_new, const void* v_new, int dtype, int n_tokens,
+                                    const int32_t* slots, void* stream) {
+    if (hd != kHD || !valid_block_size(kv_bs) || nkv < 1 || n_blocks < 1) return KVQ8_ESHAPE;
+    if (n_tokens < 0 || dtype < KVQ8_F32 || dtype > KVQ8_F16) return KVQ8_EINVAL;
+    if (n_tokens == 0) return KVQ8_OK;
+    if (!k_cache || !v_cache || !k_scale || !k_zero || !v_scale || !v_zero || !k_new || !v_new || !slots)
+        return KVQ8_EINVAL;
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache)) return KVQ8_EINVAL;
+    const long n_rows = (long)n_tokens * nkv * 2;
+    const long n_slots = (long)n_blocks * kv_bs;
+    const dim3 grid((unsigned)((n_rows + 15) / 16)), block(256);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+#define KVQ4_LAUNCH(DT)                                                                                     \
+    hipLaunchKernelGGL(kvq4_quantize_append_kernel<DT>, grid, block, 0, s, k_cache, v_cache, k_scale, k_zero, \
+                       v_scale, v_zero, n_slots, nkv, k_new, v_new, n_rows, slots)
+    if (dtype == KVQ8_F32) KVQ4_LAUNCH(KVQ8_F32);
+    else if (dtype == KVQ8_BF16) KVQ4_LAUNCH(KVQ8_BF16);
+    else KVQ4_LAUNCH(KVQ8_F16);
+#undef KVQ4_LAUNCH
+    return launch_status();
+}
+

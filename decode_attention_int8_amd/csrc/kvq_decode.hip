@@ -1,0 +1,193 @@
+// Entry points of decode attention: the int8 cache ([P3] Sec. 1-2), the
+// integer partials export, and the mixed int4 / int8 cache of the group
+// variant ([P4] Sec. 3.2-3.3).  The pipeline itself lives in
+// kvq_decode_core.h and is compiled once, here.
+#include "kvq_decode_core.h"
+
+namespace kvq {
+
+// Integer block partials of every (sequence, query head, token): one wave per
+// (sequence, kv-head, 64-token tile), with the decode kernel's loader and dot
+// code.
+template <int G>
+__global__ __launch_bounds__(kWave) void kvq8_qk_partials_kernel(DecodeArgs a, int32_t* __restrict__ partials,
+                                                                 int n_tiles) {
+    const int lane = threadIdx.x;
+    const int tg = lane >> 3;
+    const int j = lane & 7;
+    const int tile = blockIdx.x % n_tiles;
+    const int kh = (blockIdx.x / n_tiles) % a.nkv;
+    const int b = blockIdx.x / (n_tiles * a.nkv);
+    const int L = effective_len(a.r8, b, a.log2_bs);
+    const int tile_base = tile * kTile;
+    if (tile_base >= L) return;
+    uint32_t qc[G][4];
+    float qs[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+        quantize_q_segment(a.q + ((size_t)b * a.nq + (size_t)kh * G + h) * kHD, j, qc[h], qs[h]);
+    uint4 kr[8], vr[8];
+    float ksr[8], vsr[8];
+    bool valid[8];
+    load_tile_q8<false>(a, a.r8.bt + (size_t)b * a.r8.max_blocks, L, kh, tile_base, tg, j, kr, vr, ksr, vsr, valid);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const int t = tile_base + 8 * r + tg;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const int d = block_dot(qc[h], kr[r]);
+            if (valid[r] && (j & 1) == 0)
+                partials[(((size_t)b * a.nq + (size_t)kh * G + h) * a.r8.max_len + t) * 4 + (j >> 1)] = d;
+        }
+    }
+}
+
+template <int G>
+inline void launch_partials(const DecodeArgs& a, int32_t* partials, int n_tiles, hipStream_t s) {
+    hipLaunchKernelGGL(kvq8_qk_partials_kernel<G>, dim3(a.batch * a.nkv * n_tiles), dim3(kWave), 0, s, a,
+                       partials, n_tiles);
+}
+
+}  // namespace kvq
+
+using namespace kvq;
+
+extern "C" int kvq8_decode_chunk_tokens(int batch, int nkv, int max_ctx_len) {
+    if (batch < 0 || nkv < 1 || max_ctx_len < 0) return 0;
+    return default_tiles_per_wave((long)batch * nkv, max_ctx_len) * kChunkUnit;
+}
+
+static int resolve_chunk8(int batch, int nkv, int max_ctx_len, int chunk) {
+    if (chunk == 0) return kvq8_decode_chunk_tokens(batch, nkv, max_ctx_len);
+    if (chunk < 0 || chunk % kChunkUnit != 0 || chunk > 64 * kChunkUnit) return -1;
+    return chunk;
+}
+
+extern "C" size_t kvq8_decode_workspace_size(int batch, int nq, int nkv, int max_ctx_len, int chunk) {
+    if (batch < 0 || nq < 1 || nkv < 1 || max_ctx_len < 0) return 0;
+    const int ch = resolve_chunk8(batch, nkv, max_ctx_len, chunk);
+    if (ch <= 0) return 0;
+    return decode_workspace_bytes(batch, nq, (max_ctx_len + ch - 1) / ch);
+}
+
+extern "C" int kvq8_decode_attn(float* out, const float* q, int batch, int nq, const int8_t* k_cache,
+                                const int8_t* v_cache, const float* k_scale, const float* v_scale, int n_blocks,
+                                int kv_bs, int nkv, int hd, const int32_t* block_tables, int max_blocks_per_seq,
+                                const int32_t* ctx_lens, int max_ctx_len, float sm_scale, int chunk,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    if (!decode_shape_ok(batch, nq, nkv, hd, kv_bs) || n_blocks < 1 || max_blocks_per_seq < 1) return KVQ8_ESHAPE;
+    if (max_ctx_len < 0) return KVQ8_EINVAL;
+    const int ch = resolve_chunk8(batch, nkv, max_ctx_len, chunk);
+    if (ch <= 0) return KVQ8_ESHAPE;
+    if (batch == 0) return KVQ8_OK;
+    if (!out || !q || !k_cache || !v_cache || !k_scale || !v_scale || !block_tables || !ctx_lens)
+        return KVQ8_EINVAL;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return KVQ8_EINVAL;
+    const size_t need = kvq8_decode_workspace_size(batch, nq, nkv, max_ctx_len, chunk);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return KVQ8_EWORKSPACE;
+
+    DecodeArgs a = {};
+    a.q = q;
+    a.kc = k_cache;
+    a.vc = v_cache;
+    a.ks = k_scale;
+    a.vs = v_scale;
+    a.r8 = Region{block_tables, ctx_lens, max_blocks_per_seq, max_ctx_len, n_blocks, (max_ctx_len + ch - 1) / ch};
+    a.r4 = Region{nullptr, nullptr, 1, 0, 0, 0};
+    a.nq = nq;
+    a.nkv = nkv;
+    a.log2_bs = ilog2(kv_bs);
+    a.batch = batch;
+    a.tiles_per_wave = ch / kChunkUnit;
+    a.score_scale = sm_scale * kLog2e;
+    bind_workspace(a, workspace);
+    return launch_decode(a, out, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int kvq8_qk_partials(int32_t* partials, const float* q, int batch, int nq, const int8_t* k_cache,
+                                int n_blocks, int kv_bs, int nkv, int hd, const int32_t* block_tables,
+                                int max_blocks_per_seq, const int32_t* ctx_lens, int max_ctx_len, void* stream) {
+    if (!decode_shape_ok(batch, nq, nkv, hd, kv_bs) || n_blocks < 1 || max_blocks_per_seq < 1) return KVQ8_ESHAPE;
+    if (max_ctx_len < 0) return KVQ8_EINVAL;
+    if (batch == 0 || max_ctx_len == 0) return KVQ8_OK;
+    if (!partials || !q || !k_cache || !block_tables || !ctx_lens) return KVQ8_EINVAL;
+    if (!aligned16(q) || !aligned16(k_cache)) return KVQ8_EINVAL;
+    DecodeArgs a = {};
+    a.q = q;
+    a.kc = k_cache;
+    a.r8 = Region{block_tables, ctx_lens, max_blocks_per_seq, max_ctx_len, n_blocks, 1};
+    a.nq = nq;
+    a.nkv = nkv;
+    a.log2_bs = ilog2(kv_bs);
+    a.batch = batch;
+    const int n_tiles = (max_ctx_len + kTile - 1) / kTile;
+    if ((long)batch * nkv * n_tiles > 0x7FFFFFFFL) return KVQ8_ESHAPE;
+    KVQ_DISPATCH_G(nq / nkv, launch_partials, a, partials, n_tiles, static_cast<hipStream_t>(stream));
+    return launch_status();
+}
+
+extern "C" int kvq4_decode_chunk_tokens(int batch, int nkv, int max_len4, int max_len8) {
+    if (batch < 0 || nkv < 1 || max_len4 < 0 || max_len8 < 0) return 0;
+    return default_tiles_per_wave((long)batch * nkv, (long)max_len4 + max_len8) * kChunkUnit;
+}
+
+static int resolve_chunk4(int batch, int nkv, int max_len4, int max_len8, int chunk) {
+    if (chunk == 0) return kvq4_decode_chunk_tokens(batch, nkv, max_len4, max_len8);
+    if (chunk < 0 || chunk % kChunkUnit != 0 || chunk > 64 * kChunkUnit) return -1;
+    return chunk;
+}
+
+extern "C" size_t kvq4_decode_workspace_size(int batch, int nq, int nkv, int max_len4, int max_len8, int chunk) {
+    if (batch < 0 || nq < 1 || nkv < 1 || max_len4 < 0 || max_len8 < 0) return 0;
+    const int ch = resolve_chunk4(batch, nkv, max_len4, max_len8, chunk);
+    if (ch <= 0) return 0;
+    return decode_workspace_bytes(batch, nq, (max_len4 + ch - 1) / ch + (max_len8 + ch - 1) / ch);
+}
+
+extern "C" int kvq4_decode_attn(float* out, const float* q, int batch, int nq, const uint8_t* k_cache4,
+                                const uint8_t* v_cache4, const uint16_t* k_scale4, const uint16_t* k_zero4,
+                                const uint16_t* v_scale4, const uint16_t* v_zero4, int n_blocks4,
+                                const int32_t* block_tables4, int max_blocks_per_seq4, const int32_t* lens4,
+                                int max_len4, const int8_t* k_cache8, const int8_t* v_cache8,
+                                const float* k_scale8, const float* v_scale8, int n_blocks8,
+                                const int32_t* block_tables8, int max_blocks_per_seq8, const int32_t* lens8,
+                                int max_len8, int kv_bs, int nkv, int hd, float sm_scale, int chunk,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    if (!decode_shape_ok(batch, nq, nkv, hd, kv_bs)) return KVQ8_ESHAPE;
+    if (n_blocks4 < 1 || n_blocks8 < 1 || max_blocks_per_seq4 < 1 || max_blocks_per_seq8 < 1) return KVQ8_ESHAPE;
+    if (max_len4 < 0 || max_len8 < 0) return KVQ8_EINVAL;
+    const int ch = resolve_chunk4(batch, nkv, max_len4, max_len8, chunk);
+    if (ch <= 0) return KVQ8_ESHAPE;
+    if (batch == 0) return KVQ8_OK;
+    if (!out || !q || !k_cache4 || !v_cache4 || !k_scale4 || !k_zero4 || !v_scale4 || !v_zero4 ||
+        !block_tables4 || !lens4 || !k_cache8 || !v_cache8 || !k_scale8 || !v_scale8 || !block_tables8 || !lens8)
+        return KVQ8_EINVAL;
+    if (!aligned16(q) || !aligned16(k_cache4) || !aligned16(v_cache4) || !aligned16(k_cache8) ||
+        !aligned16(v_cache8))
+        return KVQ8_EINVAL;
+    const size_t need = kvq4_decode_workspace_size(batch, nq, nkv, max_len4, max_len8, chunk);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return KVQ8_EWORKSPACE;
+
+    DecodeArgs a = {};
+    a.q = q;
+    a.kc = k_cache8;
+    a.vc = v_cache8;
+    a.ks = k_scale8;
+    a.vs = v_scale8;
+    a.k4 = k_cache4;
+    a.v4 = v_cache4;
+    a.k4s = k_scale4;
+    a.k4z = k_zero4;
+    a.v4s = v_scale4;
+    a.v4z = v_zero4;
+    a.r8 = Region{block_tables8, lens8, max_blocks_per_seq8, max_len8, n_blocks8, (max_len8 + ch - 1) / ch};
+    a.r4 = Region{block_tables4, lens4, max_blocks_per_seq4, max_len4, n_blocks4, (max_len4 + ch - 1) / ch};
+    a.nq = nq;
+    a.nkv = nkv;
+    a.log2_bs = ilog2(kv_bs);
+    a.batch = batch;
+    a.tiles_per_wave = ch / kChunkUnit;
+    a.score_scale = sm_scale * kLog2e;
+    bind_workspace(a, workspace);
+    return launch_decode(a, out, static_cast<hipStream_t>(stream));
+}

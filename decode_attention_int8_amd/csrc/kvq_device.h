@@ -1,0 +1,165 @@
+// Device building blocks shared by the kernels of the int8 / int4 KV library
+// (gfx950, wave64).  Cross-lane traffic uses DPP row operations, which the
+// compiler fuses into the consuming VALU instruction.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+constexpr int kHD = 128;        // head dimension
+constexpr int kWave = 64;       // wavefront width on CDNA
+constexpr int kQBlock = 32;     // query quantization block ([P3] Sec. 2 seg. 1)
+constexpr int kTile = 64;       // tokens per wave tile in the decode kernels
+
+// DPP controls (gfx9 encoding).
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7-i inside each 8-lane half row
+constexpr int kDppRowRor8 = 0x128;    // lane i <- lane (i+8) mod 16 inside each 16-lane row
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// value from lane (lane ^ 16), within each half of the wave
+__device__ __forceinline__ float swz_xor16(float v) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+}
+// value from lane (lane ^ 32)
+__device__ __forceinline__ float xor32(float v) {
+    const int lane = __lane_id();
+    return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __float_as_int(v)));
+}
+
+// Reductions over the 8 groups of 8 lanes that hold the same value pattern
+// (lanes with equal lane % 8).  Every lane receives the result.
+__device__ __forceinline__ float group8_max(float v) {
+    v = fmaxf(v, dpp_f<kDppRowRor8>(v));
+    v = fmaxf(v, swz_xor16(v));
+    v = fmaxf(v, xor32(v));
+    return v;
+}
+__device__ __forceinline__ float group8_sum(float v) {
+    v += dpp_f<kDppRowRor8>(v);
+    v += swz_xor16(v);
+    v += xor32(v);
+    return v;
+}
+
+// signed byte k of a packed dword as float (one SDWA convert)
+__device__ __forceinline__ float sbyte_f(uint32_t w, int k) {
+    return (float)(int8_t)(w >> (8 * k));
+}
+
+// -----------------------------------------------------------------------------
+// Symmetric int8 quantization of one 128-value row held by 16 consecutive
+// lanes, 8 values per lane ([P1] Sec. 2, [P2] Sec. 2).
+//   amax = max |x| over the row (values < 1e-6 become 1)
+//   d    = amax / 127          (IEEE float32 division)
+//   code = roundf(x / d)       (IEEE division, ties away from zero), |code|<=127
+// The 16 lanes must be one aligned DPP row (lanes 16r .. 16r+15).
+// -----------------------------------------------------------------------------
+__device__ __forceinline__ void quantize_row16x8(const float (&x)[8], uint32_t& lo, uint32_t& hi, float& d) {
+#pragma clang fp contract(off)
+    float a = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(x[e]));
+    a = fmaxf(a, dpp_f<kDppXor1>(a));
+    a = fmaxf(a, dpp_f<kDppXor2>(a));
+    a = fmaxf(a, dpp_f<kDppHalfMirror>(a));
+    a = fmaxf(a, dpp_f<kDppRowRor8>(a));
+    if (a < 1e-6f) a = 1.0f;
+    d = a / 127.0f;
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        float r = roundf(x[e] / d);
+        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        w[e >> 2] |= ((uint32_t)(int)r & 0xFFu) << (8 * (e & 3));
+    }
+    lo = w[0];
+    hi = w[1];
+}
+
+// -----------------------------------------------------------------------------
+// Query quantization ([P3] Sec. 2 seg. 1) in the decode lane layout: lane
+// segment j = lane % 8 owns values 16j .. 16j+15 of the query row, so block
+// b = j / 2 is shared by lanes 2b and 2b+1.
+//   qm  = max |q| over the 32-value block (qm < 1e-6 -> 1)
+//   qsc = qm * (1/127)         (float32 constant 1/127)
+//   iq  = 127 / qm             (IEEE division)
+//   code= roundf(q * iq) clamped to [-128, 127]
+// Returns the lane's 16 codes packed in 4 dwords and its block's scale.
+// -----------------------------------------------------------------------------
+__device__ __forceinline__ void quantize_q_segment(const float* __restrict__ qrow, int j,
+                                                   uint32_t (&codes)[4], float& qsc) {
+#pragma clang fp contract(off)
+    const float4* p = reinterpret_cast<const float4*>(qrow + 16 * j);
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float4 t = p[i];
+        v[4 * i + 0] = t.x;
+        v[4 * i + 1] = t.y;
+        v[4 * i + 2] = t.z;
+        v[4 * i + 3] = t.w;
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+    m = fmaxf(m, dpp_f<kDppXor1>(m));
+    if (m < 1e-6f) m = 1.0f;
+    constexpr float kInv127 = 1.0f / 127.0f;
+    qsc = m * kInv127;
+    const float iq = 127.0f / m;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float r = roundf(v[4 * i + e] * iq);
+            r = fminf(fmaxf(r, -128.0f), 127.0f);
+            w |= ((uint32_t)(int)r & 0xFFu) << (8 * e);
+        }
+        codes[i] = w;
+    }
+}
+
+// int32 dot product of 16 query codes with 16 key codes (4 packed dwords
+// each), then the partner lane's half: the full 32-value block dot product
+// dot_b of [P3] Sec. 2 seg. 2, held by both lanes of the block.
+__device__ __forceinline__ int block_dot(const uint32_t (&qc)[4], const uint4& k) {
+    int d = __builtin_amdgcn_sdot4((int)qc[0], (int)k.x, 0, false);
+    d = __builtin_amdgcn_sdot4((int)qc[1], (int)k.y, d, false);
+    d = __builtin_amdgcn_sdot4((int)qc[2], (int)k.z, d, false);
+    d = __builtin_amdgcn_sdot4((int)qc[3], (int)k.w, d, false);
+    return d + dpp_i<kDppXor1>(d);
+}
+
+// Sum over the 4 blocks of sum_b qsc_b * dot_b: lanes of a token group hold
+// blocks (j/2) = 0..3 in pairs; after xor-2 and the half mirror every lane of
+// the 8-lane group holds the total.
+__device__ __forceinline__ float block_scaled_sum(int dot_b, float qsc_b) {
+    float f = (float)dot_b * qsc_b;
+    f += dpp_f<kDppXor2>(f);
+    f += dpp_f<kDppHalfMirror>(f);
+    return f;
+}
+
+// IEEE binary16 bits (low 16 bits of v) widened to float (exact)
+__device__ __forceinline__ float half_bits_f(uint32_t v) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)v);
+}
+
+__device__ __forceinline__ uint4 ldg16(const void* p) {
+    return *reinterpret_cast<const uint4*>(p);
+}
+
+}  // namespace kvq

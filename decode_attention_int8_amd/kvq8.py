@@ -1,0 +1,253 @@
+"""Python binding of ``libkvq8.so`` (ctypes).
+
+Argument marshalling only: every function takes torch tensors that already
+live on the GPU, checks their dtype / shape / layout, passes raw device
+pointers and the current HIP stream to the C entry point of the same name,
+and raises on a non-zero status.  No computation happens here, and there is
+no fallback: if the library is not built, every call raises.
+
+torch is imported before the library is loaded so that the library binds to
+the HIP runtime torch has already loaded (same soname), and the stream handle
+torch hands out is valid in it.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+HD = 128
+F32, BF16, F16 = 0, 1, 2
+_DTYPES = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq8.so")
+
+_c_int, _c_size, _p, _f = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+
+# name -> (restype, argtypes); mirrors include/kvq8.h
+_SIGNATURES = {
+    "kvq8_status_string": (ctypes.c_char_p, [_c_int]),
+    "kvq8_version": (ctypes.c_char_p, []),
+    "kvq8_quantize_append": (_c_int, [_p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _p, _p, _c_int, _c_int,
+                                      _p, _p]),
+    "kvq8_decode_chunk_tokens": (_c_int, [_c_int, _c_int, _c_int]),
+    "kvq8_decode_workspace_size": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
+    "kvq8_decode_attn": (_c_int, [_p, _p, _c_int, _c_int, _p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _p,
+                                  _c_int, _p, _c_int, _f, _c_int, _p, _c_size, _p]),
+    "kvq8_quantize_q": (_c_int, [_p, _p, _p, _c_int, _c_int, _p]),
+    "kvq8_qk_partials": (_c_int, [_p, _p, _c_int, _c_int, _p, _c_int, _c_int, _c_int, _c_int, _p, _c_int, _p,
+                                  _c_int, _p]),
+    "kvq4_quantize_append": (_c_int, [_p, _p, _p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _p, _p, _c_int,
+                                      _c_int, _p, _p]),
+    "kvq4_decode_chunk_tokens": (_c_int, [_c_int, _c_int, _c_int, _c_int]),
+    "kvq4_decode_workspace_size": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
+    "kvq4_decode_attn": (_c_int, [_p, _p, _c_int, _c_int,
+                                  _p, _p, _p, _p, _p, _p, _c_int, _p, _c_int, _p, _c_int,
+                                  _p, _p, _p, _p, _c_int, _p, _c_int, _p, _c_int,
+                                  _c_int, _c_int, _c_int, _f, _c_int, _p, _c_size, _p]),
+}
+
+_lib = None
+
+
+class KVQ8Error(RuntimeError):
+    pass
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise KVQ8Error(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; "
+                            f"g.build()'` (hipcc, gfx950)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        msg = lib().kvq8_status_string(status).decode()
+        raise KVQ8Error(f"{what} failed: {msg} ({status})")
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None, dtype=None, name="tensor"):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def kvq8_status_string(status: int) -> str:
+    return lib().kvq8_status_string(status).decode()
+
+
+def kvq8_version() -> str:
+    return lib().kvq8_version().decode()
+
+
+# ----------------------------------------------------------------------------
+# int8 path
+# ----------------------------------------------------------------------------
+
+def kvq8_quantize_append(k_cache, v_cache, k_scale, v_scale, k_new, v_new, slots, stream=None):
+    """Quantize k_new / v_new [n_tokens][nkv][128] (f32, bf16 or f16) into the
+    int8 cache [n_blocks][kv_bs][nkv][128] at ``slots`` (int32)."""
+    n_blocks, kv_bs, nkv, hd = k_cache.shape
+    if k_new.dtype not in _DTYPES or v_new.dtype != k_new.dtype:
+        raise ValueError("k_new / v_new must share one of float32, bfloat16, float16")
+    if tuple(k_new.shape[1:]) != (nkv, hd) or v_new.shape != k_new.shape:
+        raise ValueError("k_new / v_new must be [n_tokens][nkv][hd]")
+    if k_scale.shape != (n_blocks, kv_bs, nkv) or v_scale.shape != k_scale.shape or v_cache.shape != k_cache.shape:
+        raise ValueError("cache / scale shapes disagree")
+    if slots.shape != (k_new.shape[0],):
+        raise ValueError("slots must be [n_tokens]")
+    st = lib().kvq8_quantize_append(
+        _ptr(k_cache, torch.int8, "k_cache"), _ptr(v_cache, torch.int8, "v_cache"),
+        _ptr(k_scale, torch.float32, "k_scale"), _ptr(v_scale, torch.float32, "v_scale"),
+        n_blocks, kv_bs, nkv, hd, _ptr(k_new, name="k_new"), _ptr(v_new, name="v_new"), _DTYPES[k_new.dtype],
+        k_new.shape[0], _ptr(slots, torch.int32, "slots"), _stream(stream))
+    _check(st, "kvq8_quantize_append")
+
+
+def kvq8_decode_chunk_tokens(batch: int, nkv: int, max_ctx_len: int) -> int:
+    return lib().kvq8_decode_chunk_tokens(batch, nkv, max_ctx_len)
+
+
+def kvq8_decode_workspace_size(batch: int, nq: int, nkv: int, max_ctx_len: int, chunk: int = 0) -> int:
+    return lib().kvq8_decode_workspace_size(batch, nq, nkv, max_ctx_len, chunk)
+
+
+def alloc_workspace(nbytes: int, device) -> torch.Tensor:
+    """Device bytes for a workspace argument (16-byte aligned by torch)."""
+    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+
+def kvq8_decode_attn(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, ctx_lens, max_ctx_len: int,
+                     sm_scale: float | None = None, chunk: int = 0, workspace=None, stream=None):
+    """Decode attention: out [B][nq][128] (float32) from q [B][nq][128] over
+    the int8 cache.  ``workspace`` (uint8) is allocated when not given."""
+    B, nq, hd = q.shape
+    n_blocks, kv_bs, nkv, _ = k_cache.shape
+    if out.shape != q.shape:
+        raise ValueError("out must match q")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or ctx_lens.shape != (B,):
+        raise ValueError("block_tables must be [B][max_blocks], ctx_lens [B]")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(hd)
+    need = kvq8_decode_workspace_size(B, nq, nkv, max_ctx_len, chunk)
+    if workspace is None:
+        workspace = alloc_workspace(need, q.device)
+    st = lib().kvq8_decode_attn(
+        _ptr(out, torch.float32, "out"), _ptr(q, torch.float32, "q"), B, nq,
+        _ptr(k_cache, torch.int8, "k_cache"), _ptr(v_cache, torch.int8, "v_cache"),
+        _ptr(k_scale, torch.float32, "k_scale"), _ptr(v_scale, torch.float32, "v_scale"),
+        n_blocks, kv_bs, nkv, hd, _ptr(block_tables, torch.int32, "block_tables"), block_tables.shape[1],
+        _ptr(ctx_lens, torch.int32, "ctx_lens"), max_ctx_len, float(sm_scale), chunk,
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
+    _check(st, "kvq8_decode_attn")
+    return out
+
+
+def kvq8_quantize_q(qi, qsc, q, stream=None):
+    """Query codes qi [n][128] int8 and block scales qsc [n][4] float32."""
+    n = q.numel() // HD
+    st = lib().kvq8_quantize_q(_ptr(qi, torch.int8, "qi"), _ptr(qsc, torch.float32, "qsc"),
+                               _ptr(q, torch.float32, "q"), n, HD, _stream(stream))
+    _check(st, "kvq8_quantize_q")
+
+
+def kvq8_qk_partials(partials, q, k_cache, block_tables, ctx_lens, max_ctx_len: int, stream=None):
+    """int32 block partials [B][nq][max_ctx_len][4]."""
+    B, nq, hd = q.shape
+    n_blocks, kv_bs, nkv, _ = k_cache.shape
+    if partials.shape != (B, nq, max_ctx_len, 4):
+        raise ValueError("partials must be [B][nq][max_ctx_len][4]")
+    st = lib().kvq8_qk_partials(
+        _ptr(partials, torch.int32, "partials"), _ptr(q, torch.float32, "q"), B, nq,
+        _ptr(k_cache, torch.int8, "k_cache"), n_blocks, kv_bs, nkv, hd,
+        _ptr(block_tables, torch.int32, "block_tables"), block_tables.shape[1],
+        _ptr(ctx_lens, torch.int32, "ctx_lens"), max_ctx_len, _stream(stream))
+    _check(st, "kvq8_qk_partials")
+
+
+# ----------------------------------------------------------------------------
+# int4 group variant
+# ----------------------------------------------------------------------------
+
+def kvq4_quantize_append(k_cache, v_cache, k_scale, k_zero, v_scale, v_zero, k_new, v_new, slots, stream=None):
+    """Quantize into the int4 pool: packed codes [n_blocks][kv_bs][nkv][64]
+    uint8, scale / zero [n_blocks][kv_bs][nkv][2] float16."""
+    n_blocks, kv_bs, nkv, half = k_cache.shape
+    hd = 2 * half
+    if k_new.dtype not in _DTYPES or v_new.dtype != k_new.dtype:
+        raise ValueError("k_new / v_new must share one of float32, bfloat16, float16")
+    if tuple(k_new.shape[1:]) != (nkv, hd) or v_new.shape != k_new.shape or slots.shape != (k_new.shape[0],):
+        raise ValueError("k_new / v_new must be [n_tokens][nkv][hd], slots [n_tokens]")
+    for t, nm in ((k_scale, "k_scale"), (k_zero, "k_zero"), (v_scale, "v_scale"), (v_zero, "v_zero")):
+        if t.shape != (n_blocks, kv_bs, nkv, hd // 64):
+            raise ValueError(f"{nm} must be [n_blocks][kv_bs][nkv][{hd // 64}]")
+    st = lib().kvq4_quantize_append(
+        _ptr(k_cache, torch.uint8, "k_cache"), _ptr(v_cache, torch.uint8, "v_cache"),
+        _ptr(k_scale, torch.float16, "k_scale"), _ptr(k_zero, torch.float16, "k_zero"),
+        _ptr(v_scale, torch.float16, "v_scale"), _ptr(v_zero, torch.float16, "v_zero"),
+        n_blocks, kv_bs, nkv, hd, _ptr(k_new, name="k_new"), _ptr(v_new, name="v_new"), _DTYPES[k_new.dtype],
+        k_new.shape[0], _ptr(slots, torch.int32, "slots"), _stream(stream))
+    _check(st, "kvq4_quantize_append")
+
+
+def kvq4_decode_chunk_tokens(batch: int, nkv: int, max_len4: int, max_len8: int) -> int:
+    return lib().kvq4_decode_chunk_tokens(batch, nkv, max_len4, max_len8)
+
+
+def kvq4_decode_workspace_size(batch: int, nq: int, nkv: int, max_len4: int, max_len8: int, chunk: int = 0) -> int:
+    return lib().kvq4_decode_workspace_size(batch, nq, nkv, max_len4, max_len8, chunk)
+
+
+def kvq4_decode_attn(out, q, pool4, block_tables4, lens4, max_len4: int, pool8, block_tables8, lens8,
+                     max_len8: int, sm_scale: float | None = None, chunk: int = 0, workspace=None, stream=None):
+    """Decode attention over an int4 pool (k, v, k_scale, k_zero, v_scale,
+    v_zero) plus an int8 recent-window pool (k, v, k_scale, v_scale)."""
+    B, nq, hd = q.shape
+    k4, v4, k4s, k4z, v4s, v4z = pool4
+    k8, v8, k8s, v8s = pool8
+    n4, kv_bs, nkv, _ = k4.shape
+    n8 = k8.shape[0]
+    if k8.shape[1:] != (kv_bs, nkv, hd):
+        raise ValueError("int8 pool must share kv_bs and nkv with the int4 pool")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(hd)
+    need = kvq4_decode_workspace_size(B, nq, nkv, max_len4, max_len8, chunk)
+    if workspace is None:
+        workspace = alloc_workspace(need, q.device)
+    st = lib().kvq4_decode_attn(
+        _ptr(out, torch.float32, "out"), _ptr(q, torch.float32, "q"), B, nq,
+        _ptr(k4, torch.uint8, "k4"), _ptr(v4, torch.uint8, "v4"), _ptr(k4s, torch.float16, "k4_scale"),
+        _ptr(k4z, torch.float16, "k4_zero"), _ptr(v4s, torch.float16, "v4_scale"),
+        _ptr(v4z, torch.float16, "v4_zero"), n4, _ptr(block_tables4, torch.int32, "block_tables4"),
+        block_tables4.shape[1], _ptr(lens4, torch.int32, "lens4"), max_len4,
+        _ptr(k8, torch.int8, "k8"), _ptr(v8, torch.int8, "v8"), _ptr(k8s, torch.float32, "k8_scale"),
+        _ptr(v8s, torch.float32, "v8_scale"), n8, _ptr(block_tables8, torch.int32, "block_tables8"),
+        block_tables8.shape[1], _ptr(lens8, torch.int32, "lens8"), max_len8,
+        kv_bs, nkv, hd, float(sm_scale), chunk, _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+        _stream(stream))
+    _check(st, "kvq4_decode_attn")
+    return out

@@ -1,0 +1,251 @@
+/*
+ * kvq8.h -- C ABI of the int8 / int4 KV-cache decode-attention library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The library computes single-query (decode) attention over a paged KV cache
+ * whose keys and values are stored as int8 codes with one float32 step per
+ * (token, kv-head) row of 128 values, and fills that cache from float K/V
+ * (the write path).  An int4 group variant keeps older tokens as 4-bit codes.
+ *
+ * Sources, cited by short name:
+ *   [P1] "Day 9-3: q8 KV precision comparison" (jianying88.com news/32654):
+ *        Sec. 2 states the per-(token, head) max-abs/127 rule.
+ *   [P2] "0.8MB runs Qwen part 9-1: q8 KV halves cache and decode bandwidth"
+ *        (developer.aliyun.com article 1767759): Sec. 2 gives the allocation
+ *        (paged int8 blocks of kv_bs tokens, one float scale per token per
+ *        head) and the write path that quantizes each new token's heads.
+ *   [P3] "Day 9-2: flash_attn_single_q_q8_neon" (dtytms.com news/32657):
+ *        Sec. 2 gives the decode kernel's arguments and its three segments
+ *        (query quantized once in 32-blocks; integer block dot products
+ *        scaled afterwards, online softmax, int8 V times float weights;
+ *        one division at the end).
+ *   [P4] "UltraQuant 4-bit KV cache on AMD" (seekfood.cn news/2668800):
+ *        Sec. 3.2 group-64 asymmetric INT4 with scale and zero point,
+ *        Sec. 3.3 higher precision for recent tokens, Sec. 5.2 the scale
+ *        floor and zero-point range.
+ *
+ * Conventions common to every entry point
+ * ---------------------------------------
+ *  - Pointers marked (device) are HIP device pointers; (host) are host
+ *    pointers.  The caller owns every buffer.  The library keeps no global
+ *    state and allocates no memory.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *    stream) and the call returns without synchronizing.  Results are valid
+ *    once the stream has reached that point.
+ *  - Arguments are validated on the host before anything is launched; a
+ *    violation returns a negative status and launches nothing.  A failed
+ *    launch returns KVQ8_EHIP.
+ *  - Device-side index data (slots, block tables, context lengths) is
+ *    bounds-checked in the kernels: a slot or block id outside the pool is
+ *    skipped (the token is neither written nor read) and context lengths are
+ *    clamped to [0, min(max_ctx_len, max_blocks_per_seq * kv_bs)].
+ *  - hd (head dimension) must be 128.  kv_bs (tokens per cache block) must
+ *    be a power of two in [8, 1024].  nq must be a multiple of nkv and
+ *    nq / nkv in [1, 8]; query head h reads kv-head h / (nq / nkv).
+ *
+ * Cache layout (the pages' token-major paged layout, [P2] Sec. 2, [P3] Sec. 2)
+ * --------------------------------------------------------------------------
+ *  int8 codes   cache[n_blocks][kv_bs][nkv][128]
+ *  float steps  scale[n_blocks][kv_bs][nkv]
+ *  Token t of sequence b lives in block  block_tables[b][t / kv_bs],  row
+ *  t % kv_bs; its kv-head kh codes start at byte kh * 128 of that row.  A
+ *  "slot" is block_id * kv_bs + row; with an identity block table the step
+ *  array is the pages' [max_seq][nkv] array byte for byte.
+ */
+#ifndef KVQ8_H
+#define KVQ8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+enum kvq8_status {
+    KVQ8_OK = 0,
+    KVQ8_EINVAL = -1,     /* null pointer, negative count, unknown dtype */
+    KVQ8_ESHAPE = -2,     /* unsupported hd, kv_bs, head grouping or chunk */
+    KVQ8_EWORKSPACE = -3, /* workspace missing or smaller than required */
+    KVQ8_EHIP = -4        /* a HIP launch or runtime call failed */
+};
+
+/* Element types of float inputs to the write paths. */
+enum kvq8_dtype { KVQ8_F32 = 0, KVQ8_BF16 = 1, KVQ8_F16 = 2 };
+
+/* A static, NUL-terminated description of a status code. */
+const char* kvq8_status_string(int status);
+
+/* Library version, e.g. "kvq8 1.0 gfx950". */
+const char* kvq8_version(void);
+
+/*
+ * kvq8_quantize_append -- the write path ([P2] Sec. 2; rule of [P1] Sec. 2).
+ *
+ * For each new token i and kv-head kh, quantizes the 128-value K row and the
+ * 128-value V row independently: amax = max |x| (amax < 1e-6 is replaced by
+ * 1); step d = amax / 127 (IEEE float32 division); code = roundf(x / d)
+ * (IEEE division, ties away from zero) clamped to [-127, 127].  Codes go to
+ * the cache at slots[i], the step to scale[slots[i]][kh].  All arithmetic is
+ * float32; results are bit-exact across runs.
+ *
+ *   k_cache, v_cache  (device) int8 [n_blocks][kv_bs][nkv][hd], written
+ *   k_scale, v_scale  (device) float [n_blocks][kv_bs][nkv], written
+ *   k_new, v_new      (device) [n_tokens][nkv][hd] of `dtype` (KVQ8_F32,
+ *                     KVQ8_BF16 or KVQ8_F16), read; 16-byte aligned
+ *   slots             (device) int32 [n_tokens]: block_id * kv_bs + row;
+ *                     a slot outside [0, n_blocks * kv_bs) is skipped
+ *   n_tokens          may be 0 (nothing is launched)
+ * Tokens with equal slots race (one of them wins).
+ */
+int kvq8_quantize_append(int8_t* k_cache, int8_t* v_cache, float* k_scale, float* v_scale,
+                         int n_blocks, int kv_bs, int nkv, int hd,
+                         const void* k_new, const void* v_new, int dtype, int n_tokens,
+                         const int32_t* slots, void* stream);
+
+/*
+ * kvq8_decode_chunk_tokens -- the context chunk (tokens per split-K work
+ * item) that kvq8_decode_attn uses when called with chunk = 0.  A multiple
+ * of 256.  Pure host arithmetic.
+ */
+int kvq8_decode_chunk_tokens(int batch, int nkv, int max_ctx_len);
+
+/*
+ * kvq8_decode_workspace_size -- bytes of device workspace kvq8_decode_attn
+ * needs for these sizes (chunk = 0 selects the default chunk).  Returns 0
+ * for invalid sizes.  Pure host arithmetic.
+ */
+size_t kvq8_decode_workspace_size(int batch, int nq, int nkv, int max_ctx_len, int chunk);
+
+/*
+ * kvq8_decode_attn -- single-query decode attention over the int8 cache
+ * ([P3] Sec. 1-2, generalized to a batch of sequences, paged blocks and
+ * grouped query heads).
+ *
+ * For sequence b and query head h (kv-head kh = h / (nq / nkv)):
+ *   1. the query row is quantized once in four 32-value blocks: qm = max |q|
+ *      (qm < 1e-6 -> 1), block scale qsc = qm * (1/127), codes
+ *      roundf(q * (127 / qm)) clamped to [-128, 127]   ([P3] Sec. 2 seg. 1);
+ *   2. token t's score is sm_scale * kstep_t * sum_b qsc_b * dot_b with
+ *      dot_b the int32 dot product of block b's query and key codes
+ *      ([P3] Sec. 2 seg. 2);
+ *   3. out = sum_t softmax(score)_t * vstep_t * vcodes_t
+ *      ([P3] Sec. 2 seg. 2-3).
+ * The context is split into chunks processed in parallel, each keeping its
+ * own running max and sum (online softmax per chunk); a second kernel merges
+ * the chunks and divides by the total sum.  Accumulation is float32; the
+ * result matches the exact float64 value of the definition to about 1e-5
+ * relative.  A sequence with context length 0 gets a zero output row.
+ *
+ *   out               (device) float [batch][nq][hd], written
+ *   q                 (device) float [batch][nq][hd], read; 16-byte aligned
+ *   k_cache, v_cache  (device) int8 [n_blocks][kv_bs][nkv][hd], read
+ *   k_scale, v_scale  (device) float [n_blocks][kv_bs][nkv], read
+ *   block_tables      (device) int32 [batch][max_blocks_per_seq]
+ *   ctx_lens          (device) int32 [batch]
+ *   max_ctx_len       (host) an upper bound of ctx_lens; sizes the grid
+ *   sm_scale          score scale, normally 1 / sqrt(hd)
+ *   chunk             tokens per work item: 0 (default) or a multiple of
+ *                     256; must equal the value given to
+ *                     kvq8_decode_workspace_size
+ *   workspace         (device) at least kvq8_decode_workspace_size(...)
+ *                     bytes, 16-byte aligned; contents need no
+ *                     initialization and are overwritten
+ */
+int kvq8_decode_attn(float* out, const float* q, int batch, int nq,
+                     const int8_t* k_cache, const int8_t* v_cache,
+                     const float* k_scale, const float* v_scale,
+                     int n_blocks, int kv_bs, int nkv, int hd,
+                     const int32_t* block_tables, int max_blocks_per_seq,
+                     const int32_t* ctx_lens, int max_ctx_len, float sm_scale,
+                     int chunk, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kvq8_quantize_q -- step 1 of kvq8_decode_attn alone, exported so that the
+ * query codes and block scales can be checked bit for bit ([P3] Sec. 2
+ * seg. 1).  Runs the same device code the decode kernel runs.
+ *
+ *   qi    (device) int8 [n_vectors][hd], written
+ *   qsc   (device) float [n_vectors][hd / 32], written
+ *   q     (device) float [n_vectors][hd], read; 16-byte aligned
+ */
+int kvq8_quantize_q(int8_t* qi, float* qsc, const float* q, int n_vectors, int hd, void* stream);
+
+/*
+ * kvq8_qk_partials -- the int32 block dot products of step 2 for every
+ * (sequence, query head, token), exported for bit-exact checking
+ * ([P3] Sec. 2 seg. 2).  Runs the same tile loader and dot-product code the
+ * decode kernel runs.
+ *
+ *   partials  (device) int32 [batch][nq][max_ctx_len][4], written for
+ *             t < ctx_len (clamped as above); other entries are untouched
+ *   remaining arguments as for kvq8_decode_attn
+ */
+int kvq8_qk_partials(int32_t* partials, const float* q, int batch, int nq,
+                     const int8_t* k_cache, int n_blocks, int kv_bs, int nkv, int hd,
+                     const int32_t* block_tables, int max_blocks_per_seq,
+                     const int32_t* ctx_lens, int max_ctx_len, void* stream);
+
+/* ------------------------------------------------------------------------
+ * int4 group variant ([P4] Sec. 3.2, 3.3)
+ *
+ * int4 pool layout:
+ *   packed codes  cache4[n_blocks4][kv_bs][nkv][64] uint8, two codes per
+ *                 byte, even-indexed value in the high nibble
+ *   scale, zero   [n_blocks4][kv_bs][nkv][2] IEEE binary16 (as uint16 bits),
+ *                 one per 64-value group
+ * Recent tokens stay in an int8 pool laid out exactly as above.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * kvq4_quantize_append -- int4 write path ([P4] Sec. 3.2 with the
+ * Sec. 5.2 checklist).  Per 64-value group: scale = (max - min) / 15 in
+ * float32 (1.0 when max == min), floored at 1e-7 and rounded to binary16;
+ * with s the stored binary16 scale, zero = clamp(rint(-min / s), 0, 15)
+ * (stored as binary16, exact); code = clamp(rint(x / s + zero), 0, 15);
+ * rint is round-half-to-even.  Arguments as for kvq8_quantize_append.
+ */
+int kvq4_quantize_append(uint8_t* k_cache, uint8_t* v_cache,
+                         uint16_t* k_scale, uint16_t* k_zero, uint16_t* v_scale, uint16_t* v_zero,
+                         int n_blocks, int kv_bs, int nkv, int hd,
+                         const void* k_new, const void* v_new, int dtype, int n_tokens,
+                         const int32_t* slots, void* stream);
+
+/* Default chunk and workspace size for kvq4_decode_attn (see the kvq8
+ * counterparts).  max_len4 / max_len8 bound lens4 / lens8. */
+int kvq4_decode_chunk_tokens(int batch, int nkv, int max_len4, int max_len8);
+size_t kvq4_decode_workspace_size(int batch, int nq, int nkv, int max_len4, int max_len8, int chunk);
+
+/*
+ * kvq4_decode_attn -- decode attention over a sequence split between an
+ * int4 pool (older tokens; lens4[b] of them, positions 0.. through
+ * block_tables4) and an int8 pool (the recent window; lens8[b] tokens
+ * through block_tables8).  Attention does not depend on token order, so
+ * the split only sets each token's precision ([P4] Sec. 2.2, 3.3).
+ *
+ * The query is quantized as in kvq8_decode_attn.  For an int4 key row with
+ * codes c, group scale s_g and zero z_g, block b's score term is
+ * qsc_b * s_g * (P_b - z_g * R_b) with P_b = sum qi * c and R_b = sum qi
+ * (int32); values contribute weight * s_g * (c - z_g).  Both pools' chunks
+ * are merged as in kvq8_decode_attn.  Other arguments as there; the int4
+ * and int8 pools share kv_bs and nkv.
+ */
+int kvq4_decode_attn(float* out, const float* q, int batch, int nq,
+                     const uint8_t* k_cache4, const uint8_t* v_cache4,
+                     const uint16_t* k_scale4, const uint16_t* k_zero4,
+                     const uint16_t* v_scale4, const uint16_t* v_zero4,
+                     int n_blocks4, const int32_t* block_tables4, int max_blocks_per_seq4,
+                     const int32_t* lens4, int max_len4,
+                     const int8_t* k_cache8, const int8_t* v_cache8,
+                     const float* k_scale8, const float* v_scale8,
+                     int n_blocks8, const int32_t* block_tables8, int max_blocks_per_seq8,
+                     const int32_t* lens8, int max_len8,
+                     int kv_bs, int nkv, int hd, float sm_scale,
+                     int chunk, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ8_H */

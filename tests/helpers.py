@@ -1,0 +1,82 @@
+"""Shared pieces of the GPU parity tests: device copies of seeded inputs,
+oracle-side cache construction and the output tolerance of the float path."""
+from __future__ import annotations
+
+import numpy as np
+
+import workloads as W
+from oracle import kvq8 as O8
+
+SM = float(np.float32(1.0) / np.sqrt(np.float32(128.0)))
+ATOL = 1e-4
+RTOL = 1e-4
+
+
+def dev(x, device="cuda"):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device)
+
+
+def host(t):
+    return t.detach().cpu().numpy()
+
+
+def assert_attn_close(got, ref, what=""):
+    """|gpu - oracle| <= 1e-4 + 1e-4 |oracle| elementwise (float32
+    accumulation against the float64 definition)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    excess = np.abs(got - ref) - (ATOL + RTOL * np.abs(ref))
+    i = np.unravel_index(np.argmax(excess), excess.shape)
+    assert excess.max() <= 0, (f"{what}: |gpu-oracle| = {abs(got[i] - ref[i]):.3e} at {i} "
+                               f"(oracle {ref[i]:.6f}); max abs err {np.abs(got - ref).max():.3e}")
+    return float(np.abs(got - ref).max())
+
+
+class Q8Cache:
+    """An int8 paged cache held both on the host (oracle) and on the GPU."""
+
+    def __init__(self, n_blocks, kv_bs, nkv, device="cuda"):
+        import torch
+        self.kv_bs, self.nkv = kv_bs, nkv
+        shp = (n_blocks, kv_bs, nkv, 128)
+        self.kp = np.zeros(shp, np.int8)
+        self.vp = np.zeros(shp, np.int8)
+        self.ks = np.zeros(shp[:3], np.float32)
+        self.vs = np.zeros(shp[:3], np.float32)
+        self.gk = torch.zeros(shp, dtype=torch.int8, device=device)
+        self.gv = torch.zeros(shp, dtype=torch.int8, device=device)
+        self.gks = torch.zeros(shp[:3], dtype=torch.float32, device=device)
+        self.gvs = torch.zeros(shp[:3], dtype=torch.float32, device=device)
+
+    def append(self, k_new, v_new, slots, gk_new=None, gv_new=None):
+        """Write the same new rows through the oracle and through the GPU.
+        k_new / v_new are float32 host arrays (exact values of the device
+        inputs); gk_new / gv_new the device tensors (default: k_new as f32)."""
+        import decode_attention_int8_amd as K
+        O8.quantize_append(self.kp, self.vp, self.ks, self.vs, k_new, v_new, slots)
+        K.kvq8_quantize_append(self.gk, self.gv, self.gks, self.gvs,
+                               dev(k_new) if gk_new is None else gk_new,
+                               dev(v_new) if gv_new is None else gv_new, dev(np.asarray(slots, np.int32)))
+
+    def assert_device_matches_host(self):
+        assert np.array_equal(host(self.gk), self.kp), "K codes differ"
+        assert np.array_equal(host(self.gv), self.vp), "V codes differ"
+        assert np.array_equal(host(self.gks).view(np.uint32), self.ks.view(np.uint32)), "K steps differ"
+        assert np.array_equal(host(self.gvs).view(np.uint32), self.vs.view(np.uint32)), "V steps differ"
+
+    def pull(self):
+        """Adopt the device cache as the host cache (after a device-only fill)."""
+        self.kp, self.vp, self.ks, self.vs = host(self.gk), host(self.gv), host(self.gks), host(self.gvs)
+
+
+def fill_sequences(cache: Q8Cache, bt, lens, k, v):
+    """k, v float32 [B][Lmax][nkv][128]: append sequence b's first lens[b]
+    tokens at their paged slots."""
+    for b, L in enumerate(lens):
+        if L == 0:
+            continue
+        sl = W.slots_for_positions(bt, [b] * L, np.arange(L), cache.kv_bs)
+        cache.append(np.ascontiguousarray(k[b, :L]), np.ascontiguousarray(v[b, :L]), sl)

@@ -1,0 +1,115 @@
+"""The C ABI without a GPU: the library loads, exports every entry point the
+header declares, and its host-side validation and sizing behave as the
+header documents.  No call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from decode_attention_int8_amd import kvq8 as K
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq8.h")
+OK, EINVAL, ESHAPE, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(kvq[48]_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) == 12, names
+    lib = K.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in K._SIGNATURES, f"binding lacks {n}"
+
+
+def test_status_strings_and_version():
+    assert K.kvq8_status_string(OK) == "ok"
+    for st in (EINVAL, ESHAPE, EWORKSPACE, EHIP):
+        assert K.kvq8_status_string(st) not in ("ok", "unknown status")
+    assert K.kvq8_status_string(7) == "unknown status"
+    assert "gfx950" in K.kvq8_version()
+
+
+def _fake(addr=4096):
+    """An aligned non-null address; validation never dereferences it."""
+    return ctypes.c_void_p(addr)
+
+
+def _decode(**kw):
+    a = dict(out=_fake(), q=_fake(), batch=2, nq=16, kc=_fake(), vc=_fake(), ks=_fake(), vs=_fake(), n_blocks=64,
+             kv_bs=16, nkv=8, hd=128, bt=_fake(), mb=32, lens=_fake(), max_ctx=512, sm=0.088, chunk=0,
+             ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return K.lib().kvq8_decode_attn(*a.values())
+
+
+def test_decode_validation():
+    assert _decode(hd=64) == ESHAPE
+    assert _decode(nq=12, nkv=8) == ESHAPE            # not a multiple
+    assert _decode(nq=72, nkv=8) == ESHAPE            # group of 9
+    assert _decode(kv_bs=12) == ESHAPE
+    assert _decode(kv_bs=4) == ESHAPE
+    assert _decode(kv_bs=2048) == ESHAPE
+    assert _decode(chunk=100) == ESHAPE
+    assert _decode(max_ctx=-1) == EINVAL
+    assert _decode(q=None) == EINVAL
+    assert _decode(q=_fake(4100)) == EINVAL           # misaligned
+    assert _decode() == EWORKSPACE                    # missing workspace
+    need = K.kvq8_decode_workspace_size(2, 16, 8, 512, 0)
+    assert _decode(ws=_fake(), ws_bytes=need - 1) == EWORKSPACE
+    assert _decode(batch=0) == OK                     # nothing to do
+
+
+def test_write_validation():
+    lib = K.lib()
+    args = [_fake(), _fake(), _fake(), _fake(), 64, 16, 8, 128, _fake(), _fake(), K.F32, 10, _fake(), None]
+
+    def call(**kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return lib.kvq8_quantize_append(*a)
+    assert call(a7=96) == ESHAPE
+    assert call(a5=24) == ESHAPE
+    assert call(a10=5) == EINVAL
+    assert call(a11=-1) == EINVAL
+    assert call(a11=0) == OK
+    assert call(a12=None) == EINVAL
+    assert call(a8=_fake(4104)) == EINVAL
+    assert lib.kvq4_quantize_append(_fake(), _fake(), _fake(), _fake(), _fake(), _fake(), 64, 16, 8, 128,
+                                    _fake(), _fake(), K.BF16, 0, _fake(), None) == OK
+    assert lib.kvq4_quantize_append(_fake(), _fake(), _fake(), _fake(), _fake(), _fake(), 64, 16, 8, 100,
+                                    _fake(), _fake(), K.BF16, 3, _fake(), None) == ESHAPE
+
+
+def test_chunk_and_workspace_sizing():
+    # one-CU-per-chunk latency case: 8 kv-heads x 8K tokens
+    assert K.kvq8_decode_chunk_tokens(1, 8, 8192) == 256
+    # long batched contexts grow the chunk, capped at 8 tiles per wave
+    c = K.kvq8_decode_chunk_tokens(32, 8, 32768)
+    assert c % 256 == 0 and 256 < c <= 2048
+    for B, nq, nkv, L, ch in [(1, 16, 8, 8192, 0), (32, 32, 8, 32768, 0), (3, 8, 2, 1000, 512), (1, 1, 1, 0, 0)]:
+        chunk = ch or K.kvq8_decode_chunk_tokens(B, nkv, L)
+        n = B * nq * -(-L // chunk)
+        want = -(-n * 128 * 4 // 256) * 256 + 2 * (-(-n * 4 // 256) * 256)
+        assert K.kvq8_decode_workspace_size(B, nq, nkv, L, ch) == want
+    assert K.kvq8_decode_workspace_size(1, 16, 8, 100, 300) == 0        # bad chunk
+    n4 = K.kvq4_decode_workspace_size(4, 32, 4, 129024, 2048, 1024)
+    chunks = -(-129024 // 1024) + 2
+    assert n4 == -(-4 * 32 * chunks * 512 // 256) * 256 + 2 * (-(-4 * 32 * chunks * 4 // 256) * 256)
+
+
+def test_binding_requires_gpu_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros((4, 16, 2, 128), dtype=torch.int8)
+    s = torch.zeros((4, 16, 2), dtype=torch.float32)
+    kn = torch.zeros((3, 2, 128), dtype=torch.float32)
+    with pytest.raises(ValueError):
+        K.kvq8_quantize_append(x, x, s, s, kn, kn, torch.zeros(3, dtype=torch.int32))

@@ -1,0 +1,123 @@
+"""GPU parity of the int4 group variant against the CPU oracle: write path
+bit-exact (packed codes, binary16 scales and zero points), mixed int4 / int8
+decode within 1e-4 + 1e-4 |oracle|."""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import kvq4 as O4
+from oracle import kvq8 as O8
+from tests.helpers import SM, Q8Cache, assert_attn_close, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def K():
+    import decode_attention_int8_amd as K
+    return K
+
+
+class Q4Pool:
+    def __init__(self, nb, bs, nkv):
+        import torch
+        shp = (nb, bs, nkv)
+        self.bs = bs
+        self.h = [np.zeros(shp + (64,), np.uint8), np.zeros(shp + (64,), np.uint8)] + \
+                 [np.zeros(shp + (2,), np.float16) for _ in range(4)]
+        self.g = [torch.zeros(shp + (64,), dtype=torch.uint8, device="cuda"),
+                  torch.zeros(shp + (64,), dtype=torch.uint8, device="cuda")] + \
+                 [torch.zeros(shp + (2,), dtype=torch.float16, device="cuda") for _ in range(4)]
+
+    def append(self, K, k, v, slots, gk=None, gv=None):
+        h = self.h
+        O4.quantize_append_q4(h[0], h[1], h[2], h[3], h[4], h[5], k, v, slots)
+        K.kvq4_quantize_append(*self.g, dev(k) if gk is None else gk, dev(v) if gv is None else gv,
+                               dev(np.asarray(slots, np.int32)))
+
+    def oracle_pools(self):
+        h = self.h
+        return (h[0], h[2], h[3], h[1], h[4], h[5])
+
+    def assert_same(self):
+        for x, y in zip(self.g, self.h):
+            assert np.array_equal(host(x).view(np.uint8), y.view(np.uint8))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_q4_write_bit_exact(K, dtype):
+    import torch
+    r = W.rng(400, ["f32", "bf16", "f16"].index(dtype))
+    n, nkv, bs, nb = 333, 4, 16, 32
+    x = W.per_unit_sigma_normal(r, (n, nkv, 128), 2, 0.2, 5.0)
+    y = W.student_t3_f32(r, (n, nkv, 128), 0.5)
+    x[0, 0, :64] = 1.25                       # constant group -> scale 1
+    x[1, 1] = np.abs(x[1, 1]) + 3             # groups above zero: zero point clamps
+    x[2, 2] = -np.abs(x[2, 2]) - 3            # groups below zero
+    x[3, 3, :] = 1e-9                         # tiny spread: scale floor
+    x[3, 3, 5] = 2e-9
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dtype]
+    gx, gy = dev(x).to(tdt), dev(y).to(tdt)
+    slots = r.permutation(nb * bs)[:n].astype(np.int32)
+    slots[7] = -1
+    p = Q4Pool(nb, bs, nkv)
+    p.append(K, gx.float().cpu().numpy(), gy.float().cpu().numpy(), slots, gx, gy)
+    torch.cuda.synchronize()
+    p.assert_same()
+
+
+@pytest.mark.parametrize("g", [1, 4, 8])
+def test_q4_mixed_decode(K, g):
+    r = W.rng(410, g)
+    nkv, bs = 2, 16
+    nq = g * nkv
+    lens4 = np.array([0, 1, 300, 1500, 64], np.int32)
+    lens8 = np.array([5, 0, 64, 257, 0], np.int32)
+    B = len(lens4)
+    bt4, nb4 = W.paged_block_tables(r, lens4, bs, spare_blocks=1)
+    bt8, nb8 = W.paged_block_tables(r, lens8, bs, spare_blocks=1)
+    p4 = Q4Pool(nb4, bs, nkv)
+    c8 = Q8Cache(nb8, bs, nkv)
+    for b in range(B):
+        if lens4[b]:
+            k = W.per_unit_sigma_normal(r, (int(lens4[b]), nkv, 128), 0, 0.5, 2.0)
+            sl = W.slots_for_positions(bt4, [b] * lens4[b], np.arange(lens4[b]), bs)
+            p4.append(K, k, W.normal_f32(r, k.shape), sl)
+        if lens8[b]:
+            k = W.normal_f32(r, (int(lens8[b]), nkv, 128))
+            sl = W.slots_for_positions(bt8, [b] * lens8[b], np.arange(lens8[b]), bs)
+            c8.append(k, W.normal_f32(r, k.shape), sl)
+    import torch
+    q = W.normal_f32(r, (B, nq, 128), 2.0)
+    out = torch.full((B, nq, 128), float("nan"), dtype=torch.float32, device="cuda")
+    K.kvq4_decode_attn(out, dev(q), p4.g, dev(bt4), dev(lens4), int(lens4.max()),
+                       (c8.gk, c8.gv, c8.gks, c8.gvs), dev(bt8), dev(lens8), int(lens8.max()), SM)
+    torch.cuda.synchronize()
+    p4.assert_same()
+    ref = O4.decode_attention_mixed(q, p4.oracle_pools(), bt4, lens4, (c8.kp, c8.ks, c8.vp, c8.vs), bt8, lens8,
+                                    bs, SM)
+    assert_attn_close(host(out), ref, f"int4 mixed g={g}")
+
+
+def test_q4_only_int8_window_equals_int8_path(K):
+    import torch
+    r = W.rng(420)
+    nq, nkv, bs = 8, 2, 16
+    lens = np.array([700, 33], np.int32)
+    bt, nb = W.paged_block_tables(r, lens, bs)
+    c8 = Q8Cache(nb, bs, nkv)
+    for b in range(2):
+        k = W.normal_f32(r, (int(lens[b]), nkv, 128))
+        c8.append(k, k * np.float32(0.5), W.slots_for_positions(bt, [b] * lens[b], np.arange(lens[b]), bs))
+    p4 = Q4Pool(4, bs, nkv)
+    q = W.normal_f32(r, (2, nq, 128))
+    o4 = torch.empty((2, nq, 128), dtype=torch.float32, device="cuda")
+    o8 = torch.empty_like(o4)
+    zero = np.zeros(2, np.int32)
+    K.kvq4_decode_attn(o4, dev(q), p4.g, dev(np.zeros((2, 1), np.int32)), dev(zero), 0,
+                       (c8.gk, c8.gv, c8.gks, c8.gvs), dev(bt), dev(lens), 700, SM)
+    K.kvq8_decode_attn(o8, dev(q), c8.gk, c8.gv, c8.gks, c8.gvs, dev(bt), dev(lens), 700, SM)
+    torch.cuda.synchronize()
+    ref = O8.decode_attention_q8(q, c8.kp, c8.ks, c8.vp, c8.vs, bt, lens, bs, SM)
+    assert_attn_close(host(o4), ref, "int4 entry, int8 only")
+    assert_attn_close(host(o8), ref, "int8 entry")

@@ -1,0 +1,241 @@
+"""GPU parity of the int8 path against the CPU oracle, through the C ABI.
+
+Bit-exact: K/V codes and steps of the write path, query codes and block
+scales, int32 block partials.  Float outputs: |gpu - oracle| <= 1e-4 +
+1e-4 |oracle| elementwise.  Sizes span several tiles and chunks with ragged
+tails; the full-size workloads are in test_gpu_workloads.py.
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import kvq8 as O8
+from tests.helpers import SM, Q8Cache, assert_attn_close, dev, fill_sequences, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _torch():
+    import torch
+    return torch
+
+
+@pytest.fixture(scope="module")
+def K():
+    import decode_attention_int8_amd as K
+    return K
+
+
+# ----------------------------------------------------------------------------
+# write path
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_quantize_append_bit_exact(K, dtype):
+    torch = _torch()
+    r = W.rng(300, ["f32", "bf16", "f16"].index(dtype))
+    n, nkv, bs, nb = 777, 4, 16, 64
+    x = np.concatenate([W.normal_f32(r, (n // 2, nkv, 128)),
+                        W.student_t3_f32(r, (n - n // 2, nkv, 128), 0.5)]).astype(np.float32)
+    y = W.outlier_normal_bf16(r, (n, nkv, 128))
+    x[3, 1] = 0.0                                   # guarded zero row
+    x[5, 0, :] = 2.5                                # equal row
+    x[6, 2, :3] = [127.0, 0.5, -0.5]                # ties
+    x[6, 2, 3:] = 0.0
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dtype]
+    gx, gy = dev(x).to(tdt), dev(y).to(tdt)
+    xh = gx.float().cpu().numpy()                   # exact values the kernel sees
+    yh = gy.float().cpu().numpy()
+    slots = r.permutation(nb * bs)[:n].astype(np.int32)
+    slots[10] = -1                                  # padding token: skipped
+    slots[11] = nb * bs + 5                         # out of the pool: skipped
+    c = Q8Cache(nb, bs, nkv)
+    c.append(xh, yh, slots, gx, gy)
+    torch.cuda.synchronize()
+    c.assert_device_matches_host()
+
+
+def test_quantize_append_overwrite_and_empty(K):
+    torch = _torch()
+    r = W.rng(301)
+    c = Q8Cache(8, 16, 2)
+    a = W.normal_f32(r, (5, 2, 128))
+    c.append(a, a, np.array([0, 1, 2, 3, 4], np.int32))
+    b = W.normal_f32(r, (2, 2, 128), 7.0)
+    c.append(b, b, np.array([4, 2], np.int32))        # rewrite two slots
+    K.kvq8_quantize_append(c.gk, c.gv, c.gks, c.gvs, dev(b[:0]), dev(b[:0]), dev(np.zeros(0, np.int32)))
+    torch.cuda.synchronize()
+    c.assert_device_matches_host()
+
+
+# ----------------------------------------------------------------------------
+# query quantization and integer partials (debug exports of the decode code)
+# ----------------------------------------------------------------------------
+
+def test_quantize_q_bit_exact(K):
+    torch = _torch()
+    r = W.rng(310)
+    q = np.concatenate([W.normal_f32(r, (200, 128)), W.normal_f32(r, (50, 128), 300.0),
+                        W.normal_f32(r, (50, 128), 1e-4)])
+    q[0, 32:64] = 0.0
+    q[1, :] = 0.0
+    q[2, :32] = np.linspace(-1, 1, 32, dtype=np.float32)
+    gq = dev(q)
+    qi = torch.empty((len(q), 128), dtype=torch.int8, device="cuda")
+    qs = torch.empty((len(q), 4), dtype=torch.float32, device="cuda")
+    K.kvq8_quantize_q(qi, qs, gq)
+    want_i, want_s = O8.quantize_q_blocks(q)
+    assert np.array_equal(host(qi), want_i)
+    assert np.array_equal(host(qs).view(np.uint32), want_s.view(np.uint32))
+
+
+@pytest.mark.parametrize("nq,nkv,bs", [(1, 1, 16), (8, 2, 8), (12, 4, 64), (16, 2, 16)])
+def test_qk_partials_bit_exact(K, nq, nkv, bs):
+    torch = _torch()
+    r = W.rng(320, nq, nkv, bs)
+    lens = np.array([1, 70, 200, 0, 129], np.int32)
+    B, Lm = len(lens), int(lens.max())
+    bt, nb = W.paged_block_tables(r, lens, bs, spare_blocks=3)
+    k = W.normal_f32(r, (B, Lm, nkv, 128))
+    c = Q8Cache(nb, bs, nkv)
+    fill_sequences(c, bt, lens, k, k)
+    q = W.normal_f32(r, (B, nq, 128))
+    part = torch.full((B, nq, Lm, 4), -7, dtype=torch.int32, device="cuda")
+    K.kvq8_qk_partials(part, dev(q), c.gk, dev(bt), dev(lens), Lm)
+    got = host(part)
+    qi, _ = O8.quantize_q_blocks(q)
+    g = nq // nkv
+    for b in range(B):
+        for h in range(nq):
+            rows = O8.gather_rows(c.kp, bt[b], lens[b], bs, h // g)
+            want = O8.qk_block_partials(qi[b, h], rows)
+            assert np.array_equal(got[b, h, :lens[b]], want), (b, h)
+            assert np.all(got[b, h, lens[b]:] == -7)
+
+
+# ----------------------------------------------------------------------------
+# decode attention
+# ----------------------------------------------------------------------------
+
+def _decode(K, c, q, bt, lens, max_ctx, chunk=0):
+    torch = _torch()
+    out = torch.full(q.shape, float("nan"), dtype=torch.float32, device="cuda")
+    K.kvq8_decode_attn(out, dev(q), c.gk, c.gv, c.gks, c.gvs, dev(bt), dev(lens), max_ctx, SM, chunk=chunk)
+    torch.cuda.synchronize()
+    return host(out)
+
+
+def test_unit_experiment_shape(K):
+    # the pages' unit experiment: 1 head, L = 256, N(0, 1) K/V and query
+    for seed in range(3):
+        q, k, v = W.unit_experiment(seed)
+        bt, nb = W.paged_block_tables(None, [256], 16)
+        c = Q8Cache(nb, 16, 1)
+        fill_sequences(c, bt, [256], k[None, :, None], v[None, :, None])
+        got = _decode(K, c, q[None, None], bt, np.array([256], np.int32), 256)
+        ref = O8.decode_attention_q8(q[None, None], c.kp, c.ks, c.vp, c.vs, bt, [256], 16, SM)
+        assert_attn_close(got, ref, f"unit seed {seed}")
+
+
+@pytest.mark.parametrize("g", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("bs", [8, 16, 128])
+def test_decode_ragged_batch(K, g, bs):
+    r = W.rng(330, g, bs)
+    nkv = 2 if g < 8 else 1
+    nq = g * nkv
+    lens = np.array([1, 63, 64, 65, 300, 1025, 0, 2049], np.int32)
+    B, Lm = len(lens), int(lens.max())
+    bt, nb = W.paged_block_tables(r, lens, bs, spare_blocks=2)
+    k = W.normal_f32(r, (B, Lm, nkv, 128))
+    v = W.student_t3_f32(r, (B, Lm, nkv, 128), 0.5)
+    c = Q8Cache(nb, bs, nkv)
+    fill_sequences(c, bt, lens, k, v)
+    q = W.normal_f32(r, (B, nq, 128), 2.0)
+    got = _decode(K, c, q, bt, lens, Lm)
+    ref = O8.decode_attention_q8(q, c.kp, c.ks, c.vp, c.vs, bt, lens, bs, SM)
+    assert_attn_close(got, ref, f"g={g} bs={bs}")
+    assert np.all(got[6] == 0.0)                          # empty context
+
+
+@pytest.mark.parametrize("chunk", [256, 512, 2048, 16384])
+def test_decode_chunk_sizes_agree(K, chunk):
+    r = W.rng(331, chunk)
+    nq, nkv, bs = 8, 2, 16
+    lens = np.array([5000, 257, 4096], np.int32)
+    B, Lm = len(lens), int(lens.max())
+    bt, nb = W.paged_block_tables(r, lens, bs)
+    k = W.normal_f32(r, (B, Lm, nkv, 128))
+    v = W.normal_f32(r, (B, Lm, nkv, 128))
+    c = Q8Cache(nb, bs, nkv)
+    fill_sequences(c, bt, lens, k, v)
+    q = W.normal_f32(r, (B, nq, 128), 3.0)
+    got = _decode(K, c, q, bt, lens, Lm, chunk=chunk)
+    ref = O8.decode_attention_q8(q, c.kp, c.ks, c.vp, c.vs, bt, lens, bs, SM)
+    assert_attn_close(got, ref, f"chunk {chunk}")
+
+
+def test_decode_single_token_and_peaked_softmax(K):
+    r = W.rng(332)
+    nq, nkv, bs = 4, 1, 16
+    lens = np.array([1, 500], np.int32)
+    bt, nb = W.paged_block_tables(r, lens, bs)
+    k = W.normal_f32(r, (2, 500, nkv, 128))
+    v = W.normal_f32(r, (2, 500, nkv, 128))
+    c = Q8Cache(nb, bs, nkv)
+    fill_sequences(c, bt, lens, k, v)
+    q = W.normal_f32(r, (2, nq, 128))
+    q[1, 0] = k[1, 321, 0] * 30.0                   # one dominant token
+    got = _decode(K, c, q, bt, lens, 500)
+    ref = O8.decode_attention_q8(q, c.kp, c.ks, c.vp, c.vs, bt, lens, bs, SM)
+    assert_attn_close(got, ref, "single / peaked")
+    # L = 1: exactly the dequantized value row (weight 1)
+    np.testing.assert_allclose(got[0], np.repeat(c.vp[bt[0, 0], 0, 0][None].astype(np.float64) * c.vs[bt[0, 0], 0, 0],
+                                                 nq, 0), rtol=1e-6, atol=1e-7)
+
+
+def test_decode_clamps_lengths_and_skips_bad_blocks(K):
+    r = W.rng(333)
+    nq, nkv, bs = 4, 2, 16
+    lens = np.array([100, 100, 100], np.int32)
+    bt, nb = W.paged_block_tables(r, lens, bs)
+    k = W.normal_f32(r, (3, 100, nkv, 128))
+    c = Q8Cache(nb, bs, nkv)
+    fill_sequences(c, bt, lens, k, k)
+    q = W.normal_f32(r, (3, nq, 128))
+    glens = np.array([100, 100 + 1000, -5], np.int32)      # beyond max_ctx / negative
+    bt_bad = bt.copy()
+    bt_bad[0, 2] = nb + 100                               # block id outside the pool
+    got = _decode(K, c, q, bt_bad, glens, 100)
+    keep = np.r_[0:32, 48:100]                            # tokens of block index 2 are skipped
+    ref0 = np.stack([O8.softmax_attention_f64(
+        O8.dequantize_q_blocks(*O8.quantize_q_blocks(q[0, h][None]))[0],
+        O8.dequantize_rows_q8(O8.gather_rows(c.kp, bt[0], 100, bs, h // 2), O8.gather_rows(c.ks, bt[0], 100, bs, h // 2))[keep],
+        O8.dequantize_rows_q8(O8.gather_rows(c.vp, bt[0], 100, bs, h // 2), O8.gather_rows(c.vs, bt[0], 100, bs, h // 2))[keep],
+        SM) for h in range(nq)])
+    assert_attn_close(got[0], ref0, "bad block skipped")
+    ref1 = O8.decode_attention_q8(q[1:2], c.kp, c.ks, c.vp, c.vs, bt[1:2], [100], bs, SM)
+    assert_attn_close(got[1:2], ref1, "length clamped to max_ctx")
+    assert np.all(got[2] == 0.0)
+
+
+def test_decode_repeatable_and_stream_ordered(K):
+    torch = _torch()
+    r = W.rng(334)
+    nq, nkv, bs = 8, 4, 16
+    lens = np.array([3000, 1500], np.int32)
+    bt, nb = W.paged_block_tables(r, lens, bs)
+    k = W.normal_f32(r, (2, 3000, nkv, 128))
+    c = Q8Cache(nb, bs, nkv)
+    fill_sequences(c, bt, lens, k, k)
+    q = W.normal_f32(r, (2, nq, 128))
+    s = torch.cuda.Stream()
+    outs = []
+    with torch.cuda.stream(s):
+        gq, gbt, gl = dev(q), dev(bt), dev(lens)
+        for _ in range(3):
+            o = torch.empty((2, nq, 128), dtype=torch.float32, device="cuda")
+            K.kvq8_decode_attn(o, gq, c.gk, c.gv, c.gks, c.gvs, gbt, gl, 3000, SM)
+            outs.append(o)
+    s.synchronize()
+    a = [host(o) for o in outs]
+    assert np.array_equal(a[0], a[1]) and np.array_equal(a[1], a[2])

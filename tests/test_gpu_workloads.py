@@ -1,0 +1,173 @@
+"""GPU parity at the full sizes of the five workloads, with the default
+launch configuration (the one the benchmark times).
+
+  unit      1 / 1 heads, L = 256, N(0, 1)                     (test_gpu_kvq8)
+  qwen2b    28 layers x 16 / 8 heads, L = 8192, batch 1        layers 0 and 27
+  qwen8b    36 layers x 32 / 8 heads, batch 32, L in [1K, 32K],
+            K/V 0.5 * Student-t(3)                             layer 0, all 32 sequences
+  append64k 65536 bf16 tokens (1% outliers x20) x 8 heads, then
+            one GQA-4 decode over the 65536 tokens             everything
+  q4_128k   int4 groups + int8 window, 32 / 4 heads, batch 4,
+            L = 131072                                         sequences 0 and 3
+
+Write-path codes and steps are compared bit for bit with the oracle's own
+quantization of the same generated inputs; the decode reference is the
+oracle run on the oracle's codes.
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import kvq4 as O4
+from oracle import kvq8 as O8
+from tests.helpers import SM, assert_attn_close, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def K():
+    import decode_attention_int8_amd as K
+    return K
+
+
+def _q8_pools(torch, nb, bs, nkv):
+    shp = (nb, bs, nkv, 128)
+    return (torch.zeros(shp, dtype=torch.int8, device="cuda"), torch.zeros(shp, dtype=torch.int8, device="cuda"),
+            torch.zeros(shp[:3], dtype=torch.float32, device="cuda"),
+            torch.zeros(shp[:3], dtype=torch.float32, device="cuda"))
+
+
+def _host_pools(nb, bs, nkv):
+    shp = (nb, bs, nkv, 128)
+    return [np.zeros(shp, np.int8), np.zeros(shp, np.int8), np.zeros(shp[:3], np.float32),
+            np.zeros(shp[:3], np.float32)]
+
+
+def _same(a, b):
+    return np.array_equal(a.view(np.uint8) if a.dtype != np.int8 else a, b.view(np.uint8) if b.dtype != np.int8 else b)
+
+
+@pytest.mark.parametrize("layer", [0, 27])
+def test_qwen2b_8k_layer(K, layer):
+    import torch
+    cfg = W.QWEN2B_8K
+    L, nq, nkv, bs = cfg["L"], cfg["nq"], cfg["nkv"], cfg["kv_bs"]
+    bt, nb = W.paged_block_tables(W.rng(2, layer, 3), [L], bs)
+    k = W.torch_normal((L, nkv, 128), "cuda", (2, layer, 0))
+    v = W.torch_normal((L, nkv, 128), "cuda", (2, layer, 1))
+    q = W.torch_normal((1, nq, 128), "cuda", (2, layer, 2))
+    slots = W.slots_for_positions(bt, [0] * L, np.arange(L), bs)
+    gk, gv, gks, gvs = _q8_pools(torch, nb, bs, nkv)
+    K.kvq8_quantize_append(gk, gv, gks, gvs, k, v, dev(slots))
+    out = torch.empty((1, nq, 128), dtype=torch.float32, device="cuda")
+    K.kvq8_decode_attn(out, q, gk, gv, gks, gvs, dev(bt), dev(np.array([L], np.int32)), L, SM)
+    torch.cuda.synchronize()
+    hk, hv, hks, hvs = _host_pools(nb, bs, nkv)
+    O8.quantize_append(hk, hv, hks, hvs, host(k), host(v), slots)
+    assert _same(host(gk), hk) and _same(host(gv), hv)
+    assert _same(host(gks), hks) and _same(host(gvs), hvs)
+    ref = O8.decode_attention_q8(host(q), hk, hks, hv, hvs, bt, [L], bs, SM)
+    assert_attn_close(host(out), ref, f"qwen2b layer {layer}")
+
+
+def test_qwen8b_batch32_layer0(K):
+    import torch
+    cfg = W.QWEN8B_B32
+    nq, nkv, bs, B = cfg["nq"], cfg["nkv"], cfg["kv_bs"], cfg["batch"]
+    lens = W.qwen8b_lengths(0)
+    bt, nb = W.paged_block_tables(W.rng(3, 0, 1), lens, bs)
+    gk, gv, gks, gvs = _q8_pools(torch, nb, bs, nkv)
+    hk, hv, hks, hvs = _host_pools(nb, bs, nkv)
+    for b in range(B):
+        Lb = int(lens[b])
+        k = W.torch_student_t3((Lb, nkv, 128), "cuda", (3, 0, b, 0), 0.5)
+        v = W.torch_student_t3((Lb, nkv, 128), "cuda", (3, 0, b, 1), 0.5)
+        slots = W.slots_for_positions(bt, [b] * Lb, np.arange(Lb), bs)
+        K.kvq8_quantize_append(gk, gv, gks, gvs, k, v, dev(slots))
+        O8.quantize_append(hk, hv, hks, hvs, host(k), host(v), slots)
+        del k, v
+    q = W.torch_normal((B, nq, 128), "cuda", (3, 0, 99))
+    out = torch.empty((B, nq, 128), dtype=torch.float32, device="cuda")
+    K.kvq8_decode_attn(out, q, gk, gv, gks, gvs, dev(bt), dev(lens), int(lens.max()), SM)
+    torch.cuda.synchronize()
+    assert _same(host(gk), hk) and _same(host(gv), hv)
+    assert _same(host(gks), hks) and _same(host(gvs), hvs)
+    ref = O8.decode_attention_q8(host(q), hk, hks, hv, hvs, bt, lens, bs, SM)
+    assert_attn_close(host(out), ref, "qwen8b batch 32")
+
+
+def test_append64k_then_decode(K):
+    import torch
+    cfg = W.APPEND_64K
+    n, nq, nkv, bs = cfg["n_tok"], cfg["nq"], cfg["nkv"], cfg["kv_bs"]
+    bt, nb = W.paged_block_tables(W.rng(4, 0, 2), [n], bs)
+    k = W.torch_outlier_normal_bf16((n, nkv, 128), "cuda", (4, 0, 0))
+    v = W.torch_outlier_normal_bf16((n, nkv, 128), "cuda", (4, 0, 1))
+    slots = W.slots_for_positions(bt, [0] * n, np.arange(n), bs)
+    gk, gv, gks, gvs = _q8_pools(torch, nb, bs, nkv)
+    K.kvq8_quantize_append(gk, gv, gks, gvs, k, v, dev(slots))
+    q = W.torch_normal((1, nq, 128), "cuda", (4, 0, 3))
+    out = torch.empty((1, nq, 128), dtype=torch.float32, device="cuda")
+    K.kvq8_decode_attn(out, q, gk, gv, gks, gvs, dev(bt), dev(np.array([n], np.int32)), n, SM)
+    torch.cuda.synchronize()
+    hk, hv, hks, hvs = _host_pools(nb, bs, nkv)
+    O8.quantize_append(hk, hv, hks, hvs, host(k.float()), host(v.float()), slots)
+    assert _same(host(gk), hk) and _same(host(gv), hv)
+    assert _same(host(gks), hks) and _same(host(gvs), hvs)
+    ref = O8.decode_attention_q8(host(q), hk, hks, hv, hvs, bt, [n], bs, SM)
+    assert_attn_close(host(out), ref, "append64k decode")
+
+
+def test_q4_128k(K):
+    import torch
+    cfg = W.Q4_128K
+    B, nq, nkv, L, win, bs = cfg["batch"], cfg["nq"], cfg["nkv"], cfg["L"], cfg["window"], cfg["kv_bs"]
+    n4, n8 = L - win, win
+    bt4, nb4 = W.paged_block_tables(W.rng(5, 0, 1), [n4] * B, bs)
+    bt8, nb8 = W.paged_block_tables(W.rng(5, 0, 2), [n8] * B, bs)
+    shp4 = (nb4, bs, nkv)
+    g4 = [torch.zeros(shp4 + (64,), dtype=torch.uint8, device="cuda"),
+          torch.zeros(shp4 + (64,), dtype=torch.uint8, device="cuda")] + \
+         [torch.zeros(shp4 + (2,), dtype=torch.float16, device="cuda") for _ in range(4)]
+    g8 = _q8_pools(torch, nb8, bs, nkv)
+    sig = W.rng(5, 0, 3).uniform(0.2, 5.0, size=(B, nkv, 2))
+    checked = (0, 3)
+    host_cache = {}
+    for b in range(B):
+        sk = torch.tensor(sig[b, :, 0], dtype=torch.float32, device="cuda")[None, :, None]
+        sv = torch.tensor(sig[b, :, 1], dtype=torch.float32, device="cuda")[None, :, None]
+        k = W.torch_normal((L, nkv, 128), "cuda", (5, 0, b, 0)) * sk
+        v = W.torch_normal((L, nkv, 128), "cuda", (5, 0, b, 1)) * sv
+        s4 = W.slots_for_positions(bt4, [b] * n4, np.arange(n4), bs)
+        s8 = W.slots_for_positions(bt8, [b] * n8, np.arange(n8), bs)
+        K.kvq4_quantize_append(g4[0], g4[1], g4[2], g4[3], g4[4], g4[5], k[:n4], v[:n4], dev(s4))
+        K.kvq8_quantize_append(g8[0], g8[1], g8[2], g8[3], k[n4:], v[n4:], dev(s8))
+        if b in checked:
+            host_cache[b] = (host(k), host(v), s4, s8)
+        del k, v
+    q = W.torch_normal((B, nq, 128), "cuda", (5, 0, 99))
+    out = torch.empty((B, nq, 128), dtype=torch.float32, device="cuda")
+    K.kvq4_decode_attn(out, q, g4, dev(bt4), dev(np.full(B, n4, np.int32)), n4, g8, dev(bt8),
+                       dev(np.full(B, n8, np.int32)), n8, SM)
+    torch.cuda.synchronize()
+    got = host(out)
+    gh4 = [host(x) for x in g4]
+    gh8 = [host(x) for x in g8]
+    for b in checked:
+        k, v, s4, s8 = host_cache[b]
+        p4 = [np.zeros(shp4 + (64,), np.uint8), np.zeros(shp4 + (64,), np.uint8)] + \
+             [np.zeros(shp4 + (2,), np.float16) for _ in range(4)]
+        O4.quantize_append_q4(p4[0], p4[1], p4[2], p4[3], p4[4], p4[5], k[:n4], v[:n4], s4)
+        p8 = _host_pools(nb8, bs, nkv)
+        O8.quantize_append(p8[0], p8[1], p8[2], p8[3], k[n4:], v[n4:], s8)
+        rows4 = bt4[b][bt4[b] >= 0]
+        rows8 = bt8[b][bt8[b] >= 0]
+        for x, y in zip(gh4, p4):
+            assert _same(x[rows4], y[rows4]), f"int4 pool differs (seq {b})"
+        for x, y in zip(gh8, p8):
+            assert _same(x[rows8], y[rows8]), f"int8 window differs (seq {b})"
+        ref = O4.decode_attention_mixed(host(q)[b:b + 1], (p4[0], p4[2], p4[3], p4[1], p4[4], p4[5]),
+                                        bt4[b:b + 1], [n4], (p8[0], p8[2], p8[1], p8[3]), bt8[b:b + 1], [n8],
+                                        bs, SM)
+        assert_attn_close(got[b:b + 1], ref, f"q4_128k seq {b}")
