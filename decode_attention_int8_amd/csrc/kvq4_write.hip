@@ -59,7 +59,8 @@ __device__ __forceinline__ void quantize_group8x8(const float (&x)[8], uint32_t&
     s32 = fmaxf(s32, 1e-7f);
     s16 = f16_bits_rne(s32);
     const float s = half_bits_f(s16);
-    const float z = fminf(fmaxf(rintf(-mn / s), 0.0f), 15.0f);
+    // integer zero point in [0, 15]; + 0.0f stores a zero as +0.0
+    const float z = fminf(fmaxf(rintf(-mn / s), 0.0f), 15.0f) + 0.0f;
     z16 = f16_bits_rne(z);
     uint32_t w = 0;
 #pragma unroll

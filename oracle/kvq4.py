@@ -42,7 +42,8 @@ def quantize_groups_q4(x):
         float16 for storage, and the stored float16 value is the one used to
         compute zero and codes, so stored and used scales agree;
       * zero is clamped to [0, 15] ([P4] Sec. 5.2 says it must lie there) and
-        stored as float16, where every such integer is exact.
+        stored as float16, where every such integer is exact; a zero point
+        of 0 is stored as +0.0.
 
     x float32 [..., 128].  Returns (codes uint8 [..., 128] in [0, 15],
     scale float16 [..., 2], zero float16 [..., 2])."""
@@ -56,7 +57,9 @@ def quantize_groups_q4(x):
     s32 = np.maximum(s32, F32(1e-7)).astype(np.float32)
     s16 = s32.astype(F16)
     s = s16.astype(np.float32)
-    z = np.clip(np.rint((-mn / s).astype(np.float32)), 0, 15).astype(np.float32)
+    # the zero point is an integer in [0, 15]; adding +0 stores a zero as +0.0
+    # (rint of a small negative quotient is -0.0, the same integer)
+    z = (np.clip(np.rint((-mn / s).astype(np.float32)), 0, 15) + F32(0.0)).astype(np.float32)
     y = ((g / s[..., None]).astype(np.float32) + z[..., None]).astype(np.float32)
     c = np.clip(np.rint(y), 0, 15).astype(np.uint8)
     return c.reshape(x.shape), s16, z.astype(F16)

@@ -20,7 +20,7 @@ def _brute_group(vals):
     s32 = Fraction(1) if mx == mn else f32(f32(mx - mn) / 15)
     s32 = max(s32, f32(Fraction(1, 10 ** 7)))
     s = f16(s32)
-    z = min(15, max(0, round_half_even(f32(-mn / s))))
+    z = min(15, max(0, round_half_even(f32(-mn / s)))) + 0   # integer: no signed zero
     codes = [min(15, max(0, round_half_even(f32(f32(x / s) + z)))) for x in xs]
     return codes, s, z
 
@@ -69,6 +69,16 @@ def test_constant_groups_use_unit_scale():
     xr = kvq4.dequantize_groups_q4(c, s, z)
     np.testing.assert_array_equal(xr[:2], x[:2].astype(np.float64))
     assert np.all(xr[2] == 0.0)
+
+
+def test_zero_point_zero_is_positive_zero():
+    # a group whose minimum is slightly above zero has zero point 0; its
+    # binary16 bits are those of +0.0 (the integer 0 has one encoding here)
+    x = np.full((1, 128), 1e-9, np.float32)
+    x[0, 5] = 2e-9
+    x[0, 64:] = np.linspace(0.001, 1.0, 64, dtype=np.float32)
+    _, _, z = kvq4.quantize_groups_q4(x)
+    assert z.view(np.uint16).tolist() == [[0, 0]]
 
 
 def test_pack_high_nibble_first_and_round_trip():
