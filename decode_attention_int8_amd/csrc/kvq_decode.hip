@@ -26,17 +26,15 @@ __global__ __launch_bounds__(kWave) void kvq8_qk_partials_kernel(DecodeArgs a, i
 #pragma unroll
     for (int h = 0; h < G; ++h)
         quantize_q_segment(a.q + ((size_t)b * a.nq + (size_t)kh * G + h) * kHD, j, qc[h], qs[h]);
-    uint4 kr[8], vr[8];
-    float ksr[8], vsr[8];
-    bool valid[8];
-    load_tile_q8<false>(a, a.r8.bt + (size_t)b * a.r8.max_blocks, L, kh, tile_base, tg, j, kr, vr, ksr, vsr, valid);
+    TileQ8 T;
+    issue_tile_q8<false>(a, a.r8.bt + (size_t)b * a.r8.max_blocks, L, kh, tile_base, tg, j, T);
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
         const int t = tile_base + 8 * r + tg;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            const int d = block_dot(qc[h], kr[r]);
-            if (valid[r] && (j & 1) == 0)
+            const int d = block_dot(qc[h], T.k[r]);
+            if (T.valid[r] && (j & 1) == 0)
                 partials[(((size_t)b * a.nq + (size_t)kh * G + h) * a.r8.max_len + t) * 4 + (j >> 1)] = d;
         }
     }

@@ -78,10 +78,36 @@ __device__ __forceinline__ int effective_len(const Region& r, int b, int log2_bs
     return L < 0 ? 0 : (int)L;
 }
 
-// Block id holding tokens t0 .. t0+7 (t0 a multiple of 8), or -1.
-__device__ __forceinline__ int row_block(const Region& r, const int32_t* btb, int t0, int L, int log2_bs) {
-    const int blk = (t0 < L) ? btb[t0 >> log2_bs] : -1;
-    return (blk >= 0 && blk < r.n_blocks) ? blk : -1;
+// Block ids of the 8 rows of the tile at tile_base (row r holds tokens
+// tile_base + 8r .. +7), or -1 for rows past L or with an id outside the
+// pool.  One vector load (lane i reads row i % 8's table entry) and 8 lane
+// reads put the ids in scalar registers after a single memory round trip.
+// The table index is clamped to the row's capacity, not to L, so the load
+// does not wait for the context length.
+__device__ __forceinline__ int tile_block_raw(const Region& r, const int32_t* __restrict__ btb, int tile_base,
+                                              int log2_bs, int lane) {
+    const int t0 = tile_base + 8 * (lane & 7);
+    return btb[min(t0 >> log2_bs, r.max_blocks - 1)];
+}
+
+__device__ __forceinline__ void tile_blocks_from(const Region& r, int raw, int tile_base, int L, int lane,
+                                                 int (&blk)[8]) {
+    const int t0 = tile_base + 8 * (lane & 7);
+    const int id = (t0 < L && raw >= 0 && raw < r.n_blocks) ? raw : -1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) blk[i] = __builtin_amdgcn_readlane(id, i);
+}
+
+__device__ __forceinline__ void tile_blocks(const Region& r, const int32_t* __restrict__ btb, int tile_base, int L,
+                                            int log2_bs, int lane, int (&blk)[8]) {
+    tile_blocks_from(r, tile_block_raw(r, btb, tile_base, log2_bs, lane), tile_base, L, lane, blk);
+}
+
+// Byte offset of row r's (token group 0, kv-head kh) entry in the pool, in
+// units of one head row; wave-uniform.  An invalid row maps to 0 (slot 0 of
+// the pool, always in bounds; its lanes are masked).
+__device__ __forceinline__ size_t row_unit(int blk, int t0, int bs_mask, int nkv, int kh) {
+    return blk >= 0 ? ((size_t)blk * (bs_mask + 1) + (t0 & bs_mask)) * nkv + kh : 0;
 }
 
 // ----------------------------------------------------------------------------
@@ -128,63 +154,80 @@ struct WaveState {
 
 // ----------------------------------------------------------------------------
 // int8 tile ([P3] Sec. 2 seg. 2)
+//
+// issue_*: the block ids of the tile's 8 rows are wave-uniform, so they come
+// from scalar loads; all 16 vector loads of the rows then go out with no wait
+// in between, and the caller can overlap them with other work.  Rows whose
+// block is outside the pool are not read; lanes past the context end read
+// their (in-bounds) slot and are masked at compute time.
 // ----------------------------------------------------------------------------
+struct TileQ8 {
+    uint4 k[8], v[8];
+    float ks[8], vs[8];
+    bool valid[8];
+};
+
 template <bool WITH_V>
-__device__ __forceinline__ void load_tile_q8(const DecodeArgs& a, const int32_t* __restrict__ btb, int L, int kh,
-                                             int tile_base, int tg, int j, uint4 (&kr)[8], uint4 (&vr)[8],
-                                             float (&ksr)[8], float (&vsr)[8], bool (&valid)[8]) {
+__device__ __forceinline__ void issue_rows_q8(const DecodeArgs& a, const int (&blk)[8], int L, int kh, int tile_base,
+                                              int tg, int j, TileQ8& T) {
     const int bs_mask = (1 << a.log2_bs) - 1;
+    // lane part of every address: token group tg sits tg rows further on
+    const uint32_t lane_row = (uint32_t)tg * a.nkv;
+    size_t unit[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
         const int t0 = tile_base + 8 * r;
-        const int t = t0 + tg;
-        const int blk = row_block(a.r8, btb, t0, L, a.log2_bs);
-        valid[r] = (t < L) && (blk >= 0);
-        kr[r] = make_uint4(0, 0, 0, 0);
-        vr[r] = make_uint4(0, 0, 0, 0);
-        ksr[r] = 0.0f;
-        vsr[r] = 0.0f;
-        if (valid[r]) {
-            const size_t row = ((size_t)blk * (bs_mask + 1) + (t & bs_mask)) * a.nkv + kh;
-            kr[r] = ldg16(a.kc + row * kHD + 16 * j);
-            ksr[r] = a.ks[row];
-            if constexpr (WITH_V) {
-                vr[r] = ldg16(a.vc + row * kHD + 16 * j);
-                vsr[r] = a.vs[row];
-            }
+        T.valid[r] = (blk[r] >= 0) && (t0 + tg < L);
+        unit[r] = row_unit(blk[r], t0, bs_mask, a.nkv, kh);
+    }
+    // unconditional loads, all K rows before all V rows: the compiler can
+    // count outstanding loads exactly, and scoring starts while V is in flight
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        T.k[r] = ldg16(a.kc + unit[r] * kHD + (lane_row * kHD + 16 * j));
+        T.ks[r] = (a.ks + unit[r])[lane_row];
+    }
+    if constexpr (WITH_V) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            T.v[r] = ldg16(a.vc + unit[r] * kHD + (lane_row * kHD + 16 * j));
+            T.vs[r] = (a.vs + unit[r])[lane_row];
         }
     }
 }
 
-template <int G>
-__device__ __forceinline__ void tile_q8(const DecodeArgs& a, const int32_t* __restrict__ btb, int L, int kh,
-                                        int tile_base, int tg, int j, const uint32_t (&qc)[G][4],
-                                        const float (&qs)[G], WaveState<G>& st) {
-    uint4 kr[8], vr[8];
-    float ksr[8], vsr[8];
-    bool valid[8];
-    load_tile_q8<true>(a, btb, L, kh, tile_base, tg, j, kr, vr, ksr, vsr, valid);
+template <bool WITH_V>
+__device__ __forceinline__ void issue_tile_q8(const DecodeArgs& a, const int32_t* __restrict__ btb, int L, int kh,
+                                              int tile_base, int tg, int j, TileQ8& T) {
+    int blk[8];
+    tile_blocks(a.r8, btb, tile_base, L, a.log2_bs, __lane_id(), blk);
+    issue_rows_q8<WITH_V>(a, blk, L, kh, tile_base, tg, j, T);
+}
 
+template <int G>
+__device__ __forceinline__ void compute_tile_q8(const DecodeArgs& a, const TileQ8& T, const uint32_t (&qc)[G][4],
+                                                const float (&qs)[G], WaveState<G>& st) {
     float w[G][8];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         float s[8];
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            const float f = block_scaled_sum(block_dot(qc[h], kr[r]), qs[h]);
-            s[r] = valid[r] ? f * (ksr[r] * a.score_scale) : -INFINITY;
+            const float f = block_scaled_sum(block_dot(qc[h], T.k[r]), qs[h]);
+            s[r] = T.valid[r] ? f * (T.ks[r] * a.score_scale) : -INFINITY;
         }
         const float mref = st.rebase(h, s);
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
             const float pr = __builtin_amdgcn_exp2f(s[r] - mref);
             st.S[h] += pr;
-            w[h][r] = pr * vsr[r];
+            // masked lanes may hold a stale slot's step: never let it in
+            w[h][r] = T.valid[r] ? pr * T.vs[r] : 0.0f;
         }
     }
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-        const uint32_t vw[4] = {vr[r].x, vr[r].y, vr[r].z, vr[r].w};
+        const uint32_t vw[4] = {T.v[r].x, T.v[r].y, T.v[r].z, T.v[r].w};
         float vf[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) vf[e] = sbyte_f(vw[e >> 2], e & 3);
@@ -232,35 +275,43 @@ __device__ __forceinline__ int block_dot_q4(const Q4Query& q, const uint2& k) {
     return d + dpp_i<kDppXor1>(d);
 }
 
-template <int G>
-__device__ __forceinline__ void tile_q4(const DecodeArgs& a, const int32_t* __restrict__ btb, int L, int kh,
-                                        int tile_base, int tg, int j, const Q4Query (&q4)[G],
-                                        const float (&qs)[G], WaveState<G>& st) {
+struct TileQ4 {
+    uint2 k[8], v[8];
+    float ks[8], kz[8], vs[8], vz[8];
+    bool valid[8];
+};
+
+__device__ __forceinline__ void issue_tile_q4(const DecodeArgs& a, const int32_t* __restrict__ btb, int L, int kh,
+                                              int tile_base, int tg, int j, TileQ4& T) {
     const int bs_mask = (1 << a.log2_bs) - 1;
     const int grp = j >> 2;
-    uint2 kr[8], vr[8];
-    float ksc[8], kz[8], vsc[8], vz[8];
-    bool valid[8];
+    const uint32_t lane_row = (uint32_t)tg * a.nkv;
+    int blk[8];
+    tile_blocks(a.r4, btb, tile_base, L, a.log2_bs, __lane_id(), blk);
+    size_t unit[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
         const int t0 = tile_base + 8 * r;
-        const int t = t0 + tg;
-        const int blk = row_block(a.r4, btb, t0, L, a.log2_bs);
-        valid[r] = (t < L) && (blk >= 0);
-        kr[r] = make_uint2(0, 0);
-        vr[r] = make_uint2(0, 0);
-        ksc[r] = kz[r] = vsc[r] = vz[r] = 0.0f;
-        if (valid[r]) {
-            const size_t row = ((size_t)blk * (bs_mask + 1) + (t & bs_mask)) * a.nkv + kh;
-            kr[r] = *reinterpret_cast<const uint2*>(a.k4 + row * (kHD / 2) + 8 * j);
-            vr[r] = *reinterpret_cast<const uint2*>(a.v4 + row * (kHD / 2) + 8 * j);
-            ksc[r] = half_bits_f(a.k4s[row * 2 + grp]);
-            kz[r] = half_bits_f(a.k4z[row * 2 + grp]);
-            vsc[r] = half_bits_f(a.v4s[row * 2 + grp]);
-            vz[r] = half_bits_f(a.v4z[row * 2 + grp]);
-        }
+        T.valid[r] = (blk[r] >= 0) && (t0 + tg < L);
+        unit[r] = row_unit(blk[r], t0, bs_mask, a.nkv, kh);
     }
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        T.k[r] = *reinterpret_cast<const uint2*>(a.k4 + unit[r] * (kHD / 2) + (lane_row * (kHD / 2) + 8 * j));
+        T.ks[r] = half_bits_f((a.k4s + unit[r] * 2)[lane_row * 2 + grp]);
+        T.kz[r] = half_bits_f((a.k4z + unit[r] * 2)[lane_row * 2 + grp]);
+    }
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        T.v[r] = *reinterpret_cast<const uint2*>(a.v4 + unit[r] * (kHD / 2) + (lane_row * (kHD / 2) + 8 * j));
+        T.vs[r] = half_bits_f((a.v4s + unit[r] * 2)[lane_row * 2 + grp]);
+        T.vz[r] = half_bits_f((a.v4z + unit[r] * 2)[lane_row * 2 + grp]);
+    }
+}
 
+template <int G>
+__device__ __forceinline__ void compute_tile_q4(const DecodeArgs& a, const TileQ4& T, const Q4Query (&q4)[G],
+                                                const float (&qs)[G], WaveState<G>& st) {
     float ws[G][8];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -268,26 +319,26 @@ __device__ __forceinline__ void tile_q4(const DecodeArgs& a, const int32_t* __re
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
             // sum_b qsc_b * s_g * (P_b - z_g * R_b); z_g is an integer in [0, 15]
-            const int term = block_dot_q4(q4[h], kr[r]) - (int)kz[r] * q4[h].rsum;
-            float f = (float)term * (qs[h] * ksc[r]);
+            const int term = block_dot_q4(q4[h], T.k[r]) - (T.valid[r] ? (int)T.kz[r] : 0) * q4[h].rsum;
+            float f = (float)term * (qs[h] * T.ks[r]);
             f += dpp_f<kDppXor2>(f);
             f += dpp_f<kDppHalfMirror>(f);
-            s[r] = valid[r] ? f * a.score_scale : -INFINITY;
+            s[r] = T.valid[r] ? f * a.score_scale : -INFINITY;
         }
         const float mref = st.rebase(h, s);
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
             const float pr = __builtin_amdgcn_exp2f(s[r] - mref);
             st.S[h] += pr;
-            ws[h][r] = pr * vsc[r];
-            st.accz[h] = fmaf(ws[h][r], vz[r], st.accz[h]);
+            ws[h][r] = T.valid[r] ? pr * T.vs[r] : 0.0f;
+            st.accz[h] = fmaf(ws[h][r], T.valid[r] ? T.vz[r] : 0.0f, st.accz[h]);
         }
     }
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
         float vf[16];
-        const uint32_t lo[2] = {vr[r].x & kNib, vr[r].y & kNib};
-        const uint32_t hi[2] = {(vr[r].x >> 4) & kNib, (vr[r].y >> 4) & kNib};
+        const uint32_t lo[2] = {T.v[r].x & kNib, T.v[r].y & kNib};
+        const uint32_t hi[2] = {(T.v[r].x >> 4) & kNib, (T.v[r].y >> 4) & kNib};
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -374,11 +425,23 @@ __device__ __forceinline__ void write_partial(const DecodeArgs& a, ReduceSmem<G>
 // the chunk kernel.  Chunks [0, r4.max_chunks) cover the int4 region, the
 // rest the int8 region.
 // ----------------------------------------------------------------------------
-template <int G>
+// Walk this wave's tiles of the chunk: first, first + kWaves*64, ... < end.
+// The caller has already issued the first tile (always, so that no load
+// sits behind a branch and the compiler can count outstanding loads).
+template <class Tile, class Issue, class Compute>
+__device__ __forceinline__ void walk_tiles(int c0, int first, int end, Tile& A, Issue issue, Compute compute) {
+    for (int base = first; base < end;) {
+        compute(A);
+        base += kWaves * kTile;
+        if (base < end) issue(base, A);
+    }
+}
+
+template <int G, bool MIXED>
 __global__ __launch_bounds__(kWGThreads) void kvq_decode_chunk_kernel(DecodeArgs a) {
     __shared__ ReduceSmem<G> sm;
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int tg = lane >> 3;
     const int j = lane & 7;
 
@@ -394,44 +457,75 @@ __global__ __launch_bounds__(kWGThreads) void kvq_decode_chunk_kernel(DecodeArgs
     const int b = p / nct;
     const int c = p - b * nct;
     if (b >= a.batch) return;
-    const bool int4_region = c < a.r4.max_chunks;
+    const bool int4_region = MIXED && c < a.r4.max_chunks;
     const Region& reg = int4_region ? a.r4 : a.r8;
     const int cr = int4_region ? c : c - a.r4.max_chunks;
-    const int L = effective_len(reg, b, a.log2_bs);
     const int chunk_len = a.tiles_per_wave * kChunkUnit;
     const int c0 = cr * chunk_len;
+    const int32_t* btb = reg.bt + (size_t)b * reg.max_blocks;
+    // the first tile's table entries go out together with the length load
+    const int raw0 = tile_block_raw(reg, btb, c0 + wave * kTile, a.log2_bs, lane);
+    const int L = effective_len(reg, b, a.log2_bs);
     if (c0 >= L) return;                                   // uniform per workgroup
+    const int end = min(L, c0 + chunk_len);
+    const int first = c0 + wave * kTile;
 
-    // [P3] Sec. 2 seg. 1: the group's query heads are quantized once.
+    // [P3] Sec. 2 seg. 1: the group's query heads are quantized once.  The
+    // query loads go out first so their latency overlaps the first tile's.
+    const float* qbase = a.q + ((size_t)b * a.nq + (size_t)kh * G) * kHD;
     uint32_t qc[G][4];
     float qs[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-        quantize_q_segment(a.q + ((size_t)b * a.nq + (size_t)kh * G + h) * kHD, j, qc[h], qs[h]);
-
     WaveState<G> st;
     st.init();
-    const int32_t* btb = reg.bt + (size_t)b * reg.max_blocks;
+
+    // A wave without a tile (first >= L) still issues one: every row is then
+    // invalid, reads slot 0 of the pool and is discarded.
     if (int4_region) {
-        Q4Query q4[G];
+        if constexpr (MIXED) {
+            TileQ4 A;
+            issue_tile_q4(a, btb, L, kh, first, tg, j, A);
 #pragma unroll
-        for (int h = 0; h < G; ++h) q4[h] = split_q4(qc[h]);
-        for (int tt = 0; tt < a.tiles_per_wave; ++tt) {
-            const int tile_base = c0 + (tt * kWaves + wave) * kTile;
-            if (tile_base >= L) break;                     // uniform per wave
-            tile_q4<G>(a, btb, L, kh, tile_base, tg, j, q4, qs, st);
+            for (int h = 0; h < G; ++h) quantize_q_segment(qbase + h * kHD, j, qc[h], qs[h]);
+            Q4Query q4[G];
+#pragma unroll
+            for (int h = 0; h < G; ++h) q4[h] = split_q4(qc[h]);
+            walk_tiles(
+                c0, first, end, A, [&](int base, TileQ4& T) { issue_tile_q4(a, btb, L, kh, base, tg, j, T); },
+                [&](const TileQ4& T) { compute_tile_q4<G>(a, T, q4, qs, st); });
         }
     } else {
-        for (int tt = 0; tt < a.tiles_per_wave; ++tt) {
-            const int tile_base = c0 + (tt * kWaves + wave) * kTile;
-            if (tile_base >= L) break;                     // uniform per wave
-            tile_q8<G>(a, btb, L, kh, tile_base, tg, j, qc, qs, st);
+        TileQ8 A;
+        if constexpr (G <= 4) {
+            // query loads, then the first tile's loads, then the query
+            // quantization, which waits on the query loads only
+            float qv[G][16];
+#pragma unroll
+            for (int h = 0; h < G; ++h) load_q16(qbase + h * kHD, j, qv[h]);
+            int blk[8];
+            tile_blocks_from(a.r8, raw0, first, L, lane, blk);
+            issue_rows_q8<true>(a, blk, L, kh, first, tg, j, A);
+            // keep the first tile's loads ahead of the quantization below
+            // (loop rotation would otherwise sink them into the tile loop)
+            __asm__ volatile("" ::: "memory");
+#pragma unroll
+            for (int h = 0; h < G; ++h) quantize_q16(qv[h], qc[h], qs[h]);
+        } else {
+            issue_tile_q8<true>(a, btb, L, kh, first, tg, j, A);
+#pragma unroll
+            for (int h = 0; h < G; ++h) quantize_q_segment(qbase + h * kHD, j, qc[h], qs[h]);
         }
+        walk_tiles(
+            c0, first, end, A, [&](int base, TileQ8& T) { issue_tile_q8<true>(a, btb, L, kh, base, tg, j, T); },
+            [&](const TileQ8& T) { compute_tile_q8<G>(a, T, qc, qs, st); });
     }
     write_partial<G>(a, sm, st, b, kh, c, lane, wave);
 }
 
 // Merge the chunk partials of one (sequence, query head) and normalize.
+// The chunk maxima and sums are wave-uniform (scalar loads); each thread owns
+// one output dimension and keeps 8 partial loads in flight.
+__device__ __forceinline__ int chunk_slot(int i, int n4, int base8) { return i < n4 ? i : base8 + (i - n4); }
+
 __global__ __launch_bounds__(kHD) void kvq_merge_kernel(float* __restrict__ out, DecodeArgs a) {
     const int bh = blockIdx.x;
     const int b = bh / a.nq;
@@ -439,25 +533,34 @@ __global__ __launch_bounds__(kHD) void kvq_merge_kernel(float* __restrict__ out,
     const int chunk_len = a.tiles_per_wave * kChunkUnit;
     const int nct = n_chunks_total(a);
     const int n4 = (effective_len(a.r4, b, a.log2_bs) + chunk_len - 1) / chunk_len;
-    const int n8 = (effective_len(a.r8, b, a.log2_bs) + chunk_len - 1) / chunk_len;
+    const int n = n4 + (effective_len(a.r8, b, a.log2_bs) + chunk_len - 1) / chunk_len;
+    const int base8 = a.r4.max_chunks;
     const float* mm = a.ws_m + (size_t)bh * nct;
     const float* ss = a.ws_s + (size_t)bh * nct;
     const float* aa = a.ws_acc + (size_t)bh * nct * kHD + d;
     float M = -INFINITY;
-    for (int c = 0; c < n4; ++c) M = fmaxf(M, mm[c]);
-    for (int c = a.r4.max_chunks; c < a.r4.max_chunks + n8; ++c) M = fmaxf(M, mm[c]);
+    for (int i = 0; i < n; ++i) M = fmaxf(M, mm[chunk_slot(i, n4, base8)]);
     float res = 0.0f;
     if (M != -INFINITY) {
         float S = 0.0f, acc = 0.0f;
-        for (int c = 0; c < n4; ++c) {
-            const float f = __builtin_amdgcn_exp2f(mm[c] - M);
-            S = fmaf(ss[c], f, S);
-            acc = fmaf(aa[(size_t)c * kHD], f, acc);
+        int i = 0;
+        for (; i + 8 <= n; i += 8) {
+            float v[8], f[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int cs = chunk_slot(i + k, n4, base8);
+                v[k] = aa[(size_t)cs * kHD];
+                f[k] = __builtin_amdgcn_exp2f(mm[cs] - M);
+                S = fmaf(ss[cs], f[k], S);
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) acc = fmaf(v[k], f[k], acc);
         }
-        for (int c = a.r4.max_chunks; c < a.r4.max_chunks + n8; ++c) {
-            const float f = __builtin_amdgcn_exp2f(mm[c] - M);
-            S = fmaf(ss[c], f, S);
-            acc = fmaf(aa[(size_t)c * kHD], f, acc);
+        for (; i < n; ++i) {
+            const int cs = chunk_slot(i, n4, base8);
+            const float f = __builtin_amdgcn_exp2f(mm[cs] - M);
+            S = fmaf(ss[cs], f, S);
+            acc = fmaf(aa[(size_t)cs * kHD], f, acc);
         }
         res = acc / S;
     }
@@ -503,7 +606,10 @@ inline void bind_workspace(DecodeArgs& a, void* workspace) {
 
 template <int G>
 inline void launch_chunks(const DecodeArgs& a, int n_wg, hipStream_t s) {
-    hipLaunchKernelGGL(kvq_decode_chunk_kernel<G>, dim3(n_wg), dim3(kWGThreads), 0, s, a);
+    if (a.r4.max_chunks > 0)
+        hipLaunchKernelGGL((kvq_decode_chunk_kernel<G, true>), dim3(n_wg), dim3(kWGThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((kvq_decode_chunk_kernel<G, false>), dim3(n_wg), dim3(kWGThreads), 0, s, a);
 }
 
 #define KVQ_DISPATCH_G(g, fn, ...)           \

@@ -96,21 +96,23 @@ __device__ __forceinline__ void quantize_row16x8(const float (&x)[8], uint32_t& 
 //   qsc = qm * (1/127)         (float32 constant 1/127)
 //   iq  = 127 / qm             (IEEE division)
 //   code= roundf(q * iq) clamped to [-128, 127]
-// Returns the lane's 16 codes packed in 4 dwords and its block's scale.
+// load_q16 issues the lane's loads; quantize_q16 consumes them (split so
+// that callers can put other loads in flight in between).
 // -----------------------------------------------------------------------------
-__device__ __forceinline__ void quantize_q_segment(const float* __restrict__ qrow, int j,
-                                                   uint32_t (&codes)[4], float& qsc) {
-#pragma clang fp contract(off)
+__device__ __forceinline__ void load_q16(const float* __restrict__ qrow, int j, float (&v)[16]) {
     const float4* p = reinterpret_cast<const float4*>(qrow + 16 * j);
-    float v[16];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        float4 t = p[i];
+        const float4 t = p[i];
         v[4 * i + 0] = t.x;
         v[4 * i + 1] = t.y;
         v[4 * i + 2] = t.z;
         v[4 * i + 3] = t.w;
     }
+}
+
+__device__ __forceinline__ void quantize_q16(const float (&v)[16], uint32_t (&codes)[4], float& qsc) {
+#pragma clang fp contract(off)
     float m = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
@@ -130,6 +132,13 @@ __device__ __forceinline__ void quantize_q_segment(const float* __restrict__ qro
         }
         codes[i] = w;
     }
+}
+
+__device__ __forceinline__ void quantize_q_segment(const float* __restrict__ qrow, int j, uint32_t (&codes)[4],
+                                                   float& qsc) {
+    float v[16];
+    load_q16(qrow, j, v);
+    quantize_q16(v, codes, qsc);
 }
 
 // int32 dot product of 16 query codes with 16 key codes (4 packed dwords
