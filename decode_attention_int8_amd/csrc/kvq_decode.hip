@@ -102,6 +102,49 @@ extern "C" int kvq8_decode_attn(float* out, const float* q, int batch, int nq, c
     return launch_decode(a, out, static_cast<hipStream_t>(stream));
 }
 
+extern "C" int kvq8_append_decode_attn(float* out, const float* q, int batch, int nq, const void* k_new,
+                                       const void* v_new, int dtype, int8_t* k_cache, int8_t* v_cache,
+                                       float* k_scale, float* v_scale, int n_blocks, int kv_bs, int nkv, int hd,
+                                       const int32_t* block_tables, int max_blocks_per_seq,
+                                       const int32_t* ctx_lens, int max_ctx_len, float sm_scale, int chunk,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+    if (!decode_shape_ok(batch, nq, nkv, hd, kv_bs) || n_blocks < 1 || max_blocks_per_seq < 1) return KVQ8_ESHAPE;
+    if (max_ctx_len < 0 || dtype < KVQ8_F32 || dtype > KVQ8_F16) return KVQ8_EINVAL;
+    const int ch = resolve_chunk8(batch, nkv, max_ctx_len, chunk);
+    if (ch <= 0) return KVQ8_ESHAPE;
+    if (batch == 0) return KVQ8_OK;
+    if (!out || !q || !k_new || !v_new || !k_cache || !v_cache || !k_scale || !v_scale || !block_tables ||
+        !ctx_lens)
+        return KVQ8_EINVAL;
+    if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+        return KVQ8_EINVAL;
+    const size_t need = kvq8_decode_workspace_size(batch, nq, nkv, max_ctx_len, chunk);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return KVQ8_EWORKSPACE;
+
+    DecodeArgs a = {};
+    a.q = q;
+    a.kc = k_cache;
+    a.vc = v_cache;
+    a.ks = k_scale;
+    a.vs = v_scale;
+    a.kc_w = k_cache;
+    a.vc_w = v_cache;
+    a.ks_w = k_scale;
+    a.vs_w = v_scale;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.r8 = Region{block_tables, ctx_lens, max_blocks_per_seq, max_ctx_len, n_blocks, (max_ctx_len + ch - 1) / ch};
+    a.r4 = Region{nullptr, nullptr, 1, 0, 0, 0};
+    a.nq = nq;
+    a.nkv = nkv;
+    a.log2_bs = ilog2(kv_bs);
+    a.batch = batch;
+    a.tiles_per_wave = ch / kChunkUnit;
+    a.score_scale = sm_scale * kLog2e;
+    bind_workspace(a, workspace);
+    return launch_decode(a, out, static_cast<hipStream_t>(stream), dtype);
+}
+
 extern "C" int kvq8_qk_partials(int32_t* partials, const float* q, int batch, int nq, const int8_t* k_cache,
                                 int n_blocks, int kv_bs, int nkv, int hd, const int32_t* block_tables,
                                 int max_blocks_per_seq, const int32_t* ctx_lens, int max_ctx_len, void* stream) {

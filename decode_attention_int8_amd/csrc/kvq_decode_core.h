@@ -60,6 +60,13 @@ struct DecodeArgs {
     const uint16_t* v4s;
     const uint16_t* v4z;
     Region r8, r4;              // r4.max_chunks == 0 for the pure int8 path
+    // fused write path: the token at position L-1 of every sequence
+    const void* k_new;          // [batch][nkv][128], float32 / bf16 / f16
+    const void* v_new;
+    int8_t* kc_w;               // the int8 pool, written for that token
+    int8_t* vc_w;
+    float* ks_w;
+    float* vs_w;
     int nq, nkv, log2_bs, batch;
     int tiles_per_wave;
     float score_scale;          // sm_scale * log2(e)
@@ -90,17 +97,18 @@ __device__ __forceinline__ int tile_block_raw(const Region& r, const int32_t* __
     return btb[min(t0 >> log2_bs, r.max_blocks - 1)];
 }
 
-__device__ __forceinline__ void tile_blocks_from(const Region& r, int raw, int tile_base, int L, int lane,
-                                                 int (&blk)[8]) {
+__device__ __forceinline__ int tile_blocks_from(const Region& r, int raw, int tile_base, int L, int lane,
+                                                int (&blk)[8]) {
     const int t0 = tile_base + 8 * (lane & 7);
     const int id = (t0 < L && raw >= 0 && raw < r.n_blocks) ? raw : -1;
 #pragma unroll
     for (int i = 0; i < 8; ++i) blk[i] = __builtin_amdgcn_readlane(id, i);
+    return id;
 }
 
-__device__ __forceinline__ void tile_blocks(const Region& r, const int32_t* __restrict__ btb, int tile_base, int L,
-                                            int log2_bs, int lane, int (&blk)[8]) {
-    tile_blocks_from(r, tile_block_raw(r, btb, tile_base, log2_bs, lane), tile_base, L, lane, blk);
+__device__ __forceinline__ int tile_blocks(const Region& r, const int32_t* __restrict__ btb, int tile_base, int L,
+                                           int log2_bs, int lane, int (&blk)[8]) {
+    return tile_blocks_from(r, tile_block_raw(r, btb, tile_base, log2_bs, lane), tile_base, L, lane, blk);
 }
 
 // Byte offset of row r's (token group 0, kv-head kh) entry in the pool, in
@@ -165,6 +173,7 @@ struct TileQ8 {
     uint4 k[8], v[8];
     float ks[8], vs[8];
     bool valid[8];
+    int ids;           // lane i holds row (i % 8)'s block id (-1 when invalid)
 };
 
 template <bool WITH_V>
@@ -200,21 +209,40 @@ template <bool WITH_V>
 __device__ __forceinline__ void issue_tile_q8(const DecodeArgs& a, const int32_t* __restrict__ btb, int L, int kh,
                                               int tile_base, int tg, int j, TileQ8& T) {
     int blk[8];
-    tile_blocks(a.r8, btb, tile_base, L, a.log2_bs, __lane_id(), blk);
+    T.ids = tile_blocks(a.r8, btb, tile_base, L, a.log2_bs, __lane_id(), blk);
     issue_rows_q8<WITH_V>(a, blk, L, kh, tile_base, tg, j, T);
 }
 
-template <int G>
+// Row data of a tile, with row `nr` of token group `ntg` replaced by the
+// new token's codes when SUB (fused write path).
+struct RowSub {
+    uint4 k, v;
+    float ks, vs;
+    int nr;
+    bool me;           // this lane belongs to the replaced token group
+};
+
+template <int G, bool SUB = false>
 __device__ __forceinline__ void compute_tile_q8(const DecodeArgs& a, const TileQ8& T, const uint32_t (&qc)[G][4],
-                                                const float (&qs)[G], WaveState<G>& st) {
+                                                const float (&qs)[G], WaveState<G>& st, const RowSub* sub = nullptr) {
+    uint4 K8[8], V8[8];
+    float KS[8], VS[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const bool rep = SUB && sub->me && r == sub->nr;
+        K8[r] = rep ? sub->k : T.k[r];
+        V8[r] = rep ? sub->v : T.v[r];
+        KS[r] = rep ? sub->ks : T.ks[r];
+        VS[r] = rep ? sub->vs : T.vs[r];
+    }
     float w[G][8];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         float s[8];
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            const float f = block_scaled_sum(block_dot(qc[h], T.k[r]), qs[h]);
-            s[r] = T.valid[r] ? f * (T.ks[r] * a.score_scale) : -INFINITY;
+            const float f = block_scaled_sum(block_dot(qc[h], K8[r]), qs[h]);
+            s[r] = T.valid[r] ? f * (KS[r] * a.score_scale) : -INFINITY;
         }
         const float mref = st.rebase(h, s);
 #pragma unroll
@@ -222,12 +250,12 @@ __device__ __forceinline__ void compute_tile_q8(const DecodeArgs& a, const TileQ
             const float pr = __builtin_amdgcn_exp2f(s[r] - mref);
             st.S[h] += pr;
             // masked lanes may hold a stale slot's step: never let it in
-            w[h][r] = T.valid[r] ? pr * T.vs[r] : 0.0f;
+            w[h][r] = T.valid[r] ? pr * VS[r] : 0.0f;
         }
     }
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-        const uint32_t vw[4] = {T.v[r].x, T.v[r].y, T.v[r].z, T.v[r].w};
+        const uint32_t vw[4] = {V8[r].x, V8[r].y, V8[r].z, V8[r].w};
         float vf[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) vf[e] = sbyte_f(vw[e >> 2], e & 3);
@@ -354,6 +382,66 @@ __device__ __forceinline__ void compute_tile_q4(const DecodeArgs& a, const TileQ
 }
 
 // ----------------------------------------------------------------------------
+// fused write path ([P2] Sec. 2): the new token's K / V rows, quantized by the
+// 8 lanes of a token group (16 values per lane) with exactly the arithmetic of
+// the write kernel (max |x|, step = max / 127, roundf(x / step), clamp +-127),
+// so the codes are bit-identical to a separate kvq8_quantize_append.
+// ----------------------------------------------------------------------------
+template <int DT>
+__device__ __forceinline__ void load_new16(const void* base, size_t elem_off, float (&x)[16]) {
+    if constexpr (DT == KVQ8_F32) {
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem_off);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 t = p[i];
+            x[4 * i] = t.x;
+            x[4 * i + 1] = t.y;
+            x[4 * i + 2] = t.z;
+            x[4 * i + 3] = t.w;
+        }
+    } else {
+        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem_off);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const uint4 u = p[i];
+            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                if constexpr (DT == KVQ8_BF16) {
+                    x[8 * i + 2 * k] = __uint_as_float(w[k] << 16);
+                    x[8 * i + 2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+                } else {
+                    x[8 * i + 2 * k] = half_bits_f(w[k] & 0xFFFFu);
+                    x[8 * i + 2 * k + 1] = half_bits_f(w[k] >> 16);
+                }
+            }
+        }
+    }
+}
+
+// Quantize a 128-value row held by an aligned 8-lane group, 16 values per
+// lane: returns the lane's 16 codes (packed) and the row's step.
+__device__ __forceinline__ void quantize_row8x16(const float (&x)[16], uint4& codes, float& d) {
+#pragma clang fp contract(off)
+    float amax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(x[e]));
+    amax = fmaxf(amax, dpp_f<kDppXor1>(amax));
+    amax = fmaxf(amax, dpp_f<kDppXor2>(amax));
+    amax = fmaxf(amax, dpp_f<kDppHalfMirror>(amax));
+    if (amax < 1e-6f) amax = 1.0f;
+    d = amax / 127.0f;
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        float r = roundf(x[e] / d);
+        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        w[e >> 2] |= ((uint32_t)(int)r & 0xFFu) << (8 * (e & 3));
+    }
+    codes = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// ----------------------------------------------------------------------------
 // workgroup merge and partial write
 // ----------------------------------------------------------------------------
 template <int G>
@@ -431,13 +519,13 @@ __device__ __forceinline__ void write_partial(const DecodeArgs& a, ReduceSmem<G>
 template <class Tile, class Issue, class Compute>
 __device__ __forceinline__ void walk_tiles(int c0, int first, int end, Tile& A, Issue issue, Compute compute) {
     for (int base = first; base < end;) {
-        compute(A);
+        compute(base, A);
         base += kWaves * kTile;
         if (base < end) issue(base, A);
     }
 }
 
-template <int G, bool MIXED>
+template <int G, bool MIXED, int NEWDT>
 __global__ __launch_bounds__(kWGThreads) void kvq_decode_chunk_kernel(DecodeArgs a) {
     __shared__ ReduceSmem<G> sm;
     const int lane = threadIdx.x & (kWave - 1);
@@ -491,9 +579,30 @@ __global__ __launch_bounds__(kWGThreads) void kvq_decode_chunk_kernel(DecodeArgs
             for (int h = 0; h < G; ++h) q4[h] = split_q4(qc[h]);
             walk_tiles(
                 c0, first, end, A, [&](int base, TileQ4& T) { issue_tile_q4(a, btb, L, kh, base, tg, j, T); },
-                [&](const TileQ4& T) { compute_tile_q4<G>(a, T, q4, qs, st); });
+                [&](int, const TileQ4& T) { compute_tile_q4<G>(a, T, q4, qs, st); });
         }
     } else {
+        // Fused write path (NEWDT >= 0): the token at position L-1 belongs to
+        // one wave of one chunk (`has_new`), tile `nbase`.  Only that wave
+        // reads its K/V rows (every wave reading the same few lines would
+        // pile up on one L2 channel), after its own tile loads are out.
+        const int tn = L - 1;
+        const bool has_new = NEWDT >= 0 && tn >= c0 && tn < end && (((tn - c0) >> 6) & (kWaves - 1)) == wave;
+        const int nbase = tn & ~(kTile - 1);
+        RowSub nt;
+        nt.nr = (tn & (kTile - 1)) >> 3;
+        nt.me = tg == (tn & 7);
+        // The owner's new-token loads go out first: a conditional load that is
+        // older than every other load leaves the other waits exact, and the
+        // quantization below then overlaps the tile's memory latency.
+        float xk[16], xv[16];
+        if constexpr (NEWDT >= 0) {
+            if (has_new) {
+                const size_t off = ((size_t)b * a.nkv + kh) * kHD + 16 * j;
+                load_new16<NEWDT>(a.k_new, off, xk);
+                load_new16<NEWDT>(a.v_new, off, xv);
+            }
+        }
         TileQ8 A;
         if constexpr (G <= 4) {
             // query loads, then the first tile's loads, then the query
@@ -502,7 +611,7 @@ __global__ __launch_bounds__(kWGThreads) void kvq_decode_chunk_kernel(DecodeArgs
 #pragma unroll
             for (int h = 0; h < G; ++h) load_q16(qbase + h * kHD, j, qv[h]);
             int blk[8];
-            tile_blocks_from(a.r8, raw0, first, L, lane, blk);
+            A.ids = tile_blocks_from(a.r8, raw0, first, L, lane, blk);
             issue_rows_q8<true>(a, blk, L, kh, first, tg, j, A);
             // keep the first tile's loads ahead of the quantization below
             // (loop rotation would otherwise sink them into the tile loop)
@@ -514,57 +623,120 @@ __global__ __launch_bounds__(kWGThreads) void kvq_decode_chunk_kernel(DecodeArgs
 #pragma unroll
             for (int h = 0; h < G; ++h) quantize_q_segment(qbase + h * kHD, j, qc[h], qs[h]);
         }
+        if constexpr (NEWDT >= 0) {
+            if (has_new) {                                     // wave-uniform
+                quantize_row8x16(xk, nt.k, nt.ks);
+                quantize_row8x16(xv, nt.v, nt.vs);
+            }
+        }
         walk_tiles(
             c0, first, end, A, [&](int base, TileQ8& T) { issue_tile_q8<true>(a, btb, L, kh, base, tg, j, T); },
-            [&](const TileQ8& T) { compute_tile_q8<G>(a, T, qc, qs, st); });
+            [&](int base, const TileQ8& T) {
+                if constexpr (NEWDT >= 0) {
+                    if (has_new && base == nbase) {
+                        // the tile read the slot's previous contents: attend to
+                        // the new codes and store them in the slot
+                        const int blk = __builtin_amdgcn_readlane(T.ids, nt.nr);
+                        if (nt.me && blk >= 0) {
+                            const size_t row =
+                                row_unit(blk, base + 8 * nt.nr, (1 << a.log2_bs) - 1, a.nkv, kh) + (size_t)tg * a.nkv;
+                            *reinterpret_cast<uint4*>(a.kc_w + row * kHD + 16 * j) = nt.k;
+                            *reinterpret_cast<uint4*>(a.vc_w + row * kHD + 16 * j) = nt.v;
+                            if (j == 0) {
+                                a.ks_w[row] = nt.ks;
+                                a.vs_w[row] = nt.vs;
+                            }
+                        }
+                        compute_tile_q8<G, true>(a, T, qc, qs, st, &nt);
+                        return;
+                    }
+                }
+                compute_tile_q8<G>(a, T, qc, qs, st);
+            });
     }
     write_partial<G>(a, sm, st, b, kh, c, lane, wave);
 }
 
-// Merge the chunk partials of one (sequence, query head) and normalize.
-// The chunk maxima and sums are wave-uniform (scalar loads); each thread owns
-// one output dimension and keeps 8 partial loads in flight.
-__device__ __forceinline__ int chunk_slot(int i, int n4, int base8) { return i < n4 ? i : base8 + (i - n4); }
+// Merge the chunk partials of one (sequence, query head) and normalize
+// ([P3] Sec. 2 seg. 3 across chunks): M = max_c M_c, S = sum_c S_c 2^(M_c-M),
+// out = sum_c acc_c 2^(M_c-M) / S.  256 threads: thread (part, d) owns output
+// dimension d for half of the chunks; the two halves meet in LDS.  Chunks are
+// read in batches of kMergeBatch with every load of a batch in flight (so up
+// to 2 * kMergeBatch chunks cost one memory round trip); the loads do not wait
+// for the context lengths (chunks past them are masked afterwards), and
+// batches are combined with a running maximum.
+constexpr int kMergeBatch = 16;
+constexpr int kMergeThreads = 2 * kHD;
 
-__global__ __launch_bounds__(kHD) void kvq_merge_kernel(float* __restrict__ out, DecodeArgs a) {
+__global__ __launch_bounds__(kMergeThreads) void kvq_merge_kernel(float* __restrict__ out, DecodeArgs a) {
+    __shared__ float other[kHD + 2];
     const int bh = blockIdx.x;
     const int b = bh / a.nq;
-    const int d = threadIdx.x;
+    const int d = threadIdx.x & (kHD - 1);
+    const int part = __builtin_amdgcn_readfirstlane(threadIdx.x / kHD);
     const int chunk_len = a.tiles_per_wave * kChunkUnit;
     const int nct = n_chunks_total(a);
-    const int n4 = (effective_len(a.r4, b, a.log2_bs) + chunk_len - 1) / chunk_len;
-    const int n = n4 + (effective_len(a.r8, b, a.log2_bs) + chunk_len - 1) / chunk_len;
+    const int half = (nct + 1) / 2;
+    const int cbeg = part * half;
+    const int cend = min(nct, cbeg + half);
     const int base8 = a.r4.max_chunks;
     const float* mm = a.ws_m + (size_t)bh * nct;
     const float* ss = a.ws_s + (size_t)bh * nct;
     const float* aa = a.ws_acc + (size_t)bh * nct * kHD + d;
-    float M = -INFINITY;
-    for (int i = 0; i < n; ++i) M = fmaxf(M, mm[chunk_slot(i, n4, base8)]);
-    float res = 0.0f;
-    if (M != -INFINITY) {
-        float S = 0.0f, acc = 0.0f;
-        int i = 0;
-        for (; i + 8 <= n; i += 8) {
-            float v[8], f[8];
+    const int n4 = (effective_len(a.r4, b, a.log2_bs) + chunk_len - 1) / chunk_len;
+    const int n8 = (effective_len(a.r8, b, a.log2_bs) + chunk_len - 1) / chunk_len;
+    float M = -INFINITY, S = 0.0f, acc = 0.0f;
+    for (int c0 = cbeg; c0 < cend; c0 += kMergeBatch) {
+        float mv[kMergeBatch], sv[kMergeBatch], av[kMergeBatch];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int cs = chunk_slot(i + k, n4, base8);
-                v[k] = aa[(size_t)cs * kHD];
-                f[k] = __builtin_amdgcn_exp2f(mm[cs] - M);
-                S = fmaf(ss[cs], f[k], S);
-            }
+        for (int k = 0; k < kMergeBatch; ++k) {
+            const int cc = min(c0 + k, cend - 1);
+            mv[k] = mm[cc];
+            sv[k] = ss[cc];
+            av[k] = aa[(size_t)cc * kHD];
+        }
+        float bm = -INFINITY;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) acc = fmaf(v[k], f[k], acc);
+        for (int k = 0; k < kMergeBatch; ++k) {
+            const int c = c0 + k;
+            const bool live = c < cend && (c < n4 || (c >= base8 && c < base8 + n8));
+            mv[k] = live ? mv[k] : -INFINITY;
+            sv[k] = live ? sv[k] : 0.0f;   // a chunk never written may hold anything
+            av[k] = live ? av[k] : 0.0f;
+            bm = fmaxf(bm, mv[k]);
         }
-        for (; i < n; ++i) {
-            const int cs = chunk_slot(i, n4, base8);
-            const float f = __builtin_amdgcn_exp2f(mm[cs] - M);
-            S = fmaf(ss[cs], f, S);
-            acc = fmaf(aa[(size_t)cs * kHD], f, acc);
+        if (bm > M) {
+            const float f = __builtin_amdgcn_exp2f(M - bm);
+            S *= f;
+            acc *= f;
+            M = bm;
         }
-        res = acc / S;
+        if (M == -INFINITY) continue;
+#pragma unroll
+        for (int k = 0; k < kMergeBatch; ++k) {
+            const float f = __builtin_amdgcn_exp2f(mv[k] - M);
+            S = fmaf(sv[k], f, S);
+            acc = fmaf(av[k], f, acc);
+        }
     }
-    out[(size_t)bh * kHD + d] = res;
+    if (part == 1) {
+        other[d] = acc;
+        if (d == 0) {
+            other[kHD] = M;
+            other[kHD + 1] = S;
+        }
+    }
+    __syncthreads();
+    if (part == 0) {
+        const float M1 = other[kHD], S1 = other[kHD + 1], A1 = other[d];
+        const float Mt = fmaxf(M, M1);
+        float res = 0.0f;
+        if (Mt != -INFINITY) {
+            const float f0 = __builtin_amdgcn_exp2f(M - Mt), f1 = __builtin_amdgcn_exp2f(M1 - Mt);
+            res = fmaf(acc, f0, A1 * f1) / fmaf(S, f0, S1 * f1);
+        }
+        out[(size_t)bh * kHD + d] = res;
+    }
 }
 
 // ----------------------------------------------------------------------------
@@ -605,11 +777,18 @@ inline void bind_workspace(DecodeArgs& a, void* workspace) {
 }
 
 template <int G>
-inline void launch_chunks(const DecodeArgs& a, int n_wg, hipStream_t s) {
+inline void launch_chunks(const DecodeArgs& a, int n_wg, int new_dtype, hipStream_t s) {
+    const dim3 grid(n_wg), block(kWGThreads);
     if (a.r4.max_chunks > 0)
-        hipLaunchKernelGGL((kvq_decode_chunk_kernel<G, true>), dim3(n_wg), dim3(kWGThreads), 0, s, a);
+        hipLaunchKernelGGL((kvq_decode_chunk_kernel<G, true, -1>), grid, block, 0, s, a);
+    else if (new_dtype == KVQ8_F32)
+        hipLaunchKernelGGL((kvq_decode_chunk_kernel<G, false, KVQ8_F32>), grid, block, 0, s, a);
+    else if (new_dtype == KVQ8_BF16)
+        hipLaunchKernelGGL((kvq_decode_chunk_kernel<G, false, KVQ8_BF16>), grid, block, 0, s, a);
+    else if (new_dtype == KVQ8_F16)
+        hipLaunchKernelGGL((kvq_decode_chunk_kernel<G, false, KVQ8_F16>), grid, block, 0, s, a);
     else
-        hipLaunchKernelGGL((kvq_decode_chunk_kernel<G, false>), dim3(n_wg), dim3(kWGThreads), 0, s, a);
+        hipLaunchKernelGGL((kvq_decode_chunk_kernel<G, false, -1>), grid, block, 0, s, a);
 }
 
 #define KVQ_DISPATCH_G(g, fn, ...)           \
@@ -625,15 +804,16 @@ inline void launch_chunks(const DecodeArgs& a, int n_wg, hipStream_t s) {
     }
 
 // Enqueue the chunk kernel (if there is any context) and the merge kernel.
-inline int launch_decode(const DecodeArgs& a, float* out, hipStream_t s) {
+// new_dtype >= 0 fuses the write path of each sequence's last token.
+inline int launch_decode(const DecodeArgs& a, float* out, hipStream_t s, int new_dtype = -1) {
     const int nct = n_chunks_total(a);
     if (nct > 0) {
         const long pairs = (long)a.batch * nct;
         const long n_wg = (long)a.nkv * ((pairs + 7) / 8) * 8;
         if (n_wg > 0x7FFFFFFFL) return KVQ8_ESHAPE;
-        KVQ_DISPATCH_G(a.nq / a.nkv, launch_chunks, a, (int)n_wg, s);
+        KVQ_DISPATCH_G(a.nq / a.nkv, launch_chunks, a, (int)n_wg, new_dtype, s);
     }
-    hipLaunchKernelGGL(kvq_merge_kernel, dim3(a.batch * a.nq), dim3(kHD), 0, s, out, a);
+    hipLaunchKernelGGL(kvq_merge_kernel, dim3(a.batch * a.nq), dim3(kMergeThreads), 0, s, out, a);
     return launch_status();
 }
 

@@ -36,6 +36,8 @@ _SIGNATURES = {
     "kvq8_decode_workspace_size": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "kvq8_decode_attn": (_c_int, [_p, _p, _c_int, _c_int, _p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _p,
                                   _c_int, _p, _c_int, _f, _c_int, _p, _c_size, _p]),
+    "kvq8_append_decode_attn": (_c_int, [_p, _p, _c_int, _c_int, _p, _p, _c_int, _p, _p, _p, _p, _c_int, _c_int,
+                                         _c_int, _c_int, _p, _c_int, _p, _c_int, _f, _c_int, _p, _c_size, _p]),
     "kvq8_quantize_q": (_c_int, [_p, _p, _p, _c_int, _c_int, _p]),
     "kvq8_qk_partials": (_c_int, [_p, _p, _c_int, _c_int, _p, _c_int, _c_int, _c_int, _c_int, _p, _c_int, _p,
                                   _c_int, _p]),
@@ -164,6 +166,39 @@ def kvq8_decode_attn(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, c
         _ptr(ctx_lens, torch.int32, "ctx_lens"), max_ctx_len, float(sm_scale), chunk,
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
     _check(st, "kvq8_decode_attn")
+    return out
+
+
+def kvq8_append_decode_attn(out, q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_tables, ctx_lens,
+                            max_ctx_len: int, sm_scale: float | None = None, chunk: int = 0, workspace=None,
+                            stream=None):
+    """Write each sequence's newest token (k_new / v_new [B][nkv][128] at
+    position ctx_lens[b] - 1) into the int8 cache, then decode attention over
+    the whole context, in one pass."""
+    B, nq, hd = q.shape
+    n_blocks, kv_bs, nkv, _ = k_cache.shape
+    if out.shape != q.shape:
+        raise ValueError("out must match q")
+    if k_new.dtype not in _DTYPES or v_new.dtype != k_new.dtype:
+        raise ValueError("k_new / v_new must share one of float32, bfloat16, float16")
+    if tuple(k_new.shape) != (B, nkv, hd) or v_new.shape != k_new.shape:
+        raise ValueError("k_new / v_new must be [B][nkv][hd]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or ctx_lens.shape != (B,):
+        raise ValueError("block_tables must be [B][max_blocks], ctx_lens [B]")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(hd)
+    need = kvq8_decode_workspace_size(B, nq, nkv, max_ctx_len, chunk)
+    if workspace is None:
+        workspace = alloc_workspace(need, q.device)
+    st = lib().kvq8_append_decode_attn(
+        _ptr(out, torch.float32, "out"), _ptr(q, torch.float32, "q"), B, nq, _ptr(k_new, name="k_new"),
+        _ptr(v_new, name="v_new"), _DTYPES[k_new.dtype], _ptr(k_cache, torch.int8, "k_cache"),
+        _ptr(v_cache, torch.int8, "v_cache"), _ptr(k_scale, torch.float32, "k_scale"),
+        _ptr(v_scale, torch.float32, "v_scale"), n_blocks, kv_bs, nkv, hd,
+        _ptr(block_tables, torch.int32, "block_tables"), block_tables.shape[1],
+        _ptr(ctx_lens, torch.int32, "ctx_lens"), max_ctx_len, float(sm_scale), chunk,
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
+    _check(st, "kvq8_append_decode_attn")
     return out
 
 

@@ -162,6 +162,29 @@ int kvq8_decode_attn(float* out, const float* q, int batch, int nq,
                      int chunk, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * kvq8_append_decode_attn -- one decode step of a layer: the write path for
+ * each sequence's newest token, then decode attention over its whole
+ * context, in one pass over the cache ([P2] Sec. 2 write path followed by
+ * [P3] Sec. 2, as the layer runs them).
+ *
+ * Sequence b's newest token is at position ctx_lens[b] - 1; its K and V rows
+ * (k_new[b], v_new[b], [nkv][hd] of `dtype`) are quantized exactly as
+ * kvq8_quantize_append does, stored in the slot the block table assigns to
+ * that position (skipped when the block id is outside the pool), and used
+ * by the attention.  The cache bytes and the output equal those of
+ * kvq8_quantize_append followed by kvq8_decode_attn.  Sequences with
+ * ctx_lens[b] = 0 write nothing and get a zero row.  Other arguments as for
+ * kvq8_decode_attn (same workspace size); the cache pools are written.
+ */
+int kvq8_append_decode_attn(float* out, const float* q, int batch, int nq,
+                            const void* k_new, const void* v_new, int dtype,
+                            int8_t* k_cache, int8_t* v_cache, float* k_scale, float* v_scale,
+                            int n_blocks, int kv_bs, int nkv, int hd,
+                            const int32_t* block_tables, int max_blocks_per_seq,
+                            const int32_t* ctx_lens, int max_ctx_len, float sm_scale,
+                            int chunk, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * kvq8_quantize_q -- step 1 of kvq8_decode_attn alone, exported so that the
  * query codes and block scales can be checked bit for bit ([P3] Sec. 2
  * seg. 1).  Runs the same device code the decode kernel runs.

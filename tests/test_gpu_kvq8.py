@@ -239,3 +239,54 @@ def test_decode_repeatable_and_stream_ordered(K):
     s.synchronize()
     a = [host(o) for o in outs]
     assert np.array_equal(a[0], a[1]) and np.array_equal(a[1], a[2])
+
+
+# ----------------------------------------------------------------------------
+# fused write path + decode (one pass per layer step)
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("g,dtype", [(2, "f32"), (4, "bf16"), (1, "f16"), (8, "f32"), (3, "bf16")])
+def test_append_decode_equals_append_then_decode(K, g, dtype):
+    torch = _torch()
+    r = W.rng(340, g, ["f32", "bf16", "f16"].index(dtype))
+    nkv, bs = 2, 16
+    nq = g * nkv
+    lens = np.array([1, 64, 65, 300, 0, 2049, 1000, 257], np.int32)   # new token at lens - 1
+    B, Lm = len(lens), int(lens.max())
+    bt, nb = W.paged_block_tables(r, lens, bs, spare_blocks=2)
+    bt[6, 62] = nb + 7                        # newest token of sequence 6 sits in an invalid block
+    k = W.normal_f32(r, (B, Lm, nkv, 128))
+    v = W.student_t3_f32(r, (B, Lm, nkv, 128), 0.5)
+    prev = np.maximum(lens - 1, 0)
+    c = Q8Cache(nb, bs, nkv)
+    fill_sequences(c, bt, prev, k, v)           # history without the newest token
+    stale = W.normal_f32(r, (B, nkv, 128), 3.0)  # old contents of the newest slots
+    have = lens > 0
+    sl = np.array([bt[b, (lens[b] - 1) // bs] * bs + (lens[b] - 1) % bs if have[b] else -1 for b in range(B)],
+                  np.int32)
+    sl[6] = -1
+    c.append(stale, stale, sl)
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dtype]
+    kn = dev(np.stack([k[b, max(lens[b] - 1, 0)] for b in range(B)])).to(tdt)
+    vn = dev(np.stack([v[b, max(lens[b] - 1, 0)] for b in range(B)])).to(tdt)
+    q = W.normal_f32(r, (B, nq, 128), 2.0)
+    # separate: write path, then decode, on a copy of the cache
+    gk2, gv2, gks2, gvs2 = c.gk.clone(), c.gv.clone(), c.gks.clone(), c.gvs.clone()
+    K.kvq8_quantize_append(gk2, gv2, gks2, gvs2, kn, vn, dev(sl))
+    out_sep = torch.empty((B, nq, 128), dtype=torch.float32, device="cuda")
+    K.kvq8_decode_attn(out_sep, dev(q), gk2, gv2, gks2, gvs2, dev(bt), dev(lens), Lm, SM)
+    # fused
+    out = torch.empty((B, nq, 128), dtype=torch.float32, device="cuda")
+    K.kvq8_append_decode_attn(out, dev(q), kn, vn, c.gk, c.gv, c.gks, c.gvs, dev(bt), dev(lens), Lm, SM)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(c.gk), host(gk2)) and np.array_equal(host(c.gv), host(gv2))
+    assert np.array_equal(host(c.gks).view(np.uint32), host(gks2).view(np.uint32))
+    assert np.array_equal(host(c.gvs).view(np.uint32), host(gvs2).view(np.uint32))
+    assert np.array_equal(host(out), host(out_sep))
+    # and against the oracle: write the new tokens there too
+    O8.quantize_append(c.kp, c.vp, c.ks, c.vs, kn.float().cpu().numpy(), vn.float().cpu().numpy(), sl)
+    keep = np.ones(B, bool)
+    keep[6] = False              # block 62 of sequence 6 is outside the pool: its tokens are skipped
+    ref = O8.decode_attention_q8(q[keep], c.kp, c.ks, c.vp, c.vs, bt[keep], lens[keep], bs, SM)
+    assert_attn_close(host(out)[keep], ref, f"fused g={g} {dtype}")
+    assert np.all(host(out)[4] == 0.0)
