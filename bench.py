@@ -12,8 +12,9 @@ Cache, so the layers are streamed from HBM.
 Output: one JSON line with the effective HBM bandwidth of the whole step
 (algorithmic bytes: int8 K+V codes and float32 steps read by decode, plus the
 write path's input read and code/step writes), microseconds per step, a
-roofline entry for the decode chunk kernel timed with HIP events on its
-stream, and the CPU oracle timed on a bounded sample on the host.
+roofline entry for one decode call (chunk + merge kernel) timed with HIP
+events over the timed region on the launch stream, and the CPU oracle timed
+on a bounded sample on the host.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
@@ -35,6 +36,37 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, vendor figure
 TOK_HEAD_BYTES = 2 * 128 + 2 * 4   # K+V codes + K/V float32 steps per (token, kv-head)
 
 
+# HBM bytes per decode call from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE
+# passes over this benchmark (KiB per dispatch), scaled by what the same
+# counters read for a plain 256 MiB device copy (--calibrate-copy 256):
+# FETCH_SIZE 131085.3 KiB -> 2.000 bytes per counted byte, WRITE_SIZE
+# 262144 KiB -> 1.000.  Valid only for the kernel sources they were taken on.
+PMC = {"sources_sha256_16": "3514b3da7a76ae40",
+       "fetch_kib": {"chunk": 8614.84, "merge": 168.04}, "write_kib": {"chunk": 290.06, "merge": 8.0},
+       "fetch_scale": 268435456 / (131085.27 * 1024), "write_scale": 268435456 / (262144.0 * 1024)}
+
+
+def kernel_sources_digest() -> str:
+    import hashlib
+    import glob
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "decode_attention_int8_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes one decode call moves (chunk + merge kernels), or None when
+    the kernel sources changed since the counters were taken."""
+    if kernel_sources_digest() != PMC["sources_sha256_16"]:
+        return None
+    rd = sum(PMC["fetch_kib"].values()) * 1024 * PMC["fetch_scale"]
+    wr = sum(PMC["write_kib"].values()) * 1024 * PMC["write_scale"]
+    return int(round(rd + wr))
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -44,7 +76,23 @@ def parse():
     p.add_argument("--ctx", type=int, default=8192)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                   help="only run a plain device-to-device copy of MIB MiB (for scaling memory counters) and exit")
     return p.parse_args()
+
+
+def calibrate_copy(mib: int):
+    """A plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters give
+    the scale between those counters and bytes moved."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n, "launches": 3}), flush=True)
 
 
 class Layer:
@@ -109,6 +157,9 @@ def cpu_baseline(args, nq, nkv, bs, L, bytes_per_layer):
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build has no multi-GPU path)",
               file=sys.stderr)
@@ -125,15 +176,11 @@ def main():
     chunk = K.kvq8_decode_chunk_tokens(1, nkv, L)
     ws = K.alloc_workspace(K.kvq8_decode_workspace_size(1, nq, nkv, L, 0), "cuda")
 
-    def step(events=None):
+    def step():
         # one decode step: per layer, write the newest token and attend (one call)
-        for i, ly in enumerate(layers):
-            if events is not None:
-                events[i][0].record()
+        for ly in layers:
             K.kvq8_append_decode_attn(ly.out, ly.q, ly.k_new, ly.v_new, ly.k, ly.v, ly.ks, ly.vs, ly.bt, ly.lens, L,
                                       sm, 0, ws)
-            if events is not None:
-                events[i][1].record()
 
     # warm up eagerly on a side stream, then capture the whole step in a graph
     side = torch.cuda.Stream()
@@ -160,22 +207,13 @@ def main():
     torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
 
-    # duration of each decode call (chunk + merge kernels), from HIP events on
-    # the launch stream, over eager passes of the same step
-    ev_steps = max(1, min(args.steps, 50))
-    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in layers]
-           for _ in range(ev_steps)]
-    for st in evs:
-        step(st)
-    torch.cuda.synchronize()
-    durs = [a.elapsed_time(b) for st in evs for a, b in st]
-    decode_us = 1e3 * float(np.mean(durs))
-
     decode_bytes_layer = L * nkv * TOK_HEAD_BYTES
     write_bytes_layer = nkv * 2 * 128 * 4 + nkv * 2 * (128 + 4)
     step_bytes = n_layers * (decode_bytes_layer + write_bytes_layer)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    achieved = decode_bytes_layer / (decode_us * 1e-6) / 1e9
+    # the timed region is n_layers back-to-back calls per step on one stream
+    call_us = 1e3 * ms_per_step / n_layers
+    achieved = decode_bytes_layer / (call_us * 1e-6) / 1e9
 
     res = {
         "metric": "q8-KV decode attention: effective HBM GB/s (% of peak) and us/step at 8K ctx",
@@ -197,9 +235,9 @@ def main():
                                f"call), step replayed as a HIP graph",
                    "global_batch": 1, "seq_len": L, "chunk_tokens": chunk, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "kernel": "one kvq8_append_decode_attn call: kvq_decode_chunk_kernel<2,false,0> + kvq_merge_kernel",
-                     "bytes_per_launch": decode_bytes_layer, "avg_call_us": round(decode_us, 3)},
+                     "bytes_per_launch": decode_bytes_layer, "avg_call_us": round(call_us, 3)},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args, nq, nkv, bs, L, decode_bytes_layer + write_bytes_layer)
