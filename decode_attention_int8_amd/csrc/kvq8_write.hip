@@ -60,16 +60,22 @@ __global__ __launch_bounds__(256) void kvq8_quantize_append_kernel(
 }
 
 // One 8-lane group per query vector; lane j quantizes values 16j .. 16j+15.
+// The decode kernels' query quantization, exported: a workgroup of 256
+// threads quantizes 8 rows into LDS and copies codes and scales out.
 __global__ __launch_bounds__(256) void kvq8_quantize_q_kernel(int8_t* __restrict__ qi, float* __restrict__ qsc,
                                                               const float* __restrict__ q, long n_vectors) {
-    const int j = threadIdx.x & 7;
-    const long vec = (long)blockIdx.x * 32 + (threadIdx.x >> 3);
-    if (vec >= n_vectors) return;                  // whole 8-lane groups leave together
-    uint32_t codes[4];
-    float s;
-    quantize_q_segment(q + (size_t)vec * kHD, j, codes, s);
-    *reinterpret_cast<uint4*>(qi + (size_t)vec * kHD + 16 * j) = make_uint4(codes[0], codes[1], codes[2], codes[3]);
-    if ((j & 1) == 0) qsc[(size_t)vec * (kHD / kQBlock) + (j >> 1)] = s;
+    __shared__ QSmem sm;
+    const long row0 = (long)blockIdx.x * kMaxRows;
+    const int n = (int)min((long)kMaxRows, n_vectors - row0);
+    const float4 x = load_q4(q + (size_t)row0 * kHD, n);
+    quantize_q4(x, n, sm);
+    lds_barrier();
+    const int t = threadIdx.x;
+    if ((t >> 5) < n) {
+        reinterpret_cast<uint32_t*>(qi + (size_t)row0 * kHD)[t] = sm.qc[t >> 5][t & 31];
+        if ((t & 31) < kHD / kQBlock) qsc[(size_t)row0 * (kHD / kQBlock) + 4 * (t >> 5) + (t & 31)] =
+            sm.qs[t >> 5][t & 31];
+    }
 }
 
 }  // namespace kvq
@@ -111,7 +117,7 @@ extern "C" int kvq8_quantize_q(int8_t* qi, float* qsc, const float* q, int n_vec
     if (n_vectors < 0) return KVQ8_EINVAL;
     if (n_vectors == 0) return KVQ8_OK;
     if (!qi || !qsc || !q || !aligned16(q) || !aligned16(qi)) return KVQ8_EINVAL;
-    const dim3 grid((unsigned)((n_vectors + 31) / 32)), block(256);
+    const dim3 grid((unsigned)((n_vectors + kMaxRows - 1) / kMaxRows)), block(256);
     hipLaunchKernelGGL(kvq8_quantize_q_kernel, grid, block, 0, static_cast<hipStream_t>(stream), qi, qsc, q,
                        (long)n_vectors);
     return launch_status();

@@ -3,47 +3,56 @@
 // variant ([P4] Sec. 3.2-3.3).  The pipeline itself lives in
 // kvq_decode_core.h and is compiled once, here.
 #include "kvq_decode_core.h"
+#include "kvq_decode_mfma.h"
 
 namespace kvq {
 
-// Integer block partials of every (sequence, query head, token): one wave per
-// (sequence, kv-head, 64-token tile), with the decode kernel's loader and dot
-// code.
-template <int G>
-__global__ __launch_bounds__(kWave) void kvq8_qk_partials_kernel(DecodeArgs a, int32_t* __restrict__ partials,
-                                                                 int n_tiles) {
-    const int lane = threadIdx.x;
-    const int tg = lane >> 3;
-    const int j = lane & 7;
-    const int tile = blockIdx.x % n_tiles;
-    const int kh = (blockIdx.x / n_tiles) % a.nkv;
-    const int b = blockIdx.x / (n_tiles * a.nkv);
+// Integer block partials of every (sequence, query head, token): a workgroup
+// per (sequence, kv-head, 4 tiles of 64 tokens) runs the decode kernel's
+// query quantization, tile loader and matrix-core dot products.
+template <bool BS8>
+__global__ __launch_bounds__(kWGThreads) void kvq8_qk_partials_kernel(DecodeArgs a, int32_t* __restrict__ partials,
+                                                                      int n_groups) {
+    __shared__ QSmem qsm;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int g = lane >> 4;
+    const int m = lane & 15;
+    const int G = a.nq / a.nkv;
+    const int grp = blockIdx.x % n_groups;
+    const int kh = (blockIdx.x / n_groups) % a.nkv;
+    const int b = blockIdx.x / (n_groups * a.nkv);
+    const float4 qx = load_q4(a.q + ((size_t)b * a.nq + (size_t)kh * G) * kHD, G);
     const int L = effective_len(a.r8, b, a.log2_bs);
-    const int tile_base = tile * kTile;
-    if (tile_base >= L) return;
-    uint32_t qc[G][4];
-    float qs[G];
+    if (grp * kChunkUnit >= L) return;                    // uniform per workgroup
+    const int base = (grp * kWaves + wave) * kTile;
+    const int32_t* btb = a.r8.bt + (size_t)b * a.r8.max_blocks;
+    const int raw = mtile_raw(a.r8, btb, base, a.log2_bs, lane);
+    const LaneOff lo = lane_offsets(a, lane);
+    MTile T;
+    mtile_issue<BS8, true>(a, raw, base, kh, lane, lo, T);
+    quantize_q4(qx, G, qsm);
+    lds_barrier();
+    const MQuery Q = load_q_operand(qsm, G, g, m);
+    v4i_t d[4][2];
+    mtile_qk(T, Q, d);
+    const int H = m >> 1;
+    if (H >= G) return;
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-        quantize_q_segment(a.q + ((size_t)b * a.nq + (size_t)kh * G + h) * kHD, j, qc[h], qs[h]);
-    TileQ8 T;
-    issue_tile_q8<false>(a, a.r8.bt + (size_t)b * a.r8.max_blocks, L, kh, tile_base, tg, j, T);
+    for (int v = 0; v < 4; ++v) {
+        const int id0 = __builtin_amdgcn_readlane(T.id, 16 * v);
+        const int id1 = __builtin_amdgcn_readlane(T.id, 16 * v + 8);
+        const int id = (g & 2) ? id1 : id0;          // block of tokens 16v + 4g + r
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        const int t = tile_base + 8 * r + tg;
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const int d = block_dot(qc[h], T.k[r]);
-            if (T.valid[r] && (j & 1) == 0)
-                partials[(((size_t)b * a.nq + (size_t)kh * G + h) * a.r8.max_len + t) * 4 + (j >> 1)] = d;
-        }
+            for (int r = 0; r < 4; ++r) {
+                const int t = base + 16 * v + 4 * g + r;
+                if (t < L && id >= 0)
+                    partials[(((size_t)b * a.nq + (size_t)kh * G + H) * a.r8.max_len + t) * 4 + 2 * h + (m & 1)] =
+                        d[v][h][r];
+            }
     }
-}
-
-template <int G>
-inline void launch_partials(const DecodeArgs& a, int32_t* partials, int n_tiles, hipStream_t s) {
-    hipLaunchKernelGGL(kvq8_qk_partials_kernel<G>, dim3(a.batch * a.nkv * n_tiles), dim3(kWave), 0, s, a,
-                       partials, n_tiles);
 }
 
 }  // namespace kvq
@@ -74,6 +83,7 @@ extern "C" int kvq8_decode_attn(float* out, const float* q, int batch, int nq, c
                                 const int32_t* ctx_lens, int max_ctx_len, float sm_scale, int chunk,
                                 void* workspace, size_t workspace_bytes, void* stream) {
     if (!decode_shape_ok(batch, nq, nkv, hd, kv_bs) || n_blocks < 1 || max_blocks_per_seq < 1) return KVQ8_ESHAPE;
+    if (!rows_fit_u32(n_blocks, kv_bs, nkv)) return KVQ8_ESHAPE;
     if (max_ctx_len < 0) return KVQ8_EINVAL;
     const int ch = resolve_chunk8(batch, nkv, max_ctx_len, chunk);
     if (ch <= 0) return KVQ8_ESHAPE;
@@ -109,6 +119,7 @@ extern "C" int kvq8_append_decode_attn(float* out, const float* q, int batch, in
                                        const int32_t* ctx_lens, int max_ctx_len, float sm_scale, int chunk,
                                        void* workspace, size_t workspace_bytes, void* stream) {
     if (!decode_shape_ok(batch, nq, nkv, hd, kv_bs) || n_blocks < 1 || max_blocks_per_seq < 1) return KVQ8_ESHAPE;
+    if (!rows_fit_u32(n_blocks, kv_bs, nkv)) return KVQ8_ESHAPE;
     if (max_ctx_len < 0 || dtype < KVQ8_F32 || dtype > KVQ8_F16) return KVQ8_EINVAL;
     const int ch = resolve_chunk8(batch, nkv, max_ctx_len, chunk);
     if (ch <= 0) return KVQ8_ESHAPE;
@@ -149,6 +160,7 @@ extern "C" int kvq8_qk_partials(int32_t* partials, const float* q, int batch, in
                                 int n_blocks, int kv_bs, int nkv, int hd, const int32_t* block_tables,
                                 int max_blocks_per_seq, const int32_t* ctx_lens, int max_ctx_len, void* stream) {
     if (!decode_shape_ok(batch, nq, nkv, hd, kv_bs) || n_blocks < 1 || max_blocks_per_seq < 1) return KVQ8_ESHAPE;
+    if (!rows_fit_u32(n_blocks, kv_bs, nkv)) return KVQ8_ESHAPE;
     if (max_ctx_len < 0) return KVQ8_EINVAL;
     if (batch == 0 || max_ctx_len == 0) return KVQ8_OK;
     if (!partials || !q || !k_cache || !block_tables || !ctx_lens) return KVQ8_EINVAL;
@@ -161,9 +173,15 @@ extern "C" int kvq8_qk_partials(int32_t* partials, const float* q, int batch, in
     a.nkv = nkv;
     a.log2_bs = ilog2(kv_bs);
     a.batch = batch;
-    const int n_tiles = (max_ctx_len + kTile - 1) / kTile;
-    if ((long)batch * nkv * n_tiles > 0x7FFFFFFFL) return KVQ8_ESHAPE;
-    KVQ_DISPATCH_G(nq / nkv, launch_partials, a, partials, n_tiles, static_cast<hipStream_t>(stream));
+    const int n_groups = (max_ctx_len + kChunkUnit - 1) / kChunkUnit;
+    if ((long)batch * nkv * n_groups > 0x7FFFFFFFL) return KVQ8_ESHAPE;
+    const dim3 grid(batch * nkv * n_groups), block(kWGThreads);
+    if (kv_bs < 16)
+        hipLaunchKernelGGL(kvq8_qk_partials_kernel<true>, grid, block, 0, static_cast<hipStream_t>(stream), a,
+                           partials, n_groups);
+    else
+        hipLaunchKernelGGL(kvq8_qk_partials_kernel<false>, grid, block, 0, static_cast<hipStream_t>(stream), a,
+                           partials, n_groups);
     return launch_status();
 }
 

@@ -213,28 +213,13 @@ __device__ __forceinline__ void issue_tile_q8(const DecodeArgs& a, const int32_t
     issue_rows_q8<WITH_V>(a, blk, L, kh, tile_base, tg, j, T);
 }
 
-// Row data of a tile, with row `nr` of token group `ntg` replaced by the
-// new token's codes when SUB (fused write path).
-struct RowSub {
-    uint4 k, v;
-    float ks, vs;
-    int nr;
-    bool me;           // this lane belongs to the replaced token group
-};
-
-template <int G, bool SUB = false>
+template <int G>
 __device__ __forceinline__ void compute_tile_q8(const DecodeArgs& a, const TileQ8& T, const uint32_t (&qc)[G][4],
-                                                const float (&qs)[G], WaveState<G>& st, const RowSub* sub = nullptr) {
-    uint4 K8[8], V8[8];
-    float KS[8], VS[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        const bool rep = SUB && sub->me && r == sub->nr;
-        K8[r] = rep ? sub->k : T.k[r];
-        V8[r] = rep ? sub->v : T.v[r];
-        KS[r] = rep ? sub->ks : T.ks[r];
-        VS[r] = rep ? sub->vs : T.vs[r];
-    }
+                                                const float (&qs)[G], WaveState<G>& st) {
+    const uint4(&K8)[8] = T.k;
+    const uint4(&V8)[8] = T.v;
+    const float(&KS)[8] = T.ks;
+    const float(&VS)[8] = T.vs;
     float w[G][8];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -525,9 +510,10 @@ __device__ __forceinline__ void walk_tiles(int c0, int first, int end, Tile& A, 
     }
 }
 
-template <int G, bool MIXED, int NEWDT>
-__global__ __launch_bounds__(kWGThreads) void kvq_decode_chunk_kernel(DecodeArgs a) {
+template <int G>
+__global__ __launch_bounds__(kWGThreads) void kvq4_decode_chunk_kernel(DecodeArgs a) {
     __shared__ ReduceSmem<G> sm;
+    __shared__ QSmem qsm;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int tg = lane >> 3;
@@ -545,114 +531,63 @@ __global__ __launch_bounds__(kWGThreads) void kvq_decode_chunk_kernel(DecodeArgs
     const int b = p / nct;
     const int c = p - b * nct;
     if (b >= a.batch) return;
-    const bool int4_region = MIXED && c < a.r4.max_chunks;
+    const bool int4_region = c < a.r4.max_chunks;
     const Region& reg = int4_region ? a.r4 : a.r8;
     const int cr = int4_region ? c : c - a.r4.max_chunks;
     const int chunk_len = a.tiles_per_wave * kChunkUnit;
     const int c0 = cr * chunk_len;
     const int32_t* btb = reg.bt + (size_t)b * reg.max_blocks;
-    // the first tile's table entries go out together with the length load
+    // the query loads and the first tile's table entries go out together
+    // with the length load
+    const float4 qx = load_q4(a.q + ((size_t)b * a.nq + (size_t)kh * G) * kHD, G);
     const int raw0 = tile_block_raw(reg, btb, c0 + wave * kTile, a.log2_bs, lane);
     const int L = effective_len(reg, b, a.log2_bs);
     if (c0 >= L) return;                                   // uniform per workgroup
     const int end = min(L, c0 + chunk_len);
     const int first = c0 + wave * kTile;
 
-    // [P3] Sec. 2 seg. 1: the group's query heads are quantized once.  The
-    // query loads go out first so their latency overlaps the first tile's.
-    const float* qbase = a.q + ((size_t)b * a.nq + (size_t)kh * G) * kHD;
-    uint32_t qc[G][4];
-    float qs[G];
     WaveState<G> st;
     st.init();
+    uint32_t qc[G][4];
+    float qs[G];
+    // [P3] Sec. 2 seg. 1: the group's query heads are quantized once per
+    // workgroup (into LDS); lane segment j takes codes 16j .. 16j+15 and the
+    // scale of block j/2.
+    auto query_codes = [&]() __attribute__((always_inline)) {
+        quantize_q4(qx, G, qsm);
+        lds_barrier();
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const uint4 w = *reinterpret_cast<const uint4*>(&qsm.qc[h][4 * j]);
+            qc[h][0] = w.x;
+            qc[h][1] = w.y;
+            qc[h][2] = w.z;
+            qc[h][3] = w.w;
+            qs[h] = qsm.qs[h][j >> 1];
+        }
+    };
 
     // A wave without a tile (first >= L) still issues one: every row is then
     // invalid, reads slot 0 of the pool and is discarded.
     if (int4_region) {
-        if constexpr (MIXED) {
-            TileQ4 A;
-            issue_tile_q4(a, btb, L, kh, first, tg, j, A);
+        TileQ4 A;
+        issue_tile_q4(a, btb, L, kh, first, tg, j, A);
+        query_codes();
+        Q4Query q4[G];
 #pragma unroll
-            for (int h = 0; h < G; ++h) quantize_q_segment(qbase + h * kHD, j, qc[h], qs[h]);
-            Q4Query q4[G];
-#pragma unroll
-            for (int h = 0; h < G; ++h) q4[h] = split_q4(qc[h]);
-            walk_tiles(
-                c0, first, end, A, [&](int base, TileQ4& T) { issue_tile_q4(a, btb, L, kh, base, tg, j, T); },
-                [&](int, const TileQ4& T) { compute_tile_q4<G>(a, T, q4, qs, st); });
-        }
+        for (int h = 0; h < G; ++h) q4[h] = split_q4(qc[h]);
+        walk_tiles(
+            c0, first, end, A, [&](int base, TileQ4& T) { issue_tile_q4(a, btb, L, kh, base, tg, j, T); },
+            [&](int, const TileQ4& T) { compute_tile_q4<G>(a, T, q4, qs, st); });
     } else {
-        // Fused write path (NEWDT >= 0): the token at position L-1 belongs to
-        // one wave of one chunk (`has_new`), tile `nbase`.  Only that wave
-        // reads its K/V rows (every wave reading the same few lines would
-        // pile up on one L2 channel), after its own tile loads are out.
-        const int tn = L - 1;
-        const bool has_new = NEWDT >= 0 && tn >= c0 && tn < end && (((tn - c0) >> 6) & (kWaves - 1)) == wave;
-        const int nbase = tn & ~(kTile - 1);
-        RowSub nt;
-        nt.nr = (tn & (kTile - 1)) >> 3;
-        nt.me = tg == (tn & 7);
-        // The owner's new-token loads go out first: a conditional load that is
-        // older than every other load leaves the other waits exact, and the
-        // quantization below then overlaps the tile's memory latency.
-        float xk[16], xv[16];
-        if constexpr (NEWDT >= 0) {
-            if (has_new) {
-                const size_t off = ((size_t)b * a.nkv + kh) * kHD + 16 * j;
-                load_new16<NEWDT>(a.k_new, off, xk);
-                load_new16<NEWDT>(a.v_new, off, xv);
-            }
-        }
         TileQ8 A;
-        if constexpr (G <= 4) {
-            // query loads, then the first tile's loads, then the query
-            // quantization, which waits on the query loads only
-            float qv[G][16];
-#pragma unroll
-            for (int h = 0; h < G; ++h) load_q16(qbase + h * kHD, j, qv[h]);
-            int blk[8];
-            A.ids = tile_blocks_from(a.r8, raw0, first, L, lane, blk);
-            issue_rows_q8<true>(a, blk, L, kh, first, tg, j, A);
-            // keep the first tile's loads ahead of the quantization below
-            // (loop rotation would otherwise sink them into the tile loop)
-            __asm__ volatile("" ::: "memory");
-#pragma unroll
-            for (int h = 0; h < G; ++h) quantize_q16(qv[h], qc[h], qs[h]);
-        } else {
-            issue_tile_q8<true>(a, btb, L, kh, first, tg, j, A);
-#pragma unroll
-            for (int h = 0; h < G; ++h) quantize_q_segment(qbase + h * kHD, j, qc[h], qs[h]);
-        }
-        if constexpr (NEWDT >= 0) {
-            if (has_new) {                                     // wave-uniform
-                quantize_row8x16(xk, nt.k, nt.ks);
-                quantize_row8x16(xv, nt.v, nt.vs);
-            }
-        }
+        int blk[8];
+        A.ids = tile_blocks_from(a.r8, raw0, first, L, lane, blk);
+        issue_rows_q8<true>(a, blk, L, kh, first, tg, j, A);
+        query_codes();
         walk_tiles(
             c0, first, end, A, [&](int base, TileQ8& T) { issue_tile_q8<true>(a, btb, L, kh, base, tg, j, T); },
-            [&](int base, const TileQ8& T) {
-                if constexpr (NEWDT >= 0) {
-                    if (has_new && base == nbase) {
-                        // the tile read the slot's previous contents: attend to
-                        // the new codes and store them in the slot
-                        const int blk = __builtin_amdgcn_readlane(T.ids, nt.nr);
-                        if (nt.me && blk >= 0) {
-                            const size_t row =
-                                row_unit(blk, base + 8 * nt.nr, (1 << a.log2_bs) - 1, a.nkv, kh) + (size_t)tg * a.nkv;
-                            *reinterpret_cast<uint4*>(a.kc_w + row * kHD + 16 * j) = nt.k;
-                            *reinterpret_cast<uint4*>(a.vc_w + row * kHD + 16 * j) = nt.v;
-                            if (j == 0) {
-                                a.ks_w[row] = nt.ks;
-                                a.vs_w[row] = nt.vs;
-                            }
-                        }
-                        compute_tile_q8<G, true>(a, T, qc, qs, st, &nt);
-                        return;
-                    }
-                }
-                compute_tile_q8<G>(a, T, qc, qs, st);
-            });
+            [&](int, const TileQ8& T) { compute_tile_q8<G>(a, T, qc, qs, st); });
     }
     write_partial<G>(a, sm, st, b, kh, c, lane, wave);
 }
@@ -763,6 +698,12 @@ inline bool decode_shape_ok(int batch, int nq, int nkv, int hd, int kv_bs) {
     return g >= 1 && g <= kMaxGroup;
 }
 
+// The int8 decode kernel indexes cache rows (one per slot and kv-head) with
+// 32-bit integers.
+inline bool rows_fit_u32(int n_blocks, int kv_bs, int nkv) {
+    return (unsigned long long)n_blocks * (unsigned long long)kv_bs * (unsigned long long)nkv <= 0xFFFFFFFFull;
+}
+
 inline size_t decode_workspace_bytes(int batch, int nq, int n_chunks_total) {
     const size_t n = (size_t)batch * nq * n_chunks_total;
     return round_up(n * kHD * sizeof(float), 256) + 2 * round_up(n * sizeof(float), 256);
@@ -777,18 +718,8 @@ inline void bind_workspace(DecodeArgs& a, void* workspace) {
 }
 
 template <int G>
-inline void launch_chunks(const DecodeArgs& a, int n_wg, int new_dtype, hipStream_t s) {
-    const dim3 grid(n_wg), block(kWGThreads);
-    if (a.r4.max_chunks > 0)
-        hipLaunchKernelGGL((kvq_decode_chunk_kernel<G, true, -1>), grid, block, 0, s, a);
-    else if (new_dtype == KVQ8_F32)
-        hipLaunchKernelGGL((kvq_decode_chunk_kernel<G, false, KVQ8_F32>), grid, block, 0, s, a);
-    else if (new_dtype == KVQ8_BF16)
-        hipLaunchKernelGGL((kvq_decode_chunk_kernel<G, false, KVQ8_BF16>), grid, block, 0, s, a);
-    else if (new_dtype == KVQ8_F16)
-        hipLaunchKernelGGL((kvq_decode_chunk_kernel<G, false, KVQ8_F16>), grid, block, 0, s, a);
-    else
-        hipLaunchKernelGGL((kvq_decode_chunk_kernel<G, false, -1>), grid, block, 0, s, a);
+inline void launch_chunks4(const DecodeArgs& a, int n_wg, hipStream_t s) {
+    hipLaunchKernelGGL(kvq4_decode_chunk_kernel<G>, dim3(n_wg), dim3(kWGThreads), 0, s, a);
 }
 
 #define KVQ_DISPATCH_G(g, fn, ...)           \
@@ -803,18 +734,5 @@ inline void launch_chunks(const DecodeArgs& a, int n_wg, int new_dtype, hipStrea
         default: fn<8>(__VA_ARGS__); break;  \
     }
 
-// Enqueue the chunk kernel (if there is any context) and the merge kernel.
-// new_dtype >= 0 fuses the write path of each sequence's last token.
-inline int launch_decode(const DecodeArgs& a, float* out, hipStream_t s, int new_dtype = -1) {
-    const int nct = n_chunks_total(a);
-    if (nct > 0) {
-        const long pairs = (long)a.batch * nct;
-        const long n_wg = (long)a.nkv * ((pairs + 7) / 8) * 8;
-        if (n_wg > 0x7FFFFFFFL) return KVQ8_ESHAPE;
-        KVQ_DISPATCH_G(a.nq / a.nkv, launch_chunks, a, (int)n_wg, new_dtype, s);
-    }
-    hipLaunchKernelGGL(kvq_merge_kernel, dim3(a.batch * a.nq), dim3(kMergeThreads), 0, s, out, a);
-    return launch_status();
-}
 
 }  // namespace kvq

@@ -89,56 +89,60 @@ __device__ __forceinline__ void quantize_row16x8(const float (&x)[8], uint32_t& 
 }
 
 // -----------------------------------------------------------------------------
-// Query quantization ([P3] Sec. 2 seg. 1) in the decode lane layout: lane
-// segment j = lane % 8 owns values 16j .. 16j+15 of the query row, so block
-// b = j / 2 is shared by lanes 2b and 2b+1.
+// Query quantization ([P3] Sec. 2 seg. 1) of up to 8 query rows by a
+// workgroup of at least 256 threads, into LDS:
 //   qm  = max |q| over the 32-value block (qm < 1e-6 -> 1)
 //   qsc = qm * (1/127)         (float32 constant 1/127)
 //   iq  = 127 / qm             (IEEE division)
 //   code= roundf(q * iq) clamped to [-128, 127]
-// load_q16 issues the lane's loads; quantize_q16 consumes them (split so
-// that callers can put other loads in flight in between).
+// Thread t handles values 4(t%32) .. +3 of row t/32; the 8 threads of a
+// 32-block find its max with three DPP steps.  load_q4 issues the thread's
+// load (so that callers can put other loads behind it); quantize_q4 takes
+// the loaded values.  Every decode path and the query export use these.
 // -----------------------------------------------------------------------------
-__device__ __forceinline__ void load_q16(const float* __restrict__ qrow, int j, float (&v)[16]) {
-    const float4* p = reinterpret_cast<const float4*>(qrow + 16 * j);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float4 t = p[i];
-        v[4 * i + 0] = t.x;
-        v[4 * i + 1] = t.y;
-        v[4 * i + 2] = t.z;
-        v[4 * i + 3] = t.w;
-    }
+constexpr int kMaxRows = 8;
+
+struct QSmem {
+    uint32_t qc[kMaxRows][kHD / 4];       // codes, 4 per word (little endian)
+    float qs[kMaxRows][kHD / kQBlock];    // block scales
+};
+
+__device__ __forceinline__ float4 load_q4(const float* __restrict__ rows, int n_rows) {
+    const int t = threadIdx.x;
+    if ((t >> 5) >= n_rows || t >= 32 * kMaxRows) return make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    return *reinterpret_cast<const float4*>(rows + (size_t)(t >> 5) * kHD + 4 * (t & 31));
 }
 
-__device__ __forceinline__ void quantize_q16(const float (&v)[16], uint32_t (&codes)[4], float& qsc) {
+__device__ __forceinline__ void quantize_q4(float4 x, int n_rows, QSmem& sm) {
 #pragma clang fp contract(off)
-    float m = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
-    m = fmaxf(m, dpp_f<kDppXor1>(m));
-    if (m < 1e-6f) m = 1.0f;
-    constexpr float kInv127 = 1.0f / 127.0f;
-    qsc = m * kInv127;
-    const float iq = 127.0f / m;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    const int t = threadIdx.x;
+    const int H = t >> 5;
+    if (H < n_rows && H < kMaxRows) {
+        float mx = fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w)));
+        mx = fmaxf(mx, dpp_f<kDppXor1>(mx));
+        mx = fmaxf(mx, dpp_f<kDppXor2>(mx));
+        mx = fmaxf(mx, dpp_f<kDppHalfMirror>(mx));
+        if (mx < 1e-6f) mx = 1.0f;
+        constexpr float kInv127 = 1.0f / 127.0f;
+        const float qsc = mx * kInv127;
+        const float iq = 127.0f / mx;
+        const float xs[4] = {x.x, x.y, x.z, x.w};
         uint32_t w = 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            float r = roundf(v[4 * i + e] * iq);
+            float r = roundf(xs[e] * iq);
             r = fminf(fmaxf(r, -128.0f), 127.0f);
             w |= ((uint32_t)(int)r & 0xFFu) << (8 * e);
         }
-        codes[i] = w;
+        sm.qc[H][t & 31] = w;
+        if ((t & 7) == 0) sm.qs[H][(t & 31) >> 3] = qsc;
     }
 }
 
-__device__ __forceinline__ void quantize_q_segment(const float* __restrict__ qrow, int j, uint32_t (&codes)[4],
-                                                   float& qsc) {
-    float v[16];
-    load_q16(qrow, j, v);
-    quantize_q16(v, codes, qsc);
+// LDS-only barrier: waits for this wave's LDS traffic (not for its loads in
+// flight), then for the workgroup.
+__device__ __forceinline__ void lds_barrier() {
+    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // int32 dot product of 16 query codes with 16 key codes (4 packed dwords

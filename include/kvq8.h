@@ -134,9 +134,12 @@ size_t kvq8_decode_workspace_size(int batch, int nq, int nkv, int max_ctx_len, i
  *      ([P3] Sec. 2 seg. 2-3).
  * The context is split into chunks processed in parallel, each keeping its
  * own running max and sum (online softmax per chunk); a second kernel merges
- * the chunks and divides by the total sum.  Accumulation is float32; the
- * result matches the exact float64 value of the definition to about 1e-5
- * relative.  A sequence with context length 0 gets a zero output row.
+ * the chunks and divides by the total sum.  The integer dot products and the
+ * value accumulation run on the matrix cores (weights carried as two bf16
+ * parts, exact to 2^-16 relative); accumulation is float32 and the result
+ * matches the exact float64 value of the definition to about 1e-5 relative.
+ * A sequence with context length 0 gets a zero output row.  The pool may
+ * hold at most 2^32 - 1 rows (n_blocks * kv_bs * nkv), else KVQ8_ESHAPE.
  *
  *   out               (device) float [batch][nq][hd], written
  *   q                 (device) float [batch][nq][hd], read; 16-byte aligned
