@@ -96,10 +96,11 @@ def calibrate_copy(mib: int):
 
 
 class Layer:
-    """One layer's paged int8 cache, block table and per-step inputs."""
+    """One layer's paged int8 cache and per-step inputs.  All layers share the
+    sequence's block table and length (as an engine does: one table per
+    sequence, one pool per layer)."""
 
-    def __init__(self, K, W, torch, layer, L, nq, nkv, bs):
-        self.bt_np, nb = W.paged_block_tables(W.rng(2, layer, 3), [L], bs)
+    def __init__(self, K, W, torch, layer, L, nq, nkv, bs, bt_np, nb, bt, lens):
         shp = (nb, bs, nkv, 128)
         self.k = torch.zeros(shp, dtype=torch.int8, device="cuda")
         self.v = torch.zeros(shp, dtype=torch.int8, device="cuda")
@@ -107,15 +108,14 @@ class Layer:
         self.vs = torch.zeros(shp[:3], dtype=torch.float32, device="cuda")
         kf = W.torch_normal((L, nkv, 128), "cuda", (2, layer, 0))
         vf = W.torch_normal((L, nkv, 128), "cuda", (2, layer, 1))
-        slots = W.slots_for_positions(self.bt_np, [0] * L, np.arange(L), bs)
+        slots = W.slots_for_positions(bt_np, [0] * L, np.arange(L), bs)
         K.kvq8_quantize_append(self.k, self.v, self.ks, self.vs, kf, vf, torch.from_numpy(slots).cuda())
         self.k_new = kf[L - 1:L].clone()            # the current token's K / V (re-written each step)
         self.v_new = vf[L - 1:L].clone()
         del kf, vf
-        self.slot = torch.from_numpy(slots[L - 1:L].copy()).cuda()
         self.q = W.torch_normal((1, nq, 128), "cuda", (2, layer, 2))
-        self.bt = torch.from_numpy(self.bt_np).cuda()
-        self.lens = torch.tensor([L], dtype=torch.int32, device="cuda")
+        self.bt = bt
+        self.lens = lens
         self.out = torch.empty((1, nq, 128), dtype=torch.float32, device="cuda")
 
 
@@ -172,7 +172,10 @@ def main():
     cfg = W.QWEN2B_8K
     nq, nkv, bs, L, n_layers = cfg["nq"], cfg["nkv"], cfg["kv_bs"], args.ctx, args.layers
     sm = 1.0 / math.sqrt(128)
-    layers = [Layer(K, W, torch, i, L, nq, nkv, bs) for i in range(n_layers)]
+    bt_np, nb = W.paged_block_tables(W.rng(2, 0, 3), [L], bs)
+    bt = torch.from_numpy(bt_np).cuda()
+    lens = torch.tensor([L], dtype=torch.int32, device="cuda")
+    layers = [Layer(K, W, torch, i, L, nq, nkv, bs, bt_np, nb, bt, lens) for i in range(n_layers)]
     chunk = K.kvq8_decode_chunk_tokens(1, nkv, L)
     ws = K.alloc_workspace(K.kvq8_decode_workspace_size(1, nq, nkv, L, 0), "cuda")
 
@@ -229,7 +232,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int8 KV codes, fp32 steps and accumulation",
-        "data": "synthetic (seeded N(0,1) K/V/q, paged blocks in shuffled order)",
+        "data": "synthetic (seeded N(0,1) K/V/q; one block table in shuffled order shared by the layers' pools)",
         "config": {"workload": f"qwen2b-shaped decode: {n_layers} layers x {nq}q/{nkv}kv heads, hd 128, batch 1, "
                                f"ctx {L}, kv_bs {bs}, per layer: write the newest token + decode (one fused "
                                f"call), step replayed as a HIP graph",

@@ -61,7 +61,7 @@ using namespace kvq;
 
 extern "C" int kvq8_decode_chunk_tokens(int batch, int nkv, int max_ctx_len) {
     if (batch < 0 || nkv < 1 || max_ctx_len < 0) return 0;
-    return default_tiles_per_wave((long)batch * nkv, max_ctx_len) * kChunkUnit;
+    return default_tiles_per_wave(batch, (long)batch * nkv, max_ctx_len) * kChunkUnit;
 }
 
 static int resolve_chunk8(int batch, int nkv, int max_ctx_len, int chunk) {
@@ -187,7 +187,7 @@ extern "C" int kvq8_qk_partials(int32_t* partials, const float* q, int batch, in
 
 extern "C" int kvq4_decode_chunk_tokens(int batch, int nkv, int max_len4, int max_len8) {
     if (batch < 0 || nkv < 1 || max_len4 < 0 || max_len8 < 0) return 0;
-    return default_tiles_per_wave((long)batch * nkv, (long)max_len4 + max_len8) * kChunkUnit;
+    return default_tiles_per_wave(batch, (long)batch * nkv, (long)max_len4 + max_len8) * kChunkUnit;
 }
 
 static int resolve_chunk4(int batch, int nkv, int max_len4, int max_len8, int chunk) {
