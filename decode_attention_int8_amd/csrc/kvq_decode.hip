@@ -3,7 +3,7 @@
 // variant ([P4] Sec. 3.2-3.3).  The pipeline itself lives in
 // kvq_decode_core.h and is compiled once, here.
 #include "kvq_decode_core.h"
-#include "kvq_decode_mfma.h"
+#include "kvq_decode_mfma4.h"
 
 namespace kvq {
 
@@ -224,6 +224,9 @@ extern "C" int kvq4_decode_attn(float* out, const float* q, int batch, int nq, c
     if (!aligned16(q) || !aligned16(k_cache4) || !aligned16(v_cache4) || !aligned16(k_cache8) ||
         !aligned16(v_cache8))
         return KVQ8_EINVAL;
+    // both groups' binary16 scale (zero point) of a row are read as one word
+    if (((uintptr_t)k_scale4 | (uintptr_t)k_zero4 | (uintptr_t)v_scale4 | (uintptr_t)v_zero4) & 3u) return KVQ8_EINVAL;
+    if (!rows_fit_u32(n_blocks4, kv_bs, nkv) || !rows_fit_u32(n_blocks8, kv_bs, nkv)) return KVQ8_ESHAPE;
     const size_t need = kvq4_decode_workspace_size(batch, nq, nkv, max_len4, max_len8, chunk);
     if (!workspace || workspace_bytes < need || !aligned16(workspace)) return KVQ8_EWORKSPACE;
 

@@ -357,6 +357,34 @@ __device__ __forceinline__ void mtile_compute(const DecodeArgs& a, const MTile T
     }
 }
 
+// Fold the waves' states (in LDS: per wave M, S and acc of each head) and
+// write one partial per query head.
+__device__ __forceinline__ void mcombine_write(const DecodeArgs& a, const MSmem& sm, int G, int b, int kh, int c) {
+    const int nct = n_chunks_total(a);
+    for (int idx = threadIdx.x; idx < G * kHD; idx += kWGThreads) {
+        const int h = idx / kHD;
+        const int d = idx - h * kHD;
+        float M = sm.m[0][h];
+#pragma unroll
+        for (int wv = 1; wv < kWaves; ++wv) M = fmaxf(M, sm.m[wv][h]);
+        float tot = 0.0f, ssum = 0.0f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int wv = 0; wv < kWaves; ++wv) {
+                const float f = __builtin_amdgcn_exp2f(sm.m[wv][h] - M);
+                tot = fmaf(sm.acc[wv][h][d], f, tot);
+                ssum = fmaf(sm.s[wv][h], f, ssum);
+            }
+        }
+        const size_t pi = ((size_t)b * a.nq + (size_t)kh * G + h) * nct + c;
+        a.ws_acc[pi * kHD + d] = tot;
+        if (d == 0) {
+            a.ws_m[pi] = M;
+            a.ws_s[pi] = ssum;
+        }
+    }
+}
+
 // Fold the wave states of the workgroup and write one partial per query head.
 __device__ __forceinline__ void mwrite_partial(const DecodeArgs& a, MSmem& sm, MState& st, int G, int b, int kh,
                                                int c, int lane, int wave) {
@@ -383,29 +411,7 @@ __device__ __forceinline__ void mwrite_partial(const DecodeArgs& a, MSmem& sm, M
         }
     }
     lds_barrier();
-    const int nct = n_chunks_total(a);
-    for (int idx = threadIdx.x; idx < G * kHD; idx += kWGThreads) {
-        const int h = idx / kHD;
-        const int d = idx - h * kHD;
-        float M = sm.m[0][h];
-#pragma unroll
-        for (int wv = 1; wv < kWaves; ++wv) M = fmaxf(M, sm.m[wv][h]);
-        float tot = 0.0f, ssum = 0.0f;
-        if (M != -INFINITY) {
-#pragma unroll
-            for (int wv = 0; wv < kWaves; ++wv) {
-                const float f = __builtin_amdgcn_exp2f(sm.m[wv][h] - M);
-                tot = fmaf(sm.acc[wv][h][d], f, tot);
-                ssum = fmaf(sm.s[wv][h], f, ssum);
-            }
-        }
-        const size_t pi = ((size_t)b * a.nq + (size_t)kh * G + h) * nct + c;
-        a.ws_acc[pi * kHD + d] = tot;
-        if (d == 0) {
-            a.ws_m[pi] = M;
-            a.ws_s[pi] = ssum;
-        }
-    }
+    mcombine_write(a, sm, G, b, kh, c);
 }
 
 template <int NEWDT, bool BS8>
@@ -548,25 +554,6 @@ inline void launch_mfma(const DecodeArgs& a, int n_wg, int new_dtype, hipStream_
         launch_mfma_bs<true>(a, n_wg, new_dtype, s);
     else
         launch_mfma_bs<false>(a, n_wg, new_dtype, s);
-}
-
-// Enqueue the chunk kernel (if there is any context) and the merge kernel.
-// new_dtype >= 0 fuses the write path of each sequence's last token.  The
-// int8 cache runs on the matrix cores; the mixed int4 / int8 cache on the
-// vector units.
-inline int launch_decode(const DecodeArgs& a, float* out, hipStream_t s, int new_dtype = -1) {
-    const int nct = n_chunks_total(a);
-    if (nct > 0) {
-        const long pairs = (long)a.batch * nct;
-        const long n_wg = (long)a.nkv * ((pairs + 7) / 8) * 8;
-        if (n_wg > 0x7FFFFFFFL) return KVQ8_ESHAPE;
-        if (a.r4.max_chunks > 0)
-            KVQ_DISPATCH_G(a.nq / a.nkv, launch_chunks4, a, (int)n_wg, s)
-        else
-            launch_mfma(a, (int)n_wg, new_dtype, s);
-    }
-    hipLaunchKernelGGL(kvq_merge_kernel, dim3(a.batch * a.nq), dim3(kMergeThreads), 0, s, out, a);
-    return launch_status();
 }
 
 }  // namespace kvq

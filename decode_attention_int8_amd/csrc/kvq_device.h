@@ -46,12 +46,6 @@ __device__ __forceinline__ float group8_max(float v) {
     v = fmaxf(v, xor32(v));
     return v;
 }
-__device__ __forceinline__ float group8_sum(float v) {
-    v += dpp_f<kDppRowRor8>(v);
-    v += swz_xor16(v);
-    v += xor32(v);
-    return v;
-}
 
 // signed byte k of a packed dword as float (one SDWA convert)
 __device__ __forceinline__ float sbyte_f(uint32_t w, int k) {
@@ -145,34 +139,10 @@ __device__ __forceinline__ void lds_barrier() {
     __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// int32 dot product of 16 query codes with 16 key codes (4 packed dwords
-// each), then the partner lane's half: the full 32-value block dot product
-// dot_b of [P3] Sec. 2 seg. 2, held by both lanes of the block.
-__device__ __forceinline__ int block_dot(const uint32_t (&qc)[4], const uint4& k) {
-    int d = __builtin_amdgcn_sdot4((int)qc[0], (int)k.x, 0, false);
-    d = __builtin_amdgcn_sdot4((int)qc[1], (int)k.y, d, false);
-    d = __builtin_amdgcn_sdot4((int)qc[2], (int)k.z, d, false);
-    d = __builtin_amdgcn_sdot4((int)qc[3], (int)k.w, d, false);
-    return d + dpp_i<kDppXor1>(d);
-}
-
-// Sum over the 4 blocks of sum_b qsc_b * dot_b: lanes of a token group hold
-// blocks (j/2) = 0..3 in pairs; after xor-2 and the half mirror every lane of
-// the 8-lane group holds the total.
-__device__ __forceinline__ float block_scaled_sum(int dot_b, float qsc_b) {
-    float f = (float)dot_b * qsc_b;
-    f += dpp_f<kDppXor2>(f);
-    f += dpp_f<kDppHalfMirror>(f);
-    return f;
-}
-
 // IEEE binary16 bits (low 16 bits of v) widened to float (exact)
 __device__ __forceinline__ float half_bits_f(uint32_t v) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)v);
 }
 
-__device__ __forceinline__ uint4 ldg16(const void* p) {
-    return *reinterpret_cast<const uint4*>(p);
-}
 
 }  // namespace kvq

@@ -254,8 +254,12 @@ size_t kvq4_decode_workspace_size(int batch, int nq, int nkv, int max_len4, int 
  * codes c, group scale s_g and zero z_g, block b's score term is
  * qsc_b * s_g * (P_b - z_g * R_b) with P_b = sum qi * c and R_b = sum qi
  * (int32); values contribute weight * s_g * (c - z_g).  Both pools' chunks
- * are merged as in kvq8_decode_attn.  Other arguments as there; the int4
- * and int8 pools share kv_bs and nkv.
+ * are merged as in kvq8_decode_attn.  Both products run on the matrix cores
+ * (the int4 values enter as c - z_g, exact in f16; the weights p * s_g as in
+ * kvq8_decode_attn).  Other arguments as there; the int4 and int8 pools
+ * share kv_bs and nkv.  The four binary16 arrays (k_scale4 .. v_zero4) must
+ * be 4-byte aligned (a row's two groups are read as one word), else
+ * KVQ8_EINVAL; each pool may hold at most 2^32 - 1 rows, else KVQ8_ESHAPE.
  */
 int kvq4_decode_attn(float* out, const float* q, int batch, int nq,
                      const uint8_t* k_cache4, const uint8_t* v_cache4,

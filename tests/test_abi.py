@@ -113,3 +113,24 @@ def test_binding_requires_gpu_tensors():
     kn = torch.zeros((3, 2, 128), dtype=torch.float32)
     with pytest.raises(ValueError):
         K.kvq8_quantize_append(x, x, s, s, kn, kn, torch.zeros(3, dtype=torch.int32))
+
+
+def _decode4(**kw):
+    a = dict(out=_fake(), q=_fake(), batch=2, nq=32, k4=_fake(), v4=_fake(), k4s=_fake(), k4z=_fake(), v4s=_fake(),
+             v4z=_fake(), n4=64, bt4=_fake(), mb4=32, l4=_fake(), ml4=512, k8=_fake(), v8=_fake(), k8s=_fake(),
+             v8s=_fake(), n8=8, bt8=_fake(), mb8=4, l8=_fake(), ml8=64, kv_bs=16, nkv=4, hd=128, sm=0.088, chunk=0,
+             ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return K.lib().kvq4_decode_attn(*a.values())
+
+
+def test_decode4_validation():
+    need = K.kvq4_decode_workspace_size(2, 32, 4, 512, 64, 0)
+    ws = dict(ws=_fake(), ws_bytes=need)
+    # the binary16 scale / zero arrays are read two groups per word
+    for name in ("k4s", "k4z", "v4s", "v4z"):
+        assert _decode4(**ws, **{name: _fake(4098)}) == EINVAL, name
+    assert _decode4(hd=64, **ws) == ESHAPE
+    assert _decode4(nq=36, **ws) == ESHAPE            # group of 9
+    assert _decode4(**ws, n4=1 << 30) == ESHAPE       # more than 2^32 - 1 rows
+    assert _decode4(ws=None, ws_bytes=0) == EWORKSPACE
