@@ -9,6 +9,10 @@ Pins (tests/test_oracle_kvq4.py):
                        codes in [0, 15]; round-trip error <= half a step
                        ([P4] Sec. 3.2); constant groups are exact.
   pack/unpack_nibbles  round trip; even element in the high nibble.
+  requantize_q8_to_q4  rows whose int8 values lie exactly on an int4 grid give
+                       that grid's codes, scale and zero back; the int4 value
+                       of every element is within half an int4 step of its
+                       int8 value; constant groups take the unit scale.
   decode_attention_mixed
                        with every token in the int8 pool it equals
                        kvq8.decode_attention_q8; on values exactly on the
@@ -102,6 +106,40 @@ def quantize_append_q4(k_pool, v_pool, k_scale, k_zero, v_scale, v_zero, k_new, 
         flat = pool.reshape((nb * bs,) + pool.shape[2:])
         flat[slots[ok]] = val[ok]
     return k_pool, v_pool, k_scale, k_zero, v_scale, v_zero
+
+
+def dequantize_rows_q8_f32(codes, d) -> np.ndarray:
+    """code * step as the engine computes it: one float32 multiplication."""
+    return np.asarray(codes).astype(F32) * np.asarray(d, dtype=F32)[..., None]
+
+
+def requantize_q8_to_q4(q8_pools, q4_pools, src_slots, dst_slots):
+    """Move tokens from the int8 pool to the int4 pool ([P4] Sec. 3.3 practical
+    notes: as the sequence grows, the oldest time block is re-quantized from
+    8-bit to 4-bit).
+
+    Reading: the float values are gone once a token is in the int8 pool, so
+    the int4 codes are those of the int8 values: code * step (float32, the
+    engine's precision) goes through quantize_groups_q4.  Pair i moves slot
+    src_slots[i] of the int8 pool to slot dst_slots[i] of the int4 pool;
+    pairs with either slot outside its pool are skipped.
+
+    q8_pools = (k_codes, k_step, v_codes, v_step) as in kvq8; q4_pools =
+    (k_packed, k_scale, k_zero, v_packed, v_scale, v_zero), modified in place.
+    """
+    kc8, ks8, vc8, vs8 = q8_pools
+    k4, k4s, k4z, v4, v4s, v4z = q4_pools
+    nb8, bs, nkv, _ = kc8.shape
+    nb4 = k4.shape[0]
+    src = np.asarray(src_slots, dtype=np.int64)
+    dst = np.asarray(dst_slots, dtype=np.int64)
+    ok = (src >= 0) & (src < nb8 * bs) & (dst >= 0) & (dst < nb4 * bs)
+    src, dst = src[ok], dst[ok]
+    flat = lambda a: a.reshape((a.shape[0] * a.shape[1],) + a.shape[2:])
+    xk = dequantize_rows_q8_f32(flat(kc8)[src], flat(ks8)[src])
+    xv = dequantize_rows_q8_f32(flat(vc8)[src], flat(vs8)[src])
+    quantize_append_q4(k4, v4, k4s, k4z, v4s, v4z, xk, xv, dst)
+    return q4_pools
 
 
 def decode_attention_mixed(q, q4_pools, bt4, lens4, q8_pools, bt8, lens8, kv_bs: int, sm_scale: float):

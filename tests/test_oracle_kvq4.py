@@ -166,3 +166,100 @@ def test_page_order_and_empty_context():
     np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-14)
     z = kvq4.decode_attention_mixed(q, p4, bt4, [0], p8, bt8, [0], bs, SM)
     assert np.all(z == 0)
+
+
+# ----------------------------------------------------------------------------
+# re-quantization of aging int8 tokens into the int4 pool ([P4] Sec. 3.3)
+# ----------------------------------------------------------------------------
+
+def _rq_pools(nb8, nb4, bs, nkv):
+    q8 = (np.zeros((nb8, bs, nkv, 128), np.int8), np.zeros((nb8, bs, nkv), np.float32),
+          np.zeros((nb8, bs, nkv, 128), np.int8), np.zeros((nb8, bs, nkv), np.float32))
+    q4 = (np.zeros((nb4, bs, nkv, 64), np.uint8), np.zeros((nb4, bs, nkv, 2), np.float16),
+          np.zeros((nb4, bs, nkv, 2), np.float16), np.zeros((nb4, bs, nkv, 64), np.uint8),
+          np.zeros((nb4, bs, nkv, 2), np.float16), np.zeros((nb4, bs, nkv, 2), np.float16))
+    return q8, q4
+
+
+@pytest.mark.parametrize("j", [6, 8, 11])
+def test_requantize_reproduces_an_int4_grid(j):
+    """int8 values that lie on an int4 grid (step 2^-j, int4 scale 8 * 2^-j,
+    codes spanning 0..15) come back as exactly that grid's codes, scale and
+    zero point: closed form of the group rule, independent of the quantizer."""
+    r = W.rng(210, j)
+    bs, nkv, n = 16, 2, 40
+    q8, q4 = _rq_pools(4, 5, bs, nkv)
+    kc8, ks8, vc8, vs8 = q8
+    want = {}
+    for pool in (kc8, vc8):
+        c = r.integers(0, 16, size=pool.shape[:3] + (2, 64))
+        c[..., 0], c[..., 1] = 0, 15                  # the group spans all 16 codes
+        z = r.integers(0, 16, size=pool.shape[:3] + (2,))
+        pool[:] = (8 * (c - z[..., None])).reshape(pool.shape).astype(np.int8)
+        want[id(pool)] = (c, z)
+    ks8[:] = vs8[:] = np.float32(2.0 ** -j)
+    src = r.permutation(4 * bs)[:n]
+    dst = r.permutation(5 * bs)[:n]
+    kvq4.requantize_q8_to_q4(q8, q4, src, dst)
+    k4, k4s, k4z, v4, v4s, v4z = q4
+    for pool8, (packed, sc, zp) in ((kc8, (k4, k4s, k4z)), (vc8, (v4, v4s, v4z))):
+        c, z = want[id(pool8)]
+        c = c.reshape((-1,) + c.shape[2:])[src]          # [n][nkv][group][64]
+        z = z.reshape((-1,) + z.shape[2:])[src]          # [n][nkv][group]
+        got = kvq4.unpack_nibbles(packed.reshape((-1,) + packed.shape[2:])[dst]).reshape(c.shape)
+        assert np.array_equal(got, c)
+        assert np.all(sc.reshape(-1, nkv, 2)[dst] == np.float16(8 * 2.0 ** -j))
+        assert np.array_equal(zp.reshape(-1, nkv, 2)[dst].astype(np.int64), z)
+
+
+def test_requantize_error_within_half_an_int4_step():
+    """Every element's int4 value lies within half an int4 step of the int8
+    value it came from (groups that straddle zero, so the zero point never
+    clamps)."""
+    r = W.rng(211)
+    bs, nkv, n = 8, 4, 64
+    q8, q4 = _rq_pools(16, 8, bs, nkv)
+    kc8, ks8, vc8, vs8 = q8
+    for pool, st in ((kc8, ks8), (vc8, vs8)):
+        pool[:] = r.integers(-127, 128, size=pool.shape).astype(np.int8)
+        pool[..., 0], pool[..., 64] = -100, -100
+        pool[..., 1], pool[..., 65] = 100, 100
+        st[:] = np.exp(r.uniform(-6, 2, size=st.shape)).astype(np.float32)
+    src = r.permutation(16 * bs)[:n]
+    dst = r.permutation(8 * bs)[:n]
+    kvq4.requantize_q8_to_q4(q8, q4, src, dst)
+    k4, k4s, k4z, v4, v4s, v4z = q4
+    for (pool, st), (packed, sc, zp) in (((kc8, ks8), (k4, k4s, k4z)), ((vc8, vs8), (v4, v4s, v4z))):
+        x8 = pool.reshape(-1, nkv, 128)[src].astype(np.float64) * st.reshape(-1, nkv)[src][..., None]
+        c = kvq4.unpack_nibbles(packed.reshape(-1, nkv, 64)[dst]).astype(np.float64)
+        s = np.repeat(sc.reshape(-1, nkv, 2)[dst].astype(np.float64), 64, axis=-1)
+        z = np.repeat(zp.reshape(-1, nkv, 2)[dst].astype(np.float64), 64, axis=-1)
+        err = np.abs((c - z) * s - x8)
+        # half a step, plus the f16 rounding of the step over up to 15 steps
+        assert np.all(err <= s * (0.5 + 15 * 2.0 ** -11) + 1e-12)
+
+
+def test_requantize_constant_groups_and_skipped_pairs():
+    """An all-zero group takes the unit scale and zero point 0 (codes 0); pairs
+    whose source or destination lies outside its pool change nothing."""
+    bs, nkv = 8, 1
+    q8, q4 = _rq_pools(2, 2, bs, nkv)
+    kc8, ks8, vc8, vs8 = q8
+    kc8[:] = 5
+    kc8[:, :, :, 64:] = 0
+    vc8[:] = 0
+    ks8[:] = vs8[:] = np.float32(0.25)
+    for a in q4:
+        a.fill(0x55 if a.dtype == np.uint8 else np.float16(7.0))
+    kvq4.requantize_q8_to_q4(q8, q4, [3, -1, 99, 4], [0, 1, 2, 17])
+    k4, k4s, k4z, v4, v4s, v4z = q4
+    flat = lambda a: a.reshape((-1,) + a.shape[2:])
+    # pair (3 -> 0): K group 0 constant 1.25 -> unit scale, zero clamp(rint(-1.25)) = 0, code rint(1.25) = 1
+    assert flat(k4s)[0, 0, 1] == np.float16(1.0) and flat(k4z)[0, 0, 1] == 0
+    assert np.all(kvq4.unpack_nibbles(flat(k4)[0, 0])[64:] == 0)
+    assert np.all(kvq4.unpack_nibbles(flat(k4)[0, 0])[:64] == 1)
+    assert np.all(flat(v4s)[0] == np.float16(1.0)) and np.all(flat(v4z)[0] == 0)
+    # pairs with -1, 99 (source) or 17 (destination) are skipped
+    for a in q4:
+        fa = flat(a)
+        assert np.all(fa[1:] == (0x55 if a.dtype == np.uint8 else np.float16(7.0)))
