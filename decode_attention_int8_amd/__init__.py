@@ -12,6 +12,7 @@ from .kvq8 import (  # noqa: F401
     kvq4_decode_chunk_tokens,
     kvq4_decode_workspace_size,
     kvq4_quantize_append,
+    kvq4_requantize_q8,
     kvq8_append_decode_attn,
     kvq8_decode_attn,
     kvq8_decode_chunk_tokens,

@@ -99,6 +99,42 @@ __global__ __launch_bounds__(256) void kvq4_quantize_append_kernel(
     }
 }
 
+// Re-quantization of aging int8 tokens into the int4 pool ([P4] Sec. 3.3
+// practical notes): the int8 row's values code * step (one float32
+// multiplication each) go through the write path's group quantizer.  Same
+// lane layout as kvq4_quantize_append_kernel; pair `tok` moves int8 slot
+// src[tok] to int4 slot dst[tok].
+__global__ __launch_bounds__(256) void kvq4_requantize_q8_kernel(
+    uint8_t* __restrict__ kc4, uint8_t* __restrict__ vc4, uint16_t* __restrict__ ks4, uint16_t* __restrict__ kz4,
+    uint16_t* __restrict__ vs4, uint16_t* __restrict__ vz4, long n_slots4, const int8_t* __restrict__ kc8,
+    const int8_t* __restrict__ vc8, const float* __restrict__ ks8, const float* __restrict__ vs8, long n_slots8,
+    int nkv, long n_rows, const int32_t* __restrict__ src, const int32_t* __restrict__ dst) {
+    const int l16 = threadIdx.x & 15;
+    const long row = (long)blockIdx.x * 16 + (threadIdx.x >> 4);
+    if (row >= n_rows) return;                     // whole 16-lane rows leave together
+    const int kind = (int)(row & 1);
+    const long tr = row >> 1;
+    const long tok = tr / nkv;
+    const int kh = (int)(tr - tok * nkv);
+    const long s8 = src[tok], s4 = dst[tok];
+    if (s8 < 0 || s8 >= n_slots8 || s4 < 0 || s4 >= n_slots4) return;
+    const size_t r8 = (size_t)s8 * nkv + kh;
+    const uint2 c = *reinterpret_cast<const uint2*>((kind ? vc8 : kc8) + r8 * kHD + 8 * l16);
+    const float step = (kind ? vs8 : ks8)[r8];
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = sbyte_f(e < 4 ? c.x : c.y, e & 3) * step;
+    uint32_t packed;
+    uint16_t s16, z16;
+    quantize_group8x8(x, packed, s16, z16);
+    const size_t r4 = (size_t)s4 * nkv + kh;
+    *reinterpret_cast<uint32_t*>((kind ? vc4 : kc4) + r4 * (kHD / 2) + 4 * l16) = packed;
+    if ((l16 & 7) == 0) {
+        (kind ? vs4 : ks4)[r4 * 2 + (l16 >> 3)] = s16;
+        (kind ? vz4 : kz4)[r4 * 2 + (l16 >> 3)] = z16;
+    }
+}
+
 }  // namespace kvq
 
 using namespace kvq;
@@ -127,3 +163,24 @@ extern "C" int kvq4_quantize_append(uint8_t* k_cache, uint8_t* v_cache, uint16_t
     return launch_status();
 }
 
+
+extern "C" int kvq4_requantize_q8(uint8_t* k_cache4, uint8_t* v_cache4, uint16_t* k_scale4, uint16_t* k_zero4,
+                                  uint16_t* v_scale4, uint16_t* v_zero4, int n_blocks4, const int8_t* k_cache8,
+                                  const int8_t* v_cache8, const float* k_scale8, const float* v_scale8, int n_blocks8,
+                                  int kv_bs, int nkv, int hd, int n_tokens, const int32_t* src_slots,
+                                  const int32_t* dst_slots, void* stream) {
+    if (hd != kHD || !valid_block_size(kv_bs) || nkv < 1 || n_blocks4 < 1 || n_blocks8 < 1) return KVQ8_ESHAPE;
+    if (n_tokens < 0) return KVQ8_EINVAL;
+    if (n_tokens == 0) return KVQ8_OK;
+    if (!k_cache4 || !v_cache4 || !k_scale4 || !k_zero4 || !v_scale4 || !v_zero4 || !k_cache8 || !v_cache8 ||
+        !k_scale8 || !v_scale8 || !src_slots || !dst_slots)
+        return KVQ8_EINVAL;
+    if (!aligned16(k_cache4) || !aligned16(v_cache4) || !aligned16(k_cache8) || !aligned16(v_cache8))
+        return KVQ8_EINVAL;
+    const long n_rows = (long)n_tokens * nkv * 2;
+    const dim3 grid((unsigned)((n_rows + 15) / 16)), block(256);
+    hipLaunchKernelGGL(kvq4_requantize_q8_kernel, grid, block, 0, static_cast<hipStream_t>(stream), k_cache4,
+                       v_cache4, k_scale4, k_zero4, v_scale4, v_zero4, (long)n_blocks4 * kv_bs, k_cache8, v_cache8,
+                       k_scale8, v_scale8, (long)n_blocks8 * kv_bs, nkv, n_rows, src_slots, dst_slots);
+    return launch_status();
+}

@@ -43,6 +43,8 @@ _SIGNATURES = {
                                   _c_int, _p]),
     "kvq4_quantize_append": (_c_int, [_p, _p, _p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _p, _p, _c_int,
                                       _c_int, _p, _p]),
+    "kvq4_requantize_q8": (_c_int, [_p, _p, _p, _p, _p, _p, _c_int, _p, _p, _p, _p, _c_int,
+                                    _c_int, _c_int, _c_int, _c_int, _p, _p, _p]),
     "kvq4_decode_chunk_tokens": (_c_int, [_c_int, _c_int, _c_int, _c_int]),
     "kvq4_decode_workspace_size": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
     "kvq4_decode_attn": (_c_int, [_p, _p, _c_int, _c_int,
@@ -247,6 +249,29 @@ def kvq4_quantize_append(k_cache, v_cache, k_scale, k_zero, v_scale, v_zero, k_n
         n_blocks, kv_bs, nkv, hd, _ptr(k_new, name="k_new"), _ptr(v_new, name="v_new"), _DTYPES[k_new.dtype],
         k_new.shape[0], _ptr(slots, torch.int32, "slots"), _stream(stream))
     _check(st, "kvq4_quantize_append")
+
+
+def kvq4_requantize_q8(pool4, pool8, src_slots, dst_slots, stream=None):
+    """Move tokens from the int8 pool (k, v, k_scale, v_scale) into the int4
+    pool (k, v, k_scale, k_zero, v_scale, v_zero): pair i takes int8 slot
+    src_slots[i] to int4 slot dst_slots[i] (int32 device tensors)."""
+    k4, v4, k4s, k4z, v4s, v4z = pool4
+    k8, v8, k8s, v8s = pool8
+    n4, kv_bs, nkv, half = k4.shape
+    hd = 2 * half
+    n8 = k8.shape[0]
+    if k8.shape[1:] != (kv_bs, nkv, hd) or v8.shape != k8.shape or v4.shape != k4.shape:
+        raise ValueError("the int8 and int4 pools must share kv_bs and nkv")
+    if src_slots.shape != dst_slots.shape or src_slots.dim() != 1:
+        raise ValueError("src_slots and dst_slots must be [n_tokens]")
+    st = lib().kvq4_requantize_q8(
+        _ptr(k4, torch.uint8, "k4"), _ptr(v4, torch.uint8, "v4"), _ptr(k4s, torch.float16, "k4_scale"),
+        _ptr(k4z, torch.float16, "k4_zero"), _ptr(v4s, torch.float16, "v4_scale"),
+        _ptr(v4z, torch.float16, "v4_zero"), n4, _ptr(k8, torch.int8, "k8"), _ptr(v8, torch.int8, "v8"),
+        _ptr(k8s, torch.float32, "k8_scale"), _ptr(v8s, torch.float32, "v8_scale"), n8, kv_bs, nkv, hd,
+        src_slots.shape[0], _ptr(src_slots, torch.int32, "src_slots"), _ptr(dst_slots, torch.int32, "dst_slots"),
+        _stream(stream))
+    _check(st, "kvq4_requantize_q8")
 
 
 def kvq4_decode_chunk_tokens(batch: int, nkv: int, max_len4: int, max_len8: int) -> int:

@@ -238,6 +238,34 @@ int kvq4_quantize_append(uint8_t* k_cache, uint8_t* v_cache,
                          const void* k_new, const void* v_new, int dtype, int n_tokens,
                          const int32_t* slots, void* stream);
 
+/*
+ * kvq4_requantize_q8 -- move tokens from the int8 pool (the recent window)
+ * into the int4 pool as they age ([P4] Sec. 3.3 practical notes: the oldest
+ * time block is re-quantized from 8-bit to 4-bit as the sequence grows,
+ * off the decode's critical path).
+ *
+ * Pair i reads int8 slot src_slots[i] (block id * kv_bs + offset) of both
+ * the K and the V pool, takes the values code * step (one float32
+ * multiplication each) and writes them to int4 slot dst_slots[i] exactly as
+ * kvq4_quantize_append would write those float32 values.  A pair with either
+ * slot outside its pool is skipped.  The int8 pool is only read, so a
+ * decode may keep using it until the caller switches the tokens' table
+ * entries.
+ *
+ *   k_cache4 .. v_zero4  (device) the int4 pool as in kvq4_quantize_append,
+ *                        written; caches 16-byte aligned
+ *   k_cache8 .. v_scale8 (device) the int8 pool as in kvq8_quantize_append,
+ *                        read; caches 16-byte aligned
+ *   n_blocks4, n_blocks8 blocks in each pool (same kv_bs and nkv)
+ *   src_slots, dst_slots (device) int32 [n_tokens]
+ */
+int kvq4_requantize_q8(uint8_t* k_cache4, uint8_t* v_cache4, uint16_t* k_scale4, uint16_t* k_zero4,
+                       uint16_t* v_scale4, uint16_t* v_zero4, int n_blocks4,
+                       const int8_t* k_cache8, const int8_t* v_cache8,
+                       const float* k_scale8, const float* v_scale8, int n_blocks8,
+                       int kv_bs, int nkv, int hd, int n_tokens,
+                       const int32_t* src_slots, const int32_t* dst_slots, void* stream);
+
 /* Default chunk and workspace size for kvq4_decode_attn (see the kvq8
  * counterparts).  max_len4 / max_len8 bound lens4 / lens8. */
 int kvq4_decode_chunk_tokens(int batch, int nkv, int max_len4, int max_len8);

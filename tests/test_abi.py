@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     lib = K.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -134,3 +134,22 @@ def test_decode4_validation():
     assert _decode4(nq=36, **ws) == ESHAPE            # group of 9
     assert _decode4(**ws, n4=1 << 30) == ESHAPE       # more than 2^32 - 1 rows
     assert _decode4(ws=None, ws_bytes=0) == EWORKSPACE
+
+
+def test_requantize_validation():
+    lib = K.lib()
+    base = [_fake(), _fake(), _fake(), _fake(), _fake(), _fake(), 8, _fake(), _fake(), _fake(), _fake(), 4,
+            16, 4, 128, 10, _fake(), _fake(), None]
+
+    def call(**kw):
+        a = list(base)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return lib.kvq4_requantize_q8(*a)
+    assert call(a15=0) == OK
+    assert call(a14=96) == ESHAPE
+    assert call(a12=12) == ESHAPE
+    assert call(a6=0) == ESHAPE
+    assert call(a15=-1) == EINVAL
+    assert call(a16=None) == EINVAL
+    assert call(a7=_fake(4104)) == EINVAL             # int8 cache not 16-byte aligned

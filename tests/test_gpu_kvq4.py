@@ -121,3 +121,72 @@ def test_q4_only_int8_window_equals_int8_path(K):
     ref = O8.decode_attention_q8(q, c8.kp, c8.ks, c8.vp, c8.vs, bt, lens, bs, SM)
     assert_attn_close(host(o4), ref, "int4 entry, int8 only")
     assert_attn_close(host(o8), ref, "int8 entry")
+
+
+# ----------------------------------------------------------------------------
+# re-quantization of aging int8 tokens into the int4 pool ([P4] Sec. 3.3)
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bs", [8, 16])
+def test_requantize_bit_exact(K, bs):
+    """int8 -> int4 migration equals the oracle bit for bit (codes, binary16
+    scales and zero points), including skipped pairs and groups whose zero
+    point clamps."""
+    import torch
+    r = W.rng(420, bs)
+    nkv, nb8, nb4, n = 4, 24, 20, 150
+    c8 = Q8Cache(nb8, bs, nkv)
+    x = W.per_unit_sigma_normal(r, (nb8 * bs, nkv, 128), 2, 0.2, 5.0)
+    y = W.student_t3_f32(r, (nb8 * bs, nkv, 128), 0.5)
+    x[3, 1] = np.abs(x[3, 1]) + 2               # all above zero
+    x[4, 2, :] = 0.75                           # constant row
+    c8.append(x, y, np.arange(nb8 * bs, dtype=np.int32))
+    p4 = Q4Pool(nb4, bs, nkv)
+    src = r.permutation(nb8 * bs)[:n].astype(np.int32)
+    dst = r.permutation(nb4 * bs)[:n].astype(np.int32)
+    src[5], dst[9], src[11] = -1, nb4 * bs, nb8 * bs + 3   # skipped pairs
+    O4.requantize_q8_to_q4((c8.kp, c8.ks, c8.vp, c8.vs), p4.oracle_pools(), src, dst)
+    K.kvq4_requantize_q8(p4.g, (c8.gk, c8.gv, c8.gks, c8.gvs), dev(src), dev(dst))
+    torch.cuda.synchronize()
+    c8.assert_device_matches_host()
+    p4.assert_same()
+
+
+def test_requantize_time_block_then_decode(K):
+    """The lifecycle of the 128K workload in miniature: a sequence keeps its
+    newest tokens in the int8 window; the oldest 512-token time block moves to
+    the int4 pool (bit-exact against the oracle), the block tables are
+    switched, and the mixed decode over both pools matches the oracle."""
+    import torch
+    r = W.rng(421)
+    nq, nkv, bs, B = 16, 4, 16, 2
+    L4, L8, T = 1024, 1024, 512                     # int4 history, int8 window, time block
+    bt4, nb4 = W.paged_block_tables(r, [L4 + T] * B, bs)
+    bt8, nb8 = W.paged_block_tables(r, [L8] * B, bs)
+    p4 = Q4Pool(nb4, bs, nkv)
+    c8 = Q8Cache(nb8, bs, nkv)
+    for b in range(B):
+        s4 = W.slots_for_positions(bt4, [b] * L4, np.arange(L4), bs)
+        p4.append(K, W.normal_f32(r, (L4, nkv, 128)), W.normal_f32(r, (L4, nkv, 128)), s4)
+        s8 = W.slots_for_positions(bt8, [b] * L8, np.arange(L8), bs)
+        c8.append(W.normal_f32(r, (L8, nkv, 128), 0.7), W.normal_f32(r, (L8, nkv, 128), 1.3), s8)
+    # move window positions [0, T) of each sequence to int4 positions [L4, L4 + T)
+    src = np.concatenate([W.slots_for_positions(bt8, [b] * T, np.arange(T), bs) for b in range(B)]).astype(np.int32)
+    dst = np.concatenate([W.slots_for_positions(bt4, [b] * T, L4 + np.arange(T), bs)
+                          for b in range(B)]).astype(np.int32)
+    O4.requantize_q8_to_q4((c8.kp, c8.ks, c8.vp, c8.vs), p4.oracle_pools(), src, dst)
+    K.kvq4_requantize_q8(p4.g, (c8.gk, c8.gv, c8.gks, c8.gvs), dev(src), dev(dst))
+    torch.cuda.synchronize()
+    p4.assert_same()
+    # the window now starts T tokens later: shift its table by T / bs blocks
+    bt8n = np.full_like(bt8, -1)
+    bt8n[:, :(L8 - T) // bs] = bt8[:, T // bs:L8 // bs]
+    lens4 = np.full(B, L4 + T, np.int32)
+    lens8 = np.full(B, L8 - T, np.int32)
+    q = W.normal_f32(r, (B, nq, 128))
+    ref = O4.decode_attention_mixed(q, p4.oracle_pools(), bt4, lens4, (c8.kp, c8.ks, c8.vp, c8.vs), bt8n, lens8,
+                                    bs, SM)
+    out = torch.empty((B, nq, 128), dtype=torch.float32, device="cuda")
+    K.kvq4_decode_attn(out, dev(q), tuple(p4.g), dev(bt4), dev(lens4), L4 + T, (c8.gk, c8.gv, c8.gks, c8.gvs),
+                       dev(bt8n), dev(lens8), L8 - T, SM)
+    assert_attn_close(host(out), ref, "after migration")
