@@ -76,6 +76,8 @@ def parse():
     p.add_argument("--ctx", type=int, default=8192)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    p.add_argument("--workloads", action="store_true",
+                   help="instead of the step benchmark, time every other workload of the hot path (one JSON line each)")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB (for scaling memory counters) and exit")
     return p.parse_args()
@@ -155,10 +157,173 @@ def cpu_baseline(args, nq, nkv, bs, L, bytes_per_layer):
                       f"heads), {el:.1f} s single-threaded numpy; ms/layer {1e3 * el / layers:.1f}"}
 
 
+def time_calls(torch, fn, iters, warmup=3, graph=False):
+    """Average microseconds per call of fn() on the current stream, HIP events
+    around `iters` back-to-back calls (captured as one graph when `graph`)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(warmup):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(iters):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        run = g.replay
+    else:
+        def run():
+            for _ in range(iters):
+                fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    run()
+    e1.record()
+    torch.cuda.synchronize()
+    return 1e3 * e0.elapsed_time(e1) / iters
+
+
+def report(name, desc, nbytes, us, **extra):
+    gbs = nbytes / (us * 1e-6) / 1e9
+    line = {"workload": name, "desc": desc, "algorithmic_bytes": int(nbytes), "us_per_call": round(us, 2),
+            "GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    line.update(extra)
+    print(json.dumps(line), flush=True)
+
+
+def run_workloads():
+    """Every workload of the hot path besides the step benchmark, timed on one
+    GPU: the pages' unit experiment, the batch-32 long-context layer, the 64K
+    write path and the decode over it, the int4 128K mixed decode, and the
+    int8 -> int4 re-quantization of aging time blocks.  Inputs follow the
+    recipes of `workloads` (generated on the GPU, quantized through the
+    library's write paths)."""
+    import torch
+
+    import decode_attention_int8_amd as K
+    import workloads as W
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    sm = 1.0 / math.sqrt(128)
+
+    def q8_pool(nb, bs, nkv):
+        shp = (nb, bs, nkv, 128)
+        return [torch.zeros(shp, dtype=torch.int8, device="cuda"), torch.zeros(shp, dtype=torch.int8, device="cuda"),
+                torch.zeros(shp[:3], dtype=torch.float32, device="cuda"),
+                torch.zeros(shp[:3], dtype=torch.float32, device="cuda")]
+
+    def q4_pool(nb, bs, nkv):
+        shp = (nb, bs, nkv)
+        return [torch.zeros(shp + (64,), dtype=torch.uint8, device="cuda"),
+                torch.zeros(shp + (64,), dtype=torch.uint8, device="cuda")] + \
+               [torch.zeros(shp + (2,), dtype=torch.float16, device="cuda") for _ in range(4)]
+
+    # unit experiment: 1 / 1 heads, 256 tokens (launch-bound)
+    q, k, v = W.unit_experiment(0)
+    bt, nb = W.paged_block_tables(None, [256], 16)
+    p = q8_pool(nb, 16, 1)
+    K.kvq8_quantize_append(*p, dev(k[:, None]), dev(v[:, None]), dev(np.arange(256, dtype=np.int32)))
+    out = torch.empty((1, 1, 128), device="cuda")
+    qd, btd, ld = dev(q[None, None]), dev(bt), dev(np.array([256], np.int32))
+    ws = K.alloc_workspace(K.kvq8_decode_workspace_size(1, 1, 1, 256), "cuda")
+    us = time_calls(torch, lambda: K.kvq8_decode_attn(out, qd, *p, btd, ld, 256, sm, 0, ws), 200, graph=True)
+    report("unit_256", "decode, 1 query / 1 kv head, 256 tokens (graph replay)", 256 * 264, us)
+    del p
+
+    # batch-32 Qwen-8B-shaped layer: lengths U[1024, 32768], K, V = 0.5 Student-t(3)
+    cfg = W.QWEN8B_B32
+    lens = W.qwen8b_lengths(0)
+    B, nq, nkv, bs = cfg["batch"], cfg["nq"], cfg["nkv"], cfg["kv_bs"]
+    bt, nb = W.paged_block_tables(W.rng(3, 0, 1), lens, bs)
+    p = q8_pool(nb, bs, nkv)
+    for b in range(B):
+        kk = W.torch_student_t3((int(lens[b]), nkv, 128), "cuda", (3, 0, b, 0))
+        vv = W.torch_student_t3((int(lens[b]), nkv, 128), "cuda", (3, 0, b, 1))
+        K.kvq8_quantize_append(*p, kk, vv, dev(W.slots_for_positions(bt, [b] * int(lens[b]), np.arange(lens[b]), bs)))
+        del kk, vv
+    qd = W.torch_normal((B, nq, 128), "cuda", (3, 0, 99))
+    out = torch.empty((B, nq, 128), device="cuda")
+    btd, ld, L = dev(bt), dev(lens), int(lens.max())
+    ch = K.kvq8_decode_chunk_tokens(B, nkv, L)
+    ws = K.alloc_workspace(K.kvq8_decode_workspace_size(B, nq, nkv, L), "cuda")
+    us = time_calls(torch, lambda: K.kvq8_decode_attn(out, qd, *p, btd, ld, L, sm, 0, ws), 20)
+    report("qwen8b_b32", f"decode layer, batch 32 x 32 / 8 heads, lengths U[1024, 32768] (sum {int(lens.sum())})",
+           int(lens.sum()) * nkv * 264, us, chunk_tokens=ch)
+    del p
+
+    # 64K tokens written from bf16 (1% x20 outliers), then a GQA-4 decode over them
+    cfg = W.APPEND_64K
+    n, nq, nkv, bs = cfg["n_tok"], cfg["nq"], cfg["nkv"], cfg["kv_bs"]
+    bt, nb = W.paged_block_tables(W.rng(4, 0, 1), [n], bs)
+    p = q8_pool(nb, bs, nkv)
+    kk = W.torch_outlier_normal_bf16((n, nkv, 128), "cuda", (4, 0, 0))
+    vv = W.torch_outlier_normal_bf16((n, nkv, 128), "cuda", (4, 0, 1))
+    slots = dev(W.slots_for_positions(bt, [0] * n, np.arange(n), bs))
+    us = time_calls(torch, lambda: K.kvq8_quantize_append(*p, kk, vv, slots), 20)
+    report("append_64k", "write path, 65536 tokens x 8 kv heads from bf16", n * nkv * (2 * 128 * 2 + 2 * 132), us)
+    qd = W.torch_normal((1, nq, 128), "cuda", (4, 0, 2))
+    out = torch.empty((1, nq, 128), device="cuda")
+    btd, ld = dev(bt), dev(np.array([n], np.int32))
+    ch = K.kvq8_decode_chunk_tokens(1, nkv, n)
+    ws = K.alloc_workspace(K.kvq8_decode_workspace_size(1, nq, nkv, n), "cuda")
+    us = time_calls(torch, lambda: K.kvq8_decode_attn(out, qd, *p, btd, ld, n, sm, 0, ws), 50)
+    report("decode_64k", "decode, 1 sequence x 32 / 8 heads over the 65536 written tokens", n * nkv * 264, us,
+           chunk_tokens=ch)
+    del p, kk, vv
+
+    # int4 group cache, 128K tokens (last 2048 int8), batch 4 x 32 / 4 heads
+    cfg = W.Q4_128K
+    B, nq, nkv, L, win, bs = cfg["batch"], cfg["nq"], cfg["nkv"], cfg["L"], cfg["window"], cfg["kv_bs"]
+    n4, n8 = L - win, win
+    bt4, nb4 = W.paged_block_tables(W.rng(5, 0, 1), [n4] * B, bs)
+    bt8, nb8 = W.paged_block_tables(W.rng(5, 0, 2), [n8] * B, bs)
+    p4, p8 = q4_pool(nb4, bs, nkv), q8_pool(nb8, bs, nkv)
+    sig = W.rng(5, 0, 3).uniform(0.2, 5.0, size=(B, nkv, 2))
+    for b in range(B):
+        sk = torch.tensor(sig[b, :, 0], dtype=torch.float32, device="cuda")[None, :, None]
+        sv = torch.tensor(sig[b, :, 1], dtype=torch.float32, device="cuda")[None, :, None]
+        kk = W.torch_normal((L, nkv, 128), "cuda", (5, 0, b, 0)) * sk
+        vv = W.torch_normal((L, nkv, 128), "cuda", (5, 0, b, 1)) * sv
+        K.kvq4_quantize_append(*p4, kk[:n4], vv[:n4], dev(W.slots_for_positions(bt4, [b] * n4, np.arange(n4), bs)))
+        K.kvq8_quantize_append(*p8, kk[n4:], vv[n4:], dev(W.slots_for_positions(bt8, [b] * n8, np.arange(n8), bs)))
+        del kk, vv
+    qd = W.torch_normal((B, nq, 128), "cuda", (5, 0, 99))
+    out = torch.empty((B, nq, 128), device="cuda")
+    bt4d, l4 = dev(bt4), dev(np.full(B, n4, np.int32))
+    bt8d, l8 = dev(bt8), dev(np.full(B, n8, np.int32))
+    ch = K.kvq4_decode_chunk_tokens(B, nkv, n4, n8)
+    ws = K.alloc_workspace(K.kvq4_decode_workspace_size(B, nq, nkv, n4, n8), "cuda")
+    us = time_calls(torch, lambda: K.kvq4_decode_attn(out, qd, p4, bt4d, l4, n4, p8, bt8d, l8, n8, sm, 0, ws), 20)
+    report("q4_128k", "mixed decode, batch 4 x 32 / 4 heads, 129024 int4 + 2048 int8 tokens",
+           B * nkv * (n4 * 144 + n8 * 264), us, chunk_tokens=ch)
+
+    # re-quantization of the window's oldest 512-token time block of every
+    # sequence into the int4 pool (into the int4 pool's first 512 slots per
+    # sequence: the timing, not the cache's meaning, is what is measured here)
+    T = 512
+    src = dev(np.concatenate([W.slots_for_positions(bt8, [b] * T, np.arange(T), bs) for b in range(B)]))
+    dst = dev(np.concatenate([W.slots_for_positions(bt4, [b] * T, np.arange(T), bs) for b in range(B)]))
+    us = time_calls(torch, lambda: K.kvq4_requantize_q8(p4, p8, src, dst), 50, graph=True)
+    report("requant_block", "int8 -> int4 re-quantization of one 512-token time block x 4 sequences x 4 kv heads "
+           "(graph replay)", B * T * nkv * (264 + 144), us)
+    n_all = B * n8
+    src = dev(np.concatenate([W.slots_for_positions(bt8, [b] * n8, np.arange(n8), bs) for b in range(B)]))
+    dst = dev(np.concatenate([W.slots_for_positions(bt4, [b] * n8, np.arange(n8), bs) for b in range(B)]))
+    us = time_calls(torch, lambda: K.kvq4_requantize_q8(p4, p8, src, dst), 50)
+    report("requant_window", "int8 -> int4 re-quantization of the whole 2048-token window x 4 sequences",
+           n_all * nkv * (264 + 144), us)
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
+        return
+    if args.workloads:
+        run_workloads()
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build has no multi-GPU path)",

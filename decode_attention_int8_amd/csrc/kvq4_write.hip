@@ -2,8 +2,9 @@
 // Sec. 5.2 checklist).
 //
 // kvq4_quantize_append_kernel: one (token, kv-head, K-or-V) row per 16 lanes,
-// 8 values per lane; each 64-value group is one aligned 8-lane half row, so
-// its max / min need only quad and half-mirror DPP steps.
+// 8 values per lane, 4 rows per 16-lane group (loads first); each 64-value
+// group is one aligned 8-lane half row, so its max / min need only quad and
+// half-mirror DPP steps.
 #include "kvq8.h"
 #include "kvq_device.h"
 #include "kvq_host.h"
@@ -72,26 +73,13 @@ __device__ __forceinline__ void quantize_group8x8(const float (&x)[8], uint32_t&
     packed = w;
 }
 
-template <int DT>
-__global__ __launch_bounds__(256) void kvq4_quantize_append_kernel(
-    uint8_t* __restrict__ kc, uint8_t* __restrict__ vc, uint16_t* __restrict__ ks, uint16_t* __restrict__ kz,
-    uint16_t* __restrict__ vs, uint16_t* __restrict__ vz, long n_slots, int nkv, const void* __restrict__ k_new,
-    const void* __restrict__ v_new, long n_rows, const int32_t* __restrict__ slots) {
-    const int l16 = threadIdx.x & 15;
-    const long row = (long)blockIdx.x * 16 + (threadIdx.x >> 4);
-    if (row >= n_rows) return;                     // whole 16-lane rows leave together
-    const int kind = (int)(row & 1);
-    const long tr = row >> 1;
-    const long tok = tr / nkv;
-    const int kh = (int)(tr - tok * nkv);
-    float x[8];
-    load8_any<DT>(kind ? v_new : k_new, (size_t)tr * kHD + 8 * l16, x);
-    uint32_t packed;
-    uint16_t s16, z16;
-    quantize_group8x8(x, packed, s16, z16);
-    const long slot = slots[tok];
-    if (slot < 0 || slot >= n_slots) return;
-    const size_t dst = (size_t)slot * nkv + kh;
+constexpr int kRowsPerGroup = 4;            // rows per 16-lane group, loads first
+constexpr int kRowsPerBlock = 16 * kRowsPerGroup;
+
+__device__ __forceinline__ void store_q4_row(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
+                                             uint16_t* __restrict__ ks, uint16_t* __restrict__ kz,
+                                             uint16_t* __restrict__ vs, uint16_t* __restrict__ vz, int kind,
+                                             size_t dst, int l16, uint32_t packed, uint16_t s16, uint16_t z16) {
     *reinterpret_cast<uint32_t*>((kind ? vc : kc) + dst * (kHD / 2) + 4 * l16) = packed;
     if ((l16 & 7) == 0) {
         (kind ? vs : ks)[dst * 2 + (l16 >> 3)] = s16;
@@ -99,39 +87,84 @@ __global__ __launch_bounds__(256) void kvq4_quantize_append_kernel(
     }
 }
 
+template <int DT>
+__global__ __launch_bounds__(256) void kvq4_quantize_append_kernel(
+    uint8_t* __restrict__ kc, uint8_t* __restrict__ vc, uint16_t* __restrict__ ks, uint16_t* __restrict__ kz,
+    uint16_t* __restrict__ vs, uint16_t* __restrict__ vz, long n_slots, int nkv, const void* __restrict__ k_new,
+    const void* __restrict__ v_new, long n_rows, const int32_t* __restrict__ slots) {
+    const int l16 = threadIdx.x & 15;
+    float x[kRowsPerGroup][8];
+    long slot[kRowsPerGroup];
+#pragma unroll
+    for (int k = 0; k < kRowsPerGroup; ++k) {
+        const long row = min((long)blockIdx.x * kRowsPerBlock + k * 16 + (threadIdx.x >> 4), n_rows - 1);
+        const long tr = row >> 1;
+        load8_any<DT>((row & 1) ? v_new : k_new, (size_t)tr * kHD + 8 * l16, x[k]);
+        slot[k] = slots[tr / nkv];
+    }
+#pragma unroll
+    for (int k = 0; k < kRowsPerGroup; ++k) {
+        const long row = (long)blockIdx.x * kRowsPerBlock + k * 16 + (threadIdx.x >> 4);
+        uint32_t packed;
+        uint16_t s16, z16;
+        quantize_group8x8(x[k], packed, s16, z16);
+        if (row >= n_rows || slot[k] < 0 || slot[k] >= n_slots) continue;   // uniform per 16-lane row
+        const long tr = row >> 1;
+        const long tok = tr / nkv;
+        store_q4_row(kc, vc, ks, kz, vs, vz, (int)(row & 1), (size_t)slot[k] * nkv + (size_t)(tr - tok * nkv), l16,
+                     packed, s16, z16);
+    }
+}
+
 // Re-quantization of aging int8 tokens into the int4 pool ([P4] Sec. 3.3
 // practical notes): the int8 row's values code * step (one float32
 // multiplication each) go through the write path's group quantizer.  Same
 // lane layout as kvq4_quantize_append_kernel; pair `tok` moves int8 slot
-// src[tok] to int4 slot dst[tok].
+// src[tok] to int4 slot dst[tok].  R rows per 16-lane group (loads first):
+// 4 for large moves, 1 when a move is small and latency decides.
+template <int R>
 __global__ __launch_bounds__(256) void kvq4_requantize_q8_kernel(
     uint8_t* __restrict__ kc4, uint8_t* __restrict__ vc4, uint16_t* __restrict__ ks4, uint16_t* __restrict__ kz4,
     uint16_t* __restrict__ vs4, uint16_t* __restrict__ vz4, long n_slots4, const int8_t* __restrict__ kc8,
     const int8_t* __restrict__ vc8, const float* __restrict__ ks8, const float* __restrict__ vs8, long n_slots8,
     int nkv, long n_rows, const int32_t* __restrict__ src, const int32_t* __restrict__ dst) {
     const int l16 = threadIdx.x & 15;
-    const long row = (long)blockIdx.x * 16 + (threadIdx.x >> 4);
-    if (row >= n_rows) return;                     // whole 16-lane rows leave together
-    const int kind = (int)(row & 1);
-    const long tr = row >> 1;
-    const long tok = tr / nkv;
-    const int kh = (int)(tr - tok * nkv);
-    const long s8 = src[tok], s4 = dst[tok];
-    if (s8 < 0 || s8 >= n_slots8 || s4 < 0 || s4 >= n_slots4) return;
-    const size_t r8 = (size_t)s8 * nkv + kh;
-    const uint2 c = *reinterpret_cast<const uint2*>((kind ? vc8 : kc8) + r8 * kHD + 8 * l16);
-    const float step = (kind ? vs8 : ks8)[r8];
-    float x[8];
+    // the slot pairs first, then every row's codes and step
+    long s8[R], s4[R];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = sbyte_f(e < 4 ? c.x : c.y, e & 3) * step;
-    uint32_t packed;
-    uint16_t s16, z16;
-    quantize_group8x8(x, packed, s16, z16);
-    const size_t r4 = (size_t)s4 * nkv + kh;
-    *reinterpret_cast<uint32_t*>((kind ? vc4 : kc4) + r4 * (kHD / 2) + 4 * l16) = packed;
-    if ((l16 & 7) == 0) {
-        (kind ? vs4 : ks4)[r4 * 2 + (l16 >> 3)] = s16;
-        (kind ? vz4 : kz4)[r4 * 2 + (l16 >> 3)] = z16;
+    for (int k = 0; k < R; ++k) {
+        const long row = min((long)blockIdx.x * (16 * R) + k * 16 + (threadIdx.x >> 4), n_rows - 1);
+        const long tok = (row >> 1) / nkv;
+        s8[k] = src[tok];
+        s4[k] = dst[tok];
+    }
+    uint2 c[R];
+    float step[R];
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+        const long row = min((long)blockIdx.x * (16 * R) + k * 16 + (threadIdx.x >> 4), n_rows - 1);
+        const long tr = row >> 1;
+        const long tok = tr / nkv;
+        // an invalid source reads slot 0 (in bounds) and is not stored
+        const long sv = (s8[k] >= 0 && s8[k] < n_slots8) ? s8[k] : 0;
+        const size_t r8 = (size_t)sv * nkv + (size_t)(tr - tok * nkv);
+        c[k] = *reinterpret_cast<const uint2*>(((row & 1) ? vc8 : kc8) + r8 * kHD + 8 * l16);
+        step[k] = ((row & 1) ? vs8 : ks8)[r8];
+    }
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+        const long row = (long)blockIdx.x * (16 * R) + k * 16 + (threadIdx.x >> 4);
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = sbyte_f(e < 4 ? c[k].x : c[k].y, e & 3) * step[k];
+        uint32_t packed;
+        uint16_t s16, z16;
+        quantize_group8x8(x, packed, s16, z16);
+        if (row >= n_rows || s8[k] < 0 || s8[k] >= n_slots8 || s4[k] < 0 || s4[k] >= n_slots4) continue;
+        const long tr = row >> 1;
+        const long tok = tr / nkv;
+        store_q4_row(kc4, vc4, ks4, kz4, vs4, vz4, (int)(row & 1), (size_t)s4[k] * nkv + (size_t)(tr - tok * nkv),
+                     l16, packed, s16, z16);
     }
 }
 
@@ -151,7 +184,7 @@ extern "C" int kvq4_quantize_append(uint8_t* k_cache, uint8_t* v_cache, uint16_t
     if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache)) return KVQ8_EINVAL;
     const long n_rows = (long)n_tokens * nkv * 2;
     const long n_slots = (long)n_blocks * kv_bs;
-    const dim3 grid((unsigned)((n_rows + 15) / 16)), block(256);
+    const dim3 grid((unsigned)((n_rows + kRowsPerBlock - 1) / kRowsPerBlock)), block(256);
     hipStream_t s = static_cast<hipStream_t>(stream);
 #define KVQ4_LAUNCH(DT)                                                                                     \
     hipLaunchKernelGGL(kvq4_quantize_append_kernel<DT>, grid, block, 0, s, k_cache, v_cache, k_scale, k_zero, \
@@ -178,9 +211,15 @@ extern "C" int kvq4_requantize_q8(uint8_t* k_cache4, uint8_t* v_cache4, uint16_t
     if (!aligned16(k_cache4) || !aligned16(v_cache4) || !aligned16(k_cache8) || !aligned16(v_cache8))
         return KVQ8_EINVAL;
     const long n_rows = (long)n_tokens * nkv * 2;
-    const dim3 grid((unsigned)((n_rows + 15) / 16)), block(256);
-    hipLaunchKernelGGL(kvq4_requantize_q8_kernel, grid, block, 0, static_cast<hipStream_t>(stream), k_cache4,
-                       v_cache4, k_scale4, k_zero4, v_scale4, v_zero4, (long)n_blocks4 * kv_bs, k_cache8, v_cache8,
-                       k_scale8, v_scale8, (long)n_blocks8 * kv_bs, nkv, n_rows, src_slots, dst_slots);
+    const long n_slots4 = (long)n_blocks4 * kv_bs, n_slots8 = (long)n_blocks8 * kv_bs;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (n_rows >= 65536)
+        hipLaunchKernelGGL(kvq4_requantize_q8_kernel<4>, dim3((unsigned)((n_rows + 63) / 64)), dim3(256), 0, s,
+                           k_cache4, v_cache4, k_scale4, k_zero4, v_scale4, v_zero4, n_slots4, k_cache8, v_cache8,
+                           k_scale8, v_scale8, n_slots8, nkv, n_rows, src_slots, dst_slots);
+    else
+        hipLaunchKernelGGL(kvq4_requantize_q8_kernel<1>, dim3((unsigned)((n_rows + 15) / 16)), dim3(256), 0, s,
+                           k_cache4, v_cache4, k_scale4, k_zero4, v_scale4, v_zero4, n_slots4, k_cache8, v_cache8,
+                           k_scale8, v_scale8, n_slots8, nkv, n_rows, src_slots, dst_slots);
     return launch_status();
 }

@@ -1,8 +1,8 @@
 // Write path of the int8 KV cache and the query-quantization export.
 //
 // kvq8_quantize_append_kernel: one (token, kv-head, K-or-V) row of 128 values
-// per 16 consecutive lanes, 8 values per lane, so a 256-thread workgroup
-// quantizes 16 rows.  Each lane reads 32 B (float32) or 16 B (bf16 / f16) of
+// per 16 consecutive lanes, 8 values per lane; each 16-lane group handles 4
+// rows, so a 256-thread workgroup quantizes 64 rows.  Each lane reads 32 B (float32) or 16 B (bf16 / f16) of
 // its row and writes 8 B of codes: fully coalesced 128-B row stores into the
 // paged cache ([P2] Sec. 2 write path; rule of [P1] Sec. 2).
 #include "kvq8.h"
@@ -34,29 +34,42 @@ __device__ __forceinline__ void load8(const void* base, size_t elem_off, float (
     }
 }
 
+// Rows per 16-lane group: all of a group's loads go out before it quantizes,
+// so each wave keeps kRowsPerGroup x 4 rows in flight.
+constexpr int kRowsPerGroup = 4;
+constexpr int kRowsPerBlock = 16 * kRowsPerGroup;
+
 template <int DT>
 __global__ __launch_bounds__(256) void kvq8_quantize_append_kernel(
     int8_t* __restrict__ kc, int8_t* __restrict__ vc, float* __restrict__ ks, float* __restrict__ vs,
     long n_slots, int nkv, const void* __restrict__ k_new, const void* __restrict__ v_new,
     long n_rows, const int32_t* __restrict__ slots) {
     const int l16 = threadIdx.x & 15;
-    const long row = (long)blockIdx.x * 16 + (threadIdx.x >> 4);
-    if (row >= n_rows) return;                     // whole 16-lane rows leave together
-    const int kind = (int)(row & 1);               // 0 = K, 1 = V
-    const long tr = row >> 1;                      // token * nkv + kv-head
-    const long tok = tr / nkv;
-    const int kh = (int)(tr - tok * nkv);
-    float x[8];
-    load8<DT>(kind ? v_new : k_new, (size_t)tr * kHD + 8 * l16, x);
-    uint32_t lo, hi;
-    float d;
-    quantize_row16x8(x, lo, hi, d);
-    const long slot = slots[tok];
-    if (slot < 0 || slot >= n_slots) return;
-    const size_t dst = ((size_t)slot * nkv + kh);
-    int8_t* cache = kind ? vc : kc;
-    *reinterpret_cast<uint2*>(cache + dst * kHD + 8 * l16) = make_uint2(lo, hi);
-    if (l16 == 0) (kind ? vs : ks)[dst] = d;
+    float x[kRowsPerGroup][8];
+    long slot[kRowsPerGroup];
+    // rows past the end load the last row again and store nothing
+#pragma unroll
+    for (int k = 0; k < kRowsPerGroup; ++k) {
+        const long row = min((long)blockIdx.x * kRowsPerBlock + k * 16 + (threadIdx.x >> 4), n_rows - 1);
+        const int kind = (int)(row & 1);           // 0 = K, 1 = V
+        const long tr = row >> 1;                  // token * nkv + kv-head
+        load8<DT>(kind ? v_new : k_new, (size_t)tr * kHD + 8 * l16, x[k]);
+        slot[k] = slots[tr / nkv];
+    }
+#pragma unroll
+    for (int k = 0; k < kRowsPerGroup; ++k) {
+        const long row = (long)blockIdx.x * kRowsPerBlock + k * 16 + (threadIdx.x >> 4);
+        uint32_t lo, hi;
+        float d;
+        quantize_row16x8(x[k], lo, hi, d);         // every lane of the row takes part (DPP)
+        if (row >= n_rows || slot[k] < 0 || slot[k] >= n_slots) continue;   // uniform per 16-lane row
+        const int kind = (int)(row & 1);
+        const long tr = row >> 1;
+        const long tok = tr / nkv;
+        const size_t dst = (size_t)slot[k] * nkv + (size_t)(tr - tok * nkv);
+        *reinterpret_cast<uint2*>((kind ? vc : kc) + dst * kHD + 8 * l16) = make_uint2(lo, hi);
+        if (l16 == 0) (kind ? vs : ks)[dst] = d;
+    }
 }
 
 // One 8-lane group per query vector; lane j quantizes values 16j .. 16j+15.
@@ -93,7 +106,7 @@ extern "C" int kvq8_quantize_append(int8_t* k_cache, int8_t* v_cache, float* k_s
     if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache)) return KVQ8_EINVAL;
     const long n_rows = (long)n_tokens * nkv * 2;
     const long n_slots = (long)n_blocks * kv_bs;
-    const dim3 grid((unsigned)((n_rows + 15) / 16)), block(256);
+    const dim3 grid((unsigned)((n_rows + kRowsPerBlock - 1) / kRowsPerBlock)), block(256);
     hipStream_t s = static_cast<hipStream_t>(stream);
     switch (dtype) {
         case KVQ8_F32:

@@ -61,7 +61,8 @@ using namespace kvq;
 
 extern "C" int kvq8_decode_chunk_tokens(int batch, int nkv, int max_ctx_len) {
     if (batch < 0 || nkv < 1 || max_ctx_len < 0) return 0;
-    return default_tiles_per_wave(batch, (long)batch * nkv, max_ctx_len) * kChunkUnit;
+    // batches of varying lengths balance better with shorter work items
+    return default_tiles_per_wave((long)batch * nkv, max_ctx_len, batch <= 2 ? 8 : 4) * kChunkUnit;
 }
 
 static int resolve_chunk8(int batch, int nkv, int max_ctx_len, int chunk) {
@@ -187,7 +188,8 @@ extern "C" int kvq8_qk_partials(int32_t* partials, const float* q, int batch, in
 
 extern "C" int kvq4_decode_chunk_tokens(int batch, int nkv, int max_len4, int max_len8) {
     if (batch < 0 || nkv < 1 || max_len4 < 0 || max_len8 < 0) return 0;
-    return default_tiles_per_wave(batch, (long)batch * nkv, (long)max_len4 + max_len8) * kChunkUnit;
+    // the int4 kernel at GQA > 4 runs one workgroup per CU: long work items
+    return default_tiles_per_wave((long)batch * nkv, (long)max_len4 + max_len8, 8) * kChunkUnit;
 }
 
 static int resolve_chunk4(int batch, int nkv, int max_len4, int max_len8, int chunk) {

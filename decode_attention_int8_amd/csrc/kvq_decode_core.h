@@ -223,14 +223,11 @@ __global__ __launch_bounds__(kMergeThreads) void kvq_merge_kernel(float* __restr
 // ----------------------------------------------------------------------------
 
 // Tokens per chunk: the largest power-of-two multiple of 256 that still gives
-// at least 256 workgroups (one per CU), capped at 2048 for one or two
-// sequences and at 1024 for batches (whose lengths vary, so shorter
-// workgroups balance better).  `units` = sequences x kv-heads, `max_len` the
-// longest region.
-inline int default_tiles_per_wave(long batch, long units, long max_len) {
-    const int cap = batch <= 2 ? 8 : 4;
+// at least 256 workgroups (one per CU), capped at `max_tpw` x 256 tokens.
+// `units` = sequences x kv-heads, `max_len` the longest region.
+inline int default_tiles_per_wave(long units, long max_len, int max_tpw) {
     int tpw = 1;
-    while (tpw < cap) {
+    while (tpw < max_tpw) {
         const long next = (long)kChunkUnit * tpw * 2;
         if (units * ((max_len + next - 1) / next) < 256) break;
         tpw *= 2;

@@ -190,3 +190,24 @@ def test_requantize_time_block_then_decode(K):
     K.kvq4_decode_attn(out, dev(q), tuple(p4.g), dev(bt4), dev(lens4), L4 + T, (c8.gk, c8.gv, c8.gks, c8.gvs),
                        dev(bt8n), dev(lens8), L8 - T, SM)
     assert_attn_close(host(out), ref, "after migration")
+
+
+def test_requantize_large_bit_exact(K):
+    """A move above 65536 rows (the kernel's four-rows-per-group form), with a
+    ragged tail of rows and skipped pairs."""
+    import torch
+    r = W.rng(422)
+    nkv, bs, n = 4, 16, 8195                        # 65560 rows: not a multiple of the 64-row workgroup
+    nb8, nb4 = 540, 560
+    c8 = Q8Cache(nb8, bs, nkv)
+    x = W.per_unit_sigma_normal(r, (nb8 * bs, nkv, 128), 2, 0.2, 5.0)
+    y = W.normal_f32(r, (nb8 * bs, nkv, 128), 0.3)
+    c8.append(x, y, np.arange(nb8 * bs, dtype=np.int32))
+    p4 = Q4Pool(nb4, bs, nkv)
+    src = r.permutation(nb8 * bs)[:n].astype(np.int32)
+    dst = r.permutation(nb4 * bs)[:n].astype(np.int32)
+    src[17], dst[4000], src[n - 1] = -5, -1, nb8 * bs
+    O4.requantize_q8_to_q4((c8.kp, c8.ks, c8.vp, c8.vs), p4.oracle_pools(), src, dst)
+    K.kvq4_requantize_q8(p4.g, (c8.gk, c8.gv, c8.gks, c8.gvs), dev(src), dev(dst))
+    torch.cuda.synchronize()
+    p4.assert_same()
