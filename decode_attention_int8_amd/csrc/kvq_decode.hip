@@ -30,7 +30,7 @@ __global__ __launch_bounds__(kWGThreads) void kvq8_qk_partials_kernel(DecodeArgs
     const int raw = mtile_raw(a.r8, btb, base, a.log2_bs, lane);
     const LaneOff lo = lane_offsets(a, lane);
     MTile T;
-    mtile_issue<BS8, true>(a, raw, base, kh, lane, lo, T);
+    mtile_issue<BS8, kIssueKeys>(a, raw, base, kh, lane, lo, T);
     quantize_q4(qx, G, qsm);
     lds_barrier();
     const MQuery Q = load_q_operand(qsm, G, g, m);

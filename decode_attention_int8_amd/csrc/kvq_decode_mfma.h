@@ -128,22 +128,36 @@ __device__ __forceinline__ LaneOff lane_offsets(const DecodeArgs& a, int lane) {
     return o;
 }
 
-// Issue all loads of a tile.  Rows of invalid blocks read slot 0 of the pool
+// Which loads of a tile to issue: keys, values, steps.  A tile walk issues
+// keys and steps of the next tile before the current tile's Q.K and its
+// values after it, when the current keys are dead, so that two full tiles
+// are never held in registers at once.
+enum : int { kIssueKeys = 1, kIssueValues = 2, kIssueSteps = 4, kIssueAll = 7 };
+
+// Issue loads of a tile.  Rows of invalid blocks read slot 0 of the pool
 // (in bounds) and are masked when the tile is computed.  Row indices (in head
-// rows of 128 B) fit in 32 bits: the host rejects larger pools.
+// rows of 128 B) fit in 32 bits: the host rejects larger pools.  A call
+// without kIssueKeys takes the block ids from T.id, set by an earlier call
+// for the same tile.
 //
 // With blocks of 16 or more slots a 16-token group lies in one block, so its
 // base address is wave-uniform and the lane parts are fixed (scalar base +
 // 32-bit lane offset).  With 8-slot blocks each lane picks one of the two
 // blocks of its group.
-template <bool BS8, bool K_ONLY = false>
+template <bool BS8, int PARTS = kIssueAll>
 __device__ __forceinline__ void mtile_issue(const DecodeArgs& a, int raw, int base, int kh, int lane,
                                             const LaneOff& lo, MTile& T) {
+    constexpr bool KEYS = PARTS & kIssueKeys, VALUES = PARTS & kIssueValues, STEPS = PARTS & kIssueSteps;
     const int g = lane >> 4;
     const int m = lane & 15;
     const uint32_t bs_mask = (1u << a.log2_bs) - 1;
-    const int id = (raw >= 0 && raw < a.r8.n_blocks) ? raw : -1;
-    T.id = id;
+    int id;
+    if constexpr (KEYS) {
+        id = (raw >= 0 && raw < a.r8.n_blocks) ? raw : -1;
+        T.id = id;
+    } else {
+        id = T.id;
+    }
     const uint32_t nkv = (uint32_t)a.nkv;
     // row of the first token of 8-token group i (wave-uniform); each value is
     // computed where it is used so that a per-lane choice between two groups
@@ -156,21 +170,25 @@ __device__ __forceinline__ void mtile_issue(const DecodeArgs& a, int raw, int ba
     for (int v = 0; v < 4; ++v) {
         if constexpr (!BS8) {
             const uint32_t u = grp(2 * v);
-            const int8_t* pk = a.kc + (size_t)u * kHD;
-            const int8_t* pv = a.vc + (size_t)u * kHD;
-            T.k[v][0] = *reinterpret_cast<const v4u_t*>(pk + lo.k);
-            T.k[v][1] = *reinterpret_cast<const v4u_t*>(pk + lo.k + 64);
-            if constexpr (!K_ONLY) {
+            if constexpr (KEYS) {
+                const int8_t* pk = a.kc + (size_t)u * kHD;
+                T.k[v][0] = *reinterpret_cast<const v4u_t*>(pk + lo.k);
+                T.k[v][1] = *reinterpret_cast<const v4u_t*>(pk + lo.k + 64);
+            }
+            if constexpr (VALUES) {
+                const int8_t* pv = a.vc + (size_t)u * kHD;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) T.v[v][e] = *reinterpret_cast<const v2u_t*>(pv + lo.v[e]);
             }
         } else {
             const uint32_t u0 = grp(2 * v), u1 = grp(2 * v + 1);
-            const uint32_t rk = ((m & 8) ? u1 : u0) + (uint32_t)(m & 7) * nkv;
-            const int8_t* p = a.kc + (size_t)rk * kHD + 16 * g;
-            T.k[v][0] = *reinterpret_cast<const v4u_t*>(p);
-            T.k[v][1] = *reinterpret_cast<const v4u_t*>(p + 64);
-            if constexpr (!K_ONLY) {
+            if constexpr (KEYS) {
+                const uint32_t rk = ((m & 8) ? u1 : u0) + (uint32_t)(m & 7) * nkv;
+                const int8_t* p = a.kc + (size_t)rk * kHD + 16 * g;
+                T.k[v][0] = *reinterpret_cast<const v4u_t*>(p);
+                T.k[v][1] = *reinterpret_cast<const v4u_t*>(p + 64);
+            }
+            if constexpr (VALUES) {
                 const uint32_t rv = ((g & 2) ? u1 : u0) + (uint32_t)(4 * (g & 1)) * nkv;
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
@@ -179,7 +197,7 @@ __device__ __forceinline__ void mtile_issue(const DecodeArgs& a, int raw, int ba
             }
         }
     }
-    if constexpr (!K_ONLY) {
+    if constexpr (STEPS) {
         const uint32_t srow =
             id >= 0 ? ((((uint32_t)id << a.log2_bs) + (((uint32_t)base + lane) & bs_mask)) * nkv + kh) : 0u;
         T.ks = a.ks[srow];
@@ -242,8 +260,16 @@ __device__ __forceinline__ float exp2i(int e) { return __uint_as_float((uint32_t
 // 2^-21 relative.  To keep them in f16 range they carry a wave-wide power of
 // two 2^E with max(vstep) * 2^E < 2^15; E only ever decreases, and the
 // accumulator holds its value times 2^E.
+struct NoHook {
+    __device__ void operator()() const {}
+};
+
+// `after_qk` runs once the tile's keys are consumed (the walk issues the next
+// tile's value loads there).
+template <class Hook = NoHook>
 __device__ __forceinline__ void mtile_compute(const DecodeArgs& a, const MTile T, int base, int L, int lane,
-                                              int wave, const MQuery& Q, MState& st, MSmem& sm) {
+                                              int wave, const MQuery& Q, MState& st, MSmem& sm,
+                                              Hook after_qk = Hook()) {
     const int g = lane >> 4;
     const int m = lane & 15;
     // steps through LDS: lane l holds token base+l, the products need tokens
@@ -279,6 +305,7 @@ __device__ __forceinline__ void mtile_compute(const DecodeArgs& a, const MTile T
                 s[v][r] = f + dpp_f<kDppXor1>(f);
             }
     }
+    after_qk();
     float mt = -INFINITY;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -414,8 +441,12 @@ __device__ __forceinline__ void mwrite_partial(const DecodeArgs& a, MSmem& sm, M
     mcombine_write(a, sm, G, b, kh, c);
 }
 
-template <int NEWDT, bool BS8>
-__global__ __launch_bounds__(kWGThreads, 2) void kvq_decode_mfma_kernel(DecodeArgs a) {
+// OCC = workgroups per CU the registers are budgeted for.  With 2 the walk
+// fits only with some spilling; with 1 nothing spills, and a workgroup that
+// walks several tiles per wave streams faster that way, while one that walks
+// a single tile is better off sharing its CU.
+template <int NEWDT, bool BS8, int OCC>
+__global__ __launch_bounds__(kWGThreads, OCC) void kvq_decode_mfma_kernel(DecodeArgs a) {
     __shared__ MSmem sm;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -510,43 +541,56 @@ __global__ __launch_bounds__(kWGThreads, 2) void kvq_decode_mfma_kernel(DecodeAr
         else
             mtile_compute(a, T, base, L, lane, wave, Q, st, sm);
     };
-    // double-buffered walk: tile k+1's loads are in flight while tile k is
-    // computed; the table entries run one tile further ahead
+    // double-buffered walk: tile k+1's keys and steps are in flight while
+    // tile k is computed, its values from tile k's Q.K on; the table entries
+    // run one tile further ahead
     int base = first;
     for (int k = 0;;) {
         if (k + 1 >= n_tiles) {
             run_last(A, base);
             break;
         }
-        mtile_issue<BS8>(a, raw, base + kChunkUnit, kh, lane, lo, B);
+        mtile_issue<BS8, kIssueKeys | kIssueSteps>(a, raw, base + kChunkUnit, kh, lane, lo, B);
         raw = mtile_raw(a.r8, btb, base + 2 * kChunkUnit, a.log2_bs, lane);
-        mtile_compute(a, A, base, L, lane, wave, Q, st, sm);
+        mtile_compute(a, A, base, L, lane, wave, Q, st, sm, [&]() __attribute__((always_inline)) {
+            mtile_issue<BS8, kIssueValues>(a, 0, base + kChunkUnit, kh, lane, lo, B);
+        });
         base += kChunkUnit;
         ++k;
         if (k + 1 >= n_tiles) {
             run_last(B, base);
             break;
         }
-        mtile_issue<BS8>(a, raw, base + kChunkUnit, kh, lane, lo, A);
+        mtile_issue<BS8, kIssueKeys | kIssueSteps>(a, raw, base + kChunkUnit, kh, lane, lo, A);
         raw = mtile_raw(a.r8, btb, base + 2 * kChunkUnit, a.log2_bs, lane);
-        mtile_compute(a, B, base, L, lane, wave, Q, st, sm);
+        mtile_compute(a, B, base, L, lane, wave, Q, st, sm, [&]() __attribute__((always_inline)) {
+            mtile_issue<BS8, kIssueValues>(a, 0, base + kChunkUnit, kh, lane, lo, A);
+        });
         base += kChunkUnit;
         ++k;
     }
     mwrite_partial(a, sm, st, G, b, kh, c, lane, wave);
 }
 
-template <bool BS8>
-inline void launch_mfma_bs(const DecodeArgs& a, int n_wg, int new_dtype, hipStream_t s) {
+template <bool BS8, int OCC>
+inline void launch_mfma_occ(const DecodeArgs& a, int n_wg, int new_dtype, hipStream_t s) {
     const dim3 grid(n_wg), block(kWGThreads);
     if (new_dtype == KVQ8_F32)
-        hipLaunchKernelGGL((kvq_decode_mfma_kernel<KVQ8_F32, BS8>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((kvq_decode_mfma_kernel<KVQ8_F32, BS8, OCC>), grid, block, 0, s, a);
     else if (new_dtype == KVQ8_BF16)
-        hipLaunchKernelGGL((kvq_decode_mfma_kernel<KVQ8_BF16, BS8>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((kvq_decode_mfma_kernel<KVQ8_BF16, BS8, OCC>), grid, block, 0, s, a);
     else if (new_dtype == KVQ8_F16)
-        hipLaunchKernelGGL((kvq_decode_mfma_kernel<KVQ8_F16, BS8>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((kvq_decode_mfma_kernel<KVQ8_F16, BS8, OCC>), grid, block, 0, s, a);
     else
-        hipLaunchKernelGGL((kvq_decode_mfma_kernel<-1, BS8>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((kvq_decode_mfma_kernel<-1, BS8, OCC>), grid, block, 0, s, a);
+}
+
+template <bool BS8>
+inline void launch_mfma_bs(const DecodeArgs& a, int n_wg, int new_dtype, hipStream_t s) {
+    if (a.tiles_per_wave > 1)
+        launch_mfma_occ<BS8, 1>(a, n_wg, new_dtype, s);
+    else
+        launch_mfma_occ<BS8, 2>(a, n_wg, new_dtype, s);
 }
 
 inline void launch_mfma(const DecodeArgs& a, int n_wg, int new_dtype, hipStream_t s) {
