@@ -253,6 +253,17 @@ __device__ __forceinline__ float wave_max(float v) {
 // 2^e as a float, e in [-126, 127]
 __device__ __forceinline__ float exp2i(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
 
+// Byte `byte` of two words of int8 codes as an f16 pair (low half from wa),
+// exactly: the byte with its sign bit flipped is code + 128, which as the
+// mantissa of 2^10 gives the f16 1152 + code; one packed f16 subtraction of
+// 1152 leaves the code.
+__device__ __forceinline__ uint32_t codes_f16x2(uint32_t wa, uint32_t wb, int byte) {
+    const uint32_t sel = (uint32_t)byte | 0x00000C00u | ((uint32_t)(4 + byte) << 16) | 0x0C000000u;
+    const uint32_t x = __builtin_amdgcn_perm(wb, wa, sel) ^ 0x64806480u;
+    const v2h_t bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h_t, x) + bias);
+}
+
 // One tile.
 //
 // The value weights p * vstep enter the f16 product as a high part (11
@@ -374,9 +385,7 @@ __device__ __forceinline__ void mtile_compute(const DecodeArgs& a, const MTile T
                 const int q0 = 2 * i, q1 = 2 * i + 1;      // element q: token group 2vp + q/4, e = q%4
                 const v2u_t c0 = T.v[2 * vp + q0 / 4][q0 % 4];
                 const v2u_t c1 = T.v[2 * vp + q1 / 4][q1 % 4];
-                const float f0 = sbyte_f(sl < 4 ? c0.x : c0.y, sl & 3);
-                const float f1 = sbyte_f(sl < 4 ? c1.x : c1.y, sl & 3);
-                bw[i] = pack_f16_rtz(f0, f1);                // integers: exact
+                bw[i] = codes_f16x2(sl < 4 ? c0.x : c0.y, sl < 4 ? c1.x : c1.y, sl & 3);
             }
             const v8h_t B = __builtin_bit_cast(v8h_t, v4u_t{bw[0], bw[1], bw[2], bw[3]});
             st.acc[sl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, st.acc[sl], 0, 0, 0);
