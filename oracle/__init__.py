@@ -32,4 +32,4 @@ Sources (cited by these short names throughout):
 
 Parity status per function is listed in each module's header.
 """
-from . import kvq8, kvq4  # noqa: F401
+from . import kvq8, kvq4, kvq4_0  # noqa: F401
