@@ -1,4 +1,4 @@
-"""int8 / int4 KV-cache decode attention for AMD Instinct MI355X (gfx950).
+"""int8 / int4 / Q4_0 KV-cache decode attention for AMD Instinct MI355X (gfx950).
 
 The compute lives in the HIP library ``libkvq8.so`` (C ABI in
 ``include/kvq8.h``); :mod:`decode_attention_int8_amd.kvq8` is its thin ctypes
@@ -8,6 +8,10 @@ does, and raises if the library has not been built.
 from .kvq8 import (  # noqa: F401
     KVQ8Error,
     alloc_workspace,
+    kvq4_0_decode_attn,
+    kvq4_0_decode_chunk_tokens,
+    kvq4_0_decode_workspace_size,
+    kvq4_0_quantize_append,
     kvq4_decode_attn,
     kvq4_decode_chunk_tokens,
     kvq4_decode_workspace_size,

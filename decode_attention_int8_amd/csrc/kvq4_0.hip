@@ -1,0 +1,617 @@
+// Q4_0 KV mode ([P2] Sec. 1 and Sec. 3: the --kv-q4 switch, a Q4_0 payload
+// cache about 1.65x denser than q8 whose decode dot product reads the nibbles
+// without dequantizing them).
+//
+// Format, per (token, kv-head) row of 128 values: four blocks of 32, each
+// with a float32 step = (the block's value of largest magnitude, the negative
+// one on a sign tie) / -8, and 4-bit codes c = min(15, floor(x / step + 8.5))
+// standing for (c - 8) * step; a block of zeros has step +0 and codes 8.
+// 64 code bytes + 16 step bytes = 80 B per row against q8's 132 B.
+//
+// Byte layouts (chosen for the decode kernel's lanes):
+//   key row:   byte j = code[j] | code[64 + j] << 4
+//   value row: byte 4m + k = code[32k + 2m] | code[32k + 2m + 1] << 4
+//
+// Decode: the int8 path's matrix-core walk (see kvq_decode_mfma.h) with
+//   Q.K  the nibbles of a key half-row as the i8 operand; the accumulator
+//        input -8 * R (R = sum of the query block's codes) makes each column
+//        the block term P - 8R; block term x query block scale x key block
+//        step, the two parities of a head summed by one DPP step;
+//   P.V  one v_mfma_f32_16x16x32_f16 per (pair of token groups, slice s):
+//        columns m of slice s are d = 32(s/2) + 2m + (s & 1), all in value
+//        block s/2, so the A operand holds the weights p * vstep of that
+//        block (f16 high part + f16 remainder, rows = (head, part)) and B
+//        holds c - 8 as f16 (exact).  Up to 8 heads in one operand set.
+#include "kvq8.h"
+#include "kvq_decode_mfma.h"
+
+namespace kvq {
+
+// ----------------------------------------------------------------------------
+// write path
+// ----------------------------------------------------------------------------
+
+// Rows per 16-lane group; a 256-thread workgroup quantizes 64 rows.
+constexpr int kQ40RowsPerGroup = 4;
+constexpr int kQ40RowsPerBlock = 16 * kQ40RowsPerGroup;
+
+template <int DT>
+__device__ __forceinline__ void q40_load8(const void* base, size_t elem_off, float (&x)[8]) {
+    if constexpr (DT == KVQ8_F32) {
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem_off);
+        const float4 a = p[0], b = p[1];
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    } else {
+        const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem_off);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (DT == KVQ8_BF16) {
+                x[2 * i] = __uint_as_float(w[i] << 16);
+                x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+            } else {
+                x[2 * i] = half_bits_f(w[i] & 0xFFFFu);
+                x[2 * i + 1] = half_bits_f(w[i] >> 16);
+            }
+        }
+    }
+}
+
+// Codes of the 8 values a lane holds (elements 8 l16 .. 8 l16 + 7 of a row
+// spread over 16 lanes, so lanes 4k .. 4k+3 hold block k), one byte each,
+// and the block's step.
+__device__ __forceinline__ void q40_quantize8(const float (&x)[8], uint32_t& lo, uint32_t& hi, float& step) {
+#pragma clang fp contract(off)
+    float mx = x[0], mn = x[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) {
+        mx = fmaxf(mx, x[e]);
+        mn = fminf(mn, x[e]);
+    }
+    mx = fmaxf(mx, dpp_f<kDppXor1>(mx));
+    mx = fmaxf(mx, dpp_f<kDppXor2>(mx));
+    mn = fminf(mn, dpp_f<kDppXor1>(mn));
+    mn = fminf(mn, dpp_f<kDppXor2>(mn));
+    const float m = (-mn >= mx) ? mn : mx;           // negative extreme wins a tie
+    step = (m == 0.0f) ? 0.0f : m * -0.125f;         // exact: a power-of-two division
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        float c = 8.0f;
+        if (step != 0.0f) c = fminf(floorf(x[e] / step + 8.5f), 15.0f);
+        w[e >> 2] |= (uint32_t)(int)c << (8 * (e & 3));
+    }
+    lo = w[0];
+    hi = w[1];
+}
+
+// One (token, kv-head, K-or-V) row per 16 lanes, 4 rows per 16-lane group.
+// Codes go through LDS (one byte each) and come out in the row's layout:
+// lane l16 writes bytes 4 l16 .. 4 l16 + 3.
+template <int DT>
+__global__ __launch_bounds__(256) void kvq4_0_quantize_append_kernel(
+    uint8_t* __restrict__ kc, uint8_t* __restrict__ vc, float* __restrict__ ks, float* __restrict__ vs,
+    long n_slots, int nkv, const void* __restrict__ k_new, const void* __restrict__ v_new, long n_rows,
+    const int32_t* __restrict__ slots) {
+    __shared__ uint8_t codes[kQ40RowsPerBlock][kHD];
+    const int l16 = threadIdx.x & 15;
+    const int grp = threadIdx.x >> 4;
+    float x[kQ40RowsPerGroup][8];
+    long slot[kQ40RowsPerGroup];
+    // rows past the end load the last row again and store nothing
+#pragma unroll
+    for (int k = 0; k < kQ40RowsPerGroup; ++k) {
+        const long row = min((long)blockIdx.x * kQ40RowsPerBlock + k * 16 + grp, n_rows - 1);
+        const long tr = row >> 1;                    // token * nkv + kv-head
+        q40_load8<DT>((row & 1) ? v_new : k_new, (size_t)tr * kHD + 8 * l16, x[k]);
+        slot[k] = slots[tr / nkv];
+    }
+    float step[kQ40RowsPerGroup];
+#pragma unroll
+    for (int k = 0; k < kQ40RowsPerGroup; ++k) {
+        uint32_t lo, hi;
+        q40_quantize8(x[k], lo, hi, step[k]);
+        *reinterpret_cast<uint2*>(&codes[k * 16 + grp][8 * l16]) = make_uint2(lo, hi);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kQ40RowsPerGroup; ++k) {
+        const long row = (long)blockIdx.x * kQ40RowsPerBlock + k * 16 + grp;
+        if (row >= n_rows || slot[k] < 0 || slot[k] >= n_slots) continue;   // uniform per 16-lane row
+        const uint8_t* c = codes[k * 16 + grp];
+        const int kind = (int)(row & 1);
+        uint32_t word;
+        if (kind == 0) {
+            // key: byte j = code[j] | code[64 + j] << 4
+            const uint32_t a = *reinterpret_cast<const uint32_t*>(c + 4 * l16);
+            const uint32_t b = *reinterpret_cast<const uint32_t*>(c + 64 + 4 * l16);
+            word = a | (b << 4);
+        } else {
+            // value: byte 4m + k = code[32k + 2m] | code[32k + 2m + 1] << 4, m = l16
+            word = 0u;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const uint32_t pr = *reinterpret_cast<const uint16_t*>(c + 32 * kb + 2 * l16);
+                word |= ((pr & 0xFu) | ((pr >> 4) & 0xF0u)) << (8 * kb);
+            }
+        }
+        const long tr = row >> 1;
+        const long tok = tr / nkv;
+        const size_t dst = (size_t)slot[k] * nkv + (size_t)(tr - tok * nkv);
+        *reinterpret_cast<uint32_t*>((kind ? vc : kc) + dst * (kHD / 2) + 4 * l16) = word;
+        if ((l16 & 3) == 0) (kind ? vs : ks)[dst * 4 + (l16 >> 2)] = step[k];
+    }
+}
+
+// ----------------------------------------------------------------------------
+// decode
+// ----------------------------------------------------------------------------
+
+constexpr int kQ40RowBytes = kHD / 2;
+
+// One tile in operand layout.
+struct QTile {
+    v4u_t k[4];          // [v]: token 16v+m, key bytes 16g .. 16g+15
+    uint32_t v[4][4];    // [v][e]: token 16v+4g+e, value bytes 4m .. 4m+3
+    v4f_t ks, vs;        // block steps of token base+lane
+    int id;              // block id of token base+lane, -1 if outside the pool
+};
+
+struct QSmem40 : MSmem {
+    float kst[kWaves][4][64];     // key block step * score scale (0 if masked)
+    float vst[kWaves][4][64];     // value block step * 2^E (0 if masked)
+};
+
+// Lane parts of the load addresses (bytes), fixed for the whole kernel.
+struct QLaneOff {
+    uint32_t k;          // key row of token 16v+m, bytes 16g..
+    uint32_t v[4];       // value rows of tokens 16v+4g+e, bytes 4m..
+};
+
+__device__ __forceinline__ QLaneOff q40_lane_offsets(const DecodeArgs& a, int lane) {
+    const int g = lane >> 4;
+    const int m = lane & 15;
+    const uint32_t row = (uint32_t)a.nkv * kQ40RowBytes;
+    QLaneOff o;
+    o.k = (uint32_t)m * row + 16 * g;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o.v[e] = (uint32_t)(4 * g + e) * row + 4 * m;
+    return o;
+}
+
+// Loads of a tile (the parts as for the int8 tile).  Codes live in a.k4 /
+// a.v4 ([n_blocks][kv_bs][nkv][64]), steps in a.ks / a.vs
+// ([n_blocks][kv_bs][nkv][4]); rows of invalid blocks read slot 0.
+template <bool BS8, int PARTS = kIssueAll>
+__device__ __forceinline__ void qtile_issue(const DecodeArgs& a, int raw, int base, int kh, int lane,
+                                            const QLaneOff& lo, QTile& T) {
+    constexpr bool KEYS = PARTS & kIssueKeys, VALUES = PARTS & kIssueValues, STEPS = PARTS & kIssueSteps;
+    const int g = lane >> 4;
+    const int m = lane & 15;
+    const uint32_t bs_mask = (1u << a.log2_bs) - 1;
+    int id;
+    if constexpr (KEYS) {
+        id = (raw >= 0 && raw < a.r8.n_blocks) ? raw : -1;
+        T.id = id;
+    } else {
+        id = T.id;
+    }
+    const uint32_t nkv = (uint32_t)a.nkv;
+    auto grp = [&](int i) __attribute__((always_inline)) -> uint32_t {
+        const int idi = __builtin_amdgcn_readlane(id, 8 * i);
+        return idi >= 0 ? ((((uint32_t)idi << a.log2_bs) + (((uint32_t)base + 8 * i) & bs_mask)) * nkv + kh) : 0u;
+    };
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        if constexpr (!BS8) {
+            const uint32_t u = grp(2 * v);
+            if constexpr (KEYS)
+                T.k[v] = *reinterpret_cast<const v4u_t*>(a.k4 + (size_t)u * kQ40RowBytes + lo.k);
+            if constexpr (VALUES) {
+                const uint8_t* pv = a.v4 + (size_t)u * kQ40RowBytes;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) T.v[v][e] = *reinterpret_cast<const uint32_t*>(pv + lo.v[e]);
+            }
+        } else {
+            const uint32_t u0 = grp(2 * v), u1 = grp(2 * v + 1);
+            if constexpr (KEYS) {
+                const uint32_t rk = ((m & 8) ? u1 : u0) + (uint32_t)(m & 7) * nkv;
+                T.k[v] = *reinterpret_cast<const v4u_t*>(a.k4 + (size_t)rk * kQ40RowBytes + 16 * g);
+            }
+            if constexpr (VALUES) {
+                const uint32_t rv = ((g & 2) ? u1 : u0) + (uint32_t)(4 * (g & 1)) * nkv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    T.v[v][e] = *reinterpret_cast<const uint32_t*>(a.v4 + (size_t)(rv + (uint32_t)e * nkv) *
+                                                                           kQ40RowBytes + 4 * m);
+            }
+        }
+    }
+    if constexpr (STEPS) {
+        const uint32_t srow =
+            id >= 0 ? ((((uint32_t)id << a.log2_bs) + (((uint32_t)base + lane) & bs_mask)) * nkv + kh) : 0u;
+        T.ks = *reinterpret_cast<const v4f_t*>(a.ks + (size_t)srow * 4);
+        T.vs = *reinterpret_cast<const v4f_t*>(a.vs + (size_t)srow * 4);
+    }
+}
+
+// -8 * (sum of the query codes of block 2h + (m & 1) of head m/2), per row
+// half h: the accumulator input that turns the i8 product into P - 8R.
+__device__ __forceinline__ void q40_block_bias(const QSmem& sm, int G, int m, int (&nr)[2]) {
+    const int H = m >> 1;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        int r = 0;
+        if (H < G) {
+            const int b = 2 * h + (m & 1);
+#pragma unroll
+            for (int w = 0; w < 8; ++w) {
+                const uint32_t word = sm.qc[H][8 * b + w];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) r += (int)(int8_t)(word >> (8 * k));
+            }
+        }
+        nr[h] = -8 * r;
+    }
+}
+
+// One tile (readings of the weights, E and masking as in mtile_compute).
+template <class Hook = NoHook>
+__device__ __forceinline__ void qtile_compute(const DecodeArgs& a, const QTile T, int base, int L, int lane,
+                                              int wave, const MQuery& Q, const int (&nr)[2], MState& st,
+                                              QSmem40& sm, Hook after_qk = Hook()) {
+    const int g = lane >> 4;
+    const int m = lane & 15;
+    // steps through LDS: lane l holds token base+l, the products need tokens
+    // 16v + 4g + r
+    {
+        const bool ok = (base + lane < L) && T.id >= 0;
+        const v4f_t kv = ok ? T.ks : v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
+        const v4f_t vv = ok ? T.vs : v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
+        const float va = fmaxf(fmaxf(fabsf(vv.x), fabsf(vv.y)), fmaxf(fabsf(vv.z), fabsf(vv.w)));
+        const float vm = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max(va))));
+        if (vm > 0.0f) {
+            const int e = (int)((__float_as_uint(vm) >> 23) & 0xFFu) - 127;
+            const int Et = min(max(14 - e, -100), 100);
+            if (Et < st.E) {
+                const float f = exp2i(Et - st.E);
+#pragma unroll
+                for (int sl = 0; sl < 8; ++sl) st.acc[sl] *= f;
+                st.E = Et;
+            }
+        }
+        const float sc = exp2i(st.E);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            sm.kst[wave][b][lane] = kv[b] * a.score_scale;
+            sm.vst[wave][b][lane] = vv[b] * sc;
+        }
+        sm.kb[wave][lane] = ok ? 0.0f : -INFINITY;
+    }
+    float s[4][4];
+    {
+        v4i_t d[4][2];
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const v4u_t nib = h ? ((T.k[v] >> 4u) & kNib) : (T.k[v] & kNib);
+                d[v][h] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i_t, nib), Q.op[h],
+                                                                v4i_t{nr[h], nr[h], nr[h], nr[h]}, 0, 0, 0);
+            }
+        after_qk();
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const float4 k0 = *reinterpret_cast<const float4*>(&sm.kst[wave][m & 1][16 * v + 4 * g]);
+            const float4 k1 = *reinterpret_cast<const float4*>(&sm.kst[wave][2 + (m & 1)][16 * v + 4 * g]);
+            const float4 kb = *reinterpret_cast<const float4*>(&sm.kb[wave][16 * v + 4 * g]);
+            const float a0[4] = {k0.x, k0.y, k0.z, k0.w};
+            const float a1[4] = {k1.x, k1.y, k1.z, k1.w};
+            const float b4[4] = {kb.x, kb.y, kb.z, kb.w};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float f = (float)d[v][0][r] * Q.sc[0] * a0[r];
+                f = fmaf((float)d[v][1][r] * Q.sc[1], a1[r], f);
+                s[v][r] = (f + dpp_f<kDppXor1>(f)) + b4[r];
+            }
+        }
+    }
+    float mt = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mt = fmaxf(mt, s[v][r]);
+    mt = fmaxf(mt, swz_xor16(mt));
+    mt = fmaxf(mt, xor32(mt));
+    if (__builtin_amdgcn_ballot_w64(mt > st.M) != 0) {
+        const float fac = (mt > st.M) ? __builtin_amdgcn_exp2f(st.M - mt) : 1.0f;
+        st.M = fmaxf(st.M, mt);
+        st.S *= fac;
+        const float fa = bperm_f(fac, 4 * g);
+        const float fb = bperm_f(fac, 4 * g + 2);
+#pragma unroll
+        for (int sl = 0; sl < 8; ++sl) {
+            st.acc[sl][0] *= fa;
+            st.acc[sl][1] *= fa;
+            st.acc[sl][2] *= fb;
+            st.acc[sl][3] *= fb;
+        }
+    }
+    const float mref = (st.M == -INFINITY) ? 0.0f : st.M;
+    const bool lo_row = m & 1;
+    float p[4][4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            p[v][r] = __builtin_amdgcn_exp2f(s[v][r] - mref);
+            st.S += p[v][r];
+        }
+    const v2h_t bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+#pragma unroll
+    for (int vp = 0; vp < 2; ++vp) {
+        v8h_t A[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            uint32_t wop[2][2];
+#pragma unroll
+            for (int q2 = 0; q2 < 2; ++q2) {
+                const int v = 2 * vp + q2;
+                const float4 vv = *reinterpret_cast<const float4*>(&sm.vst[wave][b][16 * v + 4 * g]);
+                const float w[4] = {p[v][0] * vv.x, p[v][1] * vv.y, p[v][2] * vv.z, p[v][3] * vv.w};
+#pragma unroll
+                for (int pr = 0; pr < 2; ++pr) {
+                    const float h0 = __uint_as_float(__float_as_uint(w[2 * pr]) & 0xFFFFE000u);
+                    const float h1 = __uint_as_float(__float_as_uint(w[2 * pr + 1]) & 0xFFFFE000u);
+                    const uint32_t hi = pack_f16_rtz(h0, h1);
+                    const uint32_t lo = pack_f16(w[2 * pr] - h0, w[2 * pr + 1] - h1);
+                    wop[q2][pr] = lo_row ? lo : hi;
+                }
+            }
+            A[b] = __builtin_bit_cast(v8h_t, v4u_t{wop[0][0], wop[0][1], wop[1][0], wop[1][1]});
+        }
+        // the 8 tokens' value words, low and high nibbles as bytes
+        uint32_t n_lo[8], n_hi[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const uint32_t w = T.v[2 * vp + q / 4][q % 4];
+            n_lo[q] = w & kNib;
+            n_hi[q] = (w >> 4) & kNib;
+        }
+#pragma unroll
+        for (int sl = 0; sl < 8; ++sl) {
+            // d = 32(sl/2) + 2m + (sl&1): byte sl/2 of the word, high nibble for odd sl
+            const int byte = sl >> 1;
+            const uint32_t sel = (uint32_t)byte | 0x00000C00u | ((uint32_t)(4 + byte) << 16) | 0x0C000000u;
+            uint32_t bw[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t xa = (sl & 1) ? n_hi[2 * i] : n_lo[2 * i];
+                const uint32_t xb = (sl & 1) ? n_hi[2 * i + 1] : n_lo[2 * i + 1];
+                // [c_a, 0, c_b, 0] | 0x6400 in each half = 1024 + c; minus 1032 leaves c - 8
+                const uint32_t x = __builtin_amdgcn_perm(xb, xa, sel) | 0x64006400u;
+                bw[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h_t, x) + bias);
+            }
+            const v8h_t B = __builtin_bit_cast(v8h_t, v4u_t{bw[0], bw[1], bw[2], bw[3]});
+            st.acc[sl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[byte], B, st.acc[sl], 0, 0, 0);
+        }
+    }
+}
+
+// Fold the wave states and write one partial per query head (slice s of
+// lane m holds d = 32(s/2) + 2m + (s&1)).
+__device__ __forceinline__ void q40_write_partial(const DecodeArgs& a, QSmem40& sm, MState& st, int G, int b,
+                                                  int kh, int c, int lane, int wave) {
+    const int g = lane >> 4;
+    const int m = lane & 15;
+    float S = st.S;
+    S += swz_xor16(S);
+    S += xor32(S);
+    if (g == 0 && (m & 1) == 0 && (m >> 1) < G) {
+        sm.m[wave][m >> 1] = st.M;
+        sm.s[wave][m >> 1] = S;
+    }
+    const float unscale = exp2i(-st.E);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const int H = 2 * g + hh;
+        if (H < G) {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const float o0 = (st.acc[2 * kb][2 * hh] + st.acc[2 * kb][2 * hh + 1]) * unscale;
+                const float o1 = (st.acc[2 * kb + 1][2 * hh] + st.acc[2 * kb + 1][2 * hh + 1]) * unscale;
+                *reinterpret_cast<float2*>(&sm.acc[wave][H][32 * kb + 2 * m]) = make_float2(o0, o1);
+            }
+        }
+    }
+    lds_barrier();
+    mcombine_write(a, sm, G, b, kh, c);
+}
+
+template <bool BS8, int OCC>
+__global__ __launch_bounds__(kWGThreads, OCC) void kvq4_0_decode_kernel(DecodeArgs a) {
+    __shared__ QSmem40 sm;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int G = a.nq / a.nkv;
+
+    // work decode: the nkv workgroups of one (sequence, chunk) share an XCD
+    const int nct = a.r8.max_chunks;
+    const int wg = blockIdx.x;
+    const int rest = wg >> 3;
+    const int kh = rest % a.nkv;
+    const int p = (rest / a.nkv) * 8 + (wg & 7);
+    const int b = p / nct;
+    const int c = p - b * nct;
+    if (b >= a.batch) return;
+    const int chunk_len = a.tiles_per_wave * kChunkUnit;
+    const int c0 = c * chunk_len;
+    const int32_t* btb = a.r8.bt + (size_t)b * a.r8.max_blocks;
+    const int first = c0 + wave * kTile;
+    int raw = mtile_raw(a.r8, btb, first, a.log2_bs, lane);
+    const int L = effective_len(a.r8, b, a.log2_bs);
+    if (c0 >= L) return;                                       // uniform per workgroup
+    const int end = min(L, c0 + chunk_len);
+    const int n_tiles = first < end ? (end - first + kChunkUnit - 1) / kChunkUnit : 1;
+
+    const float4 qx = load_q4(a.q + ((size_t)b * a.nq + (size_t)kh * G) * kHD, G);
+    const QLaneOff lo = q40_lane_offsets(a, lane);
+    QTile A, B;
+    qtile_issue<BS8>(a, raw, first, kh, lane, lo, A);
+    raw = mtile_raw(a.r8, btb, first + kChunkUnit, a.log2_bs, lane);
+    __asm__ volatile("" ::: "memory");
+
+    quantize_q4(qx, G, sm.q);
+    lds_barrier();
+    const int g = lane >> 4;
+    const int m = lane & 15;
+    const MQuery Q = load_q_operand(sm.q, G, g, m);
+    int nr[2];
+    q40_block_bias(sm.q, G, m, nr);
+
+    MState st;
+    st.M = -INFINITY;
+    st.S = 0.0f;
+    st.E = 100;
+#pragma unroll
+    for (int sl = 0; sl < 8; ++sl) st.acc[sl] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // double-buffered walk as in the int8 kernel
+    int base = first;
+    for (int k = 0;;) {
+        if (k + 1 >= n_tiles) {
+            qtile_compute(a, A, base, L, lane, wave, Q, nr, st, sm);
+            break;
+        }
+        qtile_issue<BS8, kIssueKeys | kIssueSteps>(a, raw, base + kChunkUnit, kh, lane, lo, B);
+        raw = mtile_raw(a.r8, btb, base + 2 * kChunkUnit, a.log2_bs, lane);
+        qtile_compute(a, A, base, L, lane, wave, Q, nr, st, sm, [&]() __attribute__((always_inline)) {
+            qtile_issue<BS8, kIssueValues>(a, 0, base + kChunkUnit, kh, lane, lo, B);
+        });
+        base += kChunkUnit;
+        ++k;
+        if (k + 1 >= n_tiles) {
+            qtile_compute(a, B, base, L, lane, wave, Q, nr, st, sm);
+            break;
+        }
+        qtile_issue<BS8, kIssueKeys | kIssueSteps>(a, raw, base + kChunkUnit, kh, lane, lo, A);
+        raw = mtile_raw(a.r8, btb, base + 2 * kChunkUnit, a.log2_bs, lane);
+        qtile_compute(a, B, base, L, lane, wave, Q, nr, st, sm, [&]() __attribute__((always_inline)) {
+            qtile_issue<BS8, kIssueValues>(a, 0, base + kChunkUnit, kh, lane, lo, A);
+        });
+        base += kChunkUnit;
+        ++k;
+    }
+    q40_write_partial(a, sm, st, G, b, kh, c, lane, wave);
+}
+
+template <bool BS8>
+inline void launch_q40_bs(const DecodeArgs& a, int n_wg, hipStream_t s) {
+    const dim3 grid(n_wg), block(kWGThreads);
+    if (a.tiles_per_wave > 1)
+        hipLaunchKernelGGL((kvq4_0_decode_kernel<BS8, 1>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((kvq4_0_decode_kernel<BS8, 2>), grid, block, 0, s, a);
+}
+
+}  // namespace kvq
+
+using namespace kvq;
+
+extern "C" int kvq4_0_quantize_append(uint8_t* k_cache, uint8_t* v_cache, float* k_step, float* v_step,
+                                      int n_blocks, int kv_bs, int nkv, int hd, const void* k_new,
+                                      const void* v_new, int dtype, int n_tokens, const int32_t* slots,
+                                      void* stream) {
+    if (hd != kHD || !valid_block_size(kv_bs) || nkv < 1 || n_blocks < 1) return KVQ8_ESHAPE;
+    if (n_tokens < 0 || dtype < KVQ8_F32 || dtype > KVQ8_F16) return KVQ8_EINVAL;
+    if (n_tokens == 0) return KVQ8_OK;
+    if (!k_cache || !v_cache || !k_step || !v_step || !k_new || !v_new || !slots) return KVQ8_EINVAL;
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache) ||
+        !aligned16(k_step) || !aligned16(v_step))
+        return KVQ8_EINVAL;
+    const long n_rows = (long)n_tokens * nkv * 2;
+    const long n_slots = (long)n_blocks * kv_bs;
+    const dim3 grid((unsigned)((n_rows + kQ40RowsPerBlock - 1) / kQ40RowsPerBlock)), block(256);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    switch (dtype) {
+        case KVQ8_F32:
+            hipLaunchKernelGGL(kvq4_0_quantize_append_kernel<KVQ8_F32>, grid, block, 0, s, k_cache, v_cache, k_step,
+                               v_step, n_slots, nkv, k_new, v_new, n_rows, slots);
+            break;
+        case KVQ8_BF16:
+            hipLaunchKernelGGL(kvq4_0_quantize_append_kernel<KVQ8_BF16>, grid, block, 0, s, k_cache, v_cache,
+                               k_step, v_step, n_slots, nkv, k_new, v_new, n_rows, slots);
+            break;
+        default:
+            hipLaunchKernelGGL(kvq4_0_quantize_append_kernel<KVQ8_F16>, grid, block, 0, s, k_cache, v_cache, k_step,
+                               v_step, n_slots, nkv, k_new, v_new, n_rows, slots);
+            break;
+    }
+    return launch_status();
+}
+
+extern "C" int kvq4_0_decode_chunk_tokens(int batch, int nkv, int max_ctx_len) {
+    if (batch < 0 || nkv < 1 || max_ctx_len < 0) return 0;
+    return default_tiles_per_wave((long)batch * nkv, max_ctx_len, batch <= 2 ? 8 : 4) * kChunkUnit;
+}
+
+static int resolve_chunk40(int batch, int nkv, int max_ctx_len, int chunk) {
+    if (chunk == 0) return kvq4_0_decode_chunk_tokens(batch, nkv, max_ctx_len);
+    if (chunk < 0 || chunk % kChunkUnit != 0 || chunk > 64 * kChunkUnit) return -1;
+    return chunk;
+}
+
+extern "C" size_t kvq4_0_decode_workspace_size(int batch, int nq, int nkv, int max_ctx_len, int chunk) {
+    if (batch < 0 || nq < 1 || nkv < 1 || max_ctx_len < 0) return 0;
+    const int ch = resolve_chunk40(batch, nkv, max_ctx_len, chunk);
+    if (ch <= 0) return 0;
+    return decode_workspace_bytes(batch, nq, (max_ctx_len + ch - 1) / ch);
+}
+
+extern "C" int kvq4_0_decode_attn(float* out, const float* q, int batch, int nq, const uint8_t* k_cache,
+                                  const uint8_t* v_cache, const float* k_step, const float* v_step, int n_blocks,
+                                  int kv_bs, int nkv, int hd, const int32_t* block_tables, int max_blocks_per_seq,
+                                  const int32_t* ctx_lens, int max_ctx_len, float sm_scale, int chunk,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+    if (!decode_shape_ok(batch, nq, nkv, hd, kv_bs) || n_blocks < 1 || max_blocks_per_seq < 1) return KVQ8_ESHAPE;
+    if (!rows_fit_u32(n_blocks, kv_bs, nkv)) return KVQ8_ESHAPE;
+    if (max_ctx_len < 0) return KVQ8_EINVAL;
+    const int ch = resolve_chunk40(batch, nkv, max_ctx_len, chunk);
+    if (ch <= 0) return KVQ8_ESHAPE;
+    if (batch == 0) return KVQ8_OK;
+    if (!out || !q || !k_cache || !v_cache || !k_step || !v_step || !block_tables || !ctx_lens) return KVQ8_EINVAL;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_step) || !aligned16(v_step))
+        return KVQ8_EINVAL;
+    const size_t need = kvq4_0_decode_workspace_size(batch, nq, nkv, max_ctx_len, chunk);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return KVQ8_EWORKSPACE;
+
+    DecodeArgs a = {};
+    a.q = q;
+    a.k4 = k_cache;
+    a.v4 = v_cache;
+    a.ks = k_step;
+    a.vs = v_step;
+    a.r8 = Region{block_tables, ctx_lens, max_blocks_per_seq, max_ctx_len, n_blocks, (max_ctx_len + ch - 1) / ch};
+    a.r4 = Region{nullptr, nullptr, 1, 0, 0, 0};
+    a.nq = nq;
+    a.nkv = nkv;
+    a.log2_bs = ilog2(kv_bs);
+    a.batch = batch;
+    a.tiles_per_wave = ch / kChunkUnit;
+    a.score_scale = sm_scale * kLog2e;
+    bind_workspace(a, workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int nct = n_chunks_total(a);
+    if (nct > 0) {
+        const long pairs = (long)a.batch * nct;
+        const long n_wg = (long)a.nkv * ((pairs + 7) / 8) * 8;
+        if (n_wg > 0x7FFFFFFFL) return KVQ8_ESHAPE;
+        if (a.log2_bs < 4)
+            launch_q40_bs<true>(a, (int)n_wg, s);
+        else
+            launch_q40_bs<false>(a, (int)n_wg, s);
+    }
+    hipLaunchKernelGGL(kvq_merge_kernel<>, dim3(a.batch * a.nq), dim3(kMergeThreads), 0, s, out, a);
+    return launch_status();
+}

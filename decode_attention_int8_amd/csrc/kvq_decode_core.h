@@ -147,6 +147,8 @@ __device__ __forceinline__ void quantize_row8x16(const float (&x)[16], uint4& co
 constexpr int kMergeBatch = 16;
 constexpr int kMergeThreads = 2 * kHD;
 
+// (a template so that every source that launches it may instantiate it)
+template <int = 0>
 __global__ __launch_bounds__(kMergeThreads) void kvq_merge_kernel(float* __restrict__ out, DecodeArgs a) {
     __shared__ float other[kHD + 2];
     const int bh = blockIdx.x;

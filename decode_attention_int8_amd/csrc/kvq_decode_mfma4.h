@@ -23,7 +23,7 @@
 //   Each lane's softmax values are exactly the weights it supplies.
 #pragma once
 
-#include "kvq_decode_mfma.h"
+#include "kvq_decode_mfma_kernel.h"
 
 namespace kvq {
 
@@ -489,7 +489,7 @@ inline int launch_decode(const DecodeArgs& a, float* out, hipStream_t s, int new
         else
             launch_mfma(a, (int)n_wg, new_dtype, s);
     }
-    hipLaunchKernelGGL(kvq_merge_kernel, dim3(a.batch * a.nq), dim3(kMergeThreads), 0, s, out, a);
+    hipLaunchKernelGGL(kvq_merge_kernel<>, dim3(a.batch * a.nq), dim3(kMergeThreads), 0, s, out, a);
     return launch_status();
 }
 

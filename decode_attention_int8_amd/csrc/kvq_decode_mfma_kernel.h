@@ -1,0 +1,168 @@
+// The int8 decode chunk kernel on the matrix cores and its launchers (the
+// tile machinery is in kvq_decode_mfma.h).
+#pragma once
+
+#include "kvq_decode_mfma.h"
+
+namespace kvq {
+
+// OCC = workgroups per CU the registers are budgeted for.  With 2 the walk
+// fits only with some spilling; with 1 nothing spills, and a workgroup that
+// walks several tiles per wave streams faster that way, while one that walks
+// a single tile is better off sharing its CU.
+template <int NEWDT, bool BS8, int OCC>
+__global__ __launch_bounds__(kWGThreads, OCC) void kvq_decode_mfma_kernel(DecodeArgs a) {
+    __shared__ MSmem sm;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int G = a.nq / a.nkv;
+
+    // work decode: the nkv workgroups of one (sequence, chunk) share an XCD
+    const int nct = a.r8.max_chunks;
+    const int wg = blockIdx.x;
+    const int rest = wg >> 3;
+    const int kh = rest % a.nkv;
+    const int p = (rest / a.nkv) * 8 + (wg & 7);
+    const int b = p / nct;
+    const int c = p - b * nct;
+    if (b >= a.batch) return;
+    const int chunk_len = a.tiles_per_wave * kChunkUnit;
+    const int c0 = c * chunk_len;
+    const int32_t* btb = a.r8.bt + (size_t)b * a.r8.max_blocks;
+    const int first = c0 + wave * kTile;
+    int raw = mtile_raw(a.r8, btb, first, a.log2_bs, lane);
+    const int L = effective_len(a.r8, b, a.log2_bs);
+    if (c0 >= L) return;                                       // uniform per workgroup
+    const int end = min(L, c0 + chunk_len);
+    // tiles of this wave: first, first + 256, ... (at least one, possibly empty)
+    const int n_tiles = first < end ? (end - first + kChunkUnit - 1) / kChunkUnit : 1;
+
+    // fused write path: one wave owns the token at L-1
+    const int tn = L - 1;
+    const bool has_new = NEWDT >= 0 && tn >= c0 && tn < end && (((tn - c0) >> 6) & (kWaves - 1)) == wave;
+    // the query loads go out first (their quantization must not wait for the
+    // tile behind them), then the new token's, then the first tile's
+    const float4 qx = load_q4(a.q + ((size_t)b * a.nq + (size_t)kh * G) * kHD, G);
+    float xn[16];
+    if constexpr (NEWDT >= 0) {
+        if (has_new) {
+            // lanes 0-7: K row, lanes 8-15: V row, 16 values each (lanes above
+            // 15 repeat them)
+            const int j = lane & 15;
+            const void* src = (j < 8) ? a.k_new : a.v_new;
+            load_new16<NEWDT>(src, ((size_t)b * a.nkv + kh) * kHD + 16 * (j & 7), xn);
+        }
+    }
+
+    const LaneOff lo = lane_offsets(a, lane);
+    MTile A, B;
+    mtile_issue<BS8>(a, raw, first, kh, lane, lo, A);
+    raw = mtile_raw(a.r8, btb, first + kChunkUnit, a.log2_bs, lane);
+    __asm__ volatile("" ::: "memory");
+
+    quantize_q4(qx, G, sm.q);
+    if constexpr (NEWDT >= 0) {
+        if (has_new) {
+            uint4 codes;
+            float d;
+            quantize_row8x16(xn, codes, d);
+            const int j = lane & 15;
+            if (lane < 16) {
+                const v4u_t cw = {codes.x, codes.y, codes.z, codes.w};
+                if (j < 8)
+                    sm.nk[j] = cw;
+                else
+                    sm.nv[j - 8] = cw;
+                if ((j & 7) == 0) sm.nstep[j >> 3] = d;
+            }
+            // store into the cache slot of token tn
+            const int bid = btb[min(tn >> a.log2_bs, a.r8.max_blocks - 1)];
+            if (lane < 16 && bid >= 0 && bid < a.r8.n_blocks) {
+                const size_t row = (((size_t)bid << a.log2_bs) + (tn & ((1 << a.log2_bs) - 1))) * a.nkv + kh;
+                int8_t* dst = (j < 8 ? a.kc_w : a.vc_w) + row * kHD + 16 * (j & 7);
+                *reinterpret_cast<uint4*>(dst) = codes;
+                if ((j & 7) == 0) (j < 8 ? a.ks_w : a.vs_w)[row] = d;
+            }
+        }
+    }
+    lds_barrier();
+    const int g = lane >> 4;
+    const int m = lane & 15;
+    const MQuery Q = load_q_operand(sm.q, G, g, m);
+
+    MState st;
+    st.M = -INFINITY;
+    st.S = 0.0f;
+    st.E = 100;
+#pragma unroll
+    for (int sl = 0; sl < 8; ++sl) st.acc[sl] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // Token tn = L-1 is the last token of the sequence, so it can only lie in
+    // the last tile of a wave: only the two terminal calls substitute, with
+    // selects that match nothing outside the owner's tile.
+    auto run_last = [&](const MTile& T, int base) __attribute__((always_inline)) {
+        if constexpr (NEWDT >= 0)
+            mtile_compute(a, mtile_substitute(T, sm, base, tn, lane), base, L, lane, wave, Q, st, sm);
+        else
+            mtile_compute(a, T, base, L, lane, wave, Q, st, sm);
+    };
+    // double-buffered walk: tile k+1's keys and steps are in flight while
+    // tile k is computed, its values from tile k's Q.K on; the table entries
+    // run one tile further ahead
+    int base = first;
+    for (int k = 0;;) {
+        if (k + 1 >= n_tiles) {
+            run_last(A, base);
+            break;
+        }
+        mtile_issue<BS8, kIssueKeys | kIssueSteps>(a, raw, base + kChunkUnit, kh, lane, lo, B);
+        raw = mtile_raw(a.r8, btb, base + 2 * kChunkUnit, a.log2_bs, lane);
+        mtile_compute(a, A, base, L, lane, wave, Q, st, sm, [&]() __attribute__((always_inline)) {
+            mtile_issue<BS8, kIssueValues>(a, 0, base + kChunkUnit, kh, lane, lo, B);
+        });
+        base += kChunkUnit;
+        ++k;
+        if (k + 1 >= n_tiles) {
+            run_last(B, base);
+            break;
+        }
+        mtile_issue<BS8, kIssueKeys | kIssueSteps>(a, raw, base + kChunkUnit, kh, lane, lo, A);
+        raw = mtile_raw(a.r8, btb, base + 2 * kChunkUnit, a.log2_bs, lane);
+        mtile_compute(a, B, base, L, lane, wave, Q, st, sm, [&]() __attribute__((always_inline)) {
+            mtile_issue<BS8, kIssueValues>(a, 0, base + kChunkUnit, kh, lane, lo, A);
+        });
+        base += kChunkUnit;
+        ++k;
+    }
+    mwrite_partial(a, sm, st, G, b, kh, c, lane, wave);
+}
+
+template <bool BS8, int OCC>
+inline void launch_mfma_occ(const DecodeArgs& a, int n_wg, int new_dtype, hipStream_t s) {
+    const dim3 grid(n_wg), block(kWGThreads);
+    if (new_dtype == KVQ8_F32)
+        hipLaunchKernelGGL((kvq_decode_mfma_kernel<KVQ8_F32, BS8, OCC>), grid, block, 0, s, a);
+    else if (new_dtype == KVQ8_BF16)
+        hipLaunchKernelGGL((kvq_decode_mfma_kernel<KVQ8_BF16, BS8, OCC>), grid, block, 0, s, a);
+    else if (new_dtype == KVQ8_F16)
+        hipLaunchKernelGGL((kvq_decode_mfma_kernel<KVQ8_F16, BS8, OCC>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((kvq_decode_mfma_kernel<-1, BS8, OCC>), grid, block, 0, s, a);
+}
+
+template <bool BS8>
+inline void launch_mfma_bs(const DecodeArgs& a, int n_wg, int new_dtype, hipStream_t s) {
+    if (a.tiles_per_wave > 1)
+        launch_mfma_occ<BS8, 1>(a, n_wg, new_dtype, s);
+    else
+        launch_mfma_occ<BS8, 2>(a, n_wg, new_dtype, s);
+}
+
+inline void launch_mfma(const DecodeArgs& a, int n_wg, int new_dtype, hipStream_t s) {
+    if (a.log2_bs < 4)
+        launch_mfma_bs<true>(a, n_wg, new_dtype, s);
+    else
+        launch_mfma_bs<false>(a, n_wg, new_dtype, s);
+}
+
+}  // namespace kvq

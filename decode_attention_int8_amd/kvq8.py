@@ -51,6 +51,12 @@ _SIGNATURES = {
                                   _p, _p, _p, _p, _p, _p, _c_int, _p, _c_int, _p, _c_int,
                                   _p, _p, _p, _p, _c_int, _p, _c_int, _p, _c_int,
                                   _c_int, _c_int, _c_int, _f, _c_int, _p, _c_size, _p]),
+    "kvq4_0_quantize_append": (_c_int, [_p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _p, _p, _c_int, _c_int,
+                                        _p, _p]),
+    "kvq4_0_decode_chunk_tokens": (_c_int, [_c_int, _c_int, _c_int]),
+    "kvq4_0_decode_workspace_size": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
+    "kvq4_0_decode_attn": (_c_int, [_p, _p, _c_int, _c_int, _p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _p,
+                                    _c_int, _p, _c_int, _f, _c_int, _p, _c_size, _p]),
 }
 
 _lib = None
@@ -310,4 +316,63 @@ def kvq4_decode_attn(out, q, pool4, block_tables4, lens4, max_len4: int, pool8, 
         kv_bs, nkv, hd, float(sm_scale), chunk, _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
         _stream(stream))
     _check(st, "kvq4_decode_attn")
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Q4_0 mode
+# ----------------------------------------------------------------------------
+
+def kvq4_0_quantize_append(k_cache, v_cache, k_step, v_step, k_new, v_new, slots, stream=None):
+    """Quantize k_new / v_new [n_tokens][nkv][128] (f32, bf16 or f16) into the
+    Q4_0 pool: packed codes [n_blocks][kv_bs][nkv][64] uint8, steps
+    [n_blocks][kv_bs][nkv][4] float32, at ``slots`` (int32)."""
+    n_blocks, kv_bs, nkv, half = k_cache.shape
+    hd = 2 * half
+    if k_new.dtype not in _DTYPES or v_new.dtype != k_new.dtype:
+        raise ValueError("k_new / v_new must share one of float32, bfloat16, float16")
+    if tuple(k_new.shape[1:]) != (nkv, hd) or v_new.shape != k_new.shape or slots.shape != (k_new.shape[0],):
+        raise ValueError("k_new / v_new must be [n_tokens][nkv][hd], slots [n_tokens]")
+    if v_cache.shape != k_cache.shape or k_step.shape != (n_blocks, kv_bs, nkv, hd // 32) or \
+            v_step.shape != k_step.shape:
+        raise ValueError(f"steps must be [n_blocks][kv_bs][nkv][{hd // 32}] and the caches alike")
+    st = lib().kvq4_0_quantize_append(
+        _ptr(k_cache, torch.uint8, "k_cache"), _ptr(v_cache, torch.uint8, "v_cache"),
+        _ptr(k_step, torch.float32, "k_step"), _ptr(v_step, torch.float32, "v_step"),
+        n_blocks, kv_bs, nkv, hd, _ptr(k_new, name="k_new"), _ptr(v_new, name="v_new"), _DTYPES[k_new.dtype],
+        k_new.shape[0], _ptr(slots, torch.int32, "slots"), _stream(stream))
+    _check(st, "kvq4_0_quantize_append")
+
+
+def kvq4_0_decode_chunk_tokens(batch: int, nkv: int, max_ctx_len: int) -> int:
+    return lib().kvq4_0_decode_chunk_tokens(batch, nkv, max_ctx_len)
+
+
+def kvq4_0_decode_workspace_size(batch: int, nq: int, nkv: int, max_ctx_len: int, chunk: int = 0) -> int:
+    return lib().kvq4_0_decode_workspace_size(batch, nq, nkv, max_ctx_len, chunk)
+
+
+def kvq4_0_decode_attn(out, q, k_cache, v_cache, k_step, v_step, block_tables, ctx_lens, max_ctx_len: int,
+                       sm_scale: float | None = None, chunk: int = 0, workspace=None, stream=None):
+    """Decode attention: out [B][nq][128] (float32) from q [B][nq][128] over
+    the Q4_0 cache.  ``workspace`` (uint8) is allocated when not given."""
+    B, nq, hd = q.shape
+    n_blocks, kv_bs, nkv, _ = k_cache.shape
+    if out.shape != q.shape:
+        raise ValueError("out must match q")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or ctx_lens.shape != (B,):
+        raise ValueError("block_tables must be [B][max_blocks], ctx_lens [B]")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(hd)
+    need = kvq4_0_decode_workspace_size(B, nq, nkv, max_ctx_len, chunk)
+    if workspace is None:
+        workspace = alloc_workspace(need, q.device)
+    st = lib().kvq4_0_decode_attn(
+        _ptr(out, torch.float32, "out"), _ptr(q, torch.float32, "q"), B, nq,
+        _ptr(k_cache, torch.uint8, "k_cache"), _ptr(v_cache, torch.uint8, "v_cache"),
+        _ptr(k_step, torch.float32, "k_step"), _ptr(v_step, torch.float32, "v_step"),
+        n_blocks, kv_bs, nkv, hd, _ptr(block_tables, torch.int32, "block_tables"), block_tables.shape[1],
+        _ptr(ctx_lens, torch.int32, "ctx_lens"), max_ctx_len, float(sm_scale), chunk,
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
+    _check(st, "kvq4_0_decode_attn")
     return out

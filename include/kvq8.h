@@ -302,6 +302,66 @@ int kvq4_decode_attn(float* out, const float* q, int batch, int nq,
                      int kv_bs, int nkv, int hd, float sm_scale,
                      int chunk, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Q4_0 KV mode ([P2] Sec. 1 and Sec. 3: the --kv-q4 switch, a Q4_0 payload
+ * cache about 1.65x denser than q8 whose decode dot reads the nibbles
+ * without dequantizing them).
+ *
+ * A (token, kv-head) row of 128 values is four blocks of 32.  Per block:
+ * step = m / -8 (float32, exact) where m is the value of largest magnitude
+ * (the negative one when a positive and a negative value tie); a block of
+ * zeros has step +0 and all codes 8; otherwise
+ * code = min(15, floor(x / step + 8.5)) with an IEEE float32 division and
+ * one float32 addition, and the value it stands for is (code - 8) * step.
+ * 64 code bytes + 4 float32 steps = 80 B per row (q8: 132 B, 1.65x).
+ *
+ * Pools (caller-owned device memory, 16-byte aligned):
+ *   k_cache, v_cache  uint8 [n_blocks][kv_bs][nkv][64], two codes per byte:
+ *                     key row byte j = code[j] | code[64 + j] << 4;
+ *                     value row byte 4m + k = code[32k + 2m] |
+ *                     code[32k + 2m + 1] << 4  (k = 0..3, m = 0..15)
+ *   k_step, v_step    float32 [n_blocks][kv_bs][nkv][4], one per block
+ * ------------------------------------------------------------------------ */
+
+/*
+ * kvq4_0_quantize_append -- Q4_0 write path: quantize n_tokens new rows of
+ * K and V (k_new, v_new [n_tokens][nkv][128], 16-byte aligned, dtype as in
+ * kvq8_quantize_append) into slot slots[i] = block * kv_bs + offset.  Slots
+ * outside [0, n_blocks * kv_bs) are skipped.  Errors: KVQ8_ESHAPE for
+ * hd != 128, an invalid kv_bs (a power of two in [8, 1024]), nkv < 1 or
+ * n_blocks < 1; KVQ8_EINVAL for a null or misaligned pointer, a bad dtype
+ * or n_tokens < 0.  n_tokens == 0 enqueues nothing.
+ */
+int kvq4_0_quantize_append(uint8_t* k_cache, uint8_t* v_cache, float* k_step, float* v_step,
+                           int n_blocks, int kv_bs, int nkv, int hd,
+                           const void* k_new, const void* v_new, int dtype, int n_tokens,
+                           const int32_t* slots, void* stream);
+
+/* Default chunk and workspace size for kvq4_0_decode_attn (see the kvq8
+ * counterparts; the same rules). */
+int kvq4_0_decode_chunk_tokens(int batch, int nkv, int max_ctx_len);
+size_t kvq4_0_decode_workspace_size(int batch, int nq, int nkv, int max_ctx_len, int chunk);
+
+/*
+ * kvq4_0_decode_attn -- decode attention over the Q4_0 cache.  The query is
+ * quantized as in kvq8_decode_attn (int8 codes qi and a float32 scale qsc
+ * per 32-block); the score of a token is
+ *   sm_scale * sum_b qsc_b * kstep_b * (P_b - 8 R_b),
+ *   P_b = sum over block b of qi * code (int32),  R_b = sum of qi (int32),
+ * i.e. the dot product of the dequantized query and key, taken without
+ * dequantizing; values contribute weight * vstep_b * (code - 8).  Split-K
+ * chunks and merge as in kvq8_decode_attn; both products run on the matrix
+ * cores.  Arguments, workspace, errors and the 2^32 - 1 row limit as in
+ * kvq8_decode_attn, with the pools above (k_step / v_step 16-byte aligned).
+ */
+int kvq4_0_decode_attn(float* out, const float* q, int batch, int nq,
+                       const uint8_t* k_cache, const uint8_t* v_cache,
+                       const float* k_step, const float* v_step,
+                       int n_blocks, int kv_bs, int nkv, int hd,
+                       const int32_t* block_tables, int max_blocks_per_seq,
+                       const int32_t* ctx_lens, int max_ctx_len, float sm_scale,
+                       int chunk, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 18, names
     lib = K.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -153,3 +153,45 @@ def test_requantize_validation():
     assert call(a15=-1) == EINVAL
     assert call(a16=None) == EINVAL
     assert call(a7=_fake(4104)) == EINVAL             # int8 cache not 16-byte aligned
+
+
+def _decode40(**kw):
+    a = dict(out=_fake(), q=_fake(), batch=2, nq=16, kc=_fake(), vc=_fake(), ks=_fake(), vs=_fake(), n_blocks=64,
+             kv_bs=16, nkv=8, hd=128, bt=_fake(), mb=32, lens=_fake(), max_ctx=512, sm=0.088, chunk=0,
+             ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return K.lib().kvq4_0_decode_attn(*a.values())
+
+
+def test_q4_0_validation_and_sizing():
+    lib = K.lib()
+    need = K.kvq4_0_decode_workspace_size(2, 16, 8, 512, 0)
+    assert need == K.kvq8_decode_workspace_size(2, 16, 8, 512, 0)
+    assert K.kvq4_0_decode_chunk_tokens(1, 8, 8192) == K.kvq8_decode_chunk_tokens(1, 8, 8192)
+    ws = dict(ws=_fake(), ws_bytes=need)
+    assert _decode40(hd=64, **ws) == ESHAPE
+    assert _decode40(nq=72, **ws) == ESHAPE           # group of 9
+    assert _decode40(kv_bs=4, **ws) == ESHAPE
+    assert _decode40(chunk=100, **ws) == ESHAPE
+    assert _decode40(max_ctx=-1, **ws) == EINVAL
+    assert _decode40(ks=_fake(4104), **ws) == EINVAL  # steps are read 16 bytes at a time
+    assert _decode40(vc=None, **ws) == EINVAL
+    assert _decode40(n_blocks=1 << 30, **ws) == ESHAPE
+    assert _decode40() == EWORKSPACE
+    assert _decode40(ws=_fake(), ws_bytes=need - 1) == EWORKSPACE
+    assert _decode40(batch=0) == OK
+    args = [_fake(), _fake(), _fake(), _fake(), 64, 16, 8, 128, _fake(), _fake(), K.F32, 10, _fake(), None]
+
+    def call(**kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return lib.kvq4_0_quantize_append(*a)
+    assert call(a7=96) == ESHAPE
+    assert call(a5=24) == ESHAPE
+    assert call(a4=0) == ESHAPE
+    assert call(a10=5) == EINVAL
+    assert call(a11=-1) == EINVAL
+    assert call(a11=0) == OK
+    assert call(a12=None) == EINVAL
+    assert call(a2=_fake(4104)) == EINVAL             # step array not 16-byte aligned
