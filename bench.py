@@ -315,6 +315,80 @@ def run_workloads():
     us = time_calls(torch, lambda: K.kvq4_requantize_q8(p4, p8, src, dst), 50)
     report("requant_window", "int8 -> int4 re-quantization of the whole 2048-token window x 4 sequences",
            n_all * nkv * (264 + 144), us)
+    del p4, p8
+
+    # Q4_0 mode (80 B per row: 160 B per (token, kv-head) for K and V)
+    def q40_pool(nb, bs, nkv):
+        shp = (nb, bs, nkv)
+        return [torch.zeros(shp + (64,), dtype=torch.uint8, device="cuda"),
+                torch.zeros(shp + (64,), dtype=torch.uint8, device="cuda"),
+                torch.zeros(shp + (4,), dtype=torch.float32, device="cuda"),
+                torch.zeros(shp + (4,), dtype=torch.float32, device="cuda")]
+
+    # the 8K batch-1 layer shape, 28 layers cycled in one graph (as the step)
+    cfg = W.QWEN2B_8K
+    nl, nq, nkv, bs, L = cfg["layers"], cfg["nq"], cfg["nkv"], cfg["kv_bs"], cfg["L"]
+    bt, nb = W.paged_block_tables(W.rng(6, 0, 1), [L], bs)
+    btd, ld = dev(bt), dev(np.array([L], np.int32))
+    slots = dev(W.slots_for_positions(bt, [0] * L, np.arange(L), bs))
+    layers = []
+    for layer in range(nl):
+        p = q40_pool(nb, bs, nkv)
+        kk = W.torch_normal((L, nkv, 128), "cuda", (6, layer, 0))
+        vv = W.torch_normal((L, nkv, 128), "cuda", (6, layer, 1))
+        K.kvq4_0_quantize_append(*p, kk, vv, slots)
+        layers.append((p, W.torch_normal((1, nq, 128), "cuda", (6, layer, 2)), torch.empty((1, nq, 128), device="cuda")))
+        del kk, vv
+    ws = K.alloc_workspace(K.kvq4_0_decode_workspace_size(1, nq, nkv, L), "cuda")
+
+    def q40_step():
+        for p, qd, out in layers:
+            K.kvq4_0_decode_attn(out, qd, *p, btd, ld, L, sm, 0, ws)
+    us = time_calls(torch, q40_step, 5, graph=True) / nl
+    report("q40_8k", "Q4_0 decode, 28 layers x (1 x 16 / 8 heads, 8192 tokens), per layer call (graph replay)",
+           L * nkv * 160, us, chunk_tokens=K.kvq4_0_decode_chunk_tokens(1, nkv, L))
+    del layers
+
+    # the batch-32 long-context layer in Q4_0
+    cfg = W.QWEN8B_B32
+    lens = W.qwen8b_lengths(0)
+    B, nq, nkv, bs = cfg["batch"], cfg["nq"], cfg["nkv"], cfg["kv_bs"]
+    bt, nb = W.paged_block_tables(W.rng(3, 0, 1), lens, bs)
+    p = q40_pool(nb, bs, nkv)
+    for b in range(B):
+        kk = W.torch_student_t3((int(lens[b]), nkv, 128), "cuda", (3, 0, b, 0))
+        vv = W.torch_student_t3((int(lens[b]), nkv, 128), "cuda", (3, 0, b, 1))
+        K.kvq4_0_quantize_append(*p, kk, vv,
+                                 dev(W.slots_for_positions(bt, [b] * int(lens[b]), np.arange(lens[b]), bs)))
+        del kk, vv
+    qd = W.torch_normal((B, nq, 128), "cuda", (3, 0, 99))
+    out = torch.empty((B, nq, 128), device="cuda")
+    btd, ld, L = dev(bt), dev(lens), int(lens.max())
+    ws = K.alloc_workspace(K.kvq4_0_decode_workspace_size(B, nq, nkv, L), "cuda")
+    us = time_calls(torch, lambda: K.kvq4_0_decode_attn(out, qd, *p, btd, ld, L, sm, 0, ws), 20)
+    report("q40_qwen8b_b32", f"Q4_0 decode layer, batch 32 x 32 / 8 heads, lengths U[1024, 32768] "
+           f"(sum {int(lens.sum())})", int(lens.sum()) * nkv * 160, us,
+           chunk_tokens=K.kvq4_0_decode_chunk_tokens(B, nkv, L))
+    del p
+
+    # 64K tokens written from bf16 into the Q4_0 pool, then a GQA-4 decode
+    cfg = W.APPEND_64K
+    n, nq, nkv, bs = cfg["n_tok"], cfg["nq"], cfg["nkv"], cfg["kv_bs"]
+    bt, nb = W.paged_block_tables(W.rng(4, 0, 1), [n], bs)
+    p = q40_pool(nb, bs, nkv)
+    kk = W.torch_outlier_normal_bf16((n, nkv, 128), "cuda", (4, 0, 0))
+    vv = W.torch_outlier_normal_bf16((n, nkv, 128), "cuda", (4, 0, 1))
+    slots = dev(W.slots_for_positions(bt, [0] * n, np.arange(n), bs))
+    us = time_calls(torch, lambda: K.kvq4_0_quantize_append(*p, kk, vv, slots), 20)
+    report("q40_append_64k", "Q4_0 write path, 65536 tokens x 8 kv heads from bf16",
+           n * nkv * (2 * 128 * 2 + 2 * 80), us)
+    qd = W.torch_normal((1, nq, 128), "cuda", (4, 0, 2))
+    out = torch.empty((1, nq, 128), device="cuda")
+    btd, ld = dev(bt), dev(np.array([n], np.int32))
+    ws = K.alloc_workspace(K.kvq4_0_decode_workspace_size(1, nq, nkv, n), "cuda")
+    us = time_calls(torch, lambda: K.kvq4_0_decode_attn(out, qd, *p, btd, ld, n, sm, 0, ws), 50)
+    report("q40_decode_64k", "Q4_0 decode, 1 sequence x 32 / 8 heads over the 65536 written tokens",
+           n * nkv * 160, us, chunk_tokens=K.kvq4_0_decode_chunk_tokens(1, nkv, n))
 
 
 def main():

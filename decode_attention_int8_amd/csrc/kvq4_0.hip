@@ -429,8 +429,8 @@ __device__ __forceinline__ void q40_write_partial(const DecodeArgs& a, QSmem40& 
     mcombine_write(a, sm, G, b, kh, c);
 }
 
-template <bool BS8, int OCC>
-__global__ __launch_bounds__(kWGThreads, OCC) void kvq4_0_decode_kernel(DecodeArgs a) {
+template <bool BS8>
+__global__ __launch_bounds__(kWGThreads, 2) void kvq4_0_decode_kernel(DecodeArgs a) {
     __shared__ QSmem40 sm;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -508,11 +508,7 @@ __global__ __launch_bounds__(kWGThreads, OCC) void kvq4_0_decode_kernel(DecodeAr
 
 template <bool BS8>
 inline void launch_q40_bs(const DecodeArgs& a, int n_wg, hipStream_t s) {
-    const dim3 grid(n_wg), block(kWGThreads);
-    if (a.tiles_per_wave > 1)
-        hipLaunchKernelGGL((kvq4_0_decode_kernel<BS8, 1>), grid, block, 0, s, a);
-    else
-        hipLaunchKernelGGL((kvq4_0_decode_kernel<BS8, 2>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((kvq4_0_decode_kernel<BS8>), dim3(n_wg), dim3(kWGThreads), 0, s, a);
 }
 
 }  // namespace kvq
@@ -553,7 +549,10 @@ extern "C" int kvq4_0_quantize_append(uint8_t* k_cache, uint8_t* v_cache, float*
 
 extern "C" int kvq4_0_decode_chunk_tokens(int batch, int nkv, int max_ctx_len) {
     if (batch < 0 || nkv < 1 || max_ctx_len < 0) return 0;
-    return default_tiles_per_wave((long)batch * nkv, max_ctx_len, batch <= 2 ? 8 : 4) * kChunkUnit;
+    // two workgroups per CU: at least 512 of them; few (sequence, head) units
+    // are long enough to take 8 tiles per wave, many balance better with 4
+    const long units = (long)batch * nkv;
+    return default_tiles_per_wave(units, max_ctx_len, units <= 16 ? 8 : 4, 512) * kChunkUnit;
 }
 
 static int resolve_chunk40(int batch, int nkv, int max_ctx_len, int chunk) {

@@ -225,13 +225,13 @@ __global__ __launch_bounds__(kMergeThreads) void kvq_merge_kernel(float* __restr
 // ----------------------------------------------------------------------------
 
 // Tokens per chunk: the largest power-of-two multiple of 256 that still gives
-// at least 256 workgroups (one per CU), capped at `max_tpw` x 256 tokens.
-// `units` = sequences x kv-heads, `max_len` the longest region.
-inline int default_tiles_per_wave(long units, long max_len, int max_tpw) {
+// at least `min_wg` workgroups (default one per CU), capped at `max_tpw` x 256
+// tokens.  `units` = sequences x kv-heads, `max_len` the longest region.
+inline int default_tiles_per_wave(long units, long max_len, int max_tpw, long min_wg = 256) {
     int tpw = 1;
     while (tpw < max_tpw) {
         const long next = (long)kChunkUnit * tpw * 2;
-        if (units * ((max_len + next - 1) / next) < 256) break;
+        if (units * ((max_len + next - 1) / next) < min_wg) break;
         tpw *= 2;
     }
     return tpw;

@@ -280,10 +280,10 @@ struct NoHook {
 
 // `after_qk` runs once the tile's keys are consumed (the walk issues the next
 // tile's value loads there).
-template <class Hook = NoHook>
+template <class Hook = NoHook, class Hook2 = NoHook>
 __device__ __forceinline__ void mtile_compute(const DecodeArgs& a, const MTile T, int base, int L, int lane,
                                               int wave, const MQuery& Q, MState& st, MSmem& sm,
-                                              Hook after_qk = Hook()) {
+                                              Hook after_qk = Hook(), Hook2 after_pv = Hook2()) {
     const int g = lane >> 4;
     const int m = lane & 15;
     // steps through LDS: lane l holds token base+l, the products need tokens
@@ -394,6 +394,7 @@ __device__ __forceinline__ void mtile_compute(const DecodeArgs& a, const MTile T
             st.acc[sl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, B, st.acc[sl], 0, 0, 0);
         }
     }
+    after_pv();
 }
 
 // Fold the waves' states (in LDS: per wave M, S and acc of each head) and

@@ -6,12 +6,11 @@
 
 namespace kvq {
 
-// OCC = workgroups per CU the registers are budgeted for.  With 2 the walk
-// fits only with some spilling; with 1 nothing spills, and a workgroup that
-// walks several tiles per wave streams faster that way, while one that walks
-// a single tile is better off sharing its CU.
-template <int NEWDT, bool BS8, int OCC>
-__global__ __launch_bounds__(kWGThreads, OCC) void kvq_decode_mfma_kernel(DecodeArgs a) {
+// Two workgroups per CU: the walk fits the 256 registers of that budget
+// because a tile's values are issued only after the previous tile's P.V,
+// when its values are dead (one value buffer, two key buffers).
+template <int NEWDT, bool BS8>
+__global__ __launch_bounds__(kWGThreads, 2) void kvq_decode_mfma_kernel(DecodeArgs a) {
     __shared__ MSmem sm;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -107,8 +106,8 @@ __global__ __launch_bounds__(kWGThreads, OCC) void kvq_decode_mfma_kernel(Decode
             mtile_compute(a, T, base, L, lane, wave, Q, st, sm);
     };
     // double-buffered walk: tile k+1's keys and steps are in flight while
-    // tile k is computed, its values from tile k's Q.K on; the table entries
-    // run one tile further ahead
+    // tile k is computed, its values from the end of tile k's P.V on; the
+    // table entries run one tile further ahead
     int base = first;
     for (int k = 0;;) {
         if (k + 1 >= n_tiles) {
@@ -117,7 +116,7 @@ __global__ __launch_bounds__(kWGThreads, OCC) void kvq_decode_mfma_kernel(Decode
         }
         mtile_issue<BS8, kIssueKeys | kIssueSteps>(a, raw, base + kChunkUnit, kh, lane, lo, B);
         raw = mtile_raw(a.r8, btb, base + 2 * kChunkUnit, a.log2_bs, lane);
-        mtile_compute(a, A, base, L, lane, wave, Q, st, sm, [&]() __attribute__((always_inline)) {
+        mtile_compute(a, A, base, L, lane, wave, Q, st, sm, NoHook(), [&]() __attribute__((always_inline)) {
             mtile_issue<BS8, kIssueValues>(a, 0, base + kChunkUnit, kh, lane, lo, B);
         });
         base += kChunkUnit;
@@ -128,7 +127,7 @@ __global__ __launch_bounds__(kWGThreads, OCC) void kvq_decode_mfma_kernel(Decode
         }
         mtile_issue<BS8, kIssueKeys | kIssueSteps>(a, raw, base + kChunkUnit, kh, lane, lo, A);
         raw = mtile_raw(a.r8, btb, base + 2 * kChunkUnit, a.log2_bs, lane);
-        mtile_compute(a, B, base, L, lane, wave, Q, st, sm, [&]() __attribute__((always_inline)) {
+        mtile_compute(a, B, base, L, lane, wave, Q, st, sm, NoHook(), [&]() __attribute__((always_inline)) {
             mtile_issue<BS8, kIssueValues>(a, 0, base + kChunkUnit, kh, lane, lo, A);
         });
         base += kChunkUnit;
@@ -137,25 +136,17 @@ __global__ __launch_bounds__(kWGThreads, OCC) void kvq_decode_mfma_kernel(Decode
     mwrite_partial(a, sm, st, G, b, kh, c, lane, wave);
 }
 
-template <bool BS8, int OCC>
-inline void launch_mfma_occ(const DecodeArgs& a, int n_wg, int new_dtype, hipStream_t s) {
-    const dim3 grid(n_wg), block(kWGThreads);
-    if (new_dtype == KVQ8_F32)
-        hipLaunchKernelGGL((kvq_decode_mfma_kernel<KVQ8_F32, BS8, OCC>), grid, block, 0, s, a);
-    else if (new_dtype == KVQ8_BF16)
-        hipLaunchKernelGGL((kvq_decode_mfma_kernel<KVQ8_BF16, BS8, OCC>), grid, block, 0, s, a);
-    else if (new_dtype == KVQ8_F16)
-        hipLaunchKernelGGL((kvq_decode_mfma_kernel<KVQ8_F16, BS8, OCC>), grid, block, 0, s, a);
-    else
-        hipLaunchKernelGGL((kvq_decode_mfma_kernel<-1, BS8, OCC>), grid, block, 0, s, a);
-}
-
 template <bool BS8>
 inline void launch_mfma_bs(const DecodeArgs& a, int n_wg, int new_dtype, hipStream_t s) {
-    if (a.tiles_per_wave > 1)
-        launch_mfma_occ<BS8, 1>(a, n_wg, new_dtype, s);
+    const dim3 grid(n_wg), block(kWGThreads);
+    if (new_dtype == KVQ8_F32)
+        hipLaunchKernelGGL((kvq_decode_mfma_kernel<KVQ8_F32, BS8>), grid, block, 0, s, a);
+    else if (new_dtype == KVQ8_BF16)
+        hipLaunchKernelGGL((kvq_decode_mfma_kernel<KVQ8_BF16, BS8>), grid, block, 0, s, a);
+    else if (new_dtype == KVQ8_F16)
+        hipLaunchKernelGGL((kvq_decode_mfma_kernel<KVQ8_F16, BS8>), grid, block, 0, s, a);
     else
-        launch_mfma_occ<BS8, 2>(a, n_wg, new_dtype, s);
+        hipLaunchKernelGGL((kvq_decode_mfma_kernel<-1, BS8>), grid, block, 0, s, a);
 }
 
 inline void launch_mfma(const DecodeArgs& a, int n_wg, int new_dtype, hipStream_t s) {
