@@ -9,6 +9,8 @@ Pins (tests/test_oracle_kvq4.py):
                        codes in [0, 15]; round-trip error <= half a step
                        ([P4] Sec. 3.2); constant groups are exact.
   pack/unpack_nibbles  round trip; even element in the high nibble.
+  pack/unpack_v4       round trip; every pair keeps the page's nibble order;
+                       single-pair placement at byte 4m + 2g + k.
   requantize_q8_to_q4  rows whose int8 values lie exactly on an int4 grid give
                        that grid's codes, scale and zero back; the int4 value
                        of every element is within half an int4 step of its
@@ -79,7 +81,8 @@ def dequantize_groups_q4(codes, scale, zero) -> np.ndarray:
 
 
 def pack_nibbles(codes) -> np.ndarray:
-    """Two codes per byte, even-indexed code in the high nibble ([P4] Sec. 3.2)."""
+    """Two codes per byte, even-indexed code in the high nibble ([P4] Sec. 3.2);
+    pair (2i, 2i + 1) in byte i.  The key rows of the int4 pool."""
     c = np.asarray(codes, dtype=np.uint8)
     return ((c[..., 0::2] << 4) | c[..., 1::2]).astype(np.uint8)
 
@@ -92,8 +95,32 @@ def unpack_nibbles(packed) -> np.ndarray:
     return out
 
 
+def _v4_pair_bytes() -> np.ndarray:
+    """Byte of each pair (2i, 2i + 1) in a value row: elements 64g + 4m + 2k and
+    + 1 (group g, k = 0, 1) sit in byte 4m + 2g + k, so the 4-byte word m holds
+    elements 4m .. 4m + 3 of both groups (this library's storage order; the
+    pairing and the nibble order are the page's)."""
+    e = 2 * np.arange(64)
+    g, m, k = e // 64, (e % 64) // 4, (e % 4) // 2
+    return 4 * m + 2 * g + k
+
+
+def pack_v4(codes) -> np.ndarray:
+    """Value row of the int4 pool: pairs packed as pack_nibbles, in the byte
+    order of _v4_pair_bytes.  [..., 128] -> uint8 [..., 64]."""
+    p = pack_nibbles(codes)
+    out = np.empty_like(p)
+    out[..., _v4_pair_bytes()] = p
+    return out
+
+
+def unpack_v4(packed) -> np.ndarray:
+    return unpack_nibbles(np.asarray(packed, dtype=np.uint8)[..., _v4_pair_bytes()])
+
+
 def quantize_append_q4(k_pool, v_pool, k_scale, k_zero, v_scale, v_zero, k_new, v_new, slots):
-    """Write path for the int4 pool: packed codes [n_blocks][kv_bs][nkv][64],
+    """Write path for the int4 pool: packed codes [n_blocks][kv_bs][nkv][64]
+    (keys as pack_nibbles, values as pack_v4),
     scale and zero [n_blocks][kv_bs][nkv][2] float16.  Slots outside the pool
     are skipped.  Pools are modified in place."""
     kc, ks, kz = quantize_groups_q4(k_new)
@@ -101,7 +128,7 @@ def quantize_append_q4(k_pool, v_pool, k_scale, k_zero, v_scale, v_zero, k_new, 
     nb, bs, nkv, _ = k_pool.shape
     slots = np.asarray(slots, dtype=np.int64)
     ok = (slots >= 0) & (slots < nb * bs)
-    for pool, val in ((k_pool, pack_nibbles(kc)), (v_pool, pack_nibbles(vc)),
+    for pool, val in ((k_pool, pack_nibbles(kc)), (v_pool, pack_v4(vc)),
                       (k_scale, ks), (k_zero, kz), (v_scale, vs), (v_zero, vz)):
         flat = pool.reshape((nb * bs,) + pool.shape[2:])
         flat[slots[ok]] = val[ok]
@@ -174,7 +201,7 @@ def decode_attention_mixed(q, q4_pools, bt4, lens4, q8_pools, bt8, lens8, kv_bs:
             if n4 > 0:
                 G = lambda pool: kvq8.gather_rows(pool, bt4[b], n4, kv_bs, kh)  # noqa: E731
                 Ks.append(dequantize_groups_q4(unpack_nibbles(G(k4)), G(k4s), G(k4z)))
-                Vs.append(dequantize_groups_q4(unpack_nibbles(G(v4)), G(v4s), G(v4z)))
+                Vs.append(dequantize_groups_q4(unpack_v4(G(v4)), G(v4s), G(v4z)))
             if n8 > 0:
                 G = lambda pool: kvq8.gather_rows(pool, bt8[b], n8, kv_bs, kh)  # noqa: E731
                 Ks.append(kvq8.dequantize_rows_q8(G(k8), G(k8s)))

@@ -88,6 +88,22 @@ def test_pack_high_nibble_first_and_round_trip():
     p = kvq4.pack_nibbles(c)
     assert p.shape == (7, 64)
     assert np.array_equal(kvq4.unpack_nibbles(p), c)
+    pv = kvq4.pack_v4(c)
+    assert pv.shape == (7, 64) and np.array_equal(kvq4.unpack_v4(pv), c)
+    # value rows: the same bytes (pairs, even element high), in another order
+    assert sorted(pv[0].tolist()) == sorted(p[0].tolist())
+
+
+def test_value_row_pair_placement():
+    """Pair (e, e + 1), e = 64g + 4m + 2k, lands in byte 4m + 2g + k with the
+    even element in the high nibble: word m holds d = 4m .. 4m + 3 of both
+    groups."""
+    for e in range(0, 128, 2):
+        c = np.zeros(128, np.uint8)
+        c[e], c[e + 1] = 9, 4
+        g, m, k = e // 64, (e % 64) // 4, (e % 4) // 2
+        pv = kvq4.pack_v4(c)
+        assert np.flatnonzero(pv).tolist() == [4 * m + 2 * g + k] and pv[4 * m + 2 * g + k] == 0x94
 
 
 def _pools(r, B, n4, n8, nkv, kv_bs, k4=None, v4=None, k8=None, v8=None):
@@ -202,11 +218,12 @@ def test_requantize_reproduces_an_int4_grid(j):
     dst = r.permutation(5 * bs)[:n]
     kvq4.requantize_q8_to_q4(q8, q4, src, dst)
     k4, k4s, k4z, v4, v4s, v4z = q4
-    for pool8, (packed, sc, zp) in ((kc8, (k4, k4s, k4z)), (vc8, (v4, v4s, v4z))):
+    for pool8, (packed, sc, zp), unpack in ((kc8, (k4, k4s, k4z), kvq4.unpack_nibbles),
+                                            (vc8, (v4, v4s, v4z), kvq4.unpack_v4)):
         c, z = want[id(pool8)]
         c = c.reshape((-1,) + c.shape[2:])[src]          # [n][nkv][group][64]
         z = z.reshape((-1,) + z.shape[2:])[src]          # [n][nkv][group]
-        got = kvq4.unpack_nibbles(packed.reshape((-1,) + packed.shape[2:])[dst]).reshape(c.shape)
+        got = unpack(packed.reshape((-1,) + packed.shape[2:])[dst]).reshape(c.shape)
         assert np.array_equal(got, c)
         assert np.all(sc.reshape(-1, nkv, 2)[dst] == np.float16(8 * 2.0 ** -j))
         assert np.array_equal(zp.reshape(-1, nkv, 2)[dst].astype(np.int64), z)
@@ -229,9 +246,10 @@ def test_requantize_error_within_half_an_int4_step():
     dst = r.permutation(8 * bs)[:n]
     kvq4.requantize_q8_to_q4(q8, q4, src, dst)
     k4, k4s, k4z, v4, v4s, v4z = q4
-    for (pool, st), (packed, sc, zp) in (((kc8, ks8), (k4, k4s, k4z)), ((vc8, vs8), (v4, v4s, v4z))):
+    for (pool, st), (packed, sc, zp), unpack in (((kc8, ks8), (k4, k4s, k4z), kvq4.unpack_nibbles),
+                                                 ((vc8, vs8), (v4, v4s, v4z), kvq4.unpack_v4)):
         x8 = pool.reshape(-1, nkv, 128)[src].astype(np.float64) * st.reshape(-1, nkv)[src][..., None]
-        c = kvq4.unpack_nibbles(packed.reshape(-1, nkv, 64)[dst]).astype(np.float64)
+        c = unpack(packed.reshape(-1, nkv, 64)[dst]).astype(np.float64)
         s = np.repeat(sc.reshape(-1, nkv, 2)[dst].astype(np.float64), 64, axis=-1)
         z = np.repeat(zp.reshape(-1, nkv, 2)[dst].astype(np.float64), 64, axis=-1)
         err = np.abs((c - z) * s - x8)
