@@ -76,11 +76,24 @@ __device__ __forceinline__ void quantize_group8x8(const float (&x)[8], uint32_t&
 constexpr int kRowsPerGroup = 4;            // rows per 16-lane group, loads first
 constexpr int kRowsPerBlock = 16 * kRowsPerGroup;
 
+// Store one row: lane l16 packed the pairs of its 8 values (elements 8 l16 ..
+// 8 l16 + 7) into `packed`; `other` is lane l16 ^ 8's word.  Key rows keep
+// pair i in byte i.  Value rows put the pair 64g + 4m + 2k, +1 at byte
+// 4m + 2g + k (word m = d 4m .. 4m+3 of both groups): with j = l16 % 8, the
+// low halves of lanes j and j + 8 form word 2j, their high halves word 2j+1.
 __device__ __forceinline__ void store_q4_row(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
                                              uint16_t* __restrict__ ks, uint16_t* __restrict__ kz,
                                              uint16_t* __restrict__ vs, uint16_t* __restrict__ vz, int kind,
-                                             size_t dst, int l16, uint32_t packed, uint16_t s16, uint16_t z16) {
-    *reinterpret_cast<uint32_t*>((kind ? vc : kc) + dst * (kHD / 2) + 4 * l16) = packed;
+                                             size_t dst, int l16, uint32_t packed, uint32_t other, uint16_t s16,
+                                             uint16_t z16) {
+    if (kind == 0) {
+        *reinterpret_cast<uint32_t*>(kc + dst * (kHD / 2) + 4 * l16) = packed;
+    } else {
+        const int j = l16 & 7;
+        const uint32_t word = (l16 < 8) ? ((packed & 0xFFFFu) | (other << 16))
+                                        : ((other >> 16) | (packed & 0xFFFF0000u));
+        *reinterpret_cast<uint32_t*>(vc + dst * (kHD / 2) + 4 * (2 * j + (l16 >> 3))) = word;
+    }
     if ((l16 & 7) == 0) {
         (kind ? vs : ks)[dst * 2 + (l16 >> 3)] = s16;
         (kind ? vz : kz)[dst * 2 + (l16 >> 3)] = z16;
@@ -108,11 +121,12 @@ __global__ __launch_bounds__(256) void kvq4_quantize_append_kernel(
         uint32_t packed;
         uint16_t s16, z16;
         quantize_group8x8(x[k], packed, s16, z16);
+        const uint32_t other = (uint32_t)dpp_i<kDppRowRor8>((int)packed);     // lane l16 ^ 8
         if (row >= n_rows || slot[k] < 0 || slot[k] >= n_slots) continue;   // uniform per 16-lane row
         const long tr = row >> 1;
         const long tok = tr / nkv;
         store_q4_row(kc, vc, ks, kz, vs, vz, (int)(row & 1), (size_t)slot[k] * nkv + (size_t)(tr - tok * nkv), l16,
-                     packed, s16, z16);
+                     packed, other, s16, z16);
     }
 }
 
@@ -160,11 +174,12 @@ __global__ __launch_bounds__(256) void kvq4_requantize_q8_kernel(
         uint32_t packed;
         uint16_t s16, z16;
         quantize_group8x8(x, packed, s16, z16);
+        const uint32_t other = (uint32_t)dpp_i<kDppRowRor8>((int)packed);     // lane l16 ^ 8
         if (row >= n_rows || s8[k] < 0 || s8[k] >= n_slots8 || s4[k] < 0 || s4[k] >= n_slots4) continue;
         const long tr = row >> 1;
         const long tok = tr / nkv;
         store_q4_row(kc4, vc4, ks4, kz4, vs4, vz4, (int)(row & 1), (size_t)s4[k] * nkv + (size_t)(tr - tok * nkv),
-                     l16, packed, s16, z16);
+                     l16, packed, other, s16, z16);
     }
 }
 

@@ -188,8 +188,10 @@ extern "C" int kvq8_qk_partials(int32_t* partials, const float* q, int batch, in
 
 extern "C" int kvq4_decode_chunk_tokens(int batch, int nkv, int max_len4, int max_len8) {
     if (batch < 0 || nkv < 1 || max_len4 < 0 || max_len8 < 0) return 0;
-    // the int4 kernel at GQA > 4 runs one workgroup per CU: long work items
-    return default_tiles_per_wave((long)batch * nkv, (long)max_len4 + max_len8, 8) * kChunkUnit;
+    // two workgroups per CU: at least 512 of them; few (sequence, head) units
+    // are long enough to take 8 tiles per wave, many balance better with 4
+    const long units = (long)batch * nkv;
+    return default_tiles_per_wave(units, (long)max_len4 + max_len8, units <= 16 ? 8 : 4, 512) * kChunkUnit;
 }
 
 static int resolve_chunk4(int batch, int nkv, int max_len4, int max_len8, int chunk) {

@@ -2,25 +2,25 @@
 // [P3] Sec. 2 single pass): chunks of the int4 pool and of the int8 window
 // pool share one launch and one merge; int8 chunks run the int8 tile code.
 //
-// int4 tile (64 tokens, lane = (g, m) as in the int8 kernel), query heads in
-// sets of four (S = 0, 1):
+// int4 tile (64 tokens, lane = (g, m) as in the int8 kernel), up to 8 query
+// heads in one operand set:
 //
 // Q.K: v_mfma_i32_16x16x64_i8 per (token group v, row half h).  A = unsigned
 //   codes of token 16v+m, d = 64h+16g .. +15, unpacked from 8 packed bytes as
 //   [even d | odd d] per 4-byte word (two VALU ops per word); B = the query
-//   codes in the same order, column c = (head 4S + c/4, block parity c%2):
-//   column c receives P_b = sum q*c over block 2h + (c & 1).  The score term
-//   of a block is qsc_b * s_g * (P_b - z_g * R_b) with R_b = sum q over the
-//   block (exact integers, applied in float), g = h the code group.
+//   codes in the same order, column c = (head c/2, block parity c%2):
+//   column c receives P_b = sum q*c over block 2h + (c & 1), which lies in
+//   code group h.  The score term of a block is qsc_b * s_h * (P_b - z_h R_b)
+//   with R_b = sum q over the block (exact integers, applied in float).
 //
-// P.V: v_mfma_f32_16x16x32_f16 per (pair of token groups, d-slice s) and
-//   head set.  The group scale differs between the two halves of a row, so
-//   the weights carry it: row c = (head 4S + c/4, group (c/2)&1, part c&1),
-//   A = p * vscale_{t,group} (f16 high part or rounded remainder, times 2^E);
-//   B = c - z_{t,group of the column} as f16 (exact small integers), column
-//   m <-> d = 8m + s, group m/8.  Rows whose group differs from the column's
-//   are discarded; lane (g, m) keeps rows 2(m/8) and 2(m/8)+1 of head 4S+g.
-//   Each lane's softmax values are exactly the weights it supplies.
+// P.V: v_mfma_f32_16x16x32_f16 per (pair of token groups, d-slice s).  A
+//   value row stores the pair 64G + 4m + 2k, +1 at byte 4m + 2G + k, so the
+//   word of lane m holds d = 4m .. 4m+3 of both code groups and slice s
+//   covers d = 64(s/4) + 4m + (s%4): group s/4 for every column.  Its A
+//   operand is the weights p * vscale of that group (f16 high part or
+//   rounded remainder, times 2^E; row c = (head c/2, part c%2)) and B is
+//   c - z of that group as f16 (exact small integers).  Each lane's softmax
+//   values are exactly the weights it supplies.
 #pragma once
 
 #include "kvq_decode_mfma_kernel.h"
@@ -43,17 +43,9 @@ struct MTile4 {
 };
 
 struct MQuery4 {
-    v4i_t op[2][2];      // [set][h] B operand (codes in [even | odd] order)
-    float sc[2][2];      // [set][h] query block scale of column m
-    float R[2][2];       // [set][h] sum of the query codes of that block
-};
-
-template <int NSET>
-struct MState4 {
-    float M[NSET];       // running max of head 4S + m/4
-    float S[NSET];       // this lane's share of its sum
-    int E;               // accumulator scale exponent (wave-uniform)
-    v4f_t acc[NSET][8];  // [set][slice]: rows 4g+r (head 4S+g, group r/2, part r%2)
+    v4i_t op[2];         // [h] B operand (codes in [even | odd] order)
+    float sc[2];         // [h] query block scale of column m
+    float R[2];          // [h] sum of the query codes of that block
 };
 
 // codes of 16 consecutive d (4 words, natural order) -> [even | odd] per 8
@@ -68,26 +60,22 @@ __device__ __forceinline__ v4i_t unpack_q4(v2u_t w) {
     return v4i_t{(int)((w.x >> 4) & kNib), (int)(w.x & kNib), (int)((w.y >> 4) & kNib), (int)(w.y & kNib)};
 }
 
-template <int NSET>
 __device__ __forceinline__ MQuery4 load_q4_operand(const QSmem& sm, int G, int g, int m) {
     MQuery4 Q;
+    const int H = m >> 1;
+    const bool live = H < G;
+    const int Hc = live ? H : 0;
+    const bool mine = live && ((g >> 1) == (m & 1));
 #pragma unroll
-    for (int S = 0; S < NSET; ++S) {
-        const int H = 4 * S + (m >> 2);
-        const bool live = H < G;
-        const int Hc = live ? H : 0;
-        const bool mine = live && ((g >> 1) == (m & 1));
+    for (int h = 0; h < 2; ++h) {
+        const v4u_t c = *reinterpret_cast<const v4u_t*>(&sm.qc[Hc][16 * h + 4 * g]);
+        Q.op[h] = mine ? even_odd_order(c) : v4i_t{0, 0, 0, 0};
+        const int blk = 2 * h + (m & 1);
+        Q.sc[h] = live ? sm.qs[Hc][blk] : 0.0f;
+        int r = 0;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const v4u_t c = *reinterpret_cast<const v4u_t*>(&sm.qc[Hc][16 * h + 4 * g]);
-            Q.op[S][h] = mine ? even_odd_order(c) : v4i_t{0, 0, 0, 0};
-            const int blk = 2 * h + (m & 1);
-            Q.sc[S][h] = live ? sm.qs[Hc][blk] : 0.0f;
-            int r = 0;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) r = __builtin_amdgcn_sdot4((int)sm.qc[Hc][8 * blk + i], 0x01010101, r, false);
-            Q.R[S][h] = live ? (float)r : 0.0f;
-        }
+        for (int i = 0; i < 8; ++i) r = __builtin_amdgcn_sdot4((int)sm.qc[Hc][8 * blk + i], 0x01010101, r, false);
+        Q.R[h] = live ? (float)r : 0.0f;
     }
     return Q;
 }
@@ -151,9 +139,8 @@ __device__ __forceinline__ void mtile4_issue(const DecodeArgs& a, int raw, int b
     T.vz = *reinterpret_cast<const uint32_t*>(a.v4z + (size_t)srow * 2);
 }
 
-template <int NSET>
 __device__ __forceinline__ void mtile4_compute(const DecodeArgs& a, const MTile4& T, int base, int L, int lane,
-                                               int wave, const MQuery4& Q, MState4<NSET>& st, MSmem4& sm) {
+                                               int wave, const MQuery4& Q, MState& st, MSmem4& sm) {
     const int g = lane >> 4;
     const int m = lane & 15;
     // per-token scales through LDS (lane l holds token base+l)
@@ -168,9 +155,7 @@ __device__ __forceinline__ void mtile4_compute(const DecodeArgs& a, const MTile4
             if (Et < st.E) {
                 const float f = exp2i(Et - st.E);
 #pragma unroll
-                for (int S = 0; S < NSET; ++S)
-#pragma unroll
-                    for (int sl = 0; sl < 8; ++sl) st.acc[S][sl] *= f;
+                for (int sl = 0; sl < 8; ++sl) st.acc[sl] *= f;
                 st.E = Et;
             }
         }
@@ -188,17 +173,13 @@ __device__ __forceinline__ void mtile4_compute(const DecodeArgs& a, const MTile4
         sm.v4c[wave][1][lane] = __builtin_bit_cast(uint16_t, (_Float16)(-(1024.0f + z1)));
     }
     // Q.K and scores
-    float s[NSET][4][4];
+    float s[4][4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-        v4i_t P[NSET][2];
+        v4i_t P[2];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const v4i_t A = unpack_q4(T.k[v][h]);
-#pragma unroll
-            for (int S = 0; S < NSET; ++S)
-                P[S][h] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, Q.op[S][h], v4i_t{0, 0, 0, 0}, 0, 0, 0);
-        }
+        for (int h = 0; h < 2; ++h)
+            P[h] = __builtin_amdgcn_mfma_i32_16x16x64_i8(unpack_q4(T.k[v][h]), Q.op[h], v4i_t{0, 0, 0, 0}, 0, 0, 0);
         const float4 ks0 = *reinterpret_cast<const float4*>(&sm.k4s[wave][0][16 * v + 4 * g]);
         const float4 ks1 = *reinterpret_cast<const float4*>(&sm.k4s[wave][1][16 * v + 4 * g]);
         const float4 kz0 = *reinterpret_cast<const float4*>(&sm.k4z[wave][0][16 * v + 4 * g]);
@@ -208,70 +189,73 @@ __device__ __forceinline__ void mtile4_compute(const DecodeArgs& a, const MTile4
         const float kZ[2][4] = {{kz0.x, kz0.y, kz0.z, kz0.w}, {kz1.x, kz1.y, kz1.z, kz1.w}};
         const float kB[4] = {kb.x, kb.y, kb.z, kb.w};
 #pragma unroll
-        for (int S = 0; S < NSET; ++S)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                // P - z R is an exact integer below 2^17 in float
-                float f = fmaf(-kZ[0][r], Q.R[S][0], (float)P[S][0][r]) * (Q.sc[S][0] * kS[0][r]);
-                f = fmaf(fmaf(-kZ[1][r], Q.R[S][1], (float)P[S][1][r]), Q.sc[S][1] * kS[1][r], f);
-                s[S][v][r] = f + dpp_f<kDppXor1>(f) + kB[r];
-            }
+        for (int r = 0; r < 4; ++r) {
+            // P - z R is an exact integer below 2^17 in float
+            float f = fmaf(-kZ[0][r], Q.R[0], (float)P[0][r]) * (Q.sc[0] * kS[0][r]);
+            f = fmaf(fmaf(-kZ[1][r], Q.R[1], (float)P[1][r]), Q.sc[1] * kS[1][r], f);
+            s[v][r] = f + dpp_f<kDppXor1>(f) + kB[r];
+        }
     }
-    // softmax per head set
-    uint32_t wop[NSET][4][2];
-    const int grp_row = (m >> 1) & 1;   // code group of this lane's weight row
+    // softmax: lane (g, m) owns head m/2 for tokens 16v + 4g + r
+    float mt = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mt = fmaxf(mt, s[v][r]);
+    mt = fmaxf(mt, swz_xor16(mt));
+    mt = fmaxf(mt, xor32(mt));
+    if (__builtin_amdgcn_ballot_w64(mt > st.M) != 0) {
+        const float fac = (mt > st.M) ? __builtin_amdgcn_exp2f(st.M - mt) : 1.0f;
+        st.M = fmaxf(st.M, mt);
+        st.S *= fac;
+        // accumulator rows of this lane: heads 2g and 2g+1, whose factors sit
+        // in lanes 4g and 4g+2
+        const float fa = bperm_f(fac, 4 * g);
+        const float fb = bperm_f(fac, 4 * g + 2);
+#pragma unroll
+        for (int sl = 0; sl < 8; ++sl) {
+            st.acc[sl][0] *= fa;
+            st.acc[sl][1] *= fa;
+            st.acc[sl][2] *= fb;
+            st.acc[sl][3] *= fb;
+        }
+    }
+    const float mref = (st.M == -INFINITY) ? 0.0f : st.M;
     const bool lo_row = m & 1;
+    float p[4][4];
 #pragma unroll
-    for (int S = 0; S < NSET; ++S) {
-        float mt = -INFINITY;
+    for (int v = 0; v < 4; ++v)
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) mt = fmaxf(mt, s[S][v][r]);
-        mt = fmaxf(mt, swz_xor16(mt));
-        mt = fmaxf(mt, xor32(mt));
-        if (__builtin_amdgcn_ballot_w64(mt > st.M[S]) != 0) {
-            const float fac = (mt > st.M[S]) ? __builtin_amdgcn_exp2f(st.M[S] - mt) : 1.0f;
-            st.M[S] = fmaxf(st.M[S], mt);
-            st.S[S] *= fac;
-            // accumulator rows of this lane: head 4S + g, whose factor sits in lane 4g
-            const float fa = bperm_f(fac, 4 * g);
-#pragma unroll
-            for (int sl = 0; sl < 8; ++sl) st.acc[S][sl] *= fa;
+        for (int r = 0; r < 4; ++r) {
+            p[v][r] = __builtin_amdgcn_exp2f(s[v][r] - mref);
+            st.S += p[v][r];
         }
-        const float mref = (st.M[S] == -INFINITY) ? 0.0f : st.M[S];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const float4 vv = *reinterpret_cast<const float4*>(&sm.v4s[wave][grp_row][16 * v + 4 * g]);
-            const float v4[4] = {vv.x, vv.y, vv.z, vv.w};
-            float w[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float p = __builtin_amdgcn_exp2f(s[S][v][r] - mref);
-                st.S[S] += p;
-                w[r] = p * v4[r];
-            }
-#pragma unroll
-            for (int pr = 0; pr < 2; ++pr) {
-                const float h0 = __uint_as_float(__float_as_uint(w[2 * pr]) & 0xFFFFE000u);
-                const float h1 = __uint_as_float(__float_as_uint(w[2 * pr + 1]) & 0xFFFFE000u);
-                const uint32_t hi = pack_f16_rtz(h0, h1);
-                const uint32_t lo = pack_f16(w[2 * pr] - h0, w[2 * pr + 1] - h1);
-                wop[S][v][pr] = lo_row ? lo : hi;
-            }
-        }
-    }
-    // P.V: value codes minus zero point as f16, shared by the head sets
-    const int grp_col = m >> 3;
+    // P.V: one A operand per code group, value codes minus zero point as f16
 #pragma unroll
     for (int vp = 0; vp < 2; ++vp) {
-        // -(1024 + z) for the 8 tokens of this lane's k-range, in pairs
-        uint32_t zc[4];
+        v8h_t A[2];
+        uint32_t zc[2][4];      // [group]: -(1024 + z) of the lane's 8 tokens, in pairs
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const uint2 zz = *reinterpret_cast<const uint2*>(&sm.v4c[wave][grp_col][16 * (2 * vp + q) + 4 * g]);
-            zc[2 * q] = zz.x;
-            zc[2 * q + 1] = zz.y;
+        for (int G2 = 0; G2 < 2; ++G2) {
+            uint32_t wop[2][2];
+#pragma unroll
+            for (int q2 = 0; q2 < 2; ++q2) {
+                const int v = 2 * vp + q2;
+                const float4 vv = *reinterpret_cast<const float4*>(&sm.v4s[wave][G2][16 * v + 4 * g]);
+                const float w[4] = {p[v][0] * vv.x, p[v][1] * vv.y, p[v][2] * vv.z, p[v][3] * vv.w};
+#pragma unroll
+                for (int pr = 0; pr < 2; ++pr) {
+                    const float h0 = __uint_as_float(__float_as_uint(w[2 * pr]) & 0xFFFFE000u);
+                    const float h1 = __uint_as_float(__float_as_uint(w[2 * pr + 1]) & 0xFFFFE000u);
+                    const uint32_t hi = pack_f16_rtz(h0, h1);
+                    const uint32_t lo = pack_f16(w[2 * pr] - h0, w[2 * pr + 1] - h1);
+                    wop[q2][pr] = lo_row ? lo : hi;
+                }
+                const uint2 zz = *reinterpret_cast<const uint2*>(&sm.v4c[wave][G2][16 * v + 4 * g]);
+                zc[G2][2 * q2] = zz.x;
+                zc[G2][2 * q2 + 1] = zz.y;
+            }
+            A[G2] = __builtin_bit_cast(v8h_t, v4u_t{wop[0][0], wop[0][1], wop[1][0], wop[1][1]});
         }
         // even / odd codes of the 8 tokens' words
         uint32_t ev[8], od[8];
@@ -281,15 +265,11 @@ __device__ __forceinline__ void mtile4_compute(const DecodeArgs& a, const MTile4
             ev[q] = (w >> 4) & kNib;
             od[q] = w & kNib;
         }
-        v8h_t A[NSET];
-#pragma unroll
-        for (int S = 0; S < NSET; ++S)
-            A[S] = __builtin_bit_cast(v8h_t, v4u_t{wop[S][2 * vp][0], wop[S][2 * vp][1], wop[S][2 * vp + 1][0],
-                                                   wop[S][2 * vp + 1][1]});
 #pragma unroll
         for (int sl = 0; sl < 8; ++sl) {
-            // d = 8m + sl: byte sl/2 of the word, high nibble for even sl
+            // d = 64(sl/4) + 4m + sl%4: byte sl/2 of the word, high nibble for even sl
             const int byte = sl >> 1;
+            const int G2 = sl >> 2;
             uint32_t bw[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -298,56 +278,47 @@ __device__ __forceinline__ void mtile4_compute(const DecodeArgs& a, const MTile4
                 // [code_a, 0, code_b, 0] | 0x6400 in each half = 1024 + code
                 const uint32_t sel = (uint32_t)byte | 0x0C000000u | ((uint32_t)(4 + byte) << 16) | 0x00000C00u;
                 const uint32_t x = __builtin_amdgcn_perm(xb, xa, sel) | 0x64006400u;
-                bw[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h_t, x) + __builtin_bit_cast(v2h_t, zc[i]));
+                bw[i] = __builtin_bit_cast(uint32_t,
+                                           __builtin_bit_cast(v2h_t, x) + __builtin_bit_cast(v2h_t, zc[G2][i]));
             }
             const v8h_t B = __builtin_bit_cast(v8h_t, v4u_t{bw[0], bw[1], bw[2], bw[3]});
-#pragma unroll
-            for (int S = 0; S < NSET; ++S)
-                st.acc[S][sl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[S], B, st.acc[S][sl], 0, 0, 0);
+            st.acc[sl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[G2], B, st.acc[sl], 0, 0, 0);
         }
     }
 }
 
 // Fold an int4 wave state into the workgroup's LDS layout (per wave and
-// head: M, S, acc[128]).
-template <int NSET>
-__device__ __forceinline__ void mwave4_to_lds(MSmem4& sm, MState4<NSET>& st, int G, int lane, int wave) {
+// head: M, S, acc[128]); slice s of lane m holds d = 64(s/4) + 4m + s%4.
+__device__ __forceinline__ void mwave4_to_lds(MSmem4& sm, MState& st, int G, int lane, int wave) {
     const int g = lane >> 4;
     const int m = lane & 15;
+    float S = st.S;
+    S += swz_xor16(S);
+    S += xor32(S);
+    if (g == 0 && (m & 1) == 0 && (m >> 1) < G) {
+        sm.m[wave][m >> 1] = st.M;
+        sm.s[wave][m >> 1] = S;
+    }
     const float unscale = exp2i(-st.E);
 #pragma unroll
-    for (int S = 0; S < NSET; ++S) {
-        float Ssum = st.S[S];
-        Ssum += swz_xor16(Ssum);
-        Ssum += xor32(Ssum);
-        const int Hs = 4 * S + (m >> 2);
-        if (g == 0 && (m & 3) == 0 && Hs < G) {
-            sm.m[wave][Hs] = st.M[S];
-            sm.s[wave][Hs] = Ssum;
-        }
-        const int H = 4 * S + g;
+    for (int hh = 0; hh < 2; ++hh) {
+        const int H = 2 * g + hh;
         if (H < G) {
-            const int r0 = 2 * (m >> 3);
             float o[8];
 #pragma unroll
-            for (int sl = 0; sl < 8; ++sl) {
-                const float hi = (m >> 3) ? st.acc[S][sl][2] : st.acc[S][sl][0];
-                const float lo = (m >> 3) ? st.acc[S][sl][3] : st.acc[S][sl][1];
-                o[sl] = (hi + lo) * unscale;
-            }
-            (void)r0;
-            float4* dst = reinterpret_cast<float4*>(&sm.acc[wave][H][8 * m]);
-            dst[0] = make_float4(o[0], o[1], o[2], o[3]);
-            dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+            for (int sl = 0; sl < 8; ++sl) o[sl] = (st.acc[sl][2 * hh] + st.acc[sl][2 * hh + 1]) * unscale;
+            *reinterpret_cast<float4*>(&sm.acc[wave][H][4 * m]) = make_float4(o[0], o[1], o[2], o[3]);
+            *reinterpret_cast<float4*>(&sm.acc[wave][H][64 + 4 * m]) = make_float4(o[4], o[5], o[6], o[7]);
         }
     }
 }
 
 // One workgroup = (sequence, kv-head, chunk) of either pool: chunks
-// [0, r4.max_chunks) cover the int4 region, the rest the int8 window.
-// Two head sets keep twice the accumulators: one wave per SIMD, no spills.
-template <int NSET, bool BS8>
-__global__ __launch_bounds__(kWGThreads, NSET == 2 ? 1 : 2) void kvq4_decode_mfma_kernel(DecodeArgs a) {
+// [0, r4.max_chunks) cover the int4 region, the rest the int8 window.  Two
+// workgroups per CU (the int8 walk issues values after P.V, as in the int8
+// kernel).
+template <bool BS8>
+__global__ __launch_bounds__(kWGThreads, 2) void kvq4_decode_mfma_kernel(DecodeArgs a) {
     __shared__ MSmem4 sm;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -385,38 +356,35 @@ __global__ __launch_bounds__(kWGThreads, NSET == 2 ? 1 : 2) void kvq4_decode_mfm
         __asm__ volatile("" ::: "memory");
         quantize_q4(qx, G, sm.q);
         lds_barrier();
-        const MQuery4 Q = load_q4_operand<NSET>(sm.q, G, g, m);
-        MState4<NSET> st;
-#pragma unroll
-        for (int S = 0; S < NSET; ++S) {
-            st.M[S] = -INFINITY;
-            st.S[S] = 0.0f;
-#pragma unroll
-            for (int sl = 0; sl < 8; ++sl) st.acc[S][sl] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
-        }
+        const MQuery4 Q = load_q4_operand(sm.q, G, g, m);
+        MState st;
+        st.M = -INFINITY;
+        st.S = 0.0f;
         st.E = 100;
+#pragma unroll
+        for (int sl = 0; sl < 8; ++sl) st.acc[sl] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
         int base = first;
         for (int k = 0;;) {
             if (k + 1 >= n_tiles) {
-                mtile4_compute<NSET>(a, A, base, L, lane, wave, Q, st, sm);
+                mtile4_compute(a, A, base, L, lane, wave, Q, st, sm);
                 break;
             }
             mtile4_issue<BS8>(a, raw, base + kChunkUnit, kh, lane, lo, B);
             raw = mtile_raw(reg, btb, base + 2 * kChunkUnit, a.log2_bs, lane);
-            mtile4_compute<NSET>(a, A, base, L, lane, wave, Q, st, sm);
+            mtile4_compute(a, A, base, L, lane, wave, Q, st, sm);
             base += kChunkUnit;
             ++k;
             if (k + 1 >= n_tiles) {
-                mtile4_compute<NSET>(a, B, base, L, lane, wave, Q, st, sm);
+                mtile4_compute(a, B, base, L, lane, wave, Q, st, sm);
                 break;
             }
             mtile4_issue<BS8>(a, raw, base + kChunkUnit, kh, lane, lo, A);
             raw = mtile_raw(reg, btb, base + 2 * kChunkUnit, a.log2_bs, lane);
-            mtile4_compute<NSET>(a, B, base, L, lane, wave, Q, st, sm);
+            mtile4_compute(a, B, base, L, lane, wave, Q, st, sm);
             base += kChunkUnit;
             ++k;
         }
-        mwave4_to_lds<NSET>(sm, st, G, lane, wave);
+        mwave4_to_lds(sm, st, G, lane, wave);
         lds_barrier();
         mcombine_write(a, sm, G, b, kh, c);
     } else {
@@ -440,18 +408,22 @@ __global__ __launch_bounds__(kWGThreads, NSET == 2 ? 1 : 2) void kvq4_decode_mfm
                 mtile_compute(a, A, base, L, lane, wave, Q, st, sm);
                 break;
             }
-            mtile_issue<BS8>(a, raw, base + kChunkUnit, kh, lane, lo, B);
+            mtile_issue<BS8, kIssueKeys | kIssueSteps>(a, raw, base + kChunkUnit, kh, lane, lo, B);
             raw = mtile_raw(reg, btb, base + 2 * kChunkUnit, a.log2_bs, lane);
-            mtile_compute(a, A, base, L, lane, wave, Q, st, sm);
+            mtile_compute(a, A, base, L, lane, wave, Q, st, sm, NoHook(), [&]() __attribute__((always_inline)) {
+                mtile_issue<BS8, kIssueValues>(a, 0, base + kChunkUnit, kh, lane, lo, B);
+            });
             base += kChunkUnit;
             ++k;
             if (k + 1 >= n_tiles) {
                 mtile_compute(a, B, base, L, lane, wave, Q, st, sm);
                 break;
             }
-            mtile_issue<BS8>(a, raw, base + kChunkUnit, kh, lane, lo, A);
+            mtile_issue<BS8, kIssueKeys | kIssueSteps>(a, raw, base + kChunkUnit, kh, lane, lo, A);
             raw = mtile_raw(reg, btb, base + 2 * kChunkUnit, a.log2_bs, lane);
-            mtile_compute(a, B, base, L, lane, wave, Q, st, sm);
+            mtile_compute(a, B, base, L, lane, wave, Q, st, sm, NoHook(), [&]() __attribute__((always_inline)) {
+                mtile_issue<BS8, kIssueValues>(a, 0, base + kChunkUnit, kh, lane, lo, A);
+            });
             base += kChunkUnit;
             ++k;
         }
@@ -459,20 +431,12 @@ __global__ __launch_bounds__(kWGThreads, NSET == 2 ? 1 : 2) void kvq4_decode_mfm
     }
 }
 
-template <bool BS8>
-inline void launch_mfma4_bs(const DecodeArgs& a, int n_wg, hipStream_t s) {
-    const dim3 grid(n_wg), block(kWGThreads);
-    if (a.nq / a.nkv > 4)
-        hipLaunchKernelGGL((kvq4_decode_mfma_kernel<2, BS8>), grid, block, 0, s, a);
-    else
-        hipLaunchKernelGGL((kvq4_decode_mfma_kernel<1, BS8>), grid, block, 0, s, a);
-}
-
 inline void launch_mfma4(const DecodeArgs& a, int n_wg, hipStream_t s) {
+    const dim3 grid(n_wg), block(kWGThreads);
     if (a.log2_bs < 4)
-        launch_mfma4_bs<true>(a, n_wg, s);
+        hipLaunchKernelGGL((kvq4_decode_mfma_kernel<true>), grid, block, 0, s, a);
     else
-        launch_mfma4_bs<false>(a, n_wg, s);
+        hipLaunchKernelGGL((kvq4_decode_mfma_kernel<false>), grid, block, 0, s, a);
 }
 
 // Enqueue the chunk kernel (if there is any context) and the merge kernel.
