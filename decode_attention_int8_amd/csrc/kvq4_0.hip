@@ -611,6 +611,6 @@ extern "C" int kvq4_0_decode_attn(float* out, const float* q, int batch, int nq,
         else
             launch_q40_bs<false>(a, (int)n_wg, s);
     }
-    hipLaunchKernelGGL(kvq_merge_kernel<>, dim3(a.batch * a.nq), dim3(kMergeThreads), 0, s, out, a);
+    launch_merge(a, out, s);
     return launch_status();
 }

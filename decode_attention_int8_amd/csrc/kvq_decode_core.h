@@ -138,28 +138,28 @@ __device__ __forceinline__ void quantize_row8x16(const float (&x)[16], uint4& co
 
 // Merge the chunk partials of one (sequence, query head) and normalize
 // ([P3] Sec. 2 seg. 3 across chunks): M = max_c M_c, S = sum_c S_c 2^(M_c-M),
-// out = sum_c acc_c 2^(M_c-M) / S.  256 threads: thread (part, d) owns output
-// dimension d for half of the chunks; the two halves meet in LDS.  Chunks are
-// read in batches of kMergeBatch with every load of a batch in flight (so up
-// to 2 * kMergeBatch chunks cost one memory round trip); the loads do not wait
-// for the context lengths (chunks past them are masked afterwards), and
-// batches are combined with a running maximum.
+// out = sum_c acc_c 2^(M_c-M) / S.  PARTS x 128 threads: thread (part, d)
+// owns output dimension d for a contiguous share of the chunks; the parts
+// meet in LDS.  Chunks are read in batches of kMergeBatch with every load of a
+// batch in flight (so up to PARTS * kMergeBatch chunks cost one memory round
+// trip); the loads do not wait for the context lengths (chunks past them are
+// masked afterwards), and batches are combined with a running maximum.
 constexpr int kMergeBatch = 16;
-constexpr int kMergeThreads = 2 * kHD;
+constexpr int kMergeThreads = 2 * kHD;          // PARTS = 2
+constexpr int kMergeThreadsWide = 8 * kHD;      // PARTS = 8, for more than 32 chunks
 
-// (a template so that every source that launches it may instantiate it)
-template <int = 0>
-__global__ __launch_bounds__(kMergeThreads) void kvq_merge_kernel(float* __restrict__ out, DecodeArgs a) {
-    __shared__ float other[kHD + 2];
+template <int PARTS>
+__global__ __launch_bounds__(PARTS * kHD) void kvq_merge_kernel(float* __restrict__ out, DecodeArgs a) {
+    __shared__ float other[PARTS][kHD + 2];
     const int bh = blockIdx.x;
     const int b = bh / a.nq;
     const int d = threadIdx.x & (kHD - 1);
     const int part = __builtin_amdgcn_readfirstlane(threadIdx.x / kHD);
     const int chunk_len = a.tiles_per_wave * kChunkUnit;
     const int nct = n_chunks_total(a);
-    const int half = (nct + 1) / 2;
-    const int cbeg = part * half;
-    const int cend = min(nct, cbeg + half);
+    const int share = (nct + PARTS - 1) / PARTS;
+    const int cbeg = part * share;
+    const int cend = min(nct, cbeg + share);
     const int base8 = a.r4.max_chunks;
     const float* mm = a.ws_m + (size_t)bh * nct;
     const float* ss = a.ws_s + (size_t)bh * nct;
@@ -200,24 +200,40 @@ __global__ __launch_bounds__(kMergeThreads) void kvq_merge_kernel(float* __restr
             acc = fmaf(av[k], f, acc);
         }
     }
-    if (part == 1) {
-        other[d] = acc;
+    if (part > 0) {
+        other[part][d] = acc;
         if (d == 0) {
-            other[kHD] = M;
-            other[kHD + 1] = S;
+            other[part][kHD] = M;
+            other[part][kHD + 1] = S;
         }
     }
     __syncthreads();
     if (part == 0) {
-        const float M1 = other[kHD], S1 = other[kHD + 1], A1 = other[d];
-        const float Mt = fmaxf(M, M1);
+        float Mt = M;
+#pragma unroll
+        for (int q = 1; q < PARTS; ++q) Mt = fmaxf(Mt, other[q][kHD]);
         float res = 0.0f;
         if (Mt != -INFINITY) {
-            const float f0 = __builtin_amdgcn_exp2f(M - Mt), f1 = __builtin_amdgcn_exp2f(M1 - Mt);
-            res = fmaf(acc, f0, A1 * f1) / fmaf(S, f0, S1 * f1);
+            const float f0 = __builtin_amdgcn_exp2f(M - Mt);
+            float num = acc * f0, den = S * f0;
+#pragma unroll
+            for (int q = 1; q < PARTS; ++q) {
+                const float f = __builtin_amdgcn_exp2f(other[q][kHD] - Mt);
+                num = fmaf(other[q][d], f, num);
+                den = fmaf(other[q][kHD + 1], f, den);
+            }
+            res = num / den;
         }
         out[(size_t)bh * kHD + d] = res;
     }
+}
+
+// Enqueue the merge of a decode's chunk partials into `out`.
+inline void launch_merge(const DecodeArgs& a, float* out, hipStream_t s) {
+    if (n_chunks_total(a) > 2 * kMergeBatch)
+        hipLaunchKernelGGL(kvq_merge_kernel<8>, dim3(a.batch * a.nq), dim3(kMergeThreadsWide), 0, s, out, a);
+    else
+        hipLaunchKernelGGL(kvq_merge_kernel<2>, dim3(a.batch * a.nq), dim3(kMergeThreads), 0, s, out, a);
 }
 
 // ----------------------------------------------------------------------------

@@ -453,7 +453,7 @@ inline int launch_decode(const DecodeArgs& a, float* out, hipStream_t s, int new
         else
             launch_mfma(a, (int)n_wg, new_dtype, s);
     }
-    hipLaunchKernelGGL(kvq_merge_kernel<>, dim3(a.batch * a.nq), dim3(kMergeThreads), 0, s, out, a);
+    launch_merge(a, out, s);
     return launch_status();
 }
 

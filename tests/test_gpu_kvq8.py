@@ -174,6 +174,24 @@ def test_decode_chunk_sizes_agree(K, chunk):
     assert_attn_close(got, ref, f"chunk {chunk}")
 
 
+def test_decode_many_chunks(K):
+    """157 chunks of 256 tokens per sequence: the merge splits a head's chunks
+    over 8 parts of two batches each."""
+    r = W.rng(335)
+    nq, nkv, bs = 4, 1, 16
+    lens = np.array([40000, 9000], np.int32)
+    B, Lm = len(lens), int(lens.max())
+    bt, nb = W.paged_block_tables(r, lens, bs)
+    k = W.normal_f32(r, (B, Lm, nkv, 128))
+    v = W.student_t3_f32(r, (B, Lm, nkv, 128), 0.5)
+    c = Q8Cache(nb, bs, nkv)
+    fill_sequences(c, bt, lens, k, v)
+    q = W.normal_f32(r, (B, nq, 128), 3.0)
+    got = _decode(K, c, q, bt, lens, Lm, chunk=256)
+    ref = O8.decode_attention_q8(q, c.kp, c.ks, c.vp, c.vs, bt, lens, bs, SM)
+    assert_attn_close(got, ref, "157 chunks")
+
+
 def test_decode_single_token_and_peaked_softmax(K):
     r = W.rng(332)
     nq, nkv, bs = 4, 1, 16
