@@ -9,6 +9,8 @@ launch configuration (the one the benchmark times).
             one GQA-4 decode over the 65536 tokens             everything
   q4_128k   int4 groups + int8 window, 32 / 4 heads, batch 4,
             L = 131072                                         sequences 0 and 3
+  Q4_0      the qwen8b batch-32 layer and the 64K append + decode
+            through the Q4_0 mode                              everything
 
 Write-path codes and steps are compared bit for bit with the oracle's own
 quantization of the same generated inputs; the decode reference is the
@@ -19,6 +21,7 @@ import pytest
 
 import workloads as W
 from oracle import kvq4 as O4
+from oracle import kvq4_0 as O40
 from oracle import kvq8 as O8
 from tests.helpers import SM, assert_attn_close, dev, host
 
@@ -171,3 +174,65 @@ def test_q4_128k(K):
                                         bt4[b:b + 1], [n4], (p8[0], p8[2], p8[1], p8[3]), bt8[b:b + 1], [n8],
                                         bs, SM)
         assert_attn_close(got[b:b + 1], ref, f"q4_128k seq {b}")
+
+
+def _q40_pools(torch, nb, bs, nkv):
+    shp = (nb, bs, nkv)
+    return (torch.zeros(shp + (64,), dtype=torch.uint8, device="cuda"),
+            torch.zeros(shp + (64,), dtype=torch.uint8, device="cuda"),
+            torch.zeros(shp + (4,), dtype=torch.float32, device="cuda"),
+            torch.zeros(shp + (4,), dtype=torch.float32, device="cuda"))
+
+
+def _q40_host(nb, bs, nkv):
+    shp = (nb, bs, nkv)
+    return [np.zeros(shp + (64,), np.uint8), np.zeros(shp + (64,), np.uint8), np.zeros(shp + (4,), np.float32),
+            np.zeros(shp + (4,), np.float32)]
+
+
+def test_q40_qwen8b_batch32_layer0(K):
+    import torch
+    cfg = W.QWEN8B_B32
+    nq, nkv, bs, B = cfg["nq"], cfg["nkv"], cfg["kv_bs"], cfg["batch"]
+    lens = W.qwen8b_lengths(0)
+    bt, nb = W.paged_block_tables(W.rng(3, 0, 1), lens, bs)
+    gk, gv, gks, gvs = _q40_pools(torch, nb, bs, nkv)
+    hk, hv, hks, hvs = _q40_host(nb, bs, nkv)
+    for b in range(B):
+        Lb = int(lens[b])
+        k = W.torch_student_t3((Lb, nkv, 128), "cuda", (3, 0, b, 0), 0.5)
+        v = W.torch_student_t3((Lb, nkv, 128), "cuda", (3, 0, b, 1), 0.5)
+        slots = W.slots_for_positions(bt, [b] * Lb, np.arange(Lb), bs)
+        K.kvq4_0_quantize_append(gk, gv, gks, gvs, k, v, dev(slots))
+        O40.quantize_append_q4_0(hk, hv, hks, hvs, host(k), host(v), slots)
+        del k, v
+    q = W.torch_normal((B, nq, 128), "cuda", (3, 0, 99))
+    out = torch.empty((B, nq, 128), dtype=torch.float32, device="cuda")
+    K.kvq4_0_decode_attn(out, q, gk, gv, gks, gvs, dev(bt), dev(lens), int(lens.max()), SM)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(gk), hk) and np.array_equal(host(gv), hv)
+    assert _same(host(gks), hks) and _same(host(gvs), hvs)
+    ref = O40.decode_attention_q4_0(host(q), hk, hks, hv, hvs, bt, lens, bs, SM)
+    assert_attn_close(host(out), ref, "Q4_0 qwen8b batch 32")
+
+
+def test_q40_append64k_then_decode(K):
+    import torch
+    cfg = W.APPEND_64K
+    n, nq, nkv, bs = cfg["n_tok"], cfg["nq"], cfg["nkv"], cfg["kv_bs"]
+    bt, nb = W.paged_block_tables(W.rng(4, 0, 2), [n], bs)
+    k = W.torch_outlier_normal_bf16((n, nkv, 128), "cuda", (4, 0, 0))
+    v = W.torch_outlier_normal_bf16((n, nkv, 128), "cuda", (4, 0, 1))
+    slots = W.slots_for_positions(bt, [0] * n, np.arange(n), bs)
+    gk, gv, gks, gvs = _q40_pools(torch, nb, bs, nkv)
+    K.kvq4_0_quantize_append(gk, gv, gks, gvs, k, v, dev(slots))
+    q = W.torch_normal((1, nq, 128), "cuda", (4, 0, 3))
+    out = torch.empty((1, nq, 128), dtype=torch.float32, device="cuda")
+    K.kvq4_0_decode_attn(out, q, gk, gv, gks, gvs, dev(bt), dev(np.array([n], np.int32)), n, SM)
+    torch.cuda.synchronize()
+    hk, hv, hks, hvs = _q40_host(nb, bs, nkv)
+    O40.quantize_append_q4_0(hk, hv, hks, hvs, host(k.float()), host(v.float()), slots)
+    assert np.array_equal(host(gk), hk) and np.array_equal(host(gv), hv)
+    assert _same(host(gks), hks) and _same(host(gvs), hvs)
+    ref = O40.decode_attention_q4_0(host(q), hk, hks, hv, hvs, bt, [n], bs, SM)
+    assert_attn_close(host(out), ref, "Q4_0 append64k decode")
