@@ -78,6 +78,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--workloads", action="store_true",
                    help="instead of the step benchmark, time every other workload of the hot path (one JSON line each)")
+    p.add_argument("--only", default="", metavar="NAMES",
+                   help="with --workloads: only the comma-separated workloads (and the set-up they share)")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB (for scaling memory counters) and exit")
     return p.parse_args()
@@ -195,7 +197,7 @@ def report(name, desc, nbytes, us, **extra):
     print(json.dumps(line), flush=True)
 
 
-def run_workloads():
+def run_workloads(only=None):
     """Every workload of the hot path besides the step benchmark, timed on one
     GPU: the pages' unit experiment, the batch-32 long-context layer, the 64K
     write path and the decode over it, the int4 128K mixed decode, and the
@@ -209,6 +211,9 @@ def run_workloads():
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     sm = 1.0 / math.sqrt(128)
 
+    def want(*names):
+        return not only or any(n in only for n in names)
+
     def q8_pool(nb, bs, nkv):
         shp = (nb, bs, nkv, 128)
         return [torch.zeros(shp, dtype=torch.int8, device="cuda"), torch.zeros(shp, dtype=torch.int8, device="cuda"),
@@ -221,101 +226,105 @@ def run_workloads():
                 torch.zeros(shp + (64,), dtype=torch.uint8, device="cuda")] + \
                [torch.zeros(shp + (2,), dtype=torch.float16, device="cuda") for _ in range(4)]
 
-    # unit experiment: 1 / 1 heads, 256 tokens (launch-bound)
-    q, k, v = W.unit_experiment(0)
-    bt, nb = W.paged_block_tables(None, [256], 16)
-    p = q8_pool(nb, 16, 1)
-    K.kvq8_quantize_append(*p, dev(k[:, None]), dev(v[:, None]), dev(np.arange(256, dtype=np.int32)))
-    out = torch.empty((1, 1, 128), device="cuda")
-    qd, btd, ld = dev(q[None, None]), dev(bt), dev(np.array([256], np.int32))
-    ws = K.alloc_workspace(K.kvq8_decode_workspace_size(1, 1, 1, 256), "cuda")
-    us = time_calls(torch, lambda: K.kvq8_decode_attn(out, qd, *p, btd, ld, 256, sm, 0, ws), 200, graph=True)
-    report("unit_256", "decode, 1 query / 1 kv head, 256 tokens (graph replay)", 256 * 264, us)
-    del p
+    if want("unit_256"):
+        # unit experiment: 1 / 1 heads, 256 tokens (launch-bound)
+        q, k, v = W.unit_experiment(0)
+        bt, nb = W.paged_block_tables(None, [256], 16)
+        p = q8_pool(nb, 16, 1)
+        K.kvq8_quantize_append(*p, dev(k[:, None]), dev(v[:, None]), dev(np.arange(256, dtype=np.int32)))
+        out = torch.empty((1, 1, 128), device="cuda")
+        qd, btd, ld = dev(q[None, None]), dev(bt), dev(np.array([256], np.int32))
+        ws = K.alloc_workspace(K.kvq8_decode_workspace_size(1, 1, 1, 256), "cuda")
+        us = time_calls(torch, lambda: K.kvq8_decode_attn(out, qd, *p, btd, ld, 256, sm, 0, ws), 200, graph=True)
+        report("unit_256", "decode, 1 query / 1 kv head, 256 tokens (graph replay)", 256 * 264, us)
+        del p
 
-    # batch-32 Qwen-8B-shaped layer: lengths U[1024, 32768], K, V = 0.5 Student-t(3)
-    cfg = W.QWEN8B_B32
-    lens = W.qwen8b_lengths(0)
-    B, nq, nkv, bs = cfg["batch"], cfg["nq"], cfg["nkv"], cfg["kv_bs"]
-    bt, nb = W.paged_block_tables(W.rng(3, 0, 1), lens, bs)
-    p = q8_pool(nb, bs, nkv)
-    for b in range(B):
-        kk = W.torch_student_t3((int(lens[b]), nkv, 128), "cuda", (3, 0, b, 0))
-        vv = W.torch_student_t3((int(lens[b]), nkv, 128), "cuda", (3, 0, b, 1))
-        K.kvq8_quantize_append(*p, kk, vv, dev(W.slots_for_positions(bt, [b] * int(lens[b]), np.arange(lens[b]), bs)))
-        del kk, vv
-    qd = W.torch_normal((B, nq, 128), "cuda", (3, 0, 99))
-    out = torch.empty((B, nq, 128), device="cuda")
-    btd, ld, L = dev(bt), dev(lens), int(lens.max())
-    ch = K.kvq8_decode_chunk_tokens(B, nkv, L)
-    ws = K.alloc_workspace(K.kvq8_decode_workspace_size(B, nq, nkv, L), "cuda")
-    us = time_calls(torch, lambda: K.kvq8_decode_attn(out, qd, *p, btd, ld, L, sm, 0, ws), 20)
-    report("qwen8b_b32", f"decode layer, batch 32 x 32 / 8 heads, lengths U[1024, 32768] (sum {int(lens.sum())})",
-           int(lens.sum()) * nkv * 264, us, chunk_tokens=ch)
-    del p
+    if want("qwen8b_b32"):
+        # batch-32 Qwen-8B-shaped layer: lengths U[1024, 32768], K, V = 0.5 Student-t(3)
+        cfg = W.QWEN8B_B32
+        lens = W.qwen8b_lengths(0)
+        B, nq, nkv, bs = cfg["batch"], cfg["nq"], cfg["nkv"], cfg["kv_bs"]
+        bt, nb = W.paged_block_tables(W.rng(3, 0, 1), lens, bs)
+        p = q8_pool(nb, bs, nkv)
+        for b in range(B):
+            kk = W.torch_student_t3((int(lens[b]), nkv, 128), "cuda", (3, 0, b, 0))
+            vv = W.torch_student_t3((int(lens[b]), nkv, 128), "cuda", (3, 0, b, 1))
+            K.kvq8_quantize_append(*p, kk, vv, dev(W.slots_for_positions(bt, [b] * int(lens[b]), np.arange(lens[b]), bs)))
+            del kk, vv
+        qd = W.torch_normal((B, nq, 128), "cuda", (3, 0, 99))
+        out = torch.empty((B, nq, 128), device="cuda")
+        btd, ld, L = dev(bt), dev(lens), int(lens.max())
+        ch = K.kvq8_decode_chunk_tokens(B, nkv, L)
+        ws = K.alloc_workspace(K.kvq8_decode_workspace_size(B, nq, nkv, L), "cuda")
+        us = time_calls(torch, lambda: K.kvq8_decode_attn(out, qd, *p, btd, ld, L, sm, 0, ws), 20)
+        report("qwen8b_b32", f"decode layer, batch 32 x 32 / 8 heads, lengths U[1024, 32768] (sum {int(lens.sum())})",
+               int(lens.sum()) * nkv * 264, us, chunk_tokens=ch)
+        del p
 
-    # 64K tokens written from bf16 (1% x20 outliers), then a GQA-4 decode over them
-    cfg = W.APPEND_64K
-    n, nq, nkv, bs = cfg["n_tok"], cfg["nq"], cfg["nkv"], cfg["kv_bs"]
-    bt, nb = W.paged_block_tables(W.rng(4, 0, 1), [n], bs)
-    p = q8_pool(nb, bs, nkv)
-    kk = W.torch_outlier_normal_bf16((n, nkv, 128), "cuda", (4, 0, 0))
-    vv = W.torch_outlier_normal_bf16((n, nkv, 128), "cuda", (4, 0, 1))
-    slots = dev(W.slots_for_positions(bt, [0] * n, np.arange(n), bs))
-    us = time_calls(torch, lambda: K.kvq8_quantize_append(*p, kk, vv, slots), 20)
-    report("append_64k", "write path, 65536 tokens x 8 kv heads from bf16", n * nkv * (2 * 128 * 2 + 2 * 132), us)
-    qd = W.torch_normal((1, nq, 128), "cuda", (4, 0, 2))
-    out = torch.empty((1, nq, 128), device="cuda")
-    btd, ld = dev(bt), dev(np.array([n], np.int32))
-    ch = K.kvq8_decode_chunk_tokens(1, nkv, n)
-    ws = K.alloc_workspace(K.kvq8_decode_workspace_size(1, nq, nkv, n), "cuda")
-    us = time_calls(torch, lambda: K.kvq8_decode_attn(out, qd, *p, btd, ld, n, sm, 0, ws), 50)
-    report("decode_64k", "decode, 1 sequence x 32 / 8 heads over the 65536 written tokens", n * nkv * 264, us,
-           chunk_tokens=ch)
-    del p, kk, vv
+    if want("append_64k", "decode_64k"):
+        # 64K tokens written from bf16 (1% x20 outliers), then a GQA-4 decode over them
+        cfg = W.APPEND_64K
+        n, nq, nkv, bs = cfg["n_tok"], cfg["nq"], cfg["nkv"], cfg["kv_bs"]
+        bt, nb = W.paged_block_tables(W.rng(4, 0, 1), [n], bs)
+        p = q8_pool(nb, bs, nkv)
+        kk = W.torch_outlier_normal_bf16((n, nkv, 128), "cuda", (4, 0, 0))
+        vv = W.torch_outlier_normal_bf16((n, nkv, 128), "cuda", (4, 0, 1))
+        slots = dev(W.slots_for_positions(bt, [0] * n, np.arange(n), bs))
+        us = time_calls(torch, lambda: K.kvq8_quantize_append(*p, kk, vv, slots), 20)
+        report("append_64k", "write path, 65536 tokens x 8 kv heads from bf16", n * nkv * (2 * 128 * 2 + 2 * 132), us)
+        qd = W.torch_normal((1, nq, 128), "cuda", (4, 0, 2))
+        out = torch.empty((1, nq, 128), device="cuda")
+        btd, ld = dev(bt), dev(np.array([n], np.int32))
+        ch = K.kvq8_decode_chunk_tokens(1, nkv, n)
+        ws = K.alloc_workspace(K.kvq8_decode_workspace_size(1, nq, nkv, n), "cuda")
+        us = time_calls(torch, lambda: K.kvq8_decode_attn(out, qd, *p, btd, ld, n, sm, 0, ws), 50)
+        report("decode_64k", "decode, 1 sequence x 32 / 8 heads over the 65536 written tokens", n * nkv * 264, us,
+               chunk_tokens=ch)
+        del p, kk, vv
 
-    # int4 group cache, 128K tokens (last 2048 int8), batch 4 x 32 / 4 heads
-    cfg = W.Q4_128K
-    B, nq, nkv, L, win, bs = cfg["batch"], cfg["nq"], cfg["nkv"], cfg["L"], cfg["window"], cfg["kv_bs"]
-    n4, n8 = L - win, win
-    bt4, nb4 = W.paged_block_tables(W.rng(5, 0, 1), [n4] * B, bs)
-    bt8, nb8 = W.paged_block_tables(W.rng(5, 0, 2), [n8] * B, bs)
-    p4, p8 = q4_pool(nb4, bs, nkv), q8_pool(nb8, bs, nkv)
-    sig = W.rng(5, 0, 3).uniform(0.2, 5.0, size=(B, nkv, 2))
-    for b in range(B):
-        sk = torch.tensor(sig[b, :, 0], dtype=torch.float32, device="cuda")[None, :, None]
-        sv = torch.tensor(sig[b, :, 1], dtype=torch.float32, device="cuda")[None, :, None]
-        kk = W.torch_normal((L, nkv, 128), "cuda", (5, 0, b, 0)) * sk
-        vv = W.torch_normal((L, nkv, 128), "cuda", (5, 0, b, 1)) * sv
-        K.kvq4_quantize_append(*p4, kk[:n4], vv[:n4], dev(W.slots_for_positions(bt4, [b] * n4, np.arange(n4), bs)))
-        K.kvq8_quantize_append(*p8, kk[n4:], vv[n4:], dev(W.slots_for_positions(bt8, [b] * n8, np.arange(n8), bs)))
-        del kk, vv
-    qd = W.torch_normal((B, nq, 128), "cuda", (5, 0, 99))
-    out = torch.empty((B, nq, 128), device="cuda")
-    bt4d, l4 = dev(bt4), dev(np.full(B, n4, np.int32))
-    bt8d, l8 = dev(bt8), dev(np.full(B, n8, np.int32))
-    ch = K.kvq4_decode_chunk_tokens(B, nkv, n4, n8)
-    ws = K.alloc_workspace(K.kvq4_decode_workspace_size(B, nq, nkv, n4, n8), "cuda")
-    us = time_calls(torch, lambda: K.kvq4_decode_attn(out, qd, p4, bt4d, l4, n4, p8, bt8d, l8, n8, sm, 0, ws), 20)
-    report("q4_128k", "mixed decode, batch 4 x 32 / 4 heads, 129024 int4 + 2048 int8 tokens",
-           B * nkv * (n4 * 144 + n8 * 264), us, chunk_tokens=ch)
+    if want("q4_128k", "requant_block", "requant_window"):
+        # int4 group cache, 128K tokens (last 2048 int8), batch 4 x 32 / 4 heads
+        cfg = W.Q4_128K
+        B, nq, nkv, L, win, bs = cfg["batch"], cfg["nq"], cfg["nkv"], cfg["L"], cfg["window"], cfg["kv_bs"]
+        n4, n8 = L - win, win
+        bt4, nb4 = W.paged_block_tables(W.rng(5, 0, 1), [n4] * B, bs)
+        bt8, nb8 = W.paged_block_tables(W.rng(5, 0, 2), [n8] * B, bs)
+        p4, p8 = q4_pool(nb4, bs, nkv), q8_pool(nb8, bs, nkv)
+        sig = W.rng(5, 0, 3).uniform(0.2, 5.0, size=(B, nkv, 2))
+        for b in range(B):
+            sk = torch.tensor(sig[b, :, 0], dtype=torch.float32, device="cuda")[None, :, None]
+            sv = torch.tensor(sig[b, :, 1], dtype=torch.float32, device="cuda")[None, :, None]
+            kk = W.torch_normal((L, nkv, 128), "cuda", (5, 0, b, 0)) * sk
+            vv = W.torch_normal((L, nkv, 128), "cuda", (5, 0, b, 1)) * sv
+            K.kvq4_quantize_append(*p4, kk[:n4], vv[:n4], dev(W.slots_for_positions(bt4, [b] * n4, np.arange(n4), bs)))
+            K.kvq8_quantize_append(*p8, kk[n4:], vv[n4:], dev(W.slots_for_positions(bt8, [b] * n8, np.arange(n8), bs)))
+            del kk, vv
+        qd = W.torch_normal((B, nq, 128), "cuda", (5, 0, 99))
+        out = torch.empty((B, nq, 128), device="cuda")
+        bt4d, l4 = dev(bt4), dev(np.full(B, n4, np.int32))
+        bt8d, l8 = dev(bt8), dev(np.full(B, n8, np.int32))
+        ch = K.kvq4_decode_chunk_tokens(B, nkv, n4, n8)
+        ws = K.alloc_workspace(K.kvq4_decode_workspace_size(B, nq, nkv, n4, n8), "cuda")
+        us = time_calls(torch, lambda: K.kvq4_decode_attn(out, qd, p4, bt4d, l4, n4, p8, bt8d, l8, n8, sm, 0, ws), 20)
+        report("q4_128k", "mixed decode, batch 4 x 32 / 4 heads, 129024 int4 + 2048 int8 tokens",
+               B * nkv * (n4 * 144 + n8 * 264), us, chunk_tokens=ch)
 
-    # re-quantization of the window's oldest 512-token time block of every
-    # sequence into the int4 pool (into the int4 pool's first 512 slots per
-    # sequence: the timing, not the cache's meaning, is what is measured here)
-    T = 512
-    src = dev(np.concatenate([W.slots_for_positions(bt8, [b] * T, np.arange(T), bs) for b in range(B)]))
-    dst = dev(np.concatenate([W.slots_for_positions(bt4, [b] * T, np.arange(T), bs) for b in range(B)]))
-    us = time_calls(torch, lambda: K.kvq4_requantize_q8(p4, p8, src, dst), 50, graph=True)
-    report("requant_block", "int8 -> int4 re-quantization of one 512-token time block x 4 sequences x 4 kv heads "
-           "(graph replay)", B * T * nkv * (264 + 144), us)
-    n_all = B * n8
-    src = dev(np.concatenate([W.slots_for_positions(bt8, [b] * n8, np.arange(n8), bs) for b in range(B)]))
-    dst = dev(np.concatenate([W.slots_for_positions(bt4, [b] * n8, np.arange(n8), bs) for b in range(B)]))
-    us = time_calls(torch, lambda: K.kvq4_requantize_q8(p4, p8, src, dst), 50)
-    report("requant_window", "int8 -> int4 re-quantization of the whole 2048-token window x 4 sequences",
-           n_all * nkv * (264 + 144), us)
-    del p4, p8
+        # re-quantization of the window's oldest 512-token time block of every
+        # sequence into the int4 pool (into the int4 pool's first 512 slots per
+        # sequence: the timing, not the cache's meaning, is what is measured here)
+        T = 512
+        src = dev(np.concatenate([W.slots_for_positions(bt8, [b] * T, np.arange(T), bs) for b in range(B)]))
+        dst = dev(np.concatenate([W.slots_for_positions(bt4, [b] * T, np.arange(T), bs) for b in range(B)]))
+        us = time_calls(torch, lambda: K.kvq4_requantize_q8(p4, p8, src, dst), 50, graph=True)
+        report("requant_block", "int8 -> int4 re-quantization of one 512-token time block x 4 sequences x 4 kv heads "
+               "(graph replay)", B * T * nkv * (264 + 144), us)
+        n_all = B * n8
+        src = dev(np.concatenate([W.slots_for_positions(bt8, [b] * n8, np.arange(n8), bs) for b in range(B)]))
+        dst = dev(np.concatenate([W.slots_for_positions(bt4, [b] * n8, np.arange(n8), bs) for b in range(B)]))
+        us = time_calls(torch, lambda: K.kvq4_requantize_q8(p4, p8, src, dst), 50)
+        report("requant_window", "int8 -> int4 re-quantization of the whole 2048-token window x 4 sequences",
+               n_all * nkv * (264 + 144), us)
+        del p4, p8
 
     # Q4_0 mode (80 B per row: 160 B per (token, kv-head) for K and V)
     def q40_pool(nb, bs, nkv):
@@ -325,71 +334,73 @@ def run_workloads():
                 torch.zeros(shp + (4,), dtype=torch.float32, device="cuda"),
                 torch.zeros(shp + (4,), dtype=torch.float32, device="cuda")]
 
-    # the 8K batch-1 layer shape, 28 layers cycled in one graph (as the step)
-    cfg = W.QWEN2B_8K
-    nl, nq, nkv, bs, L = cfg["layers"], cfg["nq"], cfg["nkv"], cfg["kv_bs"], cfg["L"]
-    bt, nb = W.paged_block_tables(W.rng(6, 0, 1), [L], bs)
-    btd, ld = dev(bt), dev(np.array([L], np.int32))
-    slots = dev(W.slots_for_positions(bt, [0] * L, np.arange(L), bs))
-    layers = []
-    for layer in range(nl):
+    if want("q40_8k"):
+        # the 8K batch-1 layer shape, 28 layers cycled in one graph (as the step)
+        cfg = W.QWEN2B_8K
+        nl, nq, nkv, bs, L = cfg["layers"], cfg["nq"], cfg["nkv"], cfg["kv_bs"], cfg["L"]
+        bt, nb = W.paged_block_tables(W.rng(6, 0, 1), [L], bs)
+        btd, ld = dev(bt), dev(np.array([L], np.int32))
+        slots = dev(W.slots_for_positions(bt, [0] * L, np.arange(L), bs))
+        layers = []
+        for layer in range(nl):
+            p = q40_pool(nb, bs, nkv)
+            kk = W.torch_normal((L, nkv, 128), "cuda", (6, layer, 0))
+            vv = W.torch_normal((L, nkv, 128), "cuda", (6, layer, 1))
+            K.kvq4_0_quantize_append(*p, kk, vv, slots)
+            layers.append((p, W.torch_normal((1, nq, 128), "cuda", (6, layer, 2)), torch.empty((1, nq, 128), device="cuda")))
+            del kk, vv
+        ws = K.alloc_workspace(K.kvq4_0_decode_workspace_size(1, nq, nkv, L), "cuda")
+
+        def q40_step():
+            for p, qd, out in layers:
+                K.kvq4_0_decode_attn(out, qd, *p, btd, ld, L, sm, 0, ws)
+        us = time_calls(torch, q40_step, 5, graph=True) / nl
+        report("q40_8k", "Q4_0 decode, 28 layers x (1 x 16 / 8 heads, 8192 tokens), per layer call (graph replay)",
+               L * nkv * 160, us, chunk_tokens=K.kvq4_0_decode_chunk_tokens(1, nkv, L))
+        del layers
+
+    if want("q40_qwen8b_b32"):
+        # the batch-32 long-context layer in Q4_0
+        cfg = W.QWEN8B_B32
+        lens = W.qwen8b_lengths(0)
+        B, nq, nkv, bs = cfg["batch"], cfg["nq"], cfg["nkv"], cfg["kv_bs"]
+        bt, nb = W.paged_block_tables(W.rng(3, 0, 1), lens, bs)
         p = q40_pool(nb, bs, nkv)
-        kk = W.torch_normal((L, nkv, 128), "cuda", (6, layer, 0))
-        vv = W.torch_normal((L, nkv, 128), "cuda", (6, layer, 1))
-        K.kvq4_0_quantize_append(*p, kk, vv, slots)
-        layers.append((p, W.torch_normal((1, nq, 128), "cuda", (6, layer, 2)), torch.empty((1, nq, 128), device="cuda")))
-        del kk, vv
-    ws = K.alloc_workspace(K.kvq4_0_decode_workspace_size(1, nq, nkv, L), "cuda")
+        for b in range(B):
+            kk = W.torch_student_t3((int(lens[b]), nkv, 128), "cuda", (3, 0, b, 0))
+            vv = W.torch_student_t3((int(lens[b]), nkv, 128), "cuda", (3, 0, b, 1))
+            K.kvq4_0_quantize_append(*p, kk, vv,
+                                     dev(W.slots_for_positions(bt, [b] * int(lens[b]), np.arange(lens[b]), bs)))
+            del kk, vv
+        qd = W.torch_normal((B, nq, 128), "cuda", (3, 0, 99))
+        out = torch.empty((B, nq, 128), device="cuda")
+        btd, ld, L = dev(bt), dev(lens), int(lens.max())
+        ws = K.alloc_workspace(K.kvq4_0_decode_workspace_size(B, nq, nkv, L), "cuda")
+        us = time_calls(torch, lambda: K.kvq4_0_decode_attn(out, qd, *p, btd, ld, L, sm, 0, ws), 20)
+        report("q40_qwen8b_b32", f"Q4_0 decode layer, batch 32 x 32 / 8 heads, lengths U[1024, 32768] "
+               f"(sum {int(lens.sum())})", int(lens.sum()) * nkv * 160, us,
+               chunk_tokens=K.kvq4_0_decode_chunk_tokens(B, nkv, L))
+        del p
 
-    def q40_step():
-        for p, qd, out in layers:
-            K.kvq4_0_decode_attn(out, qd, *p, btd, ld, L, sm, 0, ws)
-    us = time_calls(torch, q40_step, 5, graph=True) / nl
-    report("q40_8k", "Q4_0 decode, 28 layers x (1 x 16 / 8 heads, 8192 tokens), per layer call (graph replay)",
-           L * nkv * 160, us, chunk_tokens=K.kvq4_0_decode_chunk_tokens(1, nkv, L))
-    del layers
-
-    # the batch-32 long-context layer in Q4_0
-    cfg = W.QWEN8B_B32
-    lens = W.qwen8b_lengths(0)
-    B, nq, nkv, bs = cfg["batch"], cfg["nq"], cfg["nkv"], cfg["kv_bs"]
-    bt, nb = W.paged_block_tables(W.rng(3, 0, 1), lens, bs)
-    p = q40_pool(nb, bs, nkv)
-    for b in range(B):
-        kk = W.torch_student_t3((int(lens[b]), nkv, 128), "cuda", (3, 0, b, 0))
-        vv = W.torch_student_t3((int(lens[b]), nkv, 128), "cuda", (3, 0, b, 1))
-        K.kvq4_0_quantize_append(*p, kk, vv,
-                                 dev(W.slots_for_positions(bt, [b] * int(lens[b]), np.arange(lens[b]), bs)))
-        del kk, vv
-    qd = W.torch_normal((B, nq, 128), "cuda", (3, 0, 99))
-    out = torch.empty((B, nq, 128), device="cuda")
-    btd, ld, L = dev(bt), dev(lens), int(lens.max())
-    ws = K.alloc_workspace(K.kvq4_0_decode_workspace_size(B, nq, nkv, L), "cuda")
-    us = time_calls(torch, lambda: K.kvq4_0_decode_attn(out, qd, *p, btd, ld, L, sm, 0, ws), 20)
-    report("q40_qwen8b_b32", f"Q4_0 decode layer, batch 32 x 32 / 8 heads, lengths U[1024, 32768] "
-           f"(sum {int(lens.sum())})", int(lens.sum()) * nkv * 160, us,
-           chunk_tokens=K.kvq4_0_decode_chunk_tokens(B, nkv, L))
-    del p
-
-    # 64K tokens written from bf16 into the Q4_0 pool, then a GQA-4 decode
-    cfg = W.APPEND_64K
-    n, nq, nkv, bs = cfg["n_tok"], cfg["nq"], cfg["nkv"], cfg["kv_bs"]
-    bt, nb = W.paged_block_tables(W.rng(4, 0, 1), [n], bs)
-    p = q40_pool(nb, bs, nkv)
-    kk = W.torch_outlier_normal_bf16((n, nkv, 128), "cuda", (4, 0, 0))
-    vv = W.torch_outlier_normal_bf16((n, nkv, 128), "cuda", (4, 0, 1))
-    slots = dev(W.slots_for_positions(bt, [0] * n, np.arange(n), bs))
-    us = time_calls(torch, lambda: K.kvq4_0_quantize_append(*p, kk, vv, slots), 20)
-    report("q40_append_64k", "Q4_0 write path, 65536 tokens x 8 kv heads from bf16",
-           n * nkv * (2 * 128 * 2 + 2 * 80), us)
-    qd = W.torch_normal((1, nq, 128), "cuda", (4, 0, 2))
-    out = torch.empty((1, nq, 128), device="cuda")
-    btd, ld = dev(bt), dev(np.array([n], np.int32))
-    ws = K.alloc_workspace(K.kvq4_0_decode_workspace_size(1, nq, nkv, n), "cuda")
-    us = time_calls(torch, lambda: K.kvq4_0_decode_attn(out, qd, *p, btd, ld, n, sm, 0, ws), 50)
-    report("q40_decode_64k", "Q4_0 decode, 1 sequence x 32 / 8 heads over the 65536 written tokens",
-           n * nkv * 160, us, chunk_tokens=K.kvq4_0_decode_chunk_tokens(1, nkv, n))
-
+    if want("q40_append_64k", "q40_decode_64k"):
+        # 64K tokens written from bf16 into the Q4_0 pool, then a GQA-4 decode
+        cfg = W.APPEND_64K
+        n, nq, nkv, bs = cfg["n_tok"], cfg["nq"], cfg["nkv"], cfg["kv_bs"]
+        bt, nb = W.paged_block_tables(W.rng(4, 0, 1), [n], bs)
+        p = q40_pool(nb, bs, nkv)
+        kk = W.torch_outlier_normal_bf16((n, nkv, 128), "cuda", (4, 0, 0))
+        vv = W.torch_outlier_normal_bf16((n, nkv, 128), "cuda", (4, 0, 1))
+        slots = dev(W.slots_for_positions(bt, [0] * n, np.arange(n), bs))
+        us = time_calls(torch, lambda: K.kvq4_0_quantize_append(*p, kk, vv, slots), 20)
+        report("q40_append_64k", "Q4_0 write path, 65536 tokens x 8 kv heads from bf16",
+               n * nkv * (2 * 128 * 2 + 2 * 80), us)
+        qd = W.torch_normal((1, nq, 128), "cuda", (4, 0, 2))
+        out = torch.empty((1, nq, 128), device="cuda")
+        btd, ld = dev(bt), dev(np.array([n], np.int32))
+        ws = K.alloc_workspace(K.kvq4_0_decode_workspace_size(1, nq, nkv, n), "cuda")
+        us = time_calls(torch, lambda: K.kvq4_0_decode_attn(out, qd, *p, btd, ld, n, sm, 0, ws), 50)
+        report("q40_decode_64k", "Q4_0 decode, 1 sequence x 32 / 8 heads over the 65536 written tokens",
+               n * nkv * 160, us, chunk_tokens=K.kvq4_0_decode_chunk_tokens(1, nkv, n))
 
 def main():
     args = parse()
@@ -397,7 +408,7 @@ def main():
         calibrate_copy(args.calibrate_copy)
         return
     if args.workloads:
-        run_workloads()
+        run_workloads([n for n in args.only.split(",") if n])
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build has no multi-GPU path)",
