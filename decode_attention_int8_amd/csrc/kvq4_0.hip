@@ -92,20 +92,24 @@ __device__ __forceinline__ void q40_quantize8(const float (&x)[8], uint32_t& lo,
 template <int DT>
 __global__ __launch_bounds__(256) void kvq4_0_quantize_append_kernel(
     uint8_t* __restrict__ kc, uint8_t* __restrict__ vc, float* __restrict__ ks, float* __restrict__ vs,
-    long n_slots, int nkv, const void* __restrict__ k_new, const void* __restrict__ v_new, long n_rows,
+    long n_slots, int nkv, const void* __restrict__ k_new, const void* __restrict__ v_new, int n_rows,
     const int32_t* __restrict__ slots) {
     __shared__ uint8_t codes[kQ40RowsPerBlock][kHD];
     const int l16 = threadIdx.x & 15;
     const int grp = threadIdx.x >> 4;
     float x[kQ40RowsPerGroup][8];
-    long slot[kQ40RowsPerGroup];
-    // rows past the end load the last row again and store nothing
+    long dst[kQ40RowsPerGroup];    // destination row (slot * nkv + head), -1 to skip
+    // rows past the end load the last row again and store nothing; indices
+    // fit in 32 bits (the host checks the row count)
 #pragma unroll
     for (int k = 0; k < kQ40RowsPerGroup; ++k) {
-        const long row = min((long)blockIdx.x * kQ40RowsPerBlock + k * 16 + grp, n_rows - 1);
-        const long tr = row >> 1;                    // token * nkv + kv-head
-        q40_load8<DT>((row & 1) ? v_new : k_new, (size_t)tr * kHD + 8 * l16, x[k]);
-        slot[k] = slots[tr / nkv];
+        const int row = (int)blockIdx.x * kQ40RowsPerBlock + k * 16 + grp;
+        const int rc = min(row, n_rows - 1);
+        const int tr = rc >> 1;                      // token * nkv + kv-head
+        const int tok = tr / nkv;
+        q40_load8<DT>((rc & 1) ? v_new : k_new, (size_t)tr * kHD + 8 * l16, x[k]);
+        const long slot = slots[tok];
+        dst[k] = (row < n_rows && slot >= 0 && slot < n_slots) ? slot * nkv + (tr - tok * nkv) : -1;
     }
     float step[kQ40RowsPerGroup];
 #pragma unroll
@@ -117,10 +121,9 @@ __global__ __launch_bounds__(256) void kvq4_0_quantize_append_kernel(
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < kQ40RowsPerGroup; ++k) {
-        const long row = (long)blockIdx.x * kQ40RowsPerBlock + k * 16 + grp;
-        if (row >= n_rows || slot[k] < 0 || slot[k] >= n_slots) continue;   // uniform per 16-lane row
+        if (dst[k] < 0) continue;                    // uniform per 16-lane row
         const uint8_t* c = codes[k * 16 + grp];
-        const int kind = (int)(row & 1);
+        const int kind = grp & 1;                    // rows alternate K, V
         uint32_t word;
         if (kind == 0) {
             // key: byte j = code[j] | code[64 + j] << 4
@@ -136,11 +139,8 @@ __global__ __launch_bounds__(256) void kvq4_0_quantize_append_kernel(
                 word |= ((pr & 0xFu) | ((pr >> 4) & 0xF0u)) << (8 * kb);
             }
         }
-        const long tr = row >> 1;
-        const long tok = tr / nkv;
-        const size_t dst = (size_t)slot[k] * nkv + (size_t)(tr - tok * nkv);
-        *reinterpret_cast<uint32_t*>((kind ? vc : kc) + dst * (kHD / 2) + 4 * l16) = word;
-        if ((l16 & 3) == 0) (kind ? vs : ks)[dst * 4 + (l16 >> 2)] = step[k];
+        *reinterpret_cast<uint32_t*>((kind ? vc : kc) + (size_t)dst[k] * (kHD / 2) + 4 * l16) = word;
+        if ((l16 & 3) == 0) (kind ? vs : ks)[dst[k] * 4 + (l16 >> 2)] = step[k];
     }
 }
 
@@ -527,21 +527,22 @@ extern "C" int kvq4_0_quantize_append(uint8_t* k_cache, uint8_t* v_cache, float*
         !aligned16(k_step) || !aligned16(v_step))
         return KVQ8_EINVAL;
     const long n_rows = (long)n_tokens * nkv * 2;
+    if (n_rows > 0x7FFFFFFFL - kQ40RowsPerBlock) return KVQ8_ESHAPE;
     const long n_slots = (long)n_blocks * kv_bs;
     const dim3 grid((unsigned)((n_rows + kQ40RowsPerBlock - 1) / kQ40RowsPerBlock)), block(256);
     hipStream_t s = static_cast<hipStream_t>(stream);
     switch (dtype) {
         case KVQ8_F32:
             hipLaunchKernelGGL(kvq4_0_quantize_append_kernel<KVQ8_F32>, grid, block, 0, s, k_cache, v_cache, k_step,
-                               v_step, n_slots, nkv, k_new, v_new, n_rows, slots);
+                               v_step, n_slots, nkv, k_new, v_new, (int)n_rows, slots);
             break;
         case KVQ8_BF16:
             hipLaunchKernelGGL(kvq4_0_quantize_append_kernel<KVQ8_BF16>, grid, block, 0, s, k_cache, v_cache,
-                               k_step, v_step, n_slots, nkv, k_new, v_new, n_rows, slots);
+                               k_step, v_step, n_slots, nkv, k_new, v_new, (int)n_rows, slots);
             break;
         default:
             hipLaunchKernelGGL(kvq4_0_quantize_append_kernel<KVQ8_F16>, grid, block, 0, s, k_cache, v_cache, k_step,
-                               v_step, n_slots, nkv, k_new, v_new, n_rows, slots);
+                               v_step, n_slots, nkv, k_new, v_new, (int)n_rows, slots);
             break;
     }
     return launch_status();

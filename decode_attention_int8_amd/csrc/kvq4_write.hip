@@ -104,29 +104,30 @@ template <int DT>
 __global__ __launch_bounds__(256) void kvq4_quantize_append_kernel(
     uint8_t* __restrict__ kc, uint8_t* __restrict__ vc, uint16_t* __restrict__ ks, uint16_t* __restrict__ kz,
     uint16_t* __restrict__ vs, uint16_t* __restrict__ vz, long n_slots, int nkv, const void* __restrict__ k_new,
-    const void* __restrict__ v_new, long n_rows, const int32_t* __restrict__ slots) {
+    const void* __restrict__ v_new, int n_rows, const int32_t* __restrict__ slots) {
     const int l16 = threadIdx.x & 15;
     float x[kRowsPerGroup][8];
-    long slot[kRowsPerGroup];
+    long dst[kRowsPerGroup];     // destination row (slot * nkv + head), -1 to skip
+    // rows past the end load the last row again and store nothing; indices
+    // fit in 32 bits (the host checks the row count)
 #pragma unroll
     for (int k = 0; k < kRowsPerGroup; ++k) {
-        const long row = min((long)blockIdx.x * kRowsPerBlock + k * 16 + (threadIdx.x >> 4), n_rows - 1);
-        const long tr = row >> 1;
-        load8_any<DT>((row & 1) ? v_new : k_new, (size_t)tr * kHD + 8 * l16, x[k]);
-        slot[k] = slots[tr / nkv];
+        const int row = (int)blockIdx.x * kRowsPerBlock + k * 16 + (threadIdx.x >> 4);
+        const int rc = min(row, n_rows - 1);
+        const int tr = rc >> 1;
+        const int tok = tr / nkv;
+        load8_any<DT>((rc & 1) ? v_new : k_new, (size_t)tr * kHD + 8 * l16, x[k]);
+        const long slot = slots[tok];
+        dst[k] = (row < n_rows && slot >= 0 && slot < n_slots) ? slot * nkv + (tr - tok * nkv) : -1;
     }
 #pragma unroll
     for (int k = 0; k < kRowsPerGroup; ++k) {
-        const long row = (long)blockIdx.x * kRowsPerBlock + k * 16 + (threadIdx.x >> 4);
         uint32_t packed;
         uint16_t s16, z16;
         quantize_group8x8(x[k], packed, s16, z16);
         const uint32_t other = (uint32_t)dpp_i<kDppRowRor8>((int)packed);     // lane l16 ^ 8
-        if (row >= n_rows || slot[k] < 0 || slot[k] >= n_slots) continue;   // uniform per 16-lane row
-        const long tr = row >> 1;
-        const long tok = tr / nkv;
-        store_q4_row(kc, vc, ks, kz, vs, vz, (int)(row & 1), (size_t)slot[k] * nkv + (size_t)(tr - tok * nkv), l16,
-                     packed, other, s16, z16);
+        if (dst[k] < 0) continue;                                          // uniform per 16-lane row
+        store_q4_row(kc, vc, ks, kz, vs, vz, (threadIdx.x >> 4) & 1, (size_t)dst[k], l16, packed, other, s16, z16);
     }
 }
 
@@ -198,12 +199,13 @@ extern "C" int kvq4_quantize_append(uint8_t* k_cache, uint8_t* v_cache, uint16_t
         return KVQ8_EINVAL;
     if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache)) return KVQ8_EINVAL;
     const long n_rows = (long)n_tokens * nkv * 2;
+    if (n_rows > 0x7FFFFFFFL - kRowsPerBlock) return KVQ8_ESHAPE;
     const long n_slots = (long)n_blocks * kv_bs;
     const dim3 grid((unsigned)((n_rows + kRowsPerBlock - 1) / kRowsPerBlock)), block(256);
     hipStream_t s = static_cast<hipStream_t>(stream);
 #define KVQ4_LAUNCH(DT)                                                                                     \
     hipLaunchKernelGGL(kvq4_quantize_append_kernel<DT>, grid, block, 0, s, k_cache, v_cache, k_scale, k_zero, \
-                       v_scale, v_zero, n_slots, nkv, k_new, v_new, n_rows, slots)
+                       v_scale, v_zero, n_slots, nkv, k_new, v_new, (int)n_rows, slots)
     if (dtype == KVQ8_F32) KVQ4_LAUNCH(KVQ8_F32);
     else if (dtype == KVQ8_BF16) KVQ4_LAUNCH(KVQ8_BF16);
     else KVQ4_LAUNCH(KVQ8_F16);

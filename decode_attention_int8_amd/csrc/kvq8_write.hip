@@ -1,74 +1,51 @@
 // Write path of the int8 KV cache and the query-quantization export.
 //
 // kvq8_quantize_append_kernel: one (token, kv-head, K-or-V) row of 128 values
-// per 16 consecutive lanes, 8 values per lane; each 16-lane group handles 4
-// rows, so a 256-thread workgroup quantizes 64 rows.  Each lane reads 32 B (float32) or 16 B (bf16 / f16) of
-// its row and writes 8 B of codes: fully coalesced 128-B row stores into the
-// paged cache ([P2] Sec. 2 write path; rule of [P1] Sec. 2).
+// per 8 consecutive lanes, 16 values per lane; each 8-lane group handles 2
+// rows, so a 256-thread workgroup quantizes 64 rows.  Each lane reads 64 B
+// (float32) or 32 B (bf16 / f16) of its row and writes 16 B of codes: whole
+// 128-B rows per 8 lanes ([P2] Sec. 2 write path; rule of [P1] Sec. 2, the
+// same quantizer as the decode's fused write path).
 #include "kvq8.h"
 #include "kvq_device.h"
 #include "kvq_host.h"
+#include "kvq_decode_core.h"
 
 namespace kvq {
 
-template <int DT>
-__device__ __forceinline__ void load8(const void* base, size_t elem_off, float (&x)[8]) {
-    if constexpr (DT == KVQ8_F32) {
-        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem_off);
-        float4 a = p[0], b = p[1];
-        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-    } else {
-        const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem_off);
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if constexpr (DT == KVQ8_BF16) {
-                x[2 * i] = __uint_as_float(w[i] << 16);
-                x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-            } else {
-                x[2 * i] = half_bits_f(w[i] & 0xFFFFu);
-                x[2 * i + 1] = half_bits_f(w[i] >> 16);
-            }
-        }
-    }
-}
-
-// Rows per 16-lane group: all of a group's loads go out before it quantizes,
-// so each wave keeps kRowsPerGroup x 4 rows in flight.
-constexpr int kRowsPerGroup = 4;
-constexpr int kRowsPerBlock = 16 * kRowsPerGroup;
+// Rows per 8-lane group: both rows' loads go out before either is quantized.
+constexpr int kRowsPerGroup = 2;
+constexpr int kRowsPerBlock = 32 * kRowsPerGroup;
 
 template <int DT>
 __global__ __launch_bounds__(256) void kvq8_quantize_append_kernel(
     int8_t* __restrict__ kc, int8_t* __restrict__ vc, float* __restrict__ ks, float* __restrict__ vs,
     long n_slots, int nkv, const void* __restrict__ k_new, const void* __restrict__ v_new,
-    long n_rows, const int32_t* __restrict__ slots) {
-    const int l16 = threadIdx.x & 15;
-    float x[kRowsPerGroup][8];
-    long slot[kRowsPerGroup];
-    // rows past the end load the last row again and store nothing
+    int n_rows, const int32_t* __restrict__ slots) {
+    const int l8 = threadIdx.x & 7;
+    float x[kRowsPerGroup][16];
+    long dst[kRowsPerGroup];     // destination row (slot * nkv + head), -1 to skip
+    // rows past the end load the last row again and store nothing; indices
+    // fit in 32 bits (the host checks the row count)
 #pragma unroll
     for (int k = 0; k < kRowsPerGroup; ++k) {
-        const long row = min((long)blockIdx.x * kRowsPerBlock + k * 16 + (threadIdx.x >> 4), n_rows - 1);
-        const int kind = (int)(row & 1);           // 0 = K, 1 = V
-        const long tr = row >> 1;                  // token * nkv + kv-head
-        load8<DT>(kind ? v_new : k_new, (size_t)tr * kHD + 8 * l16, x[k]);
-        slot[k] = slots[tr / nkv];
+        const int row = (int)blockIdx.x * kRowsPerBlock + k * 32 + (threadIdx.x >> 3);
+        const int rc = min(row, n_rows - 1);
+        const int tr = rc >> 1;                    // token * nkv + kv-head
+        const int tok = tr / nkv;
+        load_new16<DT>((rc & 1) ? v_new : k_new, (size_t)tr * kHD + 16 * l8, x[k]);
+        const long slot = slots[tok];
+        dst[k] = (row < n_rows && slot >= 0 && slot < n_slots) ? slot * nkv + (tr - tok * nkv) : -1;
     }
 #pragma unroll
     for (int k = 0; k < kRowsPerGroup; ++k) {
-        const long row = (long)blockIdx.x * kRowsPerBlock + k * 16 + (threadIdx.x >> 4);
-        uint32_t lo, hi;
+        uint4 codes;
         float d;
-        quantize_row16x8(x[k], lo, hi, d);         // every lane of the row takes part (DPP)
-        if (row >= n_rows || slot[k] < 0 || slot[k] >= n_slots) continue;   // uniform per 16-lane row
-        const int kind = (int)(row & 1);
-        const long tr = row >> 1;
-        const long tok = tr / nkv;
-        const size_t dst = (size_t)slot[k] * nkv + (size_t)(tr - tok * nkv);
-        *reinterpret_cast<uint2*>((kind ? vc : kc) + dst * kHD + 8 * l16) = make_uint2(lo, hi);
-        if (l16 == 0) (kind ? vs : ks)[dst] = d;
+        quantize_row8x16(x[k], codes, d);         // every lane of the row takes part (DPP)
+        if (dst[k] < 0) continue;                  // uniform per 8-lane row
+        const int kind = (threadIdx.x >> 3) & 1;   // rows alternate K, V (k * 32 is even)
+        *reinterpret_cast<uint4*>((kind ? vc : kc) + (size_t)dst[k] * kHD + 16 * l8) = codes;
+        if (l8 == 0) (kind ? vs : ks)[dst[k]] = d;
     }
 }
 
@@ -105,21 +82,22 @@ extern "C" int kvq8_quantize_append(int8_t* k_cache, int8_t* v_cache, float* k_s
     if (!k_cache || !v_cache || !k_scale || !v_scale || !k_new || !v_new || !slots) return KVQ8_EINVAL;
     if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache)) return KVQ8_EINVAL;
     const long n_rows = (long)n_tokens * nkv * 2;
+    if (n_rows > 0x7FFFFFFFL - kRowsPerBlock) return KVQ8_ESHAPE;
     const long n_slots = (long)n_blocks * kv_bs;
     const dim3 grid((unsigned)((n_rows + kRowsPerBlock - 1) / kRowsPerBlock)), block(256);
     hipStream_t s = static_cast<hipStream_t>(stream);
     switch (dtype) {
         case KVQ8_F32:
             hipLaunchKernelGGL(kvq8_quantize_append_kernel<KVQ8_F32>, grid, block, 0, s, k_cache, v_cache, k_scale,
-                               v_scale, n_slots, nkv, k_new, v_new, n_rows, slots);
+                               v_scale, n_slots, nkv, k_new, v_new, (int)n_rows, slots);
             break;
         case KVQ8_BF16:
             hipLaunchKernelGGL(kvq8_quantize_append_kernel<KVQ8_BF16>, grid, block, 0, s, k_cache, v_cache, k_scale,
-                               v_scale, n_slots, nkv, k_new, v_new, n_rows, slots);
+                               v_scale, n_slots, nkv, k_new, v_new, (int)n_rows, slots);
             break;
         default:
             hipLaunchKernelGGL(kvq8_quantize_append_kernel<KVQ8_F16>, grid, block, 0, s, k_cache, v_cache, k_scale,
-                               v_scale, n_slots, nkv, k_new, v_new, n_rows, slots);
+                               v_scale, n_slots, nkv, k_new, v_new, (int)n_rows, slots);
             break;
     }
     return launch_status();

@@ -53,36 +53,6 @@ __device__ __forceinline__ float sbyte_f(uint32_t w, int k) {
 }
 
 // -----------------------------------------------------------------------------
-// Symmetric int8 quantization of one 128-value row held by 16 consecutive
-// lanes, 8 values per lane ([P1] Sec. 2, [P2] Sec. 2).
-//   amax = max |x| over the row (values < 1e-6 become 1)
-//   d    = amax / 127          (IEEE float32 division)
-//   code = roundf(x / d)       (IEEE division, ties away from zero), |code|<=127
-// The 16 lanes must be one aligned DPP row (lanes 16r .. 16r+15).
-// -----------------------------------------------------------------------------
-__device__ __forceinline__ void quantize_row16x8(const float (&x)[8], uint32_t& lo, uint32_t& hi, float& d) {
-#pragma clang fp contract(off)
-    float a = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(x[e]));
-    a = fmaxf(a, dpp_f<kDppXor1>(a));
-    a = fmaxf(a, dpp_f<kDppXor2>(a));
-    a = fmaxf(a, dpp_f<kDppHalfMirror>(a));
-    a = fmaxf(a, dpp_f<kDppRowRor8>(a));
-    if (a < 1e-6f) a = 1.0f;
-    d = a / 127.0f;
-    uint32_t w[2] = {0u, 0u};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        float r = roundf(x[e] / d);
-        r = fminf(fmaxf(r, -127.0f), 127.0f);
-        w[e >> 2] |= ((uint32_t)(int)r & 0xFFu) << (8 * (e & 3));
-    }
-    lo = w[0];
-    hi = w[1];
-}
-
-// -----------------------------------------------------------------------------
 // Query quantization ([P3] Sec. 2 seg. 1) of up to 8 query rows by a
 // workgroup of at least 256 threads, into LDS:
 //   qm  = max |q| over the 32-value block (qm < 1e-6 -> 1)
