@@ -97,7 +97,10 @@ const char* kvq8_version(void);
  *   slots             (device) int32 [n_tokens]: block_id * kv_bs + row;
  *                     a slot outside [0, n_blocks * kv_bs) is skipped
  *   n_tokens          may be 0 (nothing is launched)
- * Tokens with equal slots race (one of them wins).
+ * Errors: KVQ8_ESHAPE for hd != 128, an invalid kv_bs (a power of two in
+ * [8, 1024]), nkv < 1, n_blocks < 1, or n_tokens * nkv * 2 rows above
+ * 2^31 - 65; KVQ8_EINVAL for a null or misaligned pointer, a bad dtype or
+ * n_tokens < 0.  Tokens with equal slots race (one of them wins).
  */
 int kvq8_quantize_append(int8_t* k_cache, int8_t* v_cache, float* k_scale, float* v_scale,
                          int n_blocks, int kv_bs, int nkv, int hd,
@@ -217,8 +220,10 @@ int kvq8_qk_partials(int32_t* partials, const float* q, int batch, int nq,
  * int4 group variant ([P4] Sec. 3.2, 3.3)
  *
  * int4 pool layout:
- *   packed codes  cache4[n_blocks4][kv_bs][nkv][64] uint8, two codes per
- *                 byte, even-indexed value in the high nibble
+ *   packed codes  cache4[n_blocks4][kv_bs][nkv][64] uint8, two consecutive
+ *                 codes per byte, even-indexed value in the high nibble;
+ *                 key rows hold pair i in byte i, value rows hold the pair
+ *                 starting at element 64g + 4m + 2k in byte 4m + 2g + k
  *   scale, zero   [n_blocks4][kv_bs][nkv][2] IEEE binary16 (as uint16 bits),
  *                 one per 64-value group
  * Recent tokens stay in an int8 pool laid out exactly as above.
@@ -230,7 +235,11 @@ int kvq8_qk_partials(int32_t* partials, const float* q, int batch, int nq,
  * float32 (1.0 when max == min), floored at 1e-7 and rounded to binary16;
  * with s the stored binary16 scale, zero = clamp(rint(-min / s), 0, 15)
  * (stored as binary16, exact); code = clamp(rint(x / s + zero), 0, 15);
- * rint is round-half-to-even.  Arguments as for kvq8_quantize_append.
+ * rint is round-half-to-even.  Value rows store the pair of elements
+ * 64g + 4m + 2k, 64g + 4m + 2k + 1 (group g, m = 0..15, k = 0, 1) at byte
+ * 4m + 2g + k, key rows the pair 2i, 2i + 1 at byte i; in both the even
+ * element is in the high nibble.  Arguments and errors as for
+ * kvq8_quantize_append.
  */
 int kvq4_quantize_append(uint8_t* k_cache, uint8_t* v_cache,
                          uint16_t* k_scale, uint16_t* k_zero, uint16_t* v_scale, uint16_t* v_zero,
@@ -330,7 +339,8 @@ int kvq4_decode_attn(float* out, const float* q, int batch, int nq,
  * outside [0, n_blocks * kv_bs) are skipped.  Errors: KVQ8_ESHAPE for
  * hd != 128, an invalid kv_bs (a power of two in [8, 1024]), nkv < 1 or
  * n_blocks < 1; KVQ8_EINVAL for a null or misaligned pointer, a bad dtype
- * or n_tokens < 0.  n_tokens == 0 enqueues nothing.
+ * or n_tokens < 0; KVQ8_ESHAPE also for more than 2^31 - 65 rows
+ * (n_tokens * nkv * 2).  n_tokens == 0 enqueues nothing.
  */
 int kvq4_0_quantize_append(uint8_t* k_cache, uint8_t* v_cache, float* k_step, float* v_step,
                            int n_blocks, int kv_bs, int nkv, int hd,

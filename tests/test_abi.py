@@ -195,3 +195,15 @@ def test_q4_0_validation_and_sizing():
     assert call(a11=0) == OK
     assert call(a12=None) == EINVAL
     assert call(a2=_fake(4104)) == EINVAL             # step array not 16-byte aligned
+    assert call(a11=1 << 27) == ESHAPE                # 2^31 rows: beyond 32-bit row indexing
+
+
+def test_write_row_limit():
+    """Every write path indexes rows in 32 bits and rejects larger calls before
+    launching anything."""
+    lib = K.lib()
+    big = 1 << 27                                     # x 8 heads x 2 = 2^31 rows
+    assert lib.kvq8_quantize_append(_fake(), _fake(), _fake(), _fake(), 64, 16, 8, 128, _fake(), _fake(), K.F32,
+                                    big, _fake(), None) == ESHAPE
+    assert lib.kvq4_quantize_append(_fake(), _fake(), _fake(), _fake(), _fake(), _fake(), 64, 16, 8, 128,
+                                    _fake(), _fake(), K.BF16, big, _fake(), None) == ESHAPE
