@@ -114,6 +114,55 @@ __device__ __forceinline__ void load_new16(const void* base, size_t elem_off, fl
     }
 }
 
+// The new token's rows for the fused write path: lanes 0-31 hold 4 values
+// of the K row, lanes 32-63 4 values of the V row (elements 4 (lane % 32) ..).
+template <int DT>
+__device__ __forceinline__ void load_new4(const void* base, size_t elem_off, float (&x)[4]) {
+    if constexpr (DT == KVQ8_F32) {
+        const float4 t = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem_off);
+        x[0] = t.x;
+        x[1] = t.y;
+        x[2] = t.z;
+        x[3] = t.w;
+    } else {
+        const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + elem_off);
+        const uint32_t w[2] = {u.x, u.y};
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            if constexpr (DT == KVQ8_BF16) {
+                x[2 * k] = __uint_as_float(w[k] << 16);
+                x[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+            } else {
+                x[2 * k] = half_bits_f(w[k] & 0xFFFFu);
+                x[2 * k + 1] = half_bits_f(w[k] >> 16);
+            }
+        }
+    }
+}
+
+// Quantize a 128-value row held by an aligned 32-lane half of the wave, 4
+// values per lane (the rule of quantize_row8x16, the maximum over 32 lanes):
+// returns the lane's 4 codes (one word) and the row's step.
+__device__ __forceinline__ void quantize_row32x4(const float (&x)[4], uint32_t& codes, float& d) {
+#pragma clang fp contract(off)
+    float amax = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+    amax = fmaxf(amax, dpp_f<kDppXor1>(amax));
+    amax = fmaxf(amax, dpp_f<kDppXor2>(amax));
+    amax = fmaxf(amax, dpp_f<kDppHalfMirror>(amax));
+    amax = fmaxf(amax, dpp_f<kDppRowRor8>(amax));
+    amax = fmaxf(amax, swz_xor16(amax));
+    if (amax < 1e-6f) amax = 1.0f;
+    d = amax / 127.0f;
+    uint32_t w = 0u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        float r = roundf(x[e] / d);
+        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        w |= ((uint32_t)(int)r & 0xFFu) << (8 * e);
+    }
+    codes = w;
+}
+
 // Quantize a 128-value row held by an aligned 8-lane group, 16 values per
 // lane: returns the lane's 16 codes (packed) and the row's step.
 __device__ __forceinline__ void quantize_row8x16(const float (&x)[16], uint4& codes, float& d) {

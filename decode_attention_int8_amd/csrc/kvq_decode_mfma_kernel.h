@@ -30,6 +30,9 @@ __global__ __launch_bounds__(kWGThreads, 2) void kvq_decode_mfma_kernel(DecodeAr
     const int32_t* btb = a.r8.bt + (size_t)b * a.r8.max_blocks;
     const int first = c0 + wave * kTile;
     int raw = mtile_raw(a.r8, btb, first, a.log2_bs, lane);
+    // the query rows do not depend on the length: their loads go out with the
+    // table entries, so their quantization never waits on the tile behind them
+    const float4 qx = load_q4(a.q + ((size_t)b * a.nq + (size_t)kh * G) * kHD, G);
     const int L = effective_len(a.r8, b, a.log2_bs);
     if (c0 >= L) return;                                       // uniform per workgroup
     const int end = min(L, c0 + chunk_len);
@@ -39,17 +42,12 @@ __global__ __launch_bounds__(kWGThreads, 2) void kvq_decode_mfma_kernel(DecodeAr
     // fused write path: one wave owns the token at L-1
     const int tn = L - 1;
     const bool has_new = NEWDT >= 0 && tn >= c0 && tn < end && (((tn - c0) >> 6) & (kWaves - 1)) == wave;
-    // the query loads go out first (their quantization must not wait for the
-    // tile behind them), then the new token's, then the first tile's
-    const float4 qx = load_q4(a.q + ((size_t)b * a.nq + (size_t)kh * G) * kHD, G);
-    float xn[16];
+    // then the new token's loads, then the first tile's
+    float xn[4];
     if constexpr (NEWDT >= 0) {
         if (has_new) {
-            // lanes 0-7: K row, lanes 8-15: V row, 16 values each (lanes above
-            // 15 repeat them)
-            const int j = lane & 15;
-            const void* src = (j < 8) ? a.k_new : a.v_new;
-            load_new16<NEWDT>(src, ((size_t)b * a.nkv + kh) * kHD + 16 * (j & 7), xn);
+            // lanes 0-31: K row, lanes 32-63: V row, 4 values each
+            load_new4<NEWDT>(lane < 32 ? a.k_new : a.v_new, ((size_t)b * a.nkv + kh) * kHD + 4 * (lane & 31), xn);
         }
     }
 
@@ -62,26 +60,13 @@ __global__ __launch_bounds__(kWGThreads, 2) void kvq_decode_mfma_kernel(DecodeAr
     quantize_q4(qx, G, sm.q);
     if constexpr (NEWDT >= 0) {
         if (has_new) {
-            uint4 codes;
+            // the new token's codes and steps go to LDS; its terminal tile
+            // takes them in place of the slot's stale copy and stores them
+            uint32_t codes;
             float d;
-            quantize_row8x16(xn, codes, d);
-            const int j = lane & 15;
-            if (lane < 16) {
-                const v4u_t cw = {codes.x, codes.y, codes.z, codes.w};
-                if (j < 8)
-                    sm.nk[j] = cw;
-                else
-                    sm.nv[j - 8] = cw;
-                if ((j & 7) == 0) sm.nstep[j >> 3] = d;
-            }
-            // store into the cache slot of token tn
-            const int bid = btb[min(tn >> a.log2_bs, a.r8.max_blocks - 1)];
-            if (lane < 16 && bid >= 0 && bid < a.r8.n_blocks) {
-                const size_t row = (((size_t)bid << a.log2_bs) + (tn & ((1 << a.log2_bs) - 1))) * a.nkv + kh;
-                int8_t* dst = (j < 8 ? a.kc_w : a.vc_w) + row * kHD + 16 * (j & 7);
-                *reinterpret_cast<uint4*>(dst) = codes;
-                if ((j & 7) == 0) (j < 8 ? a.ks_w : a.vs_w)[row] = d;
-            }
+            quantize_row32x4(xn, codes, d);
+            reinterpret_cast<uint32_t*>(lane < 32 ? sm.nk : sm.nv)[lane & 31] = codes;
+            if ((lane & 31) == 0) sm.nstep[lane >> 5] = d;
         }
     }
     lds_barrier();
@@ -100,10 +85,22 @@ __global__ __launch_bounds__(kWGThreads, 2) void kvq_decode_mfma_kernel(DecodeAr
     // the last tile of a wave: only the two terminal calls substitute, with
     // selects that match nothing outside the owner's tile.
     auto run_last = [&](const MTile& T, int base) __attribute__((always_inline)) {
-        if constexpr (NEWDT >= 0)
+        if constexpr (NEWDT >= 0) {
+            if (has_new) {
+                // store the new token into its cache slot: the block id is the
+                // tile's own table entry of position tn (-1 outside the pool)
+                const int bid = __builtin_amdgcn_readlane(T.id, tn - base);
+                if (bid >= 0) {
+                    const size_t row = (((size_t)bid << a.log2_bs) + (tn & ((1 << a.log2_bs) - 1))) * a.nkv + kh;
+                    const uint32_t w = reinterpret_cast<const uint32_t*>(lane < 32 ? sm.nk : sm.nv)[lane & 31];
+                    *reinterpret_cast<uint32_t*>((lane < 32 ? a.kc_w : a.vc_w) + row * kHD + 4 * (lane & 31)) = w;
+                    if ((lane & 31) == 0) (lane < 32 ? a.ks_w : a.vs_w)[row] = sm.nstep[lane >> 5];
+                }
+            }
             mtile_compute(a, mtile_substitute(T, sm, base, tn, lane), base, L, lane, wave, Q, st, sm);
-        else
+        } else {
             mtile_compute(a, T, base, L, lane, wave, Q, st, sm);
+        }
     };
     // double-buffered walk: tile k+1's keys and steps are in flight while
     // tile k is computed, its values from the end of tile k's P.V on; the
