@@ -351,8 +351,11 @@ __global__ __launch_bounds__(kWGThreads, 2) void kvq4_decode_mfma_kernel(DecodeA
     if (int4_region) {
         const LaneOff4 lo = lane_offsets4(a, lane);
         MTile4 A, B;
+        // the table entries of the tile after next go out before a tile's
+        // loads, so the loop head waits for them without waiting for the tile
+        int raw_next = mtile_raw(reg, btb, first + kChunkUnit, a.log2_bs, lane);
         mtile4_issue<BS8>(a, raw, first, kh, lane, lo, A);
-        raw = mtile_raw(reg, btb, first + kChunkUnit, a.log2_bs, lane);
+        raw = raw_next;
         __asm__ volatile("" ::: "memory");
         quantize_q4(qx, G, sm.q);
         lds_barrier();
@@ -363,26 +366,27 @@ __global__ __launch_bounds__(kWGThreads, 2) void kvq4_decode_mfma_kernel(DecodeA
         st.E = 100;
 #pragma unroll
         for (int sl = 0; sl < 8; ++sl) st.acc[sl] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
+        // two tiles per trip, one exit test at the top (as in the int8 walk)
         int base = first;
-        for (int k = 0;;) {
-            if (k + 1 >= n_tiles) {
-                mtile4_compute(a, A, base, L, lane, wave, Q, st, sm);
-                break;
-            }
+        int k = 0;
+        for (; k + 2 < n_tiles; k += 2) {
+            raw_next = mtile_raw(reg, btb, base + 2 * kChunkUnit, a.log2_bs, lane);
             mtile4_issue<BS8>(a, raw, base + kChunkUnit, kh, lane, lo, B);
-            raw = mtile_raw(reg, btb, base + 2 * kChunkUnit, a.log2_bs, lane);
+            raw = raw_next;
             mtile4_compute(a, A, base, L, lane, wave, Q, st, sm);
             base += kChunkUnit;
-            ++k;
-            if (k + 1 >= n_tiles) {
-                mtile4_compute(a, B, base, L, lane, wave, Q, st, sm);
-                break;
-            }
+            raw_next = mtile_raw(reg, btb, base + 2 * kChunkUnit, a.log2_bs, lane);
             mtile4_issue<BS8>(a, raw, base + kChunkUnit, kh, lane, lo, A);
-            raw = mtile_raw(reg, btb, base + 2 * kChunkUnit, a.log2_bs, lane);
+            raw = raw_next;
             mtile4_compute(a, B, base, L, lane, wave, Q, st, sm);
             base += kChunkUnit;
-            ++k;
+        }
+        if (k + 1 < n_tiles) {
+            mtile4_issue<BS8>(a, raw, base + kChunkUnit, kh, lane, lo, B);
+            mtile4_compute(a, A, base, L, lane, wave, Q, st, sm);
+            mtile4_compute(a, B, base + kChunkUnit, L, lane, wave, Q, st, sm);
+        } else {
+            mtile4_compute(a, A, base, L, lane, wave, Q, st, sm);
         }
         mwave4_to_lds(sm, st, G, lane, wave);
         lds_barrier();
@@ -390,8 +394,9 @@ __global__ __launch_bounds__(kWGThreads, 2) void kvq4_decode_mfma_kernel(DecodeA
     } else {
         const LaneOff lo = lane_offsets(a, lane);
         MTile A, B;
-        mtile_issue<BS8>(a, raw, first, kh, lane, lo, A);
+        mtile_issue<BS8, kIssueKeys | kIssueSteps>(a, raw, first, kh, lane, lo, A);
         raw = mtile_raw(reg, btb, first + kChunkUnit, a.log2_bs, lane);
+        mtile_issue<BS8, kIssueValues>(a, 0, first, kh, lane, lo, A);
         __asm__ volatile("" ::: "memory");
         quantize_q4(qx, G, sm.q);
         lds_barrier();
@@ -403,29 +408,29 @@ __global__ __launch_bounds__(kWGThreads, 2) void kvq4_decode_mfma_kernel(DecodeA
 #pragma unroll
         for (int sl = 0; sl < 8; ++sl) st.acc[sl] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
         int base = first;
-        for (int k = 0;;) {
-            if (k + 1 >= n_tiles) {
-                mtile_compute(a, A, base, L, lane, wave, Q, st, sm);
-                break;
-            }
+        int k = 0;
+        for (; k + 2 < n_tiles; k += 2) {
             mtile_issue<BS8, kIssueKeys | kIssueSteps>(a, raw, base + kChunkUnit, kh, lane, lo, B);
             raw = mtile_raw(reg, btb, base + 2 * kChunkUnit, a.log2_bs, lane);
             mtile_compute(a, A, base, L, lane, wave, Q, st, sm, NoHook(), [&]() __attribute__((always_inline)) {
                 mtile_issue<BS8, kIssueValues>(a, 0, base + kChunkUnit, kh, lane, lo, B);
             });
             base += kChunkUnit;
-            ++k;
-            if (k + 1 >= n_tiles) {
-                mtile_compute(a, B, base, L, lane, wave, Q, st, sm);
-                break;
-            }
             mtile_issue<BS8, kIssueKeys | kIssueSteps>(a, raw, base + kChunkUnit, kh, lane, lo, A);
             raw = mtile_raw(reg, btb, base + 2 * kChunkUnit, a.log2_bs, lane);
             mtile_compute(a, B, base, L, lane, wave, Q, st, sm, NoHook(), [&]() __attribute__((always_inline)) {
                 mtile_issue<BS8, kIssueValues>(a, 0, base + kChunkUnit, kh, lane, lo, A);
             });
             base += kChunkUnit;
-            ++k;
+        }
+        if (k + 1 < n_tiles) {
+            mtile_issue<BS8, kIssueKeys | kIssueSteps>(a, raw, base + kChunkUnit, kh, lane, lo, B);
+            mtile_compute(a, A, base, L, lane, wave, Q, st, sm, NoHook(), [&]() __attribute__((always_inline)) {
+                mtile_issue<BS8, kIssueValues>(a, 0, base + kChunkUnit, kh, lane, lo, B);
+            });
+            mtile_compute(a, B, base + kChunkUnit, L, lane, wave, Q, st, sm);
+        } else {
+            mtile_compute(a, A, base, L, lane, wave, Q, st, sm);
         }
         mwrite_partial(a, sm, st, G, b, kh, c, lane, wave);
     }
