@@ -41,9 +41,9 @@ TOK_HEAD_BYTES = 2 * 128 + 2 * 4   # K+V codes + K/V float32 steps per (token, k
 # counters read for a plain 256 MiB device copy (--calibrate-copy 256):
 # FETCH_SIZE 131085.3 KiB -> 2.000 bytes per counted byte, WRITE_SIZE
 # 262144 KiB -> 1.000.  Valid only for the kernel sources they were taken on.
-PMC = {"sources_sha256_16": "2c42b969f2277f7e",
-       "fetch_kib": {"chunk": 8581.34, "merge": 174.54}, "write_kib": {"chunk": 290.06, "merge": 8.0},
-       "fetch_scale": 268435456 / (131085.21 * 1024), "write_scale": 268435456 / (262144.0 * 1024)}
+PMC = {"sources_sha256_16": "01266161ccbe192d",
+       "fetch_kib": {"chunk": 8585.86, "merge": 174.53}, "write_kib": {"chunk": 290.06, "merge": 8.0},
+       "fetch_scale": 268435456 / (131085.15 * 1024), "write_scale": 268435456 / (262144.0 * 1024)}
 
 
 def kernel_sources_digest() -> str:
@@ -159,9 +159,11 @@ def cpu_baseline(args, nq, nkv, bs, L, bytes_per_layer):
                       f"heads), {el:.1f} s single-threaded numpy; ms/layer {1e3 * el / layers:.1f}"}
 
 
-def time_calls(torch, fn, iters, warmup=3, graph=False):
+def time_calls(torch, fn, iters, warmup=10, graph=False):
     """Average microseconds per call of fn() on the current stream, HIP events
-    around `iters` back-to-back calls (captured as one graph when `graph`)."""
+    around `iters` back-to-back calls (captured as one graph when `graph`).
+    The mode is recorded for `report`."""
+    time_calls.last_mode = "graph replay" if graph else "eager, back to back"
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -192,7 +194,8 @@ def time_calls(torch, fn, iters, warmup=3, graph=False):
 def report(name, desc, nbytes, us, **extra):
     gbs = nbytes / (us * 1e-6) / 1e9
     line = {"workload": name, "desc": desc, "algorithmic_bytes": int(nbytes), "us_per_call": round(us, 2),
-            "GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+            "GB/s": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "timing": getattr(time_calls, "last_mode", None)}
     line.update(extra)
     print(json.dumps(line), flush=True)
 
@@ -203,7 +206,10 @@ def run_workloads(only=None):
     write path and the decode over it, the int4 128K mixed decode, and the
     int8 -> int4 re-quantization of aging time blocks.  Inputs follow the
     recipes of `workloads` (generated on the GPU, quantized through the
-    library's write paths)."""
+    library's write paths).  Calls of under about 50 us are timed as one graph
+    replay of back-to-back calls (eager calls would measure the host's launch
+    path); longer ones as back-to-back eager calls, which run them faster on
+    this GPU than a graph replay does.  Each line names its timing mode."""
     import torch
 
     import decode_attention_int8_amd as K
@@ -277,7 +283,7 @@ def run_workloads(only=None):
         btd, ld = dev(bt), dev(np.array([n], np.int32))
         ch = K.kvq8_decode_chunk_tokens(1, nkv, n)
         ws = K.alloc_workspace(K.kvq8_decode_workspace_size(1, nq, nkv, n), "cuda")
-        us = time_calls(torch, lambda: K.kvq8_decode_attn(out, qd, *p, btd, ld, n, sm, 0, ws), 50)
+        us = time_calls(torch, lambda: K.kvq8_decode_attn(out, qd, *p, btd, ld, n, sm, 0, ws), 50, graph=True)
         report("decode_64k", "decode, 1 sequence x 32 / 8 heads over the 65536 written tokens", n * nkv * 264, us,
                chunk_tokens=ch)
         del p, kk, vv
@@ -321,7 +327,7 @@ def run_workloads(only=None):
         n_all = B * n8
         src = dev(np.concatenate([W.slots_for_positions(bt8, [b] * n8, np.arange(n8), bs) for b in range(B)]))
         dst = dev(np.concatenate([W.slots_for_positions(bt4, [b] * n8, np.arange(n8), bs) for b in range(B)]))
-        us = time_calls(torch, lambda: K.kvq4_requantize_q8(p4, p8, src, dst), 50)
+        us = time_calls(torch, lambda: K.kvq4_requantize_q8(p4, p8, src, dst), 50, graph=True)
         report("requant_window", "int8 -> int4 re-quantization of the whole 2048-token window x 4 sequences",
                n_all * nkv * (264 + 144), us)
         del p4, p8
@@ -398,7 +404,7 @@ def run_workloads(only=None):
         out = torch.empty((1, nq, 128), device="cuda")
         btd, ld = dev(bt), dev(np.array([n], np.int32))
         ws = K.alloc_workspace(K.kvq4_0_decode_workspace_size(1, nq, nkv, n), "cuda")
-        us = time_calls(torch, lambda: K.kvq4_0_decode_attn(out, qd, *p, btd, ld, n, sm, 0, ws), 50)
+        us = time_calls(torch, lambda: K.kvq4_0_decode_attn(out, qd, *p, btd, ld, n, sm, 0, ws), 50, graph=True)
         report("q40_decode_64k", "Q4_0 decode, 1 sequence x 32 / 8 heads over the 65536 written tokens",
                n * nkv * 160, us, chunk_tokens=K.kvq4_0_decode_chunk_tokens(1, nkv, n))
 

@@ -108,35 +108,31 @@ __global__ __launch_bounds__(kWGThreads, 2) void kvq_decode_mfma_kernel(DecodeAr
     };
     // double-buffered walk: tile k+1's keys and steps are in flight while
     // tile k is computed, its values from the end of tile k's P.V on; the
-    // table entries run one tile further ahead.  Two tiles per trip and one
-    // exit test at the top: an exit from the middle of the body would give
-    // the loop head a path on which the first half's value loads are still
-    // in flight, and its wait would then cover every load.
+    // table entries run one tile further ahead
     int base = first;
-    int k = 0;
-    for (; k + 2 < n_tiles; k += 2) {
+    for (int k = 0;;) {
+        if (k + 1 >= n_tiles) {
+            run_last(A, base);
+            break;
+        }
         mtile_issue<BS8, kIssueKeys | kIssueSteps>(a, raw, base + kChunkUnit, kh, lane, lo, B);
         raw = mtile_raw(a.r8, btb, base + 2 * kChunkUnit, a.log2_bs, lane);
         mtile_compute(a, A, base, L, lane, wave, Q, st, sm, NoHook(), [&]() __attribute__((always_inline)) {
             mtile_issue<BS8, kIssueValues>(a, 0, base + kChunkUnit, kh, lane, lo, B);
         });
         base += kChunkUnit;
+        ++k;
+        if (k + 1 >= n_tiles) {
+            run_last(B, base);
+            break;
+        }
         mtile_issue<BS8, kIssueKeys | kIssueSteps>(a, raw, base + kChunkUnit, kh, lane, lo, A);
         raw = mtile_raw(a.r8, btb, base + 2 * kChunkUnit, a.log2_bs, lane);
         mtile_compute(a, B, base, L, lane, wave, Q, st, sm, NoHook(), [&]() __attribute__((always_inline)) {
             mtile_issue<BS8, kIssueValues>(a, 0, base + kChunkUnit, kh, lane, lo, A);
         });
         base += kChunkUnit;
-    }
-    if (k + 1 < n_tiles) {
-        // two tiles left
-        mtile_issue<BS8, kIssueKeys | kIssueSteps>(a, raw, base + kChunkUnit, kh, lane, lo, B);
-        mtile_compute(a, A, base, L, lane, wave, Q, st, sm, NoHook(), [&]() __attribute__((always_inline)) {
-            mtile_issue<BS8, kIssueValues>(a, 0, base + kChunkUnit, kh, lane, lo, B);
-        });
-        run_last(B, base + kChunkUnit);
-    } else {
-        run_last(A, base);
+        ++k;
     }
     mwrite_partial(a, sm, st, G, b, kh, c, lane, wave);
 }
