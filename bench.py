@@ -33,6 +33,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, vendor figure
+# bytes of other reads between two touches of the same cache data in the timed
+# decode workloads: twice the 256 MB Infinity Cache
+MALL_FLUSH_BYTES = 512 << 20
 TOK_HEAD_BYTES = 2 * 128 + 2 * 4   # K+V codes + K/V float32 steps per (token, kv-head)
 
 
@@ -226,6 +229,22 @@ def run_workloads(only=None):
                 torch.zeros(shp[:3], dtype=torch.float32, device="cuda"),
                 torch.zeros(shp[:3], dtype=torch.float32, device="cuda")]
 
+    def mall_copies(nbytes):
+        """Cache copies to cycle through so that a call's data was last touched
+        at least 512 MB of other reads earlier, past the 256 MB Infinity Cache
+        (a working set of that size or more needs no second copy)."""
+        return 1 if nbytes >= MALL_FLUSH_BYTES else 1 + math.ceil(MALL_FLUSH_BYTES / nbytes)
+
+    def cycled(call, pools, iters):
+        """fn() calling `call(pool)` for the pools in turn, and an iteration
+        count that is a multiple of their number (at least `iters`)."""
+        state = [0]
+
+        def fn():
+            call(pools[state[0] % len(pools)])
+            state[0] += 1
+        return fn, len(pools) * math.ceil(iters / len(pools))
+
     def q4_pool(nb, bs, nkv):
         shp = (nb, bs, nkv)
         return [torch.zeros(shp + (64,), dtype=torch.uint8, device="cuda"),
@@ -283,10 +302,15 @@ def run_workloads(only=None):
         btd, ld = dev(bt), dev(np.array([n], np.int32))
         ch = K.kvq8_decode_chunk_tokens(1, nkv, n)
         ws = K.alloc_workspace(K.kvq8_decode_workspace_size(1, nq, nkv, n), "cuda")
-        us = time_calls(torch, lambda: K.kvq8_decode_attn(out, qd, *p, btd, ld, n, sm, 0, ws), 50, graph=True)
-        report("decode_64k", "decode, 1 sequence x 32 / 8 heads over the 65536 written tokens", n * nkv * 264, us,
-               chunk_tokens=ch)
-        del p, kk, vv
+        del kk, vv
+        nbytes = n * nkv * 264
+        pools = [p] + [[t.clone() for t in p] for _ in range(mall_copies(nbytes) - 1)]
+        fn, iters = cycled(lambda pp: K.kvq8_decode_attn(out, qd, *pp, btd, ld, n, sm, 0, ws), pools, 50)
+        us = time_calls(torch, fn, iters, graph=True)
+        report("decode_64k", f"decode, 1 sequence x 32 / 8 heads over the 65536 written tokens ({len(pools)} copies "
+               "of the cache cycled)", nbytes, us, chunk_tokens=ch)
+        del pools
+        del p
 
     if want("q4_128k", "requant_block", "requant_window"):
         # int4 group cache, 128K tokens (last 2048 int8), batch 4 x 32 / 4 heads
@@ -311,9 +335,15 @@ def run_workloads(only=None):
         bt8d, l8 = dev(bt8), dev(np.full(B, n8, np.int32))
         ch = K.kvq4_decode_chunk_tokens(B, nkv, n4, n8)
         ws = K.alloc_workspace(K.kvq4_decode_workspace_size(B, nq, nkv, n4, n8), "cuda")
-        us = time_calls(torch, lambda: K.kvq4_decode_attn(out, qd, p4, bt4d, l4, n4, p8, bt8d, l8, n8, sm, 0, ws), 20)
-        report("q4_128k", "mixed decode, batch 4 x 32 / 4 heads, 129024 int4 + 2048 int8 tokens",
-               B * nkv * (n4 * 144 + n8 * 264), us, chunk_tokens=ch)
+        nbytes = B * nkv * (n4 * 144 + n8 * 264)
+        pools = [(p4, p8)] + [([t.clone() for t in p4], [t.clone() for t in p8])
+                              for _ in range(mall_copies(nbytes) - 1)]
+        fn, iters = cycled(lambda pp: K.kvq4_decode_attn(out, qd, pp[0], bt4d, l4, n4, pp[1], bt8d, l8, n8, sm, 0, ws),
+                           pools, 20)
+        us = time_calls(torch, fn, iters)
+        report("q4_128k", f"mixed decode, batch 4 x 32 / 4 heads, 129024 int4 + 2048 int8 tokens ({len(pools)} "
+               "copies of the cache cycled)", nbytes, us, chunk_tokens=ch)
+        del pools
 
         # re-quantization of the window's oldest 512-token time block of every
         # sequence into the int4 pool (into the int4 pool's first 512 slots per
@@ -404,9 +434,15 @@ def run_workloads(only=None):
         out = torch.empty((1, nq, 128), device="cuda")
         btd, ld = dev(bt), dev(np.array([n], np.int32))
         ws = K.alloc_workspace(K.kvq4_0_decode_workspace_size(1, nq, nkv, n), "cuda")
-        us = time_calls(torch, lambda: K.kvq4_0_decode_attn(out, qd, *p, btd, ld, n, sm, 0, ws), 50, graph=True)
-        report("q40_decode_64k", "Q4_0 decode, 1 sequence x 32 / 8 heads over the 65536 written tokens",
-               n * nkv * 160, us, chunk_tokens=K.kvq4_0_decode_chunk_tokens(1, nkv, n))
+        del kk, vv
+        nbytes = n * nkv * 160
+        pools = [p] + [[t.clone() for t in p] for _ in range(mall_copies(nbytes) - 1)]
+        fn, iters = cycled(lambda pp: K.kvq4_0_decode_attn(out, qd, *pp, btd, ld, n, sm, 0, ws), pools, 50)
+        us = time_calls(torch, fn, iters, graph=True)
+        report("q40_decode_64k", f"Q4_0 decode, 1 sequence x 32 / 8 heads over the 65536 written tokens ({len(pools)} "
+               "copies of the cache cycled)", nbytes, us, chunk_tokens=K.kvq4_0_decode_chunk_tokens(1, nkv, n))
+        del pools
+
 
 def main():
     args = parse()
