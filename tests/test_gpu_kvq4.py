@@ -99,6 +99,38 @@ def test_q4_mixed_decode(K, g):
     assert_attn_close(host(out), ref, f"int4 mixed g={g}")
 
 
+@pytest.mark.parametrize("chunk", [512, 768, 1280, 2048])
+def test_q4_mixed_decode_chunk_sizes(K, chunk):
+    """Chunks of 2-8 tiles per wave with ragged lengths: every wave count of
+    tiles from 1 to 8 occurs (the walks run two tiles per trip, then one or
+    two more)."""
+    r = W.rng(411, chunk)
+    nkv, bs, g = 2, 16, 4
+    nq = g * nkv
+    lens4 = np.array([3001, 1, 700, 2300, 1279], np.int32)
+    lens8 = np.array([100, 64, 0, 257, 1], np.int32)
+    B = len(lens4)
+    bt4, nb4 = W.paged_block_tables(r, lens4, bs)
+    bt8, nb8 = W.paged_block_tables(r, lens8, bs, spare_blocks=1)
+    p4 = Q4Pool(nb4, bs, nkv)
+    c8 = Q8Cache(nb8, bs, nkv)
+    for b in range(B):
+        k = W.per_unit_sigma_normal(r, (int(lens4[b]), nkv, 128), 0, 0.5, 2.0)
+        p4.append(K, k, W.normal_f32(r, k.shape), W.slots_for_positions(bt4, [b] * lens4[b], np.arange(lens4[b]), bs))
+        if lens8[b]:
+            k = W.normal_f32(r, (int(lens8[b]), nkv, 128))
+            c8.append(k, W.normal_f32(r, k.shape), W.slots_for_positions(bt8, [b] * lens8[b], np.arange(lens8[b]), bs))
+    import torch
+    q = W.normal_f32(r, (B, nq, 128), 2.0)
+    out = torch.full((B, nq, 128), float("nan"), dtype=torch.float32, device="cuda")
+    K.kvq4_decode_attn(out, dev(q), p4.g, dev(bt4), dev(lens4), int(lens4.max()),
+                       (c8.gk, c8.gv, c8.gks, c8.gvs), dev(bt8), dev(lens8), int(lens8.max()), SM, chunk=chunk)
+    torch.cuda.synchronize()
+    ref = O4.decode_attention_mixed(q, p4.oracle_pools(), bt4, lens4, (c8.kp, c8.ks, c8.vp, c8.vs), bt8, lens8,
+                                    bs, SM)
+    assert_attn_close(host(out), ref, f"int4 mixed chunk {chunk}")
+
+
 def test_q4_only_int8_window_equals_int8_path(K):
     import torch
     r = W.rng(420)
