@@ -75,11 +75,18 @@ __device__ __forceinline__ void q40_quantize8(const float (&x)[8], uint32_t& lo,
     mn = fminf(mn, dpp_f<kDppXor2>(mn));
     const float m = (-mn >= mx) ? mn : mx;           // negative extreme wins a tie
     step = (m == 0.0f) ? 0.0f : m * -0.125f;         // exact: a power-of-two division
+    const float rs = __builtin_amdgcn_rcpf(step);
     uint32_t w[2] = {0u, 0u};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         float c = 8.0f;
-        if (step != 0.0f) c = fminf(floorf(x[e] / step + 8.5f), 15.0f);
+        if (step != 0.0f) {
+            // floor(x / step + 8.5), the quotient computed only near a half-integer
+            const float q = x[e] * rs;
+            c = floorf(q + 8.5f);
+            if (near_half(q)) c = floorf(x[e] / step + 8.5f);
+            c = fminf(c, 15.0f);
+        }
         w[e >> 2] |= (uint32_t)(int)c << (8 * (e & 3));
     }
     lo = w[0];

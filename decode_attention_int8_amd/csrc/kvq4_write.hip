@@ -63,11 +63,20 @@ __device__ __forceinline__ void quantize_group8x8(const float (&x)[8], uint32_t&
     // integer zero point in [0, 15]; + 0.0f stores a zero as +0.0
     const float z = fminf(fmaxf(rintf(-mn / s), 0.0f), 15.0f) + 0.0f;
     z16 = f16_bits_rne(z);
+    const float rs = __builtin_amdgcn_rcpf(s);
+    // rint(x / s + z) with z an integer, the quotient computed only near a
+    // half-integer
+    auto code = [&](float xv) __attribute__((always_inline)) {
+        const float q = xv * rs;
+        float c = rintf(q + z);
+        if (near_half(q)) c = rintf(xv / s + z);
+        return fminf(fmaxf(c, 0.0f), 15.0f);
+    };
     uint32_t w = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const float ce = fminf(fmaxf(rintf(x[2 * k] / s + z), 0.0f), 15.0f);
-        const float co = fminf(fmaxf(rintf(x[2 * k + 1] / s + z), 0.0f), 15.0f);
+        const float ce = code(x[2 * k]);
+        const float co = code(x[2 * k + 1]);
         w |= (((uint32_t)ce << 4) | (uint32_t)co) << (8 * k);
     }
     packed = w;

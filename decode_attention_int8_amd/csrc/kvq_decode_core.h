@@ -153,10 +153,14 @@ __device__ __forceinline__ void quantize_row32x4(const float (&x)[4], uint32_t& 
     amax = fmaxf(amax, swz_xor16(amax));
     if (amax < 1e-6f) amax = 1.0f;
     d = amax / 127.0f;
+    const float rd = __builtin_amdgcn_rcpf(d);
     uint32_t w = 0u;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        float r = roundf(x[e] / d);
+        // roundf(x / d), the quotient computed only near a half-integer
+        const float q = x[e] * rd;
+        float r = rintf(q);
+        if (near_half(q)) r = roundf(x[e] / d);
         r = fminf(fmaxf(r, -127.0f), 127.0f);
         w |= ((uint32_t)(int)r & 0xFFu) << (8 * e);
     }
@@ -175,10 +179,14 @@ __device__ __forceinline__ void quantize_row8x16(const float (&x)[16], uint4& co
     amax = fmaxf(amax, dpp_f<kDppHalfMirror>(amax));
     if (amax < 1e-6f) amax = 1.0f;
     d = amax / 127.0f;
+    const float rd = __builtin_amdgcn_rcpf(d);
     uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-        float r = roundf(x[e] / d);
+        // roundf(x / d), the quotient computed only near a half-integer
+        const float q = x[e] * rd;
+        float r = rintf(q);
+        if (near_half(q)) r = roundf(x[e] / d);
         r = fminf(fmaxf(r, -127.0f), 127.0f);
         w[e >> 2] |= ((uint32_t)(int)r & 0xFFu) << (8 * (e & 3));
     }

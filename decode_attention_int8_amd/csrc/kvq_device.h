@@ -109,6 +109,18 @@ __device__ __forceinline__ void lds_barrier() {
     __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Rounding a quotient to an integer without dividing.  The quantizers round
+// x / d, the IEEE quotient, to an integer (to nearest, or down after adding
+// one half).  q = x * rcp(d), with v_rcp_f32 within one ulp of 1 / d, lies
+// within |q| * 2^-21 of that quotient for normal operands, so rounding q gives
+// the same integer unless one of the two lies within that distance of a
+// half-integer.  `near_half` flags q within 2^-12 + |q| * 2^-19 of one (and
+// any q that is not finite); there the caller divides.  The margin is four
+// times the bound and more; the flag is raised for about 0.1% of the values.
+__device__ __forceinline__ bool near_half(float q) {
+    return !(fabsf(q - rintf(q)) <= 0.5f - (0x1p-12f + fabsf(q) * 0x1p-19f));
+}
+
 // IEEE binary16 bits (low 16 bits of v) widened to float (exact)
 __device__ __forceinline__ float half_bits_f(uint32_t v) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)v);
