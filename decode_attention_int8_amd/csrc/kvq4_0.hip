@@ -81,10 +81,12 @@ __device__ __forceinline__ void q40_quantize8(const float (&x)[8], uint32_t& lo,
     for (int e = 0; e < 8; ++e) {
         float c = 8.0f;
         if (step != 0.0f) {
-            // floor(x / step + 8.5), the quotient computed only near a half-integer
+            // floor(x / step + 8.5), the quotient computed only near a
+            // half-integer (|x / step| <= 8); elsewhere it is rint(q) + 8
             const float q = x[e] * rs;
-            c = floorf(q + 8.5f);
-            if (near_half(q)) c = floorf(x[e] / step + 8.5f);
+            const float rq = rintf(q);
+            c = rq + 8.0f;
+            if (near_half_small(q, rq)) c = floorf(x[e] / step + 8.5f);
             c = fminf(c, 15.0f);
         }
         w[e >> 2] |= (uint32_t)(int)c << (8 * (e & 3));
@@ -99,7 +101,7 @@ __device__ __forceinline__ void q40_quantize8(const float (&x)[8], uint32_t& lo,
 template <int DT>
 __global__ __launch_bounds__(256) void kvq4_0_quantize_append_kernel(
     uint8_t* __restrict__ kc, uint8_t* __restrict__ vc, float* __restrict__ ks, float* __restrict__ vs,
-    long n_slots, int nkv, const void* __restrict__ k_new, const void* __restrict__ v_new, int n_rows,
+    long n_slots, DivN nkv, const void* __restrict__ k_new, const void* __restrict__ v_new, int n_rows,
     const int32_t* __restrict__ slots) {
     __shared__ uint8_t codes[kQ40RowsPerBlock][kHD];
     const int l16 = threadIdx.x & 15;
@@ -113,10 +115,10 @@ __global__ __launch_bounds__(256) void kvq4_0_quantize_append_kernel(
         const int row = (int)blockIdx.x * kQ40RowsPerBlock + k * 16 + grp;
         const int rc = min(row, n_rows - 1);
         const int tr = rc >> 1;                      // token * nkv + kv-head
-        const int tok = tr / nkv;
+        const int tok = div_n(tr, nkv);
         q40_load8<DT>((rc & 1) ? v_new : k_new, (size_t)tr * kHD + 8 * l16, x[k]);
         const long slot = slots[tok];
-        dst[k] = (row < n_rows && slot >= 0 && slot < n_slots) ? slot * nkv + (tr - tok * nkv) : -1;
+        dst[k] = (row < n_rows && slot >= 0 && slot < n_slots) ? slot * nkv.n + (tr - tok * nkv.n) : -1;
     }
     float step[kQ40RowsPerGroup];
 #pragma unroll
@@ -541,15 +543,15 @@ extern "C" int kvq4_0_quantize_append(uint8_t* k_cache, uint8_t* v_cache, float*
     switch (dtype) {
         case KVQ8_F32:
             hipLaunchKernelGGL(kvq4_0_quantize_append_kernel<KVQ8_F32>, grid, block, 0, s, k_cache, v_cache, k_step,
-                               v_step, n_slots, nkv, k_new, v_new, (int)n_rows, slots);
+                               v_step, n_slots, make_divn(nkv), k_new, v_new, (int)n_rows, slots);
             break;
         case KVQ8_BF16:
             hipLaunchKernelGGL(kvq4_0_quantize_append_kernel<KVQ8_BF16>, grid, block, 0, s, k_cache, v_cache,
-                               k_step, v_step, n_slots, nkv, k_new, v_new, (int)n_rows, slots);
+                               k_step, v_step, n_slots, make_divn(nkv), k_new, v_new, (int)n_rows, slots);
             break;
         default:
             hipLaunchKernelGGL(kvq4_0_quantize_append_kernel<KVQ8_F16>, grid, block, 0, s, k_cache, v_cache, k_step,
-                               v_step, n_slots, nkv, k_new, v_new, (int)n_rows, slots);
+                               v_step, n_slots, make_divn(nkv), k_new, v_new, (int)n_rows, slots);
             break;
     }
     return launch_status();

@@ -112,7 +112,7 @@ __device__ __forceinline__ void store_q4_row(uint8_t* __restrict__ kc, uint8_t* 
 template <int DT>
 __global__ __launch_bounds__(256) void kvq4_quantize_append_kernel(
     uint8_t* __restrict__ kc, uint8_t* __restrict__ vc, uint16_t* __restrict__ ks, uint16_t* __restrict__ kz,
-    uint16_t* __restrict__ vs, uint16_t* __restrict__ vz, long n_slots, int nkv, const void* __restrict__ k_new,
+    uint16_t* __restrict__ vs, uint16_t* __restrict__ vz, long n_slots, DivN nkv, const void* __restrict__ k_new,
     const void* __restrict__ v_new, int n_rows, const int32_t* __restrict__ slots) {
     const int l16 = threadIdx.x & 15;
     float x[kRowsPerGroup][8];
@@ -124,10 +124,10 @@ __global__ __launch_bounds__(256) void kvq4_quantize_append_kernel(
         const int row = (int)blockIdx.x * kRowsPerBlock + k * 16 + (threadIdx.x >> 4);
         const int rc = min(row, n_rows - 1);
         const int tr = rc >> 1;
-        const int tok = tr / nkv;
+        const int tok = div_n(tr, nkv);
         load8_any<DT>((rc & 1) ? v_new : k_new, (size_t)tr * kHD + 8 * l16, x[k]);
         const long slot = slots[tok];
-        dst[k] = (row < n_rows && slot >= 0 && slot < n_slots) ? slot * nkv + (tr - tok * nkv) : -1;
+        dst[k] = (row < n_rows && slot >= 0 && slot < n_slots) ? slot * nkv.n + (tr - tok * nkv.n) : -1;
     }
 #pragma unroll
     for (int k = 0; k < kRowsPerGroup; ++k) {
@@ -151,14 +151,14 @@ __global__ __launch_bounds__(256) void kvq4_requantize_q8_kernel(
     uint8_t* __restrict__ kc4, uint8_t* __restrict__ vc4, uint16_t* __restrict__ ks4, uint16_t* __restrict__ kz4,
     uint16_t* __restrict__ vs4, uint16_t* __restrict__ vz4, long n_slots4, const int8_t* __restrict__ kc8,
     const int8_t* __restrict__ vc8, const float* __restrict__ ks8, const float* __restrict__ vs8, long n_slots8,
-    int nkv, long n_rows, const int32_t* __restrict__ src, const int32_t* __restrict__ dst) {
+    DivN nkv, int n_rows, const int32_t* __restrict__ src, const int32_t* __restrict__ dst) {
     const int l16 = threadIdx.x & 15;
     // the slot pairs first, then every row's codes and step
     long s8[R], s4[R];
 #pragma unroll
     for (int k = 0; k < R; ++k) {
-        const long row = min((long)blockIdx.x * (16 * R) + k * 16 + (threadIdx.x >> 4), n_rows - 1);
-        const long tok = (row >> 1) / nkv;
+        const int row = min((int)blockIdx.x * (16 * R) + k * 16 + (int)(threadIdx.x >> 4), n_rows - 1);
+        const int tok = div_n(row >> 1, nkv);
         s8[k] = src[tok];
         s4[k] = dst[tok];
     }
@@ -166,18 +166,18 @@ __global__ __launch_bounds__(256) void kvq4_requantize_q8_kernel(
     float step[R];
 #pragma unroll
     for (int k = 0; k < R; ++k) {
-        const long row = min((long)blockIdx.x * (16 * R) + k * 16 + (threadIdx.x >> 4), n_rows - 1);
-        const long tr = row >> 1;
-        const long tok = tr / nkv;
+        const int row = min((int)blockIdx.x * (16 * R) + k * 16 + (int)(threadIdx.x >> 4), n_rows - 1);
+        const int tr = row >> 1;
+        const int tok = div_n(tr, nkv);
         // an invalid source reads slot 0 (in bounds) and is not stored
         const long sv = (s8[k] >= 0 && s8[k] < n_slots8) ? s8[k] : 0;
-        const size_t r8 = (size_t)sv * nkv + (size_t)(tr - tok * nkv);
+        const size_t r8 = (size_t)sv * nkv.n + (size_t)(tr - tok * nkv.n);
         c[k] = *reinterpret_cast<const uint2*>(((row & 1) ? vc8 : kc8) + r8 * kHD + 8 * l16);
         step[k] = ((row & 1) ? vs8 : ks8)[r8];
     }
 #pragma unroll
     for (int k = 0; k < R; ++k) {
-        const long row = (long)blockIdx.x * (16 * R) + k * 16 + (threadIdx.x >> 4);
+        const int row = (int)blockIdx.x * (16 * R) + k * 16 + (int)(threadIdx.x >> 4);
         float x[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = sbyte_f(e < 4 ? c[k].x : c[k].y, e & 3) * step[k];
@@ -186,9 +186,9 @@ __global__ __launch_bounds__(256) void kvq4_requantize_q8_kernel(
         quantize_group8x8(x, packed, s16, z16);
         const uint32_t other = (uint32_t)dpp_i<kDppRowRor8>((int)packed);     // lane l16 ^ 8
         if (row >= n_rows || s8[k] < 0 || s8[k] >= n_slots8 || s4[k] < 0 || s4[k] >= n_slots4) continue;
-        const long tr = row >> 1;
-        const long tok = tr / nkv;
-        store_q4_row(kc4, vc4, ks4, kz4, vs4, vz4, (int)(row & 1), (size_t)s4[k] * nkv + (size_t)(tr - tok * nkv),
+        const int tr = row >> 1;
+        const int tok = div_n(tr, nkv);
+        store_q4_row(kc4, vc4, ks4, kz4, vs4, vz4, (int)(row & 1), (size_t)s4[k] * nkv.n + (size_t)(tr - tok * nkv.n),
                      l16, packed, other, s16, z16);
     }
 }
@@ -214,7 +214,7 @@ extern "C" int kvq4_quantize_append(uint8_t* k_cache, uint8_t* v_cache, uint16_t
     hipStream_t s = static_cast<hipStream_t>(stream);
 #define KVQ4_LAUNCH(DT)                                                                                     \
     hipLaunchKernelGGL(kvq4_quantize_append_kernel<DT>, grid, block, 0, s, k_cache, v_cache, k_scale, k_zero, \
-                       v_scale, v_zero, n_slots, nkv, k_new, v_new, (int)n_rows, slots)
+                       v_scale, v_zero, n_slots, make_divn(nkv), k_new, v_new, (int)n_rows, slots)
     if (dtype == KVQ8_F32) KVQ4_LAUNCH(KVQ8_F32);
     else if (dtype == KVQ8_BF16) KVQ4_LAUNCH(KVQ8_BF16);
     else KVQ4_LAUNCH(KVQ8_F16);
@@ -237,15 +237,16 @@ extern "C" int kvq4_requantize_q8(uint8_t* k_cache4, uint8_t* v_cache4, uint16_t
     if (!aligned16(k_cache4) || !aligned16(v_cache4) || !aligned16(k_cache8) || !aligned16(v_cache8))
         return KVQ8_EINVAL;
     const long n_rows = (long)n_tokens * nkv * 2;
+    if (n_rows > 0x7FFFFFFFL - 64) return KVQ8_ESHAPE;       // rows are indexed with 32-bit integers
     const long n_slots4 = (long)n_blocks4 * kv_bs, n_slots8 = (long)n_blocks8 * kv_bs;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (n_rows >= 65536)
         hipLaunchKernelGGL(kvq4_requantize_q8_kernel<4>, dim3((unsigned)((n_rows + 63) / 64)), dim3(256), 0, s,
                            k_cache4, v_cache4, k_scale4, k_zero4, v_scale4, v_zero4, n_slots4, k_cache8, v_cache8,
-                           k_scale8, v_scale8, n_slots8, nkv, n_rows, src_slots, dst_slots);
+                           k_scale8, v_scale8, n_slots8, make_divn(nkv), (int)n_rows, src_slots, dst_slots);
     else
         hipLaunchKernelGGL(kvq4_requantize_q8_kernel<1>, dim3((unsigned)((n_rows + 15) / 16)), dim3(256), 0, s,
                            k_cache4, v_cache4, k_scale4, k_zero4, v_scale4, v_zero4, n_slots4, k_cache8, v_cache8,
-                           k_scale8, v_scale8, n_slots8, nkv, n_rows, src_slots, dst_slots);
+                           k_scale8, v_scale8, n_slots8, make_divn(nkv), (int)n_rows, src_slots, dst_slots);
     return launch_status();
 }

@@ -20,7 +20,7 @@ constexpr int kRowsPerBlock = 32 * kRowsPerGroup;
 template <int DT>
 __global__ __launch_bounds__(256) void kvq8_quantize_append_kernel(
     int8_t* __restrict__ kc, int8_t* __restrict__ vc, float* __restrict__ ks, float* __restrict__ vs,
-    long n_slots, int nkv, const void* __restrict__ k_new, const void* __restrict__ v_new,
+    long n_slots, DivN nkv, const void* __restrict__ k_new, const void* __restrict__ v_new,
     int n_rows, const int32_t* __restrict__ slots) {
     const int l8 = threadIdx.x & 7;
     float x[kRowsPerGroup][16];
@@ -32,10 +32,10 @@ __global__ __launch_bounds__(256) void kvq8_quantize_append_kernel(
         const int row = (int)blockIdx.x * kRowsPerBlock + k * 32 + (threadIdx.x >> 3);
         const int rc = min(row, n_rows - 1);
         const int tr = rc >> 1;                    // token * nkv + kv-head
-        const int tok = tr / nkv;
+        const int tok = div_n(tr, nkv);
         load_new16<DT>((rc & 1) ? v_new : k_new, (size_t)tr * kHD + 16 * l8, x[k]);
         const long slot = slots[tok];
-        dst[k] = (row < n_rows && slot >= 0 && slot < n_slots) ? slot * nkv + (tr - tok * nkv) : -1;
+        dst[k] = (row < n_rows && slot >= 0 && slot < n_slots) ? slot * nkv.n + (tr - tok * nkv.n) : -1;
     }
 #pragma unroll
     for (int k = 0; k < kRowsPerGroup; ++k) {
@@ -89,15 +89,15 @@ extern "C" int kvq8_quantize_append(int8_t* k_cache, int8_t* v_cache, float* k_s
     switch (dtype) {
         case KVQ8_F32:
             hipLaunchKernelGGL(kvq8_quantize_append_kernel<KVQ8_F32>, grid, block, 0, s, k_cache, v_cache, k_scale,
-                               v_scale, n_slots, nkv, k_new, v_new, (int)n_rows, slots);
+                               v_scale, n_slots, make_divn(nkv), k_new, v_new, (int)n_rows, slots);
             break;
         case KVQ8_BF16:
             hipLaunchKernelGGL(kvq8_quantize_append_kernel<KVQ8_BF16>, grid, block, 0, s, k_cache, v_cache, k_scale,
-                               v_scale, n_slots, nkv, k_new, v_new, (int)n_rows, slots);
+                               v_scale, n_slots, make_divn(nkv), k_new, v_new, (int)n_rows, slots);
             break;
         default:
             hipLaunchKernelGGL(kvq8_quantize_append_kernel<KVQ8_F16>, grid, block, 0, s, k_cache, v_cache, k_scale,
-                               v_scale, n_slots, nkv, k_new, v_new, (int)n_rows, slots);
+                               v_scale, n_slots, make_divn(nkv), k_new, v_new, (int)n_rows, slots);
             break;
     }
     return launch_status();

@@ -158,9 +158,10 @@ __device__ __forceinline__ void quantize_row32x4(const float (&x)[4], uint32_t& 
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         // roundf(x / d), the quotient computed only near a half-integer
+        // (|x / d| <= 127)
         const float q = x[e] * rd;
         float r = rintf(q);
-        if (near_half(q)) r = roundf(x[e] / d);
+        if (near_half_small(q, r)) r = roundf(x[e] / d);
         r = fminf(fmaxf(r, -127.0f), 127.0f);
         w |= ((uint32_t)(int)r & 0xFFu) << (8 * e);
     }
@@ -184,9 +185,10 @@ __device__ __forceinline__ void quantize_row8x16(const float (&x)[16], uint4& co
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
         // roundf(x / d), the quotient computed only near a half-integer
+        // (|x / d| <= 127)
         const float q = x[e] * rd;
         float r = rintf(q);
-        if (near_half(q)) r = roundf(x[e] / d);
+        if (near_half_small(q, r)) r = roundf(x[e] / d);
         r = fminf(fmaxf(r, -127.0f), 127.0f);
         w[e >> 2] |= ((uint32_t)(int)r & 0xFFu) << (8 * (e & 3));
     }

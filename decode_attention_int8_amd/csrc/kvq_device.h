@@ -121,6 +121,33 @@ __device__ __forceinline__ bool near_half(float q) {
     return !(fabsf(q - rintf(q)) <= 0.5f - (0x1p-12f + fabsf(q) * 0x1p-19f));
 }
 
+// The same test for |q| <= 128 (int8 and Q4_0 codes), where the margin is at
+// most 2^-11: `rq` is rintf(q).
+__device__ __forceinline__ bool near_half_small(float q, float rq) {
+    return !(fabsf(q - rq) <= 0.5f - 0x1p-11f);
+}
+
+// Division by the kv-head count without the integer-divide sequence: for
+// 0 <= t < 2^31 and n >= 1, m = ceil(2^(32+s) / n) with 2^s >= n gives
+// t / n = (t * m) >> (32 + s) exactly.  m exceeds 2^(32+s) / n by less than
+// one, so t * m / 2^(32+s) exceeds t / n by less than t / 2^(32+s) <
+// 2^(-1-s) < 1 / n, which keeps it below the next integer.  Built on the host.
+struct DivN {
+    uint64_t m;
+    int shift;
+    int n;
+};
+
+inline DivN make_divn(int n) {
+    int s = 0;
+    while ((1LL << s) < n) ++s;
+    return DivN{((1ULL << (32 + s)) + (uint64_t)n - 1) / (uint64_t)n, 32 + s, n};
+}
+
+__device__ __forceinline__ int div_n(int t, const DivN& d) {
+    return (int)(((uint64_t)(uint32_t)t * d.m) >> d.shift);
+}
+
 // IEEE binary16 bits (low 16 bits of v) widened to float (exact)
 __device__ __forceinline__ float half_bits_f(uint32_t v) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)v);

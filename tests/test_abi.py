@@ -207,3 +207,7 @@ def test_write_row_limit():
                                     big, _fake(), None) == ESHAPE
     assert lib.kvq4_quantize_append(_fake(), _fake(), _fake(), _fake(), _fake(), _fake(), 64, 16, 8, 128,
                                     _fake(), _fake(), K.BF16, big, _fake(), None) == ESHAPE
+    assert lib.kvq4_0_quantize_append(_fake(), _fake(), _fake(), _fake(), 64, 16, 8, 128, _fake(), _fake(), K.BF16,
+                                      big, _fake(), None) == ESHAPE
+    assert lib.kvq4_requantize_q8(_fake(), _fake(), _fake(), _fake(), _fake(), _fake(), 64, _fake(), _fake(),
+                                  _fake(), _fake(), 64, 16, 8, 128, big, _fake(), _fake(), None) == ESHAPE

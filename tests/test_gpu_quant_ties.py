@@ -159,3 +159,35 @@ def test_q4_write_ties():
     p.append(K, x, y, r.permutation(nb * bs)[:n].astype(np.int32))
     torch.cuda.synchronize()
     p.assert_same()
+
+
+@pytest.mark.parametrize("nkv", [1, 3, 5, 6, 12])
+def test_write_paths_head_counts(nkv):
+    """Every write path (int8, Q4_0, int4, int8 -> int4 re-quantization) with
+    head counts that are not powers of two: the row index is divided by the
+    head count with a multiply and a shift."""
+    import torch
+    import decode_attention_int8_amd as K
+    from oracle import kvq4 as O4
+    r = W.rng(604, nkv)
+    n, bs = 203, 16
+    nb = (2 * n) // bs + 2
+    x = W.normal_f32(r, (n, nkv, 128))
+    y = W.student_t3_f32(r, (n, nkv, 128), 0.5)
+    slots = r.permutation(nb * bs)[:n].astype(np.int32)
+    slots[5] = -1
+    c8 = Q8Cache(nb, bs, nkv)
+    c8.append(x, y, slots)
+    c40 = Q40Cache(nb, bs, nkv)
+    c40.append(x, y, slots)
+    p4 = Q4Pool(nb, bs, nkv)
+    p4.append(K, x, y, slots)
+    # re-quantize the int8 rows of some tokens into other int4 slots
+    src = slots[:100].copy()
+    dst = r.permutation(nb * bs)[:100].astype(np.int32)
+    O4.requantize_q8_to_q4((c8.kp, c8.ks, c8.vp, c8.vs), p4.oracle_pools(), src, dst)
+    K.kvq4_requantize_q8(p4.g, (c8.gk, c8.gv, c8.gks, c8.gvs), dev(src), dev(dst))
+    torch.cuda.synchronize()
+    c8.assert_device_matches_host()
+    c40.assert_device_matches_host()
+    p4.assert_same()
