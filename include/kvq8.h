@@ -88,7 +88,10 @@ const char* kvq8_version(void);
  * 1); step d = amax / 127 (IEEE float32 division); code = roundf(x / d)
  * (IEEE division, ties away from zero) clamped to [-127, 127].  Codes go to
  * the cache at slots[i], the step to scale[slots[i]][kh].  All arithmetic is
- * float32; results are bit-exact across runs.
+ * float32; results are bit-exact across runs.  (The codes are those of the
+ * division; the kernel rounds x times a reciprocal of d and divides only
+ * where that product is near a half-integer, the one place the two can
+ * round apart.  The int4 and Q4_0 write paths do the same.)
  *
  *   k_cache, v_cache  (device) int8 [n_blocks][kv_bs][nkv][hd], written
  *   k_scale, v_scale  (device) float [n_blocks][kv_bs][nkv], written
