@@ -2,7 +2,9 @@
 launch configuration (the one the benchmark times).
 
   unit      1 / 1 heads, L = 256, N(0, 1)                     (test_gpu_kvq8)
-  qwen2b    28 layers x 16 / 8 heads, L = 8192, batch 1        layers 0 and 27
+  qwen2b    28 layers x 16 / 8 heads, L = 8192, batch 1        layers 0 and 27, separate
+                                                               calls and the fused step
+                                                               (eager and graph replays)
   qwen8b    36 layers x 32 / 8 heads, batch 32, L in [1K, 32K],
             K/V 0.5 * Student-t(3)                             layer 0, all 32 sequences
   append64k 65536 bf16 tokens (1% outliers x20) x 8 heads, then
@@ -72,6 +74,65 @@ def test_qwen2b_8k_layer(K, layer):
     assert _same(host(gks), hks) and _same(host(gvs), hvs)
     ref = O8.decode_attention_q8(host(q), hk, hks, hv, hvs, bt, [L], bs, SM)
     assert_attn_close(host(out), ref, f"qwen2b layer {layer}")
+
+
+@pytest.mark.parametrize("layer", [0, 27])
+def test_qwen2b_8k_fused_step_and_graph_replays(K, layer):
+    """The benchmark's step as it runs: the layer's cache holds all L tokens,
+    the slot of position L-1 holds a stale row, and one fused call writes the
+    newest token there and attends over the L tokens.  Eagerly first, checked
+    against the oracle (cache bytes and outputs); then captured in a graph and
+    replayed three times, with the stale row re-written eagerly and the stream
+    synchronized between replays, every replay equal to the eager call bit for
+    bit."""
+    import torch
+    cfg = W.QWEN2B_8K
+    L, nq, nkv, bs = cfg["L"], cfg["nq"], cfg["nkv"], cfg["kv_bs"]
+    bt, nb = W.paged_block_tables(W.rng(2, layer, 3), [L], bs)
+    k = W.torch_normal((L, nkv, 128), "cuda", (2, layer, 0))
+    v = W.torch_normal((L, nkv, 128), "cuda", (2, layer, 1))
+    q = W.torch_normal((1, nq, 128), "cuda", (2, layer, 2))
+    stale = W.torch_normal((1, nkv, 128), "cuda", (2, layer, 9)) * 3.0
+    slots = W.slots_for_positions(bt, [0] * L, np.arange(L), bs)
+    gk, gv, gks, gvs = _q8_pools(torch, nb, bs, nkv)
+    K.kvq8_quantize_append(gk, gv, gks, gvs, k, v, dev(slots))
+    last = dev(slots[L - 1:])
+    k_new, v_new = k[L - 1:L].clone(), v[L - 1:L].clone()
+    btd, ld = dev(bt), dev(np.array([L], np.int32))
+    ws = K.alloc_workspace(K.kvq8_decode_workspace_size(1, nq, nkv, L), "cuda")
+
+    def step(out):
+        K.kvq8_append_decode_attn(out, q, k_new, v_new, gk, gv, gks, gvs, btd, ld, L, SM, 0, ws)
+
+    K.kvq8_quantize_append(gk, gv, gks, gvs, stale, stale, last)
+    out_eager = torch.empty((1, nq, 128), dtype=torch.float32, device="cuda")
+    step(out_eager)
+    torch.cuda.synchronize()
+    hk, hv, hks, hvs = _host_pools(nb, bs, nkv)
+    O8.quantize_append(hk, hv, hks, hvs, host(k), host(v), slots)
+    assert _same(host(gk), hk) and _same(host(gv), hv)
+    assert _same(host(gks), hks) and _same(host(gvs), hvs)
+    ref = O8.decode_attention_q8(host(q), hk, hks, hv, hvs, bt, [L], bs, SM)
+    assert_attn_close(host(out_eager), ref, f"qwen2b fused step layer {layer}")
+
+    out = torch.empty_like(out_eager)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(out)
+    for rep in range(3):
+        K.kvq8_quantize_append(gk, gv, gks, gvs, stale, stale, last)      # eager work between replays
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out), host(out_eager)), f"replay {rep}"
+        assert _same(host(gk), hk) and _same(host(gks), hks), f"replay {rep} cache"
 
 
 def test_qwen8b_batch32_layer0(K):
