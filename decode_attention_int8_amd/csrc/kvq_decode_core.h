@@ -201,13 +201,15 @@ __device__ __forceinline__ void quantize_row8x16(const float (&x)[16], uint4& co
 // owns output dimension d for a contiguous share of the chunks; the parts
 // meet in LDS.  Chunks are read in batches of kMergeBatch with every load of a
 // batch in flight (so up to PARTS * kMergeBatch chunks cost one memory round
-// trip); the loads do not wait for the context lengths (chunks past them are
-// masked afterwards), and batches are combined with a running maximum.
+// trip), and batches are combined with a running maximum.  With LIVE (one
+// int8 region, several sequences of different lengths) a part reads only the
+// chunks below its sequence's length, after loading that length; otherwise the
+// loads do not wait for the lengths and chunks past them are masked afterwards.
 constexpr int kMergeBatch = 16;
 constexpr int kMergeThreads = 2 * kHD;          // PARTS = 2
 constexpr int kMergeThreadsWide = 8 * kHD;      // PARTS = 8, for more than 32 chunks
 
-template <int PARTS>
+template <int PARTS, bool LIVE = false>
 __global__ __launch_bounds__(PARTS * kHD) void kvq_merge_kernel(float* __restrict__ out, DecodeArgs a) {
     __shared__ float other[PARTS][kHD + 2];
     const int bh = blockIdx.x;
@@ -218,13 +220,14 @@ __global__ __launch_bounds__(PARTS * kHD) void kvq_merge_kernel(float* __restric
     const int nct = n_chunks_total(a);
     const int share = (nct + PARTS - 1) / PARTS;
     const int cbeg = part * share;
-    const int cend = min(nct, cbeg + share);
+    int cend = min(nct, cbeg + share);
     const int base8 = a.r4.max_chunks;
     const float* mm = a.ws_m + (size_t)bh * nct;
     const float* ss = a.ws_s + (size_t)bh * nct;
     const float* aa = a.ws_acc + (size_t)bh * nct * kHD + d;
     const int n4 = (effective_len(a.r4, b, a.log2_bs) + chunk_len - 1) / chunk_len;
     const int n8 = (effective_len(a.r8, b, a.log2_bs) + chunk_len - 1) / chunk_len;
+    if constexpr (LIVE) cend = min(cend, n8);      // one int8 region: chunks [0, n8) are live
     float M = -INFINITY, S = 0.0f, acc = 0.0f;
     for (int c0 = cbeg; c0 < cend; c0 += kMergeBatch) {
         float mv[kMergeBatch], sv[kMergeBatch], av[kMergeBatch];
@@ -289,10 +292,19 @@ __global__ __launch_bounds__(PARTS * kHD) void kvq_merge_kernel(float* __restric
 
 // Enqueue the merge of a decode's chunk partials into `out`.
 inline void launch_merge(const DecodeArgs& a, float* out, hipStream_t s) {
-    if (n_chunks_total(a) > 2 * kMergeBatch)
-        hipLaunchKernelGGL(kvq_merge_kernel<8>, dim3(a.batch * a.nq), dim3(kMergeThreadsWide), 0, s, out, a);
-    else
-        hipLaunchKernelGGL(kvq_merge_kernel<2>, dim3(a.batch * a.nq), dim3(kMergeThreads), 0, s, out, a);
+    const bool live = a.batch > 1 && a.r4.max_chunks == 0;
+    const dim3 grid(a.batch * a.nq);
+    if (n_chunks_total(a) > 2 * kMergeBatch) {
+        if (live)
+            hipLaunchKernelGGL((kvq_merge_kernel<8, true>), grid, dim3(kMergeThreadsWide), 0, s, out, a);
+        else
+            hipLaunchKernelGGL((kvq_merge_kernel<8, false>), grid, dim3(kMergeThreadsWide), 0, s, out, a);
+    } else {
+        if (live)
+            hipLaunchKernelGGL((kvq_merge_kernel<2, true>), grid, dim3(kMergeThreads), 0, s, out, a);
+        else
+            hipLaunchKernelGGL((kvq_merge_kernel<2, false>), grid, dim3(kMergeThreads), 0, s, out, a);
+    }
 }
 
 // ----------------------------------------------------------------------------
