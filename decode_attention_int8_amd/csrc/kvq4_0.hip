@@ -445,15 +445,16 @@ __global__ __launch_bounds__(kWGThreads, 2) void kvq4_0_decode_kernel(DecodeArgs
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int G = a.nq / a.nkv;
 
-    // work decode: the nkv workgroups of one (sequence, chunk) share an XCD
+    // work decode: the nkv workgroups of one (sequence, chunk) share an XCD,
+    // pairs laid out at an odd stride
     const int nct = a.r8.max_chunks;
     const int wg = blockIdx.x;
     const int rest = wg >> 3;
     const int kh = rest % a.nkv;
     const int p = (rest / a.nkv) * 8 + (wg & 7);
-    const int b = p / nct;
-    const int c = p - b * nct;
-    if (b >= a.batch) return;
+    const int b = p / pair_stride(nct);
+    const int c = p - b * pair_stride(nct);
+    if (b >= a.batch || c >= nct) return;
     const int chunk_len = a.tiles_per_wave * kChunkUnit;
     const int c0 = c * chunk_len;
     const int32_t* btb = a.r8.bt + (size_t)b * a.r8.max_blocks;
@@ -613,7 +614,7 @@ extern "C" int kvq4_0_decode_attn(float* out, const float* q, int batch, int nq,
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int nct = n_chunks_total(a);
     if (nct > 0) {
-        const long pairs = (long)a.batch * nct;
+        const long pairs = (long)a.batch * pair_stride(nct);
         const long n_wg = (long)a.nkv * ((pairs + 7) / 8) * 8;
         if (n_wg > 0x7FFFFFFFL) return KVQ8_ESHAPE;
         if (a.log2_bs < 4)

@@ -67,6 +67,15 @@ __device__ __host__ __forceinline__ int n_chunks_total(const DecodeArgs& a) {
     return a.r4.max_chunks + a.r8.max_chunks;
 }
 
+// Workgroups are dealt to the 8 XCDs round-robin, and the grid is laid out so
+// that pair p = (sequence, chunk) of every kv-head sits on XCD p % 8, at
+// p = sequence * stride + chunk.  With several sequences of different lengths
+// the low chunks are live for all of them and the high ones only for the
+// long ones; an even stride (a chunk count that is a multiple of 8) would put
+// chunk c of every sequence on XCD c % 8 and load the low XCDs with most of
+// the work.  An odd stride walks every chunk index over all 8 XCDs.
+__device__ __host__ __forceinline__ int pair_stride(int n_chunks) { return n_chunks | 1; }
+
 __device__ __forceinline__ int effective_len(const Region& r, int b, int log2_bs) {
     if (r.max_chunks == 0) return 0;
     long L = r.lens[b];

@@ -16,15 +16,16 @@ __global__ __launch_bounds__(kWGThreads, 2) void kvq_decode_mfma_kernel(DecodeAr
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int G = a.nq / a.nkv;
 
-    // work decode: the nkv workgroups of one (sequence, chunk) share an XCD
+    // work decode: the nkv workgroups of one (sequence, chunk) share an XCD,
+    // pairs laid out at an odd stride
     const int nct = a.r8.max_chunks;
     const int wg = blockIdx.x;
     const int rest = wg >> 3;
     const int kh = rest % a.nkv;
     const int p = (rest / a.nkv) * 8 + (wg & 7);
-    const int b = p / nct;
-    const int c = p - b * nct;
-    if (b >= a.batch) return;
+    const int b = p / pair_stride(nct);
+    const int c = p - b * pair_stride(nct);
+    if (b >= a.batch || c >= nct) return;
     const int chunk_len = a.tiles_per_wave * kChunkUnit;
     const int c0 = c * chunk_len;
     const int32_t* btb = a.r8.bt + (size_t)b * a.r8.max_blocks;
