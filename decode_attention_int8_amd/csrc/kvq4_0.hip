@@ -560,10 +560,9 @@ extern "C" int kvq4_0_quantize_append(uint8_t* k_cache, uint8_t* v_cache, float*
 
 extern "C" int kvq4_0_decode_chunk_tokens(int batch, int nkv, int max_ctx_len) {
     if (batch < 0 || nkv < 1 || max_ctx_len < 0) return 0;
-    // two workgroups per CU: at least 512 of them; few (sequence, head) units
-    // are long enough to take 8 tiles per wave, many balance better with 4
+    // two workgroups per CU: at least 512 of them, up to 2048 tokens each
     const long units = (long)batch * nkv;
-    return default_tiles_per_wave(units, max_ctx_len, units <= 16 ? 8 : 4, 512) * kChunkUnit;
+    return default_tiles_per_wave(units, max_ctx_len, 8, 512) * kChunkUnit;
 }
 
 static int resolve_chunk40(int batch, int nkv, int max_ctx_len, int chunk) {

@@ -61,8 +61,9 @@ using namespace kvq;
 
 extern "C" int kvq8_decode_chunk_tokens(int batch, int nkv, int max_ctx_len) {
     if (batch < 0 || nkv < 1 || max_ctx_len < 0) return 0;
-    // batches of varying lengths balance better with shorter work items
-    return default_tiles_per_wave((long)batch * nkv, max_ctx_len, batch <= 2 ? 8 : 4) * kChunkUnit;
+    // up to 2048 tokens per workgroup (longer chunks fill fewer workgroups
+    // and leave a longer tail; at most 8 tiles per wave)
+    return default_tiles_per_wave((long)batch * nkv, max_ctx_len, 8) * kChunkUnit;
 }
 
 static int resolve_chunk8(int batch, int nkv, int max_ctx_len, int chunk) {
