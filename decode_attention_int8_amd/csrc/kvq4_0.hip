@@ -452,8 +452,8 @@ __global__ __launch_bounds__(kWGThreads, 2) void kvq4_0_decode_kernel(DecodeArgs
     const int rest = wg >> 3;
     const int kh = rest % a.nkv;
     const int p = (rest / a.nkv) * 8 + (wg & 7);
-    const int b = p / pair_stride(nct);
-    const int c = p - b * pair_stride(nct);
+    const int b = p / pair_stride(nct, a.batch);
+    const int c = p - b * pair_stride(nct, a.batch);
     if (b >= a.batch || c >= nct) return;
     const int chunk_len = a.tiles_per_wave * kChunkUnit;
     const int c0 = c * chunk_len;
@@ -613,7 +613,7 @@ extern "C" int kvq4_0_decode_attn(float* out, const float* q, int batch, int nq,
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int nct = n_chunks_total(a);
     if (nct > 0) {
-        const long pairs = (long)a.batch * pair_stride(nct);
+        const long pairs = (long)a.batch * pair_stride(nct, a.batch);
         const long n_wg = (long)a.nkv * ((pairs + 7) / 8) * 8;
         if (n_wg > 0x7FFFFFFFL) return KVQ8_ESHAPE;
         if (a.log2_bs < 4)

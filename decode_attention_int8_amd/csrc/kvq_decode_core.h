@@ -73,8 +73,11 @@ __device__ __host__ __forceinline__ int n_chunks_total(const DecodeArgs& a) {
 // the low chunks are live for all of them and the high ones only for the
 // long ones; an even stride (a chunk count that is a multiple of 8) would put
 // chunk c of every sequence on XCD c % 8 and load the low XCDs with most of
-// the work.  An odd stride walks every chunk index over all 8 XCDs.
-__device__ __host__ __forceinline__ int pair_stride(int n_chunks) { return n_chunks | 1; }
+// the work.  An odd stride walks every chunk index over all 8 XCDs.  One
+// sequence needs no padding (its chunks already cycle over the XCDs).
+__device__ __host__ __forceinline__ int pair_stride(int n_chunks, int batch) {
+    return batch > 1 ? (n_chunks | 1) : n_chunks;
+}
 
 __device__ __forceinline__ int effective_len(const Region& r, int b, int log2_bs) {
     if (r.max_chunks == 0) return 0;

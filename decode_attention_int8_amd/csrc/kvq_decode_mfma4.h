@@ -331,8 +331,8 @@ __global__ __launch_bounds__(kWGThreads, 2) void kvq4_decode_mfma_kernel(DecodeA
     const int rest = wg >> 3;
     const int kh = rest % a.nkv;
     const int p = (rest / a.nkv) * 8 + (wg & 7);
-    const int b = p / pair_stride(nct);
-    const int c = p - b * pair_stride(nct);
+    const int b = p / pair_stride(nct, a.batch);
+    const int c = p - b * pair_stride(nct, a.batch);
     if (b >= a.batch || c >= nct) return;
     const bool int4_region = c < a.r4.max_chunks;
     const Region& reg = int4_region ? a.r4 : a.r8;
@@ -450,7 +450,7 @@ inline void launch_mfma4(const DecodeArgs& a, int n_wg, hipStream_t s) {
 inline int launch_decode(const DecodeArgs& a, float* out, hipStream_t s, int new_dtype = -1) {
     const int nct = n_chunks_total(a);
     if (nct > 0) {
-        const long pairs = (long)a.batch * pair_stride(nct);
+        const long pairs = (long)a.batch * pair_stride(nct, a.batch);
         const long n_wg = (long)a.nkv * ((pairs + 7) / 8) * 8;
         if (n_wg > 0x7FFFFFFFL) return KVQ8_ESHAPE;
         if (a.r4.max_chunks > 0)

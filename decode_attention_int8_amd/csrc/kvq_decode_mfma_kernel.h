@@ -23,8 +23,8 @@ __global__ __launch_bounds__(kWGThreads, 2) void kvq_decode_mfma_kernel(DecodeAr
     const int rest = wg >> 3;
     const int kh = rest % a.nkv;
     const int p = (rest / a.nkv) * 8 + (wg & 7);
-    const int b = p / pair_stride(nct);
-    const int c = p - b * pair_stride(nct);
+    const int b = p / pair_stride(nct, a.batch);
+    const int c = p - b * pair_stride(nct, a.batch);
     if (b >= a.batch || c >= nct) return;
     const int chunk_len = a.tiles_per_wave * kChunkUnit;
     const int c0 = c * chunk_len;
