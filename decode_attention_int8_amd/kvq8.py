@@ -106,6 +106,52 @@ def _ptr(t: torch.Tensor | None, dtype=None, name="tensor"):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _shape(t: torch.Tensor, shape, name: str):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {list(shape)}, got {list(t.shape)}")
+
+
+def _same_device(*ts):
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) > 1:
+        raise ValueError(f"all tensors must be on one device, got {sorted(map(str, devs))}")
+
+
+def _int8_pool(k_cache, v_cache, k_scale, v_scale):
+    """[n_blocks][kv_bs][nkv][128] codes and [n_blocks][kv_bs][nkv] steps, K and V alike."""
+    if k_cache.dim() != 4:
+        raise ValueError("k_cache must be [n_blocks][kv_bs][nkv][hd]")
+    _shape(v_cache, k_cache.shape, "v_cache")
+    _shape(k_scale, k_cache.shape[:3], "k_scale")
+    _shape(v_scale, k_cache.shape[:3], "v_scale")
+    return tuple(k_cache.shape)
+
+
+def _query(out, q, hd: int):
+    if q.dim() != 3 or q.shape[2] != hd:
+        raise ValueError(f"q must be [B][nq][{hd}]")
+    _shape(out, q.shape, "out")
+
+
+def _tables(block_tables, ctx_lens, B: int, suffix=""):
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError(f"block_tables{suffix} must be [B][max_blocks]")
+    _shape(ctx_lens, (B,), "ctx_lens" if not suffix else f"lens{suffix}")
+
+
+def _int4_pool(pool4):
+    """Packed codes [n_blocks][kv_bs][nkv][hd / 2], K and V alike, and four
+    [n_blocks][kv_bs][nkv][hd / 64] scale / zero tensors."""
+    k4, v4, k4s, k4z, v4s, v4z = pool4
+    if k4.dim() != 4:
+        raise ValueError("int4 codes must be [n_blocks][kv_bs][nkv][hd / 2]")
+    _shape(v4, k4.shape, "v4")
+    n, bs, nkv, half = k4.shape
+    for t, nm in ((k4s, "k4_scale"), (k4z, "k4_zero"), (v4s, "v4_scale"), (v4z, "v4_zero")):
+        _shape(t, (n, bs, nkv, 2 * half // 64), nm)
+    return n, bs, nkv, 2 * half
+
+
 def kvq8_status_string(status: int) -> str:
     return lib().kvq8_status_string(status).decode()
 
@@ -121,15 +167,14 @@ def kvq8_version() -> str:
 def kvq8_quantize_append(k_cache, v_cache, k_scale, v_scale, k_new, v_new, slots, stream=None):
     """Quantize k_new / v_new [n_tokens][nkv][128] (f32, bf16 or f16) into the
     int8 cache [n_blocks][kv_bs][nkv][128] at ``slots`` (int32)."""
-    n_blocks, kv_bs, nkv, hd = k_cache.shape
+    n_blocks, kv_bs, nkv, hd = _int8_pool(k_cache, v_cache, k_scale, v_scale)
     if k_new.dtype not in _DTYPES or v_new.dtype != k_new.dtype:
         raise ValueError("k_new / v_new must share one of float32, bfloat16, float16")
-    if tuple(k_new.shape[1:]) != (nkv, hd) or v_new.shape != k_new.shape:
+    if k_new.dim() != 3 or tuple(k_new.shape[1:]) != (nkv, hd) or v_new.shape != k_new.shape:
         raise ValueError("k_new / v_new must be [n_tokens][nkv][hd]")
-    if k_scale.shape != (n_blocks, kv_bs, nkv) or v_scale.shape != k_scale.shape or v_cache.shape != k_cache.shape:
-        raise ValueError("cache / scale shapes disagree")
     if slots.shape != (k_new.shape[0],):
         raise ValueError("slots must be [n_tokens]")
+    _same_device(k_cache, v_cache, k_scale, v_scale, k_new, v_new, slots)
     st = lib().kvq8_quantize_append(
         _ptr(k_cache, torch.int8, "k_cache"), _ptr(v_cache, torch.int8, "v_cache"),
         _ptr(k_scale, torch.float32, "k_scale"), _ptr(v_scale, torch.float32, "v_scale"),
@@ -155,12 +200,11 @@ def kvq8_decode_attn(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, c
                      sm_scale: float | None = None, chunk: int = 0, workspace=None, stream=None):
     """Decode attention: out [B][nq][128] (float32) from q [B][nq][128] over
     the int8 cache.  ``workspace`` (uint8) is allocated when not given."""
-    B, nq, hd = q.shape
-    n_blocks, kv_bs, nkv, _ = k_cache.shape
-    if out.shape != q.shape:
-        raise ValueError("out must match q")
-    if block_tables.dim() != 2 or block_tables.shape[0] != B or ctx_lens.shape != (B,):
-        raise ValueError("block_tables must be [B][max_blocks], ctx_lens [B]")
+    n_blocks, kv_bs, nkv, hd = _int8_pool(k_cache, v_cache, k_scale, v_scale)
+    _query(out, q, hd)
+    B, nq, _ = q.shape
+    _tables(block_tables, ctx_lens, B)
+    _same_device(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, ctx_lens, workspace)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(hd)
     need = kvq8_decode_workspace_size(B, nq, nkv, max_ctx_len, chunk)
@@ -183,16 +227,15 @@ def kvq8_append_decode_attn(out, q, k_new, v_new, k_cache, v_cache, k_scale, v_s
     """Write each sequence's newest token (k_new / v_new [B][nkv][128] at
     position ctx_lens[b] - 1) into the int8 cache, then decode attention over
     the whole context, in one pass."""
-    B, nq, hd = q.shape
-    n_blocks, kv_bs, nkv, _ = k_cache.shape
-    if out.shape != q.shape:
-        raise ValueError("out must match q")
+    n_blocks, kv_bs, nkv, hd = _int8_pool(k_cache, v_cache, k_scale, v_scale)
+    _query(out, q, hd)
+    B, nq, _ = q.shape
     if k_new.dtype not in _DTYPES or v_new.dtype != k_new.dtype:
         raise ValueError("k_new / v_new must share one of float32, bfloat16, float16")
     if tuple(k_new.shape) != (B, nkv, hd) or v_new.shape != k_new.shape:
         raise ValueError("k_new / v_new must be [B][nkv][hd]")
-    if block_tables.dim() != 2 or block_tables.shape[0] != B or ctx_lens.shape != (B,):
-        raise ValueError("block_tables must be [B][max_blocks], ctx_lens [B]")
+    _tables(block_tables, ctx_lens, B)
+    _same_device(out, q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_tables, ctx_lens, workspace)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(hd)
     need = kvq8_decode_workspace_size(B, nq, nkv, max_ctx_len, chunk)
@@ -211,8 +254,14 @@ def kvq8_append_decode_attn(out, q, k_new, v_new, k_cache, v_cache, k_scale, v_s
 
 
 def kvq8_quantize_q(qi, qsc, q, stream=None):
-    """Query codes qi [n][128] int8 and block scales qsc [n][4] float32."""
+    """Query codes qi [n][128] int8 and block scales qsc [n][4] float32 of
+    q [..., 128] (n = q.numel() / 128 vectors; any shapes of those sizes)."""
+    if q.dim() < 1 or q.shape[-1] != HD:
+        raise ValueError(f"q must be [..., {HD}]")
     n = q.numel() // HD
+    if qi.numel() != n * HD or qsc.numel() != n * (HD // 32):
+        raise ValueError(f"qi must hold {n} x {HD} codes and qsc {n} x {HD // 32} scales")
+    _same_device(qi, qsc, q)
     st = lib().kvq8_quantize_q(_ptr(qi, torch.int8, "qi"), _ptr(qsc, torch.float32, "qsc"),
                                _ptr(q, torch.float32, "q"), n, HD, _stream(stream))
     _check(st, "kvq8_quantize_q")
@@ -220,10 +269,15 @@ def kvq8_quantize_q(qi, qsc, q, stream=None):
 
 def kvq8_qk_partials(partials, q, k_cache, block_tables, ctx_lens, max_ctx_len: int, stream=None):
     """int32 block partials [B][nq][max_ctx_len][4]."""
-    B, nq, hd = q.shape
-    n_blocks, kv_bs, nkv, _ = k_cache.shape
-    if partials.shape != (B, nq, max_ctx_len, 4):
-        raise ValueError("partials must be [B][nq][max_ctx_len][4]")
+    if k_cache.dim() != 4:
+        raise ValueError("k_cache must be [n_blocks][kv_bs][nkv][hd]")
+    n_blocks, kv_bs, nkv, hd = k_cache.shape
+    if q.dim() != 3 or q.shape[2] != hd:
+        raise ValueError(f"q must be [B][nq][{hd}]")
+    B, nq, _ = q.shape
+    _shape(partials, (B, nq, max_ctx_len, 4), "partials")
+    _tables(block_tables, ctx_lens, B)
+    _same_device(partials, q, k_cache, block_tables, ctx_lens)
     st = lib().kvq8_qk_partials(
         _ptr(partials, torch.int32, "partials"), _ptr(q, torch.float32, "q"), B, nq,
         _ptr(k_cache, torch.int8, "k_cache"), n_blocks, kv_bs, nkv, hd,
@@ -239,15 +293,13 @@ def kvq8_qk_partials(partials, q, k_cache, block_tables, ctx_lens, max_ctx_len: 
 def kvq4_quantize_append(k_cache, v_cache, k_scale, k_zero, v_scale, v_zero, k_new, v_new, slots, stream=None):
     """Quantize into the int4 pool: packed codes [n_blocks][kv_bs][nkv][64]
     uint8, scale / zero [n_blocks][kv_bs][nkv][2] float16."""
-    n_blocks, kv_bs, nkv, half = k_cache.shape
-    hd = 2 * half
+    n_blocks, kv_bs, nkv, hd = _int4_pool((k_cache, v_cache, k_scale, k_zero, v_scale, v_zero))
     if k_new.dtype not in _DTYPES or v_new.dtype != k_new.dtype:
         raise ValueError("k_new / v_new must share one of float32, bfloat16, float16")
-    if tuple(k_new.shape[1:]) != (nkv, hd) or v_new.shape != k_new.shape or slots.shape != (k_new.shape[0],):
+    if k_new.dim() != 3 or tuple(k_new.shape[1:]) != (nkv, hd) or v_new.shape != k_new.shape or \
+            slots.shape != (k_new.shape[0],):
         raise ValueError("k_new / v_new must be [n_tokens][nkv][hd], slots [n_tokens]")
-    for t, nm in ((k_scale, "k_scale"), (k_zero, "k_zero"), (v_scale, "v_scale"), (v_zero, "v_zero")):
-        if t.shape != (n_blocks, kv_bs, nkv, hd // 64):
-            raise ValueError(f"{nm} must be [n_blocks][kv_bs][nkv][{hd // 64}]")
+    _same_device(k_cache, v_cache, k_scale, k_zero, v_scale, v_zero, k_new, v_new, slots)
     st = lib().kvq4_quantize_append(
         _ptr(k_cache, torch.uint8, "k_cache"), _ptr(v_cache, torch.uint8, "v_cache"),
         _ptr(k_scale, torch.float16, "k_scale"), _ptr(k_zero, torch.float16, "k_zero"),
@@ -263,13 +315,13 @@ def kvq4_requantize_q8(pool4, pool8, src_slots, dst_slots, stream=None):
     src_slots[i] to int4 slot dst_slots[i] (int32 device tensors)."""
     k4, v4, k4s, k4z, v4s, v4z = pool4
     k8, v8, k8s, v8s = pool8
-    n4, kv_bs, nkv, half = k4.shape
-    hd = 2 * half
-    n8 = k8.shape[0]
-    if k8.shape[1:] != (kv_bs, nkv, hd) or v8.shape != k8.shape or v4.shape != k4.shape:
-        raise ValueError("the int8 and int4 pools must share kv_bs and nkv")
+    n4, kv_bs, nkv, hd = _int4_pool(pool4)
+    n8 = _int8_pool(k8, v8, k8s, v8s)[0]
+    if tuple(k8.shape[1:]) != (kv_bs, nkv, hd):
+        raise ValueError("the int8 and int4 pools must share kv_bs, nkv and hd")
     if src_slots.shape != dst_slots.shape or src_slots.dim() != 1:
         raise ValueError("src_slots and dst_slots must be [n_tokens]")
+    _same_device(*pool4, *pool8, src_slots, dst_slots)
     st = lib().kvq4_requantize_q8(
         _ptr(k4, torch.uint8, "k4"), _ptr(v4, torch.uint8, "v4"), _ptr(k4s, torch.float16, "k4_scale"),
         _ptr(k4z, torch.float16, "k4_zero"), _ptr(v4s, torch.float16, "v4_scale"),
@@ -292,13 +344,17 @@ def kvq4_decode_attn(out, q, pool4, block_tables4, lens4, max_len4: int, pool8, 
                      max_len8: int, sm_scale: float | None = None, chunk: int = 0, workspace=None, stream=None):
     """Decode attention over an int4 pool (k, v, k_scale, k_zero, v_scale,
     v_zero) plus an int8 recent-window pool (k, v, k_scale, v_scale)."""
-    B, nq, hd = q.shape
     k4, v4, k4s, k4z, v4s, v4z = pool4
     k8, v8, k8s, v8s = pool8
-    n4, kv_bs, nkv, _ = k4.shape
-    n8 = k8.shape[0]
-    if k8.shape[1:] != (kv_bs, nkv, hd):
-        raise ValueError("int8 pool must share kv_bs and nkv with the int4 pool")
+    n4, kv_bs, nkv, hd = _int4_pool(pool4)
+    n8 = _int8_pool(k8, v8, k8s, v8s)[0]
+    if tuple(k8.shape[1:]) != (kv_bs, nkv, hd):
+        raise ValueError("int8 pool must share kv_bs, nkv and hd with the int4 pool")
+    _query(out, q, hd)
+    B, nq, _ = q.shape
+    _tables(block_tables4, lens4, B, "4")
+    _tables(block_tables8, lens8, B, "8")
+    _same_device(out, q, *pool4, *pool8, block_tables4, lens4, block_tables8, lens8, workspace)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(hd)
     need = kvq4_decode_workspace_size(B, nq, nkv, max_len4, max_len8, chunk)
@@ -323,19 +379,29 @@ def kvq4_decode_attn(out, q, pool4, block_tables4, lens4, max_len4: int, pool8, 
 # Q4_0 mode
 # ----------------------------------------------------------------------------
 
+def _q40_pool(k_cache, v_cache, k_step, v_step):
+    """Packed codes [n_blocks][kv_bs][nkv][hd / 2], K and V alike, and steps
+    [n_blocks][kv_bs][nkv][hd / 32]."""
+    if k_cache.dim() != 4:
+        raise ValueError("k_cache must be [n_blocks][kv_bs][nkv][hd / 2]")
+    _shape(v_cache, k_cache.shape, "v_cache")
+    n, bs, nkv, half = k_cache.shape
+    _shape(k_step, (n, bs, nkv, 2 * half // 32), "k_step")
+    _shape(v_step, (n, bs, nkv, 2 * half // 32), "v_step")
+    return n, bs, nkv, 2 * half
+
+
 def kvq4_0_quantize_append(k_cache, v_cache, k_step, v_step, k_new, v_new, slots, stream=None):
     """Quantize k_new / v_new [n_tokens][nkv][128] (f32, bf16 or f16) into the
     Q4_0 pool: packed codes [n_blocks][kv_bs][nkv][64] uint8, steps
     [n_blocks][kv_bs][nkv][4] float32, at ``slots`` (int32)."""
-    n_blocks, kv_bs, nkv, half = k_cache.shape
-    hd = 2 * half
+    n_blocks, kv_bs, nkv, hd = _q40_pool(k_cache, v_cache, k_step, v_step)
     if k_new.dtype not in _DTYPES or v_new.dtype != k_new.dtype:
         raise ValueError("k_new / v_new must share one of float32, bfloat16, float16")
-    if tuple(k_new.shape[1:]) != (nkv, hd) or v_new.shape != k_new.shape or slots.shape != (k_new.shape[0],):
+    if k_new.dim() != 3 or tuple(k_new.shape[1:]) != (nkv, hd) or v_new.shape != k_new.shape or \
+            slots.shape != (k_new.shape[0],):
         raise ValueError("k_new / v_new must be [n_tokens][nkv][hd], slots [n_tokens]")
-    if v_cache.shape != k_cache.shape or k_step.shape != (n_blocks, kv_bs, nkv, hd // 32) or \
-            v_step.shape != k_step.shape:
-        raise ValueError(f"steps must be [n_blocks][kv_bs][nkv][{hd // 32}] and the caches alike")
+    _same_device(k_cache, v_cache, k_step, v_step, k_new, v_new, slots)
     st = lib().kvq4_0_quantize_append(
         _ptr(k_cache, torch.uint8, "k_cache"), _ptr(v_cache, torch.uint8, "v_cache"),
         _ptr(k_step, torch.float32, "k_step"), _ptr(v_step, torch.float32, "v_step"),
@@ -356,12 +422,11 @@ def kvq4_0_decode_attn(out, q, k_cache, v_cache, k_step, v_step, block_tables, c
                        sm_scale: float | None = None, chunk: int = 0, workspace=None, stream=None):
     """Decode attention: out [B][nq][128] (float32) from q [B][nq][128] over
     the Q4_0 cache.  ``workspace`` (uint8) is allocated when not given."""
-    B, nq, hd = q.shape
-    n_blocks, kv_bs, nkv, _ = k_cache.shape
-    if out.shape != q.shape:
-        raise ValueError("out must match q")
-    if block_tables.dim() != 2 or block_tables.shape[0] != B or ctx_lens.shape != (B,):
-        raise ValueError("block_tables must be [B][max_blocks], ctx_lens [B]")
+    n_blocks, kv_bs, nkv, hd = _q40_pool(k_cache, v_cache, k_step, v_step)
+    _query(out, q, hd)
+    B, nq, _ = q.shape
+    _tables(block_tables, ctx_lens, B)
+    _same_device(out, q, k_cache, v_cache, k_step, v_step, block_tables, ctx_lens, workspace)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(hd)
     need = kvq4_0_decode_workspace_size(B, nq, nkv, max_ctx_len, chunk)

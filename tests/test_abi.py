@@ -115,6 +115,48 @@ def test_binding_requires_gpu_tensors():
         K.kvq8_quantize_append(x, x, s, s, kn, kn, torch.zeros(3, dtype=torch.int32))
 
 
+def test_binding_checks_every_buffer_shape():
+    """The C entry points see one set of sizes (taken from the key cache);
+    every other buffer is checked against them in the binding, before any
+    pointer is taken, so a short buffer never reaches a kernel."""
+    torch = pytest.importorskip("torch")
+    z = lambda *s, dt=torch.float32: torch.zeros(s, dtype=dt)  # noqa: E731
+    i8, u8, f16, i32 = torch.int8, torch.uint8, torch.float16, torch.int32
+    nb, bs, nkv, B, nq = 4, 16, 2, 3, 4
+    k8, s8 = z(nb, bs, nkv, 128, dt=i8), z(nb, bs, nkv)
+    q, bt, ln = z(B, nq, 128), z(B, 2, dt=i32), z(B, dt=i32)
+
+    def raises(fn, *a, match, **kw):
+        with pytest.raises(ValueError, match=match):
+            fn(*a, **kw)
+
+    raises(K.kvq8_decode_attn, q, q, k8, k8[:2], s8, s8, bt, ln, 32, match="v_cache")
+    raises(K.kvq8_decode_attn, q, q, k8, k8, s8, s8[:, :8], bt, ln, 32, match="v_scale")
+    raises(K.kvq8_decode_attn, z(B, nq, 64), z(B, nq, 64), k8, k8, s8, s8, bt, ln, 32, match="q must")
+    raises(K.kvq8_decode_attn, q[:, :2], q, k8, k8, s8, s8, bt, ln, 32, match="out")
+    raises(K.kvq8_decode_attn, q, q, k8, k8, s8, s8, bt[:2], ln, 32, match="block_tables")
+    raises(K.kvq8_decode_attn, q, q, k8, k8, s8, s8, bt, ln[:2], 32, match="ctx_lens")
+    kn = z(B, nkv, 128)
+    raises(K.kvq8_append_decode_attn, q, q, kn, kn, k8, k8, z(nb, bs, 1), s8, bt, ln, 32, match="k_scale")
+    raises(K.kvq8_append_decode_attn, q, q, kn[:2], kn[:2], k8, k8, s8, s8, bt, ln, 32, match="k_new")
+    raises(K.kvq8_quantize_append, k8, k8, s8, s8, z(5, nkv, 128), z(5, nkv, 128), z(4, dt=i32), match="slots")
+    raises(K.kvq8_quantize_q, z(10, 128, dt=i8), z(10, 3), z(10, 128), match="qsc")
+    raises(K.kvq8_qk_partials, z(B, nq, 32, 4, dt=i32), q, k8, bt, ln[:1], 32, match="ctx_lens")
+    raises(K.kvq8_qk_partials, z(B, nq, 31, 4, dt=i32), q, k8, bt, ln, 32, match="partials")
+
+    c4, g4 = z(nb, bs, nkv, 64, dt=u8), z(nb, bs, nkv, 2, dt=f16)
+    pool4, pool8 = (c4, c4, g4, g4, g4, g4), (k8, k8, s8, s8)
+    raises(K.kvq4_decode_attn, q, q, (c4, c4, g4, g4, g4[:1], g4), bt, ln, 32, pool8, bt, ln, 16, match="v4_scale")
+    raises(K.kvq4_decode_attn, q, q, pool4, bt, ln, 32, (k8, k8, s8, s8[:1]), bt, ln, 16, match="v_scale")
+    raises(K.kvq4_decode_attn, q, q, pool4, bt, ln, 32, pool8, bt[:1], ln, 16, match="block_tables8")
+    raises(K.kvq4_decode_attn, q[:1], q, pool4, bt, ln, 32, pool8, bt, ln, 16, match="out")
+    raises(K.kvq4_requantize_q8, pool4, (k8[:, :8], k8[:, :8], s8[:, :8], s8[:, :8]), ln, ln, match="share")
+    raises(K.kvq4_quantize_append, c4, c4[:1], g4, g4, g4, g4, kn, kn, ln, match="v4")
+    s40 = z(nb, bs, nkv, 4)
+    raises(K.kvq4_0_decode_attn, q, q, c4, c4, s40, s40[..., :2], bt, ln, 32, match="v_step")
+    raises(K.kvq4_0_quantize_append, c4, c4, s40, s40, kn, kn, ln[:1], match="slots")
+
+
 def _decode4(**kw):
     a = dict(out=_fake(), q=_fake(), batch=2, nq=32, k4=_fake(), v4=_fake(), k4s=_fake(), k4z=_fake(), v4s=_fake(),
              v4z=_fake(), n4=64, bt4=_fake(), mb4=32, l4=_fake(), ml4=512, k8=_fake(), v8=_fake(), k8s=_fake(),
