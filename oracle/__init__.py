@@ -1,4 +1,4 @@
-"""CPU oracle for int8 / int4 KV-cache decode attention.
+"""CPU oracle for int8 / int4 / 2-bit KV-cache decode attention.
 
 TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
 execute anything in this package: only the test suite, the smoke check in
@@ -32,4 +32,4 @@ Sources (cited by these short names throughout):
 
 Parity status per function is listed in each module's header.
 """
-from . import kvq8, kvq4, kvq4_0  # noqa: F401
+from . import kvq8, kvq4, kvq4_0, kvq2  # noqa: F401
