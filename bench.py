@@ -362,6 +362,62 @@ def run_workloads(only=None):
                n_all * nkv * (264 + 144), us)
         del p4, p8
 
+    def q2_pool(nb, bs, nkv):
+        shp = (nb, bs, nkv)
+        return [torch.zeros(shp + (32,), dtype=torch.uint8, device="cuda"),
+                torch.zeros(shp + (32,), dtype=torch.uint8, device="cuda")] + \
+               [torch.zeros(shp + (2,), dtype=torch.float16, device="cuda") for _ in range(4)]
+
+    if want("q2_128k", "requant2_block"):
+        # three bands, 128K tokens: 114688 2-bit + 14336 int4 + 2048 int8, batch 4 x 32 / 4 heads
+        cfg = W.Q2_128K
+        B, nq, nkv, L, bs = cfg["batch"], cfg["nq"], cfg["nkv"], cfg["L"], cfg["kv_bs"]
+        n8 = cfg["window"]
+        n4 = cfg["edge4"] - n8
+        n2 = L - n4 - n8
+        bt2, nb2 = W.paged_block_tables(W.rng(9, 0, 1), [n2] * B, bs)
+        bt4, nb4 = W.paged_block_tables(W.rng(9, 0, 2), [n4] * B, bs)
+        bt8, nb8 = W.paged_block_tables(W.rng(9, 0, 3), [n8] * B, bs)
+        p2, p4, p8 = q2_pool(nb2, bs, nkv), q4_pool(nb4, bs, nkv), q8_pool(nb8, bs, nkv)
+        sig = W.rng(9, 0, 4).uniform(0.2, 5.0, size=(B, nkv, 2))
+        for b in range(B):
+            sk = torch.tensor(sig[b, :, 0], dtype=torch.float32, device="cuda")[None, :, None]
+            sv = torch.tensor(sig[b, :, 1], dtype=torch.float32, device="cuda")[None, :, None]
+            kk = W.torch_normal((L, nkv, 128), "cuda", (9, 0, b, 0)) * sk
+            vv = W.torch_normal((L, nkv, 128), "cuda", (9, 0, b, 1)) * sv
+            K.kvq2_quantize_append(*p2, kk[:n2], vv[:n2], dev(W.slots_for_positions(bt2, [b] * n2, np.arange(n2), bs)))
+            K.kvq4_quantize_append(*p4, kk[n2:n2 + n4], vv[n2:n2 + n4],
+                                   dev(W.slots_for_positions(bt4, [b] * n4, np.arange(n4), bs)))
+            K.kvq8_quantize_append(*p8, kk[n2 + n4:], vv[n2 + n4:],
+                                   dev(W.slots_for_positions(bt8, [b] * n8, np.arange(n8), bs)))
+            del kk, vv
+        qd = W.torch_normal((B, nq, 128), "cuda", (9, 0, 99))
+        out = torch.empty((B, nq, 128), device="cuda")
+        bt2d, l2 = dev(bt2), dev(np.full(B, n2, np.int32))
+        bt4d, l4 = dev(bt4), dev(np.full(B, n4, np.int32))
+        bt8d, l8 = dev(bt8), dev(np.full(B, n8, np.int32))
+        ch = K.kvq2_decode_chunk_tokens(B, nkv, n2, n4, n8)
+        ws = K.alloc_workspace(K.kvq2_decode_workspace_size(B, nq, nkv, n2, n4, n8), "cuda")
+        nbytes = B * nkv * (n2 * 80 + n4 * 144 + n8 * 264)
+        pools = [(p2, p4, p8)] + [tuple([t.clone() for t in pp] for pp in (p2, p4, p8))
+                                  for _ in range(mall_copies(nbytes) - 1)]
+        fn, iters = cycled(lambda pp: K.kvq2_decode_attn(out, qd, pp[0], bt2d, l2, n2, pp[1], bt4d, l4, n4, pp[2],
+                                                         bt8d, l8, n8, sm, 0, ws), pools, 20)
+        us = time_calls(torch, fn, iters)
+        report("q2_128k", f"banded decode, batch 4 x 32 / 4 heads, {n2} 2-bit + {n4} int4 + {n8} int8 tokens "
+               f"({len(pools)} copies of the cache cycled)", nbytes, us, chunk_tokens=ch)
+        del pools
+
+        # re-quantization of the int4 band's oldest 512-token time block of
+        # every sequence into the 2-bit pool (timing only, as for requant_block)
+        T = 512
+        src = dev(np.concatenate([W.slots_for_positions(bt4, [b] * T, np.arange(T), bs) for b in range(B)]))
+        dst = dev(np.concatenate([W.slots_for_positions(bt2, [b] * T, np.arange(T), bs) for b in range(B)]))
+        us = time_calls(torch, lambda: K.kvq2_requantize_q4(p2, p4, src, dst), 50, graph=True)
+        report("requant2_block", "int4 -> 2-bit re-quantization of one 512-token time block x 4 sequences x 4 kv "
+               "heads (graph replay)", B * T * nkv * (144 + 80), us)
+        del p2, p4, p8
+
     # Q4_0 mode (80 B per row: 160 B per (token, kv-head) for K and V)
     def q40_pool(nb, bs, nkv):
         shp = (nb, bs, nkv)

@@ -3,7 +3,7 @@
 // variant ([P4] Sec. 3.2-3.3).  The pipeline itself lives in
 // kvq_decode_core.h and is compiled once, here.
 #include "kvq_decode_core.h"
-#include "kvq_decode_mfma4.h"
+#include "kvq_decode_group.h"
 
 namespace kvq {
 
@@ -249,6 +249,100 @@ extern "C" int kvq4_decode_attn(float* out, const float* q, int batch, int nq, c
     a.v4z = v_zero4;
     a.r8 = Region{block_tables8, lens8, max_blocks_per_seq8, max_len8, n_blocks8, (max_len8 + ch - 1) / ch};
     a.r4 = Region{block_tables4, lens4, max_blocks_per_seq4, max_len4, n_blocks4, (max_len4 + ch - 1) / ch};
+    a.nq = nq;
+    a.nkv = nkv;
+    a.log2_bs = ilog2(kv_bs);
+    a.batch = batch;
+    a.tiles_per_wave = ch / kChunkUnit;
+    a.score_scale = sm_scale * kLog2e;
+    bind_workspace(a, workspace);
+    return launch_decode(a, out, static_cast<hipStream_t>(stream));
+}
+
+// ----------------------------------------------------------------------------
+// banded group cache: 2-bit, int4 and int8 bands ([P4] Sec. 3.3)
+// ----------------------------------------------------------------------------
+
+extern "C" int kvq2_decode_chunk_tokens(int batch, int nkv, int max_len2, int max_len4, int max_len8) {
+    if (batch < 0 || nkv < 1 || max_len2 < 0 || max_len4 < 0 || max_len8 < 0) return 0;
+    const long units = (long)batch * nkv;
+    return default_tiles_per_wave(units, (long)max_len2 + max_len4 + max_len8, units <= 16 ? 8 : 4, 512) *
+           kChunkUnit;
+}
+
+static int resolve_chunk2(int batch, int nkv, int max_len2, int max_len4, int max_len8, int chunk) {
+    if (chunk == 0) return kvq2_decode_chunk_tokens(batch, nkv, max_len2, max_len4, max_len8);
+    if (chunk < 0 || chunk % kChunkUnit != 0 || chunk > 64 * kChunkUnit) return -1;
+    return chunk;
+}
+
+extern "C" size_t kvq2_decode_workspace_size(int batch, int nq, int nkv, int max_len2, int max_len4, int max_len8,
+                                             int chunk) {
+    if (batch < 0 || nq < 1 || nkv < 1 || max_len2 < 0 || max_len4 < 0 || max_len8 < 0) return 0;
+    const int ch = resolve_chunk2(batch, nkv, max_len2, max_len4, max_len8, chunk);
+    if (ch <= 0) return 0;
+    return decode_workspace_bytes(batch, nq,
+                                  (max_len2 + ch - 1) / ch + (max_len4 + ch - 1) / ch + (max_len8 + ch - 1) / ch);
+}
+
+extern "C" int kvq2_decode_attn(float* out, const float* q, int batch, int nq, const uint8_t* k_cache2,
+                                const uint8_t* v_cache2, const uint16_t* k_scale2, const uint16_t* k_zero2,
+                                const uint16_t* v_scale2, const uint16_t* v_zero2, int n_blocks2,
+                                const int32_t* block_tables2, int max_blocks_per_seq2, const int32_t* lens2,
+                                int max_len2, const uint8_t* k_cache4, const uint8_t* v_cache4,
+                                const uint16_t* k_scale4, const uint16_t* k_zero4, const uint16_t* v_scale4,
+                                const uint16_t* v_zero4, int n_blocks4, const int32_t* block_tables4,
+                                int max_blocks_per_seq4, const int32_t* lens4, int max_len4, const int8_t* k_cache8,
+                                const int8_t* v_cache8, const float* k_scale8, const float* v_scale8, int n_blocks8,
+                                const int32_t* block_tables8, int max_blocks_per_seq8, const int32_t* lens8,
+                                int max_len8, int kv_bs, int nkv, int hd, float sm_scale, int chunk,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    if (!decode_shape_ok(batch, nq, nkv, hd, kv_bs)) return KVQ8_ESHAPE;
+    if (n_blocks2 < 1 || n_blocks4 < 1 || n_blocks8 < 1 || max_blocks_per_seq2 < 1 || max_blocks_per_seq4 < 1 ||
+        max_blocks_per_seq8 < 1)
+        return KVQ8_ESHAPE;
+    if (max_len2 < 0 || max_len4 < 0 || max_len8 < 0) return KVQ8_EINVAL;
+    const int ch = resolve_chunk2(batch, nkv, max_len2, max_len4, max_len8, chunk);
+    if (ch <= 0) return KVQ8_ESHAPE;
+    if (batch == 0) return KVQ8_OK;
+    if (!out || !q || !k_cache2 || !v_cache2 || !k_scale2 || !k_zero2 || !v_scale2 || !v_zero2 || !block_tables2 ||
+        !lens2 || !k_cache4 || !v_cache4 || !k_scale4 || !k_zero4 || !v_scale4 || !v_zero4 || !block_tables4 ||
+        !lens4 || !k_cache8 || !v_cache8 || !k_scale8 || !v_scale8 || !block_tables8 || !lens8)
+        return KVQ8_EINVAL;
+    if (!aligned16(q) || !aligned16(k_cache2) || !aligned16(v_cache2) || !aligned16(k_cache4) ||
+        !aligned16(v_cache4) || !aligned16(k_cache8) || !aligned16(v_cache8))
+        return KVQ8_EINVAL;
+    // both groups' binary16 scale (zero point) of a row are read as one word
+    if (((uintptr_t)k_scale2 | (uintptr_t)k_zero2 | (uintptr_t)v_scale2 | (uintptr_t)v_zero2 | (uintptr_t)k_scale4 |
+         (uintptr_t)k_zero4 | (uintptr_t)v_scale4 | (uintptr_t)v_zero4) & 3u)
+        return KVQ8_EINVAL;
+    if (!rows_fit_u32(n_blocks2, kv_bs, nkv) || !rows_fit_u32(n_blocks4, kv_bs, nkv) ||
+        !rows_fit_u32(n_blocks8, kv_bs, nkv))
+        return KVQ8_ESHAPE;
+    const size_t need = kvq2_decode_workspace_size(batch, nq, nkv, max_len2, max_len4, max_len8, chunk);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return KVQ8_EWORKSPACE;
+
+    BandArgs a = {};
+    a.q = q;
+    a.kc = k_cache8;
+    a.vc = v_cache8;
+    a.ks = k_scale8;
+    a.vs = v_scale8;
+    a.k4 = k_cache4;
+    a.v4 = v_cache4;
+    a.k4s = k_scale4;
+    a.k4z = k_zero4;
+    a.v4s = v_scale4;
+    a.v4z = v_zero4;
+    a.k2 = k_cache2;
+    a.v2 = v_cache2;
+    a.k2s = k_scale2;
+    a.k2z = k_zero2;
+    a.v2s = v_scale2;
+    a.v2z = v_zero2;
+    a.r8 = Region{block_tables8, lens8, max_blocks_per_seq8, max_len8, n_blocks8, (max_len8 + ch - 1) / ch};
+    a.r4 = Region{block_tables4, lens4, max_blocks_per_seq4, max_len4, n_blocks4, (max_len4 + ch - 1) / ch};
+    a.r2 = Region{block_tables2, lens2, max_blocks_per_seq2, max_len2, n_blocks2, (max_len2 + ch - 1) / ch};
     a.nq = nq;
     a.nkv = nkv;
     a.log2_bs = ilog2(kv_bs);

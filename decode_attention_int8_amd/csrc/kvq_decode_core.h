@@ -10,6 +10,8 @@
 // seg. 3).
 #pragma once
 
+#include <type_traits>
+
 #include "kvq8.h"
 #include "kvq_device.h"
 #include "kvq_host.h"
@@ -63,9 +65,29 @@ struct DecodeArgs {
     float score_scale;          // sm_scale * log2(e)
 };
 
+// The banded cache adds the 2-bit pool, in an argument block of its own so
+// that the int8, int4 and Q4_0 kernels keep theirs.  Chunk index space:
+// [0, r2) 2-bit, [r2, r2 + r4) int4, then int8.
+struct BandArgs : DecodeArgs {
+    const uint8_t* k2;          // [n_blocks2][bs][nkv][32]
+    const uint8_t* v2;
+    const uint16_t* k2s;        // [n_blocks2][bs][nkv][2] binary16
+    const uint16_t* k2z;
+    const uint16_t* v2s;
+    const uint16_t* v2z;
+    Region r2;
+};
+
 __device__ __host__ __forceinline__ int n_chunks_total(const DecodeArgs& a) {
     return a.r4.max_chunks + a.r8.max_chunks;
 }
+
+__device__ __host__ __forceinline__ int n_chunks_total(const BandArgs& a) {
+    return a.r2.max_chunks + a.r4.max_chunks + a.r8.max_chunks;
+}
+
+template <class Args>
+inline constexpr bool kBanded = std::is_same_v<Args, BandArgs>;
 
 // Workgroups are dealt to the 8 XCDs round-robin, and the grid is laid out so
 // that pair p = (sequence, chunk) of every kv-head sits on XCD p % 8, at
@@ -221,8 +243,9 @@ constexpr int kMergeBatch = 16;
 constexpr int kMergeThreads = 2 * kHD;          // PARTS = 2
 constexpr int kMergeThreadsWide = 8 * kHD;      // PARTS = 8, for more than 32 chunks
 
-template <int PARTS, bool LIVE = false>
-__global__ __launch_bounds__(PARTS * kHD) void kvq_merge_kernel(float* __restrict__ out, DecodeArgs a) {
+template <int PARTS, bool LIVE = false, class Args = DecodeArgs>
+__global__ __launch_bounds__(PARTS * kHD) void kvq_merge_kernel(float* __restrict__ out, Args a) {
+    constexpr bool HAS2 = kBanded<Args>;
     __shared__ float other[PARTS][kHD + 2];
     const int bh = blockIdx.x;
     const int b = bh / a.nq;
@@ -233,10 +256,13 @@ __global__ __launch_bounds__(PARTS * kHD) void kvq_merge_kernel(float* __restric
     const int share = (nct + PARTS - 1) / PARTS;
     const int cbeg = part * share;
     int cend = min(nct, cbeg + share);
-    const int base8 = a.r4.max_chunks;
+    int base4 = 0, n2 = 0;
+    if constexpr (HAS2) base4 = a.r2.max_chunks;
+    const int base8 = base4 + a.r4.max_chunks;
     const float* mm = a.ws_m + (size_t)bh * nct;
     const float* ss = a.ws_s + (size_t)bh * nct;
     const float* aa = a.ws_acc + (size_t)bh * nct * kHD + d;
+    if constexpr (HAS2) n2 = (effective_len(a.r2, b, a.log2_bs) + chunk_len - 1) / chunk_len;
     const int n4 = (effective_len(a.r4, b, a.log2_bs) + chunk_len - 1) / chunk_len;
     const int n8 = (effective_len(a.r8, b, a.log2_bs) + chunk_len - 1) / chunk_len;
     if constexpr (LIVE) cend = min(cend, n8);      // one int8 region: chunks [0, n8) are live
@@ -254,7 +280,11 @@ __global__ __launch_bounds__(PARTS * kHD) void kvq_merge_kernel(float* __restric
 #pragma unroll
         for (int k = 0; k < kMergeBatch; ++k) {
             const int c = c0 + k;
-            const bool live = c < cend && (c < n4 || (c >= base8 && c < base8 + n8));
+            bool live;
+            if constexpr (HAS2)
+                live = c < cend && (c < n2 || (c >= base4 && c < base4 + n4) || (c >= base8 && c < base8 + n8));
+            else
+                live = c < cend && (c < n4 || (c >= base8 && c < base8 + n8));
             mv[k] = live ? mv[k] : -INFINITY;
             sv[k] = live ? sv[k] : 0.0f;   // a chunk never written may hold anything
             av[k] = live ? av[k] : 0.0f;
@@ -303,6 +333,14 @@ __global__ __launch_bounds__(PARTS * kHD) void kvq_merge_kernel(float* __restric
 }
 
 // Enqueue the merge of a decode's chunk partials into `out`.
+inline void launch_merge(const BandArgs& a, float* out, hipStream_t s) {
+    const dim3 grid(a.batch * a.nq);
+    if (n_chunks_total(a) > 2 * kMergeBatch)
+        hipLaunchKernelGGL((kvq_merge_kernel<8, false, BandArgs>), grid, dim3(kMergeThreadsWide), 0, s, out, a);
+    else
+        hipLaunchKernelGGL((kvq_merge_kernel<2, false, BandArgs>), grid, dim3(kMergeThreads), 0, s, out, a);
+}
+
 inline void launch_merge(const DecodeArgs& a, float* out, hipStream_t s) {
     const bool live = a.batch > 1 && a.r4.max_chunks == 0;
     const dim3 grid(a.batch * a.nq);
@@ -354,7 +392,9 @@ inline size_t decode_workspace_bytes(int batch, int nq, int n_chunks_total) {
     return round_up(n * kHD * sizeof(float), 256) + 2 * round_up(n * sizeof(float), 256);
 }
 
-inline void bind_workspace(DecodeArgs& a, void* workspace) {
+// The partials' places in the workspace (every region set first).
+template <class Args>
+inline void bind_workspace(Args& a, void* workspace) {
     const size_t n = (size_t)a.batch * a.nq * n_chunks_total(a);
     char* ws = static_cast<char*>(workspace);
     a.ws_acc = reinterpret_cast<float*>(ws);

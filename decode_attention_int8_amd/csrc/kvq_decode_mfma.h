@@ -399,7 +399,8 @@ __device__ __forceinline__ void mtile_compute(const DecodeArgs& a, const MTile T
 
 // Fold the waves' states (in LDS: per wave M, S and acc of each head) and
 // write one partial per query head.
-__device__ __forceinline__ void mcombine_write(const DecodeArgs& a, const MSmem& sm, int G, int b, int kh, int c) {
+template <class Args>
+__device__ __forceinline__ void mcombine_write(const Args& a, const MSmem& sm, int G, int b, int kh, int c) {
     const int nct = n_chunks_total(a);
     for (int idx = threadIdx.x; idx < G * kHD; idx += kWGThreads) {
         const int h = idx / kHD;
@@ -426,7 +427,8 @@ __device__ __forceinline__ void mcombine_write(const DecodeArgs& a, const MSmem&
 }
 
 // Fold the wave states of the workgroup and write one partial per query head.
-__device__ __forceinline__ void mwrite_partial(const DecodeArgs& a, MSmem& sm, MState& st, int G, int b, int kh,
+template <class Args>
+__device__ __forceinline__ void mwrite_partial(const Args& a, MSmem& sm, MState& st, int G, int b, int kh,
                                                int c, int lane, int wave) {
     const int g = lane >> 4;
     const int m = lane & 15;

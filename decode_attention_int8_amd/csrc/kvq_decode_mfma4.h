@@ -60,6 +60,10 @@ __device__ __forceinline__ v4i_t unpack_q4(v2u_t w) {
     return v4i_t{(int)((w.x >> 4) & kNib), (int)(w.x & kNib), (int)((w.y >> 4) & kNib), (int)(w.y & kNib)};
 }
 
+// The query operand of the group tiles; EVEN_ODD orders each word's codes as
+// the int4 key unpacking does, otherwise they stay in natural order (2-bit
+// keys).
+template <bool EVEN_ODD = true>
 __device__ __forceinline__ MQuery4 load_q4_operand(const QSmem& sm, int G, int g, int m) {
     MQuery4 Q;
     const int H = m >> 1;
@@ -69,7 +73,10 @@ __device__ __forceinline__ MQuery4 load_q4_operand(const QSmem& sm, int G, int g
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const v4u_t c = *reinterpret_cast<const v4u_t*>(&sm.qc[Hc][16 * h + 4 * g]);
-        Q.op[h] = mine ? even_odd_order(c) : v4i_t{0, 0, 0, 0};
+        if constexpr (EVEN_ODD)
+            Q.op[h] = mine ? even_odd_order(c) : v4i_t{0, 0, 0, 0};
+        else
+            Q.op[h] = mine ? __builtin_bit_cast(v4i_t, c) : v4i_t{0, 0, 0, 0};
         const int blk = 2 * h + (m & 1);
         Q.sc[h] = live ? sm.qs[Hc][blk] : 0.0f;
         int r = 0;
@@ -312,155 +319,5 @@ __device__ __forceinline__ void mwave4_to_lds(MSmem4& sm, MState& st, int G, int
         }
     }
 }
-
-// One workgroup = (sequence, kv-head, chunk) of either pool: chunks
-// [0, r4.max_chunks) cover the int4 region, the rest the int8 window.  Two
-// workgroups per CU (the int8 walk issues values after P.V, as in the int8
-// kernel).
-template <bool BS8>
-__global__ __launch_bounds__(kWGThreads, 2) void kvq4_decode_mfma_kernel(DecodeArgs a) {
-    __shared__ MSmem4 sm;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int g = lane >> 4;
-    const int m = lane & 15;
-    const int G = a.nq / a.nkv;
-
-    const int nct = n_chunks_total(a);
-    const int wg = blockIdx.x;
-    const int rest = wg >> 3;
-    const int kh = rest % a.nkv;
-    const int p = (rest / a.nkv) * 8 + (wg & 7);
-    const int b = p / pair_stride(nct, a.batch);
-    const int c = p - b * pair_stride(nct, a.batch);
-    if (b >= a.batch || c >= nct) return;
-    const bool int4_region = c < a.r4.max_chunks;
-    const Region& reg = int4_region ? a.r4 : a.r8;
-    const int cr = int4_region ? c : c - a.r4.max_chunks;
-    const int chunk_len = a.tiles_per_wave * kChunkUnit;
-    const int c0 = cr * chunk_len;
-    const int32_t* btb = reg.bt + (size_t)b * reg.max_blocks;
-    const int first = c0 + wave * kTile;
-    const float4 qx = load_q4(a.q + ((size_t)b * a.nq + (size_t)kh * G) * kHD, G);
-    int raw = mtile_raw(reg, btb, first, a.log2_bs, lane);
-    const int L = effective_len(reg, b, a.log2_bs);
-    if (c0 >= L) return;                                       // uniform per workgroup
-    const int end = min(L, c0 + chunk_len);
-    const int n_tiles = first < end ? (end - first + kChunkUnit - 1) / kChunkUnit : 1;
-
-    if (int4_region) {
-        const LaneOff4 lo = lane_offsets4(a, lane);
-        MTile4 A, B;
-        // the table entries of the tile after next go out before a tile's
-        // loads, so the loop head waits for them without waiting for the tile
-        int raw_next = mtile_raw(reg, btb, first + kChunkUnit, a.log2_bs, lane);
-        mtile4_issue<BS8>(a, raw, first, kh, lane, lo, A);
-        raw = raw_next;
-        __asm__ volatile("" ::: "memory");
-        quantize_q4(qx, G, sm.q);
-        lds_barrier();
-        const MQuery4 Q = load_q4_operand(sm.q, G, g, m);
-        MState st;
-        st.M = -INFINITY;
-        st.S = 0.0f;
-        st.E = 100;
-#pragma unroll
-        for (int sl = 0; sl < 8; ++sl) st.acc[sl] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
-        // two tiles per trip, one exit test at the top (as in the int8 walk)
-        int base = first;
-        int k = 0;
-        for (; k + 2 < n_tiles; k += 2) {
-            raw_next = mtile_raw(reg, btb, base + 2 * kChunkUnit, a.log2_bs, lane);
-            mtile4_issue<BS8>(a, raw, base + kChunkUnit, kh, lane, lo, B);
-            raw = raw_next;
-            mtile4_compute(a, A, base, L, lane, wave, Q, st, sm);
-            base += kChunkUnit;
-            raw_next = mtile_raw(reg, btb, base + 2 * kChunkUnit, a.log2_bs, lane);
-            mtile4_issue<BS8>(a, raw, base + kChunkUnit, kh, lane, lo, A);
-            raw = raw_next;
-            mtile4_compute(a, B, base, L, lane, wave, Q, st, sm);
-            base += kChunkUnit;
-        }
-        if (k + 1 < n_tiles) {
-            mtile4_issue<BS8>(a, raw, base + kChunkUnit, kh, lane, lo, B);
-            mtile4_compute(a, A, base, L, lane, wave, Q, st, sm);
-            mtile4_compute(a, B, base + kChunkUnit, L, lane, wave, Q, st, sm);
-        } else {
-            mtile4_compute(a, A, base, L, lane, wave, Q, st, sm);
-        }
-        mwave4_to_lds(sm, st, G, lane, wave);
-        lds_barrier();
-        mcombine_write(a, sm, G, b, kh, c);
-    } else {
-        const LaneOff lo = lane_offsets(a, lane);
-        MTile A, B;
-        mtile_issue<BS8, kIssueKeys | kIssueSteps>(a, raw, first, kh, lane, lo, A);
-        raw = mtile_raw(reg, btb, first + kChunkUnit, a.log2_bs, lane);
-        mtile_issue<BS8, kIssueValues>(a, 0, first, kh, lane, lo, A);
-        __asm__ volatile("" ::: "memory");
-        quantize_q4(qx, G, sm.q);
-        lds_barrier();
-        const MQuery Q = load_q_operand(sm.q, G, g, m);
-        MState st;
-        st.M = -INFINITY;
-        st.S = 0.0f;
-        st.E = 100;
-#pragma unroll
-        for (int sl = 0; sl < 8; ++sl) st.acc[sl] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
-        int base = first;
-        int k = 0;
-        for (; k + 2 < n_tiles; k += 2) {
-            mtile_issue<BS8, kIssueKeys | kIssueSteps>(a, raw, base + kChunkUnit, kh, lane, lo, B);
-            raw = mtile_raw(reg, btb, base + 2 * kChunkUnit, a.log2_bs, lane);
-            mtile_compute(a, A, base, L, lane, wave, Q, st, sm, NoHook(), [&]() __attribute__((always_inline)) {
-                mtile_issue<BS8, kIssueValues>(a, 0, base + kChunkUnit, kh, lane, lo, B);
-            });
-            base += kChunkUnit;
-            mtile_issue<BS8, kIssueKeys | kIssueSteps>(a, raw, base + kChunkUnit, kh, lane, lo, A);
-            raw = mtile_raw(reg, btb, base + 2 * kChunkUnit, a.log2_bs, lane);
-            mtile_compute(a, B, base, L, lane, wave, Q, st, sm, NoHook(), [&]() __attribute__((always_inline)) {
-                mtile_issue<BS8, kIssueValues>(a, 0, base + kChunkUnit, kh, lane, lo, A);
-            });
-            base += kChunkUnit;
-        }
-        if (k + 1 < n_tiles) {
-            mtile_issue<BS8, kIssueKeys | kIssueSteps>(a, raw, base + kChunkUnit, kh, lane, lo, B);
-            mtile_compute(a, A, base, L, lane, wave, Q, st, sm, NoHook(), [&]() __attribute__((always_inline)) {
-                mtile_issue<BS8, kIssueValues>(a, 0, base + kChunkUnit, kh, lane, lo, B);
-            });
-            mtile_compute(a, B, base + kChunkUnit, L, lane, wave, Q, st, sm);
-        } else {
-            mtile_compute(a, A, base, L, lane, wave, Q, st, sm);
-        }
-        mwrite_partial(a, sm, st, G, b, kh, c, lane, wave);
-    }
-}
-
-inline void launch_mfma4(const DecodeArgs& a, int n_wg, hipStream_t s) {
-    const dim3 grid(n_wg), block(kWGThreads);
-    if (a.log2_bs < 4)
-        hipLaunchKernelGGL((kvq4_decode_mfma_kernel<true>), grid, block, 0, s, a);
-    else
-        hipLaunchKernelGGL((kvq4_decode_mfma_kernel<false>), grid, block, 0, s, a);
-}
-
-// Enqueue the chunk kernel (if there is any context) and the merge kernel.
-// new_dtype >= 0 fuses the write path of each sequence's last token.  The
-// int8 cache and the mixed int4 / int8 cache both run on the matrix cores.
-inline int launch_decode(const DecodeArgs& a, float* out, hipStream_t s, int new_dtype = -1) {
-    const int nct = n_chunks_total(a);
-    if (nct > 0) {
-        const long pairs = (long)a.batch * pair_stride(nct, a.batch);
-        const long n_wg = (long)a.nkv * ((pairs + 7) / 8) * 8;
-        if (n_wg > 0x7FFFFFFFL) return KVQ8_ESHAPE;
-        if (a.r4.max_chunks > 0)
-            launch_mfma4(a, (int)n_wg, s);
-        else
-            launch_mfma(a, (int)n_wg, new_dtype, s);
-    }
-    launch_merge(a, out, s);
-    return launch_status();
-}
-
 
 }  // namespace kvq

@@ -51,6 +51,17 @@ _SIGNATURES = {
                                   _p, _p, _p, _p, _p, _p, _c_int, _p, _c_int, _p, _c_int,
                                   _p, _p, _p, _p, _c_int, _p, _c_int, _p, _c_int,
                                   _c_int, _c_int, _c_int, _f, _c_int, _p, _c_size, _p]),
+    "kvq2_quantize_append": (_c_int, [_p, _p, _p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _p, _p, _c_int,
+                                      _c_int, _p, _p]),
+    "kvq2_requantize_q4": (_c_int, [_p, _p, _p, _p, _p, _p, _c_int, _p, _p, _p, _p, _p, _p, _c_int,
+                                    _c_int, _c_int, _c_int, _c_int, _p, _p, _p]),
+    "kvq2_decode_chunk_tokens": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int]),
+    "kvq2_decode_workspace_size": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
+    "kvq2_decode_attn": (_c_int, [_p, _p, _c_int, _c_int,
+                                  _p, _p, _p, _p, _p, _p, _c_int, _p, _c_int, _p, _c_int,
+                                  _p, _p, _p, _p, _p, _p, _c_int, _p, _c_int, _p, _c_int,
+                                  _p, _p, _p, _p, _c_int, _p, _c_int, _p, _c_int,
+                                  _c_int, _c_int, _c_int, _f, _c_int, _p, _c_size, _p]),
     "kvq4_0_quantize_append": (_c_int, [_p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _p, _p, _c_int, _c_int,
                                         _p, _p]),
     "kvq4_0_decode_chunk_tokens": (_c_int, [_c_int, _c_int, _c_int]),
@@ -137,6 +148,24 @@ def _tables(block_tables, ctx_lens, B: int, suffix=""):
     if block_tables.dim() != 2 or block_tables.shape[0] != B:
         raise ValueError(f"block_tables{suffix} must be [B][max_blocks]")
     _shape(ctx_lens, (B,), "ctx_lens" if not suffix else f"lens{suffix}")
+
+
+def _group_pool(pool, codes_per_byte: int, names):
+    """Packed codes [n_blocks][kv_bs][nkv][hd / codes_per_byte], K and V
+    alike, and four [n_blocks][kv_bs][nkv][hd / 64] scale / zero tensors."""
+    kc, vc, ks, kz, vs, vz = pool
+    if kc.dim() != 4:
+        raise ValueError(f"{names[0]} must be [n_blocks][kv_bs][nkv][hd / {codes_per_byte}]")
+    _shape(vc, kc.shape, names[1])
+    n, bs, nkv, row = kc.shape
+    hd = codes_per_byte * row
+    for t, nm in zip((ks, kz, vs, vz), names[2:]):
+        _shape(t, (n, bs, nkv, hd // 64), nm)
+    return n, bs, nkv, hd
+
+
+def _int2_pool(pool2):
+    return _group_pool(pool2, 4, ("k2", "v2", "k2_scale", "k2_zero", "v2_scale", "v2_zero"))
 
 
 def _int4_pool(pool4):
@@ -440,4 +469,100 @@ def kvq4_0_decode_attn(out, q, k_cache, v_cache, k_step, v_step, block_tables, c
         _ptr(ctx_lens, torch.int32, "ctx_lens"), max_ctx_len, float(sm_scale), chunk,
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
     _check(st, "kvq4_0_decode_attn")
+    return out
+
+
+# ----------------------------------------------------------------------------
+# 2-bit band of the group variant
+# ----------------------------------------------------------------------------
+
+def _pool_ptrs(pool, codes_dtype, prefix):
+    kc, vc, ks, kz, vs, vz = pool
+    return (_ptr(kc, codes_dtype, f"k{prefix}"), _ptr(vc, codes_dtype, f"v{prefix}"),
+            _ptr(ks, torch.float16, f"k{prefix}_scale"), _ptr(kz, torch.float16, f"k{prefix}_zero"),
+            _ptr(vs, torch.float16, f"v{prefix}_scale"), _ptr(vz, torch.float16, f"v{prefix}_zero"))
+
+
+def kvq2_quantize_append(k_cache, v_cache, k_scale, k_zero, v_scale, v_zero, k_new, v_new, slots, stream=None):
+    """Quantize into the 2-bit pool: packed codes [n_blocks][kv_bs][nkv][32]
+    uint8, scale / zero [n_blocks][kv_bs][nkv][2] float16."""
+    pool = (k_cache, v_cache, k_scale, k_zero, v_scale, v_zero)
+    n_blocks, kv_bs, nkv, hd = _int2_pool(pool)
+    if k_new.dtype not in _DTYPES or v_new.dtype != k_new.dtype:
+        raise ValueError("k_new / v_new must share one of float32, bfloat16, float16")
+    if k_new.dim() != 3 or tuple(k_new.shape[1:]) != (nkv, hd) or v_new.shape != k_new.shape or \
+            slots.shape != (k_new.shape[0],):
+        raise ValueError("k_new / v_new must be [n_tokens][nkv][hd], slots [n_tokens]")
+    _same_device(*pool, k_new, v_new, slots)
+    st = lib().kvq2_quantize_append(
+        *_pool_ptrs(pool, torch.uint8, "2"), n_blocks, kv_bs, nkv, hd, _ptr(k_new, name="k_new"),
+        _ptr(v_new, name="v_new"), _DTYPES[k_new.dtype], k_new.shape[0], _ptr(slots, torch.int32, "slots"),
+        _stream(stream))
+    _check(st, "kvq2_quantize_append")
+
+
+def kvq2_requantize_q4(pool2, pool4, src_slots, dst_slots, stream=None):
+    """Move tokens from the int4 pool (k, v, k_scale, k_zero, v_scale,
+    v_zero) into the 2-bit pool (same order): pair i takes int4 slot
+    src_slots[i] to 2-bit slot dst_slots[i] (int32 device tensors)."""
+    n2, kv_bs, nkv, hd = _int2_pool(pool2)
+    n4 = _int4_pool(pool4)[0]
+    if tuple(pool4[0].shape[1:3]) != (kv_bs, nkv) or 2 * pool4[0].shape[3] != hd:
+        raise ValueError("the int4 and 2-bit pools must share kv_bs, nkv and hd")
+    if src_slots.shape != dst_slots.shape or src_slots.dim() != 1:
+        raise ValueError("src_slots and dst_slots must be [n_tokens]")
+    _same_device(*pool2, *pool4, src_slots, dst_slots)
+    st = lib().kvq2_requantize_q4(
+        *_pool_ptrs(pool2, torch.uint8, "2"), n2, *_pool_ptrs(pool4, torch.uint8, "4"), n4, kv_bs, nkv, hd,
+        src_slots.shape[0], _ptr(src_slots, torch.int32, "src_slots"), _ptr(dst_slots, torch.int32, "dst_slots"),
+        _stream(stream))
+    _check(st, "kvq2_requantize_q4")
+
+
+def kvq2_decode_chunk_tokens(batch: int, nkv: int, max_len2: int, max_len4: int, max_len8: int) -> int:
+    return lib().kvq2_decode_chunk_tokens(batch, nkv, max_len2, max_len4, max_len8)
+
+
+def kvq2_decode_workspace_size(batch: int, nq: int, nkv: int, max_len2: int, max_len4: int, max_len8: int,
+                               chunk: int = 0) -> int:
+    return lib().kvq2_decode_workspace_size(batch, nq, nkv, max_len2, max_len4, max_len8, chunk)
+
+
+def kvq2_decode_attn(out, q, pool2, block_tables2, lens2, max_len2: int, pool4, block_tables4, lens4,
+                     max_len4: int, pool8, block_tables8, lens8, max_len8: int, sm_scale: float | None = None,
+                     chunk: int = 0, workspace=None, stream=None):
+    """Decode attention over a 2-bit band (pool2: k, v, k_scale, k_zero,
+    v_scale, v_zero), an int4 band (pool4, the same order) and an int8
+    window (pool8: k, v, k_scale, v_scale)."""
+    n2, kv_bs, nkv, hd = _int2_pool(pool2)
+    n4 = _int4_pool(pool4)[0]
+    k8, v8, k8s, v8s = pool8
+    n8 = _int8_pool(k8, v8, k8s, v8s)[0]
+    if tuple(pool4[0].shape[1:3]) != (kv_bs, nkv) or 2 * pool4[0].shape[3] != hd or \
+            tuple(k8.shape[1:]) != (kv_bs, nkv, hd):
+        raise ValueError("the three pools must share kv_bs, nkv and hd")
+    _query(out, q, hd)
+    B, nq, _ = q.shape
+    _tables(block_tables2, lens2, B, "2")
+    _tables(block_tables4, lens4, B, "4")
+    _tables(block_tables8, lens8, B, "8")
+    _same_device(out, q, *pool2, *pool4, *pool8, block_tables2, lens2, block_tables4, lens4, block_tables8, lens8,
+                 workspace)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(hd)
+    need = kvq2_decode_workspace_size(B, nq, nkv, max_len2, max_len4, max_len8, chunk)
+    if workspace is None:
+        workspace = alloc_workspace(need, q.device)
+    st = lib().kvq2_decode_attn(
+        _ptr(out, torch.float32, "out"), _ptr(q, torch.float32, "q"), B, nq,
+        *_pool_ptrs(pool2, torch.uint8, "2"), n2, _ptr(block_tables2, torch.int32, "block_tables2"),
+        block_tables2.shape[1], _ptr(lens2, torch.int32, "lens2"), max_len2,
+        *_pool_ptrs(pool4, torch.uint8, "4"), n4, _ptr(block_tables4, torch.int32, "block_tables4"),
+        block_tables4.shape[1], _ptr(lens4, torch.int32, "lens4"), max_len4,
+        _ptr(k8, torch.int8, "k8"), _ptr(v8, torch.int8, "v8"), _ptr(k8s, torch.float32, "k8_scale"),
+        _ptr(v8s, torch.float32, "v8_scale"), n8, _ptr(block_tables8, torch.int32, "block_tables8"),
+        block_tables8.shape[1], _ptr(lens8, torch.int32, "lens8"), max_len8,
+        kv_bs, nkv, hd, float(sm_scale), chunk, _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+        _stream(stream))
+    _check(st, "kvq2_decode_attn")
     return out

@@ -379,6 +379,110 @@ int kvq4_0_decode_attn(float* out, const float* q, int batch, int nq,
                        const int32_t* ctx_lens, int max_ctx_len, float sm_scale,
                        int chunk, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * 2-bit band of the group variant ([P4] Sec. 2.2 time-adaptive bits and
+ * Sec. 3.3 band schedule: the oldest tokens take 2 bits, the middle band
+ * int4, the recent window int8; the page's example edges are 2048 and 16384
+ * tokens from the newest).  The caller decides which tokens sit in which
+ * band through the three pools' block tables and lengths.
+ *
+ * Codes: the [P4] Sec. 3.2 group quantizer with two bits, on groups of 64
+ * values: scale = (max - min) / 3 in float32 (1.0 when max == min), floored
+ * at 1e-7 and rounded to binary16; with s the stored binary16 scale,
+ * zero = clamp(rint(-min / s), 0, 3) (stored as binary16, exact);
+ * code = clamp(rint(x / s + zero), 0, 3); rint rounds half to even; the
+ * value a code stands for is (code - zero) * s.
+ *
+ * 2-bit pool layout (this library's packing, four codes per byte):
+ *   packed codes  cache2[n_blocks2][kv_bs][nkv][32] uint8;
+ *                 key rows: 32-bit word 2g + h holds element
+ *                 64h + 16g + 4k + j at bits 8j + 2k (g, j, k = 0..3);
+ *                 value rows: 16-bit word m holds element
+ *                 64(s / 4) + 4m + s % 4 at bits 2s (s = 0..7, m = 0..15)
+ *   scale, zero   [n_blocks2][kv_bs][nkv][2] IEEE binary16 (as uint16 bits)
+ * 32 + 32 code bytes + 8 + 8 scale / zero bytes = 80 B per (token, kv-head)
+ * (int4: 144 B, int8: 264 B).
+ * ------------------------------------------------------------------------ */
+
+/*
+ * kvq2_quantize_append -- 2-bit write path: quantize n_tokens new rows of K
+ * and V (k_new, v_new [n_tokens][nkv][128], 16-byte aligned, dtype as in
+ * kvq8_quantize_append) into 2-bit slot slots[i] = block * kv_bs + offset.
+ * Arguments, skipped slots and errors as for kvq4_quantize_append.
+ */
+int kvq2_quantize_append(uint8_t* k_cache, uint8_t* v_cache,
+                         uint16_t* k_scale, uint16_t* k_zero, uint16_t* v_scale, uint16_t* v_zero,
+                         int n_blocks, int kv_bs, int nkv, int hd,
+                         const void* k_new, const void* v_new, int dtype, int n_tokens,
+                         const int32_t* slots, void* stream);
+
+/*
+ * kvq2_requantize_q4 -- move tokens from the int4 pool into the 2-bit pool
+ * as they leave the int4 band ([P4] Sec. 3.3 practical notes: the oldest
+ * time block drops to fewer bits, off the decode's critical path).
+ *
+ * Pair i reads int4 slot src_slots[i] of both the K and the V pool, takes
+ * the values (code - zero) * scale (exact in float32) and writes them to
+ * 2-bit slot dst_slots[i] exactly as kvq2_quantize_append would write those
+ * float32 values.  A pair with either slot outside its pool is skipped; the
+ * int4 pool is only read.
+ *
+ *   k_cache2 .. v_zero2  (device) the 2-bit pool, written; caches 16-byte
+ *                        aligned
+ *   k_cache4 .. v_zero4  (device) the int4 pool as in kvq4_quantize_append,
+ *                        read; caches 16-byte aligned
+ *   n_blocks2, n_blocks4 blocks in each pool (same kv_bs and nkv)
+ *   src_slots, dst_slots (device) int32 [n_tokens]
+ *
+ * Errors as for kvq4_requantize_q8.
+ */
+int kvq2_requantize_q4(uint8_t* k_cache2, uint8_t* v_cache2, uint16_t* k_scale2, uint16_t* k_zero2,
+                       uint16_t* v_scale2, uint16_t* v_zero2, int n_blocks2,
+                       const uint8_t* k_cache4, const uint8_t* v_cache4,
+                       const uint16_t* k_scale4, const uint16_t* k_zero4,
+                       const uint16_t* v_scale4, const uint16_t* v_zero4, int n_blocks4,
+                       int kv_bs, int nkv, int hd, int n_tokens,
+                       const int32_t* src_slots, const int32_t* dst_slots, void* stream);
+
+/* Default chunk and workspace size for kvq2_decode_attn (the kvq4 rules over
+ * the three bands' lengths together). */
+int kvq2_decode_chunk_tokens(int batch, int nkv, int max_len2, int max_len4, int max_len8);
+size_t kvq2_decode_workspace_size(int batch, int nq, int nkv, int max_len2, int max_len4, int max_len8,
+                                  int chunk);
+
+/*
+ * kvq2_decode_attn -- decode attention over a sequence split into three
+ * bands: lens2[b] tokens in the 2-bit pool (block_tables2), lens4[b] in the
+ * int4 pool (block_tables4) and lens8[b] in the int8 pool (block_tables8).
+ * Attention does not depend on token order, so the bands only set each
+ * token's precision.
+ *
+ * A 2-bit key row contributes qsc_b * s_g * (P_b - z_g * R_b) per query
+ * block as an int4 row does (P_b = sum qi * c, R_b = sum qi, int32), a
+ * value row weight * s_g * (c - z_g); int4 and int8 rows as in
+ * kvq4_decode_attn.  All three bands' chunks share one launch and one
+ * merge.  The pools share kv_bs and nkv; the eight binary16 arrays must be
+ * 4-byte aligned, each pool may hold at most 2^32 - 1 rows; other arguments,
+ * workspace and errors as in kvq4_decode_attn.
+ */
+int kvq2_decode_attn(float* out, const float* q, int batch, int nq,
+                     const uint8_t* k_cache2, const uint8_t* v_cache2,
+                     const uint16_t* k_scale2, const uint16_t* k_zero2,
+                     const uint16_t* v_scale2, const uint16_t* v_zero2,
+                     int n_blocks2, const int32_t* block_tables2, int max_blocks_per_seq2,
+                     const int32_t* lens2, int max_len2,
+                     const uint8_t* k_cache4, const uint8_t* v_cache4,
+                     const uint16_t* k_scale4, const uint16_t* k_zero4,
+                     const uint16_t* v_scale4, const uint16_t* v_zero4,
+                     int n_blocks4, const int32_t* block_tables4, int max_blocks_per_seq4,
+                     const int32_t* lens4, int max_len4,
+                     const int8_t* k_cache8, const int8_t* v_cache8,
+                     const float* k_scale8, const float* v_scale8,
+                     int n_blocks8, const int32_t* block_tables8, int max_blocks_per_seq8,
+                     const int32_t* lens8, int max_len8,
+                     int kv_bs, int nkv, int hd, float sm_scale,
+                     int chunk, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

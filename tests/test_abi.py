@@ -253,3 +253,80 @@ def test_write_row_limit():
                                       big, _fake(), None) == ESHAPE
     assert lib.kvq4_requantize_q8(_fake(), _fake(), _fake(), _fake(), _fake(), _fake(), 64, _fake(), _fake(),
                                   _fake(), _fake(), 64, 16, 8, 128, big, _fake(), _fake(), None) == ESHAPE
+
+
+def _decode2(**kw):
+    a = dict(out=_fake(), q=_fake(), batch=2, nq=32,
+             k2=_fake(), v2=_fake(), k2s=_fake(), k2z=_fake(), v2s=_fake(), v2z=_fake(), n2=64, bt2=_fake(),
+             mb2=64, l2=_fake(), ml2=1024,
+             k4=_fake(), v4=_fake(), k4s=_fake(), k4z=_fake(), v4s=_fake(), v4z=_fake(), n4=64, bt4=_fake(),
+             mb4=32, l4=_fake(), ml4=512,
+             k8=_fake(), v8=_fake(), k8s=_fake(), v8s=_fake(), n8=8, bt8=_fake(), mb8=4, l8=_fake(), ml8=64,
+             kv_bs=16, nkv=4, hd=128, sm=0.088, chunk=0, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return K.lib().kvq2_decode_attn(*a.values())
+
+
+def test_decode2_validation_and_sizing():
+    need = K.kvq2_decode_workspace_size(2, 32, 4, 1024, 512, 64, 0)
+    ch = K.kvq2_decode_chunk_tokens(2, 4, 1024, 512, 64)
+    assert ch == K.kvq4_decode_chunk_tokens(2, 4, 1024 + 512, 64)       # the same rule over all bands
+    n = 2 * 32 * (-(-1024 // ch) + -(-512 // ch) + -(-64 // ch))
+    assert need == -(-n * 512 // 256) * 256 + 2 * (-(-n * 4 // 256) * 256)
+    assert K.kvq2_decode_workspace_size(2, 32, 4, 1024, 512, 64, 300) == 0      # bad chunk
+    ws = dict(ws=_fake(), ws_bytes=need)
+    for name in ("k2s", "k2z", "v2s", "v2z", "k4s", "v4z"):
+        assert _decode2(**ws, **{name: _fake(4098)}) == EINVAL, name
+    for name in ("k2", "v2", "bt2", "l2"):
+        assert _decode2(**ws, **{name: None}) == EINVAL, name
+    assert _decode2(k2=_fake(4104), **ws) == EINVAL                      # codes 16-byte aligned
+    assert _decode2(hd=64, **ws) == ESHAPE
+    assert _decode2(nq=36, **ws) == ESHAPE
+    assert _decode2(n2=0, **ws) == ESHAPE
+    assert _decode2(mb2=0, **ws) == ESHAPE
+    assert _decode2(n2=1 << 30, **ws) == ESHAPE                          # more than 2^32 - 1 rows
+    assert _decode2(ml2=-1, **ws) == EINVAL
+    assert _decode2(ws=_fake(), ws_bytes=need - 1) == EWORKSPACE
+    assert _decode2(batch=0, **ws) == OK
+
+
+def test_write2_and_requant2_validation():
+    lib = K.lib()
+    w = [_fake()] * 6 + [8, 16, 4, 128, _fake(), _fake(), 0, 10, _fake(), None]
+    assert lib.kvq2_quantize_append(*w[:9], 64, *w[10:]) == ESHAPE
+    assert lib.kvq2_quantize_append(*w[:7], 12, *w[8:]) == ESHAPE        # kv_bs not a power of two
+    assert lib.kvq2_quantize_append(*w[:12], 3, *w[13:]) == EINVAL       # dtype
+    assert lib.kvq2_quantize_append(*w[:13], -1, *w[14:]) == EINVAL
+    assert lib.kvq2_quantize_append(*w[:13], 0, *w[14:]) == OK
+    assert lib.kvq2_quantize_append(*w[:10], _fake(4100), *w[11:]) == EINVAL
+    assert lib.kvq2_quantize_append(*w[:13], 1 << 28, *w[14:]) == ESHAPE  # 2^31 rows
+    r = [_fake()] * 6 + [8] + [_fake()] * 6 + [4, 16, 4, 128, 10, _fake(), _fake(), None]
+    assert lib.kvq2_requantize_q4(*r[:6], 0, *r[7:]) == ESHAPE
+    assert lib.kvq2_requantize_q4(*r[:13], 0, *r[14:]) == ESHAPE
+    assert lib.kvq2_requantize_q4(*r[:17], -1, *r[18:]) == EINVAL
+    assert lib.kvq2_requantize_q4(*r[:17], 0, *r[18:]) == OK
+    assert lib.kvq2_requantize_q4(*r[:17], 1 << 28, *r[18:]) == ESHAPE
+    assert lib.kvq2_requantize_q4(*r[:18], None, *r[19:]) == EINVAL
+
+
+def test_binding_checks_two_bit_pools():
+    torch = pytest.importorskip("torch")
+    z = lambda *s, dt=torch.float32: torch.zeros(s, dtype=dt)  # noqa: E731
+    u8, f16, i8, i32 = torch.uint8, torch.float16, torch.int8, torch.int32
+    nb, bs, nkv, B, nq = 4, 16, 2, 3, 4
+    c2, g = z(nb, bs, nkv, 32, dt=u8), z(nb, bs, nkv, 2, dt=f16)
+    c4 = z(nb, bs, nkv, 64, dt=u8)
+    p2, p4 = (c2, c2, g, g, g, g), (c4, c4, g, g, g, g)
+    p8 = (z(nb, bs, nkv, 128, dt=i8), z(nb, bs, nkv, 128, dt=i8), z(nb, bs, nkv), z(nb, bs, nkv))
+    q, bt, ln = z(B, nq, 128), z(B, 2, dt=i32), z(B, dt=i32)
+    with pytest.raises(ValueError, match="v2_zero"):
+        K.kvq2_decode_attn(q, q, (c2, c2, g, g, g, g[:1]), bt, ln, 32, p4, bt, ln, 32, p8, bt, ln, 32)
+    with pytest.raises(ValueError, match="share"):
+        K.kvq2_decode_attn(q, q, p2, bt, ln, 32, (c4[:, :8],) * 2 + (g[:, :8],) * 4, bt, ln, 32, p8, bt, ln, 32)
+    with pytest.raises(ValueError, match="lens2"):
+        K.kvq2_decode_attn(q, q, p2, bt, ln[:1], 32, p4, bt, ln, 32, p8, bt, ln, 32)
+    with pytest.raises(ValueError, match="share"):
+        K.kvq2_requantize_q4(p2, (c4[:, :8],) * 2 + (g[:, :8],) * 4, ln, ln)
+    kn = z(5, nkv, 128)
+    with pytest.raises(ValueError, match="slots"):
+        K.kvq2_quantize_append(*p2, kn, kn, ln)

@@ -116,7 +116,8 @@ def test_quantize_append_large_and_overwrite(K):
     c = Q40Cache(nb, bs, nkv)
     c.append(x, x[::-1].copy(), slots)
     b = W.normal_f32(r, (3, nkv, 128), 9.0)
-    c.append(b, b, slots[[5, 7, 5]])                # rewrite slots, one twice (last write wins)
+    c.append(b[:2], b[:2], slots[[5, 7]])           # rewrite two slots
+    c.append(b[2:], b[2:], slots[[5]])              # and one again: the later call wins
     K.kvq4_0_quantize_append(c.gk, c.gv, c.gks, c.gvs, dev(b[:0]), dev(b[:0]), dev(np.zeros(0, np.int32)))
     torch.cuda.synchronize()
     c.assert_device_matches_host()

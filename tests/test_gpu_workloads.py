@@ -11,6 +11,8 @@ launch configuration (the one the benchmark times).
             one GQA-4 decode over the 65536 tokens             everything
   q4_128k   int4 groups + int8 window, 32 / 4 heads, batch 4,
             L = 131072                                         sequences 0 and 3
+  q2_128k   the same shape in three bands: 2-bit up to 16384
+            tokens from the newest, int4 up to 2048, int8 window   sequences 0 and 3
   Q4_0      the qwen8b batch-32 layer and the 64K append + decode
             through the Q4_0 mode                              everything
 
@@ -22,6 +24,7 @@ import numpy as np
 import pytest
 
 import workloads as W
+from oracle import kvq2 as O2
 from oracle import kvq4 as O4
 from oracle import kvq4_0 as O40
 from oracle import kvq8 as O8
@@ -235,6 +238,70 @@ def test_q4_128k(K):
                                         bt4[b:b + 1], [n4], (p8[0], p8[2], p8[1], p8[3]), bt8[b:b + 1], [n8],
                                         bs, SM)
         assert_attn_close(got[b:b + 1], ref, f"q4_128k seq {b}")
+
+
+def test_q2_128k(K):
+    import torch
+    cfg = W.Q2_128K
+    B, nq, nkv, L, bs = cfg["batch"], cfg["nq"], cfg["nkv"], cfg["L"], cfg["kv_bs"]
+    n8 = cfg["window"]
+    n4 = cfg["edge4"] - n8
+    n2 = L - n4 - n8
+    assert (n2, n4, n8) == O2.band_lengths(L)
+    bt2, nb2 = W.paged_block_tables(W.rng(9, 0, 1), [n2] * B, bs)
+    bt4, nb4 = W.paged_block_tables(W.rng(9, 0, 2), [n4] * B, bs)
+    bt8, nb8 = W.paged_block_tables(W.rng(9, 0, 3), [n8] * B, bs)
+
+    def group_pool(nb, row, host_side):
+        shp = (nb, bs, nkv)
+        if host_side:
+            return [np.zeros(shp + (row,), np.uint8), np.zeros(shp + (row,), np.uint8)] + \
+                   [np.zeros(shp + (2,), np.float16) for _ in range(4)]
+        return [torch.zeros(shp + (row,), dtype=torch.uint8, device="cuda"),
+                torch.zeros(shp + (row,), dtype=torch.uint8, device="cuda")] + \
+               [torch.zeros(shp + (2,), dtype=torch.float16, device="cuda") for _ in range(4)]
+    g2, g4 = group_pool(nb2, 32, False), group_pool(nb4, 64, False)
+    g8 = _q8_pools(torch, nb8, bs, nkv)
+    sig = W.rng(9, 0, 4).uniform(0.2, 5.0, size=(B, nkv, 2))
+    checked = (0, 3)
+    host_cache = {}
+    for b in range(B):
+        sk = torch.tensor(sig[b, :, 0], dtype=torch.float32, device="cuda")[None, :, None]
+        sv = torch.tensor(sig[b, :, 1], dtype=torch.float32, device="cuda")[None, :, None]
+        k = W.torch_normal((L, nkv, 128), "cuda", (9, 0, b, 0)) * sk
+        v = W.torch_normal((L, nkv, 128), "cuda", (9, 0, b, 1)) * sv
+        s2 = W.slots_for_positions(bt2, [b] * n2, np.arange(n2), bs)
+        s4 = W.slots_for_positions(bt4, [b] * n4, np.arange(n4), bs)
+        s8 = W.slots_for_positions(bt8, [b] * n8, np.arange(n8), bs)
+        K.kvq2_quantize_append(*g2, k[:n2], v[:n2], dev(s2))
+        K.kvq4_quantize_append(*g4, k[n2:n2 + n4], v[n2:n2 + n4], dev(s4))
+        K.kvq8_quantize_append(*g8, k[n2 + n4:], v[n2 + n4:], dev(s8))
+        if b in checked:
+            host_cache[b] = (host(k), host(v), s2, s4, s8)
+        del k, v
+    q = W.torch_normal((B, nq, 128), "cuda", (9, 0, 99))
+    out = torch.empty((B, nq, 128), dtype=torch.float32, device="cuda")
+    K.kvq2_decode_attn(out, q, g2, dev(bt2), dev(np.full(B, n2, np.int32)), n2, g4, dev(bt4),
+                       dev(np.full(B, n4, np.int32)), n4, g8, dev(bt8), dev(np.full(B, n8, np.int32)), n8, SM)
+    torch.cuda.synchronize()
+    got = host(out)
+    gh2, gh4, gh8 = [host(x) for x in g2], [host(x) for x in g4], [host(x) for x in g8]
+    for b in checked:
+        k, v, s2, s4, s8 = host_cache[b]
+        p2, p4 = group_pool(nb2, 32, True), group_pool(nb4, 64, True)
+        O2.quantize_append_q2(p2[0], p2[1], p2[2], p2[3], p2[4], p2[5], k[:n2], v[:n2], s2)
+        O4.quantize_append_q4(p4[0], p4[1], p4[2], p4[3], p4[4], p4[5], k[n2:n2 + n4], v[n2:n2 + n4], s4)
+        p8 = _host_pools(nb8, bs, nkv)
+        O8.quantize_append(p8[0], p8[1], p8[2], p8[3], k[n2 + n4:], v[n2 + n4:], s8)
+        for gh, ph, bt, name in ((gh2, p2, bt2, "2-bit"), (gh4, p4, bt4, "int4"), (gh8, p8, bt8, "int8")):
+            rows = bt[b][bt[b] >= 0]
+            for x, y in zip(gh, ph):
+                assert _same(x[rows], y[rows]), f"{name} pool differs (seq {b})"
+        ref = O2.decode_attention_banded(
+            host(q)[b:b + 1], (p2[0], p2[2], p2[3], p2[1], p2[4], p2[5]), bt2[b:b + 1], [n2],
+            (p4[0], p4[2], p4[3], p4[1], p4[4], p4[5]), bt4[b:b + 1], [n4], (p8[0], p8[2], p8[1], p8[3]),
+            bt8[b:b + 1], [n8], bs, SM)
+        assert_attn_close(got[b:b + 1], ref, f"q2_128k seq {b}")
 
 
 def _q40_pools(torch, nb, bs, nkv):

@@ -175,6 +175,9 @@ QWEN8B_B32 = dict(layers=36, nq=32, nkv=8, batch=32, L_lo=1024, L_hi=32768, kv_b
 APPEND_64K = dict(n_tok=65536, nq=32, nkv=8, kv_bs=16)
 # int4 group variant: 32 / 4 heads, batch 4, 128K context, last 2048 tokens int8.
 Q4_128K = dict(nq=32, nkv=4, batch=4, L=131072, window=2048, kv_bs=16, group=64)
+# The same shape with the page's three-band schedule: the newest 2048 tokens
+# int8, those up to 16384 from the newest int4, all older ones 2-bit.
+Q2_128K = dict(nq=32, nkv=4, batch=4, L=131072, window=2048, edge4=16384, kv_bs=16, group=64)
 
 
 def unit_experiment(seed: int = 0, sigma: float = 1.0):
