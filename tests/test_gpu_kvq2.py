@@ -231,3 +231,22 @@ def test_aging_round_trip_decode(K):
     q = W.normal_f32(r, (1, g * nkv, 128))
     got, ref = _decode_and_check(K, q, bands, (np.array([n], np.int32), zero, zero), "aged")
     assert_attn_close(got, ref, "aged 2-bit decode")
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_banded_decode_random_shapes(K, case):
+    """Seeded random shapes: batch 1-6, kv heads 1-4, GQA 1-8, block sizes
+    8-128, band lengths 0-1500 each (whole sequences empty too), default or
+    explicit chunk sizes."""
+    r = W.rng(814, case)
+    B = int(r.integers(1, 7))
+    nkv = int(r.integers(1, 5))
+    g = int(r.integers(1, 9))
+    bs = int(2 ** r.integers(3, 8))
+    lens = [np.where(r.random(B) < 0.2, 0, r.integers(1, 1500, size=B)).astype(np.int32) for _ in range(3)]
+    chunk = int(r.choice([0, 256, 512, 1024]))
+    bands = _banded(K, r, lens[0], lens[1], lens[2], g * nkv, nkv, bs)
+    q = W.normal_f32(r, (B, g * nkv, 128), float(r.uniform(0.5, 3.0)))
+    what = f"case {case}: B={B} nkv={nkv} g={g} bs={bs} chunk={chunk} lens={[l.tolist() for l in lens]}"
+    got, ref = _decode_and_check(K, q, bands, tuple(lens), what, chunk=chunk)
+    assert_attn_close(got, ref, what)
