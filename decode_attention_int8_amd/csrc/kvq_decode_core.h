@@ -272,8 +272,13 @@ __global__ __launch_bounds__(PARTS * kHD) void kvq_merge_kernel(float* __restric
 #pragma unroll
         for (int k = 0; k < kMergeBatch; ++k) {
             const int cc = min(c0 + k, cend - 1);
-            mv[k] = mm[cc];
-            sv[k] = ss[cc];
+            // M and S are the same for every thread of the part; as scalar
+            // loads they ran out of scalar registers and were waited for in
+            // turn.  Vector loads of the same word go out with the acc loads.
+            int cv = cc;
+            __asm__("" : "+v"(cv));
+            mv[k] = mm[cv];
+            sv[k] = ss[cv];
             av[k] = aa[(size_t)cc * kHD];
         }
         float bm = -INFINITY;
