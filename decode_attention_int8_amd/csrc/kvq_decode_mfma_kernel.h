@@ -12,6 +12,24 @@ namespace kvq {
 template <int NEWDT, bool BS8>
 __global__ __launch_bounds__(kWGThreads, 2) void kvq_decode_mfma_kernel(DecodeArgs a) {
     __shared__ MSmem sm;
+    // The arguments the prologue needs, read in one batch: left to itself
+    // the compiler loads each at its first use, behind the previous wait, and
+    // at batch 1 (every workgroup its CU's first) those round trips add up.
+    {
+        const void* p0 = a.q;
+        const void* p1 = a.r8.bt;
+        const void* p2 = a.r8.lens;
+        const void* p3 = a.kc;
+        const void* p4 = a.ks;
+        __asm__ volatile("" ::"s"(p0), "s"(p1), "s"(p2), "s"(p3), "s"(p4), "s"(a.nq), "s"(a.nkv), "s"(a.batch),
+                         "s"(a.r8.max_chunks), "s"(a.tiles_per_wave), "s"(a.r8.max_blocks), "s"(a.r8.max_len),
+                         "s"(a.log2_bs), "s"(a.r8.n_blocks));
+        if constexpr (NEWDT >= 0) {
+            const void* p5 = a.k_new;
+            const void* p6 = a.v_new;
+            __asm__ volatile("" ::"s"(p5), "s"(p6));
+        }
+    }
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int G = a.nq / a.nkv;
