@@ -441,6 +441,18 @@ __device__ __forceinline__ void q40_write_partial(const DecodeArgs& a, QSmem40& 
 template <bool BS8>
 __global__ __launch_bounds__(kWGThreads, 2) void kvq4_0_decode_kernel(DecodeArgs a) {
     __shared__ QSmem40 sm;
+    // the arguments the prologue needs, read in one batch (as in the int8
+    // chunk kernel)
+    {
+        const void* p0 = a.q;
+        const void* p1 = a.r8.bt;
+        const void* p2 = a.r8.lens;
+        const void* p3 = a.k4;
+        const void* p4 = a.ks;
+        __asm__ volatile("" ::"s"(p0), "s"(p1), "s"(p2), "s"(p3), "s"(p4), "s"(a.nq), "s"(a.nkv), "s"(a.batch),
+                         "s"(a.r8.max_chunks), "s"(a.tiles_per_wave), "s"(a.r8.max_blocks), "s"(a.r8.max_len),
+                         "s"(a.log2_bs), "s"(a.r8.n_blocks));
+    }
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int G = a.nq / a.nkv;
