@@ -337,6 +337,106 @@ __global__ __launch_bounds__(PARTS * kHD) void kvq_merge_kernel(float* __restric
     }
 }
 
+// The merge of one region for a single sequence (a batch-1 int8 or Q4_0
+// decode, where the merge is on the step's critical path): the arguments in
+// one batch, and the length read after the partials' loads are issued, so
+// that one memory round trip serves them all.
+template <int PARTS>
+__global__ __launch_bounds__(PARTS * kHD) void kvq_merge1_kernel(float* __restrict__ out, DecodeArgs a) {
+    __shared__ float other[PARTS][kHD + 2];
+    {
+        const void* p0 = a.ws_acc;
+        const void* p1 = a.ws_m;
+        const void* p2 = a.ws_s;
+        const void* p3 = a.r8.lens;
+        const void* p4 = out;
+        __asm__ volatile("" ::"s"(p0), "s"(p1), "s"(p2), "s"(p3), "s"(p4), "s"(a.nq), "s"(a.tiles_per_wave),
+                         "s"(a.r8.max_chunks), "s"(a.r8.max_len), "s"(a.r8.max_blocks), "s"(a.log2_bs));
+    }
+    const int bh = blockIdx.x;
+    const int b = bh / a.nq;
+    const int d = threadIdx.x & (kHD - 1);
+    const int part = __builtin_amdgcn_readfirstlane(threadIdx.x / kHD);
+    const int chunk_len = a.tiles_per_wave * kChunkUnit;
+    const int nct = a.r8.max_chunks;
+    const int share = (nct + PARTS - 1) / PARTS;
+    const int cbeg = part * share;
+    const int cend = min(nct, cbeg + share);
+    const float* mm = a.ws_m + (size_t)bh * nct;
+    const float* ss = a.ws_s + (size_t)bh * nct;
+    const float* aa = a.ws_acc + (size_t)bh * nct * kHD + d;
+    // the length bound: max_len, and what the block table can hold
+    const int lim = (int)min((long)a.r8.max_len, (long)a.r8.max_blocks << a.log2_bs);
+    float M = -INFINITY, S = 0.0f, acc = 0.0f;
+    for (int c0 = cbeg; c0 < cend; c0 += kMergeBatch) {
+        float mv[kMergeBatch], sv[kMergeBatch], av[kMergeBatch];
+#pragma unroll
+        for (int k = 0; k < kMergeBatch; ++k) {
+            int cv = min(c0 + k, cend - 1);
+            __asm__("" : "+v"(cv));
+            mv[k] = mm[cv];
+            sv[k] = ss[cv];
+            av[k] = aa[(size_t)cv * kHD];
+        }
+        int bv = b;
+        __asm__("" : "+v"(bv));
+        const int lraw = a.r8.lens[bv];
+        // every load of the batch is issued before anything waits on one
+        __builtin_amdgcn_sched_barrier(0);
+        const int L = min(lraw, lim);
+        const int n8 = L > 0 ? (int)((unsigned)(L + chunk_len - 1) / (unsigned)chunk_len) : 0;
+        float bm = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < kMergeBatch; ++k) {
+            const int c = c0 + k;
+            const bool live = c < cend && c < n8;
+            mv[k] = live ? mv[k] : -INFINITY;
+            sv[k] = live ? sv[k] : 0.0f;   // a chunk never written may hold anything
+            av[k] = live ? av[k] : 0.0f;
+            bm = fmaxf(bm, mv[k]);
+        }
+        if (bm > M) {
+            const float f = __builtin_amdgcn_exp2f(M - bm);
+            S *= f;
+            acc *= f;
+            M = bm;
+        }
+        if (M == -INFINITY) continue;
+#pragma unroll
+        for (int k = 0; k < kMergeBatch; ++k) {
+            const float f = __builtin_amdgcn_exp2f(mv[k] - M);
+            S = fmaf(sv[k], f, S);
+            acc = fmaf(av[k], f, acc);
+        }
+    }
+    if (part > 0) {
+        other[part][d] = acc;
+        if (d == 0) {
+            other[part][kHD] = M;
+            other[part][kHD + 1] = S;
+        }
+    }
+    __syncthreads();
+    if (part == 0) {
+        float Mt = M;
+#pragma unroll
+        for (int q = 1; q < PARTS; ++q) Mt = fmaxf(Mt, other[q][kHD]);
+        float res = 0.0f;
+        if (Mt != -INFINITY) {
+            const float f0 = __builtin_amdgcn_exp2f(M - Mt);
+            float num = acc * f0, den = S * f0;
+#pragma unroll
+            for (int q = 1; q < PARTS; ++q) {
+                const float f = __builtin_amdgcn_exp2f(other[q][kHD] - Mt);
+                num = fmaf(other[q][d], f, num);
+                den = fmaf(other[q][kHD + 1], f, den);
+            }
+            res = num / den;
+        }
+        out[(size_t)bh * kHD + d] = res;
+    }
+}
+
 // Enqueue the merge of a decode's chunk partials into `out`.
 inline void launch_merge(const BandArgs& a, float* out, hipStream_t s) {
     const dim3 grid(a.batch * a.nq);
@@ -349,7 +449,12 @@ inline void launch_merge(const BandArgs& a, float* out, hipStream_t s) {
 inline void launch_merge(const DecodeArgs& a, float* out, hipStream_t s) {
     const bool live = a.batch > 1 && a.r4.max_chunks == 0;
     const dim3 grid(a.batch * a.nq);
-    if (n_chunks_total(a) > 2 * kMergeBatch) {
+    if (a.batch == 1 && a.r4.max_chunks == 0) {
+        if (n_chunks_total(a) > 2 * kMergeBatch)
+            hipLaunchKernelGGL((kvq_merge1_kernel<8>), grid, dim3(kMergeThreadsWide), 0, s, out, a);
+        else
+            hipLaunchKernelGGL((kvq_merge1_kernel<2>), grid, dim3(kMergeThreads), 0, s, out, a);
+    } else if (n_chunks_total(a) > 2 * kMergeBatch) {
         if (live)
             hipLaunchKernelGGL((kvq_merge_kernel<8, true>), grid, dim3(kMergeThreadsWide), 0, s, out, a);
         else
