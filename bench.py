@@ -44,9 +44,9 @@ TOK_HEAD_BYTES = 2 * 128 + 2 * 4   # K+V codes + K/V float32 steps per (token, k
 # counters read for a plain 256 MiB device copy (--calibrate-copy 256):
 # FETCH_SIZE 131085.3 KiB -> 2.000 bytes per counted byte, WRITE_SIZE
 # 262144 KiB -> 1.000.  Valid only for the kernel sources they were taken on.
-PMC = {"sources_sha256_16": "7f40e77f6008555b",
-       "fetch_kib": {"chunk": 8591.88, "merge": 170.55}, "write_kib": {"chunk": 290.06, "merge": 8.00},
-       "fetch_scale": 268435456 / (131085.21 * 1024), "write_scale": 268435456 / (262144.0 * 1024)}
+PMC = {"sources_sha256_16": "6bcd0fc70f8e05fe",
+       "fetch_kib": {"chunk": 8591.97, "merge": 164.53}, "write_kib": {"chunk": 290.06, "merge": 8.00},
+       "fetch_scale": 268435456 / (131085.15 * 1024), "write_scale": 268435456 / (262144.0 * 1024)}
 
 
 def kernel_sources_digest() -> str:
@@ -587,7 +587,7 @@ def main():
                    "global_batch": 1, "seq_len": L, "chunk_tokens": chunk, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "kernel": "one kvq8_append_decode_attn call: kvq_decode_mfma_kernel<0,false> + kvq_merge_kernel<2,false,DecodeArgs>",
+                     "kernel": "one kvq8_append_decode_attn call: kvq_decode_mfma_kernel<0,false> + kvq_merge1_kernel<2>",
                      "bytes_per_launch": decode_bytes_layer, "avg_call_us": round(call_us, 3)},
     }
     if not args.no_cpu_baseline:
