@@ -1,7 +1,9 @@
 """Large cache blocks (kv_bs 256 and 1024, the largest the library accepts)
 through every write path and decode: a 64-token tile then lies inside one
-block, and sequences end inside, at and just past block boundaries.  Codes
-bit for bit, outputs within 1e-4 + 1e-4 |oracle|."""
+block, and sequences end inside, at and just past block boundaries.  Also a
+single sequence shorter than the length bound (the one-region merge masks
+chunks that were never written).  Codes bit for bit, outputs within
+1e-4 + 1e-4 |oracle|."""
 import numpy as np
 import pytest
 
@@ -119,3 +121,36 @@ def test_group_bands_large_blocks(K, bs):
     ref2 = O2.decode_attention_banded(q, p2.oracle_pools(), bt2, lens2, p4.oracle_pools(), bt4, lens4,
                                       (c8.kp, c8.ks, c8.vp, c8.vs), bt8, lens8, bs, SM)
     assert_attn_close(host(out2), ref2, f"three bands bs={bs}")
+
+
+@pytest.mark.parametrize("L", [300, 0, -3, 5000])
+def test_batch1_lengths_below_the_bound(K, L):
+    """One sequence whose length is below max_ctx_len (chunks past it are
+    never written and must be masked by the merge), empty, negative, and at
+    the bound: int8 and Q4_0 decodes against the oracle."""
+    import torch
+    r = W.rng(903, L + 10)
+    nq, nkv, bs, bound = 8, 2, 16, 5000
+    n = max(L, 0)
+    bt, nb = W.paged_block_tables(r, [bound], bs)
+    k = W.normal_f32(r, (1, bound, nkv, 128))
+    v = W.normal_f32(r, (1, bound, nkv, 128))
+    lens = np.array([L], np.int32)
+    c8 = Q8Cache(nb, bs, nkv)
+    c40 = Q40Cache(nb, bs, nkv)
+    if n:
+        sl = W.slots_for_positions(bt, [0] * n, np.arange(n), bs)
+        c8.append(np.ascontiguousarray(k[0, :n]), np.ascontiguousarray(v[0, :n]), sl)
+        c40.append(np.ascontiguousarray(k[0, :n]), np.ascontiguousarray(v[0, :n]), sl)
+    q = W.normal_f32(r, (1, nq, 128))
+    out = torch.full((1, nq, 128), float("nan"), dtype=torch.float32, device="cuda")
+    K.kvq8_decode_attn(out, dev(q), c8.gk, c8.gv, c8.gks, c8.gvs, dev(bt), dev(lens), bound, SM)
+    out40 = torch.full((1, nq, 128), float("nan"), dtype=torch.float32, device="cuda")
+    K.kvq4_0_decode_attn(out40, dev(q), c40.gk, c40.gv, c40.gks, c40.gvs, dev(bt), dev(lens), bound, SM)
+    torch.cuda.synchronize()
+    ref = O8.decode_attention_q8(q, c8.kp, c8.ks, c8.vp, c8.vs, bt, [n], bs, SM)
+    ref40 = O40.decode_attention_q4_0(q, c40.kp, c40.ks, c40.vp, c40.vs, bt, [n], bs, SM)
+    assert_attn_close(host(out), ref, f"int8 L={L}")
+    assert_attn_close(host(out40), ref40, f"Q4_0 L={L}")
+    if n == 0:
+        assert np.all(host(out) == 0.0) and np.all(host(out40) == 0.0)
