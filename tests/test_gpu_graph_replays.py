@@ -1,5 +1,5 @@
-"""HIP graph capture and replay of every decode and re-quantization entry
-point (the int8 fused step has its own replay test with the qwen2b
+"""HIP graph capture and replay of every decode, re-quantization and
+write entry point (the int8 fused step has its own replay test with the qwen2b
 workload).  Each call is checked eagerly against the oracle, then captured
 once and replayed three times.  Between replays the program does eager work
 of its own: it poisons the output, overwrites the destination rows and
@@ -174,3 +174,40 @@ def test_requantize_replays(K):
     O2.requantize_q4_to_q2(p4.oracle_pools(), p2.oracle_pools(), src4, dst2)
     s4, d2 = dev(src4), dev(dst2)
     _requant_replays(lambda: K.kvq2_requantize_q4(p2.g, p4.g, s4, d2), p2.g, p2.h, "int4 -> 2-bit")
+
+
+@pytest.mark.parametrize("mode", ["int8", "int4", "2-bit", "Q4_0"])
+def test_write_path_replays(K, mode):
+    """The quantize-append of 300 bf16 rows into a paged pool, with the pool
+    zeroed eagerly between replays; the eager write equals the oracle's."""
+    import torch
+    r = W.rng(954, ["int8", "int4", "2-bit", "Q4_0"].index(mode))
+    n, nb = 300, 24
+    x = W.per_unit_sigma_normal(r, (n, NKV, 128), 1, 0.2, 5.0)
+    y = W.student_t3_f32(r, x.shape, 0.5)
+    kb = torch.from_numpy(x).to("cuda", torch.bfloat16)
+    vb = torch.from_numpy(y).to("cuda", torch.bfloat16)
+    xe, ye = host(kb.float()), host(vb.float())      # the exact values the kernel reads
+    slots = r.permutation(nb * BS)[:n].astype(np.int32)
+    sd = dev(slots)
+    if mode == "int8":
+        c = Q8Cache(nb, BS, NKV)
+        O8.quantize_append(c.kp, c.vp, c.ks, c.vs, xe, ye, slots)
+        pool, expect = [c.gk, c.gv, c.gks, c.gvs], [c.kp, c.vp, c.ks, c.vs]
+        call = lambda: K.kvq8_quantize_append(*pool, kb, vb, sd)
+    elif mode == "Q4_0":
+        c = Q40Cache(nb, BS, NKV)
+        O40.quantize_append_q4_0(c.kp, c.vp, c.ks, c.vs, xe, ye, slots)
+        pool, expect = [c.gk, c.gv, c.gks, c.gvs], [c.kp, c.vp, c.ks, c.vs]
+        call = lambda: K.kvq4_0_quantize_append(*pool, kb, vb, sd)
+    elif mode == "int4":
+        p = Q4Pool(nb, BS, NKV)
+        O4.quantize_append_q4(*p.h, xe, ye, slots)
+        pool, expect = p.g, p.h
+        call = lambda: K.kvq4_quantize_append(*pool, kb, vb, sd)
+    else:
+        p = Q2Pool(nb, BS, NKV)
+        O2.quantize_append_q2(*p.h, xe, ye, slots)
+        pool, expect = p.g, p.h
+        call = lambda: K.kvq2_quantize_append(*pool, kb, vb, sd)
+    _requant_replays(call, pool, expect, f"{mode} write")
