@@ -191,3 +191,72 @@ def test_write_paths_head_counts(nkv):
     c8.assert_device_matches_host()
     c40.assert_device_matches_host()
     p4.assert_same()
+
+
+def _query_rows(r, n):
+    """Query rows whose 32-blocks put q * (127 / qm) on or beside
+    half-integers: qm = 127 * 2^k makes the multiplier 2^-k exact, so
+    (j + 1/2) 2^k lands exactly on j + 1/2; other blocks sit one ulp beside
+    such values, or within a few ulps of them for a multiplier that is not a
+    power of two."""
+    out = np.empty((n, 128), F32)
+    j = np.arange(-126, 126, dtype=F32)
+    for i in range(n):
+        for b in range(4):
+            kind = (i + b) % 3
+            if kind < 2:
+                unit = F32(2.0) ** int(r.integers(-8, 4))
+                vals = (r.choice(j, 31) + F32(0.5)) * unit
+                if kind == 1:
+                    vals = _ulp_neighbours(vals, r)
+            else:
+                unit = F32(F32(r.uniform(0.05, 20.0)) / F32(127.0))
+                vals = _ulp_neighbours(((r.choice(j, 31) + F32(0.5)) * unit).astype(F32), r)
+            vals = np.clip(vals, F32(-126.9) * unit, F32(126.9) * unit)
+            blk = np.concatenate([[F32(127.0) * unit * (F32(-1.0) if r.integers(0, 2) else F32(1.0))], vals])
+            out[i, 32 * b:32 * b + 32] = r.permutation(blk.astype(F32))
+    return out
+
+
+def test_query_ties_codes_partials_and_decode():
+    """The query quantizer on rows with exact half-integer products (ties away
+    from zero): the exported codes and scales, the decode's int32 block dots
+    and the decode output all follow the oracle."""
+    import torch
+    import decode_attention_int8_amd as K
+    from tests.helpers import SM, assert_attn_close, fill_sequences
+    r = W.rng(605)
+    q = _query_rows(r, 240)
+    qi = torch.empty((len(q), 128), dtype=torch.int8, device="cuda")
+    qs = torch.empty((len(q), 4), dtype=torch.float32, device="cuda")
+    K.kvq8_quantize_q(qi, qs, dev(q))
+    want_i, want_s = O8.quantize_q_blocks(q)
+    # the rows do hold exact ties, and at least one where rounding half to even differs
+    y = q.reshape(-1, 4, 32) * (F32(127.0) / np.abs(q.reshape(-1, 4, 32)).max(-1, keepdims=True))
+    assert np.sum(np.abs(y - np.floor(y)) == 0.5) > 1000
+    assert np.any(np.rint(y).astype(np.int64) != want_i.reshape(-1, 4, 32))
+    assert np.array_equal(host(qi), want_i)
+    assert np.array_equal(host(qs).view(np.uint32), want_s.view(np.uint32))
+
+    B, nkv, nq, bs = 6, 2, 8, 16
+    lens = np.array([1, 300, 64, 777, 5, 256], np.int32)
+    Lm = int(lens.max())
+    bt, nb = W.paged_block_tables(r, lens, bs)
+    k = W.normal_f32(r, (B, Lm, nkv, 128))
+    v = W.normal_f32(r, (B, Lm, nkv, 128))
+    c = Q8Cache(nb, bs, nkv)
+    fill_sequences(c, bt, lens, k, v)
+    qd = q[:B * nq].reshape(B, nq, 128)
+    part = torch.full((B, nq, Lm, 4), -7, dtype=torch.int32, device="cuda")
+    K.kvq8_qk_partials(part, dev(qd), c.gk, dev(bt), dev(lens), Lm)
+    out = torch.empty((B, nq, 128), dtype=torch.float32, device="cuda")
+    K.kvq8_decode_attn(out, dev(qd), c.gk, c.gv, c.gks, c.gvs, dev(bt), dev(lens), Lm, SM)
+    torch.cuda.synchronize()
+    got = host(part)
+    qiq, _ = O8.quantize_q_blocks(qd)
+    for b in range(B):
+        for h in range(nq):
+            rows = O8.gather_rows(c.kp, bt[b], lens[b], bs, h // (nq // nkv))
+            assert np.array_equal(got[b, h, :lens[b]], O8.qk_block_partials(qiq[b, h], rows)), (b, h)
+    ref = O8.decode_attention_q8(qd, c.kp, c.ks, c.vp, c.vs, bt, lens, bs, SM)
+    assert_attn_close(host(out), ref, "tie queries")
