@@ -265,13 +265,14 @@ extern "C" int kvq2_quantize_append(uint8_t* k_cache, uint8_t* v_cache, uint16_t
     const dim3 grid((unsigned)((n_rows + kRows2PerBlock - 1) / kRows2PerBlock)), block(256);
     hipStream_t s = static_cast<hipStream_t>(stream);
 #define KVQ2_LAUNCH(DT)                                                                                     \
-    hipLaunchKernelGGL(kvq2_quantize_append_kernel<DT>, grid, block, 0, s, k_cache, v_cache, k_scale, k_zero, \
+    launch(kvq2_quantize_append_kernel<DT>, grid, block, s, k_cache, v_cache, k_scale, k_zero, \
                        v_scale, v_zero, n_slots, make_divn(nkv), k_new, v_new, (int)n_rows, slots)
-    if (dtype == KVQ8_F32) KVQ2_LAUNCH(KVQ8_F32);
-    else if (dtype == KVQ8_BF16) KVQ2_LAUNCH(KVQ8_BF16);
-    else KVQ2_LAUNCH(KVQ8_F16);
+    int st;
+    if (dtype == KVQ8_F32) st = KVQ2_LAUNCH(KVQ8_F32);
+    else if (dtype == KVQ8_BF16) st = KVQ2_LAUNCH(KVQ8_BF16);
+    else st = KVQ2_LAUNCH(KVQ8_F16);
 #undef KVQ2_LAUNCH
-    return launch_status();
+    return st;
 }
 
 extern "C" int kvq2_requantize_q4(uint8_t* k_cache2, uint8_t* v_cache2, uint16_t* k_scale2, uint16_t* k_zero2,
@@ -292,15 +293,16 @@ extern "C" int kvq2_requantize_q4(uint8_t* k_cache2, uint8_t* v_cache2, uint16_t
     if (n_rows > 0x7FFFFFFFL - 64) return KVQ8_ESHAPE;       // rows are indexed with 32-bit integers
     const long n_slots2 = (long)n_blocks2 * kv_bs, n_slots4 = (long)n_blocks4 * kv_bs;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    int st;
     if (n_rows >= 65536)
-        hipLaunchKernelGGL(kvq2_requantize_q4_kernel<4>, dim3((unsigned)((n_rows + 63) / 64)), dim3(256), 0, s,
+        st = launch(kvq2_requantize_q4_kernel<4>, dim3((unsigned)((n_rows + 63) / 64)), dim3(256), s,
                            k_cache2, v_cache2, k_scale2, k_zero2, v_scale2, v_zero2, n_slots2, k_cache4, v_cache4,
                            k_scale4, k_zero4, v_scale4, v_zero4, n_slots4, make_divn(nkv), (int)n_rows, src_slots,
                            dst_slots);
     else
-        hipLaunchKernelGGL(kvq2_requantize_q4_kernel<1>, dim3((unsigned)((n_rows + 15) / 16)), dim3(256), 0, s,
+        st = launch(kvq2_requantize_q4_kernel<1>, dim3((unsigned)((n_rows + 15) / 16)), dim3(256), s,
                            k_cache2, v_cache2, k_scale2, k_zero2, v_scale2, v_zero2, n_slots2, k_cache4, v_cache4,
                            k_scale4, k_zero4, v_scale4, v_zero4, n_slots4, make_divn(nkv), (int)n_rows, src_slots,
                            dst_slots);
-    return launch_status();
+    return st;
 }

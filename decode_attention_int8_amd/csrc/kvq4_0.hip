@@ -529,8 +529,8 @@ __global__ __launch_bounds__(kWGThreads, 2) void kvq4_0_decode_kernel(DecodeArgs
 }
 
 template <bool BS8>
-inline void launch_q40_bs(const DecodeArgs& a, int n_wg, hipStream_t s) {
-    hipLaunchKernelGGL((kvq4_0_decode_kernel<BS8>), dim3(n_wg), dim3(kWGThreads), 0, s, a);
+inline int launch_q40_bs(const DecodeArgs& a, int n_wg, hipStream_t s) {
+    return launch((kvq4_0_decode_kernel<BS8>), dim3(n_wg), dim3(kWGThreads), s, a);
 }
 
 }  // namespace kvq
@@ -553,21 +553,22 @@ extern "C" int kvq4_0_quantize_append(uint8_t* k_cache, uint8_t* v_cache, float*
     const long n_slots = (long)n_blocks * kv_bs;
     const dim3 grid((unsigned)((n_rows + kQ40RowsPerBlock - 1) / kQ40RowsPerBlock)), block(256);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    int st;
     switch (dtype) {
         case KVQ8_F32:
-            hipLaunchKernelGGL(kvq4_0_quantize_append_kernel<KVQ8_F32>, grid, block, 0, s, k_cache, v_cache, k_step,
+            st = launch(kvq4_0_quantize_append_kernel<KVQ8_F32>, grid, block, s, k_cache, v_cache, k_step,
                                v_step, n_slots, make_divn(nkv), k_new, v_new, (int)n_rows, slots);
             break;
         case KVQ8_BF16:
-            hipLaunchKernelGGL(kvq4_0_quantize_append_kernel<KVQ8_BF16>, grid, block, 0, s, k_cache, v_cache,
+            st = launch(kvq4_0_quantize_append_kernel<KVQ8_BF16>, grid, block, s, k_cache, v_cache,
                                k_step, v_step, n_slots, make_divn(nkv), k_new, v_new, (int)n_rows, slots);
             break;
         default:
-            hipLaunchKernelGGL(kvq4_0_quantize_append_kernel<KVQ8_F16>, grid, block, 0, s, k_cache, v_cache, k_step,
+            st = launch(kvq4_0_quantize_append_kernel<KVQ8_F16>, grid, block, s, k_cache, v_cache, k_step,
                                v_step, n_slots, make_divn(nkv), k_new, v_new, (int)n_rows, slots);
             break;
     }
-    return launch_status();
+    return st;
 }
 
 extern "C" int kvq4_0_decode_chunk_tokens(int batch, int nkv, int max_ctx_len) {
@@ -597,7 +598,7 @@ extern "C" int kvq4_0_decode_attn(float* out, const float* q, int batch, int nq,
                                   void* workspace, size_t workspace_bytes, void* stream) {
     if (!decode_shape_ok(batch, nq, nkv, hd, kv_bs) || n_blocks < 1 || max_blocks_per_seq < 1) return KVQ8_ESHAPE;
     if (!rows_fit_u32(n_blocks, kv_bs, nkv)) return KVQ8_ESHAPE;
-    if (max_ctx_len < 0) return KVQ8_EINVAL;
+    if (max_ctx_len < 0 || !score_scale_ok(sm_scale)) return KVQ8_EINVAL;
     const int ch = resolve_chunk40(batch, nkv, max_ctx_len, chunk);
     if (ch <= 0) return KVQ8_ESHAPE;
     if (batch == 0) return KVQ8_OK;
@@ -620,7 +621,7 @@ extern "C" int kvq4_0_decode_attn(float* out, const float* q, int batch, int nq,
     a.log2_bs = ilog2(kv_bs);
     a.batch = batch;
     a.tiles_per_wave = ch / kChunkUnit;
-    a.score_scale = sm_scale * kLog2e;
+    a.score_scale = score_scale(sm_scale) * kLog2e;
     bind_workspace(a, workspace);
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int nct = n_chunks_total(a);
@@ -628,11 +629,8 @@ extern "C" int kvq4_0_decode_attn(float* out, const float* q, int batch, int nq,
         const long pairs = (long)a.batch * pair_stride(nct, a.batch);
         const long n_wg = (long)a.nkv * ((pairs + 7) / 8) * 8;
         if (n_wg > 0x7FFFFFFFL) return KVQ8_ESHAPE;
-        if (a.log2_bs < 4)
-            launch_q40_bs<true>(a, (int)n_wg, s);
-        else
-            launch_q40_bs<false>(a, (int)n_wg, s);
+        const int st = a.log2_bs < 4 ? launch_q40_bs<true>(a, (int)n_wg, s) : launch_q40_bs<false>(a, (int)n_wg, s);
+        if (st != KVQ8_OK) return st;
     }
-    launch_merge(a, out, s);
-    return launch_status();
+    return launch_merge(a, out, s);
 }

@@ -86,21 +86,22 @@ extern "C" int kvq8_quantize_append(int8_t* k_cache, int8_t* v_cache, float* k_s
     const long n_slots = (long)n_blocks * kv_bs;
     const dim3 grid((unsigned)((n_rows + kRowsPerBlock - 1) / kRowsPerBlock)), block(256);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    int st;
     switch (dtype) {
         case KVQ8_F32:
-            hipLaunchKernelGGL(kvq8_quantize_append_kernel<KVQ8_F32>, grid, block, 0, s, k_cache, v_cache, k_scale,
+            st = launch(kvq8_quantize_append_kernel<KVQ8_F32>, grid, block, s, k_cache, v_cache, k_scale,
                                v_scale, n_slots, make_divn(nkv), k_new, v_new, (int)n_rows, slots);
             break;
         case KVQ8_BF16:
-            hipLaunchKernelGGL(kvq8_quantize_append_kernel<KVQ8_BF16>, grid, block, 0, s, k_cache, v_cache, k_scale,
+            st = launch(kvq8_quantize_append_kernel<KVQ8_BF16>, grid, block, s, k_cache, v_cache, k_scale,
                                v_scale, n_slots, make_divn(nkv), k_new, v_new, (int)n_rows, slots);
             break;
         default:
-            hipLaunchKernelGGL(kvq8_quantize_append_kernel<KVQ8_F16>, grid, block, 0, s, k_cache, v_cache, k_scale,
+            st = launch(kvq8_quantize_append_kernel<KVQ8_F16>, grid, block, s, k_cache, v_cache, k_scale,
                                v_scale, n_slots, make_divn(nkv), k_new, v_new, (int)n_rows, slots);
             break;
     }
-    return launch_status();
+    return st;
 }
 
 extern "C" int kvq8_quantize_q(int8_t* qi, float* qsc, const float* q, int n_vectors, int hd, void* stream) {
@@ -109,7 +110,6 @@ extern "C" int kvq8_quantize_q(int8_t* qi, float* qsc, const float* q, int n_vec
     if (n_vectors == 0) return KVQ8_OK;
     if (!qi || !qsc || !q || !aligned16(q) || !aligned16(qi)) return KVQ8_EINVAL;
     const dim3 grid((unsigned)((n_vectors + kMaxRows - 1) / kMaxRows)), block(256);
-    hipLaunchKernelGGL(kvq8_quantize_q_kernel, grid, block, 0, static_cast<hipStream_t>(stream), qi, qsc, q,
-                       (long)n_vectors);
-    return launch_status();
+    return launch(kvq8_quantize_q_kernel, grid, block, static_cast<hipStream_t>(stream), qi, qsc, q,
+                  (long)n_vectors);
 }

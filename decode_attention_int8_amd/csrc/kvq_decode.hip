@@ -86,7 +86,7 @@ extern "C" int kvq8_decode_attn(float* out, const float* q, int batch, int nq, c
                                 void* workspace, size_t workspace_bytes, void* stream) {
     if (!decode_shape_ok(batch, nq, nkv, hd, kv_bs) || n_blocks < 1 || max_blocks_per_seq < 1) return KVQ8_ESHAPE;
     if (!rows_fit_u32(n_blocks, kv_bs, nkv)) return KVQ8_ESHAPE;
-    if (max_ctx_len < 0) return KVQ8_EINVAL;
+    if (max_ctx_len < 0 || !score_scale_ok(sm_scale)) return KVQ8_EINVAL;
     const int ch = resolve_chunk8(batch, nkv, max_ctx_len, chunk);
     if (ch <= 0) return KVQ8_ESHAPE;
     if (batch == 0) return KVQ8_OK;
@@ -109,7 +109,7 @@ extern "C" int kvq8_decode_attn(float* out, const float* q, int batch, int nq, c
     a.log2_bs = ilog2(kv_bs);
     a.batch = batch;
     a.tiles_per_wave = ch / kChunkUnit;
-    a.score_scale = sm_scale * kLog2e;
+    a.score_scale = score_scale(sm_scale) * kLog2e;
     bind_workspace(a, workspace);
     return launch_decode(a, out, static_cast<hipStream_t>(stream));
 }
@@ -122,7 +122,8 @@ extern "C" int kvq8_append_decode_attn(float* out, const float* q, int batch, in
                                        void* workspace, size_t workspace_bytes, void* stream) {
     if (!decode_shape_ok(batch, nq, nkv, hd, kv_bs) || n_blocks < 1 || max_blocks_per_seq < 1) return KVQ8_ESHAPE;
     if (!rows_fit_u32(n_blocks, kv_bs, nkv)) return KVQ8_ESHAPE;
-    if (max_ctx_len < 0 || dtype < KVQ8_F32 || dtype > KVQ8_F16) return KVQ8_EINVAL;
+    if (max_ctx_len < 0 || dtype < KVQ8_F32 || dtype > KVQ8_F16 || !score_scale_ok(sm_scale))
+        return KVQ8_EINVAL;
     const int ch = resolve_chunk8(batch, nkv, max_ctx_len, chunk);
     if (ch <= 0) return KVQ8_ESHAPE;
     if (batch == 0) return KVQ8_OK;
@@ -153,7 +154,7 @@ extern "C" int kvq8_append_decode_attn(float* out, const float* q, int batch, in
     a.log2_bs = ilog2(kv_bs);
     a.batch = batch;
     a.tiles_per_wave = ch / kChunkUnit;
-    a.score_scale = sm_scale * kLog2e;
+    a.score_scale = score_scale(sm_scale) * kLog2e;
     bind_workspace(a, workspace);
     return launch_decode(a, out, static_cast<hipStream_t>(stream), dtype);
 }
@@ -179,12 +180,10 @@ extern "C" int kvq8_qk_partials(int32_t* partials, const float* q, int batch, in
     if ((long)batch * nkv * n_groups > 0x7FFFFFFFL) return KVQ8_ESHAPE;
     const dim3 grid(batch * nkv * n_groups), block(kWGThreads);
     if (kv_bs < 16)
-        hipLaunchKernelGGL(kvq8_qk_partials_kernel<true>, grid, block, 0, static_cast<hipStream_t>(stream), a,
-                           partials, n_groups);
-    else
-        hipLaunchKernelGGL(kvq8_qk_partials_kernel<false>, grid, block, 0, static_cast<hipStream_t>(stream), a,
-                           partials, n_groups);
-    return launch_status();
+        return launch(kvq8_qk_partials_kernel<true>, grid, block, static_cast<hipStream_t>(stream), a, partials,
+                      n_groups);
+    return launch(kvq8_qk_partials_kernel<false>, grid, block, static_cast<hipStream_t>(stream), a, partials,
+                  n_groups);
 }
 
 extern "C" int kvq4_decode_chunk_tokens(int batch, int nkv, int max_len4, int max_len8) {
@@ -219,7 +218,7 @@ extern "C" int kvq4_decode_attn(float* out, const float* q, int batch, int nq, c
                                 void* workspace, size_t workspace_bytes, void* stream) {
     if (!decode_shape_ok(batch, nq, nkv, hd, kv_bs)) return KVQ8_ESHAPE;
     if (n_blocks4 < 1 || n_blocks8 < 1 || max_blocks_per_seq4 < 1 || max_blocks_per_seq8 < 1) return KVQ8_ESHAPE;
-    if (max_len4 < 0 || max_len8 < 0) return KVQ8_EINVAL;
+    if (max_len4 < 0 || max_len8 < 0 || !score_scale_ok(sm_scale)) return KVQ8_EINVAL;
     const int ch = resolve_chunk4(batch, nkv, max_len4, max_len8, chunk);
     if (ch <= 0) return KVQ8_ESHAPE;
     if (batch == 0) return KVQ8_OK;
@@ -254,7 +253,7 @@ extern "C" int kvq4_decode_attn(float* out, const float* q, int batch, int nq, c
     a.log2_bs = ilog2(kv_bs);
     a.batch = batch;
     a.tiles_per_wave = ch / kChunkUnit;
-    a.score_scale = sm_scale * kLog2e;
+    a.score_scale = score_scale(sm_scale) * kLog2e;
     bind_workspace(a, workspace);
     return launch_decode(a, out, static_cast<hipStream_t>(stream));
 }
@@ -301,7 +300,7 @@ extern "C" int kvq2_decode_attn(float* out, const float* q, int batch, int nq, c
     if (n_blocks2 < 1 || n_blocks4 < 1 || n_blocks8 < 1 || max_blocks_per_seq2 < 1 || max_blocks_per_seq4 < 1 ||
         max_blocks_per_seq8 < 1)
         return KVQ8_ESHAPE;
-    if (max_len2 < 0 || max_len4 < 0 || max_len8 < 0) return KVQ8_EINVAL;
+    if (max_len2 < 0 || max_len4 < 0 || max_len8 < 0 || !score_scale_ok(sm_scale)) return KVQ8_EINVAL;
     const int ch = resolve_chunk2(batch, nkv, max_len2, max_len4, max_len8, chunk);
     if (ch <= 0) return KVQ8_ESHAPE;
     if (batch == 0) return KVQ8_OK;
@@ -348,7 +347,7 @@ extern "C" int kvq2_decode_attn(float* out, const float* q, int batch, int nq, c
     a.log2_bs = ilog2(kv_bs);
     a.batch = batch;
     a.tiles_per_wave = ch / kChunkUnit;
-    a.score_scale = sm_scale * kLog2e;
+    a.score_scale = score_scale(sm_scale) * kLog2e;
     bind_workspace(a, workspace);
     return launch_decode(a, out, static_cast<hipStream_t>(stream));
 }

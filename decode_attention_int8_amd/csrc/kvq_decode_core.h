@@ -438,33 +438,25 @@ __global__ __launch_bounds__(PARTS * kHD) void kvq_merge1_kernel(float* __restri
 }
 
 // Enqueue the merge of a decode's chunk partials into `out`.
-inline void launch_merge(const BandArgs& a, float* out, hipStream_t s) {
+inline int launch_merge(const BandArgs& a, float* out, hipStream_t s) {
     const dim3 grid(a.batch * a.nq);
     if (n_chunks_total(a) > 2 * kMergeBatch)
-        hipLaunchKernelGGL((kvq_merge_kernel<8, false, BandArgs>), grid, dim3(kMergeThreadsWide), 0, s, out, a);
-    else
-        hipLaunchKernelGGL((kvq_merge_kernel<2, false, BandArgs>), grid, dim3(kMergeThreads), 0, s, out, a);
+        return launch((kvq_merge_kernel<8, false, BandArgs>), grid, dim3(kMergeThreadsWide), s, out, a);
+    return launch((kvq_merge_kernel<2, false, BandArgs>), grid, dim3(kMergeThreads), s, out, a);
 }
 
-inline void launch_merge(const DecodeArgs& a, float* out, hipStream_t s) {
+inline int launch_merge(const DecodeArgs& a, float* out, hipStream_t s) {
     const bool live = a.batch > 1 && a.r4.max_chunks == 0;
-    const dim3 grid(a.batch * a.nq);
-    if (a.batch == 1 && a.r4.max_chunks == 0) {
-        if (n_chunks_total(a) > 2 * kMergeBatch)
-            hipLaunchKernelGGL((kvq_merge1_kernel<8>), grid, dim3(kMergeThreadsWide), 0, s, out, a);
-        else
-            hipLaunchKernelGGL((kvq_merge1_kernel<2>), grid, dim3(kMergeThreads), 0, s, out, a);
-    } else if (n_chunks_total(a) > 2 * kMergeBatch) {
-        if (live)
-            hipLaunchKernelGGL((kvq_merge_kernel<8, true>), grid, dim3(kMergeThreadsWide), 0, s, out, a);
-        else
-            hipLaunchKernelGGL((kvq_merge_kernel<8, false>), grid, dim3(kMergeThreadsWide), 0, s, out, a);
-    } else {
-        if (live)
-            hipLaunchKernelGGL((kvq_merge_kernel<2, true>), grid, dim3(kMergeThreads), 0, s, out, a);
-        else
-            hipLaunchKernelGGL((kvq_merge_kernel<2, false>), grid, dim3(kMergeThreads), 0, s, out, a);
-    }
+    const bool wide = n_chunks_total(a) > 2 * kMergeBatch;
+    const dim3 grid(a.batch * a.nq), block(wide ? kMergeThreadsWide : kMergeThreads);
+    if (a.batch == 1 && a.r4.max_chunks == 0)
+        return wide ? launch((kvq_merge1_kernel<8>), grid, block, s, out, a)
+                    : launch((kvq_merge1_kernel<2>), grid, block, s, out, a);
+    if (wide)
+        return live ? launch((kvq_merge_kernel<8, true>), grid, block, s, out, a)
+                    : launch((kvq_merge_kernel<8, false>), grid, block, s, out, a);
+    return live ? launch((kvq_merge_kernel<2, true>), grid, block, s, out, a)
+                : launch((kvq_merge_kernel<2, false>), grid, block, s, out, a);
 }
 
 // ----------------------------------------------------------------------------

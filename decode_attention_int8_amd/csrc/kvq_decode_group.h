@@ -189,12 +189,10 @@ __global__ __launch_bounds__(kWGThreads, 2) void kvq4_decode_mfma_kernel(Args a)
 }
 
 template <class Args>
-inline void launch_mfma4(const Args& a, int n_wg, hipStream_t s) {
+inline int launch_mfma4(const Args& a, int n_wg, hipStream_t s) {
     const dim3 grid(n_wg), block(kWGThreads);
-    if (a.log2_bs < 4)
-        hipLaunchKernelGGL((kvq4_decode_mfma_kernel<true, Args>), grid, block, 0, s, a);
-    else
-        hipLaunchKernelGGL((kvq4_decode_mfma_kernel<false, Args>), grid, block, 0, s, a);
+    if (a.log2_bs < 4) return launch((kvq4_decode_mfma_kernel<true, Args>), grid, block, s, a);
+    return launch((kvq4_decode_mfma_kernel<false, Args>), grid, block, s, a);
 }
 
 // Enqueue the chunk kernel (if there is any context) and the merge kernel.
@@ -207,15 +205,16 @@ inline int launch_decode(const Args& a, float* out, hipStream_t s, int new_dtype
         const long pairs = (long)a.batch * pair_stride(nct, a.batch);
         const long n_wg = (long)a.nkv * ((pairs + 7) / 8) * 8;
         if (n_wg > 0x7FFFFFFFL) return KVQ8_ESHAPE;
+        int st;
         if constexpr (kBanded<Args>)
-            launch_mfma4(a, (int)n_wg, s);
+            st = launch_mfma4(a, (int)n_wg, s);
         else if (a.r4.max_chunks > 0)
-            launch_mfma4(a, (int)n_wg, s);
+            st = launch_mfma4(a, (int)n_wg, s);
         else
-            launch_mfma(a, (int)n_wg, new_dtype, s);
+            st = launch_mfma(a, (int)n_wg, new_dtype, s);
+        if (st != KVQ8_OK) return st;
     }
-    launch_merge(a, out, s);
-    return launch_status();
+    return launch_merge(a, out, s);
 }
 
 }  // namespace kvq

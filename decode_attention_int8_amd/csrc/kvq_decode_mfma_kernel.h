@@ -58,9 +58,12 @@ __global__ __launch_bounds__(kWGThreads, 2) void kvq_decode_mfma_kernel(DecodeAr
     // tiles of this wave: first, first + 256, ... (at least one, possibly empty)
     const int n_tiles = first < end ? (end - first + kChunkUnit - 1) / kChunkUnit : 1;
 
-    // fused write path: one wave owns the token at L-1
+    // fused write path: one wave owns the token at L-1.  A length above the
+    // bound (clamped to L) puts the new token past what the call attends:
+    // it is then neither written nor attended.
     const int tn = L - 1;
-    const bool has_new = NEWDT >= 0 && tn >= c0 && tn < end && (((tn - c0) >> 6) & (kWaves - 1)) == wave;
+    const bool has_new = NEWDT >= 0 && a.r8.lens[b] == L && tn >= c0 && tn < end &&
+                         (((tn - c0) >> 6) & (kWaves - 1)) == wave;
     // then the new token's loads, then the first tile's
     float xn[4];
     if constexpr (NEWDT >= 0) {
@@ -157,23 +160,16 @@ __global__ __launch_bounds__(kWGThreads, 2) void kvq_decode_mfma_kernel(DecodeAr
 }
 
 template <bool BS8>
-inline void launch_mfma_bs(const DecodeArgs& a, int n_wg, int new_dtype, hipStream_t s) {
+inline int launch_mfma_bs(const DecodeArgs& a, int n_wg, int new_dtype, hipStream_t s) {
     const dim3 grid(n_wg), block(kWGThreads);
-    if (new_dtype == KVQ8_F32)
-        hipLaunchKernelGGL((kvq_decode_mfma_kernel<KVQ8_F32, BS8>), grid, block, 0, s, a);
-    else if (new_dtype == KVQ8_BF16)
-        hipLaunchKernelGGL((kvq_decode_mfma_kernel<KVQ8_BF16, BS8>), grid, block, 0, s, a);
-    else if (new_dtype == KVQ8_F16)
-        hipLaunchKernelGGL((kvq_decode_mfma_kernel<KVQ8_F16, BS8>), grid, block, 0, s, a);
-    else
-        hipLaunchKernelGGL((kvq_decode_mfma_kernel<-1, BS8>), grid, block, 0, s, a);
+    if (new_dtype == KVQ8_F32) return launch((kvq_decode_mfma_kernel<KVQ8_F32, BS8>), grid, block, s, a);
+    if (new_dtype == KVQ8_BF16) return launch((kvq_decode_mfma_kernel<KVQ8_BF16, BS8>), grid, block, s, a);
+    if (new_dtype == KVQ8_F16) return launch((kvq_decode_mfma_kernel<KVQ8_F16, BS8>), grid, block, s, a);
+    return launch((kvq_decode_mfma_kernel<-1, BS8>), grid, block, s, a);
 }
 
-inline void launch_mfma(const DecodeArgs& a, int n_wg, int new_dtype, hipStream_t s) {
-    if (a.log2_bs < 4)
-        launch_mfma_bs<true>(a, n_wg, new_dtype, s);
-    else
-        launch_mfma_bs<false>(a, n_wg, new_dtype, s);
+inline int launch_mfma(const DecodeArgs& a, int n_wg, int new_dtype, hipStream_t s) {
+    return a.log2_bs < 4 ? launch_mfma_bs<true>(a, n_wg, new_dtype, s) : launch_mfma_bs<false>(a, n_wg, new_dtype, s);
 }
 
 }  // namespace kvq

@@ -13,7 +13,6 @@ torch hands out is valid in it.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 
 import torch
@@ -103,6 +102,12 @@ def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _scale(sm_scale):
+    """The score scale argument: None passes 0, which the library reads as
+    its default 1 / sqrt(hd)."""
+    return 0.0 if sm_scale is None else float(sm_scale)
 
 
 def _ptr(t: torch.Tensor | None, dtype=None, name="tensor"):
@@ -234,8 +239,6 @@ def kvq8_decode_attn(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, c
     B, nq, _ = q.shape
     _tables(block_tables, ctx_lens, B)
     _same_device(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, ctx_lens, workspace)
-    if sm_scale is None:
-        sm_scale = 1.0 / math.sqrt(hd)
     need = kvq8_decode_workspace_size(B, nq, nkv, max_ctx_len, chunk)
     if workspace is None:
         workspace = alloc_workspace(need, q.device)
@@ -244,7 +247,7 @@ def kvq8_decode_attn(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, c
         _ptr(k_cache, torch.int8, "k_cache"), _ptr(v_cache, torch.int8, "v_cache"),
         _ptr(k_scale, torch.float32, "k_scale"), _ptr(v_scale, torch.float32, "v_scale"),
         n_blocks, kv_bs, nkv, hd, _ptr(block_tables, torch.int32, "block_tables"), block_tables.shape[1],
-        _ptr(ctx_lens, torch.int32, "ctx_lens"), max_ctx_len, float(sm_scale), chunk,
+        _ptr(ctx_lens, torch.int32, "ctx_lens"), max_ctx_len, _scale(sm_scale), chunk,
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
     _check(st, "kvq8_decode_attn")
     return out
@@ -265,8 +268,6 @@ def kvq8_append_decode_attn(out, q, k_new, v_new, k_cache, v_cache, k_scale, v_s
         raise ValueError("k_new / v_new must be [B][nkv][hd]")
     _tables(block_tables, ctx_lens, B)
     _same_device(out, q, k_new, v_new, k_cache, v_cache, k_scale, v_scale, block_tables, ctx_lens, workspace)
-    if sm_scale is None:
-        sm_scale = 1.0 / math.sqrt(hd)
     need = kvq8_decode_workspace_size(B, nq, nkv, max_ctx_len, chunk)
     if workspace is None:
         workspace = alloc_workspace(need, q.device)
@@ -276,7 +277,7 @@ def kvq8_append_decode_attn(out, q, k_new, v_new, k_cache, v_cache, k_scale, v_s
         _ptr(v_cache, torch.int8, "v_cache"), _ptr(k_scale, torch.float32, "k_scale"),
         _ptr(v_scale, torch.float32, "v_scale"), n_blocks, kv_bs, nkv, hd,
         _ptr(block_tables, torch.int32, "block_tables"), block_tables.shape[1],
-        _ptr(ctx_lens, torch.int32, "ctx_lens"), max_ctx_len, float(sm_scale), chunk,
+        _ptr(ctx_lens, torch.int32, "ctx_lens"), max_ctx_len, _scale(sm_scale), chunk,
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
     _check(st, "kvq8_append_decode_attn")
     return out
@@ -384,8 +385,6 @@ def kvq4_decode_attn(out, q, pool4, block_tables4, lens4, max_len4: int, pool8, 
     _tables(block_tables4, lens4, B, "4")
     _tables(block_tables8, lens8, B, "8")
     _same_device(out, q, *pool4, *pool8, block_tables4, lens4, block_tables8, lens8, workspace)
-    if sm_scale is None:
-        sm_scale = 1.0 / math.sqrt(hd)
     need = kvq4_decode_workspace_size(B, nq, nkv, max_len4, max_len8, chunk)
     if workspace is None:
         workspace = alloc_workspace(need, q.device)
@@ -398,7 +397,7 @@ def kvq4_decode_attn(out, q, pool4, block_tables4, lens4, max_len4: int, pool8, 
         _ptr(k8, torch.int8, "k8"), _ptr(v8, torch.int8, "v8"), _ptr(k8s, torch.float32, "k8_scale"),
         _ptr(v8s, torch.float32, "v8_scale"), n8, _ptr(block_tables8, torch.int32, "block_tables8"),
         block_tables8.shape[1], _ptr(lens8, torch.int32, "lens8"), max_len8,
-        kv_bs, nkv, hd, float(sm_scale), chunk, _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+        kv_bs, nkv, hd, _scale(sm_scale), chunk, _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
         _stream(stream))
     _check(st, "kvq4_decode_attn")
     return out
@@ -456,8 +455,6 @@ def kvq4_0_decode_attn(out, q, k_cache, v_cache, k_step, v_step, block_tables, c
     B, nq, _ = q.shape
     _tables(block_tables, ctx_lens, B)
     _same_device(out, q, k_cache, v_cache, k_step, v_step, block_tables, ctx_lens, workspace)
-    if sm_scale is None:
-        sm_scale = 1.0 / math.sqrt(hd)
     need = kvq4_0_decode_workspace_size(B, nq, nkv, max_ctx_len, chunk)
     if workspace is None:
         workspace = alloc_workspace(need, q.device)
@@ -466,7 +463,7 @@ def kvq4_0_decode_attn(out, q, k_cache, v_cache, k_step, v_step, block_tables, c
         _ptr(k_cache, torch.uint8, "k_cache"), _ptr(v_cache, torch.uint8, "v_cache"),
         _ptr(k_step, torch.float32, "k_step"), _ptr(v_step, torch.float32, "v_step"),
         n_blocks, kv_bs, nkv, hd, _ptr(block_tables, torch.int32, "block_tables"), block_tables.shape[1],
-        _ptr(ctx_lens, torch.int32, "ctx_lens"), max_ctx_len, float(sm_scale), chunk,
+        _ptr(ctx_lens, torch.int32, "ctx_lens"), max_ctx_len, _scale(sm_scale), chunk,
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
     _check(st, "kvq4_0_decode_attn")
     return out
@@ -548,8 +545,6 @@ def kvq2_decode_attn(out, q, pool2, block_tables2, lens2, max_len2: int, pool4, 
     _tables(block_tables8, lens8, B, "8")
     _same_device(out, q, *pool2, *pool4, *pool8, block_tables2, lens2, block_tables4, lens4, block_tables8, lens8,
                  workspace)
-    if sm_scale is None:
-        sm_scale = 1.0 / math.sqrt(hd)
     need = kvq2_decode_workspace_size(B, nq, nkv, max_len2, max_len4, max_len8, chunk)
     if workspace is None:
         workspace = alloc_workspace(need, q.device)
@@ -562,7 +557,7 @@ def kvq2_decode_attn(out, q, pool2, block_tables2, lens2, max_len2: int, pool4, 
         _ptr(k8, torch.int8, "k8"), _ptr(v8, torch.int8, "v8"), _ptr(k8s, torch.float32, "k8_scale"),
         _ptr(v8s, torch.float32, "v8_scale"), n8, _ptr(block_tables8, torch.int32, "block_tables8"),
         block_tables8.shape[1], _ptr(lens8, torch.int32, "lens8"), max_len8,
-        kv_bs, nkv, hd, float(sm_scale), chunk, _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+        kv_bs, nkv, hd, _scale(sm_scale), chunk, _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
         _stream(stream))
     _check(st, "kvq2_decode_attn")
     return out

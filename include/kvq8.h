@@ -33,8 +33,10 @@
  *    stream) and the call returns without synchronizing.  Results are valid
  *    once the stream has reached that point.
  *  - Arguments are validated on the host before anything is launched; a
- *    violation returns a negative status and launches nothing.  A failed
- *    launch returns KVQ8_EHIP.
+ *    violation returns a negative status and launches nothing.  A launch
+ *    that the runtime rejects returns KVQ8_EHIP; the status is that of this
+ *    call's own launches (an error left pending by an earlier, unrelated
+ *    HIP call is neither reported nor cleared).
  *  - Device-side index data (slots, block tables, context lengths) is
  *    bounds-checked in the kernels: a slot or block id outside the pool is
  *    skipped (the token is neither written nor read) and context lengths are
@@ -141,8 +143,9 @@ size_t kvq8_decode_workspace_size(int batch, int nq, int nkv, int max_ctx_len, i
  * The context is split into chunks processed in parallel, each keeping its
  * own running max and sum (online softmax per chunk); a second kernel merges
  * the chunks and divides by the total sum.  The integer dot products and the
- * value accumulation run on the matrix cores (weights carried as two bf16
- * parts, exact to 2^-16 relative); accumulation is float32 and the result
+ * value accumulation run on the matrix cores (each weight is carried as an
+ * f16 high part of 11 significant bits plus the f16 rounding of the
+ * remainder, together exact to 2^-21 relative); accumulation is float32 and the result
  * matches the exact float64 value of the definition to about 1e-5 relative.
  * A sequence with context length 0 gets a zero output row.  The pool may
  * hold at most 2^32 - 1 rows (n_blocks * kv_bs * nkv), else KVQ8_ESHAPE.
@@ -154,7 +157,9 @@ size_t kvq8_decode_workspace_size(int batch, int nq, int nkv, int max_ctx_len, i
  *   block_tables      (device) int32 [batch][max_blocks_per_seq]
  *   ctx_lens          (device) int32 [batch]
  *   max_ctx_len       (host) an upper bound of ctx_lens; sizes the grid
- *   sm_scale          score scale, normally 1 / sqrt(hd)
+ *   sm_scale          score scale; 0 or a negative value selects the
+ *                     method's 1 / sqrt(hd) ([P1] Sec. 1-2); NaN or an
+ *                     infinite value returns KVQ8_EINVAL
  *   chunk             tokens per work item: 0 (default) or a multiple of
  *                     256; must equal the value given to
  *                     kvq8_decode_workspace_size
@@ -182,7 +187,11 @@ int kvq8_decode_attn(float* out, const float* q, int batch, int nq,
  * that position (skipped when the block id is outside the pool), and used
  * by the attention.  The cache bytes and the output equal those of
  * kvq8_quantize_append followed by kvq8_decode_attn.  Sequences with
- * ctx_lens[b] = 0 write nothing and get a zero row.  Other arguments as for
+ * ctx_lens[b] = 0 write nothing and get a zero row.  A sequence whose
+ * ctx_lens[b] exceeds the bound (max_ctx_len, or max_blocks_per_seq * kv_bs)
+ * is attended over the clamped length like in kvq8_decode_attn, and its new
+ * token, which lies past that length, is not written: no cached token is
+ * overwritten.  Other arguments as for
  * kvq8_decode_attn (same workspace size); the cache pools are written.
  */
 int kvq8_append_decode_attn(float* out, const float* q, int batch, int nq,

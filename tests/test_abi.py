@@ -67,6 +67,18 @@ def test_decode_validation():
     assert _decode(batch=0) == OK                     # nothing to do
 
 
+def test_decode_score_scale_argument():
+    """sm_scale: a NaN or infinite value is rejected before anything runs;
+    0 and negative values select the library's default 1 / sqrt(hd) and pass
+    validation (here they stop at the missing workspace)."""
+    for bad in (float("nan"), float("inf"), float("-inf")):
+        assert _decode(sm=bad) == EINVAL
+    for ok in (0.0, -1.0, 0.088, 3.0):
+        assert _decode(sm=ok) == EWORKSPACE
+    # the binding passes 0 for "no scale given": the default is the library's
+    assert K._scale(None) == 0.0 and K._scale(0.5) == 0.5
+
+
 def test_write_validation():
     lib = K.lib()
     args = [_fake(), _fake(), _fake(), _fake(), 64, 16, 8, 128, _fake(), _fake(), K.F32, 10, _fake(), None]

@@ -308,3 +308,84 @@ def test_append_decode_equals_append_then_decode(K, g, dtype):
     ref = O8.decode_attention_q8(q[keep], c.kp, c.ks, c.vp, c.vs, bt[keep], lens[keep], bs, SM)
     assert_attn_close(host(out)[keep], ref, f"fused g={g} {dtype}")
     assert np.all(host(out)[4] == 0.0)
+
+
+@pytest.mark.parametrize("max_ctx,lens", [
+    (120, [60, 121, 500, 120]),          # max_ctx_len binds (a table row holds 128 tokens)
+    (200, [60, 129, 500, 128]),          # the table row binds
+])
+def test_append_decode_lengths_above_the_bound(K, max_ctx, lens):
+    """A sequence whose length exceeds max_ctx_len, or what its block-table
+    row can hold, is attended over the clamped length and its new token is
+    not written: every cached token stays as it was, and the output equals
+    the oracle over the clamped context."""
+    torch = _torch()
+    r = W.rng(345, max_ctx)
+    nkv, nq, bs, mb = 2, 4, 16, 8
+    lens = np.array(lens, np.int32)
+    B = len(lens)
+    clamp = np.minimum(lens, min(max_ctx, mb * bs)).astype(np.int32)
+    nb = B * mb + 2
+    bt = r.permutation(nb)[:B * mb].reshape(B, mb).astype(np.int32)
+    k = W.normal_f32(r, (B, mb * bs, nkv, 128))
+    v = W.normal_f32(r, (B, mb * bs, nkv, 128))
+    c = Q8Cache(nb, bs, nkv)
+    fill_sequences(c, bt, np.full(B, mb * bs, np.int32), k, v)      # every slot of every row holds a token
+    before = [host(t).copy() for t in (c.gk, c.gv, c.gks, c.gvs)]
+    kn = W.normal_f32(r, (B, nkv, 128), 5.0)
+    vn = W.normal_f32(r, (B, nkv, 128), 5.0)
+    q = W.normal_f32(r, (B, nq, 128))
+    out = torch.empty((B, nq, 128), dtype=torch.float32, device="cuda")
+    K.kvq8_append_decode_attn(out, dev(q), dev(kn), dev(vn), c.gk, c.gv, c.gks, c.gvs, dev(bt), dev(lens),
+                              max_ctx, SM)
+    torch.cuda.synchronize()
+    # only the in-bound sequences' newest slots were written, exactly as the write path does
+    sl = np.array([bt[b, (lens[b] - 1) // bs] * bs + (lens[b] - 1) % bs if lens[b] == clamp[b] else -1
+                   for b in range(B)], np.int32)
+    assert list(sl >= 0) == [True, False, False, True]
+    O8.quantize_append(c.kp, c.vp, c.ks, c.vs, kn, vn, sl)
+    c.assert_device_matches_host()
+    flat_before = [x.reshape(nb * bs, -1) for x in before]
+    flat_after = [host(t).reshape(nb * bs, -1) for t in (c.gk, c.gv, c.gks, c.gvs)]
+    untouched = np.setdiff1d(np.arange(nb * bs), sl[sl >= 0])
+    for x0, x1 in zip(flat_before, flat_after):
+        assert np.array_equal(x0[untouched], x1[untouched])
+    ref = O8.decode_attention_q8(q, c.kp, c.ks, c.vp, c.vs, bt, clamp, bs, SM)
+    assert_attn_close(host(out), ref, "lengths above the bound")
+
+
+def test_default_score_scale_is_one_over_sqrt_hd(K):
+    """No score scale given: the library's default equals an explicit
+    1 / sqrt(128) bit for bit (int8 and Q4_0 decodes)."""
+    torch = _torch()
+    r = W.rng(346)
+    nkv, nq, bs = 2, 8, 16
+    lens = np.array([300, 17, 1024], np.int32)
+    B, Lm = len(lens), int(lens.max())
+    bt, nb = W.paged_block_tables(r, lens, bs)
+    k = W.normal_f32(r, (B, Lm, nkv, 128))
+    c = Q8Cache(nb, bs, nkv)
+    fill_sequences(c, bt, lens, k, k)
+    q = dev(W.normal_f32(r, (B, nq, 128), 3.0))
+    outs = []
+    for sm in (None, 0.0, -2.0, SM):
+        o = torch.empty((B, nq, 128), dtype=torch.float32, device="cuda")
+        K.kvq8_decode_attn(o, q, c.gk, c.gv, c.gks, c.gvs, dev(bt), dev(lens), Lm, sm)
+        outs.append(host(o))
+    torch.cuda.synchronize()
+    for o in outs[:3]:
+        assert np.array_equal(o.view(np.uint32), outs[3].view(np.uint32))
+    # Q4_0 cache from the same keys
+    k4 = torch.zeros((nb, bs, nkv, 64), dtype=torch.uint8, device="cuda")
+    v4 = torch.zeros_like(k4)
+    ks4 = torch.zeros((nb, bs, nkv, 4), dtype=torch.float32, device="cuda")
+    vs4 = torch.zeros_like(ks4)
+    for b in range(B):
+        sl = W.slots_for_positions(bt, [b] * int(lens[b]), np.arange(lens[b]), bs)
+        K.kvq4_0_quantize_append(k4, v4, ks4, vs4, dev(k[b, :lens[b]]), dev(k[b, :lens[b]]), dev(sl))
+    o1 = torch.empty((B, nq, 128), dtype=torch.float32, device="cuda")
+    o2 = torch.empty_like(o1)
+    K.kvq4_0_decode_attn(o1, q, k4, v4, ks4, vs4, dev(bt), dev(lens), Lm)
+    K.kvq4_0_decode_attn(o2, q, k4, v4, ks4, vs4, dev(bt), dev(lens), Lm, SM)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(o1).view(np.uint32), host(o2).view(np.uint32))
