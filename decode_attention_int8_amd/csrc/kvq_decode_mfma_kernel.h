@@ -60,10 +60,9 @@ __global__ __launch_bounds__(kWGThreads, 2) void kvq_decode_mfma_kernel(DecodeAr
 
     // fused write path: one wave owns the token at L-1.  A length above the
     // bound (clamped to L) puts the new token past what the call attends:
-    // it is then neither written nor attended.
-    const int tn = L - 1;
-    const bool has_new = NEWDT >= 0 && a.r8.lens[b] == L && tn >= c0 && tn < end &&
-                         (((tn - c0) >> 6) & (kWaves - 1)) == wave;
+    // it is then neither written nor attended, and tn = -1 matches no token.
+    const int tn = a.r8.lens[b] == L ? L - 1 : -1;
+    const bool has_new = NEWDT >= 0 && tn >= c0 && tn < end && (((tn - c0) >> 6) & (kWaves - 1)) == wave;
     // then the new token's loads, then the first tile's
     float xn[4];
     if constexpr (NEWDT >= 0) {
@@ -109,7 +108,8 @@ __global__ __launch_bounds__(kWGThreads, 2) void kvq_decode_mfma_kernel(DecodeAr
 
     // Token tn = L-1 is the last token of the sequence, so it can only lie in
     // the last tile of a wave: only the two terminal calls substitute, with
-    // selects that match nothing outside the owner's tile.
+    // selects that match nothing outside the owner's tile (and nothing at all
+    // when tn = -1).
     auto run_last = [&](const MTile& T, int base) __attribute__((always_inline)) {
         if constexpr (NEWDT >= 0) {
             if (has_new) {
