@@ -24,6 +24,7 @@ from .kvq8 import (  # noqa: F401
     kvq4_requantize_q8,
     kvq8_append_decode_attn,
     kvq8_decode_attn,
+    kvq8_decode_attn_noalloc,
     kvq8_decode_chunk_tokens,
     kvq8_decode_workspace_size,
     kvq8_qk_partials,

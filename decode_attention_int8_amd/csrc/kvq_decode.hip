@@ -2,6 +2,9 @@
 // integer partials export, and the mixed int4 / int8 cache of the group
 // variant ([P4] Sec. 3.2-3.3).  The pipeline itself lives in
 // kvq_decode_core.h and is compiled once, here.
+#include <atomic>
+#include <mutex>
+
 #include "kvq_decode_core.h"
 #include "kvq_decode_group.h"
 
@@ -79,11 +82,50 @@ extern "C" size_t kvq8_decode_workspace_size(int batch, int nq, int nkv, int max
     return decode_workspace_bytes(batch, nq, (max_ctx_len + ch - 1) / ch);
 }
 
-extern "C" int kvq8_decode_attn(float* out, const float* q, int batch, int nq, const int8_t* k_cache,
-                                const int8_t* v_cache, const float* k_scale, const float* v_scale, int n_blocks,
-                                int kv_bs, int nkv, int hd, const int32_t* block_tables, int max_blocks_per_seq,
-                                const int32_t* ctx_lens, int max_ctx_len, float sm_scale, int chunk,
-                                void* workspace, size_t workspace_bytes, void* stream) {
+// Decode without a caller workspace: the chunk partials go to `scratch`, a
+// library-owned device array (each device holds its own copy while the
+// process runs).  Its device address is looked up once per device, with that
+// device current; host code uses only that address, never the array's name.
+constexpr size_t kScratchBytes = KVQ8_DECODE_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's address of `scratch` (KVQ8_EINVAL when `stream`
+// belongs to another device, KVQ8_EHIP when the runtime fails).
+int scratch_address(hipStream_t stream, void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KVQ8_EHIP;
+    if (stream) {
+        hipDevice_t sdev = -1;
+        if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return KVQ8_EHIP;
+        if (sdev != dev) return KVQ8_EINVAL;
+    }
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KVQ8_EHIP;
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return KVQ8_OK;
+}
+}  // namespace
+
+// kvq8_decode_attn with its workspace, or (own_scratch) with the library's
+// scratch array.  Every argument is checked before the scratch address is
+// looked up or anything is launched.
+static int decode8(float* out, const float* q, int batch, int nq, const int8_t* k_cache, const int8_t* v_cache,
+                   const float* k_scale, const float* v_scale, int n_blocks, int kv_bs, int nkv, int hd,
+                   const int32_t* block_tables, int max_blocks_per_seq, const int32_t* ctx_lens, int max_ctx_len,
+                   float sm_scale, int chunk, void* workspace, size_t workspace_bytes, void* stream,
+                   bool own_scratch) {
     if (!decode_shape_ok(batch, nq, nkv, hd, kv_bs) || n_blocks < 1 || max_blocks_per_seq < 1) return KVQ8_ESHAPE;
     if (!rows_fit_u32(n_blocks, kv_bs, nkv)) return KVQ8_ESHAPE;
     if (max_ctx_len < 0 || !score_scale_ok(sm_scale)) return KVQ8_EINVAL;
@@ -94,7 +136,14 @@ extern "C" int kvq8_decode_attn(float* out, const float* q, int batch, int nq, c
         return KVQ8_EINVAL;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return KVQ8_EINVAL;
     const size_t need = kvq8_decode_workspace_size(batch, nq, nkv, max_ctx_len, chunk);
-    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return KVQ8_EWORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (own_scratch) {
+        if (need > kScratchBytes) return KVQ8_EWORKSPACE;
+        const int st = scratch_address(s, &workspace);
+        if (st != KVQ8_OK) return st;
+    } else if (!workspace || workspace_bytes < need || !aligned16(workspace)) {
+        return KVQ8_EWORKSPACE;
+    }
 
     DecodeArgs a = {};
     a.q = q;
@@ -111,7 +160,26 @@ extern "C" int kvq8_decode_attn(float* out, const float* q, int batch, int nq, c
     a.tiles_per_wave = ch / kChunkUnit;
     a.score_scale = score_scale(sm_scale) * kLog2e;
     bind_workspace(a, workspace);
-    return launch_decode(a, out, static_cast<hipStream_t>(stream));
+    return launch_decode(a, out, s);
+}
+
+extern "C" int kvq8_decode_attn(float* out, const float* q, int batch, int nq, const int8_t* k_cache,
+                                const int8_t* v_cache, const float* k_scale, const float* v_scale, int n_blocks,
+                                int kv_bs, int nkv, int hd, const int32_t* block_tables, int max_blocks_per_seq,
+                                const int32_t* ctx_lens, int max_ctx_len, float sm_scale, int chunk,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    return decode8(out, q, batch, nq, k_cache, v_cache, k_scale, v_scale, n_blocks, kv_bs, nkv, hd, block_tables,
+                   max_blocks_per_seq, ctx_lens, max_ctx_len, sm_scale, chunk, workspace, workspace_bytes, stream,
+                   false);
+}
+
+extern "C" int kvq8_decode_attn_noalloc(float* out, const float* q, int batch, int nq, const int8_t* k_cache,
+                                        const int8_t* v_cache, const float* k_scale, const float* v_scale,
+                                        int n_blocks, int kv_bs, int nkv, int hd, const int32_t* block_tables,
+                                        int max_blocks_per_seq, const int32_t* ctx_lens, int max_ctx_len,
+                                        float sm_scale, int chunk, void* stream) {
+    return decode8(out, q, batch, nq, k_cache, v_cache, k_scale, v_scale, n_blocks, kv_bs, nkv, hd, block_tables,
+                   max_blocks_per_seq, ctx_lens, max_ctx_len, sm_scale, chunk, nullptr, 0, stream, true);
 }
 
 extern "C" int kvq8_append_decode_attn(float* out, const float* q, int batch, int nq, const void* k_new,

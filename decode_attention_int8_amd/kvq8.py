@@ -35,6 +35,8 @@ _SIGNATURES = {
     "kvq8_decode_workspace_size": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int]),
     "kvq8_decode_attn": (_c_int, [_p, _p, _c_int, _c_int, _p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int, _p,
                                   _c_int, _p, _c_int, _f, _c_int, _p, _c_size, _p]),
+    "kvq8_decode_attn_noalloc": (_c_int, [_p, _p, _c_int, _c_int, _p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int,
+                                          _p, _c_int, _p, _c_int, _f, _c_int, _p]),
     "kvq8_append_decode_attn": (_c_int, [_p, _p, _c_int, _c_int, _p, _p, _c_int, _p, _p, _p, _p, _c_int, _c_int,
                                          _c_int, _c_int, _p, _c_int, _p, _c_int, _f, _c_int, _p, _c_size, _p]),
     "kvq8_quantize_q": (_c_int, [_p, _p, _p, _c_int, _c_int, _p]),
@@ -250,6 +252,27 @@ def kvq8_decode_attn(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, c
         _ptr(ctx_lens, torch.int32, "ctx_lens"), max_ctx_len, _scale(sm_scale), chunk,
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
     _check(st, "kvq8_decode_attn")
+    return out
+
+
+def kvq8_decode_attn_noalloc(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, ctx_lens, max_ctx_len: int,
+                             sm_scale: float | None = None, chunk: int = 0, stream=None):
+    """kvq8_decode_attn without a workspace: the library keeps the chunk
+    partials in its own device array (KVQ8_DECODE_SCRATCH_BYTES per device),
+    so the call allocates nothing.  Calls that overlap on one device race on
+    that array; order them on one stream."""
+    n_blocks, kv_bs, nkv, hd = _int8_pool(k_cache, v_cache, k_scale, v_scale)
+    _query(out, q, hd)
+    B, nq, _ = q.shape
+    _tables(block_tables, ctx_lens, B)
+    _same_device(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, ctx_lens)
+    st = lib().kvq8_decode_attn_noalloc(
+        _ptr(out, torch.float32, "out"), _ptr(q, torch.float32, "q"), B, nq,
+        _ptr(k_cache, torch.int8, "k_cache"), _ptr(v_cache, torch.int8, "v_cache"),
+        _ptr(k_scale, torch.float32, "k_scale"), _ptr(v_scale, torch.float32, "v_scale"),
+        n_blocks, kv_bs, nkv, hd, _ptr(block_tables, torch.int32, "block_tables"), block_tables.shape[1],
+        _ptr(ctx_lens, torch.int32, "ctx_lens"), max_ctx_len, _scale(sm_scale), chunk, _stream(stream))
+    _check(st, "kvq8_decode_attn_noalloc")
     return out
 
 

@@ -176,6 +176,37 @@ int kvq8_decode_attn(float* out, const float* q, int batch, int nq,
                      int chunk, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * kvq8_decode_attn_noalloc -- kvq8_decode_attn for callers that cannot
+ * allocate device memory or pass a workspace: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.
+ *
+ * Same arguments, computation and results as kvq8_decode_attn (bit for bit,
+ * with the same chunk), without `workspace` and `workspace_bytes`: the chunk
+ * partials go to a library-owned device array of KVQ8_DECODE_SCRATCH_BYTES
+ * (16 MiB) that every device the library runs on holds until the process
+ * ends.  Its address is looked up on the first call on each device (the
+ * current device); the call allocates nothing and frees nothing.
+ *
+ * Limits and errors: sizes whose kvq8_decode_workspace_size exceeds
+ * KVQ8_DECODE_SCRATCH_BYTES return KVQ8_EWORKSPACE (nothing launched);
+ * a `stream` that belongs to a device other than the current one returns
+ * KVQ8_EINVAL; other errors as for kvq8_decode_attn.  All calls on one
+ * device share that device's array and nothing needs clearing between them
+ * (each call writes every partial it reads), but calls whose executions
+ * overlap on one device -- on different streams, or in different threads
+ * without stream ordering -- race on it: order them on one stream.
+ */
+#define KVQ8_DECODE_SCRATCH_BYTES ((size_t)16 << 20)
+
+int kvq8_decode_attn_noalloc(float* out, const float* q, int batch, int nq,
+                             const int8_t* k_cache, const int8_t* v_cache,
+                             const float* k_scale, const float* v_scale,
+                             int n_blocks, int kv_bs, int nkv, int hd,
+                             const int32_t* block_tables, int max_blocks_per_seq,
+                             const int32_t* ctx_lens, int max_ctx_len, float sm_scale,
+                             int chunk, void* stream);
+
+/*
  * kvq8_append_decode_attn -- one decode step of a layer: the write path for
  * each sequence's newest token, then decode attention over its whole
  * context, in one pass over the cache ([P2] Sec. 2 write path followed by

@@ -17,12 +17,12 @@ OK, EINVAL, ESHAPE, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(kvq[48]_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(kvq[248]_\w+)\s*\(", text, flags=re.M)))
 
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 24, names
     lib = K.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -342,3 +342,22 @@ def test_binding_checks_two_bit_pools():
     kn = z(5, nkv, 128)
     with pytest.raises(ValueError, match="slots"):
         K.kvq2_quantize_append(*p2, kn, kn, ln)
+
+
+def test_noalloc_decode_validation():
+    """kvq8_decode_attn_noalloc checks its arguments as kvq8_decode_attn does
+    and rejects sizes whose partials exceed the library's scratch array
+    (KVQ8_DECODE_SCRATCH_BYTES, 16 MiB) before touching the device."""
+    lib = K.lib()
+    limit = 16 << 20
+
+    def call(batch=2, nq=16, nkv=8, max_ctx=512, chunk=0, sm=0.088, q=_fake(), hd=128):
+        return lib.kvq8_decode_attn_noalloc(_fake(), q, batch, nq, _fake(), _fake(), _fake(), _fake(), 64 << 10,
+                                            16, nkv, hd, _fake(), 4096, _fake(), max_ctx, sm, chunk, None)
+    assert call(hd=64) == ESHAPE
+    assert call(chunk=100) == ESHAPE
+    assert call(q=None) == EINVAL
+    assert call(sm=float("nan")) == EINVAL
+    assert call(batch=0) == OK
+    assert K.kvq8_decode_workspace_size(64, 64, 8, 65536, 0) > limit
+    assert call(batch=64, nq=64, max_ctx=65536) == EWORKSPACE
