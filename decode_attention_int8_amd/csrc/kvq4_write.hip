@@ -171,8 +171,10 @@ __global__ __launch_bounds__(256) void kvq4_requantize_q8_kernel(
         const int tok = div_n(tr, nkv);
         // an invalid source reads slot 0 (in bounds) and is not stored
         const long sv = (s8[k] >= 0 && s8[k] < n_slots8) ? s8[k] : 0;
-        const size_t r8 = (size_t)sv * nkv.n + (size_t)(tr - tok * nkv.n);
-        c[k] = *reinterpret_cast<const uint2*>(((row & 1) ? vc8 : kc8) + r8 * kHD + 8 * l16);
+        const int kh = tr - tok * nkv.n;
+        const size_t r8 = (size_t)sv * nkv.n + (size_t)kh;
+        const size_t c8 = (size_t)sv * nkv.n + (size_t)q8_col(kh, sv, q8_rot_group(nkv.n));
+        c[k] = *reinterpret_cast<const uint2*>(((row & 1) ? vc8 : kc8) + c8 * kHD + 8 * l16);
         step[k] = ((row & 1) ? vs8 : ks8)[r8];
     }
 #pragma unroll

@@ -23,8 +23,10 @@ __global__ __launch_bounds__(256) void kvq8_quantize_append_kernel(
     long n_slots, DivN nkv, const void* __restrict__ k_new, const void* __restrict__ v_new,
     int n_rows, const int32_t* __restrict__ slots) {
     const int l8 = threadIdx.x & 7;
+    const int p = q8_rot_group(nkv.n);
     float x[kRowsPerGroup][16];
     long dst[kRowsPerGroup];     // destination row (slot * nkv + head), -1 to skip
+    long cdst[kRowsPerGroup];    // its code row (slot * nkv + column)
     // rows past the end load the last row again and store nothing; indices
     // fit in 32 bits (the host checks the row count)
 #pragma unroll
@@ -35,7 +37,9 @@ __global__ __launch_bounds__(256) void kvq8_quantize_append_kernel(
         const int tok = div_n(tr, nkv);
         load_new16<DT>((rc & 1) ? v_new : k_new, (size_t)tr * kHD + 16 * l8, x[k]);
         const long slot = slots[tok];
-        dst[k] = (row < n_rows && slot >= 0 && slot < n_slots) ? slot * nkv.n + (tr - tok * nkv.n) : -1;
+        const int kh = tr - tok * nkv.n;
+        dst[k] = (row < n_rows && slot >= 0 && slot < n_slots) ? slot * nkv.n + kh : -1;
+        cdst[k] = slot * nkv.n + q8_col(kh, slot, p);
     }
 #pragma unroll
     for (int k = 0; k < kRowsPerGroup; ++k) {
@@ -44,7 +48,7 @@ __global__ __launch_bounds__(256) void kvq8_quantize_append_kernel(
         quantize_row8x16(x[k], codes, d);         // every lane of the row takes part (DPP)
         if (dst[k] < 0) continue;                  // uniform per 8-lane row
         const int kind = (threadIdx.x >> 3) & 1;   // rows alternate K, V (k * 32 is even)
-        *reinterpret_cast<uint4*>((kind ? vc : kc) + (size_t)dst[k] * kHD + 16 * l8) = codes;
+        *reinterpret_cast<uint4*>((kind ? vc : kc) + (size_t)cdst[k] * kHD + 16 * l8) = codes;
         if (l8 == 0) (kind ? vs : ks)[dst[k]] = d;
     }
 }

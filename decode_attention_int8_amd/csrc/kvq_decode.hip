@@ -31,7 +31,7 @@ __global__ __launch_bounds__(kWGThreads) void kvq8_qk_partials_kernel(DecodeArgs
     const int base = (grp * kWaves + wave) * kTile;
     const int32_t* btb = a.r8.bt + (size_t)b * a.r8.max_blocks;
     const int raw = mtile_raw(a.r8, btb, base, a.log2_bs, lane);
-    const LaneOff lo = lane_offsets(a, lane);
+    const LaneOff lo = lane_offsets(a, lane, kh);
     MTile T;
     mtile_issue<BS8, kIssueKeys>(a, raw, base, kh, lane, lo, T);
     quantize_q4(qx, G, qsm);

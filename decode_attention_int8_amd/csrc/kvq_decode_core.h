@@ -101,13 +101,27 @@ __device__ __host__ __forceinline__ int pair_stride(int n_chunks, int batch) {
     return batch > 1 ? (n_chunks | 1) : n_chunks;
 }
 
-__device__ __forceinline__ int effective_len(const Region& r, int b, int log2_bs) {
-    if (r.max_chunks == 0) return 0;
-    long L = r.lens[b];
+// A sequence's length clamped to [0, min(max_len, max_blocks * kv_bs)]:
+// from its raw value, and from the lengths array.
+__device__ __forceinline__ int clamp_len(const Region& r, int raw, int log2_bs) {
+    long L = raw;
     const long cap = (long)r.max_blocks << log2_bs;
     if (L > r.max_len) L = r.max_len;
     if (L > cap) L = cap;
     return L < 0 ? 0 : (int)L;
+}
+
+__device__ __forceinline__ int effective_len(const Region& r, int b, int log2_bs) {
+    if (r.max_chunks == 0) return 0;
+    return clamp_len(r, r.lens[b], log2_bs);
+}
+
+// The same, also giving the length as read (0 for an empty region).
+__device__ __forceinline__ int effective_len(const Region& r, int b, int log2_bs, int& raw) {
+    raw = 0;
+    if (r.max_chunks == 0) return 0;
+    raw = r.lens[b];
+    return clamp_len(r, raw, log2_bs);
 }
 
 // ----------------------------------------------------------------------------

@@ -144,7 +144,7 @@ __global__ __launch_bounds__(kWGThreads, 2) void kvq4_decode_mfma_kernel(Args a)
         if constexpr (HAS2)
             group_walk<BS8, MTile2>(a, reg, btb, raw, first, L, n_tiles, qx, G, b, kh, c, lane, wave, sm);
     } else {
-        const LaneOff lo = lane_offsets(a, lane);
+        const LaneOff lo = lane_offsets(a, lane, kh);
         MTile A, B;
         mtile_issue<BS8, kIssueKeys | kIssueSteps>(a, raw, first, kh, lane, lo, A);
         raw = mtile_raw(reg, btb, first + kChunkUnit, a.log2_bs, lane);

@@ -111,20 +111,32 @@ __device__ __forceinline__ int mtile_raw(const Region& r, const int32_t* __restr
     return btb[min((base + lane) >> log2_bs, r.max_blocks - 1)];
 }
 
-// Lane parts of the load addresses (bytes), fixed for the whole kernel.
+// Lane parts of the load addresses (bytes from the start of the token
+// group's first slot row), fixed for the whole kernel: the key row of token
+// 16v+m, bytes 16g.., and the value rows of tokens 16v+4g+e, bytes 8m.., each
+// at the column where kv-head kh is stored in that token's slot (the pool's
+// storage order, q8_col: a token's slot index modulo 8 is its lane's token
+// index modulo 8, since token groups start on block boundaries).
 struct LaneOff {
-    uint32_t k;        // key row of token 16v+m, bytes 16g..
-    uint32_t v[4];     // value rows of tokens 16v+4g+e, bytes 8m..
+    uint32_t k;
+    uint32_t v[4];
+    uint32_t kc;       // the key column alone (bytes), for 8-slot blocks
+    uint32_t vc[4];
 };
 
-__device__ __forceinline__ LaneOff lane_offsets(const DecodeArgs& a, int lane) {
+__device__ __forceinline__ LaneOff lane_offsets(const DecodeArgs& a, int lane, int kh) {
     const int g = lane >> 4;
     const int m = lane & 15;
-    const uint32_t row = (uint32_t)a.nkv * kHD;        // bytes between consecutive slots of one head
+    const uint32_t row = (uint32_t)a.nkv * kHD;        // bytes between consecutive slots
+    const int p = q8_rot_group(a.nkv);
     LaneOff o;
-    o.k = (uint32_t)m * row + 16 * g;
+    o.kc = (uint32_t)q8_col(kh, m, p) * kHD;
+    o.k = (uint32_t)m * row + 16 * g + o.kc;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o.v[e] = (uint32_t)(4 * g + e) * row + 8 * m;
+    for (int e = 0; e < 4; ++e) {
+        o.vc[e] = (uint32_t)q8_col(kh, 4 * g + e, p) * kHD;
+        o.v[e] = (uint32_t)(4 * g + e) * row + 8 * m + o.vc[e];
+    }
     return o;
 }
 
@@ -159,12 +171,13 @@ __device__ __forceinline__ void mtile_issue(const DecodeArgs& a, int raw, int ba
         id = T.id;
     }
     const uint32_t nkv = (uint32_t)a.nkv;
-    // row of the first token of 8-token group i (wave-uniform); each value is
+    // slot row (slot * nkv) of the first token of 8-token group i
+    // (wave-uniform; the lane offsets add the head's column); each value is
     // computed where it is used so that a per-lane choice between two groups
     // stays a select and never becomes an indexed array
     auto grp = [&](int i) __attribute__((always_inline)) -> uint32_t {
         const int idi = __builtin_amdgcn_readlane(id, 8 * i);
-        return idi >= 0 ? ((((uint32_t)idi << a.log2_bs) + (((uint32_t)base + 8 * i) & bs_mask)) * nkv + kh) : 0u;
+        return idi >= 0 ? ((((uint32_t)idi << a.log2_bs) + (((uint32_t)base + 8 * i) & bs_mask)) * nkv) : 0u;
     };
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -184,7 +197,7 @@ __device__ __forceinline__ void mtile_issue(const DecodeArgs& a, int raw, int ba
             const uint32_t u0 = grp(2 * v), u1 = grp(2 * v + 1);
             if constexpr (KEYS) {
                 const uint32_t rk = ((m & 8) ? u1 : u0) + (uint32_t)(m & 7) * nkv;
-                const int8_t* p = a.kc + (size_t)rk * kHD + 16 * g;
+                const int8_t* p = a.kc + (size_t)rk * kHD + 16 * g + lo.kc;
                 T.k[v][0] = *reinterpret_cast<const v4u_t*>(p);
                 T.k[v][1] = *reinterpret_cast<const v4u_t*>(p + 64);
             }
@@ -192,8 +205,8 @@ __device__ __forceinline__ void mtile_issue(const DecodeArgs& a, int raw, int ba
                 const uint32_t rv = ((g & 2) ? u1 : u0) + (uint32_t)(4 * (g & 1)) * nkv;
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    T.v[v][e] =
-                        *reinterpret_cast<const v2u_t*>(a.vc + (size_t)(rv + (uint32_t)e * nkv) * kHD + 8 * m);
+                    T.v[v][e] = *reinterpret_cast<const v2u_t*>(a.vc + (size_t)(rv + (uint32_t)e * nkv) * kHD + 8 * m +
+                                                                 lo.vc[e]);
             }
         }
     }

@@ -52,7 +52,8 @@ __global__ __launch_bounds__(kWGThreads, 2) void kvq_decode_mfma_kernel(DecodeAr
     // the query rows do not depend on the length: their loads go out with the
     // table entries, so their quantization never waits on the tile behind them
     const float4 qx = load_q4(a.q + ((size_t)b * a.nq + (size_t)kh * G) * kHD, G);
-    const int L = effective_len(a.r8, b, a.log2_bs);
+    int lraw;       // the length as given (read once, for the fused write path)
+    const int L = effective_len(a.r8, b, a.log2_bs, lraw);
     if (c0 >= L) return;                                       // uniform per workgroup
     const int end = min(L, c0 + chunk_len);
     // tiles of this wave: first, first + 256, ... (at least one, possibly empty)
@@ -61,18 +62,19 @@ __global__ __launch_bounds__(kWGThreads, 2) void kvq_decode_mfma_kernel(DecodeAr
     // fused write path: one wave owns the token at L-1.  A length above the
     // bound (clamped to L) puts the new token past what the call attends:
     // it is then neither written nor attended, and tn = -1 matches no token.
-    const int tn = a.r8.lens[b] == L ? L - 1 : -1;
+    const int tn = lraw == L ? L - 1 : -1;
     const bool has_new = NEWDT >= 0 && tn >= c0 && tn < end && (((tn - c0) >> 6) & (kWaves - 1)) == wave;
-    // then the new token's loads, then the first tile's
+    // then the new token's loads, then the first tile's.  Every wave loads
+    // the new rows (L2 hits after the first): a load in a branch leaves the
+    // compiler's wait before the tile's loads counting it, so that the owner
+    // wave would wait a round trip before issuing its tile.
     float xn[4];
     if constexpr (NEWDT >= 0) {
-        if (has_new) {
-            // lanes 0-31: K row, lanes 32-63: V row, 4 values each
-            load_new4<NEWDT>(lane < 32 ? a.k_new : a.v_new, ((size_t)b * a.nkv + kh) * kHD + 4 * (lane & 31), xn);
-        }
+        // lanes 0-31: K row, lanes 32-63: V row, 4 values each
+        load_new4<NEWDT>(lane < 32 ? a.k_new : a.v_new, ((size_t)b * a.nkv + kh) * kHD + 4 * (lane & 31), xn);
     }
 
-    const LaneOff lo = lane_offsets(a, lane);
+    const LaneOff lo = lane_offsets(a, lane, kh);
     MTile A, B;
     // the same issue order as the walk (keys and steps, the next table entries,
     // values), so that the loop head's wait for those entries is the same
@@ -117,9 +119,11 @@ __global__ __launch_bounds__(kWGThreads, 2) void kvq_decode_mfma_kernel(DecodeAr
                 // tile's own table entry of position tn (-1 outside the pool)
                 const int bid = __builtin_amdgcn_readlane(T.id, tn - base);
                 if (bid >= 0) {
-                    const size_t row = (((size_t)bid << a.log2_bs) + (tn & ((1 << a.log2_bs) - 1))) * a.nkv + kh;
+                    const size_t slot = ((size_t)bid << a.log2_bs) + (tn & ((1 << a.log2_bs) - 1));
+                    const size_t row = slot * a.nkv + kh;
+                    const size_t crow = slot * a.nkv + q8_col(kh, (long)slot, q8_rot_group(a.nkv));
                     const uint32_t w = reinterpret_cast<const uint32_t*>(lane < 32 ? sm.nk : sm.nv)[lane & 31];
-                    *reinterpret_cast<uint32_t*>((lane < 32 ? a.kc_w : a.vc_w) + row * kHD + 4 * (lane & 31)) = w;
+                    *reinterpret_cast<uint32_t*>((lane < 32 ? a.kc_w : a.vc_w) + crow * kHD + 4 * (lane & 31)) = w;
                     if ((lane & 31) == 0) (lane < 32 ? a.ks_w : a.vs_w)[row] = sm.nstep[lane >> 5];
                 }
             }

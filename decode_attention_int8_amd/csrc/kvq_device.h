@@ -148,6 +148,25 @@ __device__ __forceinline__ int div_n(int t, const DivN& d) {
     return (int)(((uint64_t)(uint32_t)t * d.m) >> d.shift);
 }
 
+// Storage order of the int8 pool's code rows.  The codes of a token slot s
+// form one row of nkv x 128 bytes; head kh of that slot sits at column
+//   (kh & ~(P - 1)) | ((kh + s) & (P - 1)),
+// P = the largest power of two dividing nkv, at most 8: within each aligned
+// group of P heads the heads rotate with the slot (P = 1 keeps column kh).
+// A kv-head's rows then spread over every column position of the row
+// instead of one: reading one fixed 128-byte column of many 1 KB rows is
+// slower for some positions than for others on this memory system, and
+// the decode's work items each read one head.  P divides the block size
+// and a tile's token groups start on block boundaries, so the column of a
+// load depends only on the lane.  The steps are not rotated.
+__host__ __device__ __forceinline__ int q8_rot_group(int nkv) {
+    const int p = nkv & -nkv;
+    return p < 8 ? p : 8;
+}
+__host__ __device__ __forceinline__ int q8_col(int kh, long slot, int p) {
+    return (kh & ~(p - 1)) | ((kh + (int)(slot & 7)) & (p - 1));
+}
+
 // IEEE binary16 bits (low 16 bits of v) widened to float (exact)
 __device__ __forceinline__ float half_bits_f(uint32_t v) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)v);

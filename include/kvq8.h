@@ -47,12 +47,19 @@
  *
  * Cache layout (the pages' token-major paged layout, [P2] Sec. 2, [P3] Sec. 2)
  * --------------------------------------------------------------------------
- *  int8 codes   cache[n_blocks][kv_bs][nkv][128]
+ *  int8 codes   cache[n_blocks][kv_bs][nkv * 128]
  *  float steps  scale[n_blocks][kv_bs][nkv]
  *  Token t of sequence b lives in block  block_tables[b][t / kv_bs],  row
- *  t % kv_bs; its kv-head kh codes start at byte kh * 128 of that row.  A
- *  "slot" is block_id * kv_bs + row; with an identity block table the step
- *  array is the pages' [max_seq][nkv] array byte for byte.
+ *  t % kv_bs.  A "slot" is block_id * kv_bs + row; with an identity block
+ *  table the step array is the pages' [max_seq][nkv] array byte for byte.
+ *  The codes of slot s form one row of nkv x 128 bytes, in which kv-head kh
+ *  sits at column  (kh & ~(P - 1)) | ((kh + s) & (P - 1))  (byte offset
+ *  128 times that), P = the largest power of two dividing nkv, at most 8:
+ *  within each aligned group of P heads the heads rotate with the slot
+ *  (nkv odd: column kh, the pages' order).  Every kernel reading or writing
+ *  int8 code rows uses this order; it spreads each head's rows over all
+ *  column positions, which the memory system serves faster than one fixed
+ *  column of many rows.
  */
 #ifndef KVQ8_H
 #define KVQ8_H
@@ -95,7 +102,8 @@ const char* kvq8_version(void);
  * where that product is near a half-integer, the one place the two can
  * round apart.  The int4 and Q4_0 write paths do the same.)
  *
- *   k_cache, v_cache  (device) int8 [n_blocks][kv_bs][nkv][hd], written
+ *   k_cache, v_cache  (device) int8 [n_blocks][kv_bs][nkv * hd] in the storage
+ *                     order above, written
  *   k_scale, v_scale  (device) float [n_blocks][kv_bs][nkv], written
  *   k_new, v_new      (device) [n_tokens][nkv][hd] of `dtype` (KVQ8_F32,
  *                     KVQ8_BF16 or KVQ8_F16), read; 16-byte aligned
@@ -152,7 +160,8 @@ size_t kvq8_decode_workspace_size(int batch, int nq, int nkv, int max_ctx_len, i
  *
  *   out               (device) float [batch][nq][hd], written
  *   q                 (device) float [batch][nq][hd], read; 16-byte aligned
- *   k_cache, v_cache  (device) int8 [n_blocks][kv_bs][nkv][hd], read
+ *   k_cache, v_cache  (device) int8 [n_blocks][kv_bs][nkv * hd] in the storage
+ *                     order above, read
  *   k_scale, v_scale  (device) float [n_blocks][kv_bs][nkv], read
  *   block_tables      (device) int32 [batch][max_blocks_per_seq]
  *   ctx_lens          (device) int32 [batch]

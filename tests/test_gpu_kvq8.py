@@ -10,7 +10,7 @@ import pytest
 
 import workloads as W
 from oracle import kvq8 as O8
-from tests.helpers import SM, Q8Cache, assert_attn_close, dev, fill_sequences, host
+from tests.helpers import SM, Q8Cache, assert_attn_close, dev, fill_sequences, host, q8_columns
 
 pytestmark = pytest.mark.gpu
 
@@ -389,3 +389,46 @@ def test_default_score_scale_is_one_over_sqrt_hd(K):
     K.kvq4_0_decode_attn(o2, q, k4, v4, ks4, vs4, dev(bt), dev(lens), Lm, SM)
     torch.cuda.synchronize()
     assert np.array_equal(host(o1).view(np.uint32), host(o2).view(np.uint32))
+
+
+@pytest.mark.parametrize("nkv,bs", [(1, 16), (2, 8), (3, 16), (4, 16), (6, 8), (8, 16), (8, 8), (12, 16), (16, 16)])
+def test_int8_pool_storage_order(K, nkv, bs):
+    """Where the write path puts a head's codes: head kh of slot s at column
+    (kh & ~(P - 1)) | ((kh + s) & (P - 1)) of the slot's row, P the largest
+    power of two dividing nkv (at most 8).  Each (token, head) row is a
+    constant that names it, so its codes say where it went."""
+    torch = _torch()
+    nb = 3
+    n = nb * bs
+    x = np.zeros((n, nkv, 128), np.float32)
+    for t in range(n):
+        for h in range(nkv):
+            x[t, h] = 1.0 + (t % 8) * 16 + h        # code 127 everywhere, the step names (t, h)
+    c = Q8Cache(nb, bs, nkv)
+    slots = np.arange(n, dtype=np.int32)[::-1].copy()  # token t -> slot n - 1 - t
+    c.append(x, x, slots)
+    torch.cuda.synchronize()
+    c.assert_device_matches_host()
+    raw = host(c.gk).reshape(n, nkv * 128)
+    assert np.all(raw == 127)
+    # steps are not rotated; the codes follow the rule (spelled out for nkv = 8 and 12)
+    cols = q8_columns(n, nkv)
+    if nkv == 8:
+        assert cols[0].tolist() == list(range(8)) and cols[1].tolist() == [1, 2, 3, 4, 5, 6, 7, 0]
+        assert cols[9].tolist() == [1, 2, 3, 4, 5, 6, 7, 0]
+    if nkv == 12:
+        assert cols[1].tolist() == [1, 2, 3, 0, 5, 6, 7, 4, 9, 10, 11, 8]
+    if nkv in (1, 3):
+        assert np.all(cols == np.arange(nkv)[None, :])
+    # a row whose codes differ per head: head h holds code h + 1 in element 0
+    y = np.zeros((n, nkv, 128), np.float32)
+    y[:, :, 1] = 127.0
+    for h in range(nkv):
+        y[:, h, 0] = h + 1
+    c2 = Q8Cache(nb, bs, nkv)
+    c2.append(y, y, slots)
+    torch.cuda.synchronize()
+    raw = host(c2.gk).reshape(n, nkv, 128)
+    for s in range(n):
+        assert raw[s, cols[s], 0].tolist() == [h + 1 for h in range(nkv)], (s, raw[s, :, 0])
+    c2.assert_device_matches_host()
