@@ -124,6 +124,60 @@ __device__ __forceinline__ int effective_len(const Region& r, int b, int log2_bs
     return clamp_len(r, raw, log2_bs);
 }
 
+// Dense work list of a batch decode over one int8 region (at most 64
+// sequences).  The live (sequence, chunk) pairs are numbered so that every
+// sequence's full chunks come first (sequence by sequence) and the partial
+// last chunks after them, longest first; pair j then goes to XCD j % 8 like
+// any pair index.  Each XCD so gets every eighth pair of that order (the
+// same work to within a chunk), the workgroups past the last live pair are
+// all at the end of the grid, and the last workgroups dispatched are the
+// shortest.  Every lane computes it from the lengths (lane i reads sequence
+// i's); the results are wave-uniform.  Returns false for j past the last pair.
+constexpr int kDenseMaxBatch = kWave;
+
+struct DenseItem {
+    int b, c, L, lraw;
+};
+
+__device__ __forceinline__ bool dense_item(const Region& r, int batch, int log2_bs, int chunk_len, int j, int lane,
+                                           DenseItem& it) {
+    int raw = 0, Li = 0;
+    if (lane < batch) {
+        raw = r.lens[lane];
+        Li = clamp_len(r, raw, log2_bs);
+    }
+    const int full = Li / chunk_len;
+    const int rem = Li - full * chunk_len;
+    int pre = full;                                        // inclusive prefix sum over lanes
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int o = __shfl_up(pre, d);
+        if (lane >= d) pre += o;
+    }
+    const int n_full = __builtin_amdgcn_readlane(pre, kWave - 1);
+    int b, c;
+    if (j < n_full) {
+        b = (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(pre > j));
+        c = j - (__builtin_amdgcn_readlane(pre, b) - __builtin_amdgcn_readlane(full, b));
+    } else {
+        const int want = j - n_full;
+        if (want >= (int)__builtin_popcountll(__builtin_amdgcn_ballot_w64(rem > 0))) return false;
+        // rank among the partial chunks: longer first, equal lengths by sequence
+        int rank = 0;
+        for (int k = 0; k < batch; ++k) {
+            const int rk = __builtin_amdgcn_readlane(rem, k);
+            rank += (rk > rem || (rk == rem && k < lane)) ? 1 : 0;
+        }
+        b = (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(rem > 0 && rank == want));
+        c = __builtin_amdgcn_readlane(full, b);
+    }
+    it.b = b;
+    it.c = c;
+    it.L = __builtin_amdgcn_readlane(Li, b);
+    it.lraw = __builtin_amdgcn_readlane(raw, b);
+    return true;
+}
+
 // ----------------------------------------------------------------------------
 // fused write path ([P2] Sec. 2): the new token's K / V rows, quantized by the
 // 8 lanes of a token group (16 values per lane) with exactly the arithmetic of

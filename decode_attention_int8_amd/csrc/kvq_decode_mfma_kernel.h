@@ -9,7 +9,7 @@ namespace kvq {
 // Two workgroups per CU: the walk fits the 256 registers of that budget
 // because a tile's values are issued only after the previous tile's P.V,
 // when its values are dead (one value buffer, two key buffers).
-template <int NEWDT, bool BS8>
+template <int NEWDT, bool BS8, bool DENSE>
 __global__ __launch_bounds__(kWGThreads, 2) void kvq_decode_mfma_kernel(DecodeArgs a) {
     __shared__ MSmem sm;
     // The arguments the prologue needs, read in one batch: left to itself
@@ -34,27 +34,40 @@ __global__ __launch_bounds__(kWGThreads, 2) void kvq_decode_mfma_kernel(DecodeAr
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int G = a.nq / a.nkv;
 
-    // work decode: the nkv workgroups of one (sequence, chunk) share an XCD,
-    // pairs laid out at an odd stride
+    // work decode: the nkv workgroups of one (sequence, chunk) pair share an
+    // XCD (pair p on XCD p % 8).  Batches take the dense pair order of
+    // dense_item; otherwise pairs are laid out at an odd stride.
     const int nct = a.r8.max_chunks;
     const int wg = blockIdx.x;
     const int rest = wg >> 3;
     const int kh = rest % a.nkv;
     const int p = (rest / a.nkv) * 8 + (wg & 7);
-    const int b = p / pair_stride(nct, a.batch);
-    const int c = p - b * pair_stride(nct, a.batch);
-    if (b >= a.batch || c >= nct) return;
     const int chunk_len = a.tiles_per_wave * kChunkUnit;
+    int b, c, raw, L, lraw;     // lraw: the length as given (read once, for the fused write path)
+    float4 qx;
+    if constexpr (DENSE) {
+        DenseItem it;
+        if (!dense_item(a.r8, a.batch, a.log2_bs, chunk_len, p, lane, it)) return;
+        b = it.b;
+        c = it.c;
+        L = it.L;
+        lraw = it.lraw;
+        raw = mtile_raw(a.r8, a.r8.bt + (size_t)b * a.r8.max_blocks, c * chunk_len + wave * kTile, a.log2_bs, lane);
+        qx = load_q4(a.q + ((size_t)b * a.nq + (size_t)kh * G) * kHD, G);
+    } else {
+        b = p / pair_stride(nct, a.batch);
+        c = p - b * pair_stride(nct, a.batch);
+        if (b >= a.batch || c >= nct) return;
+        raw = mtile_raw(a.r8, a.r8.bt + (size_t)b * a.r8.max_blocks, c * chunk_len + wave * kTile, a.log2_bs, lane);
+        // the query rows do not depend on the length: their loads go out with
+        // the table entries, so their quantization never waits on the tile
+        qx = load_q4(a.q + ((size_t)b * a.nq + (size_t)kh * G) * kHD, G);
+        L = effective_len(a.r8, b, a.log2_bs, lraw);
+        if (c * chunk_len >= L) return;                        // uniform per workgroup
+    }
     const int c0 = c * chunk_len;
     const int32_t* btb = a.r8.bt + (size_t)b * a.r8.max_blocks;
     const int first = c0 + wave * kTile;
-    int raw = mtile_raw(a.r8, btb, first, a.log2_bs, lane);
-    // the query rows do not depend on the length: their loads go out with the
-    // table entries, so their quantization never waits on the tile behind them
-    const float4 qx = load_q4(a.q + ((size_t)b * a.nq + (size_t)kh * G) * kHD, G);
-    int lraw;       // the length as given (read once, for the fused write path)
-    const int L = effective_len(a.r8, b, a.log2_bs, lraw);
-    if (c0 >= L) return;                                       // uniform per workgroup
     const int end = min(L, c0 + chunk_len);
     // tiles of this wave: first, first + 256, ... (at least one, possibly empty)
     const int n_tiles = first < end ? (end - first + kChunkUnit - 1) / kChunkUnit : 1;
@@ -163,17 +176,24 @@ __global__ __launch_bounds__(kWGThreads, 2) void kvq_decode_mfma_kernel(DecodeAr
     mwrite_partial(a, sm, st, G, b, kh, c, lane, wave);
 }
 
-template <bool BS8>
+template <bool BS8, bool DENSE>
 inline int launch_mfma_bs(const DecodeArgs& a, int n_wg, int new_dtype, hipStream_t s) {
     const dim3 grid(n_wg), block(kWGThreads);
-    if (new_dtype == KVQ8_F32) return launch((kvq_decode_mfma_kernel<KVQ8_F32, BS8>), grid, block, s, a);
-    if (new_dtype == KVQ8_BF16) return launch((kvq_decode_mfma_kernel<KVQ8_BF16, BS8>), grid, block, s, a);
-    if (new_dtype == KVQ8_F16) return launch((kvq_decode_mfma_kernel<KVQ8_F16, BS8>), grid, block, s, a);
-    return launch((kvq_decode_mfma_kernel<-1, BS8>), grid, block, s, a);
+    if (new_dtype == KVQ8_F32) return launch((kvq_decode_mfma_kernel<KVQ8_F32, BS8, DENSE>), grid, block, s, a);
+    if (new_dtype == KVQ8_BF16) return launch((kvq_decode_mfma_kernel<KVQ8_BF16, BS8, DENSE>), grid, block, s, a);
+    if (new_dtype == KVQ8_F16) return launch((kvq_decode_mfma_kernel<KVQ8_F16, BS8, DENSE>), grid, block, s, a);
+    return launch((kvq_decode_mfma_kernel<-1, BS8, DENSE>), grid, block, s, a);
 }
 
+// Batches of 2 .. 64 sequences take the dense work order (one more memory
+// round trip per workgroup, for the lengths, before its table entries; a
+// single sequence has nothing to balance and keeps that round trip off its
+// critical path).
 inline int launch_mfma(const DecodeArgs& a, int n_wg, int new_dtype, hipStream_t s) {
-    return a.log2_bs < 4 ? launch_mfma_bs<true>(a, n_wg, new_dtype, s) : launch_mfma_bs<false>(a, n_wg, new_dtype, s);
+    const bool dense = a.batch > 1 && a.batch <= kDenseMaxBatch;
+    if (a.log2_bs < 4)
+        return dense ? launch_mfma_bs<true, true>(a, n_wg, new_dtype, s) : launch_mfma_bs<true, false>(a, n_wg, new_dtype, s);
+    return dense ? launch_mfma_bs<false, true>(a, n_wg, new_dtype, s) : launch_mfma_bs<false, false>(a, n_wg, new_dtype, s);
 }
 
 }  // namespace kvq

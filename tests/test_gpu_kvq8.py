@@ -432,3 +432,35 @@ def test_int8_pool_storage_order(K, nkv, bs):
     for s in range(n):
         assert raw[s, cols[s], 0].tolist() == [h + 1 for h in range(nkv)], (s, raw[s, :, 0])
     c2.assert_device_matches_host()
+
+
+@pytest.mark.parametrize("B,chunk", [(2, 256), (17, 512), (64, 256), (65, 256)])
+def test_decode_batches_dense_work_order(K, B, chunk):
+    """Batches of 2 .. 64 sequences number their (sequence, chunk) pairs
+    densely (full chunks first, partial ones longest first); 65 takes the
+    strided order.  Lengths include 0, 1, exact chunk multiples, negative
+    values and values above the bound; every pair must be computed once."""
+    r = W.rng(347, B, chunk)
+    nkv, nq, bs = 2, 4, 16
+    max_ctx = 3 * chunk + 100
+    lens = r.integers(0, max_ctx + 1, size=B).astype(np.int32)
+    lens[0] = 0
+    lens[1] = 1
+    if B > 2:
+        lens[2] = chunk
+        lens[-1] = -3
+    if B > 5:
+        lens[3] = 2 * chunk
+        lens[4] = max_ctx + 500          # clamped to max_ctx
+    cap = np.clip(lens, 0, max_ctx)
+    bt, nb = W.paged_block_tables(r, np.maximum(lens, 0), bs, spare_blocks=1)
+    Lm = int(np.maximum(lens, 0).max())
+    k = W.normal_f32(r, (B, Lm, nkv, 128))
+    v = W.normal_f32(r, (B, Lm, nkv, 128))
+    c = Q8Cache(nb, bs, nkv)
+    fill_sequences(c, bt, np.maximum(lens, 0), k, v)
+    q = W.normal_f32(r, (B, nq, 128))
+    got = _decode(K, c, q, bt, lens, max_ctx, chunk=chunk)
+    ref = O8.decode_attention_q8(q, c.kp, c.ks, c.vp, c.vs, bt, cap, bs, SM)
+    assert_attn_close(got, ref, f"B={B} chunk={chunk}")
+    assert np.all(got[cap == 0] == 0.0)
