@@ -348,7 +348,7 @@ __device__ __forceinline__ void qtile_compute(const DecodeArgs& a, const QTile T
         }
     }
     const float mref = (st.M == -INFINITY) ? 0.0f : st.M;
-    const bool lo_row = m & 1;
+    const uint32_t part_mask = weight_part_mask(m);
     float p[4][4];
 #pragma unroll
     for (int v = 0; v < 4; ++v)
@@ -371,11 +371,7 @@ __device__ __forceinline__ void qtile_compute(const DecodeArgs& a, const QTile T
                 const float w[4] = {p[v][0] * vv.x, p[v][1] * vv.y, p[v][2] * vv.z, p[v][3] * vv.w};
 #pragma unroll
                 for (int pr = 0; pr < 2; ++pr) {
-                    const float h0 = __uint_as_float(__float_as_uint(w[2 * pr]) & 0xFFFFE000u);
-                    const float h1 = __uint_as_float(__float_as_uint(w[2 * pr + 1]) & 0xFFFFE000u);
-                    const uint32_t hi = pack_f16_rtz(h0, h1);
-                    const uint32_t lo = pack_f16(w[2 * pr] - h0, w[2 * pr + 1] - h1);
-                    wop[q2][pr] = lo_row ? lo : hi;
+                    wop[q2][pr] = weight_part_f16x2(w[2 * pr], w[2 * pr + 1], part_mask);
                 }
             }
             A[b] = __builtin_bit_cast(v8h_t, v4u_t{wop[0][0], wop[0][1], wop[1][0], wop[1][1]});

@@ -20,8 +20,8 @@
 //
 // P.V: one v_mfma_f32_16x16x32_f16 per (pair of token groups, d-slice s):
 //   A = weights  A[c][k]: row c = head c/2, the f16 high part of
-//                p * vstep for even c and the f16 rounding of the remainder
-//                for odd c (together exact to 2^-21 relative)
+//                p * vstep for even c and the remainder below it (rounded
+//                toward zero) for odd c (together within 2^-21 relative)
 //   B = values   B[k][m] = V[token k][8m + s] as f16 (exact for int8)
 // The weights are exactly the lane's own scores' tokens, so no data moves
 // between the two products.  Lane (g, m) accumulates rows 4g..4g+3 = heads
@@ -77,13 +77,24 @@ struct MSmem {
 typedef float v2f_t __attribute__((ext_vector_type(2)));
 typedef _Float16 v2h_t __attribute__((ext_vector_type(2)));
 
-// two floats to f16, round to nearest even, `lo` in the low half
-__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f_t{lo, hi}, v2h_t));
-}
 // two floats to f16, round toward zero (used where the values are exact)
 __device__ __forceinline__ uint32_t pack_f16_rtz(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+}
+
+// The value weights enter the f16 products in two parts: rows with even
+// index take the high part of each weight (its f16 rounding toward zero: the
+// top 11 significant bits), rows with odd index the f16 of the remainder
+// below it (rounded toward zero: within 2^-10 of the remainder, so the two
+// together are within 2^-21 of the weight).  part_mask is all-zero for the
+// even rows and keeps the top 11 significant bits for the odd ones, so one
+// masked subtraction per weight gives either part and the conversion is the
+// same instruction for both.
+__device__ __forceinline__ uint32_t weight_part_mask(int m) { return (m & 1) ? 0xFFFFE000u : 0u; }
+
+__device__ __forceinline__ uint32_t weight_part_f16x2(float w0, float w1, uint32_t part_mask) {
+    return pack_f16_rtz(w0 - __uint_as_float(__float_as_uint(w0) & part_mask),
+                        w1 - __uint_as_float(__float_as_uint(w1) & part_mask));
 }
 
 __device__ __forceinline__ float bperm_f(float v, int src_lane) {
@@ -283,8 +294,8 @@ __device__ __forceinline__ uint32_t codes_f16x2(uint32_t wa, uint32_t wb, int by
 // One tile.
 //
 // The value weights p * vstep enter the f16 product as a high part (11
-// significant bits, exact in f16) and the f16 rounding of the remainder:
-// 2^-21 relative.  To keep them in f16 range they carry a wave-wide power of
+// significant bits, exact in f16) and the remainder below it rounded toward
+// zero: within 2^-21 relative.  To keep them in f16 range they carry a wave-wide power of
 // two 2^E with max(vstep) * 2^E < 2^15; E only ever decreases, and the
 // accumulator holds its value times 2^E.
 struct NoHook {
@@ -367,7 +378,7 @@ __device__ __forceinline__ void mtile_compute(const DecodeArgs& a, const MTile T
     // a head whose tokens so far are all masked keeps M = -inf: its weights
     // must come out 0, not exp2(-inf - -inf)
     const float mref = (st.M == -INFINITY) ? 0.0f : st.M;
-    const bool lo_row = m & 1;
+    const uint32_t part_mask = weight_part_mask(m);
     uint32_t wop[4][2];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -382,11 +393,7 @@ __device__ __forceinline__ void mtile_compute(const DecodeArgs& a, const MTile T
         }
 #pragma unroll
         for (int pr = 0; pr < 2; ++pr) {
-            const float h0 = __uint_as_float(__float_as_uint(w[2 * pr]) & 0xFFFFE000u);
-            const float h1 = __uint_as_float(__float_as_uint(w[2 * pr + 1]) & 0xFFFFE000u);
-            const uint32_t hi = pack_f16_rtz(h0, h1);
-            const uint32_t lo = pack_f16(w[2 * pr] - h0, w[2 * pr + 1] - h1);
-            wop[v][pr] = lo_row ? lo : hi;
+            wop[v][pr] = weight_part_f16x2(w[2 * pr], w[2 * pr + 1], part_mask);
         }
     }
 #pragma unroll

@@ -18,7 +18,7 @@
 //   word of lane m holds d = 4m .. 4m+3 of both code groups and slice s
 //   covers d = 64(s/4) + 4m + (s%4): group s/4 for every column.  Its A
 //   operand is the weights p * vscale of that group (f16 high part or
-//   rounded remainder, times 2^E; row c = (head c/2, part c%2)) and B is
+//   remainder below it, times 2^E; row c = (head c/2, part c%2)) and B is
 //   c - z of that group as f16 (exact small integers).  Each lane's softmax
 //   values are exactly the weights it supplies.
 #pragma once
@@ -228,7 +228,7 @@ __device__ __forceinline__ void mtile4_compute(const DecodeArgs& a, const MTile4
         }
     }
     const float mref = (st.M == -INFINITY) ? 0.0f : st.M;
-    const bool lo_row = m & 1;
+    const uint32_t part_mask = weight_part_mask(m);
     float p[4][4];
 #pragma unroll
     for (int v = 0; v < 4; ++v)
@@ -252,11 +252,7 @@ __device__ __forceinline__ void mtile4_compute(const DecodeArgs& a, const MTile4
                 const float w[4] = {p[v][0] * vv.x, p[v][1] * vv.y, p[v][2] * vv.z, p[v][3] * vv.w};
 #pragma unroll
                 for (int pr = 0; pr < 2; ++pr) {
-                    const float h0 = __uint_as_float(__float_as_uint(w[2 * pr]) & 0xFFFFE000u);
-                    const float h1 = __uint_as_float(__float_as_uint(w[2 * pr + 1]) & 0xFFFFE000u);
-                    const uint32_t hi = pack_f16_rtz(h0, h1);
-                    const uint32_t lo = pack_f16(w[2 * pr] - h0, w[2 * pr + 1] - h1);
-                    wop[q2][pr] = lo_row ? lo : hi;
+                    wop[q2][pr] = weight_part_f16x2(w[2 * pr], w[2 * pr + 1], part_mask);
                 }
                 const uint2 zz = *reinterpret_cast<const uint2*>(&sm.v4c[wave][G2][16 * v + 4 * g]);
                 zc[G2][2 * q2] = zz.x;

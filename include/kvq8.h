@@ -152,8 +152,9 @@ size_t kvq8_decode_workspace_size(int batch, int nq, int nkv, int max_ctx_len, i
  * own running max and sum (online softmax per chunk); a second kernel merges
  * the chunks and divides by the total sum.  The integer dot products and the
  * value accumulation run on the matrix cores (each weight is carried as an
- * f16 high part of 11 significant bits plus the f16 rounding of the
- * remainder, together exact to 2^-21 relative); accumulation is float32 and the result
+ * f16 high part of 11 significant bits plus the f16 of the remainder,
+ * rounded toward zero, together within 2^-21 relative); accumulation is
+ * float32 and the result
  * matches the exact float64 value of the definition to about 1e-5 relative.
  * A sequence with context length 0 gets a zero output row.  The pool may
  * hold at most 2^32 - 1 rows (n_blocks * kv_bs * nkv), else KVQ8_ESHAPE.
