@@ -58,9 +58,18 @@ __device__ __forceinline__ void q40_load8(const void* base, size_t elem_off, flo
     }
 }
 
-// Codes of the 8 values a lane holds (elements 8 l16 .. 8 l16 + 7 of a row
-// spread over 16 lanes, so lanes 4k .. 4k+3 hold block k), one byte each,
-// and the block's step.
+// A row of 128 values is spread over 16 lanes: lane l16 = 4r + k holds the
+// 8 values 32k + 8r .. 32k + 8r + 7, so lane k of every quad holds block k
+// and the four lanes of block k sit 4 apart.  Both byte layouts are then
+// built inside quads (key bytes pair element j with j + 64: lanes k and
+// k ^ 2; value words gather one byte from each block: a 4 x 4 byte transpose
+// in the quad) and the block extremes are two row rotations.
+//
+// Codes of a lane's 8 values, one byte each, and its block's step.  The code
+// is floor(x / step + 8.5) clamped to 15: rint(x * rcp(step)) + 8 where
+// x * rcp(step) is not within 2^-11 of a half-integer; elsewhere (about 0.1%
+// of the values, or a quotient that is not finite) the lane divides.  A zero
+// block has step +0 and codes 8.
 __device__ __forceinline__ void q40_quantize8(const float (&x)[8], uint32_t& lo, uint32_t& hi, float& step) {
 #pragma clang fp contract(off)
     float mx = x[0], mn = x[0];
@@ -69,87 +78,106 @@ __device__ __forceinline__ void q40_quantize8(const float (&x)[8], uint32_t& lo,
         mx = fmaxf(mx, x[e]);
         mn = fminf(mn, x[e]);
     }
-    mx = fmaxf(mx, dpp_f<kDppXor1>(mx));
-    mx = fmaxf(mx, dpp_f<kDppXor2>(mx));
-    mn = fminf(mn, dpp_f<kDppXor1>(mn));
-    mn = fminf(mn, dpp_f<kDppXor2>(mn));
+    // the block's four lanes: 4 and 8 apart in the 16-lane row
+    mx = fmaxf(mx, dpp_f<kDppRowRor8>(mx));
+    mn = fminf(mn, dpp_f<kDppRowRor8>(mn));
+    mx = fmaxf(mx, dpp_f<kDppRowRor4>(mx));
+    mn = fminf(mn, dpp_f<kDppRowRor4>(mn));
     const float m = (-mn >= mx) ? mn : mx;           // negative extreme wins a tie
-    step = (m == 0.0f) ? 0.0f : m * -0.125f;         // exact: a power-of-two division
+    const bool zero = m == 0.0f;
+    step = zero ? 0.0f : m * -0.125f;                // exact: a power-of-two division
     const float rs = __builtin_amdgcn_rcpf(step);
-    uint32_t w[2] = {0u, 0u};
+    float c[8];
+    bool slow[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        float c = 8.0f;
-        if (step != 0.0f) {
-            // floor(x / step + 8.5), the quotient computed only near a
-            // half-integer (|x / step| <= 8); elsewhere it is rint(q) + 8
-            const float q = x[e] * rs;
-            const float rq = rintf(q);
-            c = rq + 8.0f;
-            if (near_half_small(q, rq)) c = floorf(x[e] / step + 8.5f);
-            c = fminf(c, 15.0f);
-        }
-        w[e >> 2] |= (uint32_t)(int)c << (8 * (e & 3));
+        const float q = x[e] * rs;                   // |x / step| <= 8
+        const float rq = rintf(q);
+        slow[e] = !zero && near_half_small(q, rq);
+        c[e] = fminf(rq + 8.0f, 15.0f);
     }
-    lo = w[0];
-    hi = w[1];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        if (__builtin_amdgcn_ballot_w64(slow[e]) != 0) {      // rare: one wave-uniform test per value
+            const float cd = fminf(floorf(x[e] / step + 8.5f), 15.0f);
+            c[e] = slow[e] ? cd : c[e];
+        }
+    }
+    uint32_t w[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[e >> 2] |= (uint32_t)(int)c[e] << (8 * (e & 3));
+    lo = zero ? 0x08080808u : w[0];
+    hi = zero ? 0x08080808u : w[1];
 }
 
-// One (token, kv-head, K-or-V) row per 16 lanes, 4 rows per 16-lane group.
-// Codes go through LDS (one byte each) and come out in the row's layout:
-// lane l16 writes bytes 4 l16 .. 4 l16 + 3.
+// Quad transpose of value bytes: lane q of a quad holds W = [P0 P1 P2 P3]
+// (the packed pairs of its block); it returns [byte q of W from quad lanes
+// 0, 1, 2, 3], the value row word that takes one byte from every block.
+__device__ __forceinline__ uint32_t q40_value_word(uint32_t W, int q) {
+    const uint32_t q1 = (uint32_t)dpp_i<kDppQuadRot1>((int)W);   // lane q + 1
+    const uint32_t q2 = (uint32_t)dpp_i<kDppXor2>((int)W);       // lane q + 2
+    const uint32_t q3 = (uint32_t)dpp_i<kDppQuadRot3>((int)W);   // lane q + 3
+    // Z byte j = byte q of lane q + j's word
+    const uint32_t sel_lo = (uint32_t)q | ((uint32_t)(4 + q) << 8) | 0x0C0C0000u;
+    const uint32_t sel_hi = 0x00000C0Cu | ((uint32_t)q << 16) | ((uint32_t)(4 + q) << 24);
+    const uint32_t Z = __builtin_amdgcn_perm(q1, W, sel_lo) | __builtin_amdgcn_perm(q3, q2, sel_hi);
+    // byte t must come from lane t = q + j: rotate left by q bytes
+    return __builtin_amdgcn_alignbit(Z, Z, (32u - 8u * (uint32_t)q) & 31u);
+}
+
+// One (token, kv-head, K-or-V) row per 16 lanes, 4 rows per 16-lane group;
+// a wave quantizes only key rows or only value rows (kind = wave & 1).
 template <int DT>
 __global__ __launch_bounds__(256) void kvq4_0_quantize_append_kernel(
     uint8_t* __restrict__ kc, uint8_t* __restrict__ vc, float* __restrict__ ks, float* __restrict__ vs,
     long n_slots, DivN nkv, const void* __restrict__ k_new, const void* __restrict__ v_new, int n_rows,
     const int32_t* __restrict__ slots) {
-    __shared__ uint8_t codes[kQ40RowsPerBlock][kHD];
     const int l16 = threadIdx.x & 15;
-    const int grp = threadIdx.x >> 4;
+    const int qk = l16 & 3;                        // block of the lane's values
+    const int qr = l16 >> 2;                       // their place in the block
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int kind = wave & 1;                     // 0: key rows, 1: value rows
+    const int g4 = (threadIdx.x >> 4) & 3;         // 16-lane group in the wave
     float x[kQ40RowsPerGroup][8];
     long dst[kQ40RowsPerGroup];    // destination row (slot * nkv + head), -1 to skip
     // rows past the end load the last row again and store nothing; indices
     // fit in 32 bits (the host checks the row count)
 #pragma unroll
     for (int k = 0; k < kQ40RowsPerGroup; ++k) {
-        const int row = (int)blockIdx.x * kQ40RowsPerBlock + k * 16 + grp;
-        const int rc = min(row, n_rows - 1);
-        const int tr = rc >> 1;                      // token * nkv + kv-head
+        const int pair = (int)blockIdx.x * (kQ40RowsPerBlock / 2) + (wave >> 1) * 16 + g4 * 4 + k;
+        const int row = 2 * pair + kind;
+        const int tr = min(row, n_rows - 1) >> 1;  // token * nkv + kv-head
         const int tok = div_n(tr, nkv);
-        q40_load8<DT>((rc & 1) ? v_new : k_new, (size_t)tr * kHD + 8 * l16, x[k]);
+        q40_load8<DT>(kind ? v_new : k_new, (size_t)tr * kHD + 32 * qk + 8 * qr, x[k]);
         const long slot = slots[tok];
         dst[k] = (row < n_rows && slot >= 0 && slot < n_slots) ? slot * nkv.n + (tr - tok * nkv.n) : -1;
     }
-    float step[kQ40RowsPerGroup];
 #pragma unroll
     for (int k = 0; k < kQ40RowsPerGroup; ++k) {
         uint32_t lo, hi;
-        q40_quantize8(x[k], lo, hi, step[k]);
-        *reinterpret_cast<uint2*>(&codes[k * 16 + grp][8 * l16]) = make_uint2(lo, hi);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < kQ40RowsPerGroup; ++k) {
-        if (dst[k] < 0) continue;                    // uniform per 16-lane row
-        const uint8_t* c = codes[k * 16 + grp];
-        const int kind = grp & 1;                    // rows alternate K, V
-        uint32_t word;
+        float step;
+        q40_quantize8(x[k], lo, hi, step);          // every lane of the row takes part (DPP)
+        uint32_t word, off;
         if (kind == 0) {
-            // key: byte j = code[j] | code[64 + j] << 4
-            const uint32_t a = *reinterpret_cast<const uint32_t*>(c + 4 * l16);
-            const uint32_t b = *reinterpret_cast<const uint32_t*>(c + 64 + 4 * l16);
-            word = a | (b << 4);
+            // key byte j = code[j] | code[64 + j] << 4: blocks k and k + 2
+            // are quad lanes q and q ^ 2; lanes of blocks 0, 1 write the low
+            // 4 bytes of their 8, their partners the high 4
+            const bool low = qk < 2;
+            const uint32_t recv = (uint32_t)dpp_i<kDppXor2>((int)(low ? hi : lo));
+            word = low ? (lo | (recv << 4)) : (recv | (hi << 4));
+            off = 32u * (uint32_t)(qk & 1) + 8u * (uint32_t)qr + (low ? 0u : 4u);
         } else {
-            // value: byte 4m + k = code[32k + 2m] | code[32k + 2m + 1] << 4, m = l16
-            word = 0u;
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                const uint32_t pr = *reinterpret_cast<const uint16_t*>(c + 32 * kb + 2 * l16);
-                word |= ((pr & 0xFu) | ((pr >> 4) & 0xF0u)) << (8 * kb);
-            }
+            // value byte 4m + kb = code[32 kb + 2m] | code[32 kb + 2m + 1] << 4:
+            // the lane's pairs m = 4r .. 4r + 3 of block k, then one byte of
+            // every block per word
+            const uint32_t a = lo | (lo >> 4), b = hi | (hi >> 4);  // bytes 0, 2: the pairs
+            const uint32_t W = __builtin_amdgcn_perm(b, a, 0x06040200u);
+            word = q40_value_word(W, qk);
+            off = 16u * (uint32_t)qr + 4u * (uint32_t)qk;
         }
-        *reinterpret_cast<uint32_t*>((kind ? vc : kc) + (size_t)dst[k] * (kHD / 2) + 4 * l16) = word;
-        if ((l16 & 3) == 0) (kind ? vs : ks)[dst[k] * 4 + (l16 >> 2)] = step[k];
+        if (dst[k] < 0) continue;                    // uniform per 16-lane row
+        *reinterpret_cast<uint32_t*>((kind ? vc : kc) + (size_t)dst[k] * (kHD / 2) + off) = word;
+        if (qr == 0) (kind ? vs : ks)[dst[k] * 4 + qk] = step;
     }
 }
 

@@ -18,6 +18,10 @@ constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7-i inside each 8-lane half row
 constexpr int kDppRowRor8 = 0x128;    // lane i <- lane (i+8) mod 16 inside each 16-lane row
+constexpr int kDppRowRor4 = 0x124;    // rotation of each 16-lane row by 4 lanes (either way: used where
+                                      // only the set of lanes 4 apart matters)
+constexpr int kDppQuadRot1 = 0x39;    // quad_perm [1,2,3,0]: lane q <- lane (q+1) mod 4
+constexpr int kDppQuadRot3 = 0x93;    // quad_perm [3,0,1,2]: lane q <- lane (q+3) mod 4
 
 template <int CTRL>
 __device__ __forceinline__ int dpp_i(int v) {
