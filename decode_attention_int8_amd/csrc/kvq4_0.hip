@@ -140,6 +140,7 @@ __global__ __launch_bounds__(256) void kvq4_0_quantize_append_kernel(
     const int g4 = (threadIdx.x >> 4) & 3;         // 16-lane group in the wave
     float x[kQ40RowsPerGroup][8];
     long dst[kQ40RowsPerGroup];    // destination row (slot * nkv + head), -1 to skip
+    long cdst[kQ40RowsPerGroup];   // its code row (slot * nkv + column, the storage order q8_col)
     // rows past the end load the last row again and store nothing; indices
     // fit in 32 bits (the host checks the row count)
 #pragma unroll
@@ -150,7 +151,9 @@ __global__ __launch_bounds__(256) void kvq4_0_quantize_append_kernel(
         const int tok = div_n(tr, nkv);
         q40_load8<DT>(kind ? v_new : k_new, (size_t)tr * kHD + 32 * qk + 8 * qr, x[k]);
         const long slot = slots[tok];
-        dst[k] = (row < n_rows && slot >= 0 && slot < n_slots) ? slot * nkv.n + (tr - tok * nkv.n) : -1;
+        const int kh = tr - tok * nkv.n;
+        dst[k] = (row < n_rows && slot >= 0 && slot < n_slots) ? slot * nkv.n + kh : -1;
+        cdst[k] = slot * nkv.n + q8_col(kh, slot, q8_rot_group(nkv.n));
     }
 #pragma unroll
     for (int k = 0; k < kQ40RowsPerGroup; ++k) {
@@ -176,7 +179,7 @@ __global__ __launch_bounds__(256) void kvq4_0_quantize_append_kernel(
             off = 16u * (uint32_t)qr + 4u * (uint32_t)qk;
         }
         if (dst[k] < 0) continue;                    // uniform per 16-lane row
-        *reinterpret_cast<uint32_t*>((kind ? vc : kc) + (size_t)dst[k] * (kHD / 2) + off) = word;
+        *reinterpret_cast<uint32_t*>((kind ? vc : kc) + (size_t)cdst[k] * (kHD / 2) + off) = word;
         if (qr == 0) (kind ? vs : ks)[dst[k] * 4 + qk] = step;
     }
 }
@@ -204,16 +207,25 @@ struct QSmem40 : MSmem {
 struct QLaneOff {
     uint32_t k;          // key row of token 16v+m, bytes 16g..
     uint32_t v[4];       // value rows of tokens 16v+4g+e, bytes 4m..
+    uint32_t kc;         // the key column alone (bytes), for 8-slot blocks
+    uint32_t vc[4];
 };
 
-__device__ __forceinline__ QLaneOff q40_lane_offsets(const DecodeArgs& a, int lane) {
+// Each at the column where kv-head kh is stored in that token's slot (the
+// int8 pool's storage order, q8_col, over 64-byte columns).
+__device__ __forceinline__ QLaneOff q40_lane_offsets(const DecodeArgs& a, int lane, int kh) {
     const int g = lane >> 4;
     const int m = lane & 15;
     const uint32_t row = (uint32_t)a.nkv * kQ40RowBytes;
+    const int p = q8_rot_group(a.nkv);
     QLaneOff o;
-    o.k = (uint32_t)m * row + 16 * g;
+    o.kc = (uint32_t)q8_col(kh, m, p) * kQ40RowBytes;
+    o.k = (uint32_t)m * row + 16 * g + o.kc;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o.v[e] = (uint32_t)(4 * g + e) * row + 4 * m;
+    for (int e = 0; e < 4; ++e) {
+        o.vc[e] = (uint32_t)q8_col(kh, 4 * g + e, p) * kQ40RowBytes;
+        o.v[e] = (uint32_t)(4 * g + e) * row + 4 * m + o.vc[e];
+    }
     return o;
 }
 
@@ -237,7 +249,7 @@ __device__ __forceinline__ void qtile_issue(const DecodeArgs& a, int raw, int ba
     const uint32_t nkv = (uint32_t)a.nkv;
     auto grp = [&](int i) __attribute__((always_inline)) -> uint32_t {
         const int idi = __builtin_amdgcn_readlane(id, 8 * i);
-        return idi >= 0 ? ((((uint32_t)idi << a.log2_bs) + (((uint32_t)base + 8 * i) & bs_mask)) * nkv + kh) : 0u;
+        return idi >= 0 ? ((((uint32_t)idi << a.log2_bs) + (((uint32_t)base + 8 * i) & bs_mask)) * nkv) : 0u;
     };
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -254,14 +266,14 @@ __device__ __forceinline__ void qtile_issue(const DecodeArgs& a, int raw, int ba
             const uint32_t u0 = grp(2 * v), u1 = grp(2 * v + 1);
             if constexpr (KEYS) {
                 const uint32_t rk = ((m & 8) ? u1 : u0) + (uint32_t)(m & 7) * nkv;
-                T.k[v] = *reinterpret_cast<const v4u_t*>(a.k4 + (size_t)rk * kQ40RowBytes + 16 * g);
+                T.k[v] = *reinterpret_cast<const v4u_t*>(a.k4 + (size_t)rk * kQ40RowBytes + 16 * g + lo.kc);
             }
             if constexpr (VALUES) {
                 const uint32_t rv = ((g & 2) ? u1 : u0) + (uint32_t)(4 * (g & 1)) * nkv;
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    T.v[v][e] = *reinterpret_cast<const uint32_t*>(a.v4 + (size_t)(rv + (uint32_t)e * nkv) *
-                                                                           kQ40RowBytes + 4 * m);
+                    T.v[v][e] = *reinterpret_cast<const uint32_t*>(
+                        a.v4 + (size_t)(rv + (uint32_t)e * nkv) * kQ40RowBytes + 4 * m + lo.vc[e]);
             }
         }
     }
@@ -502,7 +514,7 @@ __global__ __launch_bounds__(kWGThreads, 2) void kvq4_0_decode_kernel(DecodeArgs
     const int n_tiles = first < end ? (end - first + kChunkUnit - 1) / kChunkUnit : 1;
 
     const float4 qx = load_q4(a.q + ((size_t)b * a.nq + (size_t)kh * G) * kHD, G);
-    const QLaneOff lo = q40_lane_offsets(a, lane);
+    const QLaneOff lo = q40_lane_offsets(a, lane, kh);
     QTile A, B;
     qtile_issue<BS8>(a, raw, first, kh, lane, lo, A);
     raw = mtile_raw(a.r8, btb, first + kChunkUnit, a.log2_bs, lane);

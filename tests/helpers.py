@@ -35,34 +35,35 @@ def assert_attn_close(got, ref, what=""):
     return float(np.abs(got - ref).max())
 
 
-def q8_columns(n_slots, nkv):
-    """The library's storage order of int8 code rows: column of head kh in
-    the row of slot s (within each aligned group of P heads, P the largest
-    power of two dividing nkv, at most 8, the heads rotate with the slot)."""
+def pool_columns(n_slots, nkv):
+    """The library's storage order of the int8 and Q4_0 code pools: the
+    column of head kh in the row of slot s (within each aligned group of P
+    heads, P the largest power of two dividing nkv, at most 8, the heads
+    rotate with the slot).  Steps are not rotated."""
     p = min(nkv & -nkv, 8)
     s = np.arange(n_slots)[:, None]
     kh = np.arange(nkv)[None, :]
     return (kh & ~(p - 1)) | ((kh + s) & (p - 1))
 
 
-def q8_pages_order(pool):
-    """An int8 code pool as the library stores it -> the pages' layout
-    [n_blocks][kv_bs][nkv][128] (head kh at column kh), as the oracle keeps it."""
+def pool_pages_order(pool):
+    """A code pool [n_blocks][kv_bs][nkv][row bytes] as the library stores it
+    -> the pages' layout (head kh at column kh), as the oracle keeps it."""
     pool = np.asarray(pool)
-    nb, bs, nkv, hd = pool.shape
-    flat = pool.reshape(nb * bs, nkv, hd)
-    col = q8_columns(nb * bs, nkv)
+    nb, bs, nkv, w = pool.shape
+    flat = pool.reshape(nb * bs, nkv, w)
+    col = pool_columns(nb * bs, nkv)
     return np.take_along_axis(flat, col[:, :, None], axis=1).reshape(pool.shape)
 
 
-def q8_library_order(pool):
-    """The inverse of q8_pages_order: a pool in the pages' layout -> the
+def pool_library_order(pool):
+    """The inverse of pool_pages_order: a pool in the pages' layout -> the
     library's storage order."""
     pool = np.asarray(pool)
-    nb, bs, nkv, hd = pool.shape
-    flat = pool.reshape(nb * bs, nkv, hd)
+    nb, bs, nkv, w = pool.shape
+    flat = pool.reshape(nb * bs, nkv, w)
     out = np.empty_like(flat)
-    col = q8_columns(nb * bs, nkv)
+    col = pool_columns(nb * bs, nkv)
     np.put_along_axis(out, col[:, :, None], flat, axis=1)
     return out.reshape(pool.shape)
 
@@ -94,14 +95,14 @@ class Q8Cache:
                                dev(v_new) if gv_new is None else gv_new, dev(np.asarray(slots, np.int32)))
 
     def assert_device_matches_host(self):
-        assert np.array_equal(q8_pages_order(host(self.gk)), self.kp), "K codes differ"
-        assert np.array_equal(q8_pages_order(host(self.gv)), self.vp), "V codes differ"
+        assert np.array_equal(pool_pages_order(host(self.gk)), self.kp), "K codes differ"
+        assert np.array_equal(pool_pages_order(host(self.gv)), self.vp), "V codes differ"
         assert np.array_equal(host(self.gks).view(np.uint32), self.ks.view(np.uint32)), "K steps differ"
         assert np.array_equal(host(self.gvs).view(np.uint32), self.vs.view(np.uint32)), "V steps differ"
 
     def pull(self):
         """Adopt the device cache as the host cache (after a device-only fill)."""
-        self.kp, self.vp = q8_pages_order(host(self.gk)), q8_pages_order(host(self.gv))
+        self.kp, self.vp = pool_pages_order(host(self.gk)), pool_pages_order(host(self.gv))
         self.ks, self.vs = host(self.gks), host(self.gvs)
 
 

@@ -12,7 +12,7 @@ from oracle import kvq2 as O2
 from oracle import kvq4 as O4
 from oracle import kvq4_0 as O40
 from oracle import kvq8 as O8
-from tests.helpers import SM, Q8Cache, assert_attn_close, dev, fill_sequences, host, q8_library_order
+from tests.helpers import SM, Q8Cache, assert_attn_close, dev, fill_sequences, host, pool_library_order
 from tests.test_gpu_kvq2 import Q2Pool, _banded
 from tests.test_gpu_kvq4 import Q4Pool
 from tests.test_gpu_kvq4_0 import Q40Cache
@@ -194,12 +194,13 @@ def test_write_path_replays(K, mode):
         c = Q8Cache(nb, BS, NKV)
         O8.quantize_append(c.kp, c.vp, c.ks, c.vs, xe, ye, slots)
         pool = [c.gk, c.gv, c.gks, c.gvs]
-        expect = [q8_library_order(c.kp), q8_library_order(c.vp), c.ks, c.vs]   # the device's storage order
+        expect = [pool_library_order(c.kp), pool_library_order(c.vp), c.ks, c.vs]   # the device's storage order
         call = lambda: K.kvq8_quantize_append(*pool, kb, vb, sd)
     elif mode == "Q4_0":
         c = Q40Cache(nb, BS, NKV)
         O40.quantize_append_q4_0(c.kp, c.vp, c.ks, c.vs, xe, ye, slots)
-        pool, expect = [c.gk, c.gv, c.gks, c.gvs], [c.kp, c.vp, c.ks, c.vs]
+        pool = [c.gk, c.gv, c.gks, c.gvs]
+        expect = [pool_library_order(c.kp), pool_library_order(c.vp), c.ks, c.vs]   # the device's storage order
         call = lambda: K.kvq4_0_quantize_append(*pool, kb, vb, sd)
     elif mode == "int4":
         p = Q4Pool(nb, BS, NKV)

@@ -10,7 +10,7 @@ import pytest
 
 import workloads as W
 from oracle import kvq8 as O8
-from tests.helpers import SM, Q8Cache, assert_attn_close, dev, fill_sequences, host, q8_columns
+from tests.helpers import SM, Q8Cache, assert_attn_close, dev, fill_sequences, host, pool_columns
 
 pytestmark = pytest.mark.gpu
 
@@ -412,7 +412,7 @@ def test_int8_pool_storage_order(K, nkv, bs):
     raw = host(c.gk).reshape(n, nkv * 128)
     assert np.all(raw == 127)
     # steps are not rotated; the codes follow the rule (spelled out for nkv = 8 and 12)
-    cols = q8_columns(n, nkv)
+    cols = pool_columns(n, nkv)
     if nkv == 8:
         assert cols[0].tolist() == list(range(8)) and cols[1].tolist() == [1, 2, 3, 4, 5, 6, 7, 0]
         assert cols[9].tolist() == [1, 2, 3, 4, 5, 6, 7, 0]

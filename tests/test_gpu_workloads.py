@@ -28,7 +28,7 @@ from oracle import kvq2 as O2
 from oracle import kvq4 as O4
 from oracle import kvq4_0 as O40
 from oracle import kvq8 as O8
-from tests.helpers import SM, assert_attn_close, dev, host, q8_pages_order
+from tests.helpers import SM, assert_attn_close, dev, host, pool_pages_order
 
 pytestmark = pytest.mark.gpu
 
@@ -73,7 +73,7 @@ def test_qwen2b_8k_layer(K, layer):
     torch.cuda.synchronize()
     hk, hv, hks, hvs = _host_pools(nb, bs, nkv)
     O8.quantize_append(hk, hv, hks, hvs, host(k), host(v), slots)
-    assert _same(q8_pages_order(host(gk)), hk) and _same(q8_pages_order(host(gv)), hv)
+    assert _same(pool_pages_order(host(gk)), hk) and _same(pool_pages_order(host(gv)), hv)
     assert _same(host(gks), hks) and _same(host(gvs), hvs)
     ref = O8.decode_attention_q8(host(q), hk, hks, hv, hvs, bt, [L], bs, SM)
     assert_attn_close(host(out), ref, f"qwen2b layer {layer}")
@@ -113,7 +113,7 @@ def test_qwen2b_8k_fused_step_and_graph_replays(K, layer):
     torch.cuda.synchronize()
     hk, hv, hks, hvs = _host_pools(nb, bs, nkv)
     O8.quantize_append(hk, hv, hks, hvs, host(k), host(v), slots)
-    assert _same(q8_pages_order(host(gk)), hk) and _same(q8_pages_order(host(gv)), hv)
+    assert _same(pool_pages_order(host(gk)), hk) and _same(pool_pages_order(host(gv)), hv)
     assert _same(host(gks), hks) and _same(host(gvs), hvs)
     ref = O8.decode_attention_q8(host(q), hk, hks, hv, hvs, bt, [L], bs, SM)
     assert_attn_close(host(out_eager), ref, f"qwen2b fused step layer {layer}")
@@ -135,7 +135,7 @@ def test_qwen2b_8k_fused_step_and_graph_replays(K, layer):
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(host(out), host(out_eager)), f"replay {rep}"
-        assert _same(q8_pages_order(host(gk)), hk) and _same(host(gks), hks), f"replay {rep} cache"
+        assert _same(pool_pages_order(host(gk)), hk) and _same(host(gks), hks), f"replay {rep} cache"
 
 
 def test_qwen8b_batch32_layer0(K):
@@ -158,7 +158,7 @@ def test_qwen8b_batch32_layer0(K):
     out = torch.empty((B, nq, 128), dtype=torch.float32, device="cuda")
     K.kvq8_decode_attn(out, q, gk, gv, gks, gvs, dev(bt), dev(lens), int(lens.max()), SM)
     torch.cuda.synchronize()
-    assert _same(q8_pages_order(host(gk)), hk) and _same(q8_pages_order(host(gv)), hv)
+    assert _same(pool_pages_order(host(gk)), hk) and _same(pool_pages_order(host(gv)), hv)
     assert _same(host(gks), hks) and _same(host(gvs), hvs)
     ref = O8.decode_attention_q8(host(q), hk, hks, hv, hvs, bt, lens, bs, SM)
     assert_attn_close(host(out), ref, "qwen8b batch 32")
@@ -180,7 +180,7 @@ def test_append64k_then_decode(K):
     torch.cuda.synchronize()
     hk, hv, hks, hvs = _host_pools(nb, bs, nkv)
     O8.quantize_append(hk, hv, hks, hvs, host(k.float()), host(v.float()), slots)
-    assert _same(q8_pages_order(host(gk)), hk) and _same(q8_pages_order(host(gv)), hv)
+    assert _same(pool_pages_order(host(gk)), hk) and _same(pool_pages_order(host(gv)), hv)
     assert _same(host(gks), hks) and _same(host(gvs), hvs)
     ref = O8.decode_attention_q8(host(q), hk, hks, hv, hvs, bt, [n], bs, SM)
     assert_attn_close(host(out), ref, "append64k decode")
@@ -221,7 +221,7 @@ def test_q4_128k(K):
     got = host(out)
     gh4 = [host(x) for x in g4]
     gh8 = [host(x) for x in g8]
-    gh8[:2] = [q8_pages_order(x) for x in gh8[:2]]      # codes in the pages' order, as the oracle keeps them
+    gh8[:2] = [pool_pages_order(x) for x in gh8[:2]]      # codes in the pages' order, as the oracle keeps them
     for b in checked:
         k, v, s4, s8 = host_cache[b]
         p4 = [np.zeros(shp4 + (64,), np.uint8), np.zeros(shp4 + (64,), np.uint8)] + \
@@ -287,7 +287,7 @@ def test_q2_128k(K):
     torch.cuda.synchronize()
     got = host(out)
     gh2, gh4, gh8 = [host(x) for x in g2], [host(x) for x in g4], [host(x) for x in g8]
-    gh8[:2] = [q8_pages_order(x) for x in gh8[:2]]      # codes in the pages' order, as the oracle keeps them
+    gh8[:2] = [pool_pages_order(x) for x in gh8[:2]]      # codes in the pages' order, as the oracle keeps them
     for b in checked:
         k, v, s2, s4, s8 = host_cache[b]
         p2, p4 = group_pool(nb2, 32, True), group_pool(nb4, 64, True)
@@ -340,7 +340,7 @@ def test_q40_qwen8b_batch32_layer0(K):
     out = torch.empty((B, nq, 128), dtype=torch.float32, device="cuda")
     K.kvq4_0_decode_attn(out, q, gk, gv, gks, gvs, dev(bt), dev(lens), int(lens.max()), SM)
     torch.cuda.synchronize()
-    assert np.array_equal(host(gk), hk) and np.array_equal(host(gv), hv)
+    assert np.array_equal(pool_pages_order(host(gk)), hk) and np.array_equal(pool_pages_order(host(gv)), hv)
     assert _same(host(gks), hks) and _same(host(gvs), hvs)
     ref = O40.decode_attention_q4_0(host(q), hk, hks, hv, hvs, bt, lens, bs, SM)
     assert_attn_close(host(out), ref, "Q4_0 qwen8b batch 32")
@@ -362,7 +362,7 @@ def test_q40_append64k_then_decode(K):
     torch.cuda.synchronize()
     hk, hv, hks, hvs = _q40_host(nb, bs, nkv)
     O40.quantize_append_q4_0(hk, hv, hks, hvs, host(k.float()), host(v.float()), slots)
-    assert np.array_equal(host(gk), hk) and np.array_equal(host(gv), hv)
+    assert np.array_equal(pool_pages_order(host(gk)), hk) and np.array_equal(pool_pages_order(host(gv)), hv)
     assert _same(host(gks), hks) and _same(host(gvs), hvs)
     ref = O40.decode_attention_q4_0(host(q), hk, hks, hv, hvs, bt, [n], bs, SM)
     assert_attn_close(host(out), ref, "Q4_0 append64k decode")
