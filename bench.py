@@ -44,9 +44,9 @@ TOK_HEAD_BYTES = 2 * 128 + 2 * 4   # K+V codes + K/V float32 steps per (token, k
 # counters read for a plain 256 MiB device copy (--calibrate-copy 256):
 # FETCH_SIZE 131085.3 KiB -> 2.000 bytes per counted byte, WRITE_SIZE
 # 262144 KiB -> 1.000.  Valid only for the kernel sources they were taken on.
-PMC = {"sources_sha256_16": "6bcd0fc70f8e05fe",
-       "fetch_kib": {"chunk": 8591.97, "merge": 164.53}, "write_kib": {"chunk": 290.06, "merge": 8.00},
-       "fetch_scale": 268435456 / (131085.15 * 1024), "write_scale": 268435456 / (262144.0 * 1024)}
+PMC = {"sources_sha256_16": "d0ae435e2a8791c9",
+       "fetch_kib": {"chunk": 8616.80, "merge": 164.54}, "write_kib": {"chunk": 290.06, "merge": 8.00},
+       "fetch_scale": 268435456 / (131085.44 * 1024), "write_scale": 268435456 / (262144.0 * 1024)}
 
 
 def kernel_sources_digest() -> str:
@@ -360,7 +360,7 @@ def run_workloads(only=None):
         btd, ld, L = dev(bt), dev(lens), int(lens.max())
         ch = K.kvq8_decode_chunk_tokens(B, nkv, L)
         ws = K.alloc_workspace(K.kvq8_decode_workspace_size(B, nq, nkv, L), "cuda")
-        us = time_calls(torch, lambda: K.kvq8_decode_attn(out, qd, *p, btd, ld, L, sm, 0, ws), 20)
+        us = time_calls(torch, lambda: K.kvq8_decode_attn(out, qd, *p, btd, ld, L, sm, 0, ws), 50, warmup=30)
         report("qwen8b_b32", f"decode layer, batch 32 x 32 / 8 heads, lengths U[1024, 32768] (sum {int(lens.sum())})",
                int(lens.sum()) * nkv * 264, us, chunk_tokens=ch)
         del p
@@ -374,7 +374,7 @@ def run_workloads(only=None):
         kk = W.torch_outlier_normal_bf16((n, nkv, 128), "cuda", (4, 0, 0))
         vv = W.torch_outlier_normal_bf16((n, nkv, 128), "cuda", (4, 0, 1))
         slots = dev(W.slots_for_positions(bt, [0] * n, np.arange(n), bs))
-        us = time_calls(torch, lambda: K.kvq8_quantize_append(*p, kk, vv, slots), 20)
+        us = time_calls(torch, lambda: K.kvq8_quantize_append(*p, kk, vv, slots), 50, warmup=30)
         report("append_64k", "write path, 65536 tokens x 8 kv heads from bf16", n * nkv * (2 * 128 * 2 + 2 * 132), us)
         qd = W.torch_normal((1, nq, 128), "cuda", (4, 0, 2))
         out = torch.empty((1, nq, 128), device="cuda")
@@ -418,8 +418,8 @@ def run_workloads(only=None):
         pools = [(p4, p8)] + [([t.clone() for t in p4], [t.clone() for t in p8])
                               for _ in range(mall_copies(nbytes) - 1)]
         fn, iters = cycled(lambda pp: K.kvq4_decode_attn(out, qd, pp[0], bt4d, l4, n4, pp[1], bt8d, l8, n8, sm, 0, ws),
-                           pools, 20)
-        us = time_calls(torch, fn, iters)
+                           pools, 48)
+        us = time_calls(torch, fn, iters, warmup=24)
         report("q4_128k", f"mixed decode, batch 4 x 32 / 4 heads, 129024 int4 + 2048 int8 tokens ({len(pools)} "
                "copies of the cache cycled)", nbytes, us, chunk_tokens=ch)
         del pools
@@ -481,8 +481,8 @@ def run_workloads(only=None):
         pools = [(p2, p4, p8)] + [tuple([t.clone() for t in pp] for pp in (p2, p4, p8))
                                   for _ in range(mall_copies(nbytes) - 1)]
         fn, iters = cycled(lambda pp: K.kvq2_decode_attn(out, qd, pp[0], bt2d, l2, n2, pp[1], bt4d, l4, n4, pp[2],
-                                                         bt8d, l8, n8, sm, 0, ws), pools, 20)
-        us = time_calls(torch, fn, iters)
+                                                         bt8d, l8, n8, sm, 0, ws), pools, 48)
+        us = time_calls(torch, fn, iters, warmup=24)
         report("q2_128k", f"banded decode, batch 4 x 32 / 4 heads, {n2} 2-bit + {n4} int4 + {n8} int8 tokens "
                f"({len(pools)} copies of the cache cycled)", nbytes, us, chunk_tokens=ch)
         del pools
@@ -547,7 +547,7 @@ def run_workloads(only=None):
         out = torch.empty((B, nq, 128), device="cuda")
         btd, ld, L = dev(bt), dev(lens), int(lens.max())
         ws = K.alloc_workspace(K.kvq4_0_decode_workspace_size(B, nq, nkv, L), "cuda")
-        us = time_calls(torch, lambda: K.kvq4_0_decode_attn(out, qd, *p, btd, ld, L, sm, 0, ws), 20)
+        us = time_calls(torch, lambda: K.kvq4_0_decode_attn(out, qd, *p, btd, ld, L, sm, 0, ws), 50, warmup=30)
         report("q40_qwen8b_b32", f"Q4_0 decode layer, batch 32 x 32 / 8 heads, lengths U[1024, 32768] "
                f"(sum {int(lens.sum())})", int(lens.sum()) * nkv * 160, us,
                chunk_tokens=K.kvq4_0_decode_chunk_tokens(B, nkv, L))
@@ -562,7 +562,7 @@ def run_workloads(only=None):
         kk = W.torch_outlier_normal_bf16((n, nkv, 128), "cuda", (4, 0, 0))
         vv = W.torch_outlier_normal_bf16((n, nkv, 128), "cuda", (4, 0, 1))
         slots = dev(W.slots_for_positions(bt, [0] * n, np.arange(n), bs))
-        us = time_calls(torch, lambda: K.kvq4_0_quantize_append(*p, kk, vv, slots), 20)
+        us = time_calls(torch, lambda: K.kvq4_0_quantize_append(*p, kk, vv, slots), 50, warmup=30)
         report("q40_append_64k", "Q4_0 write path, 65536 tokens x 8 kv heads from bf16",
                n * nkv * (2 * 128 * 2 + 2 * 80), us)
         qd = W.torch_normal((1, nq, 128), "cuda", (4, 0, 2))
