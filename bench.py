@@ -670,7 +670,7 @@ def main():
                    "global_batch": 1, "seq_len": L, "chunk_tokens": chunk, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "kernel": "one kvq8_append_decode_attn call: kvq_decode_mfma_kernel<0,false> + kvq_merge1_kernel<2>",
+                     "kernel": "one kvq8_append_decode_attn call: kvq_decode_mfma_kernel<0, false, false> + kvq_merge1_kernel<2>",
                      "bytes_per_launch": decode_bytes_layer, "avg_call_us": round(call_us, 3),
                      "note": "latency-bound: batch 1 moves 17.3 MB per layer call through two dependent "
                              "launches (chunk kernel, then merge), about 2.2 us of transfer at peak; the "
