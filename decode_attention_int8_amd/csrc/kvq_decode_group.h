@@ -23,7 +23,7 @@ struct GroupTileOps<MTile4> {
         mtile4_issue<BS8>(a, raw, base, kh, lane, lo, T);
     }
     static __device__ __forceinline__ void compute(const DecodeArgs& a, const MTile4& T, int base, int L, int lane,
-                                                   int wave, const MQuery4& Q, MState& st, MSmem4& sm) {
+                                                   int wave, const MQuery4& Q, MStateG& st, MSmem4& sm) {
         mtile4_compute(a, T, base, L, lane, wave, Q, st, sm);
     }
 };
@@ -39,7 +39,7 @@ struct GroupTileOps<MTile2> {
         mtile2_issue<BS8>(a, raw, base, kh, lane, lo, T);
     }
     static __device__ __forceinline__ void compute(const BandArgs& a, const MTile2& T, int base, int L, int lane,
-                                                   int wave, const MQuery4& Q, MState& st, MSmem4& sm) {
+                                                   int wave, const MQuery4& Q, MStateG& st, MSmem4& sm) {
         mtile2_compute(a, T, base, L, lane, wave, Q, st, sm);
     }
 };
@@ -64,12 +64,14 @@ __device__ __forceinline__ void group_walk(const Args& a, const Region& reg, con
     quantize_q4(qx, G, sm.q);
     lds_barrier();
     const MQuery4 Q = load_q4_operand<Ops::kEvenOdd>(sm.q, G, g, m);
-    MState st;
+    MStateG st;
     st.M = -INFINITY;
     st.S = 0.0f;
     st.E = 100;
 #pragma unroll
     for (int sl = 0; sl < 8; ++sl) st.acc[sl] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
+    st.accz[0] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
+    st.accz[1] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
     int base = first;
     int k = 0;
     for (; k + 2 < n_tiles; k += 2) {

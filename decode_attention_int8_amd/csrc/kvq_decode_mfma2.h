@@ -10,11 +10,12 @@
 //   qsc_b * s_h * (P_b - z_h R_b).
 //
 // P.V: the 16-bit word m of a value row holds d = 64(s/4) + 4m + s%4 at bits
-//   2s, the int4 tile's slice order.  Two tokens' words side by side give,
-//   after a shift by 2s and a mask, both tokens' codes of slice s in the low
-//   bits of two f16 halves; an OR with 1024's pattern makes them exact f16
-//   1024 + c and one packed f16 add of -(1024 + z) leaves c - z.  The weights
-//   (A operand, one per code group) are the int4 tile's.
+//   2s, the int4 tile's slice order.  Two tokens' words interleaved byte by
+//   byte give, after a shift by 2(s%4) and a mask, both tokens' codes of
+//   slices s and s + 4 as four bytes; two fp8 -> f16 conversions (as in the
+//   int4 tile) make them the exact f16 pairs of both slices.  The weights (A
+//   operand, one per code group) and the zero-point products are the int4
+//   tile's.
 #pragma once
 
 #include "kvq_decode_mfma4.h"
@@ -93,7 +94,7 @@ __device__ __forceinline__ void mtile2_issue(const BandArgs& a, int raw, int bas
 }
 
 __device__ __forceinline__ void mtile2_compute(const BandArgs& a, const MTile2& T, int base, int L, int lane,
-                                               int wave, const MQuery4& Q, MState& st, MSmem4& sm) {
+                                               int wave, const MQuery4& Q, MStateG& st, MSmem4& sm) {
     const int g = lane >> 4;
     const int m = lane & 15;
     // per-token scales through LDS (lane l holds token base+l)
@@ -109,6 +110,8 @@ __device__ __forceinline__ void mtile2_compute(const BandArgs& a, const MTile2& 
                 const float f = exp2i(Et - st.E);
 #pragma unroll
                 for (int sl = 0; sl < 8; ++sl) st.acc[sl] *= f;
+                st.accz[0] *= f;
+                st.accz[1] *= f;
                 st.E = Et;
             }
         }
@@ -120,10 +123,8 @@ __device__ __forceinline__ void mtile2_compute(const BandArgs& a, const MTile2& 
         sm.kb[wave][lane] = ok ? 0.0f : -INFINITY;
         sm.v4s[wave][0][lane] = ok ? vs0 * sc : 0.0f;
         sm.v4s[wave][1][lane] = ok ? vs1 * sc : 0.0f;
-        // -(1024 + z) is exact in binary16 for z in [0, 3]
-        const float z0 = ok ? half_bits_f(T.vz & 0xFFFFu) : 0.0f, z1 = ok ? half_bits_f(T.vz >> 16) : 0.0f;
-        sm.v4c[wave][0][lane] = __builtin_bit_cast(uint16_t, (_Float16)(-(1024.0f + z0)));
-        sm.v4c[wave][1][lane] = __builtin_bit_cast(uint16_t, (_Float16)(-(1024.0f + z1)));
+        sm.v4z[wave][0][lane] = ok ? (uint16_t)(T.vz & 0xFFFFu) : (uint16_t)0;
+        sm.v4z[wave][1][lane] = ok ? (uint16_t)(T.vz >> 16) : (uint16_t)0;
     }
     // Q.K and scores
     float s[4][4];
@@ -169,6 +170,13 @@ __device__ __forceinline__ void mtile2_compute(const BandArgs& a, const MTile2& 
             st.acc[sl][2] *= fb;
             st.acc[sl][3] *= fb;
         }
+#pragma unroll
+        for (int G2 = 0; G2 < 2; ++G2) {
+            st.accz[G2][0] *= fa;
+            st.accz[G2][1] *= fa;
+            st.accz[G2][2] *= fb;
+            st.accz[G2][3] *= fb;
+        }
     }
     const float mref = (st.M == -INFINITY) ? 0.0f : st.M;
     const uint32_t part_mask = weight_part_mask(m);
@@ -180,11 +188,12 @@ __device__ __forceinline__ void mtile2_compute(const BandArgs& a, const MTile2& 
             p[v][r] = __builtin_amdgcn_exp2f(s[v][r] - mref);
             st.S += p[v][r];
         }
-    // P.V: one A operand per code group, value codes minus zero point as f16
+    // P.V: one A operand per code group, the codes as f16, the zero points
+    // through their own product per group
 #pragma unroll
     for (int vp = 0; vp < 2; ++vp) {
         v8h_t A[2];
-        uint32_t zc[2][4];      // [group]: -(1024 + z) of the lane's 8 tokens, in pairs
+        uint32_t zc[2][4];      // [group]: binary16 z of the lane's 8 tokens, in pairs
 #pragma unroll
         for (int G2 = 0; G2 < 2; ++G2) {
             uint32_t wop[2][2];
@@ -197,33 +206,34 @@ __device__ __forceinline__ void mtile2_compute(const BandArgs& a, const MTile2& 
                 for (int pr = 0; pr < 2; ++pr) {
                     wop[q2][pr] = weight_part_f16x2(w[2 * pr], w[2 * pr + 1], part_mask);
                 }
-                const uint2 zz = *reinterpret_cast<const uint2*>(&sm.v4c[wave][G2][16 * v + 4 * g]);
+                const uint2 zz = *reinterpret_cast<const uint2*>(&sm.v4z[wave][G2][16 * v + 4 * g]);
                 zc[G2][2 * q2] = zz.x;
                 zc[G2][2 * q2 + 1] = zz.y;
             }
             A[G2] = __builtin_bit_cast(v8h_t, v4u_t{wop[0][0], wop[0][1], wop[1][0], wop[1][1]});
+            const v8h_t Z = __builtin_bit_cast(v8h_t, v4u_t{zc[G2][0], zc[G2][1], zc[G2][2], zc[G2][3]});
+            st.accz[G2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[G2], Z, st.accz[G2], 0, 0, 0);
         }
         // tokens 2i and 2i+1 of the lane's 8 (token group 2vp + q/4, e = q%4)
-        // side by side: low and high 16 bits
-        uint32_t tw[4];
+        // interleaved: bytes [a0, b0, a1, b1] of their 16-bit words, so slice
+        // sl < 4 sits at bits 2sl of bytes 0-1 and slice sl + 4 of bytes 2-3
+        uint32_t bw[8][4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int q0 = 2 * i, q1 = 2 * i + 1;
-            tw[i] = T.v[2 * vp + q0 / 4][q0 % 4] | (T.v[2 * vp + q1 / 4][q1 % 4] << 16);
+            const uint32_t tw = __builtin_amdgcn_perm(T.v[2 * vp + q1 / 4][q1 % 4], T.v[2 * vp + q0 / 4][q0 % 4],
+                                                      0x05010400u);
+#pragma unroll
+            for (int sl = 0; sl < 4; ++sl) {
+                const uint32_t x = (tw >> (2 * sl)) & kCrumb;
+                bw[sl][i] = fp8_codes_f16x2<false>(x);
+                bw[sl + 4][i] = fp8_codes_f16x2<true>(x);
+            }
         }
 #pragma unroll
         for (int sl = 0; sl < 8; ++sl) {
-            const int G2 = sl >> 2;
-            uint32_t bw[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                // [c_a, c_b] in the low bits of each half | 0x6400 = 1024 + c
-                const uint32_t x = ((tw[i] >> (2 * sl)) & 0x00030003u) | 0x64006400u;
-                bw[i] = __builtin_bit_cast(uint32_t,
-                                           __builtin_bit_cast(v2h_t, x) + __builtin_bit_cast(v2h_t, zc[G2][i]));
-            }
-            const v8h_t B = __builtin_bit_cast(v8h_t, v4u_t{bw[0], bw[1], bw[2], bw[3]});
-            st.acc[sl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[G2], B, st.acc[sl], 0, 0, 0);
+            const v8h_t B = __builtin_bit_cast(v8h_t, v4u_t{bw[sl][0], bw[sl][1], bw[sl][2], bw[sl][3]});
+            st.acc[sl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[sl >> 2], B, st.acc[sl], 0, 0, 0);
         }
     }
 }

@@ -19,8 +19,14 @@
 //   covers d = 64(s/4) + 4m + (s%4): group s/4 for every column.  Its A
 //   operand is the weights p * vscale of that group (f16 high part or
 //   remainder below it, times 2^E; row c = (head c/2, part c%2)) and B is
-//   c - z of that group as f16 (exact small integers).  Each lane's softmax
-//   values are exactly the weights it supplies.
+//   the code c as f16.  A byte holding a code 0..15 is, read as an OCP fp8
+//   e4m3 number, exactly c * 2^-9, so one fp8 -> f16 conversion with scale
+//   2^9 turns two tokens' code bytes into the exact f16 pair.  The zero
+//   points enter through one more product per group and token pair, with B
+//   = z of each token in every column: sum_t w_t z_t, subtracted from every
+//   slice of the group when the wave folds its state (sum w (c - z) = sum w c
+//   - sum w z, both exact integers times the same weights).  Each lane's
+//   softmax values are exactly the weights it supplies.
 #pragma once
 
 #include "kvq_decode_mfma_kernel.h"
@@ -32,8 +38,22 @@ struct MSmem4 : MSmem {
     float k4s[kWaves][2][64];      // key group scale * score scale (0 if masked)
     float k4z[kWaves][2][64];      // key group zero point
     float v4s[kWaves][2][64];      // value group scale * 2^E (0 if masked)
-    uint16_t v4c[kWaves][2][64];   // binary16 of -(1024 + value zero point)
+    uint16_t v4z[kWaves][2][64];   // binary16 value zero point (0 if masked)
 };
+
+// Wave state of the group walks: the int8 walk's plus, per code group, the
+// products of the weights with the value zero points (same rows as acc, the
+// same value in every column).
+struct MStateG : MState {
+    v4f_t accz[2];
+};
+
+// two code bytes (word half HI) -> their values as an f16 pair: a byte
+// 0..15 is c * 2^-9 as fp8 e4m3, scaled by 2^9
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8_codes_f16x2(uint32_t x) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 512.0f, HI));
+}
 
 struct MTile4 {
     v2u_t k[4][2];       // [v][h]: token 16v+m, packed bytes 32h+8g .. +7
@@ -147,7 +167,7 @@ __device__ __forceinline__ void mtile4_issue(const DecodeArgs& a, int raw, int b
 }
 
 __device__ __forceinline__ void mtile4_compute(const DecodeArgs& a, const MTile4& T, int base, int L, int lane,
-                                               int wave, const MQuery4& Q, MState& st, MSmem4& sm) {
+                                               int wave, const MQuery4& Q, MStateG& st, MSmem4& sm) {
     const int g = lane >> 4;
     const int m = lane & 15;
     // per-token scales through LDS (lane l holds token base+l)
@@ -163,6 +183,8 @@ __device__ __forceinline__ void mtile4_compute(const DecodeArgs& a, const MTile4
                 const float f = exp2i(Et - st.E);
 #pragma unroll
                 for (int sl = 0; sl < 8; ++sl) st.acc[sl] *= f;
+                st.accz[0] *= f;
+                st.accz[1] *= f;
                 st.E = Et;
             }
         }
@@ -174,10 +196,8 @@ __device__ __forceinline__ void mtile4_compute(const DecodeArgs& a, const MTile4
         sm.kb[wave][lane] = ok ? 0.0f : -INFINITY;
         sm.v4s[wave][0][lane] = ok ? vs0 * sc : 0.0f;
         sm.v4s[wave][1][lane] = ok ? vs1 * sc : 0.0f;
-        // -(1024 + z) is exact in binary16 for z in [0, 15]
-        const float z0 = ok ? half_bits_f(T.vz & 0xFFFFu) : 0.0f, z1 = ok ? half_bits_f(T.vz >> 16) : 0.0f;
-        sm.v4c[wave][0][lane] = __builtin_bit_cast(uint16_t, (_Float16)(-(1024.0f + z0)));
-        sm.v4c[wave][1][lane] = __builtin_bit_cast(uint16_t, (_Float16)(-(1024.0f + z1)));
+        sm.v4z[wave][0][lane] = ok ? (uint16_t)(T.vz & 0xFFFFu) : (uint16_t)0;
+        sm.v4z[wave][1][lane] = ok ? (uint16_t)(T.vz >> 16) : (uint16_t)0;
     }
     // Q.K and scores
     float s[4][4];
@@ -226,6 +246,13 @@ __device__ __forceinline__ void mtile4_compute(const DecodeArgs& a, const MTile4
             st.acc[sl][2] *= fb;
             st.acc[sl][3] *= fb;
         }
+#pragma unroll
+        for (int G2 = 0; G2 < 2; ++G2) {
+            st.accz[G2][0] *= fa;
+            st.accz[G2][1] *= fa;
+            st.accz[G2][2] *= fb;
+            st.accz[G2][3] *= fb;
+        }
     }
     const float mref = (st.M == -INFINITY) ? 0.0f : st.M;
     const uint32_t part_mask = weight_part_mask(m);
@@ -237,11 +264,12 @@ __device__ __forceinline__ void mtile4_compute(const DecodeArgs& a, const MTile4
             p[v][r] = __builtin_amdgcn_exp2f(s[v][r] - mref);
             st.S += p[v][r];
         }
-    // P.V: one A operand per code group, value codes minus zero point as f16
+    // P.V: one A operand per code group, the codes as f16, the zero points
+    // through their own product per group
 #pragma unroll
     for (int vp = 0; vp < 2; ++vp) {
         v8h_t A[2];
-        uint32_t zc[2][4];      // [group]: -(1024 + z) of the lane's 8 tokens, in pairs
+        uint32_t zc[2][4];      // [group]: binary16 z of the lane's 8 tokens, in pairs
 #pragma unroll
         for (int G2 = 0; G2 < 2; ++G2) {
             uint32_t wop[2][2];
@@ -254,45 +282,45 @@ __device__ __forceinline__ void mtile4_compute(const DecodeArgs& a, const MTile4
                 for (int pr = 0; pr < 2; ++pr) {
                     wop[q2][pr] = weight_part_f16x2(w[2 * pr], w[2 * pr + 1], part_mask);
                 }
-                const uint2 zz = *reinterpret_cast<const uint2*>(&sm.v4c[wave][G2][16 * v + 4 * g]);
+                const uint2 zz = *reinterpret_cast<const uint2*>(&sm.v4z[wave][G2][16 * v + 4 * g]);
                 zc[G2][2 * q2] = zz.x;
                 zc[G2][2 * q2 + 1] = zz.y;
             }
             A[G2] = __builtin_bit_cast(v8h_t, v4u_t{wop[0][0], wop[0][1], wop[1][0], wop[1][1]});
+            const v8h_t Z = __builtin_bit_cast(v8h_t, v4u_t{zc[G2][0], zc[G2][1], zc[G2][2], zc[G2][3]});
+            st.accz[G2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[G2], Z, st.accz[G2], 0, 0, 0);
         }
-        // even / odd codes of the 8 tokens' words
-        uint32_t ev[8], od[8];
+        // codes of slice sl (d = 64(sl/4) + 4m + sl%4: byte sl/2 of the word,
+        // high nibble for even sl) for tokens 2i, 2i+1 of the lane's 8
+        // (token group 2vp + q/4, e = q%4) as one f16 pair
+        uint32_t bw[8][4];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const uint32_t w = T.v[2 * vp + q / 4][q % 4];
-            ev[q] = (w >> 4) & kNib;
-            od[q] = w & kNib;
+        for (int i = 0; i < 4; ++i) {
+            const int q0 = 2 * i, q1 = 2 * i + 1;
+            const uint32_t wa = T.v[2 * vp + q0 / 4][q0 % 4], wb = T.v[2 * vp + q1 / 4][q1 % 4];
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) {
+                // bytes [a(2hb), b(2hb), a(2hb+1), b(2hb+1)]
+                const uint32_t x = __builtin_amdgcn_perm(wb, wa, hb ? 0x07030602u : 0x05010400u);
+                const uint32_t xh = (x >> 4) & kNib, xl = x & kNib;
+                bw[4 * hb + 0][i] = fp8_codes_f16x2<false>(xh);
+                bw[4 * hb + 1][i] = fp8_codes_f16x2<false>(xl);
+                bw[4 * hb + 2][i] = fp8_codes_f16x2<true>(xh);
+                bw[4 * hb + 3][i] = fp8_codes_f16x2<true>(xl);
+            }
         }
 #pragma unroll
         for (int sl = 0; sl < 8; ++sl) {
-            // d = 64(sl/4) + 4m + sl%4: byte sl/2 of the word, high nibble for even sl
-            const int byte = sl >> 1;
-            const int G2 = sl >> 2;
-            uint32_t bw[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t xa = (sl & 1) ? od[2 * i] : ev[2 * i];
-                const uint32_t xb = (sl & 1) ? od[2 * i + 1] : ev[2 * i + 1];
-                // [code_a, 0, code_b, 0] | 0x6400 in each half = 1024 + code
-                const uint32_t sel = (uint32_t)byte | 0x0C000000u | ((uint32_t)(4 + byte) << 16) | 0x00000C00u;
-                const uint32_t x = __builtin_amdgcn_perm(xb, xa, sel) | 0x64006400u;
-                bw[i] = __builtin_bit_cast(uint32_t,
-                                           __builtin_bit_cast(v2h_t, x) + __builtin_bit_cast(v2h_t, zc[G2][i]));
-            }
-            const v8h_t B = __builtin_bit_cast(v8h_t, v4u_t{bw[0], bw[1], bw[2], bw[3]});
-            st.acc[sl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[G2], B, st.acc[sl], 0, 0, 0);
+            const v8h_t B = __builtin_bit_cast(v8h_t, v4u_t{bw[sl][0], bw[sl][1], bw[sl][2], bw[sl][3]});
+            st.acc[sl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[sl >> 2], B, st.acc[sl], 0, 0, 0);
         }
     }
 }
 
-// Fold an int4 wave state into the workgroup's LDS layout (per wave and
-// head: M, S, acc[128]); slice s of lane m holds d = 64(s/4) + 4m + s%4.
-__device__ __forceinline__ void mwave4_to_lds(MSmem4& sm, MState& st, int G, int lane, int wave) {
+// Fold a group-walk wave state into the workgroup's LDS layout (per wave and
+// head: M, S, acc[128]); slice s of lane m holds d = 64(s/4) + 4m + s%4, and
+// the zero-point products of its group come off here.
+__device__ __forceinline__ void mwave4_to_lds(MSmem4& sm, MStateG& st, int G, int lane, int wave) {
     const int g = lane >> 4;
     const int m = lane & 15;
     float S = st.S;
@@ -309,7 +337,10 @@ __device__ __forceinline__ void mwave4_to_lds(MSmem4& sm, MState& st, int G, int
         if (H < G) {
             float o[8];
 #pragma unroll
-            for (int sl = 0; sl < 8; ++sl) o[sl] = (st.acc[sl][2 * hh] + st.acc[sl][2 * hh + 1]) * unscale;
+            for (int sl = 0; sl < 8; ++sl) {
+                const v4f_t& z = st.accz[sl >> 2];
+                o[sl] = ((st.acc[sl][2 * hh] - z[2 * hh]) + (st.acc[sl][2 * hh + 1] - z[2 * hh + 1])) * unscale;
+            }
             *reinterpret_cast<float4*>(&sm.acc[wave][H][4 * m]) = make_float4(o[0], o[1], o[2], o[3]);
             *reinterpret_cast<float4*>(&sm.acc[wave][H][64 + 4 * m]) = make_float4(o[4], o[5], o[6], o[7]);
         }
