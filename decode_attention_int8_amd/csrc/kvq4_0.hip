@@ -69,9 +69,14 @@ __device__ __forceinline__ void q40_load8(const void* base, size_t elem_off, flo
 // is floor(x / step + 8.5) clamped to 15: rint(x * rcp(step)) + 8 where
 // x * rcp(step) is not within 2^-11 of a half-integer; elsewhere (about 0.1%
 // of the values, or a quotient that is not finite) the lane divides.  A zero
-// block has step +0 and codes 8.
+// block has step +0 and codes 8.  rint(q) + 8 is the low byte of q + 1.5 *
+// 2^23 + 8 (|q| <= 8: the sum's unit is 1, and the addition rounds half to
+// even like rint); four such bytes are gathered by two byte permutes, and
+// the one code that can reach 16 (q = +8) is brought to 15 on the packed
+// word.
 __device__ __forceinline__ void q40_quantize8(const float (&x)[8], uint32_t& lo, uint32_t& hi, float& step) {
 #pragma clang fp contract(off)
+    constexpr float kMagic = 12582920.0f;            // 1.5 * 2^23 + 8
     float mx = x[0], mn = x[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) {
@@ -87,25 +92,30 @@ __device__ __forceinline__ void q40_quantize8(const float (&x)[8], uint32_t& lo,
     const bool zero = m == 0.0f;
     step = zero ? 0.0f : m * -0.125f;                // exact: a power-of-two division
     const float rs = __builtin_amdgcn_rcpf(step);
-    float c[8];
+    uint32_t cb[8];                                  // low byte: the code (16 for q = +8)
     bool slow[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const float q = x[e] * rs;                   // |x / step| <= 8
-        const float rq = rintf(q);
+        const float f = q + kMagic;
+        const float rq = f - kMagic;                 // rint(q)
         slow[e] = !zero && near_half_small(q, rq);
-        c[e] = fminf(rq + 8.0f, 15.0f);
+        cb[e] = __float_as_uint(f);
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         if (__builtin_amdgcn_ballot_w64(slow[e]) != 0) {      // rare: one wave-uniform test per value
             const float cd = fminf(floorf(x[e] / step + 8.5f), 15.0f);
-            c[e] = slow[e] ? cd : c[e];
+            cb[e] = slow[e] ? (uint32_t)(int)cd : cb[e];
         }
     }
-    uint32_t w[2] = {0u, 0u};
+    uint32_t w[2];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) w[e >> 2] |= (uint32_t)(int)c[e] << (8 * (e & 3));
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t v = __builtin_amdgcn_perm(cb[4 * h + 1], cb[4 * h], 0x0C0C0400u) |
+                           __builtin_amdgcn_perm(cb[4 * h + 3], cb[4 * h + 2], 0x04000C0Cu);
+        w[h] = v - ((v >> 4) & 0x01010101u);         // 16 -> 15, codes 0..15 unchanged
+    }
     lo = zero ? 0x08080808u : w[0];
     hi = zero ? 0x08080808u : w[1];
 }
