@@ -407,7 +407,10 @@ __device__ __forceinline__ void qtile_compute(const DecodeArgs& a, const QTile T
             p[v][r] = __builtin_amdgcn_exp2f(s[v][r] - mref);
             st.S += p[v][r];
         }
-    const v2h_t bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+    // -8 in every f16 of a B operand: the products sum_t w_t * (-8) of a
+    // block, added to both of its slices
+    const v8h_t neg8 = {(_Float16)-8.0f, (_Float16)-8.0f, (_Float16)-8.0f, (_Float16)-8.0f,
+                        (_Float16)-8.0f, (_Float16)-8.0f, (_Float16)-8.0f, (_Float16)-8.0f};
 #pragma unroll
     for (int vp = 0; vp < 2; ++vp) {
         v8h_t A[4];
@@ -426,30 +429,31 @@ __device__ __forceinline__ void qtile_compute(const DecodeArgs& a, const QTile T
             }
             A[b] = __builtin_bit_cast(v8h_t, v4u_t{wop[0][0], wop[0][1], wop[1][0], wop[1][1]});
         }
-        // the 8 tokens' value words, low and high nibbles as bytes
-        uint32_t n_lo[8], n_hi[8];
+        // codes of slice sl (d = 32(sl/2) + 2m + (sl&1): byte sl/2 of the
+        // word, high nibble for odd sl) for tokens 2i, 2i+1 of the lane's 8
+        // (token group 2vp + q/4, e = q%4) as one f16 pair: a code byte
+        // 0..15 is c * 2^-9 as OCP fp8 e4m3, converted with scale 2^9
+        uint32_t bw[8][4];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const uint32_t w = T.v[2 * vp + q / 4][q % 4];
-            n_lo[q] = w & kNib;
-            n_hi[q] = (w >> 4) & kNib;
+        for (int i = 0; i < 4; ++i) {
+            const int q0 = 2 * i, q1 = 2 * i + 1;
+            const uint32_t wa = T.v[2 * vp + q0 / 4][q0 % 4], wb = T.v[2 * vp + q1 / 4][q1 % 4];
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) {
+                // bytes [a(2hb), b(2hb), a(2hb+1), b(2hb+1)]
+                const uint32_t x = __builtin_amdgcn_perm(wb, wa, hb ? 0x07030602u : 0x05010400u);
+                const uint32_t xl = x & kNib, xh = (x >> 4) & kNib;
+                bw[4 * hb + 0][i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(xl, 512.0f, false));
+                bw[4 * hb + 1][i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(xh, 512.0f, false));
+                bw[4 * hb + 2][i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(xl, 512.0f, true));
+                bw[4 * hb + 3][i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(xh, 512.0f, true));
+            }
         }
 #pragma unroll
         for (int sl = 0; sl < 8; ++sl) {
-            // d = 32(sl/2) + 2m + (sl&1): byte sl/2 of the word, high nibble for odd sl
-            const int byte = sl >> 1;
-            const uint32_t sel = (uint32_t)byte | 0x00000C00u | ((uint32_t)(4 + byte) << 16) | 0x0C000000u;
-            uint32_t bw[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t xa = (sl & 1) ? n_hi[2 * i] : n_lo[2 * i];
-                const uint32_t xb = (sl & 1) ? n_hi[2 * i + 1] : n_lo[2 * i + 1];
-                // [c_a, 0, c_b, 0] | 0x6400 in each half = 1024 + c; minus 1032 leaves c - 8
-                const uint32_t x = __builtin_amdgcn_perm(xb, xa, sel) | 0x64006400u;
-                bw[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2h_t, x) + bias);
-            }
-            const v8h_t B = __builtin_bit_cast(v8h_t, v4u_t{bw[0], bw[1], bw[2], bw[3]});
-            st.acc[sl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[byte], B, st.acc[sl], 0, 0, 0);
+            const v8h_t B = __builtin_bit_cast(v8h_t, v4u_t{bw[sl][0], bw[sl][1], bw[sl][2], bw[sl][3]});
+            st.acc[sl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[sl >> 1], B, st.acc[sl], 0, 0, 0);
+            st.acc[sl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[sl >> 1], neg8, st.acc[sl], 0, 0, 0);
         }
     }
 }
