@@ -21,7 +21,9 @@
 //        columns m of slice s are d = 32(s/2) + 2m + (s & 1), all in value
 //        block s/2, so the A operand holds the weights p * vstep of that
 //        block (f16 high part + f16 remainder, rows = (head, part)) and B
-//        holds c - 8 as f16 (exact).  Up to 8 heads in one operand set.
+//        holds c as f16 (exact; one fp8 -> f16 conversion per token pair);
+//        a second product with B = -8 everywhere adds the -8 sum_t w_t of
+//        the block.  Up to 8 heads in one operand set.
 #include "kvq8.h"
 #include "kvq_decode_mfma.h"
 
