@@ -202,7 +202,7 @@ __global__ __launch_bounds__(256) void kvq2_requantize_q4_kernel(
             sc[k] = vs4[r4 * 2 + h];
             zp[k] = vz4[r4 * 2 + h];
         } else {
-            c0[k] = *reinterpret_cast<const uint32_t*>(kc4 + r4 * (kHD / 2) + 4 * l16);
+            c0[k] = *reinterpret_cast<const uint32_t*>(kc4 + r4 * (kHD / 2) + q4_key_offset(l16));
             c1[k] = 0u;
             sc[k] = ks4[r4 * 2 + h];
             zp[k] = kz4[r4 * 2 + h];

@@ -86,17 +86,18 @@ constexpr int kRowsPerGroup = 4;            // rows per 16-lane group, loads fir
 constexpr int kRowsPerBlock = 16 * kRowsPerGroup;
 
 // Store one row: lane l16 packed the pairs of its 8 values (elements 8 l16 ..
-// 8 l16 + 7) into `packed`; `other` is lane l16 ^ 8's word.  Key rows keep
-// pair i in byte i.  Value rows put the pair 64g + 4m + 2k, +1 at byte
-// 4m + 2g + k (word m = d 4m .. 4m+3 of both groups): with j = l16 % 8, the
-// low halves of lanes j and j + 8 form word 2j, their high halves word 2j+1.
+// 8 l16 + 7) into `packed`; `other` is lane l16 ^ 8's word.  Key rows take
+// the storage order of q4_key_offset.  Value rows put the pair 64g + 4m + 2k, +1
+// at byte 4m + 2g + k (word m = d 4m .. 4m+3 of both groups): with j = l16 %
+// 8, the low halves of lanes j and j + 8 form word 2j, their high halves word
+// 2j+1.
 __device__ __forceinline__ void store_q4_row(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
                                              uint16_t* __restrict__ ks, uint16_t* __restrict__ kz,
                                              uint16_t* __restrict__ vs, uint16_t* __restrict__ vz, int kind,
                                              size_t dst, int l16, uint32_t packed, uint32_t other, uint16_t s16,
                                              uint16_t z16) {
     if (kind == 0) {
-        *reinterpret_cast<uint32_t*>(kc + dst * (kHD / 2) + 4 * l16) = packed;
+        *reinterpret_cast<uint32_t*>(kc + dst * (kHD / 2) + q4_key_offset(l16)) = packed;
     } else {
         const int j = l16 & 7;
         const uint32_t word = (l16 < 8) ? ((packed & 0xFFFFu) | (other << 16))

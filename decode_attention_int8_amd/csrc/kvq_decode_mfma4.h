@@ -5,9 +5,11 @@
 // int4 tile (64 tokens, lane = (g, m) as in the int8 kernel), up to 8 query
 // heads in one operand set:
 //
-// Q.K: v_mfma_i32_16x16x64_i8 per (token group v, row half h).  A = unsigned
+// Q.K: v_mfma_i32_16x16x64_i8 per (token group v, code group h).  A = unsigned
 //   codes of token 16v+m, d = 64h+16g .. +15, unpacked from 8 packed bytes as
-//   [even d | odd d] per 4-byte word (two VALU ops per word); B = the query
+//   [even d | odd d] per 4-byte word (two VALU ops per word); the key row's
+//   storage order (q4_key_offset) puts both groups' bytes of lane group g in
+//   one 16-byte load.  B = the query
 //   codes in the same order, column c = (head c/2, block parity c%2):
 //   column c receives P_b = sum q*c over block 2h + (c & 1), which lies in
 //   code group h.  The score term of a block is qsc_b * s_h * (P_b - z_h R_b)
@@ -56,7 +58,7 @@ __device__ __forceinline__ uint32_t fp8_codes_f16x2(uint32_t x) {
 }
 
 struct MTile4 {
-    v2u_t k[4][2];       // [v][h]: token 16v+m, packed bytes 32h+8g .. +7
+    v2u_t k[4][2];       // [v][h]: token 16v+m, codes 64h + 16g .. +15 (row bytes 16g + 8h .. +7)
     uint32_t v[4][4];    // [v][e]: token 16v+4g+e, packed bytes 4m .. 4m+3
     uint32_t ks, kz, vs, vz;   // token base+lane: both groups' binary16 scale / zero
     int id;
@@ -108,7 +110,7 @@ __device__ __forceinline__ MQuery4 load_q4_operand(const QSmem& sm, int G, int g
 }
 
 struct LaneOff4 {
-    uint32_t k;          // packed key row of token 16v+m, bytes 8g..
+    uint32_t k;          // packed key row of token 16v+m, bytes 16g .. 16g+15 (q4_key_offset order)
     uint32_t v[4];       // packed value rows of tokens 16v+4g+e, bytes 4m..
 };
 
@@ -117,7 +119,7 @@ __device__ __forceinline__ LaneOff4 lane_offsets4(const DecodeArgs& a, int lane)
     const int m = lane & 15;
     const uint32_t row = (uint32_t)a.nkv * (kHD / 2);
     LaneOff4 o;
-    o.k = (uint32_t)m * row + 8 * g;
+    o.k = (uint32_t)m * row + 16 * g;
 #pragma unroll
     for (int e = 0; e < 4; ++e) o.v[e] = (uint32_t)(4 * g + e) * row + 4 * m;
     return o;
@@ -143,16 +145,17 @@ __device__ __forceinline__ void mtile4_issue(const DecodeArgs& a, int raw, int b
             const uint32_t u = grp(2 * v);
             const uint8_t* pk = a.k4 + (size_t)u * (kHD / 2);
             const uint8_t* pv = a.v4 + (size_t)u * (kHD / 2);
-            T.k[v][0] = *reinterpret_cast<const v2u_t*>(pk + lo.k);
-            T.k[v][1] = *reinterpret_cast<const v2u_t*>(pk + lo.k + 32);
+            const v4u_t kk = *reinterpret_cast<const v4u_t*>(pk + lo.k);
+            T.k[v][0] = v2u_t{kk.x, kk.y};
+            T.k[v][1] = v2u_t{kk.z, kk.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) T.v[v][e] = *reinterpret_cast<const uint32_t*>(pv + lo.v[e]);
         } else {
             const uint32_t u0 = grp(2 * v), u1 = grp(2 * v + 1);
             const uint32_t rk = ((m & 8) ? u1 : u0) + (uint32_t)(m & 7) * nkv;
-            const uint8_t* p = a.k4 + (size_t)rk * (kHD / 2) + 8 * g;
-            T.k[v][0] = *reinterpret_cast<const v2u_t*>(p);
-            T.k[v][1] = *reinterpret_cast<const v2u_t*>(p + 32);
+            const v4u_t kk = *reinterpret_cast<const v4u_t*>(a.k4 + (size_t)rk * (kHD / 2) + 16 * g);
+            T.k[v][0] = v2u_t{kk.x, kk.y};
+            T.k[v][1] = v2u_t{kk.z, kk.w};
             const uint32_t rv = ((g & 2) ? u1 : u0) + (uint32_t)(4 * (g & 1)) * nkv;
 #pragma unroll
             for (int e = 0; e < 4; ++e)

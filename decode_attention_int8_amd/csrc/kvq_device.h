@@ -171,6 +171,15 @@ __host__ __device__ __forceinline__ int q8_col(int kh, long slot, int p) {
     return (kh & ~(p - 1)) | ((kh + (int)(slot & 7)) & (p - 1));
 }
 
+// Storage order of an int4 key row (64 bytes, two codes per byte, even element
+// in the high nibble): eight 8-byte parts, part 2c + h holding the pairs 32h +
+// 8c .. 32h + 8c + 7, i.e. codes 64h + 16c .. 64h + 16c + 15, so that the 16
+// bytes at 16c carry the same 16 d of both code groups (one 16-byte load per
+// decode lane).  The byte offset of pairs 4w .. 4w + 3 (w = 0..15):
+__host__ __device__ __forceinline__ unsigned q4_key_offset(int w) {
+    return 16u * (unsigned)((w >> 1) & 3) + 8u * (unsigned)(w >> 3) + 4u * (unsigned)(w & 1);
+}
+
 // IEEE binary16 bits (low 16 bits of v) widened to float (exact)
 __device__ __forceinline__ float half_bits_f(uint32_t v) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)v);

@@ -275,8 +275,10 @@ int kvq8_qk_partials(int32_t* partials, const float* q, int batch, int nq,
  * int4 pool layout:
  *   packed codes  cache4[n_blocks4][kv_bs][nkv][64] uint8, two consecutive
  *                 codes per byte, even-indexed value in the high nibble;
- *                 key rows hold pair i in byte i, value rows hold the pair
- *                 starting at element 64g + 4m + 2k in byte 4m + 2g + k
+ *                 key rows hold the pair starting at element 64h + 16c + 2j
+ *                 (h = 0, 1; c = 0..3; j = 0..7) in byte 16c + 8h + j, value
+ *                 rows hold the pair starting at element 64g + 4m + 2k in
+ *                 byte 4m + 2g + k
  *   scale, zero   [n_blocks4][kv_bs][nkv][2] IEEE binary16 (as uint16 bits),
  *                 one per 64-value group
  * Recent tokens stay in an int8 pool laid out exactly as above.
@@ -290,8 +292,9 @@ int kvq8_qk_partials(int32_t* partials, const float* q, int batch, int nq,
  * (stored as binary16, exact); code = clamp(rint(x / s + zero), 0, 15);
  * rint is round-half-to-even.  Value rows store the pair of elements
  * 64g + 4m + 2k, 64g + 4m + 2k + 1 (group g, m = 0..15, k = 0, 1) at byte
- * 4m + 2g + k, key rows the pair 2i, 2i + 1 at byte i; in both the even
- * element is in the high nibble.  Arguments and errors as for
+ * 4m + 2g + k, key rows the pair 64h + 16c + 2j, +1 (h = 0, 1, c = 0..3,
+ * j = 0..7) at byte 16c + 8h + j; in both the even element is in the high
+ * nibble.  Arguments and errors as for
  * kvq8_quantize_append.
  */
 int kvq4_quantize_append(uint8_t* k_cache, uint8_t* v_cache,

@@ -68,6 +68,25 @@ def pool_library_order(pool):
     return out.reshape(pool.shape)
 
 
+# The library's storage order of an int4 key row: 8-byte part 2c + h holds the
+# pages' part 4h + c (pairs 32h + 8c .. +7, codes 64h + 16c .. +15).
+Q4_KEY_PAGES_PART = np.array([2 * (p % 4) + p // 4 for p in range(8)])     # pages part p <- library part
+Q4_KEY_LIBRARY_PART = np.array([4 * (p % 2) + p // 2 for p in range(8)])   # library part p <- pages part
+
+
+def q4_key_pages_order(pool):
+    """An int4 key pool [..][64] as the library stores it -> the pages' row
+    layout (pair i in byte i), as the oracle keeps it."""
+    pool = np.asarray(pool)
+    return pool.reshape(pool.shape[:-1] + (8, 8))[..., Q4_KEY_PAGES_PART, :].reshape(pool.shape)
+
+
+def q4_key_library_order(pool):
+    """The inverse of q4_key_pages_order."""
+    pool = np.asarray(pool)
+    return pool.reshape(pool.shape[:-1] + (8, 8))[..., Q4_KEY_LIBRARY_PART, :].reshape(pool.shape)
+
+
 class Q8Cache:
     """An int8 paged cache held both on the host (oracle) and on the GPU."""
 

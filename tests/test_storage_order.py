@@ -1,0 +1,46 @@
+"""The library's storage orders, as the header states them, against the test
+helpers that convert device pools to the pages' layout (CPU only):
+
+* int4 key rows: the pair starting at element 64h + 16c + 2j (h = 0, 1;
+  c = 0..3; j = 0..7) sits in byte 16c + 8h + j, even element in the high
+  nibble; the pages' layout (the oracle's) keeps pair i in byte i.
+* int8 / Q4_0 code pools: head kh of slot s at column (kh & ~(P-1)) |
+  ((kh + s) & (P-1)), P the largest power of two dividing nkv, at most 8."""
+import numpy as np
+
+from oracle import kvq4 as O4
+from tests.helpers import pool_columns, pool_library_order, pool_pages_order, q4_key_library_order, q4_key_pages_order
+
+
+def test_q4_key_order_matches_header_formula():
+    codes = (np.arange(128) * 7 + 3) % 16                    # every pair distinct enough to locate
+    pages = O4.pack_nibbles(codes.astype(np.uint8))          # pair i in byte i
+    lib = q4_key_library_order(pages[None])[0]
+    for h in range(2):
+        for c in range(4):
+            for j in range(8):
+                e = 64 * h + 16 * c + 2 * j
+                assert lib[16 * c + 8 * h + j] == (codes[e] << 4 | codes[e + 1]), (h, c, j)
+    assert np.array_equal(q4_key_pages_order(lib[None])[0], pages)
+
+
+def test_q4_key_order_round_trip():
+    r = np.random.default_rng(3)
+    x = r.integers(0, 256, (5, 16, 3, 64), dtype=np.uint8)
+    assert np.array_equal(q4_key_pages_order(q4_key_library_order(x)), x)
+    assert np.array_equal(q4_key_library_order(q4_key_pages_order(x)), x)
+    assert not np.array_equal(q4_key_library_order(x), x)
+
+
+def test_int8_rotation_matches_header_formula():
+    for nkv in range(1, 17):
+        p = 1
+        while nkv % (2 * p) == 0 and 2 * p <= 8:
+            p *= 2
+        col = pool_columns(40, nkv)
+        for s in range(40):
+            assert sorted(col[s]) == list(range(nkv))        # a permutation of the row's columns
+            for kh in range(nkv):
+                assert col[s, kh] == (kh & ~(p - 1)) | ((kh + s) & (p - 1))
+        x = np.random.default_rng(nkv).integers(-127, 128, (5, 8, nkv, 128)).astype(np.int8)
+        assert np.array_equal(pool_pages_order(pool_library_order(x)), x)
