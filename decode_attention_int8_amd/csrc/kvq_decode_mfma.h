@@ -188,7 +188,9 @@ __device__ __forceinline__ void mtile_issue(const DecodeArgs& a, int raw, int ba
     // stays a select and never becomes an indexed array
     auto grp = [&](int i) __attribute__((always_inline)) -> uint32_t {
         const int idi = __builtin_amdgcn_readlane(id, 8 * i);
-        return idi >= 0 ? ((((uint32_t)idi << a.log2_bs) + (((uint32_t)base + 8 * i) & bs_mask)) * nkv) : 0u;
+        // a block outside the pool reads block 0 (in bounds; its tokens are masked)
+        const uint32_t idc = (uint32_t)max(idi, 0);
+        return ((idc << a.log2_bs) + (((uint32_t)base + 8 * i) & bs_mask)) * nkv;
     };
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
