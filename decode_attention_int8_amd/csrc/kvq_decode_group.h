@@ -117,11 +117,17 @@ __global__ __launch_bounds__(kWGThreads, 2) void kvq4_decode_mfma_kernel(Args a)
     const int rest = wg >> 3;
     const int kh = rest % a.nkv;
     const int p = (rest / a.nkv) * 8 + (wg & 7);
-    const int b = p / pair_stride(nct, a.batch);
-    const int c = p - b * pair_stride(nct, a.batch);
-    if (b >= a.batch || c >= nct) return;
+    // The heaviest chunks first: rank r = p / batch runs over the int8
+    // window's chunks, then the int4 band's, then the 2-bit band's, each for
+    // every sequence (b = p % batch), so the workgroups dispatched last are the
+    // lightest ones.  Pair p runs on XCD p % 8 with its nkv workgroups.
     int m2 = 0;
     if constexpr (HAS2) m2 = a.r2.max_chunks;
+    const int n4c = a.r4.max_chunks, n8c = a.r8.max_chunks;
+    const int b = p % a.batch;
+    const int r = p / a.batch;
+    if (r >= nct) return;
+    const int c = r < n8c ? m2 + n4c + r : (r < n8c + n4c ? m2 + (r - n8c) : r - n8c - n4c);
     const int kind = (HAS2 && c < m2) ? 2 : (c < m2 + a.r4.max_chunks ? 4 : 8);
     const Region* regp = kind == 4 ? &a.r4 : &a.r8;
     if constexpr (HAS2) {
