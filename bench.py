@@ -181,8 +181,8 @@ def _oracle_units_worker(job):
 
 
 def host_workers() -> int:
-    """Host cores this process may use, at most 16 (a GPU machine's share of its
-    host)."""
+    """Host cores this process may use, at most 16 (the share of a shared
+    host's cores that goes with one GPU)."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
@@ -588,7 +588,7 @@ def main():
         run_workloads([n for n in args.only.split(",") if n])
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build has no multi-GPU path)",
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the library has no multi-GPU path)",
               file=sys.stderr)
         sys.exit(2)
     import workloads as W
