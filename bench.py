@@ -330,6 +330,12 @@ def run_workloads(only=None):
                 torch.zeros(shp + (64,), dtype=torch.uint8, device="cuda")] + \
                [torch.zeros(shp + (2,), dtype=torch.float16, device="cuda") for _ in range(4)]
 
+    def q2_pool(nb, bs, nkv):
+        shp = (nb, bs, nkv)
+        return [torch.zeros(shp + (32,), dtype=torch.uint8, device="cuda"),
+                torch.zeros(shp + (32,), dtype=torch.uint8, device="cuda")] + \
+               [torch.zeros(shp + (2,), dtype=torch.float16, device="cuda") for _ in range(4)]
+
     if want("unit_256"):
         # unit experiment: 1 / 1 heads, 256 tokens (launch-bound)
         q, k, v = W.unit_experiment(0)
@@ -391,6 +397,29 @@ def run_workloads(only=None):
         del pools
         del p
 
+    if want("q4_append_64k", "q2_append_64k"):
+        # the group write paths on the 64K bf16 rows of the int8 write workload
+        cfg = W.APPEND_64K
+        n, nkv, bs = cfg["n_tok"], cfg["nkv"], cfg["kv_bs"]
+        bt, nb = W.paged_block_tables(W.rng(4, 0, 1), [n], bs)
+        kk = W.torch_outlier_normal_bf16((n, nkv, 128), "cuda", (4, 0, 0))
+        vv = W.torch_outlier_normal_bf16((n, nkv, 128), "cuda", (4, 0, 1))
+        slots = dev(W.slots_for_positions(bt, [0] * n, np.arange(n), bs))
+        if want("q4_append_64k"):
+            p4 = q4_pool(nb, bs, nkv)
+            us = time_calls(torch, lambda: K.kvq4_quantize_append(*p4, kk, vv, slots), 50, warmup=30)
+            # per (token, kv-head): K and V rows read (bf16), codes + binary16 scale / zero of both groups written
+            report("q4_append_64k", "int4 write path, 65536 tokens x 8 kv heads from bf16",
+                   n * nkv * (2 * 128 * 2 + 2 * (64 + 8)), us)
+            del p4
+        if want("q2_append_64k"):
+            p2 = q2_pool(nb, bs, nkv)
+            us = time_calls(torch, lambda: K.kvq2_quantize_append(*p2, kk, vv, slots), 50, warmup=30)
+            report("q2_append_64k", "2-bit write path, 65536 tokens x 8 kv heads from bf16",
+                   n * nkv * (2 * 128 * 2 + 2 * (32 + 8)), us)
+            del p2
+        del kk, vv
+
     if want("q4_128k", "requant_block", "requant_window"):
         # int4 group cache, 128K tokens (last 2048 int8), batch 4 x 32 / 4 heads
         cfg = W.Q4_128K
@@ -440,12 +469,6 @@ def run_workloads(only=None):
         report("requant_window", "int8 -> int4 re-quantization of the whole 2048-token window x 4 sequences",
                n_all * nkv * (264 + 144), us)
         del p4, p8
-
-    def q2_pool(nb, bs, nkv):
-        shp = (nb, bs, nkv)
-        return [torch.zeros(shp + (32,), dtype=torch.uint8, device="cuda"),
-                torch.zeros(shp + (32,), dtype=torch.uint8, device="cuda")] + \
-               [torch.zeros(shp + (2,), dtype=torch.float16, device="cuda") for _ in range(4)]
 
     if want("q2_128k", "requant2_block"):
         # three bands, 128K tokens: 114688 2-bit + 14336 int4 + 2048 int8, batch 4 x 32 / 4 heads

@@ -69,18 +69,35 @@ __device__ __forceinline__ void quantize_group8x8_q2(const float (&x)[8], uint32
     const float z = fminf(fmaxf(rintf(-mn / s), 0.0f), 3.0f) + 0.0f;
     z16 = __builtin_bit_cast(uint16_t, (_Float16)z);
     const float rs = __builtin_amdgcn_rcpf(s);
-    uint32_t w = 0;
+    // code = clamp(rint(x / s + z), 0, 3) with z an integer, the quotient
+    // computed only near a half-integer.  Elsewhere the clamped q + z plus
+    // 1.5 * 2^23 holds rint(q + z) in its low byte (the addition rounds half
+    // to even like rint); the codes are gathered by byte permutes and a dot
+    // product with (1, 4, 16, 64).
+    constexpr float kMagic = 12582912.0f;
+    uint32_t cb[8];
+    bool slow[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        // rint(x / s + z) with z an integer, the quotient computed only near a
-        // half-integer
         const float q = x[e] * rs;
-        float c = rintf(q + z);
-        if (near_half(q)) c = rintf(x[e] / s + z);
-        c = fminf(fmaxf(c, 0.0f), 3.0f);
-        w |= (uint32_t)c << (2 * e);
+        slow[e] = near_half(q);
+        cb[e] = __float_as_uint(__builtin_amdgcn_fmed3f(q + z, 0.0f, 3.0f) + kMagic);
     }
-    codes = w;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        if (__builtin_amdgcn_ballot_w64(slow[e]) != 0) {      // rare: one wave-uniform test per value
+            const float cd = fminf(fmaxf(rintf(x[e] / s + z), 0.0f), 3.0f);
+            cb[e] = slow[e] ? (uint32_t)(int)cd : cb[e];
+        }
+    }
+    uint32_t w[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t b = __builtin_amdgcn_perm(cb[4 * h + 1], cb[4 * h], 0x0C0C0400u) |
+                           __builtin_amdgcn_perm(cb[4 * h + 3], cb[4 * h + 2], 0x04000C0Cu);
+        w[h] = __builtin_amdgcn_udot4(b, 0x40100401u, 0u, false);     // c0 + 4 c1 + 16 c2 + 64 c3
+    }
+    codes = w[0] | (w[1] << 8);
 }
 
 // Store one row.  Lane l16 holds elements 8 l16 + e: group h = l16 / 8, and

@@ -64,22 +64,36 @@ __device__ __forceinline__ void quantize_group8x8(const float (&x)[8], uint32_t&
     const float z = fminf(fmaxf(rintf(-mn / s), 0.0f), 15.0f) + 0.0f;
     z16 = f16_bits_rne(z);
     const float rs = __builtin_amdgcn_rcpf(s);
-    // rint(x / s + z) with z an integer, the quotient computed only near a
-    // half-integer
-    auto code = [&](float xv) __attribute__((always_inline)) {
-        const float q = xv * rs;
-        float c = rintf(q + z);
-        if (near_half(q)) c = rintf(xv / s + z);
-        return fminf(fmaxf(c, 0.0f), 15.0f);
-    };
-    uint32_t w = 0;
+    // code = clamp(rint(x / s + z), 0, 15) with z an integer, the quotient
+    // computed only near a half-integer.  Elsewhere the clamped q + z plus
+    // 1.5 * 2^23 holds rint(q + z) in its low byte (the addition rounds half
+    // to even like rint), so the codes are gathered with byte permutes.
+    constexpr float kMagic = 12582912.0f;
+    uint32_t cb[8];
+    bool slow[8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const float ce = code(x[2 * k]);
-        const float co = code(x[2 * k + 1]);
-        w |= (((uint32_t)ce << 4) | (uint32_t)co) << (8 * k);
+    for (int e = 0; e < 8; ++e) {
+        const float q = x[e] * rs;
+        slow[e] = near_half(q);
+        cb[e] = __float_as_uint(__builtin_amdgcn_fmed3f(q + z, 0.0f, 15.0f) + kMagic);
     }
-    packed = w;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        if (__builtin_amdgcn_ballot_w64(slow[e]) != 0) {      // rare: one wave-uniform test per value
+            const float cd = fminf(fmaxf(rintf(x[e] / s + z), 0.0f), 15.0f);
+            cb[e] = slow[e] ? (uint32_t)(int)cd : cb[e];
+        }
+    }
+    // bytes [c0, c1, c2, c3] and [c4 .. c7]; (b << 4) | (b >> 8) puts the
+    // pairs (c0, c1) and (c2, c3) in bytes 0 and 2, even element high
+    uint32_t pr[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t b = __builtin_amdgcn_perm(cb[4 * h + 1], cb[4 * h], 0x0C0C0400u) |
+                           __builtin_amdgcn_perm(cb[4 * h + 3], cb[4 * h + 2], 0x04000C0Cu);
+        pr[h] = (b << 4) | (b >> 8);
+    }
+    packed = __builtin_amdgcn_perm(pr[1], pr[0], 0x06040200u);
 }
 
 constexpr int kRowsPerGroup = 4;            // rows per 16-lane group, loads first
