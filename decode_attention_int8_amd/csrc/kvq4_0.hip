@@ -95,20 +95,20 @@ __device__ __forceinline__ void q40_quantize8(const float (&x)[8], uint32_t& lo,
     step = zero ? 0.0f : m * -0.125f;                // exact: a power-of-two division
     const float rs = __builtin_amdgcn_rcpf(step);
     uint32_t cb[8];                                  // low byte: the code (16 for q = +8)
-    bool slow[8];
+    uint64_t slow[8];                                // wave masks of the lanes that divide
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const float q = x[e] * rs;                   // |x / step| <= 8
         const float f = q + kMagic;
         const float rq = f - kMagic;                 // rint(q)
-        slow[e] = !zero && near_half_small(q, rq);
+        slow[e] = __builtin_amdgcn_ballot_w64(near_half_small(q, rq));   // a zero block (q = NaN) too
         cb[e] = __float_as_uint(f);
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        if (__builtin_amdgcn_ballot_w64(slow[e]) != 0) {      // rare: one wave-uniform test per value
+        if (slow[e] != 0) {                         // rare: one wave-uniform test per value
             const float cd = fminf(floorf(x[e] / step + 8.5f), 15.0f);
-            cb[e] = slow[e] ? (uint32_t)(int)cd : cb[e];
+            cb[e] = ((slow[e] >> (threadIdx.x & 63)) & 1) ? (uint32_t)(int)cd : cb[e];
         }
     }
     uint32_t w[2];
