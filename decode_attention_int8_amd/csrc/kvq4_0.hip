@@ -33,166 +33,213 @@ namespace kvq {
 // write path
 // ----------------------------------------------------------------------------
 
-// Rows per 16-lane group; a 256-thread workgroup quantizes 64 rows.
+// Rows per 8-lane group; a 256-thread workgroup quantizes 128 rows.
 constexpr int kQ40RowsPerGroup = 4;
-constexpr int kQ40RowsPerBlock = 16 * kQ40RowsPerGroup;
+constexpr int kQ40RowsPerBlock = 32 * kQ40RowsPerGroup;
+
+// A lane's 16 input values as loaded: 16 float32 or 16 half-width values.
+template <int DT>
+struct Q40Raw {
+    uint4 u[DT == KVQ8_F32 ? 4 : 2];
+};
 
 template <int DT>
-__device__ __forceinline__ void q40_load8(const void* base, size_t elem_off, float (&x)[8]) {
-    if constexpr (DT == KVQ8_F32) {
-        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem_off);
-        const float4 a = p[0], b = p[1];
-        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-    } else {
-        const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem_off);
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+__device__ __forceinline__ void q40_load16(const void* base, size_t byte_off, Q40Raw<DT>& r) {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const char*>(base) + byte_off);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if constexpr (DT == KVQ8_BF16) {
-                x[2 * i] = __uint_as_float(w[i] << 16);
-                x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    for (int i = 0; i < (DT == KVQ8_F32 ? 4 : 2); ++i) r.u[i] = p[i];
+}
+
+template <int DT>
+__device__ __forceinline__ void q40_unpack16(const Q40Raw<DT>& r, float (&x)[16]) {
+#pragma unroll
+    for (int i = 0; i < (DT == KVQ8_F32 ? 4 : 2); ++i) {
+        const uint32_t w[4] = {r.u[i].x, r.u[i].y, r.u[i].z, r.u[i].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if constexpr (DT == KVQ8_F32) {
+                x[4 * i + j] = __uint_as_float(w[j]);
+            } else if constexpr (DT == KVQ8_BF16) {
+                x[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
+                x[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
             } else {
-                x[2 * i] = half_bits_f(w[i] & 0xFFFFu);
-                x[2 * i + 1] = half_bits_f(w[i] >> 16);
+                x[8 * i + 2 * j] = half_bits_f(w[j] & 0xFFFFu);
+                x[8 * i + 2 * j + 1] = half_bits_f(w[j] >> 16);
             }
         }
     }
 }
 
-// A row of 128 values is spread over 16 lanes: lane l16 = 4r + k holds the
-// 8 values 32k + 8r .. 32k + 8r + 7, so lane k of every quad holds block k
-// and the four lanes of block k sit 4 apart.  Both byte layouts are then
-// built inside quads (key bytes pair element j with j + 64: lanes k and
-// k ^ 2; value words gather one byte from each block: a 4 x 4 byte transpose
-// in the quad) and the block extremes are two row rotations.
+// A row of 128 values is spread over 8 lanes, 16 values each: block k's
+// first half (values 32k .. 32k + 15) on lane k, its second half on lane
+// 7 - k.  A block's extreme is then one half-row mirror, key bytes pair
+// lanes 2 apart (blocks k and k + 2, same half) and each quad holds one half
+// of all four blocks (lanes 0..3 in block order, lanes 4..7 reversed).
 //
-// Codes of a lane's 8 values, one byte each, and its block's step.  The code
-// is floor(x / step + 8.5) clamped to 15: rint(x * rcp(step)) + 8 where
-// x * rcp(step) is not within 2^-11 of a half-integer; elsewhere (about 0.1%
-// of the values, or a quotient that is not finite) the lane divides.  A zero
-// block has step +0 and codes 8.  rint(q) + 8 is the low byte of q + 1.5 *
-// 2^23 + 8 (|q| <= 8: the sum's unit is 1, and the addition rounds half to
-// even like rint); four such bytes are gathered by two byte permutes, and
-// the one code that can reach 16 (q = +8) is brought to 15 on the packed
+// Codes of a lane's 16 values, one byte each (c[h] holds values 4h .. 4h + 3),
+// and its block's step.
+//
+// The block extreme is the value of largest magnitude, the negative one on a
+// tie: the largest of the keys rotl(bits, 1) (magnitude above, sign in bit
+// 0) as unsigned integers.
+//
+// The code is floor(x / step + 8.5) clamped to 15.  f = fma(x, rcp(step),
+// 136.5 + 2^-15) lies in [128, 256), so its unit is 2^-16: the mantissa is
+// (x * rcp(step) + 8.5) * 2^16, rounded, plus 2.  Bits 16..23 of f are then
+// the code (the exponent's low bit is 0) and bits 0..15 the fraction plus 2.
+// Where those low bits are 0..3 the quotient + 8.5 lies within 2^-15 of an
+// integer and the lane divides instead (about 0.01% of the values, and every
+// value of a zero block, whose quotients are NaN).  Elsewhere it lies at
+// least 1.5 * 2^-16 from one, far more than one rcp error (8 * 2^-23) plus
+// the division's and the addition's roundings, so the floor read from f is
+// the floor of the correctly rounded x / step + 8.5.  A zero block has step
+// +0 and codes 8.  Four code bytes are gathered by two byte permutes, and
+// the one code that can reach 16 (q >= 7.5) is brought to 15 on the packed
 // word.
-__device__ __forceinline__ void q40_quantize8(const float (&x)[8], uint32_t& lo, uint32_t& hi, float& step) {
+__device__ __forceinline__ void q40_quantize16(const float (&x)[16], uint32_t (&c)[4], float& step) {
 #pragma clang fp contract(off)
-    constexpr float kMagic = 12582920.0f;            // 1.5 * 2^23 + 8
-    float mx = x[0], mn = x[0];
+    constexpr float kMagic = 136.500030517578125f;   // 128 + 8.5 + 2^-15
+    uint32_t km = 0;
 #pragma unroll
-    for (int e = 1; e < 8; ++e) {
-        mx = fmaxf(mx, x[e]);
-        mn = fminf(mn, x[e]);
+    for (int e = 0; e < 16; ++e) {
+        const uint32_t u = __float_as_uint(x[e]);
+        km = max(km, __builtin_amdgcn_alignbit(u, u, 31u));   // rotl(u, 1)
     }
-    // the block's four lanes: 4 and 8 apart in the 16-lane row
-    mx = fmaxf(mx, dpp_f<kDppRowRor8>(mx));
-    mn = fminf(mn, dpp_f<kDppRowRor8>(mn));
-    mx = fmaxf(mx, dpp_f<kDppRowRor4>(mx));
-    mn = fminf(mn, dpp_f<kDppRowRor4>(mn));
-    const float m = (-mn >= mx) ? mn : mx;           // negative extreme wins a tie
-    const bool zero = m == 0.0f;
-    step = zero ? 0.0f : m * -0.125f;                // exact: a power-of-two division
+    km = max(km, (uint32_t)dpp_i<kDppHalfMirror>((int)km));   // the block's other lane
+    const float m = __uint_as_float(__builtin_amdgcn_alignbit(km, km, 1u));   // rotr(km, 1)
+    step = km < 2u ? 0.0f : m * -0.125f;             // exact: a power-of-two division
     const float rs = __builtin_amdgcn_rcpf(step);
-    uint32_t cb[8];                                  // low byte: the code (16 for q = +8)
-    uint64_t slow[8];                                // wave masks of the lanes that divide
+    uint32_t cb[16];                                 // byte 2: the code (16 for q >= 7.5)
+    uint64_t slow[16];                               // wave masks of the lanes that divide
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const float q = x[e] * rs;                   // |x / step| <= 8
-        const float f = q + kMagic;
-        const float rq = f - kMagic;                 // rint(q)
-        slow[e] = __builtin_amdgcn_ballot_w64(near_half_small(q, rq));   // a zero block (q = NaN) too
-        cb[e] = __float_as_uint(f);
+    for (int e = 0; e < 16; ++e) {
+        cb[e] = __float_as_uint(__builtin_fmaf(x[e], rs, kMagic));
+        slow[e] = __builtin_amdgcn_ballot_w64((uint16_t)cb[e] <= 3u);
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < 16; ++e) {
         if (slow[e] != 0) {                         // rare: one wave-uniform test per value
-            const float cd = fminf(floorf(x[e] / step + 8.5f), 15.0f);
-            cb[e] = ((slow[e] >> (threadIdx.x & 63)) & 1) ? (uint32_t)(int)cd : cb[e];
+            const float cd = step == 0.0f ? 8.0f : fminf(floorf(x[e] / step + 8.5f), 15.0f);
+            cb[e] = ((slow[e] >> (threadIdx.x & 63)) & 1) ? (uint32_t)(int)cd << 16 : cb[e];
         }
     }
-    uint32_t w[2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const uint32_t v = __builtin_amdgcn_perm(cb[4 * h + 1], cb[4 * h], 0x0C0C0400u) |
-                           __builtin_amdgcn_perm(cb[4 * h + 3], cb[4 * h + 2], 0x04000C0Cu);
-        w[h] = v - ((v >> 4) & 0x01010101u);         // 16 -> 15, codes 0..15 unchanged
+    for (int h = 0; h < 4; ++h) {
+        const uint32_t v = __builtin_amdgcn_perm(cb[4 * h + 1], cb[4 * h], 0x0C0C0602u) |
+                           __builtin_amdgcn_perm(cb[4 * h + 3], cb[4 * h + 2], 0x06020C0Cu);
+        c[h] = v - ((v >> 4) & 0x01010101u);         // 16 -> 15, codes 0..15 unchanged
     }
-    lo = zero ? 0x08080808u : w[0];
-    hi = zero ? 0x08080808u : w[1];
 }
 
-// Quad transpose of value bytes: lane q of a quad holds W = [P0 P1 P2 P3]
-// (the packed pairs of its block); it returns [byte q of W from quad lanes
-// 0, 1, 2, 3], the value row word that takes one byte from every block.
-__device__ __forceinline__ uint32_t q40_value_word(uint32_t W, int q) {
+// Byte selectors of the quad gather of value bytes, fixed per lane: the lane
+// at quad position q builds the value word whose byte k comes from byte q of
+// the word W held by the quad lane of block k (position k, or 3 - k in the
+// second quad of the 8-lane group).  Sources are W itself and W of the lanes
+// q + 1, q + 2, q + 3 (mod 4), two per byte permute.
+struct Q40Gather {
+    uint32_t lo, hi;     // selectors over (W of lane q + 1 : W) and (W of lane q + 3 : W of lane q + 2)
+};
+
+__device__ __forceinline__ Q40Gather q40_gather_selectors(int q, bool reversed) {
+    Q40Gather s{0, 0};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int src = reversed ? 3 - k : k;
+        const int j = (src - q) & 3;
+        const uint32_t b = (uint32_t)((j & 1) ? 4 + q : q);
+        s.lo |= (j < 2 ? b : 0x0Cu) << (8 * k);
+        s.hi |= (j >= 2 ? b : 0x0Cu) << (8 * k);
+    }
+    return s;
+}
+
+__device__ __forceinline__ uint32_t q40_value_word(uint32_t W, const Q40Gather& s) {
     const uint32_t q1 = (uint32_t)dpp_i<kDppQuadRot1>((int)W);   // lane q + 1
     const uint32_t q2 = (uint32_t)dpp_i<kDppXor2>((int)W);       // lane q + 2
     const uint32_t q3 = (uint32_t)dpp_i<kDppQuadRot3>((int)W);   // lane q + 3
-    // Z byte j = byte q of lane q + j's word
-    const uint32_t sel_lo = (uint32_t)q | ((uint32_t)(4 + q) << 8) | 0x0C0C0000u;
-    const uint32_t sel_hi = 0x00000C0Cu | ((uint32_t)q << 16) | ((uint32_t)(4 + q) << 24);
-    const uint32_t Z = __builtin_amdgcn_perm(q1, W, sel_lo) | __builtin_amdgcn_perm(q3, q2, sel_hi);
-    // byte t must come from lane t = q + j: rotate left by q bytes
-    return __builtin_amdgcn_alignbit(Z, Z, (32u - 8u * (uint32_t)q) & 31u);
+    return __builtin_amdgcn_perm(q1, W, s.lo) | __builtin_amdgcn_perm(q3, q2, s.hi);
 }
 
-// One (token, kv-head, K-or-V) row per 16 lanes, 4 rows per 16-lane group;
+// One (token, kv-head, K-or-V) row per 8 lanes, 4 rows per 8-lane group;
 // a wave quantizes only key rows or only value rows (kind = wave & 1).
+// Row numbers of the pool (slot * nkv + head) fit in 32 bits: the host
+// checks n_slots * nkv, and ns_cap = min(n_slots, 2^31) turns the slot test
+// into one unsigned compare.
 template <int DT>
 __global__ __launch_bounds__(256) void kvq4_0_quantize_append_kernel(
     uint8_t* __restrict__ kc, uint8_t* __restrict__ vc, float* __restrict__ ks, float* __restrict__ vs,
-    long n_slots, DivN nkv, const void* __restrict__ k_new, const void* __restrict__ v_new, int n_rows,
+    uint32_t ns_cap, DivN nkv, const void* __restrict__ k_new, const void* __restrict__ v_new, int n_rows,
     const int32_t* __restrict__ slots) {
-    const int l16 = threadIdx.x & 15;
-    const int qk = l16 & 3;                        // block of the lane's values
-    const int qr = l16 >> 2;                       // their place in the block
+    constexpr int kInBytes = DT == KVQ8_F32 ? 4 : 2;
+    const int l8 = threadIdx.x & 7;
+    const int half = l8 >> 2;                      // 0: first halves of the blocks, 1: second halves
+    const int q = l8 & 3;                          // quad position
+    const int kb = half ? 3 - q : q;               // block of the lane's values
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int kind = wave & 1;                     // 0: key rows, 1: value rows
-    const int g4 = (threadIdx.x >> 4) & 3;         // 16-lane group in the wave
-    float x[kQ40RowsPerGroup][8];
-    long dst[kQ40RowsPerGroup];    // destination row (slot * nkv + head), -1 to skip
-    long cdst[kQ40RowsPerGroup];   // its code row (slot * nkv + column, the storage order q8_col)
+    const int g8 = (threadIdx.x >> 3) & 7;         // 8-lane group in the wave
+    const void* src = kind ? v_new : k_new;
+    uint8_t* codes = kind ? vc : kc;
+    float* steps = kind ? vs : ks;
+    const uint32_t in_off = (uint32_t)(32 * kb + 16 * half) * kInBytes;
+    const Q40Gather gsel = q40_gather_selectors(q, half != 0);
+    const int rot = q8_rot_group(nkv.n);
+    Q40Raw<DT> raw[kQ40RowsPerGroup];
+    int trs[kQ40RowsPerGroup];
     // rows past the end load the last row again and store nothing; indices
     // fit in 32 bits (the host checks the row count)
 #pragma unroll
     for (int k = 0; k < kQ40RowsPerGroup; ++k) {
-        const int pair = (int)blockIdx.x * (kQ40RowsPerBlock / 2) + (wave >> 1) * 16 + g4 * 4 + k;
-        const int row = 2 * pair + kind;
-        const int tr = min(row, n_rows - 1) >> 1;  // token * nkv + kv-head
-        const int tok = div_n(tr, nkv);
-        q40_load8<DT>(kind ? v_new : k_new, (size_t)tr * kHD + 32 * qk + 8 * qr, x[k]);
-        const long slot = slots[tok];
-        const int kh = tr - tok * nkv.n;
-        dst[k] = (row < n_rows && slot >= 0 && slot < n_slots) ? slot * nkv.n + kh : -1;
-        cdst[k] = slot * nkv.n + q8_col(kh, slot, q8_rot_group(nkv.n));
+        const int pair = (int)blockIdx.x * (kQ40RowsPerBlock / 2) + ((wave >> 1) * 8 + g8) * kQ40RowsPerGroup + k;
+        trs[k] = min(2 * pair + kind, n_rows - 1) >> 1;   // token * nkv + kv-head
+        q40_load16<DT>(src, (size_t)trs[k] * (kHD * kInBytes) + in_off, raw[k]);
     }
 #pragma unroll
     for (int k = 0; k < kQ40RowsPerGroup; ++k) {
-        uint32_t lo, hi;
+        const int pair = (int)blockIdx.x * (kQ40RowsPerBlock / 2) + ((wave >> 1) * 8 + g8) * kQ40RowsPerGroup + k;
+        const int tr = trs[k];
+        const int tok = div_n(tr, nkv);
+        const uint32_t slot = (uint32_t)slots[tok];
+        const int kh = tr - tok * nkv.n;
+        float x[16];
+        q40_unpack16<DT>(raw[k], x);
+        uint32_t c[4];
         float step;
-        q40_quantize8(x[k], lo, hi, step);          // every lane of the row takes part (DPP)
-        uint32_t word, off;
+        q40_quantize16(x, c, step);                 // both lanes of a block take part (DPP)
+        uint32_t w0, w1;
+        uint32_t off;
         if (kind == 0) {
-            // key byte j = code[j] | code[64 + j] << 4: blocks k and k + 2
-            // are quad lanes q and q ^ 2; lanes of blocks 0, 1 write the low
-            // 4 bytes of their 8, their partners the high 4
-            const bool low = qk < 2;
-            const uint32_t recv = (uint32_t)dpp_i<kDppXor2>((int)(low ? hi : lo));
-            word = low ? (lo | (recv << 4)) : (recv | (hi << 4));
-            off = 32u * (uint32_t)(qk & 1) + 8u * (uint32_t)qr + (low ? 0u : 4u);
+            // key byte j = code[j] | code[64 + j] << 4: blocks k and k + 2 of
+            // one half are quad lanes q and q ^ 2; the block 0 / 1 lane
+            // writes the low 8 of their 16 bytes, its partner the high 8
+            const bool low = kb < 2;
+            const uint32_t r0 = (uint32_t)dpp_i<kDppXor2>((int)(low ? c[2] : c[0]));
+            const uint32_t r1 = (uint32_t)dpp_i<kDppXor2>((int)(low ? c[3] : c[1]));
+            w0 = low ? (c[0] | (r0 << 4)) : (r0 | (c[2] << 4));
+            w1 = low ? (c[1] | (r1 << 4)) : (r1 | (c[3] << 4));
+            off = 32u * (uint32_t)(kb & 1) + 16u * (uint32_t)half + (low ? 0u : 8u);
         } else {
             // value byte 4m + kb = code[32 kb + 2m] | code[32 kb + 2m + 1] << 4:
-            // the lane's pairs m = 4r .. 4r + 3 of block k, then one byte of
-            // every block per word
-            const uint32_t a = lo | (lo >> 4), b = hi | (hi >> 4);  // bytes 0, 2: the pairs
-            const uint32_t W = __builtin_amdgcn_perm(b, a, 0x06040200u);
-            word = q40_value_word(W, qk);
-            off = 16u * (uint32_t)qr + 4u * (uint32_t)qk;
+            // the lane's pairs m = 8 half .. 8 half + 7 of block kb, then one
+            // byte of every block per word: words m = 8 half + q and m + 4
+            uint32_t a[4];
+#pragma unroll
+            for (int h = 0; h < 4; ++h) a[h] = c[h] | (c[h] >> 4);   // bytes 0, 2: the pairs
+            w0 = q40_value_word(__builtin_amdgcn_perm(a[1], a[0], 0x06040200u), gsel);
+            w1 = q40_value_word(__builtin_amdgcn_perm(a[3], a[2], 0x06040200u), gsel);
+            off = 32u * (uint32_t)half + 4u * (uint32_t)q;
         }
-        if (dst[k] < 0) continue;                    // uniform per 16-lane row
-        *reinterpret_cast<uint32_t*>((kind ? vc : kc) + (size_t)cdst[k] * (kHD / 2) + off) = word;
-        if (qr == 0) (kind ? vs : ks)[dst[k] * 4 + qk] = step;
+        if (2 * pair + kind >= n_rows || slot >= ns_cap) continue;   // uniform per 8-lane row
+        const uint32_t drow = slot * (uint32_t)nkv.n + (uint32_t)kh;
+        const uint32_t crow = slot * (uint32_t)nkv.n + (uint32_t)q8_col(kh, slot, rot);
+        uint8_t* dst = codes + (size_t)crow * (kHD / 2) + off;
+        if (kind == 0) {
+            *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
+        } else {
+            *reinterpret_cast<uint32_t*>(dst) = w0;
+            *reinterpret_cast<uint32_t*>(dst + 16) = w1;
+        }
+        if (half == 0) steps[(size_t)drow * 4 + kb] = step;
     }
 }
 
@@ -605,21 +652,25 @@ extern "C" int kvq4_0_quantize_append(uint8_t* k_cache, uint8_t* v_cache, float*
     const long n_rows = (long)n_tokens * nkv * 2;
     if (n_rows > 0x7FFFFFFFL - kQ40RowsPerBlock) return KVQ8_ESHAPE;
     const long n_slots = (long)n_blocks * kv_bs;
+    // pool rows (slot * nkv + head) are 32-bit in the kernel: more than 2^32
+    // rows would take over 320 GiB of codes and steps
+    if (n_slots * nkv > 0xFFFFFFFFL) return KVQ8_ESHAPE;
+    const uint32_t ns_cap = (uint32_t)(n_slots < 0x80000000L ? n_slots : 0x80000000L);
     const dim3 grid((unsigned)((n_rows + kQ40RowsPerBlock - 1) / kQ40RowsPerBlock)), block(256);
     hipStream_t s = static_cast<hipStream_t>(stream);
     int st;
     switch (dtype) {
         case KVQ8_F32:
             st = launch(kvq4_0_quantize_append_kernel<KVQ8_F32>, grid, block, s, k_cache, v_cache, k_step,
-                               v_step, n_slots, make_divn(nkv), k_new, v_new, (int)n_rows, slots);
+                               v_step, ns_cap, make_divn(nkv), k_new, v_new, (int)n_rows, slots);
             break;
         case KVQ8_BF16:
             st = launch(kvq4_0_quantize_append_kernel<KVQ8_BF16>, grid, block, s, k_cache, v_cache,
-                               k_step, v_step, n_slots, make_divn(nkv), k_new, v_new, (int)n_rows, slots);
+                               k_step, v_step, ns_cap, make_divn(nkv), k_new, v_new, (int)n_rows, slots);
             break;
         default:
             st = launch(kvq4_0_quantize_append_kernel<KVQ8_F16>, grid, block, s, k_cache, v_cache, k_step,
-                               v_step, n_slots, make_divn(nkv), k_new, v_new, (int)n_rows, slots);
+                               v_step, ns_cap, make_divn(nkv), k_new, v_new, (int)n_rows, slots);
             break;
     }
     return st;

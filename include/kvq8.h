@@ -403,8 +403,10 @@ int kvq4_decode_attn(float* out, const float* q, int batch, int nq,
  * outside [0, n_blocks * kv_bs) are skipped.  Errors: KVQ8_ESHAPE for
  * hd != 128, an invalid kv_bs (a power of two in [8, 1024]), nkv < 1 or
  * n_blocks < 1; KVQ8_EINVAL for a null or misaligned pointer, a bad dtype
- * or n_tokens < 0; KVQ8_ESHAPE also for more than 2^31 - 65 rows
- * (n_tokens * nkv * 2).  n_tokens == 0 enqueues nothing.
+ * or n_tokens < 0; KVQ8_ESHAPE also for more than 2^31 - 129 rows
+ * (n_tokens * nkv * 2) and for a pool of 2^32 or more rows (n_blocks *
+ * kv_bs * nkv; such a pool would hold over 320 GiB).  n_tokens == 0
+ * enqueues nothing.
  */
 int kvq4_0_quantize_append(uint8_t* k_cache, uint8_t* v_cache, float* k_step, float* v_step,
                            int n_blocks, int kv_bs, int nkv, int hd,

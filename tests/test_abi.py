@@ -250,6 +250,7 @@ def test_q4_0_validation_and_sizing():
     assert call(a12=None) == EINVAL
     assert call(a2=_fake(4104)) == EINVAL             # step array not 16-byte aligned
     assert call(a11=1 << 27) == ESHAPE                # 2^31 rows: beyond 32-bit row indexing
+    assert call(a4=1 << 25) == ESHAPE                 # 2^25 x 16 slots x 8 heads: pool rows beyond 32 bits
 
 
 def test_write_row_limit():
