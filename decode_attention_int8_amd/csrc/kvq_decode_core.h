@@ -243,7 +243,7 @@ __device__ __forceinline__ void load_new4(const void* base, size_t elem_off, flo
 }
 
 // Quantize a 128-value row held by an aligned 32-lane half of the wave, 4
-// values per lane (the rule of quantize_row8x16, the maximum over 32 lanes):
+// values per lane (the int8 write path's rule, the maximum over 32 lanes):
 // returns the lane's 4 codes (one word) and the row's step.
 __device__ __forceinline__ void quantize_row32x4(const float (&x)[4], uint32_t& codes, float& d) {
 #pragma clang fp contract(off)
@@ -268,33 +268,6 @@ __device__ __forceinline__ void quantize_row32x4(const float (&x)[4], uint32_t& 
         w |= ((uint32_t)(int)r & 0xFFu) << (8 * e);
     }
     codes = w;
-}
-
-// Quantize a 128-value row held by an aligned 8-lane group, 16 values per
-// lane: returns the lane's 16 codes (packed) and the row's step.
-__device__ __forceinline__ void quantize_row8x16(const float (&x)[16], uint4& codes, float& d) {
-#pragma clang fp contract(off)
-    float amax = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(x[e]));
-    amax = fmaxf(amax, dpp_f<kDppXor1>(amax));
-    amax = fmaxf(amax, dpp_f<kDppXor2>(amax));
-    amax = fmaxf(amax, dpp_f<kDppHalfMirror>(amax));
-    if (amax < 1e-6f) amax = 1.0f;
-    d = amax / 127.0f;
-    const float rd = __builtin_amdgcn_rcpf(d);
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        // roundf(x / d), the quotient computed only near a half-integer
-        // (|x / d| <= 127)
-        const float q = x[e] * rd;
-        float r = rintf(q);
-        if (near_half_small(q, r)) r = roundf(x[e] / d);
-        r = fminf(fmaxf(r, -127.0f), 127.0f);
-        w[e >> 2] |= ((uint32_t)(int)r & 0xFFu) << (8 * (e & 3));
-    }
-    codes = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 // Merge the chunk partials of one (sequence, query head) and normalize

@@ -111,9 +111,11 @@ const char* kvq8_version(void);
  *                     a slot outside [0, n_blocks * kv_bs) is skipped
  *   n_tokens          may be 0 (nothing is launched)
  * Errors: KVQ8_ESHAPE for hd != 128, an invalid kv_bs (a power of two in
- * [8, 1024]), nkv < 1, n_blocks < 1, or n_tokens * nkv * 2 rows above
- * 2^31 - 65; KVQ8_EINVAL for a null or misaligned pointer, a bad dtype or
- * n_tokens < 0.  Tokens with equal slots race (one of them wins).
+ * [8, 1024]), nkv < 1, n_blocks < 1, n_tokens * nkv * 2 rows above
+ * 2^31 - 65, or a pool of 2^32 or more rows (n_blocks * kv_bs * nkv; such
+ * a pool would hold 512 GiB of codes); KVQ8_EINVAL for a null or misaligned
+ * pointer, a bad dtype or n_tokens < 0.  Tokens with equal slots race (one
+ * of them wins).
  */
 int kvq8_quantize_append(int8_t* k_cache, int8_t* v_cache, float* k_scale, float* v_scale,
                          int n_blocks, int kv_bs, int nkv, int hd,

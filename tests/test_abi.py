@@ -260,6 +260,9 @@ def test_write_row_limit():
     big = 1 << 27                                     # x 8 heads x 2 = 2^31 rows
     assert lib.kvq8_quantize_append(_fake(), _fake(), _fake(), _fake(), 64, 16, 8, 128, _fake(), _fake(), K.F32,
                                     big, _fake(), None) == ESHAPE
+    # a pool of 2^25 x 16 slots x 8 heads = 2^32 rows: beyond 32-bit pool rows
+    assert lib.kvq8_quantize_append(_fake(), _fake(), _fake(), _fake(), 1 << 25, 16, 8, 128, _fake(), _fake(),
+                                    K.F32, 10, _fake(), None) == ESHAPE
     assert lib.kvq4_quantize_append(_fake(), _fake(), _fake(), _fake(), _fake(), _fake(), 64, 16, 8, 128,
                                     _fake(), _fake(), K.BF16, big, _fake(), None) == ESHAPE
     assert lib.kvq4_0_quantize_append(_fake(), _fake(), _fake(), _fake(), 64, 16, 8, 128, _fake(), _fake(), K.BF16,
