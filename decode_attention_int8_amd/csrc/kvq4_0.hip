@@ -37,39 +37,6 @@ namespace kvq {
 constexpr int kQ40RowsPerGroup = 4;
 constexpr int kQ40RowsPerBlock = 32 * kQ40RowsPerGroup;
 
-// A lane's 16 input values as loaded: 16 float32 or 16 half-width values.
-template <int DT>
-struct Q40Raw {
-    uint4 u[DT == KVQ8_F32 ? 4 : 2];
-};
-
-template <int DT>
-__device__ __forceinline__ void q40_load16(const void* base, size_t byte_off, Q40Raw<DT>& r) {
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const char*>(base) + byte_off);
-#pragma unroll
-    for (int i = 0; i < (DT == KVQ8_F32 ? 4 : 2); ++i) r.u[i] = p[i];
-}
-
-template <int DT>
-__device__ __forceinline__ void q40_unpack16(const Q40Raw<DT>& r, float (&x)[16]) {
-#pragma unroll
-    for (int i = 0; i < (DT == KVQ8_F32 ? 4 : 2); ++i) {
-        const uint32_t w[4] = {r.u[i].x, r.u[i].y, r.u[i].z, r.u[i].w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if constexpr (DT == KVQ8_F32) {
-                x[4 * i + j] = __uint_as_float(w[j]);
-            } else if constexpr (DT == KVQ8_BF16) {
-                x[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
-                x[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
-            } else {
-                x[8 * i + 2 * j] = half_bits_f(w[j] & 0xFFFFu);
-                x[8 * i + 2 * j + 1] = half_bits_f(w[j] >> 16);
-            }
-        }
-    }
-}
-
 // A row of 128 values is spread over 8 lanes, 16 values each: block k's
 // first half (values 32k .. 32k + 15) on lane k, its second half on lane
 // 7 - k.  A block's extreme is then one half-row mirror, key bytes pair
@@ -184,7 +151,7 @@ __global__ __launch_bounds__(256) void kvq4_0_quantize_append_kernel(
     const uint32_t in_off = (uint32_t)(32 * kb + 16 * half) * kInBytes;
     const Q40Gather gsel = q40_gather_selectors(q, half != 0);
     const int rot = q8_rot_group(nkv.n);
-    Q40Raw<DT> raw[kQ40RowsPerGroup];
+    Raw16<DT> raw[kQ40RowsPerGroup];
     int trs[kQ40RowsPerGroup];
     // rows past the end load the last row again and store nothing; indices
     // fit in 32 bits (the host checks the row count)
@@ -192,7 +159,7 @@ __global__ __launch_bounds__(256) void kvq4_0_quantize_append_kernel(
     for (int k = 0; k < kQ40RowsPerGroup; ++k) {
         const int pair = (int)blockIdx.x * (kQ40RowsPerBlock / 2) + ((wave >> 1) * 8 + g8) * kQ40RowsPerGroup + k;
         trs[k] = min(2 * pair + kind, n_rows - 1) >> 1;   // token * nkv + kv-head
-        q40_load16<DT>(src, (size_t)trs[k] * (kHD * kInBytes) + in_off, raw[k]);
+        load_raw16<DT>(src, (size_t)trs[k] * (kHD * kInBytes) + in_off, raw[k]);
     }
 #pragma unroll
     for (int k = 0; k < kQ40RowsPerGroup; ++k) {
@@ -202,7 +169,7 @@ __global__ __launch_bounds__(256) void kvq4_0_quantize_append_kernel(
         const uint32_t slot = (uint32_t)slots[tok];
         const int kh = tr - tok * nkv.n;
         float x[16];
-        q40_unpack16<DT>(raw[k], x);
+        unpack_raw16<DT>(raw[k], x);
         uint32_t c[4];
         float step;
         q40_quantize16(x, c, step);                 // both lanes of a block take part (DPP)

@@ -1,10 +1,11 @@
 // Write path of the int4 group variant ([P4] Sec. 3.2 quantizer with the
 // Sec. 5.2 checklist).
 //
-// kvq4_quantize_append_kernel: one (token, kv-head, K-or-V) row per 16 lanes,
-// 8 values per lane, 4 rows per 16-lane group (loads first); each 64-value
-// group is one aligned 8-lane half row, so its max / min need only quad and
-// half-mirror DPP steps.
+// kvq4_quantize_append_kernel: one (token, kv-head, K-or-V) row per 8 lanes,
+// 16 values per lane, 4 rows per 8-lane group (loads first); each 64-value
+// group is one quad, so its max / min need two quad DPP steps.
+// kvq4_requantize_q8_kernel: one row per 16 lanes, 8 values per lane (each
+// group an aligned 8-lane half row).
 #include "kvq8.h"
 #include "kvq_device.h"
 #include "kvq_host.h"
@@ -96,8 +97,140 @@ __device__ __forceinline__ void quantize_group8x8(const float (&x)[8], uint32_t&
     packed = __builtin_amdgcn_perm(pr[1], pr[0], 0x06040200u);
 }
 
-constexpr int kRowsPerGroup = 4;            // rows per 16-lane group, loads first
-constexpr int kRowsPerBlock = 16 * kRowsPerGroup;
+// The group quantizer of the append kernel: the lane's 16 values of a
+// 64-value group held by a quad.  Returns the packed pairs (value 2k in the
+// high nibble of byte k: pk[0] bytes 0..3, pk[1] bytes 4..7), the binary16
+// scale and the zero point.
+//
+// code = clamp(rint(x / s + z), 0, 15), z an integer.  f = fma(x, rcp(s),
+// z + 128.5 + 2^-15), clamped to [128.25, 143.75], lies in [128, 256): its
+// unit is 2^-16 and its mantissa is (x * rcp(s) + z + 0.5) * 2^16, rounded,
+// plus 2, so bits 16..19 are the code and bits 0..15 the fraction plus 2.
+// The clamp holds q + z = x / s + z below -0.25 at code 0 and above 15.25
+// at code 15, where every rounding gives that code.  Where the low bits are
+// 0..3 the quotient + z lies within 2^-15 of a half-integer and the lane
+// divides instead; elsewhere it lies at least 1.5 * 2^-16 from one, more
+// than one rcp error (|q| <= 16: 2^-19) plus the division's and the
+// addition's roundings (2^-19 each), so the code read from f is the
+// correctly rounded rint's.
+__device__ __forceinline__ void quantize_group4x16(const float (&x)[16], uint32_t (&pk)[2], uint16_t& s16,
+                                                   uint16_t& z16) {
+#pragma clang fp contract(off)
+    float mx = x[0], mn = x[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) {
+        mx = fmaxf(mx, x[e]);
+        mn = fminf(mn, x[e]);
+    }
+    mx = fmaxf(mx, dpp_f<kDppXor1>(mx));
+    mn = fminf(mn, dpp_f<kDppXor1>(mn));
+    mx = fmaxf(mx, dpp_f<kDppXor2>(mx));
+    mn = fminf(mn, dpp_f<kDppXor2>(mn));
+    float s32 = (mx == mn) ? 1.0f : (mx - mn) / 15.0f;
+    s32 = fmaxf(s32, 1e-7f);
+    s16 = f16_bits_rne(s32);
+    const float s = half_bits_f(s16);
+    // integer zero point in [0, 15]; + 0.0f stores a zero as +0.0
+    const float z = fminf(fmaxf(rintf(-mn / s), 0.0f), 15.0f) + 0.0f;
+    z16 = f16_bits_rne(z);
+    const float rs = __builtin_amdgcn_rcpf(s);
+    const float m = z + 128.500030517578125f;       // exact: z is an integer
+    uint32_t cb[16];                                 // bits 16..19: the code
+    uint64_t slow[16];                               // wave masks of the lanes that divide
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        cb[e] = __float_as_uint(__builtin_amdgcn_fmed3f(__builtin_fmaf(x[e], rs, m), 128.25f, 143.75f));
+        slow[e] = __builtin_amdgcn_ballot_w64((uint16_t)cb[e] <= 3u);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        if (slow[e] != 0) {                         // rare: one wave-uniform test per value
+            const float cd = fminf(fmaxf(rintf(x[e] / s + z), 0.0f), 15.0f);
+            cb[e] = ((slow[e] >> (threadIdx.x & 63)) & 1) ? (uint32_t)(int)cd << 16 : cb[e];
+        }
+    }
+    // bytes [c0, c1, c2, c3]; (b << 4) | (b >> 8) puts the pairs (c0, c1) and
+    // (c2, c3) in bytes 0 and 2, even element high
+    uint32_t pr[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        const uint32_t b = __builtin_amdgcn_perm(cb[4 * h + 1], cb[4 * h], 0x0C0C0602u) |
+                           __builtin_amdgcn_perm(cb[4 * h + 3], cb[4 * h + 2], 0x06020C0Cu);
+        pr[h] = (b << 4) | (b >> 8);
+    }
+    pk[0] = __builtin_amdgcn_perm(pr[1], pr[0], 0x06040200u);
+    pk[1] = __builtin_amdgcn_perm(pr[3], pr[2], 0x06040200u);
+}
+
+constexpr int kRowsPerGroup = 4;            // rows per 8-lane group, loads first
+constexpr int kRowsPerBlock = 32 * kRowsPerGroup;
+
+// A row's lanes: lane l of the 8-lane group holds elements 64g + 16c ..
+// 64g + 16c + 15 with g = l / 4 and c = l % 4 for g = 0, 3 - l % 4 for
+// g = 1, so lanes l and 7 - l (one half-mirror DPP step) hold the same c of
+// the two groups.  Key rows: the lane's pairs 64g + 16c + 2j go to bytes
+// 16c + 8g + j, 8 contiguous bytes.  Value rows: the pair 64g + 4m + 2k, +1
+// goes to byte 4m + 2g + k, so words m = 4c .. 4c + 3 take two bytes from
+// each lane of the mirror pair; the g = 0 lane writes words 4c, 4c + 1, its
+// partner words 4c + 2, 4c + 3.  Row numbers of the pool (slot * nkv + head)
+// fit in 32 bits (the host checks n_slots * nkv; ns_cap = min(n_slots,
+// 2^31)).
+template <int DT>
+__global__ __launch_bounds__(256) void kvq4_quantize_append_kernel(
+    uint8_t* __restrict__ kc, uint8_t* __restrict__ vc, uint16_t* __restrict__ ks, uint16_t* __restrict__ kz,
+    uint16_t* __restrict__ vs, uint16_t* __restrict__ vz, uint32_t ns_cap, DivN nkv,
+    const void* __restrict__ k_new, const void* __restrict__ v_new, int n_rows, const int32_t* __restrict__ slots) {
+    constexpr int kInBytes = DT == KVQ8_F32 ? 4 : 2;
+    const int l8 = threadIdx.x & 7;
+    const int g = l8 >> 2;
+    const int c = g ? 3 - (l8 & 3) : (l8 & 3);
+    const int kind = (threadIdx.x >> 3) & 1;       // rows alternate K, V (k * 32 is even)
+    const void* src = kind ? v_new : k_new;
+    const uint32_t in_off = (uint32_t)(64 * g + 16 * c) * kInBytes;
+    const uint32_t out_off = 16u * (uint32_t)c + 8u * (uint32_t)g;   // key and value rows alike
+    uint8_t* codes = kind ? vc : kc;
+    uint16_t* scales = kind ? vs : ks;
+    uint16_t* zeros = kind ? vz : kz;
+    Raw16<DT> raw[kRowsPerGroup];
+    int trs[kRowsPerGroup];
+    uint32_t slot[kRowsPerGroup];
+    // rows past the end load the last row again and store nothing; indices
+    // fit in 32 bits (the host checks the row count)
+#pragma unroll
+    for (int k = 0; k < kRowsPerGroup; ++k) {
+        const int row = (int)blockIdx.x * kRowsPerBlock + k * 32 + (threadIdx.x >> 3);
+        const int tr = min(row, n_rows - 1) >> 1;  // token * nkv + kv-head
+        trs[k] = tr;
+        load_raw16<DT>(src, (size_t)tr * (kHD * kInBytes) + in_off, raw[k]);
+        slot[k] = (uint32_t)slots[div_n(tr, nkv)];
+    }
+#pragma unroll
+    for (int k = 0; k < kRowsPerGroup; ++k) {
+        float x[16];
+        unpack_raw16<DT>(raw[k], x);
+        uint32_t pk[2];
+        uint16_t s16, z16;
+        quantize_group4x16(x, pk, s16, z16);        // every lane of the group takes part (DPP)
+        uint2 word;
+        if (kind == 0) {
+            word = make_uint2(pk[0], pk[1]);
+        } else {
+            // the g = 0 lane needs the partner's bytes 0..3, the g = 1 lane
+            // the partner's bytes 4..7
+            const uint32_t r = (uint32_t)dpp_i<kDppHalfMirror>((int)(g ? pk[0] : pk[1]));
+            const uint32_t lo = g ? r : pk[0], hi = g ? pk[1] : r;
+            word = make_uint2(__builtin_amdgcn_perm(hi, lo, 0x05040100u), __builtin_amdgcn_perm(hi, lo, 0x07060302u));
+        }
+        const int row = (int)blockIdx.x * kRowsPerBlock + k * 32 + (threadIdx.x >> 3);
+        if (row >= n_rows || slot[k] >= ns_cap) continue;   // uniform per 8-lane row
+        const uint32_t drow = slot[k] * (uint32_t)nkv.n + (uint32_t)(trs[k] - div_n(trs[k], nkv) * nkv.n);
+        *reinterpret_cast<uint2*>(codes + (size_t)drow * (kHD / 2) + out_off) = word;
+        if (c == 0) {
+            scales[(size_t)drow * 2 + g] = s16;
+            zeros[(size_t)drow * 2 + g] = z16;
+        }
+    }
+}
 
 // Store one row: lane l16 packed the pairs of its 8 values (elements 8 l16 ..
 // 8 l16 + 7) into `packed`; `other` is lane l16 ^ 8's word.  Key rows take
@@ -121,37 +254,6 @@ __device__ __forceinline__ void store_q4_row(uint8_t* __restrict__ kc, uint8_t* 
     if ((l16 & 7) == 0) {
         (kind ? vs : ks)[dst * 2 + (l16 >> 3)] = s16;
         (kind ? vz : kz)[dst * 2 + (l16 >> 3)] = z16;
-    }
-}
-
-template <int DT>
-__global__ __launch_bounds__(256) void kvq4_quantize_append_kernel(
-    uint8_t* __restrict__ kc, uint8_t* __restrict__ vc, uint16_t* __restrict__ ks, uint16_t* __restrict__ kz,
-    uint16_t* __restrict__ vs, uint16_t* __restrict__ vz, long n_slots, DivN nkv, const void* __restrict__ k_new,
-    const void* __restrict__ v_new, int n_rows, const int32_t* __restrict__ slots) {
-    const int l16 = threadIdx.x & 15;
-    float x[kRowsPerGroup][8];
-    long dst[kRowsPerGroup];     // destination row (slot * nkv + head), -1 to skip
-    // rows past the end load the last row again and store nothing; indices
-    // fit in 32 bits (the host checks the row count)
-#pragma unroll
-    for (int k = 0; k < kRowsPerGroup; ++k) {
-        const int row = (int)blockIdx.x * kRowsPerBlock + k * 16 + (threadIdx.x >> 4);
-        const int rc = min(row, n_rows - 1);
-        const int tr = rc >> 1;
-        const int tok = div_n(tr, nkv);
-        load8_any<DT>((rc & 1) ? v_new : k_new, (size_t)tr * kHD + 8 * l16, x[k]);
-        const long slot = slots[tok];
-        dst[k] = (row < n_rows && slot >= 0 && slot < n_slots) ? slot * nkv.n + (tr - tok * nkv.n) : -1;
-    }
-#pragma unroll
-    for (int k = 0; k < kRowsPerGroup; ++k) {
-        uint32_t packed;
-        uint16_t s16, z16;
-        quantize_group8x8(x[k], packed, s16, z16);
-        const uint32_t other = (uint32_t)dpp_i<kDppRowRor8>((int)packed);     // lane l16 ^ 8
-        if (dst[k] < 0) continue;                                          // uniform per 16-lane row
-        store_q4_row(kc, vc, ks, kz, vs, vz, (threadIdx.x >> 4) & 1, (size_t)dst[k], l16, packed, other, s16, z16);
     }
 }
 
@@ -227,11 +329,15 @@ extern "C" int kvq4_quantize_append(uint8_t* k_cache, uint8_t* v_cache, uint16_t
     const long n_rows = (long)n_tokens * nkv * 2;
     if (n_rows > 0x7FFFFFFFL - kRowsPerBlock) return KVQ8_ESHAPE;
     const long n_slots = (long)n_blocks * kv_bs;
+    // pool rows (slot * nkv + head) are 32-bit in the kernel: 2^32 rows would
+    // take 256 GiB of codes per cache
+    if (n_slots * nkv > 0xFFFFFFFFL) return KVQ8_ESHAPE;
+    const uint32_t ns_cap = (uint32_t)(n_slots < 0x80000000L ? n_slots : 0x80000000L);
     const dim3 grid((unsigned)((n_rows + kRowsPerBlock - 1) / kRowsPerBlock)), block(256);
     hipStream_t s = static_cast<hipStream_t>(stream);
 #define KVQ4_LAUNCH(DT)                                                                                     \
     launch(kvq4_quantize_append_kernel<DT>, grid, block, s, k_cache, v_cache, k_scale, k_zero, \
-                       v_scale, v_zero, n_slots, make_divn(nkv), k_new, v_new, (int)n_rows, slots)
+                       v_scale, v_zero, ns_cap, make_divn(nkv), k_new, v_new, (int)n_rows, slots)
     int st;
     if (dtype == KVQ8_F32) st = KVQ4_LAUNCH(KVQ8_F32);
     else if (dtype == KVQ8_BF16) st = KVQ4_LAUNCH(KVQ8_BF16);

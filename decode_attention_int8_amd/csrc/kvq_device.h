@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kvq8.h"
+
 namespace kvq {
 
 constexpr int kHD = 128;        // head dimension
@@ -185,5 +187,38 @@ __device__ __forceinline__ float half_bits_f(uint32_t v) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)v);
 }
 
+// A lane's 16 consecutive input values of a write path as loaded (16
+// float32 or 16 binary16 / bfloat16 values), and widened to float (exact).
+template <int DT>
+struct Raw16 {
+    uint4 u[DT == KVQ8_F32 ? 4 : 2];
+};
+
+template <int DT>
+__device__ __forceinline__ void load_raw16(const void* base, size_t byte_off, Raw16<DT>& r) {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const char*>(base) + byte_off);
+#pragma unroll
+    for (int i = 0; i < (DT == KVQ8_F32 ? 4 : 2); ++i) r.u[i] = p[i];
+}
+
+template <int DT>
+__device__ __forceinline__ void unpack_raw16(const Raw16<DT>& r, float (&x)[16]) {
+#pragma unroll
+    for (int i = 0; i < (DT == KVQ8_F32 ? 4 : 2); ++i) {
+        const uint32_t w[4] = {r.u[i].x, r.u[i].y, r.u[i].z, r.u[i].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if constexpr (DT == KVQ8_F32) {
+                x[4 * i + j] = __uint_as_float(w[j]);
+            } else if constexpr (DT == KVQ8_BF16) {
+                x[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
+                x[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+            } else {
+                x[8 * i + 2 * j] = half_bits_f(w[j] & 0xFFFFu);
+                x[8 * i + 2 * j + 1] = half_bits_f(w[j] >> 16);
+            }
+        }
+    }
+}
 
 }  // namespace kvq
