@@ -1,13 +1,19 @@
 // Write paths of the 2-bit band ([P4] Sec. 3.2 group quantizer at two bits,
 // Sec. 3.3 re-quantization of aging blocks).
 //
-// Lane layout as in the int4 write path: one (token, kv-head, K-or-V) row per
-// 16 lanes, 8 values per lane (elements 8 l16 .. 8 l16 + 7), so each 64-value
-// group is one aligned 8-lane half row.  The codes go out in the 2-bit row
-// layouts: key word 2g + h holds d = 64h + 16g + 4k + j at bits 8j + 2k (lanes
-// 2w and 2w + 1 of a half row fill word w = 2g + h between them); the value
-// row's 16-bit word m holds d = 64(s/4) + 4m + s%4 at bits 2s (lane j of the
-// low half and lane j + 8 of the high half fill words 2j and 2j + 1).
+// The 2-bit row layouts: key word 2g + h holds d = 64h + 16g + 4k + j at bits
+// 8j + 2k; the value row's 16-bit word m holds d = 64(s/4) + 4m + s%4 at bits
+// 2s.
+//
+// kvq2_quantize_append_kernel: the int4 append kernel's lanes, one row per 8
+// lanes, lane l holding elements 64g + 16c .. + 15 (g = l / 4; c = l % 4, or
+// 3 - l % 4 for g = 1), so a lane's 16 codes are key word 2c + g, and its
+// value bytes meet those of lane 7 - l (the other group, same c) in words
+// 4c .. 4c + 3.
+// kvq2_requantize_q4_kernel: one row per 16 lanes, 8 values per lane
+// (elements 8 l16 .. 8 l16 + 7), each group an aligned 8-lane half row: lanes
+// 2w and 2w + 1 of a half row fill key word w = 2g + h between them; lane j of
+// the low half and lane j + 8 of the high half fill value words 2j and 2j + 1.
 #include "kvq8.h"
 #include "kvq_device.h"
 #include "kvq_host.h"
@@ -15,31 +21,8 @@
 namespace kvq {
 
 constexpr int kRow2Bytes = kHD / 4;
-constexpr int kRows2PerGroup = 4;             // rows per 16-lane group, loads first
-constexpr int kRows2PerBlock = 16 * kRows2PerGroup;
-
-template <int DT>
-__device__ __forceinline__ void load8_q2(const void* base, size_t elem_off, float (&x)[8]) {
-    if constexpr (DT == KVQ8_F32) {
-        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem_off);
-        const float4 u = p[0], v = p[1];
-        x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
-        x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
-    } else {
-        const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem_off);
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if constexpr (DT == KVQ8_BF16) {
-                x[2 * i] = __uint_as_float(w[i] << 16);
-                x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-            } else {
-                x[2 * i] = half_bits_f(w[i] & 0xFFFFu);
-                x[2 * i + 1] = half_bits_f(w[i] >> 16);
-            }
-        }
-    }
-}
+constexpr int kRows2PerGroup = 4;             // rows per 8-lane group, loads first
+constexpr int kRows2PerBlock = 32 * kRows2PerGroup;
 
 // Quantize the lane's 8 values of a 64-value group held by an aligned 8-lane
 // half row to 2-bit codes: scale = (max - min) / 3 (1 for a constant group),
@@ -143,37 +126,69 @@ __device__ __forceinline__ void q2_parts(uint32_t codes, int l16, uint32_t& kpar
     vpart = vp;
 }
 
+// Row numbers of the pool (slot * nkv + head) fit in 32 bits (the host checks
+// n_slots * nkv; ns_cap = min(n_slots, 2^31)).
 template <int DT>
 __global__ __launch_bounds__(256) void kvq2_quantize_append_kernel(
     uint8_t* __restrict__ kc, uint8_t* __restrict__ vc, uint16_t* __restrict__ ks, uint16_t* __restrict__ kz,
-    uint16_t* __restrict__ vs, uint16_t* __restrict__ vz, long n_slots, DivN nkv, const void* __restrict__ k_new,
-    const void* __restrict__ v_new, int n_rows, const int32_t* __restrict__ slots) {
-    const int l16 = threadIdx.x & 15;
-    float x[kRows2PerGroup][8];
-    long dst[kRows2PerGroup];    // destination row (slot * nkv + head), -1 to skip
+    uint16_t* __restrict__ vs, uint16_t* __restrict__ vz, uint32_t ns_cap, DivN nkv,
+    const void* __restrict__ k_new, const void* __restrict__ v_new, int n_rows, const int32_t* __restrict__ slots) {
+    constexpr int kInBytes = DT == KVQ8_F32 ? 4 : 2;
+    const int l8 = threadIdx.x & 7;
+    const int g = l8 >> 2;
+    const int c = g ? 3 - (l8 & 3) : (l8 & 3);
+    const int kind = (threadIdx.x >> 3) & 1;       // rows alternate K, V (k * 32 is even)
+    const void* src = kind ? v_new : k_new;
+    const uint32_t in_off = (uint32_t)(64 * g + 16 * c) * kInBytes;
+    // key word 2c + g; value words 4c + 2g, 4c + 2g + 1 (bytes 8c + 4g ..)
+    const uint32_t out_off = kind ? 8u * (uint32_t)c + 4u * (uint32_t)g : 4u * (uint32_t)(2 * c + g);
+    // value bytes of words 4c + 2g, + 1: [own v(2g), partner v(2g), own
+    // v(2g + 1), partner v(2g + 1)] with the group 0 byte low in each word
+    const uint32_t vsel = g ? 0x03070206u : 0x05010400u;
+    uint8_t* codes = kind ? vc : kc;
+    uint16_t* scales = kind ? vs : ks;
+    uint16_t* zeros = kind ? vz : kz;
+    Raw16<DT> raw[kRows2PerGroup];
+    int trs[kRows2PerGroup];
+    uint32_t slot[kRows2PerGroup];
     // rows past the end load the last row again and store nothing; indices
     // fit in 32 bits (the host checks the row count)
 #pragma unroll
     for (int k = 0; k < kRows2PerGroup; ++k) {
-        const int row = (int)blockIdx.x * kRows2PerBlock + k * 16 + (threadIdx.x >> 4);
-        const int rc = min(row, n_rows - 1);
-        const int tr = rc >> 1;
-        const int tok = div_n(tr, nkv);
-        load8_q2<DT>((rc & 1) ? v_new : k_new, (size_t)tr * kHD + 8 * l16, x[k]);
-        const long slot = slots[tok];
-        dst[k] = (row < n_rows && slot >= 0 && slot < n_slots) ? slot * nkv.n + (tr - tok * nkv.n) : -1;
+        const int row = (int)blockIdx.x * kRows2PerBlock + k * 32 + (threadIdx.x >> 3);
+        const int tr = min(row, n_rows - 1) >> 1;  // token * nkv + kv-head
+        trs[k] = tr;
+        load_raw16<DT>(src, (size_t)tr * (kHD * kInBytes) + in_off, raw[k]);
+        slot[k] = (uint32_t)slots[div_n(tr, nkv)];
     }
 #pragma unroll
     for (int k = 0; k < kRows2PerGroup; ++k) {
-        uint32_t codes, kpart, vpart;
+        float x[16];
+        unpack_raw16<DT>(raw[k], x);
+        uint32_t cb[4];
         uint16_t s16, z16;
-        quantize_group8x8_q2(x[k], codes, s16, z16);
-        q2_parts(codes, l16, kpart, vpart);
-        const uint32_t kother = (uint32_t)dpp_i<kDppXor1>((int)kpart);      // lane l16 ^ 1
-        const uint32_t vother = (uint32_t)dpp_i<kDppRowRor8>((int)vpart);   // lane l16 ^ 8
-        if (dst[k] < 0) continue;                                          // uniform per 16-lane row
-        store_q2_row(kc, vc, ks, kz, vs, vz, (threadIdx.x >> 4) & 1, (size_t)dst[k], l16, kpart, kother, vpart,
-                     vother, s16, z16);
+        quad_group_codes<3>(x, cb, s16, z16);       // every lane of the group takes part (DPP)
+        uint32_t word;
+        if (kind == 0) {
+            // element t = 4k + j of the lane at bits 8j + 2k: byte j of code
+            // word k, shifted by 2k
+            word = cb[0] | (cb[1] << 2) | (cb[2] << 4) | (cb[3] << 6);
+        } else {
+            // value byte i = codes 4i .. 4i + 3 at bits 0, 2, 4, 6
+            uint32_t v = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v |= __builtin_amdgcn_udot4(cb[i], 0x40100401u, 0u, false) << (8 * i);
+            const uint32_t r = (uint32_t)dpp_i<kDppHalfMirror>((int)v);   // the other group's lane
+            word = __builtin_amdgcn_perm(r, v, vsel);
+        }
+        const int row = (int)blockIdx.x * kRows2PerBlock + k * 32 + (threadIdx.x >> 3);
+        if (row >= n_rows || slot[k] >= ns_cap) continue;   // uniform per 8-lane row
+        const uint32_t drow = slot[k] * (uint32_t)nkv.n + (uint32_t)(trs[k] - div_n(trs[k], nkv) * nkv.n);
+        *reinterpret_cast<uint32_t*>(codes + (size_t)drow * kRow2Bytes + out_off) = word;
+        if (c == 0) {
+            scales[(size_t)drow * 2 + g] = s16;
+            zeros[(size_t)drow * 2 + g] = z16;
+        }
     }
 }
 
@@ -279,11 +294,15 @@ extern "C" int kvq2_quantize_append(uint8_t* k_cache, uint8_t* v_cache, uint16_t
     const long n_rows = (long)n_tokens * nkv * 2;
     if (n_rows > 0x7FFFFFFFL - kRows2PerBlock) return KVQ8_ESHAPE;
     const long n_slots = (long)n_blocks * kv_bs;
+    // pool rows (slot * nkv + head) are 32-bit in the kernel: 2^32 rows would
+    // take 160 GiB per cache (codes, scales and zeros)
+    if (n_slots * nkv > 0xFFFFFFFFL) return KVQ8_ESHAPE;
+    const uint32_t ns_cap = (uint32_t)(n_slots < 0x80000000L ? n_slots : 0x80000000L);
     const dim3 grid((unsigned)((n_rows + kRows2PerBlock - 1) / kRows2PerBlock)), block(256);
     hipStream_t s = static_cast<hipStream_t>(stream);
 #define KVQ2_LAUNCH(DT)                                                                                     \
     launch(kvq2_quantize_append_kernel<DT>, grid, block, s, k_cache, v_cache, k_scale, k_zero, \
-                       v_scale, v_zero, n_slots, make_divn(nkv), k_new, v_new, (int)n_rows, slots)
+                       v_scale, v_zero, ns_cap, make_divn(nkv), k_new, v_new, (int)n_rows, slots)
     int st;
     if (dtype == KVQ8_F32) st = KVQ2_LAUNCH(KVQ8_F32);
     else if (dtype == KVQ8_BF16) st = KVQ2_LAUNCH(KVQ8_BF16);

@@ -97,71 +97,6 @@ __device__ __forceinline__ void quantize_group8x8(const float (&x)[8], uint32_t&
     packed = __builtin_amdgcn_perm(pr[1], pr[0], 0x06040200u);
 }
 
-// The group quantizer of the append kernel: the lane's 16 values of a
-// 64-value group held by a quad.  Returns the packed pairs (value 2k in the
-// high nibble of byte k: pk[0] bytes 0..3, pk[1] bytes 4..7), the binary16
-// scale and the zero point.
-//
-// code = clamp(rint(x / s + z), 0, 15), z an integer.  f = fma(x, rcp(s),
-// z + 128.5 + 2^-15), clamped to [128.25, 143.75], lies in [128, 256): its
-// unit is 2^-16 and its mantissa is (x * rcp(s) + z + 0.5) * 2^16, rounded,
-// plus 2, so bits 16..19 are the code and bits 0..15 the fraction plus 2.
-// The clamp holds q + z = x / s + z below -0.25 at code 0 and above 15.25
-// at code 15, where every rounding gives that code.  Where the low bits are
-// 0..3 the quotient + z lies within 2^-15 of a half-integer and the lane
-// divides instead; elsewhere it lies at least 1.5 * 2^-16 from one, more
-// than one rcp error (|q| <= 16: 2^-19) plus the division's and the
-// addition's roundings (2^-19 each), so the code read from f is the
-// correctly rounded rint's.
-__device__ __forceinline__ void quantize_group4x16(const float (&x)[16], uint32_t (&pk)[2], uint16_t& s16,
-                                                   uint16_t& z16) {
-#pragma clang fp contract(off)
-    float mx = x[0], mn = x[0];
-#pragma unroll
-    for (int e = 1; e < 16; ++e) {
-        mx = fmaxf(mx, x[e]);
-        mn = fminf(mn, x[e]);
-    }
-    mx = fmaxf(mx, dpp_f<kDppXor1>(mx));
-    mn = fminf(mn, dpp_f<kDppXor1>(mn));
-    mx = fmaxf(mx, dpp_f<kDppXor2>(mx));
-    mn = fminf(mn, dpp_f<kDppXor2>(mn));
-    float s32 = (mx == mn) ? 1.0f : (mx - mn) / 15.0f;
-    s32 = fmaxf(s32, 1e-7f);
-    s16 = f16_bits_rne(s32);
-    const float s = half_bits_f(s16);
-    // integer zero point in [0, 15]; + 0.0f stores a zero as +0.0
-    const float z = fminf(fmaxf(rintf(-mn / s), 0.0f), 15.0f) + 0.0f;
-    z16 = f16_bits_rne(z);
-    const float rs = __builtin_amdgcn_rcpf(s);
-    const float m = z + 128.500030517578125f;       // exact: z is an integer
-    uint32_t cb[16];                                 // bits 16..19: the code
-    uint64_t slow[16];                               // wave masks of the lanes that divide
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        cb[e] = __float_as_uint(__builtin_amdgcn_fmed3f(__builtin_fmaf(x[e], rs, m), 128.25f, 143.75f));
-        slow[e] = __builtin_amdgcn_ballot_w64((uint16_t)cb[e] <= 3u);
-    }
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        if (slow[e] != 0) {                         // rare: one wave-uniform test per value
-            const float cd = fminf(fmaxf(rintf(x[e] / s + z), 0.0f), 15.0f);
-            cb[e] = ((slow[e] >> (threadIdx.x & 63)) & 1) ? (uint32_t)(int)cd << 16 : cb[e];
-        }
-    }
-    // bytes [c0, c1, c2, c3]; (b << 4) | (b >> 8) puts the pairs (c0, c1) and
-    // (c2, c3) in bytes 0 and 2, even element high
-    uint32_t pr[4];
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-        const uint32_t b = __builtin_amdgcn_perm(cb[4 * h + 1], cb[4 * h], 0x0C0C0602u) |
-                           __builtin_amdgcn_perm(cb[4 * h + 3], cb[4 * h + 2], 0x06020C0Cu);
-        pr[h] = (b << 4) | (b >> 8);
-    }
-    pk[0] = __builtin_amdgcn_perm(pr[1], pr[0], 0x06040200u);
-    pk[1] = __builtin_amdgcn_perm(pr[3], pr[2], 0x06040200u);
-}
-
 constexpr int kRowsPerGroup = 4;            // rows per 8-lane group, loads first
 constexpr int kRowsPerBlock = 32 * kRowsPerGroup;
 
@@ -208,9 +143,15 @@ __global__ __launch_bounds__(256) void kvq4_quantize_append_kernel(
     for (int k = 0; k < kRowsPerGroup; ++k) {
         float x[16];
         unpack_raw16<DT>(raw[k], x);
-        uint32_t pk[2];
+        uint32_t cb[4], pk[2];
         uint16_t s16, z16;
-        quantize_group4x16(x, pk, s16, z16);        // every lane of the group takes part (DPP)
+        quad_group_codes<15>(x, cb, s16, z16);      // every lane of the group takes part (DPP)
+        // (b << 4) | (b >> 8) puts the pairs (c0, c1) and (c2, c3) of a code
+        // word in bytes 0 and 2, even element high
+#pragma unroll
+        for (int h = 0; h < 4; ++h) cb[h] = (cb[h] << 4) | (cb[h] >> 8);
+        pk[0] = __builtin_amdgcn_perm(cb[1], cb[0], 0x06040200u);   // pairs 0..3: value 2k high in byte k
+        pk[1] = __builtin_amdgcn_perm(cb[3], cb[2], 0x06040200u);   // pairs 4..7
         uint2 word;
         if (kind == 0) {
             word = make_uint2(pk[0], pk[1]);

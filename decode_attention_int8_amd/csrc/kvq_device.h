@@ -221,4 +221,65 @@ __device__ __forceinline__ void unpack_raw16(const Raw16<DT>& r, float (&x)[16])
     }
 }
 
+
+// The [P4] Sec. 3.2 group quantizer at QMAX = 2^bits - 1 for a 64-value group
+// held by a quad, 16 values per lane: scale = (max - min) / QMAX (1 for a
+// constant group), floored at 1e-7 and rounded to binary16 (s16) before use;
+// zero = rint(-min / s) clamped to [0, QMAX] (z16 its binary16 bits, +0.0 for
+// zero).  Returns the lane's codes, byte i of b[h] the code of value 4h + i.
+//
+// code = clamp(rint(x / s + z), 0, QMAX), z an integer.  f = fma(x, rcp(s),
+// z + 128.5 + 2^-15), clamped to [128.25, 128.75 + QMAX], lies in [128,
+// 256): its unit is 2^-16 and its mantissa is (x * rcp(s) + z + 0.5) * 2^16,
+// rounded, plus 2, so bits 16..19 are the code and bits 0..15 the fraction
+// plus 2.  The clamp holds x / s + z below -0.25 at code 0 and above QMAX +
+// 0.25 at QMAX, where every rounding gives that code.  Where the low bits are
+// 0..3 the quotient + z lies within 2^-15 of a half-integer and the lane
+// divides instead; elsewhere it lies at least 1.5 * 2^-16 from one, more than
+// one rcp error (|x / s| <= 16: 2^-19) plus the division's and the
+// addition's roundings (2^-19 each), so the code read from f is the correctly
+// rounded rint's.
+template <int QMAX>
+__device__ __forceinline__ void quad_group_codes(const float (&x)[16], uint32_t (&b)[4], uint16_t& s16,
+                                                 uint16_t& z16) {
+#pragma clang fp contract(off)
+    float mx = x[0], mn = x[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) {
+        mx = fmaxf(mx, x[e]);
+        mn = fminf(mn, x[e]);
+    }
+    mx = fmaxf(mx, dpp_f<kDppXor1>(mx));
+    mn = fminf(mn, dpp_f<kDppXor1>(mn));
+    mx = fmaxf(mx, dpp_f<kDppXor2>(mx));
+    mn = fminf(mn, dpp_f<kDppXor2>(mn));
+    float s32 = (mx == mn) ? 1.0f : (mx - mn) / (float)QMAX;
+    s32 = fmaxf(s32, 1e-7f);
+    s16 = __builtin_bit_cast(uint16_t, (_Float16)s32);
+    const float s = half_bits_f(s16);
+    // + 0.0f stores a zero as +0.0
+    const float z = fminf(fmaxf(rintf(-mn / s), 0.0f), (float)QMAX) + 0.0f;
+    z16 = __builtin_bit_cast(uint16_t, (_Float16)z);
+    const float rs = __builtin_amdgcn_rcpf(s);
+    const float m = z + 128.500030517578125f;       // exact: z is an integer
+    uint32_t cb[16];                                 // bits 16..19: the code
+    uint64_t slow[16];                               // wave masks of the lanes that divide
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        cb[e] = __float_as_uint(__builtin_amdgcn_fmed3f(__builtin_fmaf(x[e], rs, m), 128.25f, 128.75f + QMAX));
+        slow[e] = __builtin_amdgcn_ballot_w64((uint16_t)cb[e] <= 3u);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        if (slow[e] != 0) {                         // rare: one wave-uniform test per value
+            const float cd = fminf(fmaxf(rintf(x[e] / s + z), 0.0f), (float)QMAX);
+            cb[e] = ((slow[e] >> (threadIdx.x & 63)) & 1) ? (uint32_t)(int)cd << 16 : cb[e];
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+        b[h] = __builtin_amdgcn_perm(cb[4 * h + 1], cb[4 * h], 0x0C0C0602u) |
+               __builtin_amdgcn_perm(cb[4 * h + 3], cb[4 * h + 2], 0x06020C0Cu);
+}
+
 }  // namespace kvq
