@@ -325,13 +325,13 @@ def run_workloads(only=None):
         return fn, len(pools) * math.ceil(iters / len(pools))
 
     def q4_pool(nb, bs, nkv):
-        shp = (nb, bs, nkv)
+        shp = (nb, nkv, bs)                        # head-major inside a block
         return [torch.zeros(shp + (64,), dtype=torch.uint8, device="cuda"),
                 torch.zeros(shp + (64,), dtype=torch.uint8, device="cuda")] + \
                [torch.zeros(shp + (2,), dtype=torch.float16, device="cuda") for _ in range(4)]
 
     def q2_pool(nb, bs, nkv):
-        shp = (nb, bs, nkv)
+        shp = (nb, nkv, bs)                        # head-major inside a block
         return [torch.zeros(shp + (32,), dtype=torch.uint8, device="cuda"),
                 torch.zeros(shp + (32,), dtype=torch.uint8, device="cuda")] + \
                [torch.zeros(shp + (2,), dtype=torch.float16, device="cuda") for _ in range(4)]

@@ -40,11 +40,11 @@ struct LaneOff2 {
 __device__ __forceinline__ LaneOff2 lane_offsets2(const BandArgs& a, int lane) {
     const int g = lane >> 4;
     const int m = lane & 15;
-    const uint32_t row = (uint32_t)a.nkv * kRow2;
+    (void)a;
     LaneOff2 o;
-    o.k = (uint32_t)m * row + 8 * g;
+    o.k = (uint32_t)m * kRow2 + 8 * g;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o.v[e] = (uint32_t)(4 * g + e) * row + 2 * m;
+    for (int e = 0; e < 4; ++e) o.v[e] = (uint32_t)(4 * g + e) * kRow2 + 2 * m;
     return o;
 }
 
@@ -68,7 +68,7 @@ __device__ __forceinline__ void mtile2_issue(const BandArgs& a, int raw, int bas
         const int idi = __builtin_amdgcn_readlane(id, 8 * i);
         // a block outside the pool reads block 0 (in bounds; its tokens are masked)
         const uint32_t idc = (uint32_t)max(idi, 0);
-        return ((idc << a.log2_bs) + (((uint32_t)base + 8 * i) & bs_mask)) * nkv + kh;
+        return ((idc * nkv + kh) << a.log2_bs) + (((uint32_t)base + 8 * i) & bs_mask);
     };
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -80,15 +80,15 @@ __device__ __forceinline__ void mtile2_issue(const BandArgs& a, int raw, int bas
             for (int e = 0; e < 4; ++e) T.v[v][e] = *reinterpret_cast<const uint16_t*>(pv + lo.v[e]);
         } else {
             const uint32_t u0 = grp(2 * v), u1 = grp(2 * v + 1);
-            const uint32_t rk = ((m & 8) ? u1 : u0) + (uint32_t)(m & 7) * nkv;
+            const uint32_t rk = ((m & 8) ? u1 : u0) + (uint32_t)(m & 7);
             T.k[v] = *reinterpret_cast<const v2u_t*>(a.k2 + (size_t)rk * kRow2 + 8 * g);
-            const uint32_t rv = ((g & 2) ? u1 : u0) + (uint32_t)(4 * (g & 1)) * nkv;
+            const uint32_t rv = ((g & 2) ? u1 : u0) + (uint32_t)(4 * (g & 1));
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                T.v[v][e] = *reinterpret_cast<const uint16_t*>(a.v2 + (size_t)(rv + (uint32_t)e * nkv) * kRow2 + 2 * m);
+                T.v[v][e] = *reinterpret_cast<const uint16_t*>(a.v2 + (size_t)(rv + (uint32_t)e) * kRow2 + 2 * m);
         }
     }
-    const uint32_t srow = id >= 0 ? ((((uint32_t)id << a.log2_bs) + (((uint32_t)base + lane) & bs_mask)) * nkv + kh) : 0u;
+    const uint32_t srow = id >= 0 ? ((((uint32_t)id * nkv + kh) << a.log2_bs) + (((uint32_t)base + lane) & bs_mask)) : 0u;
     T.ks = *reinterpret_cast<const uint32_t*>(a.k2s + (size_t)srow * 2);
     T.kz = *reinterpret_cast<const uint32_t*>(a.k2z + (size_t)srow * 2);
     T.vs = *reinterpret_cast<const uint32_t*>(a.v2s + (size_t)srow * 2);

@@ -117,11 +117,11 @@ struct LaneOff4 {
 __device__ __forceinline__ LaneOff4 lane_offsets4(const DecodeArgs& a, int lane) {
     const int g = lane >> 4;
     const int m = lane & 15;
-    const uint32_t row = (uint32_t)a.nkv * (kHD / 2);
+    (void)a;
     LaneOff4 o;
-    o.k = (uint32_t)m * row + 16 * g;
+    o.k = (uint32_t)m * (kHD / 2) + 16 * g;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o.v[e] = (uint32_t)(4 * g + e) * row + 4 * m;
+    for (int e = 0; e < 4; ++e) o.v[e] = (uint32_t)(4 * g + e) * (kHD / 2) + 4 * m;
     return o;
 }
 
@@ -139,7 +139,7 @@ __device__ __forceinline__ void mtile4_issue(const DecodeArgs& a, int raw, int b
         const int idi = __builtin_amdgcn_readlane(id, 8 * i);
         // a block outside the pool reads block 0 (in bounds; its tokens are masked)
         const uint32_t idc = (uint32_t)max(idi, 0);
-        return ((idc << a.log2_bs) + (((uint32_t)base + 8 * i) & bs_mask)) * nkv + kh;
+        return ((idc * nkv + kh) << a.log2_bs) + (((uint32_t)base + 8 * i) & bs_mask);
     };
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -154,17 +154,17 @@ __device__ __forceinline__ void mtile4_issue(const DecodeArgs& a, int raw, int b
             for (int e = 0; e < 4; ++e) T.v[v][e] = *reinterpret_cast<const uint32_t*>(pv + lo.v[e]);
         } else {
             const uint32_t u0 = grp(2 * v), u1 = grp(2 * v + 1);
-            const uint32_t rk = ((m & 8) ? u1 : u0) + (uint32_t)(m & 7) * nkv;
+            const uint32_t rk = ((m & 8) ? u1 : u0) + (uint32_t)(m & 7);
             const v4u_t kk = *reinterpret_cast<const v4u_t*>(a.k4 + (size_t)rk * (kHD / 2) + 16 * g);
             T.k[v][0] = v2u_t{kk.x, kk.y};
             T.k[v][1] = v2u_t{kk.z, kk.w};
-            const uint32_t rv = ((g & 2) ? u1 : u0) + (uint32_t)(4 * (g & 1)) * nkv;
+            const uint32_t rv = ((g & 2) ? u1 : u0) + (uint32_t)(4 * (g & 1));
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                T.v[v][e] = *reinterpret_cast<const uint32_t*>(a.v4 + (size_t)(rv + (uint32_t)e * nkv) * (kHD / 2) + 4 * m);
+                T.v[v][e] = *reinterpret_cast<const uint32_t*>(a.v4 + (size_t)(rv + (uint32_t)e) * (kHD / 2) + 4 * m);
         }
     }
-    const uint32_t srow = id >= 0 ? ((((uint32_t)id << a.log2_bs) + (((uint32_t)base + lane) & bs_mask)) * nkv + kh) : 0u;
+    const uint32_t srow = id >= 0 ? ((((uint32_t)id * nkv + kh) << a.log2_bs) + (((uint32_t)base + lane) & bs_mask)) : 0u;
     T.ks = *reinterpret_cast<const uint32_t*>(a.k4s + (size_t)srow * 2);
     T.kz = *reinterpret_cast<const uint32_t*>(a.k4z + (size_t)srow * 2);
     T.vs = *reinterpret_cast<const uint32_t*>(a.v4s + (size_t)srow * 2);

@@ -173,6 +173,19 @@ __host__ __device__ __forceinline__ int q8_col(int kh, long slot, int p) {
     return (kh & ~(p - 1)) | ((kh + (int)(slot & 7)) & (p - 1));
 }
 
+// Row order of the int4 and 2-bit pools (codes, scales and zeros alike):
+// head-major inside each block, row ((slot / kv_bs) * nkv + kh) * kv_bs +
+// slot % kv_bs, so the kv_bs rows of one (block, kv-head) are contiguous
+// (1 KB of int4 codes for 16 slots) and a decode work item, which reads one
+// kv-head, reads whole cache lines.
+__host__ __device__ __forceinline__ size_t hm_row(long slot, int kh, int nkv, int log2_bs) {
+    return ((((size_t)slot >> log2_bs) * (size_t)nkv + (size_t)kh) << log2_bs) |
+           ((size_t)slot & (((size_t)1 << log2_bs) - 1));
+}
+__device__ __forceinline__ uint32_t hm_row32(uint32_t slot, uint32_t kh, uint32_t nkv, int log2_bs) {
+    return (((slot >> log2_bs) * nkv + kh) << log2_bs) | (slot & ((1u << log2_bs) - 1));
+}
+
 // Storage order of an int4 key row (64 bytes, two codes per byte, even element
 // in the high nibble): eight 8-byte parts, part 2c + h holding the pairs 32h +
 // 8c .. 32h + 8c + 7, i.e. codes 64h + 16c .. 64h + 16c + 15, so that the 16
@@ -280,6 +293,30 @@ __device__ __forceinline__ void quad_group_codes(const float (&x)[16], uint32_t 
     for (int h = 0; h < 4; ++h)
         b[h] = __builtin_amdgcn_perm(cb[4 * h + 1], cb[4 * h], 0x0C0C0602u) |
                __builtin_amdgcn_perm(cb[4 * h + 3], cb[4 * h + 2], 0x06020C0Cu);
+}
+
+// The lanes of a row in the int4 and 2-bit write kernels (one (token,
+// kv-head, K-or-V) row per 8 lanes, rows alternating K and V): lane l of the
+// 8-lane group holds elements 64g + 16c .. 64g + 16c + 15 with g = l / 4 and
+// c = l % 4 for g = 0, 3 - l % 4 for g = 1.  Each 64-value group is a quad,
+// and lanes l and 7 - l (one half-mirror DPP step) hold the same c of the
+// two groups.
+struct GroupLane {
+    int g, c, kind;
+    __device__ __forceinline__ GroupLane() {
+        const int l8 = threadIdx.x & 7;
+        g = l8 >> 2;
+        c = g ? 3 - (l8 & 3) : (l8 & 3);
+        kind = (threadIdx.x >> 3) & 1;             // rows alternate K, V (groups 32 apart are even)
+    }
+};
+
+// Pair q of the write kernels' n pairs per kv-head, taken kv-head-major
+// (q = kv-head * n + i), so consecutive rows are consecutive tokens of one
+// kv-head: contiguous rows of a head-major pool when their slots are.
+__device__ __forceinline__ void head_major_pair(int q, const DivN& n, int& i, int& kh) {
+    kh = div_n(q, n);
+    i = q - kh * n.n;
 }
 
 }  // namespace kvq

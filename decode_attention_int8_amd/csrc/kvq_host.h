@@ -54,4 +54,9 @@ inline float score_scale(float sm_scale) { return sm_scale > 0.0f ? sm_scale : 1
 
 inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// The slot bound a write kernel tests with one unsigned compare: min(n_slots,
+// 2^31), so that (uint32_t)slot < slot_cap(n_slots) holds exactly for an
+// int32 slot in [0, n_slots).
+inline uint32_t slot_cap(long n_slots) { return (uint32_t)(n_slots < 0x80000000L ? n_slots : 0x80000000L); }
+
 }  // namespace kvq

@@ -158,16 +158,17 @@ def _tables(block_tables, ctx_lens, B: int, suffix=""):
 
 
 def _group_pool(pool, codes_per_byte: int, names):
-    """Packed codes [n_blocks][kv_bs][nkv][hd / codes_per_byte], K and V
-    alike, and four [n_blocks][kv_bs][nkv][hd / 64] scale / zero tensors."""
+    """Packed codes [n_blocks][nkv][kv_bs][hd / codes_per_byte] (head-major
+    inside a block), K and V alike, and four [n_blocks][nkv][kv_bs][hd / 64]
+    scale / zero tensors.  Returns (n_blocks, kv_bs, nkv, hd)."""
     kc, vc, ks, kz, vs, vz = pool
     if kc.dim() != 4:
-        raise ValueError(f"{names[0]} must be [n_blocks][kv_bs][nkv][hd / {codes_per_byte}]")
+        raise ValueError(f"{names[0]} must be [n_blocks][nkv][kv_bs][hd / {codes_per_byte}]")
     _shape(vc, kc.shape, names[1])
-    n, bs, nkv, row = kc.shape
+    n, nkv, bs, row = kc.shape
     hd = codes_per_byte * row
     for t, nm in zip((ks, kz, vs, vz), names[2:]):
-        _shape(t, (n, bs, nkv, hd // 64), nm)
+        _shape(t, (n, nkv, bs, hd // 64), nm)
     return n, bs, nkv, hd
 
 
@@ -176,16 +177,7 @@ def _int2_pool(pool2):
 
 
 def _int4_pool(pool4):
-    """Packed codes [n_blocks][kv_bs][nkv][hd / 2], K and V alike, and four
-    [n_blocks][kv_bs][nkv][hd / 64] scale / zero tensors."""
-    k4, v4, k4s, k4z, v4s, v4z = pool4
-    if k4.dim() != 4:
-        raise ValueError("int4 codes must be [n_blocks][kv_bs][nkv][hd / 2]")
-    _shape(v4, k4.shape, "v4")
-    n, bs, nkv, half = k4.shape
-    for t, nm in ((k4s, "k4_scale"), (k4z, "k4_zero"), (v4s, "v4_scale"), (v4z, "v4_zero")):
-        _shape(t, (n, bs, nkv, 2 * half // 64), nm)
-    return n, bs, nkv, 2 * half
+    return _group_pool(pool4, 2, ("k4", "v4", "k4_scale", "k4_zero", "v4_scale", "v4_zero"))
 
 
 def kvq8_status_string(status: int) -> str:
@@ -344,8 +336,8 @@ def kvq8_qk_partials(partials, q, k_cache, block_tables, ctx_lens, max_ctx_len: 
 # ----------------------------------------------------------------------------
 
 def kvq4_quantize_append(k_cache, v_cache, k_scale, k_zero, v_scale, v_zero, k_new, v_new, slots, stream=None):
-    """Quantize into the int4 pool: packed codes [n_blocks][kv_bs][nkv][64]
-    uint8, scale / zero [n_blocks][kv_bs][nkv][2] float16."""
+    """Quantize into the int4 pool: packed codes [n_blocks][nkv][kv_bs][64]
+    uint8, scale / zero [n_blocks][nkv][kv_bs][2] float16."""
     n_blocks, kv_bs, nkv, hd = _int4_pool((k_cache, v_cache, k_scale, k_zero, v_scale, v_zero))
     if k_new.dtype not in _DTYPES or v_new.dtype != k_new.dtype:
         raise ValueError("k_new / v_new must share one of float32, bfloat16, float16")
@@ -504,8 +496,8 @@ def _pool_ptrs(pool, codes_dtype, prefix):
 
 
 def kvq2_quantize_append(k_cache, v_cache, k_scale, k_zero, v_scale, v_zero, k_new, v_new, slots, stream=None):
-    """Quantize into the 2-bit pool: packed codes [n_blocks][kv_bs][nkv][32]
-    uint8, scale / zero [n_blocks][kv_bs][nkv][2] float16."""
+    """Quantize into the 2-bit pool: packed codes [n_blocks][nkv][kv_bs][32]
+    uint8, scale / zero [n_blocks][nkv][kv_bs][2] float16."""
     pool = (k_cache, v_cache, k_scale, k_zero, v_scale, v_zero)
     n_blocks, kv_bs, nkv, hd = _int2_pool(pool)
     if k_new.dtype not in _DTYPES or v_new.dtype != k_new.dtype:
@@ -527,7 +519,7 @@ def kvq2_requantize_q4(pool2, pool4, src_slots, dst_slots, stream=None):
     src_slots[i] to 2-bit slot dst_slots[i] (int32 device tensors)."""
     n2, kv_bs, nkv, hd = _int2_pool(pool2)
     n4 = _int4_pool(pool4)[0]
-    if tuple(pool4[0].shape[1:3]) != (kv_bs, nkv) or 2 * pool4[0].shape[3] != hd:
+    if tuple(pool4[0].shape[1:3]) != (nkv, kv_bs) or 2 * pool4[0].shape[3] != hd:
         raise ValueError("the int4 and 2-bit pools must share kv_bs, nkv and hd")
     if src_slots.shape != dst_slots.shape or src_slots.dim() != 1:
         raise ValueError("src_slots and dst_slots must be [n_tokens]")
@@ -558,7 +550,7 @@ def kvq2_decode_attn(out, q, pool2, block_tables2, lens2, max_len2: int, pool4, 
     n4 = _int4_pool(pool4)[0]
     k8, v8, k8s, v8s = pool8
     n8 = _int8_pool(k8, v8, k8s, v8s)[0]
-    if tuple(pool4[0].shape[1:3]) != (kv_bs, nkv) or 2 * pool4[0].shape[3] != hd or \
+    if tuple(pool4[0].shape[1:3]) != (nkv, kv_bs) or 2 * pool4[0].shape[3] != hd or \
             tuple(k8.shape[1:]) != (kv_bs, nkv, hd):
         raise ValueError("the three pools must share kv_bs, nkv and hd")
     _query(out, q, hd)

@@ -274,16 +274,20 @@ int kvq8_qk_partials(int32_t* partials, const float* q, int batch, int nq,
 /* ------------------------------------------------------------------------
  * int4 group variant ([P4] Sec. 3.2, 3.3)
  *
- * int4 pool layout:
- *   packed codes  cache4[n_blocks4][kv_bs][nkv][64] uint8, two consecutive
+ * int4 pool layout (head-major inside each block: the kv_bs rows of one
+ * (block, kv-head) are contiguous, so a decode work item, which reads one
+ * kv-head, reads whole cache lines):
+ *   packed codes  cache4[n_blocks4][nkv][kv_bs][64] uint8, two consecutive
  *                 codes per byte, even-indexed value in the high nibble;
  *                 key rows hold the pair starting at element 64h + 16c + 2j
  *                 (h = 0, 1; c = 0..3; j = 0..7) in byte 16c + 8h + j, value
  *                 rows hold the pair starting at element 64g + 4m + 2k in
  *                 byte 4m + 2g + k
- *   scale, zero   [n_blocks4][kv_bs][nkv][2] IEEE binary16 (as uint16 bits),
+ *   scale, zero   [n_blocks4][nkv][kv_bs][2] IEEE binary16 (as uint16 bits),
  *                 one per 64-value group
- * Recent tokens stay in an int8 pool laid out exactly as above.
+ * Slot s = block * kv_bs + offset of kv-head kh is row (block * nkv + kh) *
+ * kv_bs + offset of each array.  Recent tokens stay in an int8 pool laid
+ * out as above ([n_blocks][kv_bs][nkv * 128]).
  * ------------------------------------------------------------------------ */
 
 /*
@@ -454,13 +458,14 @@ int kvq4_0_decode_attn(float* out, const float* q, int batch, int nq,
  * code = clamp(rint(x / s + zero), 0, 3); rint rounds half to even; the
  * value a code stands for is (code - zero) * s.
  *
- * 2-bit pool layout (this library's packing, four codes per byte):
- *   packed codes  cache2[n_blocks2][kv_bs][nkv][32] uint8;
+ * 2-bit pool layout (this library's packing, four codes per byte; rows
+ * head-major inside each block as in the int4 pool):
+ *   packed codes  cache2[n_blocks2][nkv][kv_bs][32] uint8;
  *                 key rows: 32-bit word 2g + h holds element
  *                 64h + 16g + 4k + j at bits 8j + 2k (g, j, k = 0..3);
  *                 value rows: 16-bit word m holds element
  *                 64(s / 4) + 4m + s % 4 at bits 2s (s = 0..7, m = 0..15)
- *   scale, zero   [n_blocks2][kv_bs][nkv][2] IEEE binary16 (as uint16 bits)
+ *   scale, zero   [n_blocks2][nkv][kv_bs][2] IEEE binary16 (as uint16 bits)
  * 32 + 32 code bytes + 8 + 8 scale / zero bytes = 80 B per (token, kv-head)
  * (int4: 144 B, int8: 264 B).
  * ------------------------------------------------------------------------ */

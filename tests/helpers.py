@@ -87,6 +87,18 @@ def q4_key_library_order(pool):
     return pool.reshape(pool.shape[:-1] + (8, 8))[..., Q4_KEY_LIBRARY_PART, :].reshape(pool.shape)
 
 
+def head_major(pool):
+    """A pool [n_blocks][kv_bs][nkv][..] in the pages' slot-major order (as
+    the oracle keeps it) -> the device order of the int4 and 2-bit pools,
+    [n_blocks][nkv][kv_bs][..] (the rows of one block and kv-head contiguous)."""
+    return np.ascontiguousarray(np.swapaxes(np.asarray(pool), 1, 2))
+
+
+def slot_major(pool):
+    """The inverse of head_major."""
+    return np.ascontiguousarray(np.swapaxes(np.asarray(pool), 1, 2))
+
+
 class Q8Cache:
     """An int8 paged cache held both on the host (oracle) and on the GPU."""
 

@@ -156,17 +156,18 @@ def test_binding_checks_every_buffer_shape():
     raises(K.kvq8_qk_partials, z(B, nq, 32, 4, dt=i32), q, k8, bt, ln[:1], 32, match="ctx_lens")
     raises(K.kvq8_qk_partials, z(B, nq, 31, 4, dt=i32), q, k8, bt, ln, 32, match="partials")
 
-    c4, g4 = z(nb, bs, nkv, 64, dt=u8), z(nb, bs, nkv, 2, dt=f16)
+    c4, g4 = z(nb, nkv, bs, 64, dt=u8), z(nb, nkv, bs, 2, dt=f16)     # head-major inside a block
     pool4, pool8 = (c4, c4, g4, g4, g4, g4), (k8, k8, s8, s8)
     raises(K.kvq4_decode_attn, q, q, (c4, c4, g4, g4, g4[:1], g4), bt, ln, 32, pool8, bt, ln, 16, match="v4_scale")
     raises(K.kvq4_decode_attn, q, q, pool4, bt, ln, 32, (k8, k8, s8, s8[:1]), bt, ln, 16, match="v_scale")
     raises(K.kvq4_decode_attn, q, q, pool4, bt, ln, 32, pool8, bt[:1], ln, 16, match="block_tables8")
     raises(K.kvq4_decode_attn, q[:1], q, pool4, bt, ln, 32, pool8, bt, ln, 16, match="out")
     raises(K.kvq4_requantize_q8, pool4, (k8[:, :8], k8[:, :8], s8[:, :8], s8[:, :8]), ln, ln, match="share")
+    raises(K.kvq4_requantize_q8, (c4[:, :1],) * 2 + (g4[:, :1],) * 4, pool8, ln, ln, match="share")
     raises(K.kvq4_quantize_append, c4, c4[:1], g4, g4, g4, g4, kn, kn, ln, match="v4")
-    s40 = z(nb, bs, nkv, 4)
-    raises(K.kvq4_0_decode_attn, q, q, c4, c4, s40, s40[..., :2], bt, ln, 32, match="v_step")
-    raises(K.kvq4_0_quantize_append, c4, c4, s40, s40, kn, kn, ln[:1], match="slots")
+    c40, s40 = z(nb, bs, nkv, 64, dt=u8), z(nb, bs, nkv, 4)
+    raises(K.kvq4_0_decode_attn, q, q, c40, c40, s40, s40[..., :2], bt, ln, 32, match="v_step")
+    raises(K.kvq4_0_quantize_append, c40, c40, s40, s40, kn, kn, ln[:1], match="slots")
 
 
 def _decode4(**kw):
@@ -330,19 +331,19 @@ def test_binding_checks_two_bit_pools():
     z = lambda *s, dt=torch.float32: torch.zeros(s, dtype=dt)  # noqa: E731
     u8, f16, i8, i32 = torch.uint8, torch.float16, torch.int8, torch.int32
     nb, bs, nkv, B, nq = 4, 16, 2, 3, 4
-    c2, g = z(nb, bs, nkv, 32, dt=u8), z(nb, bs, nkv, 2, dt=f16)
-    c4 = z(nb, bs, nkv, 64, dt=u8)
+    c2, g = z(nb, nkv, bs, 32, dt=u8), z(nb, nkv, bs, 2, dt=f16)     # head-major inside a block
+    c4 = z(nb, nkv, bs, 64, dt=u8)
     p2, p4 = (c2, c2, g, g, g, g), (c4, c4, g, g, g, g)
     p8 = (z(nb, bs, nkv, 128, dt=i8), z(nb, bs, nkv, 128, dt=i8), z(nb, bs, nkv), z(nb, bs, nkv))
     q, bt, ln = z(B, nq, 128), z(B, 2, dt=i32), z(B, dt=i32)
     with pytest.raises(ValueError, match="v2_zero"):
         K.kvq2_decode_attn(q, q, (c2, c2, g, g, g, g[:1]), bt, ln, 32, p4, bt, ln, 32, p8, bt, ln, 32)
     with pytest.raises(ValueError, match="share"):
-        K.kvq2_decode_attn(q, q, p2, bt, ln, 32, (c4[:, :8],) * 2 + (g[:, :8],) * 4, bt, ln, 32, p8, bt, ln, 32)
+        K.kvq2_decode_attn(q, q, p2, bt, ln, 32, (c4[:, :, :8],) * 2 + (g[:, :, :8],) * 4, bt, ln, 32, p8, bt, ln, 32)
     with pytest.raises(ValueError, match="lens2"):
         K.kvq2_decode_attn(q, q, p2, bt, ln[:1], 32, p4, bt, ln, 32, p8, bt, ln, 32)
     with pytest.raises(ValueError, match="share"):
-        K.kvq2_requantize_q4(p2, (c4[:, :8],) * 2 + (g[:, :8],) * 4, ln, ln)
+        K.kvq2_requantize_q4(p2, (c4[:, :, :8],) * 2 + (g[:, :, :8],) * 4, ln, ln)
     kn = z(5, nkv, 128)
     with pytest.raises(ValueError, match="slots"):
         K.kvq2_quantize_append(*p2, kn, kn, ln)

@@ -12,8 +12,7 @@ from oracle import kvq2 as O2
 from oracle import kvq4 as O4
 from oracle import kvq4_0 as O40
 from oracle import kvq8 as O8
-from tests.helpers import (SM, Q8Cache, assert_attn_close, dev, fill_sequences, host, pool_library_order,
-                           q4_key_library_order)
+from tests.helpers import SM, Q8Cache, assert_attn_close, dev, fill_sequences, host, pool_library_order
 from tests.test_gpu_kvq2 import Q2Pool, _banded
 from tests.test_gpu_kvq4 import Q4Pool
 from tests.test_gpu_kvq4_0 import Q40Cache
@@ -166,7 +165,7 @@ def test_requantize_replays(K):
     O4.requantize_q8_to_q4((c8.kp, c8.ks, c8.vp, c8.vs), p4.oracle_pools(), src8, dst4)
     s8, d4 = dev(src8), dev(dst4)
     _requant_replays(lambda: K.kvq4_requantize_q8(p4.g, (c8.gk, c8.gv, c8.gks, c8.gvs), s8, d4), p4.g,
-                     [q4_key_library_order(p4.h[0])] + p4.h[1:], "int8 -> int4")    # the device's storage order
+                     p4.device_expect(), "int8 -> int4")
 
     src4 = r.permutation(nb4 * BS)[:n].astype(np.int32)
     dst2 = r.permutation(nb2 * BS)[:n].astype(np.int32)
@@ -174,7 +173,7 @@ def test_requantize_replays(K):
     p2 = Q2Pool(nb2, BS, NKV)
     O2.requantize_q4_to_q2(p4.oracle_pools(), p2.oracle_pools(), src4, dst2)
     s4, d2 = dev(src4), dev(dst2)
-    _requant_replays(lambda: K.kvq2_requantize_q4(p2.g, p4.g, s4, d2), p2.g, p2.h, "int4 -> 2-bit")
+    _requant_replays(lambda: K.kvq2_requantize_q4(p2.g, p4.g, s4, d2), p2.g, p2.device_expect(), "int4 -> 2-bit")
 
 
 @pytest.mark.parametrize("mode", ["int8", "int4", "2-bit", "Q4_0"])
@@ -206,11 +205,11 @@ def test_write_path_replays(K, mode):
     elif mode == "int4":
         p = Q4Pool(nb, BS, NKV)
         O4.quantize_append_q4(*p.h, xe, ye, slots)
-        pool, expect = p.g, [q4_key_library_order(p.h[0])] + p.h[1:]             # the device's storage order
+        pool, expect = p.g, p.device_expect()
         call = lambda: K.kvq4_quantize_append(*pool, kb, vb, sd)
     else:
         p = Q2Pool(nb, BS, NKV)
         O2.quantize_append_q2(*p.h, xe, ye, slots)
-        pool, expect = p.g, p.h
+        pool, expect = p.g, p.device_expect()
         call = lambda: K.kvq2_quantize_append(*pool, kb, vb, sd)
     _requant_replays(call, pool, expect, f"{mode} write")

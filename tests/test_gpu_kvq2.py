@@ -6,7 +6,7 @@ import pytest
 
 import workloads as W
 from oracle import kvq2 as O2
-from tests.helpers import SM, Q8Cache, assert_attn_close, dev, host
+from tests.helpers import SM, Q8Cache, assert_attn_close, dev, head_major, host, slot_major
 from tests.test_gpu_kvq4 import Q4Pool
 
 pytestmark = pytest.mark.gpu
@@ -24,13 +24,13 @@ class Q2Pool:
 
     def __init__(self, nb, bs, nkv):
         import torch
-        shp = (nb, bs, nkv)
+        shp, gshp = (nb, bs, nkv), (nb, nkv, bs)     # oracle slot-major, device head-major
         self.bs = bs
         self.h = [np.zeros(shp + (32,), np.uint8), np.zeros(shp + (32,), np.uint8)] + \
                  [np.zeros(shp + (2,), np.float16) for _ in range(4)]
-        self.g = [torch.zeros(shp + (32,), dtype=torch.uint8, device="cuda"),
-                  torch.zeros(shp + (32,), dtype=torch.uint8, device="cuda")] + \
-                 [torch.zeros(shp + (2,), dtype=torch.float16, device="cuda") for _ in range(4)]
+        self.g = [torch.zeros(gshp + (32,), dtype=torch.uint8, device="cuda"),
+                  torch.zeros(gshp + (32,), dtype=torch.uint8, device="cuda")] + \
+                 [torch.zeros(gshp + (2,), dtype=torch.float16, device="cuda") for _ in range(4)]
 
     def append(self, K, k, v, slots, gk=None, gv=None):
         h = self.h
@@ -42,9 +42,13 @@ class Q2Pool:
         h = self.h
         return (h[0], h[2], h[3], h[1], h[4], h[5])
 
+    def device_expect(self):
+        """The oracle's pool in the device's order."""
+        return [head_major(x) for x in self.h]
+
     def assert_same(self, what=""):
         for i, (x, y) in enumerate(zip(self.g, self.h)):
-            assert np.array_equal(host(x).view(np.uint8), y.view(np.uint8)), f"{what} array {i} differs"
+            assert np.array_equal(slot_major(host(x)).view(np.uint8), y.view(np.uint8)), f"{what} array {i} differs"
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])

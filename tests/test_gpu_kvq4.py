@@ -7,7 +7,8 @@ import pytest
 import workloads as W
 from oracle import kvq4 as O4
 from oracle import kvq8 as O8
-from tests.helpers import SM, Q8Cache, assert_attn_close, dev, host, q4_key_pages_order
+from tests.helpers import (SM, Q8Cache, assert_attn_close, dev, head_major, host, q4_key_library_order,
+                           q4_key_pages_order, slot_major)
 
 pytestmark = pytest.mark.gpu
 
@@ -19,15 +20,18 @@ def K():
 
 
 class Q4Pool:
+    """An int4 pool held both on the host (oracle: slot-major, key rows in the
+    pages' order) and on the GPU (head-major, the library's key order)."""
+
     def __init__(self, nb, bs, nkv):
         import torch
-        shp = (nb, bs, nkv)
+        shp, gshp = (nb, bs, nkv), (nb, nkv, bs)
         self.bs = bs
         self.h = [np.zeros(shp + (64,), np.uint8), np.zeros(shp + (64,), np.uint8)] + \
                  [np.zeros(shp + (2,), np.float16) for _ in range(4)]
-        self.g = [torch.zeros(shp + (64,), dtype=torch.uint8, device="cuda"),
-                  torch.zeros(shp + (64,), dtype=torch.uint8, device="cuda")] + \
-                 [torch.zeros(shp + (2,), dtype=torch.float16, device="cuda") for _ in range(4)]
+        self.g = [torch.zeros(gshp + (64,), dtype=torch.uint8, device="cuda"),
+                  torch.zeros(gshp + (64,), dtype=torch.uint8, device="cuda")] + \
+                 [torch.zeros(gshp + (2,), dtype=torch.float16, device="cuda") for _ in range(4)]
 
     def append(self, K, k, v, slots, gk=None, gv=None):
         h = self.h
@@ -39,9 +43,13 @@ class Q4Pool:
         h = self.h
         return (h[0], h[2], h[3], h[1], h[4], h[5])
 
+    def device_expect(self):
+        """The oracle's pool in the device's order."""
+        return [head_major(q4_key_library_order(self.h[0]))] + [head_major(x) for x in self.h[1:]]
+
     def assert_same(self):
-        # key rows compared in the pages' order, as the oracle keeps them
-        got = [q4_key_pages_order(host(self.g[0]))] + [host(x) for x in self.g[1:]]
+        # compared in the oracle's order: slot-major, key rows in the pages' order
+        got = [q4_key_pages_order(slot_major(host(self.g[0])))] + [slot_major(host(x)) for x in self.g[1:]]
         for x, y in zip(got, self.h):
             assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
 

@@ -28,7 +28,7 @@ from oracle import kvq2 as O2
 from oracle import kvq4 as O4
 from oracle import kvq4_0 as O40
 from oracle import kvq8 as O8
-from tests.helpers import SM, assert_attn_close, dev, host, pool_pages_order, q4_key_pages_order
+from tests.helpers import SM, assert_attn_close, dev, host, pool_pages_order, q4_key_pages_order, slot_major
 
 pytestmark = pytest.mark.gpu
 
@@ -193,10 +193,10 @@ def test_q4_128k(K):
     n4, n8 = L - win, win
     bt4, nb4 = W.paged_block_tables(W.rng(5, 0, 1), [n4] * B, bs)
     bt8, nb8 = W.paged_block_tables(W.rng(5, 0, 2), [n8] * B, bs)
-    shp4 = (nb4, bs, nkv)
-    g4 = [torch.zeros(shp4 + (64,), dtype=torch.uint8, device="cuda"),
-          torch.zeros(shp4 + (64,), dtype=torch.uint8, device="cuda")] + \
-         [torch.zeros(shp4 + (2,), dtype=torch.float16, device="cuda") for _ in range(4)]
+    shp4, gshp4 = (nb4, bs, nkv), (nb4, nkv, bs)         # oracle slot-major, device head-major
+    g4 = [torch.zeros(gshp4 + (64,), dtype=torch.uint8, device="cuda"),
+          torch.zeros(gshp4 + (64,), dtype=torch.uint8, device="cuda")] + \
+         [torch.zeros(gshp4 + (2,), dtype=torch.float16, device="cuda") for _ in range(4)]
     g8 = _q8_pools(torch, nb8, bs, nkv)
     sig = W.rng(5, 0, 3).uniform(0.2, 5.0, size=(B, nkv, 2))
     checked = (0, 3)
@@ -219,7 +219,7 @@ def test_q4_128k(K):
                        dev(np.full(B, n8, np.int32)), n8, SM)
     torch.cuda.synchronize()
     got = host(out)
-    gh4 = [host(x) for x in g4]
+    gh4 = [slot_major(host(x)) for x in g4]             # the oracle's slot-major order
     gh4[0] = q4_key_pages_order(gh4[0])                 # int4 key rows in the pages' order
     gh8 = [host(x) for x in g8]
     gh8[:2] = [pool_pages_order(x) for x in gh8[:2]]      # codes in the pages' order, as the oracle keeps them
@@ -255,10 +255,11 @@ def test_q2_128k(K):
     bt8, nb8 = W.paged_block_tables(W.rng(9, 0, 3), [n8] * B, bs)
 
     def group_pool(nb, row, host_side):
-        shp = (nb, bs, nkv)
-        if host_side:
+        if host_side:                                   # the oracle's slot-major order
+            shp = (nb, bs, nkv)
             return [np.zeros(shp + (row,), np.uint8), np.zeros(shp + (row,), np.uint8)] + \
                    [np.zeros(shp + (2,), np.float16) for _ in range(4)]
+        shp = (nb, nkv, bs)                             # the device's head-major order
         return [torch.zeros(shp + (row,), dtype=torch.uint8, device="cuda"),
                 torch.zeros(shp + (row,), dtype=torch.uint8, device="cuda")] + \
                [torch.zeros(shp + (2,), dtype=torch.float16, device="cuda") for _ in range(4)]
@@ -287,7 +288,8 @@ def test_q2_128k(K):
                        dev(np.full(B, n4, np.int32)), n4, g8, dev(bt8), dev(np.full(B, n8, np.int32)), n8, SM)
     torch.cuda.synchronize()
     got = host(out)
-    gh2, gh4, gh8 = [host(x) for x in g2], [host(x) for x in g4], [host(x) for x in g8]
+    gh2, gh4 = [slot_major(host(x)) for x in g2], [slot_major(host(x)) for x in g4]
+    gh8 = [host(x) for x in g8]
     gh4[0] = q4_key_pages_order(gh4[0])                 # int4 key rows in the pages' order
     gh8[:2] = [pool_pages_order(x) for x in gh8[:2]]      # codes in the pages' order, as the oracle keeps them
     for b in checked:

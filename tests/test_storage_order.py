@@ -9,7 +9,8 @@ helpers that convert device pools to the pages' layout (CPU only):
 import numpy as np
 
 from oracle import kvq4 as O4
-from tests.helpers import pool_columns, pool_library_order, pool_pages_order, q4_key_library_order, q4_key_pages_order
+from tests.helpers import (head_major, pool_columns, pool_library_order, pool_pages_order, q4_key_library_order,
+                           q4_key_pages_order, slot_major)
 
 
 def test_q4_key_order_matches_header_formula():
@@ -44,3 +45,18 @@ def test_int8_rotation_matches_header_formula():
                 assert col[s, kh] == (kh & ~(p - 1)) | ((kh + s) & (p - 1))
         x = np.random.default_rng(nkv).integers(-127, 128, (5, 8, nkv, 128)).astype(np.int8)
         assert np.array_equal(pool_pages_order(pool_library_order(x)), x)
+
+
+def test_head_major_rows_match_header_formula():
+    """The int4 / 2-bit pools keep slot s = block * kv_bs + offset of kv-head
+    kh in row (block * nkv + kh) * kv_bs + offset (include/kvq8.h); the tests'
+    conversion from the oracle's slot-major arrays must put it there."""
+    nb, bs, nkv = 3, 8, 5
+    slot = np.arange(nb * bs).reshape(nb, bs, 1)
+    kh = np.arange(nkv).reshape(1, 1, nkv)
+    x = (slot * 100 + kh).astype(np.int64)              # [n_blocks][kv_bs][nkv], one value per (slot, head)
+    rows = head_major(x).reshape(-1)
+    for s in range(nb * bs):
+        for h in range(nkv):
+            assert rows[((s // bs) * nkv + h) * bs + s % bs] == s * 100 + h
+    assert np.array_equal(slot_major(head_major(x)), x)
