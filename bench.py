@@ -522,7 +522,7 @@ def run_workloads(only=None):
 
     # Q4_0 mode (80 B per row: 160 B per (token, kv-head) for K and V)
     def q40_pool(nb, bs, nkv):
-        shp = (nb, bs, nkv)
+        shp = (nb, nkv, bs)                        # head-major inside a block
         return [torch.zeros(shp + (64,), dtype=torch.uint8, device="cuda"),
                 torch.zeros(shp + (64,), dtype=torch.uint8, device="cuda"),
                 torch.zeros(shp + (4,), dtype=torch.float32, device="cuda"),

@@ -145,22 +145,21 @@ extern "C" int kvq8_quantize_append(int8_t* k_cache, int8_t* v_cache, float* k_s
     // pool rows (slot * nkv + head) are 32-bit in the kernel: 2^32 rows would
     // take 512 GiB of codes
     if (n_slots * nkv > 0xFFFFFFFFL) return KVQ8_ESHAPE;
-    const uint32_t ns_cap = (uint32_t)(n_slots < 0x80000000L ? n_slots : 0x80000000L);
     const dim3 grid((unsigned)((n_rows + kRowsPerBlock - 1) / kRowsPerBlock)), block(256);
     hipStream_t s = static_cast<hipStream_t>(stream);
     int st;
     switch (dtype) {
         case KVQ8_F32:
             st = launch(kvq8_quantize_append_kernel<KVQ8_F32>, grid, block, s, k_cache, v_cache, k_scale,
-                               v_scale, ns_cap, make_divn(nkv), k_new, v_new, (int)n_rows, slots);
+                               v_scale, slot_cap(n_slots), make_divn(nkv), k_new, v_new, (int)n_rows, slots);
             break;
         case KVQ8_BF16:
             st = launch(kvq8_quantize_append_kernel<KVQ8_BF16>, grid, block, s, k_cache, v_cache, k_scale,
-                               v_scale, ns_cap, make_divn(nkv), k_new, v_new, (int)n_rows, slots);
+                               v_scale, slot_cap(n_slots), make_divn(nkv), k_new, v_new, (int)n_rows, slots);
             break;
         default:
             st = launch(kvq8_quantize_append_kernel<KVQ8_F16>, grid, block, s, k_cache, v_cache, k_scale,
-                               v_scale, ns_cap, make_divn(nkv), k_new, v_new, (int)n_rows, slots);
+                               v_scale, slot_cap(n_slots), make_divn(nkv), k_new, v_new, (int)n_rows, slots);
             break;
     }
     return st;

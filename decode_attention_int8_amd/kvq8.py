@@ -423,21 +423,22 @@ def kvq4_decode_attn(out, q, pool4, block_tables4, lens4, max_len4: int, pool8, 
 # ----------------------------------------------------------------------------
 
 def _q40_pool(k_cache, v_cache, k_step, v_step):
-    """Packed codes [n_blocks][kv_bs][nkv][hd / 2], K and V alike, and steps
-    [n_blocks][kv_bs][nkv][hd / 32]."""
+    """Packed codes [n_blocks][nkv][kv_bs][hd / 2] (head-major inside a
+    block), K and V alike, and steps [n_blocks][nkv][kv_bs][hd / 32].
+    Returns (n_blocks, kv_bs, nkv, hd)."""
     if k_cache.dim() != 4:
-        raise ValueError("k_cache must be [n_blocks][kv_bs][nkv][hd / 2]")
+        raise ValueError("k_cache must be [n_blocks][nkv][kv_bs][hd / 2]")
     _shape(v_cache, k_cache.shape, "v_cache")
-    n, bs, nkv, half = k_cache.shape
-    _shape(k_step, (n, bs, nkv, 2 * half // 32), "k_step")
-    _shape(v_step, (n, bs, nkv, 2 * half // 32), "v_step")
+    n, nkv, bs, half = k_cache.shape
+    _shape(k_step, (n, nkv, bs, 2 * half // 32), "k_step")
+    _shape(v_step, (n, nkv, bs, 2 * half // 32), "v_step")
     return n, bs, nkv, 2 * half
 
 
 def kvq4_0_quantize_append(k_cache, v_cache, k_step, v_step, k_new, v_new, slots, stream=None):
     """Quantize k_new / v_new [n_tokens][nkv][128] (f32, bf16 or f16) into the
-    Q4_0 pool: packed codes [n_blocks][kv_bs][nkv][64] uint8, steps
-    [n_blocks][kv_bs][nkv][4] float32, at ``slots`` (int32)."""
+    Q4_0 pool: packed codes [n_blocks][nkv][kv_bs][64] uint8, steps
+    [n_blocks][nkv][kv_bs][4] float32, at ``slots`` (int32)."""
     n_blocks, kv_bs, nkv, hd = _q40_pool(k_cache, v_cache, k_step, v_step)
     if k_new.dtype not in _DTYPES or v_new.dtype != k_new.dtype:
         raise ValueError("k_new / v_new must share one of float32, bfloat16, float16")

@@ -391,15 +391,15 @@ int kvq4_decode_attn(float* out, const float* q, int batch, int nq,
  * 64 code bytes + 4 float32 steps = 80 B per row (q8: 132 B, 1.65x).
  *
  * Pools (caller-owned device memory, 16-byte aligned):
- *   k_cache, v_cache  uint8 [n_blocks][kv_bs][nkv * 64], two codes per byte:
+ *   k_cache, v_cache  uint8 [n_blocks][nkv][kv_bs][64], two codes per byte:
  *                     key row byte j = code[j] | code[64 + j] << 4;
  *                     value row byte 4m + k = code[32k + 2m] |
  *                     code[32k + 2m + 1] << 4  (k = 0..3, m = 0..15);
- *                     the 64-byte rows of a slot's heads in the int8
- *                     pool's storage order (head kh of slot s at column
- *                     (kh & ~(P - 1)) | ((kh + s) & (P - 1)))
- *   k_step, v_step    float32 [n_blocks][kv_bs][nkv][4], one per block
- *                     (not rotated)
+ *                     rows head-major inside each block as in the int4
+ *                     pool: slot s = block * kv_bs + offset of kv-head kh
+ *                     is row (block * nkv + kh) * kv_bs + offset
+ *   k_step, v_step    float32 [n_blocks][nkv][kv_bs][4], one per block,
+ *                     rows in the same order
  * ------------------------------------------------------------------------ */
 
 /*

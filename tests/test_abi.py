@@ -165,7 +165,7 @@ def test_binding_checks_every_buffer_shape():
     raises(K.kvq4_requantize_q8, pool4, (k8[:, :8], k8[:, :8], s8[:, :8], s8[:, :8]), ln, ln, match="share")
     raises(K.kvq4_requantize_q8, (c4[:, :1],) * 2 + (g4[:, :1],) * 4, pool8, ln, ln, match="share")
     raises(K.kvq4_quantize_append, c4, c4[:1], g4, g4, g4, g4, kn, kn, ln, match="v4")
-    c40, s40 = z(nb, bs, nkv, 64, dt=u8), z(nb, bs, nkv, 4)
+    c40, s40 = z(nb, nkv, bs, 64, dt=u8), z(nb, nkv, bs, 4)     # head-major inside a block
     raises(K.kvq4_0_decode_attn, q, q, c40, c40, s40, s40[..., :2], bt, ln, 32, match="v_step")
     raises(K.kvq4_0_quantize_append, c40, c40, s40, s40, kn, kn, ln[:1], match="slots")
 

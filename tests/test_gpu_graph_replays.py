@@ -200,7 +200,7 @@ def test_write_path_replays(K, mode):
         c = Q40Cache(nb, BS, NKV)
         O40.quantize_append_q4_0(c.kp, c.vp, c.ks, c.vs, xe, ye, slots)
         pool = [c.gk, c.gv, c.gks, c.gvs]
-        expect = [pool_library_order(c.kp), pool_library_order(c.vp), c.ks, c.vs]   # the device's storage order
+        expect = c.device_expect()
         call = lambda: K.kvq4_0_quantize_append(*pool, kb, vb, sd)
     elif mode == "int4":
         p = Q4Pool(nb, BS, NKV)

@@ -9,7 +9,7 @@ import pytest
 
 import workloads as W
 from oracle import kvq4_0 as Q, kvq8 as O8
-from tests.helpers import SM, assert_attn_close, dev, host, pool_pages_order
+from tests.helpers import SM, assert_attn_close, dev, head_major, host, slot_major
 
 pytestmark = pytest.mark.gpu
 
@@ -31,15 +31,19 @@ class Q40Cache:
     def __init__(self, n_blocks, kv_bs, nkv):
         import torch
         self.kv_bs, self.nkv = kv_bs, nkv
-        shp = (n_blocks, kv_bs, nkv)
+        shp, gshp = (n_blocks, kv_bs, nkv), (n_blocks, nkv, kv_bs)   # oracle slot-major, device head-major
         self.kp = np.zeros(shp + (64,), np.uint8)
         self.vp = np.zeros(shp + (64,), np.uint8)
         self.ks = np.zeros(shp + (4,), np.float32)
         self.vs = np.zeros(shp + (4,), np.float32)
-        self.gk = torch.zeros(self.kp.shape, dtype=torch.uint8, device="cuda")
-        self.gv = torch.zeros(self.vp.shape, dtype=torch.uint8, device="cuda")
-        self.gks = torch.zeros(self.ks.shape, dtype=torch.float32, device="cuda")
-        self.gvs = torch.zeros(self.vs.shape, dtype=torch.float32, device="cuda")
+        self.gk = torch.zeros(gshp + (64,), dtype=torch.uint8, device="cuda")
+        self.gv = torch.zeros(gshp + (64,), dtype=torch.uint8, device="cuda")
+        self.gks = torch.zeros(gshp + (4,), dtype=torch.float32, device="cuda")
+        self.gvs = torch.zeros(gshp + (4,), dtype=torch.float32, device="cuda")
+
+    def device_expect(self):
+        """The oracle's pool in the device's order (k, v, k_step, v_step)."""
+        return [head_major(x) for x in (self.kp, self.vp, self.ks, self.vs)]
 
     def append(self, k_new, v_new, slots, gk_new=None, gv_new=None):
         import decode_attention_int8_amd as K
@@ -49,10 +53,10 @@ class Q40Cache:
                                  dev(v_new) if gv_new is None else gv_new, dev(np.asarray(slots, np.int32)))
 
     def assert_device_matches_host(self):
-        assert np.array_equal(pool_pages_order(host(self.gk)), self.kp), "K codes differ"
-        assert np.array_equal(pool_pages_order(host(self.gv)), self.vp), "V codes differ"
-        assert np.array_equal(host(self.gks).view(np.uint32), self.ks.view(np.uint32)), "K steps differ"
-        assert np.array_equal(host(self.gvs).view(np.uint32), self.vs.view(np.uint32)), "V steps differ"
+        assert np.array_equal(slot_major(host(self.gk)), self.kp), "K codes differ"
+        assert np.array_equal(slot_major(host(self.gv)), self.vp), "V codes differ"
+        assert np.array_equal(slot_major(host(self.gks)).view(np.uint32), self.ks.view(np.uint32)), "K steps differ"
+        assert np.array_equal(slot_major(host(self.gvs)).view(np.uint32), self.vs.view(np.uint32)), "V steps differ"
 
 
 def _fill(cache, bt, lens, k, v):

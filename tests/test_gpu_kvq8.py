@@ -376,9 +376,9 @@ def test_default_score_scale_is_one_over_sqrt_hd(K):
     for o in outs[:3]:
         assert np.array_equal(o.view(np.uint32), outs[3].view(np.uint32))
     # Q4_0 cache from the same keys
-    k4 = torch.zeros((nb, bs, nkv, 64), dtype=torch.uint8, device="cuda")
+    k4 = torch.zeros((nb, nkv, bs, 64), dtype=torch.uint8, device="cuda")     # head-major inside a block
     v4 = torch.zeros_like(k4)
-    ks4 = torch.zeros((nb, bs, nkv, 4), dtype=torch.float32, device="cuda")
+    ks4 = torch.zeros((nb, nkv, bs, 4), dtype=torch.float32, device="cuda")
     vs4 = torch.zeros_like(ks4)
     for b in range(B):
         sl = W.slots_for_positions(bt, [b] * int(lens[b]), np.arange(lens[b]), bs)

@@ -311,7 +311,7 @@ def test_q2_128k(K):
 
 
 def _q40_pools(torch, nb, bs, nkv):
-    shp = (nb, bs, nkv)
+    shp = (nb, nkv, bs)                                 # the device's head-major order
     return (torch.zeros(shp + (64,), dtype=torch.uint8, device="cuda"),
             torch.zeros(shp + (64,), dtype=torch.uint8, device="cuda"),
             torch.zeros(shp + (4,), dtype=torch.float32, device="cuda"),
@@ -344,8 +344,8 @@ def test_q40_qwen8b_batch32_layer0(K):
     out = torch.empty((B, nq, 128), dtype=torch.float32, device="cuda")
     K.kvq4_0_decode_attn(out, q, gk, gv, gks, gvs, dev(bt), dev(lens), int(lens.max()), SM)
     torch.cuda.synchronize()
-    assert np.array_equal(pool_pages_order(host(gk)), hk) and np.array_equal(pool_pages_order(host(gv)), hv)
-    assert _same(host(gks), hks) and _same(host(gvs), hvs)
+    assert np.array_equal(slot_major(host(gk)), hk) and np.array_equal(slot_major(host(gv)), hv)
+    assert _same(slot_major(host(gks)), hks) and _same(slot_major(host(gvs)), hvs)
     ref = O40.decode_attention_q4_0(host(q), hk, hks, hv, hvs, bt, lens, bs, SM)
     assert_attn_close(host(out), ref, "Q4_0 qwen8b batch 32")
 
@@ -366,7 +366,7 @@ def test_q40_append64k_then_decode(K):
     torch.cuda.synchronize()
     hk, hv, hks, hvs = _q40_host(nb, bs, nkv)
     O40.quantize_append_q4_0(hk, hv, hks, hvs, host(k.float()), host(v.float()), slots)
-    assert np.array_equal(pool_pages_order(host(gk)), hk) and np.array_equal(pool_pages_order(host(gv)), hv)
-    assert _same(host(gks), hks) and _same(host(gvs), hvs)
+    assert np.array_equal(slot_major(host(gk)), hk) and np.array_equal(slot_major(host(gv)), hv)
+    assert _same(slot_major(host(gks)), hks) and _same(slot_major(host(gvs)), hvs)
     ref = O40.decode_attention_q4_0(host(q), hk, hks, hv, hvs, bt, [n], bs, SM)
     assert_attn_close(host(out), ref, "Q4_0 append64k decode")
