@@ -36,7 +36,7 @@ def assert_attn_close(got, ref, what=""):
 
 
 def pool_columns(n_slots, nkv):
-    """The library's storage order of the int8 and Q4_0 code pools: the
+    """The library's storage order of the int8 code pool: the
     column of head kh in the row of slot s (within each aligned group of P
     heads, P the largest power of two dividing nkv, at most 8, the heads
     rotate with the slot).  Steps are not rotated."""

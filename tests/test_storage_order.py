@@ -4,8 +4,10 @@ helpers that convert device pools to the pages' layout (CPU only):
 * int4 key rows: the pair starting at element 64h + 16c + 2j (h = 0, 1;
   c = 0..3; j = 0..7) sits in byte 16c + 8h + j, even element in the high
   nibble; the pages' layout (the oracle's) keeps pair i in byte i.
-* int8 / Q4_0 code pools: head kh of slot s at column (kh & ~(P-1)) |
-  ((kh + s) & (P-1)), P the largest power of two dividing nkv, at most 8."""
+* int8 code pools: head kh of slot s at column (kh & ~(P-1)) |
+  ((kh + s) & (P-1)), P the largest power of two dividing nkv, at most 8.
+* int4, 2-bit and Q4_0 pools: head-major inside each block, slot s of head
+  kh at row (s / kv_bs * nkv + kh) * kv_bs + s % kv_bs."""
 import numpy as np
 
 from oracle import kvq4 as O4
