@@ -330,8 +330,9 @@ int kvq4_quantize_append(uint8_t* k_cache, uint8_t* v_cache,
  *   n_blocks4, n_blocks8 blocks in each pool (same kv_bs and nkv)
  *   src_slots, dst_slots (device) int32 [n_tokens]
  *
- * Returns KVQ8_ESHAPE for a bad hd, kv_bs or nkv or for more than 2^31 - 65
- * rows (n_tokens * nkv * 2: rows are indexed with 32-bit integers), and
+ * Returns KVQ8_ESHAPE for a bad hd, kv_bs or nkv, for more than 2^31 - 129
+ * rows (n_tokens * nkv * 2: rows are indexed with 32-bit integers) and for a
+ * destination pool of 2^32 or more rows (n_blocks * kv_bs * nkv), and
  * KVQ8_EINVAL for a null or misaligned pointer or n_tokens < 0.
  */
 int kvq4_requantize_q8(uint8_t* k_cache4, uint8_t* v_cache4, uint16_t* k_scale4, uint16_t* k_zero4,

@@ -270,6 +270,23 @@ def test_write_row_limit():
                                       big, _fake(), None) == ESHAPE
     assert lib.kvq4_requantize_q8(_fake(), _fake(), _fake(), _fake(), _fake(), _fake(), 64, _fake(), _fake(),
                                   _fake(), _fake(), 64, 16, 8, 128, big, _fake(), _fake(), None) == ESHAPE
+    # pools of 2^25 blocks x 16 slots x 8 heads = 2^32 rows: beyond the 32-bit
+    # pool rows of the int4, 2-bit and Q4_0 writers and re-quantizations
+    huge = 1 << 25
+    assert lib.kvq4_quantize_append(_fake(), _fake(), _fake(), _fake(), _fake(), _fake(), huge, 16, 8, 128,
+                                    _fake(), _fake(), K.BF16, 10, _fake(), None) == ESHAPE
+    assert lib.kvq2_quantize_append(_fake(), _fake(), _fake(), _fake(), _fake(), _fake(), huge, 16, 8, 128,
+                                    _fake(), _fake(), K.BF16, 10, _fake(), None) == ESHAPE
+    assert lib.kvq4_0_quantize_append(_fake(), _fake(), _fake(), _fake(), huge, 16, 8, 128, _fake(), _fake(),
+                                      K.BF16, 10, _fake(), None) == ESHAPE
+    assert lib.kvq4_requantize_q8(_fake(), _fake(), _fake(), _fake(), _fake(), _fake(), huge, _fake(), _fake(),
+                                  _fake(), _fake(), 64, 16, 8, 128, 10, _fake(), _fake(), None) == ESHAPE
+    assert lib.kvq2_requantize_q4(_fake(), _fake(), _fake(), _fake(), _fake(), _fake(), huge, _fake(), _fake(),
+                                  _fake(), _fake(), _fake(), _fake(), 64, 16, 8, 128, 10, _fake(), _fake(),
+                                  None) == ESHAPE
+    assert lib.kvq2_requantize_q4(_fake(), _fake(), _fake(), _fake(), _fake(), _fake(), 64, _fake(), _fake(),
+                                  _fake(), _fake(), _fake(), _fake(), huge, 16, 8, 128, 10, _fake(), _fake(),
+                                  None) == ESHAPE
 
 
 def _decode2(**kw):
