@@ -501,7 +501,8 @@ int kvq2_quantize_append(uint8_t* k_cache, uint8_t* v_cache,
  *   n_blocks2, n_blocks4 blocks in each pool (same kv_bs and nkv)
  *   src_slots, dst_slots (device) int32 [n_tokens]
  *
- * Errors as for kvq4_requantize_q8.
+ * Errors as for kvq4_requantize_q8 (here either pool of 2^32 or more rows
+ * is rejected).
  */
 int kvq2_requantize_q4(uint8_t* k_cache2, uint8_t* v_cache2, uint16_t* k_scale2, uint16_t* k_zero2,
                        uint16_t* v_scale2, uint16_t* v_zero2, int n_blocks2,
