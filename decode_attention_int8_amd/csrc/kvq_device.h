@@ -115,20 +115,14 @@ __device__ __forceinline__ void lds_barrier() {
     __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Rounding a quotient to an integer without dividing.  The quantizers round
-// x / d, the IEEE quotient, to an integer (to nearest, or down after adding
-// one half).  q = x * rcp(d), with v_rcp_f32 within one ulp of 1 / d, lies
-// within |q| * 2^-21 of that quotient for normal operands, so rounding q gives
-// the same integer unless one of the two lies within that distance of a
-// half-integer.  `near_half` flags q within 2^-12 + |q| * 2^-19 of one (and
-// any q that is not finite); there the caller divides.  The margin is four
-// times the bound and more; the flag is raised for about 0.1% of the values.
-__device__ __forceinline__ bool near_half(float q) {
-    return !(fabsf(q - rintf(q)) <= 0.5f - (0x1p-12f + fabsf(q) * 0x1p-19f));
-}
-
-// The same test for |q| <= 128 (int8 and Q4_0 codes), where the margin is at
-// most 2^-11: `rq` is rintf(q).
+// Rounding a quotient to an integer without dividing (the decode's fused
+// write path; the other write paths use an FMA onto a fixed-point grid).  The
+// quantizer rounds x / d, the IEEE quotient, to nearest.  q = x * rcp(d), with
+// v_rcp_f32 within one ulp of 1 / d, lies within |q| * 2^-21 of that quotient
+// for normal operands, so rounding q gives the same integer unless one of the
+// two lies within that distance of a half-integer.  For |q| <= 128,
+// `near_half_small` flags q within 2^-11 of one (`rq` is rintf(q); a q that is
+// not finite is flagged too); there the caller divides.
 __device__ __forceinline__ bool near_half_small(float q, float rq) {
     return !(fabsf(q - rq) <= 0.5f - 0x1p-11f);
 }
