@@ -2,7 +2,8 @@
 through the C ABI: kv-head counts 1-8 (not only powers of two), query groups
 1-8, block sizes 8-256, batches of 1-5 sequences with ragged lengths
 (empty ones included), the default and explicit chunk lengths, and, for the
-int8 cache, the fused write-then-attend call.  Each case draws its shape
+int8 cache, the fused write-then-attend call; and every write path and
+re-quantization over random pools and slot lists.  Each case draws its shape
 from its own seed, so a failure names a reproducible configuration.
 Outputs within 1e-4 + 1e-4 |oracle|; the pools written by the library
 equal the oracle's bit for bit."""
@@ -10,11 +11,12 @@ import numpy as np
 import pytest
 
 import workloads as W
+from oracle import kvq2 as O2
 from oracle import kvq4 as O4
 from oracle import kvq4_0 as O40
 from oracle import kvq8 as O8
 from tests.helpers import SM, Q8Cache, assert_attn_close, dev, fill_sequences, host
-from tests.test_gpu_kvq2 import _banded, _decode_and_check
+from tests.test_gpu_kvq2 import Q2Pool, _banded, _decode_and_check
 from tests.test_gpu_kvq4 import Q4Pool
 from tests.test_gpu_kvq4_0 import Q40Cache
 
@@ -143,3 +145,71 @@ def test_q40_decode(K, seed):
     torch.cuda.synchronize()
     ref = O40.decode_attention_q4_0(q, c.kp, c.ks, c.vp, c.vs, bt, lens, bs, SM)
     assert_attn_close(host(out), ref, what)
+
+
+# ----------------------------------------------------------------------------
+# write paths and re-quantizations: random pools, row counts and slot lists
+# (a permutation of the pool's slots with some rows sent to a negative slot
+# and some past the pool, both skipped); pools bit for bit against the oracle
+# ----------------------------------------------------------------------------
+
+def _write_shape(seed):
+    r = W.rng(991, seed)
+    nkv = int(r.integers(1, 13))
+    bs = int(r.choice([8, 16, 32, 64, 256]))
+    n = int(r.choice([1, 7, 64, 65, 300, 1000, 2500]))
+    nb = n // bs + int(r.integers(1, 4))
+    return r, nkv, bs, n, nb
+
+
+def _slots(r, n, n_slots):
+    sl = r.permutation(n_slots)[:n].astype(np.int32)
+    k = max(n // 10, 1) if n > 1 else 0
+    sl[r.choice(n, size=k, replace=False)] = -1 - r.integers(0, 5, size=k)
+    if n > 2:
+        sl[int(r.integers(0, n))] = n_slots + int(r.integers(0, 7))
+    return sl
+
+
+def _rows(r, n, nkv):
+    x = W.per_unit_sigma_normal(r, (n, nkv, 128), 1, 0.2, 5.0)
+    y = W.student_t3_f32(r, (n, nkv, 128), 0.5)
+    return x, y
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_write_paths(K, seed):
+    import torch
+    r, nkv, bs, n, nb = _write_shape(seed)
+    what = f"seed {seed}: nkv={nkv} bs={bs} n={n} blocks={nb}"
+    c8, p4, p2, c40 = Q8Cache(nb, bs, nkv), Q4Pool(nb, bs, nkv), Q2Pool(nb, bs, nkv), Q40Cache(nb, bs, nkv)
+    x, y = _rows(r, n, nkv)
+    c8.append(x, y, _slots(r, n, nb * bs))
+    p4.append(K, x, y, _slots(r, n, nb * bs))
+    p2.append(K, x, y, _slots(r, n, nb * bs))
+    c40.append(x, y, _slots(r, n, nb * bs))
+    torch.cuda.synchronize()
+    c8.assert_device_matches_host()
+    p4.assert_same()
+    p2.assert_same(what)
+    c40.assert_device_matches_host()
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_requantizations(K, seed):
+    import torch
+    r, nkv, bs, n, nb = _write_shape(seed + 100)
+    c8, p4, p2 = Q8Cache(nb, bs, nkv), Q4Pool(nb + 1, bs, nkv), Q2Pool(nb + 2, bs, nkv)
+    x, y = _rows(r, nb * bs, nkv)
+    c8.append(x, y, np.arange(nb * bs, dtype=np.int32))
+    # int8 -> int4, then int4 -> 2-bit, over random slot pairs with skips
+    src, dst = _slots(r, n, nb * bs), _slots(r, n, (nb + 1) * bs)
+    O4.requantize_q8_to_q4((c8.kp, c8.ks, c8.vp, c8.vs), p4.oracle_pools(), src, dst)
+    K.kvq4_requantize_q8(p4.g, (c8.gk, c8.gv, c8.gks, c8.gvs), dev(src), dev(dst))
+    src2, dst2 = _slots(r, n, (nb + 1) * bs), _slots(r, n, (nb + 2) * bs)
+    O2.requantize_q4_to_q2(p4.oracle_pools(), p2.oracle_pools(), src2, dst2)
+    K.kvq2_requantize_q4(p2.g, p4.g, dev(src2), dev(dst2))
+    torch.cuda.synchronize()
+    c8.assert_device_matches_host()
+    p4.assert_same()
+    p2.assert_same(f"seed {seed}: nkv={nkv} bs={bs} n={n}")
