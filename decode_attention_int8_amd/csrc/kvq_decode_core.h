@@ -284,7 +284,7 @@ constexpr int kMergeBatch = 16;
 constexpr int kMergeThreads = 2 * kHD;          // PARTS = 2
 constexpr int kMergeThreadsWide = 8 * kHD;      // PARTS = 8, for more than 32 chunks
 
-template <int PARTS, bool LIVE = false, class Args = DecodeArgs>
+template <int PARTS, bool LIVE = false, class Args = DecodeArgs, int BATCH = kMergeBatch>
 __global__ __launch_bounds__(PARTS * kHD) void kvq_merge_kernel(float* __restrict__ out, Args a) {
     constexpr bool HAS2 = kBanded<Args>;
     __shared__ float other[PARTS][kHD + 2];
@@ -308,10 +308,10 @@ __global__ __launch_bounds__(PARTS * kHD) void kvq_merge_kernel(float* __restric
     const int n8 = (effective_len(a.r8, b, a.log2_bs) + chunk_len - 1) / chunk_len;
     if constexpr (LIVE) cend = min(cend, n8);      // one int8 region: chunks [0, n8) are live
     float M = -INFINITY, S = 0.0f, acc = 0.0f;
-    for (int c0 = cbeg; c0 < cend; c0 += kMergeBatch) {
-        float mv[kMergeBatch], sv[kMergeBatch], av[kMergeBatch];
+    for (int c0 = cbeg; c0 < cend; c0 += BATCH) {
+        float mv[BATCH], sv[BATCH], av[BATCH];
 #pragma unroll
-        for (int k = 0; k < kMergeBatch; ++k) {
+        for (int k = 0; k < BATCH; ++k) {
             const int cc = min(c0 + k, cend - 1);
             // M and S are the same for every thread of the part; as scalar
             // loads they ran out of scalar registers and were waited for in
@@ -324,7 +324,7 @@ __global__ __launch_bounds__(PARTS * kHD) void kvq_merge_kernel(float* __restric
         }
         float bm = -INFINITY;
 #pragma unroll
-        for (int k = 0; k < kMergeBatch; ++k) {
+        for (int k = 0; k < BATCH; ++k) {
             const int c = c0 + k;
             bool live;
             if constexpr (HAS2)
@@ -344,7 +344,7 @@ __global__ __launch_bounds__(PARTS * kHD) void kvq_merge_kernel(float* __restric
         }
         if (M == -INFINITY) continue;
 #pragma unroll
-        for (int k = 0; k < kMergeBatch; ++k) {
+        for (int k = 0; k < BATCH; ++k) {
             const float f = __builtin_amdgcn_exp2f(mv[k] - M);
             S = fmaf(sv[k], f, S);
             acc = fmaf(av[k], f, acc);
@@ -479,11 +479,20 @@ __global__ __launch_bounds__(PARTS * kHD) void kvq_merge1_kernel(float* __restri
 }
 
 // Enqueue the merge of a decode's chunk partials into `out`.
+// A part's share of at most kMergeBatch / 2 chunks is read in one half-size
+// batch (the other half of a full batch would only repeat its last chunk).
+inline bool half_batch(int n_chunks, int parts) { return (n_chunks + parts - 1) / parts <= kMergeBatch / 2; }
+
 inline int launch_merge(const BandArgs& a, float* out, hipStream_t s) {
     const dim3 grid(a.batch * a.nq);
-    if (n_chunks_total(a) > 2 * kMergeBatch)
-        return launch((kvq_merge_kernel<8, false, BandArgs>), grid, dim3(kMergeThreadsWide), s, out, a);
-    return launch((kvq_merge_kernel<2, false, BandArgs>), grid, dim3(kMergeThreads), s, out, a);
+    constexpr int H = kMergeBatch / 2;
+    const int nct = n_chunks_total(a);
+    if (nct > 2 * kMergeBatch)
+        return half_batch(nct, 8)
+                   ? launch((kvq_merge_kernel<8, false, BandArgs, H>), grid, dim3(kMergeThreadsWide), s, out, a)
+                   : launch((kvq_merge_kernel<8, false, BandArgs>), grid, dim3(kMergeThreadsWide), s, out, a);
+    return half_batch(nct, 2) ? launch((kvq_merge_kernel<2, false, BandArgs, H>), grid, dim3(kMergeThreads), s, out, a)
+                              : launch((kvq_merge_kernel<2, false, BandArgs>), grid, dim3(kMergeThreads), s, out, a);
 }
 
 inline int launch_merge(const DecodeArgs& a, float* out, hipStream_t s) {
@@ -493,9 +502,18 @@ inline int launch_merge(const DecodeArgs& a, float* out, hipStream_t s) {
     if (a.batch == 1 && a.r4.max_chunks == 0)
         return wide ? launch((kvq_merge1_kernel<8>), grid, block, s, out, a)
                     : launch((kvq_merge1_kernel<2>), grid, block, s, out, a);
-    if (wide)
+    constexpr int H = kMergeBatch / 2;
+    const int nct = n_chunks_total(a);
+    if (wide) {
+        if (half_batch(nct, 8))
+            return live ? launch((kvq_merge_kernel<8, true, DecodeArgs, H>), grid, block, s, out, a)
+                        : launch((kvq_merge_kernel<8, false, DecodeArgs, H>), grid, block, s, out, a);
         return live ? launch((kvq_merge_kernel<8, true>), grid, block, s, out, a)
                     : launch((kvq_merge_kernel<8, false>), grid, block, s, out, a);
+    }
+    if (half_batch(nct, 2))
+        return live ? launch((kvq_merge_kernel<2, true, DecodeArgs, H>), grid, block, s, out, a)
+                    : launch((kvq_merge_kernel<2, false, DecodeArgs, H>), grid, block, s, out, a);
     return live ? launch((kvq_merge_kernel<2, true>), grid, block, s, out, a)
                 : launch((kvq_merge_kernel<2, false>), grid, block, s, out, a);
 }
