@@ -44,9 +44,9 @@ TOK_HEAD_BYTES = 2 * 128 + 2 * 4   # K+V codes + K/V float32 steps per (token, k
 # counters read for a plain 256 MiB device copy (--calibrate-copy 256):
 # FETCH_SIZE 131085.2 KiB -> 2.000 bytes per counted byte, WRITE_SIZE
 # 262144 KiB -> 1.000.  Valid only for the kernel sources they were taken on.
-PMC = {"sources_sha256_16": "727ace04b1690354",
-       "fetch_kib": {"chunk": 8616.29, "merge": 164.55}, "write_kib": {"chunk": 290.06, "merge": 8.00},
-       "fetch_scale": 268435456 / (131085.17 * 1024), "write_scale": 268435456 / (262144.0 * 1024)}
+PMC = {"sources_sha256_16": "bae4b79eb05f8ff9",
+       "fetch_kib": {"chunk": 8619.32, "merge": 164.56}, "write_kib": {"chunk": 290.06, "merge": 8.00},
+       "fetch_scale": 268435456 / (131085.21 * 1024), "write_scale": 268435456 / (262144.0 * 1024)}
 
 
 def kernel_sources_digest() -> str:
