@@ -78,12 +78,18 @@ __device__ __forceinline__ void group_walk(const Args& a, const Region& reg, con
         raw_next = mtile_raw(reg, btb, base + 2 * kChunkUnit, a.log2_bs, lane);
         Ops::template issue<BS8>(a, raw, base + kChunkUnit, kh, lane, lo, B);
         raw = raw_next;
+        // the tile's vector work ahead of the other wave's loads on this SIMD
+        // (int4 128K decode ~3% faster; the 2-bit band unchanged)
+        __builtin_amdgcn_s_setprio(2);
         Ops::compute(a, A, base, L, lane, wave, Q, st, sm);
+        __builtin_amdgcn_s_setprio(0);
         base += kChunkUnit;
         raw_next = mtile_raw(reg, btb, base + 2 * kChunkUnit, a.log2_bs, lane);
         Ops::template issue<BS8>(a, raw, base + kChunkUnit, kh, lane, lo, A);
         raw = raw_next;
+        __builtin_amdgcn_s_setprio(2);
         Ops::compute(a, B, base, L, lane, wave, Q, st, sm);
+        __builtin_amdgcn_s_setprio(0);
         base += kChunkUnit;
     }
     if (k + 1 < n_tiles) {
