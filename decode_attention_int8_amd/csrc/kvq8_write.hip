@@ -71,11 +71,11 @@ __device__ __forceinline__ void quantize_row8x16(const float (&x)[16], uint4& co
 // Row numbers of the pool (slot * nkv + head) fit in 32 bits: the host
 // checks n_slots * nkv, and ns_cap = min(n_slots, 2^31) turns the slot test
 // into one unsigned compare.
-template <int DT>
 // 16 code bytes of a lane as a native vector (the operand type of the
 // non-temporal store builtin)
 typedef uint32_t Codes16 __attribute__((ext_vector_type(4)));
 
+template <int DT>
 __global__ __launch_bounds__(256) void kvq8_quantize_append_kernel(
     int8_t* __restrict__ kc, int8_t* __restrict__ vc, float* __restrict__ ks, float* __restrict__ vs,
     uint32_t ns_cap, DivN nkv, const void* __restrict__ k_new, const void* __restrict__ v_new,
