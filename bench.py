@@ -44,8 +44,8 @@ TOK_HEAD_BYTES = 2 * 128 + 2 * 4   # K+V codes + K/V float32 steps per (token, k
 # counters read for a plain 256 MiB device copy (--calibrate-copy 256):
 # FETCH_SIZE 131085.3 KiB -> 2.000 bytes per counted byte, WRITE_SIZE
 # 262144 KiB -> 1.000.  Valid only for the kernel sources they were taken on.
-PMC = {"sources_sha256_16": "79da362a4620a315",
-       "fetch_kib": {"chunk": 8619.30, "merge": 164.55}, "write_kib": {"chunk": 290.06, "merge": 8.00},
+PMC = {"sources_sha256_16": "9da138b901489462",
+       "fetch_kib": {"chunk": 8619.30, "merge": 164.56}, "write_kib": {"chunk": 290.06, "merge": 8.00},
        "fetch_scale": 268435456 / (131085.31 * 1024), "write_scale": 268435456 / (262144.0 * 1024)}
 
 
